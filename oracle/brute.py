@@ -1,0 +1,107 @@
+"""Independent numpy (float64) formulations used to pin the C oracle.
+
+TEST INFRASTRUCTURE ONLY (same rule as the rest of ``oracle/``).
+
+These are deliberately written differently from ``qmoe_oracle.c`` so that one
+mistake cannot hide in both:
+
+- codes are read as one little-endian bit stream (``np.unpackbits`` with
+  ``bitorder='little'``) cut into consecutive ``bits``-wide fields, instead of
+  per-format shifts and masks. For INT4 (low nibble first), INT2 (low bits
+  first) and INT3 (code i at bits [3i, 3i+3) of the little-endian 24-bit
+  word) that stream reading is the same packing;
+- scales are expanded with ``np.repeat`` over the block and multiplied in bulk;
+- top-k is a full stable sort by (-logit, expert index) (``np.lexsort``);
+- the layer is computed densely: every expert runs on every token through
+  BLAS matmuls, and a [T, E] gate matrix that is zero off the top-k selects
+  and weights the results (a masked mixture), instead of per-route loops.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def unpack_codes(codes: np.ndarray, bits: int, K: int) -> np.ndarray:
+    """uint8 [..., K*bits/8] -> int64 [..., K] via a little-endian bit stream."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    lead = codes.shape[:-1]
+    stream = np.unpackbits(codes, axis=-1, bitorder="little")          # [..., 8*nbytes]
+    fields = stream.reshape(*lead, K, bits).astype(np.int64)
+    weights = (1 << np.arange(bits, dtype=np.int64))
+    return (fields * weights).sum(axis=-1)
+
+
+def pack_codes(q: np.ndarray, bits: int) -> np.ndarray:
+    """int [..., K] codes in [0, 2^bits) -> uint8 [..., K*bits/8] (little-endian bit stream)."""
+    q = np.asarray(q, dtype=np.int64)
+    assert q.min(initial=0) >= 0 and q.max(initial=0) < (1 << bits)
+    lead, K = q.shape[:-1], q.shape[-1]
+    assert (K * bits) % 8 == 0
+    bitsarr = ((q[..., None] >> np.arange(bits)) & 1).astype(np.uint8)   # [..., K, bits]
+    stream = bitsarr.reshape(*lead, K * bits)
+    return np.packbits(stream, axis=-1, bitorder="little")
+
+
+def dequant_dense(codes: np.ndarray, scales: np.ndarray, bits: int, block_size: int,
+                  zero_point: int, K: int) -> np.ndarray:
+    q = unpack_codes(codes, bits, K)
+    s = np.repeat(np.asarray(scales, dtype=np.float16).astype(np.float64), block_size, axis=-1)
+    return (q - zero_point).astype(np.float64) * s
+
+
+def topk_brute(logits64: np.ndarray, k: int) -> np.ndarray:
+    """Stable full sort of every token's experts by (-logit, index); first k ids."""
+    T, E = logits64.shape
+    idx = np.arange(E)
+    out = np.empty((T, k), dtype=np.int64)
+    for t in range(T):
+        order = np.lexsort((idx, -logits64[t]))     # primary: -logit, secondary: index
+        out[t] = order[:k]
+    return out
+
+
+def softmax_selected(logits64: np.ndarray, ids: np.ndarray) -> np.ndarray:
+    sel = np.take_along_axis(logits64, ids, axis=1)
+    z = np.exp(sel - sel.max(axis=1, keepdims=True))
+    return z / z.sum(axis=1, keepdims=True)
+
+
+def silu(v: np.ndarray) -> np.ndarray:
+    return v * (0.5 * (1.0 + np.tanh(0.5 * v)))      # sigmoid via tanh identity
+
+
+def dense_masked_forward(x64: np.ndarray, logits64: np.ndarray, weights, spec,
+                         *, swap_gate_up: bool = False, zp_delta: int = 0,
+                         softmax_all: bool = False) -> np.ndarray:
+    """Masked-mixture formulation of the layer in float64.
+
+    The keyword switches plant deliberate mistakes; tests use them to show that
+    the comparison against the oracle would notice each one.
+    """
+    T = x64.shape[0]
+    E, H, I, k = spec.num_experts, spec.hidden, spec.inter, spec.top_k
+    ids = topk_brute(logits64, k)
+    if softmax_all:
+        z = np.exp(logits64 - logits64.max(axis=1, keepdims=True))
+        p = z / z.sum(axis=1, keepdims=True)
+        w = np.take_along_axis(p, ids, axis=1)
+    else:
+        w = softmax_selected(logits64, ids)
+    gate = np.zeros((T, E), dtype=np.float64)
+    np.put_along_axis(gate, ids, w, axis=1)
+    out = np.zeros((T, H), dtype=np.float64)
+    zp = spec.zero_point + zp_delta
+    for e in range(E):
+        if not gate[:, e].any():
+            continue
+        W1 = dequant_dense(weights.fc1_codes[e], weights.fc1_scales[e], spec.bits,
+                           spec.block_size, zp, H)                   # [2I, H]
+        W2 = dequant_dense(weights.fc2_codes[e], weights.fc2_scales[e], spec.bits,
+                           spec.block_size, zp, I)                   # [H, I]
+        gu = x64 @ W1.T                                             # [T, 2I]
+        g, u = gu[:, :I], gu[:, I:]
+        if swap_gate_up:
+            g, u = u, g
+        h = silu(g) * u
+        out += gate[:, e:e + 1] * (h @ W2.T)
+    return out

@@ -1,0 +1,336 @@
+/*
+ * Plain, slow CPU oracle for the quantized MoE layer (com.microsoft::QMoE
+ * semantics with SwiGLU experts).
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the CPU
+ * baseline leg of the benchmark may load this library. It shares no code,
+ * header, table or helper with the GPU library, and the GPU library never
+ * calls it.
+ *
+ * Every quantity is computed in double precision from the stored inputs read
+ * as exact values. Sources (web pages on onnxruntime pull requests):
+ *
+ *  - "Document and test packed token inputs for MoE and QMoE" (Description):
+ *    input [total_tokens, hidden], router [total_tokens, num_experts], output
+ *    [total_tokens, hidden]; routing is token-local, so packed sequences need
+ *    no boundaries. QMoE takes raw router logits; the reference block applies
+ *    a softmax over the top-k logits (review comments on the test harness).
+ *  - "[CUDA/CPU] Add AVX2 INT4 cold-expert kernel and zero-cold doorbell
+ *    short-circuit" (Motivation & Summary, item 3): SwiGLU contract, fc1 rows
+ *    = 2 * inter_size, unsigned codes with a zero-point code.
+ *  - "[CUDA] Add INT4 and INT3 QMoE CPU/GPU offload support" (Description):
+ *    integer quantization with expert_weight_bits 4/3 and block sizes
+ *    {32, 64, 128}; scales stored [N, K/block] (not block-major).
+ *  - "[CUDA] Add MoEPacked CPU/GPU hybrid offload ..." (Key Changes, item 4
+ *    and the review-fix commit): the partial sums stay in fp32 and the
+ *    combine rounds once; NaN stays NaN when rounding to bf16; dot products
+ *    get K-sized heap scratch, not stack arrays.
+ *
+ * Readings taken where the pages leave a step open:
+ *  - top-k on raw logits, ties to the lower expert index, slots ordered by
+ *    descending logit then ascending index;
+ *  - softmax over the k selected logits (normalized routing weights);
+ *  - fc1 rows [0, I) are the gate, rows [I, 2I) the up projection, and
+ *    h = silu(gate) * up with silu(g) = g / (1 + exp(-g)) and no clamp;
+ *  - W[n][k] = (q[n][k] - zp) * s[n][k / block]; INT4 two codes per byte low
+ *    nibble first, INT2 four per byte low bits first, INT3 eight codes per
+ *    three bytes with code i at bits [3i, 3i+3) of the little-endian 24-bit
+ *    word;
+ *  - the permutation is the stable counting sort of route ids r = t*k + j by
+ *    expert;
+ *  - the output is the double accumulator rounded once to fp32 and, for bf16
+ *    outputs, that fp32 rounded to bf16 (round to nearest even).
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_OK 0
+#define ORACLE_BAD_ARG 1
+#define ORACLE_NO_MEM 2
+
+/* IEEE binary16 bit pattern -> double (exact). */
+double oracle_half_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int exponent = (h >> 10) & 31;
+    int mantissa = h & 1023;
+    double v;
+    if (exponent == 0)
+        v = ldexp((double)mantissa, -24);                 /* subnormal or zero */
+    else if (exponent == 31)
+        v = mantissa ? NAN : INFINITY;
+    else
+        v = ldexp((double)(mantissa | 1024), exponent - 25);
+    return sign ? -v : v;
+}
+
+/* fp32 -> bf16 bit pattern, round to nearest even; NaN stays NaN. */
+uint16_t oracle_f32_to_bf16(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return (uint16_t)((u >> 16) | 0x0040u);           /* quiet NaN, sign kept */
+    uint32_t lsb = (u >> 16) & 1u;
+    u += 0x7fffu + lsb;
+    return (uint16_t)(u >> 16);
+}
+
+/* Unsigned code number kk of one packed row. */
+static int code_at(const uint8_t *row, int64_t kk, int bits)
+{
+    if (bits == 4) {
+        uint8_t b = row[kk >> 1];
+        return (kk & 1) ? (b >> 4) : (b & 15);
+    }
+    if (bits == 2) {
+        uint8_t b = row[kk >> 2];
+        return (b >> (2 * (kk & 3))) & 3;
+    }
+    /* bits == 3 */
+    int64_t g = kk >> 3;
+    int i = (int)(kk & 7);
+    uint32_t w = (uint32_t)row[3 * g] | ((uint32_t)row[3 * g + 1] << 8) |
+                 ((uint32_t)row[3 * g + 2] << 16);
+    return (int)((w >> (3 * i)) & 7u);
+}
+
+static int64_t row_bytes(int64_t K, int bits) { return K * bits / 8; }
+
+static int valid_format(int64_t K, int bits, int bs)
+{
+    if (bits != 2 && bits != 3 && bits != 4) return 0;
+    if (bs <= 0 || K <= 0 || K % bs != 0) return 0;
+    if (K % 8 != 0) return 0;
+    return 1;
+}
+
+/* W[n][kk] = (q - zp) * s for one [N, K] matrix; out is [N, K] double. */
+int oracle_dequant(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
+                   int bits, int bs, int zp, double *out)
+{
+    if (!codes || !scales || !out || N < 0 || !valid_format(K, bits, bs)) return ORACLE_BAD_ARG;
+    int64_t rb = row_bytes(K, bits), nblk = K / bs;
+    for (int64_t n = 0; n < N; ++n) {
+        const uint8_t *row = codes + n * rb;
+        for (int64_t kk = 0; kk < K; ++kk) {
+            double s = oracle_half_to_double(scales[n * nblk + kk / bs]);
+            out[n * K + kk] = (double)(code_at(row, kk, bits) - zp) * s;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* Top-k selection and softmax over the selected logits, per token. */
+int oracle_route(const double *logits, int64_t T, int64_t E, int k,
+                 int32_t *topk_id, double *topk_w)
+{
+    if (!logits || !topk_id || !topk_w || T < 0 || E < 1 || k < 1 || k > E) return ORACLE_BAD_ARG;
+    unsigned char *taken = (unsigned char *)malloc((size_t)E);
+    if (!taken) return ORACLE_NO_MEM;
+    for (int64_t t = 0; t < T; ++t) {
+        const double *l = logits + t * E;
+        memset(taken, 0, (size_t)E);
+        for (int j = 0; j < k; ++j) {
+            int64_t best = -1;
+            for (int64_t e = 0; e < E; ++e) {
+                if (taken[e]) continue;
+                /* strict '>' keeps the lowest index among equal logits */
+                if (best < 0 || l[e] > l[best]) best = e;
+            }
+            taken[best] = 1;
+            topk_id[t * k + j] = (int32_t)best;
+        }
+        double lmax = l[topk_id[t * k]];
+        double denom = 0.0;
+        for (int j = 0; j < k; ++j) denom += exp(l[topk_id[t * k + j]] - lmax);
+        for (int j = 0; j < k; ++j) topk_w[t * k + j] = exp(l[topk_id[t * k + j]] - lmax) / denom;
+    }
+    free(taken);
+    return ORACLE_OK;
+}
+
+/* Stable counting sort of the routes r = t*k + j by expert. */
+int oracle_permute(const int32_t *topk_id, int64_t R, int64_t E, int32_t *counts,
+                   int32_t *offsets, int32_t *sorted_routes, int32_t *inv_pos)
+{
+    if (!topk_id || !counts || !offsets || !sorted_routes || !inv_pos || R < 0 || E < 1)
+        return ORACLE_BAD_ARG;
+    for (int64_t e = 0; e < E; ++e) counts[e] = 0;
+    for (int64_t r = 0; r < R; ++r) {
+        if (topk_id[r] < 0 || topk_id[r] >= E) return ORACLE_BAD_ARG;
+        counts[topk_id[r]]++;
+    }
+    offsets[0] = 0;
+    for (int64_t e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+    int32_t *cursor = (int32_t *)malloc((size_t)E * sizeof(int32_t));
+    if (!cursor) return ORACLE_NO_MEM;
+    for (int64_t e = 0; e < E; ++e) cursor[e] = offsets[e];
+    for (int64_t r = 0; r < R; ++r) {
+        int32_t pos = cursor[topk_id[r]]++;
+        sorted_routes[pos] = (int32_t)r;
+        inv_pos[r] = pos;
+    }
+    free(cursor);
+    return ORACLE_OK;
+}
+
+/* Rounding-point emulation (off by default). Each flag rounds one
+ * intermediate to bf16, to measure what a bf16 datapath costs. */
+#define EMU_W_BF16 1       /* dequantized weight (q - zp) * s */
+#define EMU_H_BF16 2       /* SwiGLU output h */
+#define EMU_GU_BF16 4      /* gate and up dot products */
+
+static double to_bf16(double v) {
+    uint32_t u = (uint32_t)oracle_f32_to_bf16((float)v) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+typedef struct {
+    int64_t hidden, inter, num_experts;
+    int32_t top_k, bits, block_size, zero_point;
+    int32_t emulate;     /* EMU_* bitmask, 0 for the plain definition */
+    int32_t pad;
+} oracle_layer;
+
+typedef struct {
+    const oracle_layer *L;
+    const double *x, *logits;
+    const uint8_t *fc1_codes, *fc2_codes;
+    const uint16_t *fc1_scales, *fc2_scales;
+    double *out;
+    int64_t t0, t1;
+    int status;
+} job;
+
+/* dot of one dequantized weight row with a double vector */
+static double row_dot(const uint8_t *row, const uint16_t *srow, const double *v, int64_t K,
+                      int bits, int bs, int zp, int emu_w)
+{
+    double acc = 0.0;
+    for (int64_t kk = 0; kk < K; ++kk) {
+        double w = (double)(code_at(row, kk, bits) - zp) * oracle_half_to_double(srow[kk / bs]);
+        if (emu_w) w = to_bf16(w);
+        acc += w * v[kk];
+    }
+    return acc;
+}
+
+static void *run_tokens(void *arg)
+{
+    job *jb = (job *)arg;
+    const oracle_layer *L = jb->L;
+    int64_t H = L->hidden, I = L->inter, E = L->num_experts;
+    int k = L->top_k, bits = L->bits, bs = L->block_size, zp = L->zero_point;
+    int64_t rb1 = row_bytes(H, bits), rb2 = row_bytes(I, bits);
+    int64_t nb1 = H / bs, nb2 = I / bs;
+    int emu_w = (L->emulate & EMU_W_BF16) != 0;
+    int emu_h = (L->emulate & EMU_H_BF16) != 0;
+    int emu_gu = (L->emulate & EMU_GU_BF16) != 0;
+
+    double *h = (double *)malloc((size_t)I * sizeof(double));
+    double *acc = (double *)malloc((size_t)H * sizeof(double));
+    int32_t *ids = (int32_t *)malloc((size_t)k * sizeof(int32_t));
+    double *w = (double *)malloc((size_t)k * sizeof(double));
+    if (!h || !acc || !ids || !w) {
+        jb->status = ORACLE_NO_MEM;
+        free(h); free(acc); free(ids); free(w);
+        return NULL;
+    }
+    for (int64_t t = jb->t0; t < jb->t1; ++t) {
+        const double *xt = jb->x + t * H;
+        int st = oracle_route(jb->logits + t * E, 1, E, k, ids, w);
+        if (st != ORACLE_OK) { jb->status = st; break; }
+        for (int64_t m = 0; m < H; ++m) acc[m] = 0.0;
+        for (int j = 0; j < k; ++j) {
+            int64_t e = ids[j];
+            const uint8_t *c1 = jb->fc1_codes + e * (2 * I) * rb1;
+            const uint16_t *s1 = jb->fc1_scales + e * (2 * I) * nb1;
+            const uint8_t *c2 = jb->fc2_codes + e * H * rb2;
+            const uint16_t *s2 = jb->fc2_scales + e * H * nb2;
+            for (int64_t n = 0; n < I; ++n) {
+                double g = row_dot(c1 + n * rb1, s1 + n * nb1, xt, H, bits, bs, zp, emu_w);
+                double u = row_dot(c1 + (I + n) * rb1, s1 + (I + n) * nb1, xt, H, bits, bs, zp, emu_w);
+                if (emu_gu) { g = to_bf16(g); u = to_bf16(u); }
+                double hv = g / (1.0 + exp(-g)) * u;
+                h[n] = emu_h ? to_bf16(hv) : hv;
+            }
+            for (int64_t m = 0; m < H; ++m) {
+                double y = row_dot(c2 + m * rb2, s2 + m * nb2, h, I, bits, bs, zp, emu_w);
+                acc[m] += w[j] * y;
+            }
+        }
+        for (int64_t m = 0; m < H; ++m) jb->out[t * H + m] = acc[m];
+    }
+    free(h); free(acc); free(ids); free(w);
+    return NULL;
+}
+
+/*
+ * Whole layer: out[t][m] = sum_j w[t][j] * (W2[e] silu(W1g[e] x_t) * (W1u[e] x_t))[m]
+ * for the k experts e = topk_id[t][j], accumulated in double.
+ * x: [T, H] double, logits: [T, E] double, out: [T, H] double.
+ * Tokens are split into contiguous ranges over nthreads POSIX threads.
+ */
+int oracle_forward(const oracle_layer *L, const double *x, const double *logits,
+                   const uint8_t *fc1_codes, const uint16_t *fc1_scales,
+                   const uint8_t *fc2_codes, const uint16_t *fc2_scales,
+                   int64_t T, double *out, int nthreads)
+{
+    if (!L || T < 0) return ORACLE_BAD_ARG;
+    if (T == 0) return ORACLE_OK;
+    if (!x || !logits || !fc1_codes || !fc1_scales || !fc2_codes || !fc2_scales || !out)
+        return ORACLE_BAD_ARG;
+    if (L->num_experts < 1 || L->top_k < 1 || L->top_k > L->num_experts) return ORACLE_BAD_ARG;
+    if (!valid_format(L->hidden, L->bits, L->block_size) ||
+        !valid_format(L->inter, L->bits, L->block_size))
+        return ORACLE_BAD_ARG;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > T) nthreads = (int)T;
+    job *jobs = (job *)calloc((size_t)nthreads, sizeof(job));
+    pthread_t *th = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+    if (!jobs || !th) { free(jobs); free(th); return ORACLE_NO_MEM; }
+    for (int i = 0; i < nthreads; ++i) {
+        jobs[i] = (job){L, x, logits, fc1_codes, fc2_codes, fc1_scales, fc2_scales, out,
+                        T * i / nthreads, T * (i + 1) / nthreads, ORACLE_OK};
+    }
+    int started = 0;
+    for (int i = 1; i < nthreads; ++i) {
+        if (pthread_create(&th[i], NULL, run_tokens, &jobs[i]) != 0) break;
+        started = i;
+    }
+    run_tokens(&jobs[0]);
+    for (int i = 1; i <= started; ++i) pthread_join(th[i], NULL);
+    for (int i = started + 1; i < nthreads; ++i) run_tokens(&jobs[i]);  /* not started */
+    int st = ORACLE_OK;
+    for (int i = 0; i < nthreads; ++i)
+        if (jobs[i].status != ORACLE_OK) st = jobs[i].status;
+    free(jobs); free(th);
+    return st;
+}
+
+/* Final rounding: double accumulator -> fp32 (one rounding) and -> bf16 of that fp32. */
+void oracle_round_output(const double *acc, int64_t n, float *out_f32, uint16_t *out_bf16)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        float f = (float)acc[i];
+        if (out_f32) out_f32[i] = f;
+        if (out_bf16) out_bf16[i] = oracle_f32_to_bf16(f);
+    }
+}
+
+/* Batch helpers for exhaustive checks. */
+void oracle_half_to_double_n(const uint16_t *h, int64_t n, double *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_half_to_double(h[i]);
+}
+
+void oracle_f32_to_bf16_n(const float *f, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_f32_to_bf16(f[i]);
+}

@@ -1,0 +1,358 @@
+"""Pins for the CPU oracle: each check ties it to something other than itself.
+
+The pages print no worked numeric example for the QMoE layer, so the pins are
+closed forms, library routines, brute force on small inputs, invariants and
+the hand-written packing vectors in ``tests/golden/packing.json``.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import brute
+import qmoe_inputs as qi
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "packing.json")
+
+
+# ---------------------------------------------------------------- conversions
+
+def test_half_decode_all_patterns():
+    """All 65,536 fp16 patterns against numpy's float16 -> float64 conversion."""
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = oracle.half_to_double(h)
+    ref = h.view(np.float16).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # signed zeros and infinities keep their sign
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+@pytest.mark.parametrize("chunk", range(16))
+def test_bf16_rounding_all_floats(chunk):
+    """fp32 -> bf16 round-to-nearest-even over all 2^32 patterns (16 slices)
+    against torch's conversion; NaN must stay NaN."""
+    n = 1 << 28
+    step = 1 << 24
+    base = chunk * n
+    for off in range(0, n, step):
+        u = np.arange(base + off, base + off + step, dtype=np.uint64).astype(np.uint32)
+        f = u.view(np.float32)
+        got = oracle.f32_to_bf16_bits(f)
+        ref = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        isnan = np.isnan(f)
+        got_nan = ((got & 0x7F80) == 0x7F80) & ((got & 0x7F) != 0)
+        assert np.array_equal(got_nan, isnan)
+        assert np.array_equal(got[~isnan], ref[~isnan])
+
+
+# ---------------------------------------------------------------- packing / dequant
+
+def _golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+@pytest.mark.parametrize("case", _golden()["packing"], ids=lambda c: f"int{c['bits']}-{c['bytes']}")
+def test_packing_golden(case):
+    bits, codes, want = case["bits"], case["codes"], np.array(case["bytes"], dtype=np.uint8)
+    K = len(codes)
+    assert np.array_equal(brute.pack_codes(np.array([codes]), bits)[0], want)
+    assert np.array_equal(brute.unpack_codes(want[None], bits, K)[0], codes)
+    # oracle reads the same codes: scale 1.0 (fp16 0x3C00), zero point 0.
+    # K may be shorter than a block, so use block size = K (the oracle only
+    # requires K % 8 == 0 and K % bs == 0).
+    if K % 8 == 0:
+        s = np.full((1, 1), 0x3C00, dtype=np.uint16).view(np.float16)
+        got = oracle.dequant(want[None], s, bits, K, 0, K)[0]
+        assert np.array_equal(got, np.array(codes, dtype=np.float64))
+
+
+@pytest.mark.parametrize("case", _golden()["dequant"], ids=lambda c: f"int{c['bits']}")
+def test_dequant_golden(case):
+    bits, zp, codes = case["bits"], case["zero_point"], case["codes"]
+    K = 8 * ((len(codes) + 7) // 8)
+    q = np.zeros(K, dtype=np.int64)
+    q[: len(codes)] = codes
+    packed = brute.pack_codes(q[None], bits)
+    s = np.full((1, 1), case["scale_fp16_bits"], dtype=np.uint16).view(np.float16)
+    assert float(s[0, 0]) == case["scale"]
+    got = oracle.dequant(packed, s, bits, K, zp, K)[0][: len(codes)]
+    assert np.array_equal(got, np.array(case["values"], dtype=np.float64))
+
+
+@pytest.mark.parametrize("bits,bs,K", [(4, 32, 64), (4, 64, 256), (4, 128, 2048),
+                                       (3, 32, 64), (3, 64, 768), (3, 128, 256),
+                                       (2, 32, 96), (2, 64, 128), (2, 128, 2048)])
+def test_dequant_matches_bitstream_reading(bits, bs, K):
+    """C per-format shifts vs the numpy bit-stream reading, random rows and scales."""
+    rng = np.random.default_rng(bits * 1000 + bs + K)
+    N = 37
+    codes = rng.integers(0, 256, size=(N, K * bits // 8), dtype=np.uint8)
+    scales = (rng.standard_normal((N, K // bs)) * 3).astype(np.float16)
+    zp = 1 << (bits - 1)
+    got = oracle.dequant(codes, scales, bits, bs, zp, K)
+    ref = brute.dequant_dense(codes, scales, bits, bs, zp, K)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_dequant_exhaustive_codes_times_scales(bits):
+    """Every code times every finite fp16 scale: (q - zp) * s is exact in
+    float64 and equals the integer multiple of the decoded scale."""
+    zp = 1 << (bits - 1)
+    ncodes = 1 << bits
+    allh = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    finite = np.isfinite(allh.view(np.float16))
+    hs = allh[finite]
+    # one row per scale, K = 8*ncodes codes cycling through all codes
+    K = 8 * ncodes
+    q = np.tile(np.arange(ncodes), K // ncodes)
+    packed = np.broadcast_to(brute.pack_codes(q[None], bits), (hs.size, K * bits // 8)).copy()
+    scales = np.repeat(hs.view(np.float16)[:, None], K // K, axis=1)       # block = K
+    got = oracle.dequant(packed, scales, bits, K, zp, K)
+    s64 = hs.view(np.float16).astype(np.float64)
+    ref = (q[None, :] - zp).astype(np.float64) * s64[:, None]
+    assert np.array_equal(got, ref)
+    # exact in fp32 as well: at most 11 + 3 significant bits
+    assert np.array_equal(got.astype(np.float32).astype(np.float64), got)
+
+
+# ---------------------------------------------------------------- routing
+
+def _logits_with_ties(T, E, rng):
+    l = rng.standard_normal((T, E))
+    # quantize hard so that many logits tie
+    l = np.round(l * 2) / 2
+    return l
+
+
+@pytest.mark.parametrize("E,k", [(4, 2), (8, 8), (16, 1), (128, 8), (64, 6)])
+def test_topk_against_stable_sort(E, k):
+    rng = np.random.default_rng(E * 31 + k)
+    T = 300
+    for logits in (rng.standard_normal((T, E)), _logits_with_ties(T, E, rng),
+                   np.zeros((T, E))):
+        ids, w = oracle.route(logits, k)
+        assert np.array_equal(ids, brute.topk_brute(logits, k))
+        np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-15 * k)
+
+
+def test_topk_bf16_logits_ties():
+    """bf16 logits tie often; the lower expert index must win."""
+    rng = np.random.default_rng(7)
+    l = torch.from_numpy(rng.standard_normal((2000, 128))).to(torch.bfloat16)
+    l64 = l.to(torch.float64).numpy()
+    ids, _ = oracle.route(l, 8)
+    assert np.array_equal(ids, brute.topk_brute(l64, 8))
+    # the draw really exercises ties among the selected/next experts
+    srt = -np.sort(-l64, axis=1)
+    assert (srt[:, 7] == srt[:, 8]).mean() > 0.01
+
+
+def test_topk_constructed_ties():
+    logits = np.array([[1.0, 3.0, 3.0, 0.5, 3.0],
+                       [2.0, 2.0, 2.0, 2.0, 2.0],
+                       [-1.0, 0.0, -1.0, 0.0, 5.0]])
+    ids, w = oracle.route(logits, 3)
+    assert ids.tolist() == [[1, 2, 4], [0, 1, 2], [4, 1, 3]]
+    np.testing.assert_allclose(w[0], [1 / 3] * 3, rtol=0, atol=1e-16)
+    np.testing.assert_allclose(w[1], [1 / 3] * 3, rtol=0, atol=1e-16)
+
+
+def test_softmax_full_k_is_softmax():
+    """With k = E the routing weights are the textbook softmax (torch, fp64)."""
+    rng = np.random.default_rng(11)
+    logits = rng.standard_normal((64, 16)) * 4
+    ids, w = oracle.route(logits, 16)
+    ref = torch.softmax(torch.from_numpy(logits), dim=1).numpy()
+    got = np.zeros_like(ref)
+    np.put_along_axis(got, ids.astype(np.int64), w, axis=1)
+    np.testing.assert_allclose(got, ref, rtol=1e-14, atol=1e-300)
+
+
+def test_softmax_k1_is_one():
+    rng = np.random.default_rng(12)
+    ids, w = oracle.route(rng.standard_normal((50, 32)), 1)
+    assert np.all(w == 1.0)
+
+
+def test_softmax_selected_closed_form():
+    logits = np.array([[0.0, np.log(3.0), -50.0, np.log(2.0)]])
+    ids, w = oracle.route(logits, 3)
+    assert ids.tolist() == [[1, 3, 0]]
+    np.testing.assert_allclose(w[0], [0.5, 1 / 3, 1 / 6], rtol=1e-15)
+
+
+# ---------------------------------------------------------------- permutation
+
+@pytest.mark.parametrize("T,E,k,skew", [(0, 8, 2, False), (1, 128, 8, False), (4, 4, 2, False),
+                                        (513, 128, 8, True), (2000, 64, 4, False)])
+def test_permutation_against_stable_argsort(T, E, k, skew):
+    rng = np.random.default_rng(T + E + k)
+    logits = rng.standard_normal((T, E))
+    if skew:
+        logits += qi.zipf_bias(E, 1.1, rng)[None, :]
+    ids, _ = oracle.route(logits, k) if T else (np.zeros((0, k), np.int32), None)
+    counts, offsets, sorted_routes, inv_pos = oracle.permute(ids, E)
+    flat = ids.reshape(-1)
+    R = flat.size
+    assert np.array_equal(sorted_routes, np.argsort(flat, kind="stable"))
+    assert np.array_equal(counts, np.bincount(flat, minlength=E))
+    assert offsets[0] == 0 and offsets[-1] == R and np.all(np.diff(offsets) == counts)
+    assert np.array_equal(np.sort(sorted_routes), np.arange(R))
+    assert np.all(np.diff(flat[sorted_routes]) >= 0)
+    assert np.array_equal(inv_pos[sorted_routes], np.arange(R))
+
+
+# ---------------------------------------------------------------- whole layer
+
+def _small_spec(**kw):
+    return qi.spec_with(qi.TINY, **kw)
+
+
+def _run(wl, nthreads=4, emulate=0):
+    return oracle.forward(oracle.Layer.from_spec(wl.spec), wl.tokens.x, wl.tokens.logits,
+                          wl.weights, nthreads=nthreads, emulate=emulate)
+
+
+def _brute(wl, **kw):
+    return brute.dense_masked_forward(oracle.as_f64(wl.tokens.x), oracle.as_f64(wl.tokens.logits),
+                                      wl.weights, wl.spec, **kw)
+
+
+def _close(a, b, rtol=1e-12):
+    scale = np.abs(b).max() + 1e-300
+    return np.abs(a - b).max() <= rtol * scale
+
+
+def test_tiny_layer_against_dense_masked():
+    wl = qi.make_workload("tiny")
+    acc = _run(wl)
+    ref = _brute(wl)
+    assert _close(acc, ref)
+    f32, _ = oracle.round_output(acc)
+    f32_ref = ref.astype(np.float32)
+    ulps = np.abs(f32.view(np.int32).astype(np.int64) - f32_ref.view(np.int32).astype(np.int64))
+    assert ulps.max() <= 1
+
+
+@pytest.mark.parametrize("name,T", [("decode", 4), ("int3", 3), ("stack", 2), ("prefill", 3)])
+def test_qwen_shaped_slices_against_dense_masked(name, T):
+    wl = qi.make_workload(name, T=T)
+    acc = _run(wl, nthreads=4)
+    ref = _brute(wl)
+    assert _close(acc, ref)
+
+
+@pytest.mark.parametrize("bits,bs", [(4, 64), (4, 128), (3, 32), (3, 128), (2, 64), (2, 128)])
+def test_formats_against_dense_masked(bits, bs):
+    spec = _small_spec(hidden=256, inter=128, num_experts=6, top_k=3, bits=bits,
+                       block_size=bs, zero_point=1 << (bits - 1), act_dtype="bf16")
+    wl = qi.make_layer(spec, T=9, seed=100 + bits * 10 + bs)
+    assert _close(_run(wl), _brute(wl))
+
+
+def test_planted_mistakes_are_visible():
+    """Each plausible slip in the layer definition moves the result far beyond
+    rounding noise, so the dense-masked pin would catch it."""
+    wl = qi.make_workload("tiny")
+    acc = _run(wl)
+    for kw in ({"swap_gate_up": True}, {"zp_delta": 1}, {"softmax_all": True}):
+        bad = _brute(wl, **kw)
+        assert not _close(acc, bad, rtol=1e-3), kw
+
+
+def test_single_expert_is_dense_swiglu_mlp():
+    """E=1, k=1 reduces to a dense SwiGLU MLP on the dequantized weights."""
+    spec = _small_spec(num_experts=1, top_k=1, hidden=128, inter=64, act_dtype="bf16")
+    wl = qi.make_layer(spec, T=7, seed=5)
+    acc = _run(wl)
+    W1 = brute.dequant_dense(wl.weights.fc1_codes[0], wl.weights.fc1_scales[0], 4, 32, 8, 128)
+    W2 = brute.dequant_dense(wl.weights.fc2_codes[0], wl.weights.fc2_scales[0], 4, 32, 8, 64)
+    x = torch.from_numpy(oracle.as_f64(wl.tokens.x))
+    gu = x @ torch.from_numpy(W1).T
+    h = torch.nn.functional.silu(gu[:, :64]) * gu[:, 64:]
+    ref = (h @ torch.from_numpy(W2).T).numpy()
+    assert _close(acc, ref)
+
+
+def test_zero_point_codes_give_zero_output():
+    spec = _small_spec(act_dtype="bf16")
+    wl = qi.make_layer(spec, T=5, seed=9)
+    q1 = np.full((spec.num_experts, 2 * spec.inter, spec.hidden), spec.zero_point)
+    wl.weights.fc1_codes = np.ascontiguousarray(brute.pack_codes(q1, 4))
+    acc = _run(wl)
+    assert np.all(acc == 0.0)
+
+
+def test_identical_experts_reduce_to_one():
+    """All experts equal: the routing weights sum to one, so the output is the
+    single-expert FFN whatever the routing."""
+    spec = _small_spec(num_experts=5, top_k=3, act_dtype="bf16")
+    wl = qi.make_layer(spec, T=6, seed=21)
+    w = wl.weights
+    for arr_name in ("fc1_codes", "fc1_scales", "fc2_codes", "fc2_scales"):
+        a = getattr(w, arr_name)
+        setattr(w, arr_name, np.ascontiguousarray(np.broadcast_to(a[:1], a.shape)))
+    acc = _run(wl)
+    one = qi.Workload("one", qi.spec_with(spec, num_experts=1, top_k=1), wl.tokens, qi.LayerWeights(
+        w.fc1_codes[:1].copy(), w.fc1_scales[:1].copy(), w.fc2_codes[:1].copy(), w.fc2_scales[:1].copy()))
+    one.tokens = qi.Tokens(wl.tokens.x, wl.tokens.logits[:, :1].contiguous())
+    ref = _run(one)
+    assert _close(acc, ref, rtol=1e-13)
+
+
+def test_packed_equals_per_sequence_runs():
+    """Token-local routing: concatenating per-sequence runs reproduces the
+    packed run bit for bit."""
+    wl = qi.make_workload("prefill", T=24)
+    assert len(wl.tokens.seq_lens) == 16 and sum(wl.tokens.seq_lens) == 24
+    packed = _run(wl, nthreads=3)
+    parts, s = [], 0
+    for n in wl.tokens.seq_lens:
+        sub = qi.Workload("seq", wl.spec, qi.Tokens(wl.tokens.x[s:s + n], wl.tokens.logits[s:s + n]),
+                          wl.weights)
+        parts.append(_run(sub, nthreads=2))
+        s += n
+    assert np.array_equal(np.concatenate(parts), packed)
+
+
+def test_thread_count_does_not_change_result():
+    wl = qi.make_workload("decode", T=4)
+    assert np.array_equal(_run(wl, nthreads=1), _run(wl, nthreads=4))
+
+
+def test_empty_input():
+    wl = qi.make_workload("tiny", T=0)
+    assert _run(wl).shape == (0, 64)
+
+
+def test_routing_weights_sum_to_one_on_workloads():
+    for name, T in (("decode", 4), ("prefill", 512), ("stack", 256)):
+        wl = qi.make_workload(name, T=T)
+        _, w = oracle.route(wl.tokens.logits, wl.spec.top_k)
+        np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-14)
+
+
+def test_zipf_skew_present():
+    wl = qi.make_workload("prefill", T=2048)
+    ids, _ = oracle.route(wl.tokens.logits, 8)
+    counts = np.bincount(ids.reshape(-1), minlength=128)
+    assert counts.max() > 0.8 * 2048          # top experts take nearly every token
+    assert (counts == 0).sum() > 10           # a long tail of idle experts
+
+
+def test_emulated_bf16_points_stay_close():
+    """The bf16 datapath reading (bf16 weights and bf16 h) moves the result by
+    well under the 1e-2 per-token relative-L2 bound on a Qwen3-shaped slice."""
+    wl = qi.make_workload("decode", T=4)
+    exact = _run(wl)
+    emu = _run(wl, emulate=oracle.EMU_W_BF16 | oracle.EMU_H_BF16)
+    rel = np.linalg.norm(emu - exact, axis=1) / np.linalg.norm(exact, axis=1)
+    assert rel.max() < 5e-3
+    assert rel.max() > 1e-5          # the emulation really changes something
