@@ -1,0 +1,171 @@
+/*
+ * qmoe.h - C ABI of the MI355X (gfx950) quantized mixture-of-experts layer.
+ *
+ * The layer follows com.microsoft::QMoE semantics with SwiGLU experts, as the
+ * onnxruntime pull-request pages describe them:
+ *  - packed token-major I/O: x [T, hidden], router logits [T, num_experts],
+ *    out [T, hidden]; sequences are concatenated without padding because
+ *    routing is token-local ("Document and test packed token inputs for MoE and
+ *    QMoE", Description);
+ *  - raw router logits in; top-k, then a softmax over the k selected logits
+ *    (same page, review comments on the CPU test harness and on top-k
+ *    normalization);
+ *  - integer experts with expert_weight_bits 4/3/2, block sizes 32/64/128,
+ *    fp16 scales stored [N, K/block] and unsigned codes with a zero-point
+ *    ("[CUDA] Add INT4 and INT3 QMoE CPU/GPU offload support", Description;
+ *    "[CUDA/CPU] Add AVX2 INT4 cold-expert kernel and zero-cold doorbell
+ *    short-circuit for QMoE offload", Motivation & Summary item 3: swiglu,
+ *    fc1 rows = 2 * inter_size; "[CUDA] Add MoEPacked CPU/GPU hybrid offload
+ *    and consolidate QMoE/GGUF offload optimizations", Summary: INT2 experts);
+ *  - the routing-weighted combine accumulates in fp32 and rounds to the
+ *    activation dtype once (the MoEPacked page, Key Changes item 4).
+ *
+ * Weight layout (device memory, owned by the caller, read-only here):
+ *   fc1_codes  uint8  [E][2*inter][hidden*bits/8]  rows [0,I) gate, [I,2I) up
+ *   fc1_scales fp16   [E][2*inter][hidden/block]
+ *   fc2_codes  uint8  [E][hidden][inter*bits/8]
+ *   fc2_scales fp16   [E][hidden][inter/block]
+ * Codes are unsigned, K contiguous. INT4: two codes per byte, low nibble
+ * first. INT2: four per byte, low bits first. INT3: eight codes per three
+ * bytes, code i at bits [3i, 3i+3) of the little-endian 24-bit word.
+ * W[n][k] = (q[n][k] - zero_point) * scale[n][k / block].
+ *
+ * Conventions for every call:
+ *  - no exception crosses the ABI; each call returns a qmoe_status;
+ *  - every argument is validated on the host before any device work; a call
+ *    that returns an error has enqueued nothing;
+ *  - device pointers must be 16-byte aligned;
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream);
+ *    work is enqueued asynchronously and the call returns without
+ *    synchronizing; only launch errors are reported (QMOE_ERR_HIP);
+ *  - a handle may be used from one stream at a time.
+ */
+#ifndef QMOE_H
+#define QMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum qmoe_status {
+    QMOE_OK = 0,
+    QMOE_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, bad size, bad enum */
+    QMOE_ERR_UNSUPPORTED = 2,   /* valid but not implemented (e.g. huge top_k) */
+    QMOE_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required */
+    QMOE_ERR_HIP = 4,           /* a HIP runtime call or kernel launch failed */
+    QMOE_ERR_OOM = 5            /* host allocation failed */
+} qmoe_status;
+
+typedef enum qmoe_dtype {
+    QMOE_F32 = 0,               /* x, logits and out are float32 */
+    QMOE_BF16 = 1               /* x, logits and out are bfloat16 */
+} qmoe_dtype;
+
+/* Layer description, passed by value into qmoe_create and validated once. */
+typedef struct qmoe_config {
+    uint32_t struct_size;       /* sizeof(qmoe_config): ABI guard */
+    int32_t top_k;              /* 1 <= top_k <= min(num_experts, 32) */
+    int64_t hidden;             /* H > 0, multiple of block_size */
+    int64_t inter;              /* I > 0, multiple of block_size */
+    int64_t num_experts;        /* 1 <= E <= 1024 */
+    int32_t bits;               /* 2, 3 or 4 */
+    int32_t block_size;         /* 32, 64 or 128 */
+    int32_t zero_point;         /* 0 <= zp < 2^bits, or -1 for 2^(bits-1) */
+    int32_t act_dtype;          /* qmoe_dtype */
+    int32_t normalize_routing;  /* must be 1: softmax over the selected k */
+    int32_t reserved;           /* must be 0 */
+    int64_t max_tokens;         /* largest T accepted by qmoe_forward (>= 0) */
+} qmoe_config;
+
+/* Device pointers to the expert weights (layout in the file comment). */
+typedef struct qmoe_weights {
+    const void *fc1_codes;
+    const void *fc1_scales;
+    const void *fc2_codes;
+    const void *fc2_scales;
+} qmoe_weights;
+
+typedef struct qmoe_handle qmoe_handle;
+
+/*
+ * Create a layer handle. Validates the config and the weight pointers and
+ * stores them; the weights are neither copied nor freed and must outlive the
+ * handle. `device` is the HIP device ordinal the weights live on.
+ * On success *out receives the handle; on error *out is set to NULL.
+ */
+qmoe_status qmoe_create(const qmoe_config *config, const qmoe_weights *weights, int device,
+                        qmoe_handle **out);
+
+/*
+ * Bytes of device workspace qmoe_forward needs for `num_tokens` tokens
+ * (0 <= num_tokens <= max_tokens). The workspace holds the routing arrays,
+ * the permutation, the per-route intermediate activations and per-route fp32
+ * FC2 outputs; it carries no state between calls.
+ */
+qmoe_status qmoe_workspace_size(const qmoe_handle *handle, int64_t num_tokens, size_t *bytes);
+
+/*
+ * The layer forward pass: out[t] = sum_j w[t][j] * FFN_{e[t][j]}(x[t]).
+ *  x       device [num_tokens, hidden]       act_dtype, row-major
+ *  logits  device [num_tokens, num_experts]  act_dtype, raw router logits
+ *  out     device [num_tokens, hidden]       act_dtype (written)
+ *  workspace / workspace_bytes: caller-owned device scratch of at least
+ *          qmoe_workspace_size(num_tokens) bytes.
+ * num_tokens == 0 returns QMOE_OK and launches nothing. Tokens 1..4 take the
+ * memory-bound decode path; larger counts take the grouped-GEMM prefill path.
+ */
+qmoe_status qmoe_forward(qmoe_handle *handle, const void *x, const void *logits, void *out,
+                         int64_t num_tokens, void *workspace, size_t workspace_bytes,
+                         void *stream);
+
+/* Release a handle (host state only). qmoe_destroy(NULL) returns QMOE_OK. */
+qmoe_status qmoe_destroy(qmoe_handle *handle);
+
+/* Static, human-readable text for a status code. */
+const char *qmoe_status_string(qmoe_status status);
+
+/*
+ * Test exports. Same conventions as above.
+ *
+ * qmoe_route runs only the routing stage of the prefill path on `num_tokens`
+ * tokens (any count 1..max_tokens) and copies its results out:
+ *   topk_id        int32 [T, top_k]   selected experts, slot order
+ *   topk_w         fp32  [T, top_k]   softmax over the selected logits
+ *   expert_offsets int32 [E + 1]      exclusive prefix sum of routes per expert
+ *   sorted_routes  int32 [T * top_k]  route ids r = t*top_k + j, stably sorted by expert
+ *   inv_pos        int32 [T * top_k]  position of route r in sorted_routes
+ * All output pointers are device pointers; any of them may be NULL to skip it.
+ */
+qmoe_status qmoe_route(qmoe_handle *handle, const void *logits, int64_t num_tokens,
+                       int32_t *topk_id, float *topk_w, int32_t *expert_offsets,
+                       int32_t *sorted_routes, int32_t *inv_pos, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
+/*
+ * qmoe_dequant writes the dequantized matrix of one expert of FC1 (fc = 1,
+ * [2*inter, hidden]) or FC2 (fc = 2, [hidden, inter]) using the kernels' own
+ * unpacking routines:
+ *   out_f32  device fp32 [N, K]: (q - zp) * scale as read by the decode path
+ *   out_bf16 device bf16 bits [N, K]: the round-to-nearest-even bf16 value the
+ *            prefill path stages for the matrix cores
+ * Either output may be NULL.
+ */
+qmoe_status qmoe_dequant(qmoe_handle *handle, int fc, int64_t expert, float *out_f32,
+                         uint16_t *out_bf16, void *stream);
+
+/*
+ * Byte offsets, inside the workspace of a qmoe_forward call on `num_tokens`
+ * tokens, of the routing results that call leaves behind: topk_id (int32
+ * [T, top_k]) and topk_w (fp32 [T, top_k]). Both paths write them.
+ */
+qmoe_status qmoe_workspace_routing(const qmoe_handle *handle, int64_t num_tokens,
+                                   size_t *topk_id_offset, size_t *topk_w_offset);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMOE_H */

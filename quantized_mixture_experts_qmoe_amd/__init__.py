@@ -1,0 +1,221 @@
+"""Python binding of libqmoe, the gfx950 quantized MoE layer.
+
+Argument marshalling only: torch tensors supply device memory and the current
+HIP stream; every step of the layer runs in the library's HIP kernels. There
+is no CPU fallback: if ``libqmoe.so`` is missing or fails to load, every entry
+point raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqmoe.so")
+
+QMOE_F32, QMOE_BF16 = 0, 1
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration",
+          3: "workspace missing or too small", 4: "HIP runtime error", 5: "out of host memory"}
+
+EXPORTS = ("qmoe_create", "qmoe_workspace_size", "qmoe_forward", "qmoe_destroy",
+           "qmoe_status_string", "qmoe_route", "qmoe_dequant", "qmoe_workspace_routing")
+
+
+class QMoEError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {STATUS.get(status, status)} (status {status})")
+        self.status = status
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("top_k", ctypes.c_int32),
+                ("hidden", ctypes.c_int64), ("inter", ctypes.c_int64),
+                ("num_experts", ctypes.c_int64), ("bits", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("zero_point", ctypes.c_int32),
+                ("act_dtype", ctypes.c_int32), ("normalize_routing", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("max_tokens", ctypes.c_int64)]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [("fc1_codes", ctypes.c_void_p), ("fc1_scales", ctypes.c_void_p),
+                ("fc2_codes", ctypes.c_void_p), ("fc2_scales", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libqmoe.so (built in-tree by ``_build.build``); raise if absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m quantized_mixture_experts_qmoe_amd._build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+        L.qmoe_create.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(Weights), ctypes.c_int,
+                                  ctypes.POINTER(P)]
+        L.qmoe_workspace_size.argtypes = [P, i64, ctypes.POINTER(sz)]
+        L.qmoe_forward.argtypes = [P, P, P, P, i64, P, sz, P]
+        L.qmoe_destroy.argtypes = [P]
+        L.qmoe_status_string.argtypes = [i32]
+        L.qmoe_status_string.restype = ctypes.c_char_p
+        L.qmoe_route.argtypes = [P, P, i64, P, P, P, P, P, P, sz, P]
+        L.qmoe_dequant.argtypes = [P, ctypes.c_int, i64, P, P, P]
+        L.qmoe_workspace_routing.argtypes = [P, i64, ctypes.POINTER(sz), ctypes.POINTER(sz)]
+        for name in ("qmoe_create", "qmoe_workspace_size", "qmoe_forward", "qmoe_destroy",
+                     "qmoe_route", "qmoe_dequant", "qmoe_workspace_routing"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(st: int, what: str):
+    if st != 0:
+        raise QMoEError(st, what)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream: Optional[torch.cuda.Stream] = None) -> ctypes.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+_ACT = {torch.bfloat16: QMOE_BF16, torch.float32: QMOE_F32}
+
+
+@dataclass
+class LayerConfig:
+    hidden: int
+    inter: int
+    num_experts: int
+    top_k: int
+    bits: int
+    block_size: int
+    zero_point: int = -1
+    act_dtype: torch.dtype = torch.bfloat16
+    max_tokens: int = 8192
+
+
+class QMoELayer:
+    """One quantized MoE layer resident on a GPU.
+
+    Weight tensors (on the GPU, contiguous, owned by the caller and kept alive
+    by this object): fc1_codes uint8 [E, 2I, H*bits/8], fc1_scales fp16
+    [E, 2I, H/bs], fc2_codes uint8 [E, H, I*bits/8], fc2_scales fp16 [E, H, I/bs].
+    """
+
+    def __init__(self, cfg: LayerConfig, fc1_codes: torch.Tensor, fc1_scales: torch.Tensor,
+                 fc2_codes: torch.Tensor, fc2_scales: torch.Tensor):
+        for t in (fc1_codes, fc1_scales, fc2_codes, fc2_scales):
+            if not t.is_cuda or not t.is_contiguous():
+                raise ValueError("weights must be contiguous GPU tensors")
+        if fc1_codes.dtype != torch.uint8 or fc2_codes.dtype != torch.uint8:
+            raise ValueError("codes must be uint8")
+        if fc1_scales.dtype != torch.float16 or fc2_scales.dtype != torch.float16:
+            raise ValueError("scales must be float16")
+        if cfg.act_dtype not in _ACT:
+            raise ValueError("act_dtype must be torch.bfloat16 or torch.float32")
+        self.cfg = cfg
+        self.device = fc1_codes.device
+        self._keep = (fc1_codes, fc1_scales, fc2_codes, fc2_scales)
+        c = Config(ctypes.sizeof(Config), cfg.top_k, cfg.hidden, cfg.inter, cfg.num_experts,
+                   cfg.bits, cfg.block_size, cfg.zero_point, _ACT[cfg.act_dtype], 1, 0,
+                   cfg.max_tokens)
+        w = Weights(fc1_codes.data_ptr(), fc1_scales.data_ptr(), fc2_codes.data_ptr(),
+                    fc2_scales.data_ptr())
+        h = ctypes.c_void_p()
+        _check(lib().qmoe_create(ctypes.byref(c), ctypes.byref(w), self.device.index or 0,
+                                 ctypes.byref(h)), "qmoe_create")
+        self._h = h
+        self._ws: Optional[torch.Tensor] = None
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().qmoe_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def workspace_size(self, num_tokens: int) -> int:
+        n = ctypes.c_size_t()
+        _check(lib().qmoe_workspace_size(self._h, num_tokens, ctypes.byref(n)), "qmoe_workspace_size")
+        return n.value
+
+    def workspace(self, num_tokens: int) -> torch.Tensor:
+        need = self.workspace_size(num_tokens)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(max(need, 256), dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def _check_tokens(self, x: torch.Tensor, logits: torch.Tensor):
+        c = self.cfg
+        if x.dtype != c.act_dtype or logits.dtype != c.act_dtype:
+            raise ValueError("x and logits must have the layer's activation dtype")
+        if x.dim() != 2 or x.shape[1] != c.hidden or logits.shape != (x.shape[0], c.num_experts):
+            raise ValueError("expected x [T, hidden] and logits [T, num_experts]")
+        if x.device != self.device or logits.device != self.device:
+            raise ValueError("x and logits must be on the layer's device")
+        if not x.is_contiguous() or not logits.is_contiguous():
+            raise ValueError("x and logits must be contiguous")
+
+    def forward(self, x: torch.Tensor, logits: torch.Tensor, out: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+        self._check_tokens(x, logits)
+        T = x.shape[0]
+        if out is None:
+            out = torch.empty_like(x)
+        ws = workspace if workspace is not None else self.workspace(T)
+        _check(lib().qmoe_forward(self._h, _ptr(x), _ptr(logits), _ptr(out), T, _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream()), "qmoe_forward")
+        return out
+
+    __call__ = forward
+
+    def routing_from_workspace(self, num_tokens: int, workspace: torch.Tensor):
+        """(topk_id [T, k] int32, topk_w [T, k] fp32) left in `workspace` by forward()."""
+        a, b = ctypes.c_size_t(), ctypes.c_size_t()
+        _check(lib().qmoe_workspace_routing(self._h, num_tokens, ctypes.byref(a), ctypes.byref(b)),
+               "qmoe_workspace_routing")
+        R = num_tokens * self.cfg.top_k
+        ids = workspace[a.value:a.value + 4 * R].view(torch.int32).view(num_tokens, self.cfg.top_k)
+        w = workspace[b.value:b.value + 4 * R].view(torch.float32).view(num_tokens, self.cfg.top_k)
+        return ids, w
+
+    def route(self, logits: torch.Tensor):
+        """Routing stage only: (topk_id, topk_w, expert_offsets, sorted_routes, inv_pos)."""
+        c = self.cfg
+        T = logits.shape[0]
+        if logits.dtype != c.act_dtype or logits.shape != (T, c.num_experts) or not logits.is_contiguous():
+            raise ValueError("logits must be contiguous [T, num_experts] of the activation dtype")
+        R = T * c.top_k
+        dev = self.device
+        ids = torch.empty((T, c.top_k), dtype=torch.int32, device=dev)
+        w = torch.empty((T, c.top_k), dtype=torch.float32, device=dev)
+        offs = torch.empty(c.num_experts + 1, dtype=torch.int32, device=dev)
+        srt = torch.empty(R, dtype=torch.int32, device=dev)
+        inv = torch.empty(R, dtype=torch.int32, device=dev)
+        ws = self.workspace(T)
+        _check(lib().qmoe_route(self._h, _ptr(logits), T, _ptr(ids), _ptr(w), _ptr(offs), _ptr(srt),
+                                _ptr(inv), _ptr(ws), ws.numel(), _stream()), "qmoe_route")
+        return ids, w, offs, srt, inv
+
+    def dequant(self, fc: int, expert: int):
+        """(fp32 [N, K] as the decode path reads it, bf16 [N, K] as the prefill path stages it)."""
+        c = self.cfg
+        N, K = (2 * c.inter, c.hidden) if fc == 1 else (c.hidden, c.inter)
+        f = torch.empty((N, K), dtype=torch.float32, device=self.device)
+        b = torch.empty((N, K), dtype=torch.int16, device=self.device)
+        _check(lib().qmoe_dequant(self._h, fc, expert, _ptr(f), _ptr(b), _stream()), "qmoe_dequant")
+        return f, b.view(torch.bfloat16)

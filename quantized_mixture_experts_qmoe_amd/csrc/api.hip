@@ -1,0 +1,266 @@
+// C ABI of libqmoe: validation, workspace layout and dispatch.
+//
+// Validation happens once, on the host, before any device work: the pages
+// record admission paths that disagreed about a normalized field and a
+// division by zero on an expert count of zero, fixed by validating positive,
+// representable dimensions up front ("[CUDA] Add INT4 and INT3 QMoE CPU/GPU
+// offload support", review-fix commits: weights_prepacked=-1 normalization
+// and E=0 rejection). Environment overrides are read once, at create.
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+
+#include "device.h"
+#include "internal.h"
+
+struct qmoe_handle {
+  qmoe::Layer L;
+  int device;
+  bool force_prefill;
+};
+
+namespace qmoe {
+
+static int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+GemvShape gemv_shape(int64_t K, int min_rows_block) {
+  GemvShape s;
+  s.units = static_cast<int>(K / 32);
+  int p = 1;
+  while (p < s.units && p < 64) p <<= 1;
+  s.lpr = p;
+  int upl = (s.units + s.lpr - 1) / s.lpr;
+  s.upl = upl <= 1 ? 1 : upl <= 2 ? 2 : 4;
+  s.rows_wave = kWave / s.lpr;
+  int steps = (min_rows_block + 4 * s.rows_wave - 1) / (4 * s.rows_wave);
+  if (steps < 1) steps = 1;
+  s.rows_block = 4 * s.rows_wave * steps;
+  return s;
+}
+
+bool use_decode_path(const Layer& L, bool force_prefill, int64_t T) {
+  return !force_prefill && T >= 1 && T <= 4;
+}
+
+static Workspace layout(const Layer& L, int64_t T, bool decode) {
+  Workspace W;
+  memset(&W, 0, sizeof W);
+  const int64_t R = T * L.k;
+  W.R = R;
+  W.decode = decode;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = static_cast<size_t>(round_up(static_cast<int64_t>(off + bytes), 256));
+    return at;
+  };
+  W.topk_id = take(R * 4);
+  W.topk_w = take(R * 4);
+  if (decode) {
+    const GemvShape s2 = gemv_shape(L.I, 64);
+    W.n_counters = static_cast<int>((L.H + s2.rows_block - 1) / s2.rows_block);
+    W.counters = take(static_cast<size_t>(W.n_counters) * 4);
+    W.h32 = take(static_cast<size_t>(R * L.I * 4));
+    W.y32 = take(static_cast<size_t>(R * L.H * 4));
+  } else {
+    W.nchunks = (R + kRouteChunk - 1) / kRouteChunk;
+    W.max_tiles = (R + kTileM - 1) / kTileM + L.E;
+    W.hist = take(static_cast<size_t>(W.nchunks * L.E * 4));
+    W.chunk_base = take(static_cast<size_t>(W.nchunks * L.E * 4));
+    W.counts = take(static_cast<size_t>(L.E * 4));
+    W.offsets = take(static_cast<size_t>((L.E + 1) * 4));
+    W.sorted_routes = take(static_cast<size_t>(R * 4));
+    W.inv_pos = take(static_cast<size_t>(R * 4));
+    W.tiles = take(static_cast<size_t>(W.max_tiles * 16));
+    W.num_tiles = take(4);
+    W.xbf16 = L.act_bf16 ? 0 : take(static_cast<size_t>(T * L.H * 2));
+    W.hbf16 = take(static_cast<size_t>(R * L.I * 2));
+    W.yf32 = take(static_cast<size_t>(R * L.H * 4));
+  }
+  W.total = off;
+  return W;
+}
+
+}  // namespace qmoe
+
+using namespace qmoe;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+class DeviceGuard {
+ public:
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev_) != hipSuccess) prev_ = -1;
+    ok_ = true;
+    if (prev_ != dev) ok_ = hipSetDevice(dev) == hipSuccess;
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev_ >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev_) (void)hipSetDevice(prev_);
+  }
+  bool ok() const { return ok_; }
+
+ private:
+  int prev_ = -1;
+  bool ok_ = false;
+};
+
+size_t required_bytes(const qmoe_handle* h, int64_t T) {
+  if (use_decode_path(h->L, h->force_prefill, T)) {
+    const size_t d = layout(h->L, T, true).total;
+    const size_t p = layout(h->L, T, false).total;   // qmoe_route needs the routing layout
+    return d > p ? d : p;
+  }
+  return layout(h->L, T, false).total;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qmoe_status_string(qmoe_status st) {
+  switch (st) {
+    case QMOE_OK: return "ok";
+    case QMOE_ERR_INVALID_ARG: return "invalid argument";
+    case QMOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case QMOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case QMOE_ERR_HIP: return "HIP runtime error";
+    case QMOE_ERR_OOM: return "out of host memory";
+  }
+  return "unknown status";
+}
+
+qmoe_status qmoe_create(const qmoe_config* c, const qmoe_weights* w, int device, qmoe_handle** out) {
+  if (!out) return QMOE_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (!c || !w) return QMOE_ERR_INVALID_ARG;
+  if (c->struct_size != sizeof(qmoe_config)) return QMOE_ERR_INVALID_ARG;
+  if (c->hidden <= 0 || c->inter <= 0 || c->num_experts <= 0) return QMOE_ERR_INVALID_ARG;
+  if (c->top_k < 1 || c->top_k > c->num_experts) return QMOE_ERR_INVALID_ARG;
+  if (c->bits != 2 && c->bits != 3 && c->bits != 4) return QMOE_ERR_INVALID_ARG;
+  if (c->block_size != 32 && c->block_size != 64 && c->block_size != 128) return QMOE_ERR_INVALID_ARG;
+  if (c->hidden % c->block_size != 0 || c->inter % c->block_size != 0) return QMOE_ERR_INVALID_ARG;
+  if (c->zero_point < -1 || c->zero_point >= (1 << c->bits)) return QMOE_ERR_INVALID_ARG;
+  if (c->act_dtype != QMOE_F32 && c->act_dtype != QMOE_BF16) return QMOE_ERR_INVALID_ARG;
+  if (c->reserved != 0 || c->max_tokens < 0) return QMOE_ERR_INVALID_ARG;
+  if (c->normalize_routing != 0 && c->normalize_routing != 1) return QMOE_ERR_INVALID_ARG;
+  if (c->normalize_routing == 0) return QMOE_ERR_UNSUPPORTED;
+  if (!w->fc1_codes || !w->fc1_scales || !w->fc2_codes || !w->fc2_scales) return QMOE_ERR_INVALID_ARG;
+  if (!aligned16(w->fc1_codes) || !aligned16(w->fc1_scales) || !aligned16(w->fc2_codes) ||
+      !aligned16(w->fc2_scales))
+    return QMOE_ERR_INVALID_ARG;
+  // limits of this implementation
+  if (c->num_experts > kMaxExperts || c->top_k > kMaxTopK) return QMOE_ERR_UNSUPPORTED;
+  if (c->hidden > 8192 || c->inter > 8192) return QMOE_ERR_UNSUPPORTED;
+  if (c->max_tokens > (int64_t{1} << 31) / (c->top_k * int64_t{kTileN})) return QMOE_ERR_UNSUPPORTED;
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess) return QMOE_ERR_HIP;
+  if (device < 0 || device >= ndev) return QMOE_ERR_INVALID_ARG;
+
+  qmoe_handle* h = new (std::nothrow) qmoe_handle;
+  if (!h) return QMOE_ERR_OOM;
+  Layer& L = h->L;
+  L.H = c->hidden;
+  L.I = c->inter;
+  L.E = c->num_experts;
+  L.k = c->top_k;
+  L.bits = c->bits;
+  L.bs = c->block_size;
+  L.zp = c->zero_point < 0 ? (1 << (c->bits - 1)) : c->zero_point;
+  L.act_bf16 = c->act_dtype == QMOE_BF16;
+  L.max_tokens = c->max_tokens;
+  L.fc1_codes = static_cast<const uint8_t*>(w->fc1_codes);
+  L.fc1_scales = static_cast<const uint16_t*>(w->fc1_scales);
+  L.fc2_codes = static_cast<const uint8_t*>(w->fc2_codes);
+  L.fc2_scales = static_cast<const uint16_t*>(w->fc2_scales);
+  L.fc1_row_bytes = L.H * L.bits / 8;
+  L.fc2_row_bytes = L.I * L.bits / 8;
+  L.fc1_nblk = L.H / L.bs;
+  L.fc2_nblk = L.I / L.bs;
+  h->device = device;
+  const char* force = getenv("QMOE_FORCE_PATH");
+  h->force_prefill = force && strcmp(force, "prefill") == 0;
+  *out = h;
+  return QMOE_OK;
+}
+
+qmoe_status qmoe_workspace_size(const qmoe_handle* h, int64_t T, size_t* bytes) {
+  if (!h || !bytes || T < 0 || T > h->L.max_tokens) return QMOE_ERR_INVALID_ARG;
+  *bytes = required_bytes(h, T);
+  return QMOE_OK;
+}
+
+qmoe_status qmoe_workspace_routing(const qmoe_handle* h, int64_t T, size_t* id_off, size_t* w_off) {
+  if (!h || !id_off || !w_off || T < 0 || T > h->L.max_tokens) return QMOE_ERR_INVALID_ARG;
+  const Workspace W = layout(h->L, T, use_decode_path(h->L, h->force_prefill, T));
+  *id_off = W.topk_id;
+  *w_off = W.topk_w;
+  return QMOE_OK;
+}
+
+qmoe_status qmoe_forward(qmoe_handle* h, const void* x, const void* logits, void* out, int64_t T,
+                         void* ws, size_t ws_bytes, void* stream) {
+  if (!h || T < 0 || T > h->L.max_tokens) return QMOE_ERR_INVALID_ARG;
+  if (T == 0) return QMOE_OK;
+  if (!x || !logits || !out || !aligned16(x) || !aligned16(logits) || !aligned16(out))
+    return QMOE_ERR_INVALID_ARG;
+  if (!ws || !aligned16(ws) || ws_bytes < required_bytes(h, T)) return QMOE_ERR_WORKSPACE;
+  DeviceGuard guard(h->device);
+  if (!guard.ok()) return QMOE_ERR_HIP;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  hipError_t err;
+  if (use_decode_path(h->L, h->force_prefill, T)) {
+    const Workspace W = layout(h->L, T, true);
+    err = launch_decode(h->L, x, logits, out, T, base, W, s);
+  } else {
+    const Workspace W = layout(h->L, T, false);
+    err = launch_route(h->L, logits, T, base, W, s);
+    if (err == hipSuccess) err = launch_prefill(h->L, x, out, T, base, W, s);
+  }
+  return err == hipSuccess ? QMOE_OK : QMOE_ERR_HIP;
+}
+
+qmoe_status qmoe_route(qmoe_handle* h, const void* logits, int64_t T, int32_t* topk_id, float* topk_w,
+                       int32_t* expert_offsets, int32_t* sorted_routes, int32_t* inv_pos, void* ws,
+                       size_t ws_bytes, void* stream) {
+  if (!h || T < 1 || T > h->L.max_tokens) return QMOE_ERR_INVALID_ARG;
+  if (!logits || !aligned16(logits)) return QMOE_ERR_INVALID_ARG;
+  const Workspace W = layout(h->L, T, false);
+  if (!ws || !aligned16(ws) || ws_bytes < W.total) return QMOE_ERR_WORKSPACE;
+  DeviceGuard guard(h->device);
+  if (!guard.ok()) return QMOE_ERR_HIP;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  hipError_t err = launch_route(h->L, logits, T, base, W, s);
+  const size_t R = static_cast<size_t>(W.R);
+  auto copy = [&](void* dst, size_t off, size_t bytes) {
+    if (dst && err == hipSuccess) err = hipMemcpyAsync(dst, base + off, bytes, hipMemcpyDeviceToDevice, s);
+  };
+  copy(topk_id, W.topk_id, R * 4);
+  copy(topk_w, W.topk_w, R * 4);
+  copy(expert_offsets, W.offsets, static_cast<size_t>(h->L.E + 1) * 4);
+  copy(sorted_routes, W.sorted_routes, R * 4);
+  copy(inv_pos, W.inv_pos, R * 4);
+  return err == hipSuccess ? QMOE_OK : QMOE_ERR_HIP;
+}
+
+qmoe_status qmoe_dequant(qmoe_handle* h, int fc, int64_t expert, float* out_f32, uint16_t* out_bf16,
+                         void* stream) {
+  if (!h || (fc != 1 && fc != 2) || expert < 0 || expert >= h->L.E) return QMOE_ERR_INVALID_ARG;
+  if (!out_f32 && !out_bf16) return QMOE_OK;
+  DeviceGuard guard(h->device);
+  if (!guard.ok()) return QMOE_ERR_HIP;
+  hipError_t err = launch_dequant(h->L, fc, expert, out_f32, out_bf16, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? QMOE_OK : QMOE_ERR_HIP;
+}
+
+qmoe_status qmoe_destroy(qmoe_handle* h) {
+  delete h;
+  return QMOE_OK;
+}
+
+}  // extern "C"

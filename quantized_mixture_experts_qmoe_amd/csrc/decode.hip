@@ -1,0 +1,433 @@
+// Decode path (1..4 tokens): memory-bound dequant-GEMVs.
+//
+// Every active expert's weights are streamed from HBM once and applied to
+// all (at most four) tokens that selected it. Two launches:
+//   1. decode_fc1: each workgroup recomputes the top-k routing of the <= 4
+//      tokens in its prologue (a few hundred logits), owns one (expert, block
+//      of gate rows) pair, and writes h = silu(gate) * up in fp32 per route;
+//   2. decode_fc2: each workgroup owns one (expert, block of output rows)
+//      pair and writes the per-route fp32 FC2 rows; the last workgroup to
+//      finish a block of output rows combines the k slots of every token in
+//      slot order and rounds once.
+//
+// Semantics: SwiGLU experts with fc1 rows = 2 * inter ("[CUDA/CPU] Add AVX2
+// INT4 cold-expert kernel and zero-cold doorbell short-circuit for QMoE
+// offload", Motivation & Summary item 3); fp32 partial sums rounded once by
+// the combine ("[CUDA] Add MoEPacked CPU/GPU hybrid offload and consolidate
+// QMoE/GGUF offload optimizations", Key Changes item 4).
+//
+// Arithmetic: codes are turned into bf16 pairs 1 + q/128 (exact) and dotted
+// with bf16 activations by v_dot2_f32_bf16 into an fp32 accumulator that
+// starts at -(1 + zp/128) * sum(x); the block result is then
+// sum((q - zp) * x) / 128, scaled by 128 * s. fp32 activations (and the fp32
+// FC2 input h) use plain fp32 FMAs on the integer codes instead.
+#include "device.h"
+#include "internal.h"
+
+namespace qmoe {
+
+namespace {
+
+template <int BITS, int UPL>
+struct XPairs {
+  uint32_t p[UPL][16];
+  float corr[UPL];
+};
+
+template <int UPL>
+struct XFloats {
+  float v[UPL][32];
+  float sum[UPL];
+};
+
+// Activation unit (32 bf16 values at x) -> pairs matching unit_pair<BITS>.
+template <int BITS>
+__device__ __forceinline__ void load_x_pairs(const uint16_t* x, int zp, uint32_t (&pairs)[16],
+                                             float& corr) {
+  uint32_t v[16];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint4 c = reinterpret_cast<const uint4*>(x)[q];
+    v[4 * q + 0] = c.x; v[4 * q + 1] = c.y; v[4 * q + 2] = c.z; v[4 * q + 3] = c.w;
+  }
+  float sum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) sum += bf16_to_f32((v[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+#pragma unroll
+  for (int p = 0; p < 16; ++p) {
+    const int a = pair_a(BITS, p), b = pair_b(BITS, p);
+    const uint32_t xa = (v[a >> 1] >> (16 * (a & 1))) & 0xFFFFu;
+    const uint32_t xb = (v[b >> 1] >> (16 * (b & 1))) & 0xFFFFu;
+    pairs[p] = xa | (xb << 16);
+  }
+  corr = -(1.0f + static_cast<float>(zp) * (1.0f / 128.0f)) * sum;
+}
+
+// sum((q - zp) * x) / 128 over one unit, bf16 activations.
+template <int BITS>
+__device__ __forceinline__ float unit_dot_pairs(const uint32_t (&wp)[16], const uint32_t (&xp)[16],
+                                                float corr) {
+  float acc = corr;
+#pragma unroll
+  for (int p = 0; p < 16; ++p) acc = dot2_bf16(wp[p], xp[p], acc);
+  return acc;
+}
+
+// sum(q * v) over one unit, fp32 values (natural code order).
+template <int BITS>
+__device__ __forceinline__ float unit_dot_f32(const UnitWords<BITS>& u, const float (&v)[32]) {
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) acc = fmaf(static_cast<float>(unit_code<BITS>(u, i)), v[i], acc);
+  return acc;
+}
+
+struct RoutingLds {
+  int32_t ids[kDecodeMaxTokens * kMaxTopK];
+  float w[kDecodeMaxTokens * kMaxTopK];
+};
+
+// slot[t] = the slot of expert e in token t's selection, or -1.
+__device__ __forceinline__ void token_slots(const RoutingLds& R, int T, int k, int e,
+                                            int (&slot)[kDecodeMaxTokens]) {
+#pragma unroll
+  for (int t = 0; t < kDecodeMaxTokens; ++t) {
+    slot[t] = -1;
+    if (t < T)
+      for (int j = 0; j < k; ++j)
+        if (R.ids[t * k + j] == e) slot[t] = j;
+  }
+}
+
+}  // namespace
+
+// grid = (ceil(I / rows_block), T * k), block = 256 (4 waves)
+template <int BITS, int UPL, bool BF16>
+__global__ __launch_bounds__(256) void decode_fc1_kernel(
+    const void* __restrict__ xv, const void* __restrict__ logitsv, int T, int E, int k,
+    const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales, int H, int I, int bs,
+    int zp, int64_t row_bytes, int64_t nblk, int lpr, int rows_block,
+    int32_t* __restrict__ ws_ids, float* __restrict__ ws_w, float* __restrict__ h32,
+    int32_t* __restrict__ counters, int n_counters) {
+  __shared__ RoutingLds R;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  if (wave < T) {
+    if constexpr (BF16)
+      topk_softmax_wave(static_cast<const uint16_t*>(logitsv) + static_cast<int64_t>(wave) * E, E, k,
+                        lane, R.ids + wave * k, R.w + wave * k);
+    else
+      topk_softmax_wave(static_cast<const float*>(logitsv) + static_cast<int64_t>(wave) * E, E, k,
+                        lane, R.ids + wave * k, R.w + wave * k);
+  }
+  __syncthreads();
+  const int nroutes = T * k;
+  if (blockIdx.x == 0 && blockIdx.y == 0) {
+    for (int i = threadIdx.x; i < nroutes; i += 256) {
+      ws_ids[i] = R.ids[i];
+      ws_w[i] = R.w[i];
+    }
+    for (int i = threadIdx.x; i < n_counters; i += 256) counters[i] = 0;
+  }
+  const int r = blockIdx.y;
+  const int e = R.ids[r];
+  for (int q = 0; q < r; ++q)
+    if (R.ids[q] == e) return;  // the first slot that chose e owns it
+  int slot[kDecodeMaxTokens];
+  token_slots(R, T, k, e, slot);
+
+  const int units = H / 32;
+  const int row_in_wave = lane / lpr, lane_in_row = lane % lpr;
+  const int rows_wave = kWave / lpr;
+  const uint8_t* ebase = codes + static_cast<int64_t>(e) * (2 * I) * row_bytes;
+  const uint16_t* sbase = scales + static_cast<int64_t>(e) * (2 * I) * nblk;
+
+  // activations of the tokens that use e, for this lane's units
+  XPairs<BITS, UPL> xp[kDecodeMaxTokens];
+  XFloats<UPL> xf[kDecodeMaxTokens];
+#pragma unroll
+  for (int t = 0; t < kDecodeMaxTokens; ++t) {
+    if (slot[t] < 0) continue;
+#pragma unroll
+    for (int i = 0; i < UPL; ++i) {
+      const int u = lane_in_row + lpr * i;
+      if (u >= units) continue;
+      if constexpr (BF16) {
+        load_x_pairs<BITS>(static_cast<const uint16_t*>(xv) + static_cast<int64_t>(t) * H + 32 * u, zp,
+                           xp[t].p[i], xp[t].corr[i]);
+      } else {
+        const float* xs = static_cast<const float*>(xv) + static_cast<int64_t>(t) * H + 32 * u;
+        float s = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 32; ++c) {
+          xf[t].v[i][c] = xs[c];
+          s += xs[c];
+        }
+        xf[t].sum[i] = s;
+      }
+    }
+  }
+
+  const int rows_per_wave = rows_block / 4;
+  const int nsteps = rows_per_wave / rows_wave;
+  const int n_wave0 = blockIdx.x * rows_block + wave * rows_per_wave + row_in_wave;
+  for (int step = 0; step < nsteps; ++step) {
+    const int n = n_wave0 + step * rows_wave;
+    const bool valid = n < I;
+    float g[kDecodeMaxTokens], up[kDecodeMaxTokens];
+#pragma unroll
+    for (int t = 0; t < kDecodeMaxTokens; ++t) g[t] = up[t] = 0.0f;
+    if (valid) {
+      UnitWords<BITS> gw[UPL], uw[UPL];
+      float gs[UPL], us[UPL];
+#pragma unroll
+      for (int i = 0; i < UPL; ++i) {
+        const int u = lane_in_row + lpr * i;
+        if (u >= units) continue;
+        gw[i] = load_unit<BITS>(ebase + static_cast<int64_t>(n) * row_bytes + u * (4 * BITS));
+        uw[i] = load_unit<BITS>(ebase + static_cast<int64_t>(I + n) * row_bytes + u * (4 * BITS));
+        gs[i] = half_to_f32(sbase[static_cast<int64_t>(n) * nblk + (32 * u) / bs]);
+        us[i] = half_to_f32(sbase[static_cast<int64_t>(I + n) * nblk + (32 * u) / bs]);
+      }
+#pragma unroll
+      for (int i = 0; i < UPL; ++i) {
+        const int u = lane_in_row + lpr * i;
+        if (u >= units) continue;
+        if constexpr (BF16) {
+          uint32_t gp[16], upp[16];
+#pragma unroll
+          for (int p = 0; p < 16; ++p) {
+            gp[p] = unit_pair<BITS>(gw[i], p);
+            upp[p] = unit_pair<BITS>(uw[i], p);
+          }
+          const float gsc = 128.0f * gs[i], usc = 128.0f * us[i];
+#pragma unroll
+          for (int t = 0; t < kDecodeMaxTokens; ++t) {
+            if (slot[t] < 0) continue;
+            g[t] = fmaf(gsc, unit_dot_pairs<BITS>(gp, xp[t].p[i], xp[t].corr[i]), g[t]);
+            up[t] = fmaf(usc, unit_dot_pairs<BITS>(upp, xp[t].p[i], xp[t].corr[i]), up[t]);
+          }
+        } else {
+#pragma unroll
+          for (int t = 0; t < kDecodeMaxTokens; ++t) {
+            if (slot[t] < 0) continue;
+            const float zs = static_cast<float>(zp) * xf[t].sum[i];
+            g[t] = fmaf(gs[i], unit_dot_f32<BITS>(gw[i], xf[t].v[i]) - zs, g[t]);
+            up[t] = fmaf(us[i], unit_dot_f32<BITS>(uw[i], xf[t].v[i]) - zs, up[t]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < kDecodeMaxTokens; ++t) {
+      if (slot[t] < 0) continue;
+      const float gt = group_sum(g[t], lpr);
+      const float ut = group_sum(up[t], lpr);
+      if (valid && lane_in_row == 0)
+        h32[static_cast<int64_t>(t * k + slot[t]) * I + n] = silu_mul(gt, ut);
+    }
+  }
+}
+
+// grid = (n_counters = ceil(H / rows_block), T * k), block = 256
+template <int BITS, int UPL, bool OUT_BF16>
+__global__ __launch_bounds__(256) void decode_fc2_kernel(
+    const float* __restrict__ h32, const int32_t* __restrict__ ws_ids,
+    const float* __restrict__ ws_w, int T, int k, const uint8_t* __restrict__ codes,
+    const uint16_t* __restrict__ scales, int H, int I, int bs, int zp, int64_t row_bytes,
+    int64_t nblk, int lpr, int rows_block, float* __restrict__ y32,
+    int32_t* __restrict__ counters, void* __restrict__ out) {
+  __shared__ RoutingLds R;
+  __shared__ int s_last;
+  const int nroutes = T * k;
+  for (int i = threadIdx.x; i < nroutes; i += 256) {
+    R.ids[i] = ws_ids[i];
+    R.w[i] = ws_w[i];
+  }
+  __syncthreads();
+  // number of distinct experts = number of workgroups per row block that work
+  bool first = false;
+  if (static_cast<int>(threadIdx.x) < nroutes) {
+    first = true;
+    for (int q = 0; q < static_cast<int>(threadIdx.x); ++q)
+      if (R.ids[q] == R.ids[threadIdx.x]) first = false;
+  }
+  const int n_distinct = __syncthreads_count(first);
+
+  const int r = blockIdx.y;
+  const int e = R.ids[r];
+  for (int q = 0; q < r; ++q)
+    if (R.ids[q] == e) return;
+  int slot[kDecodeMaxTokens];
+  token_slots(R, T, k, e, slot);
+
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  const int units = I / 32;
+  const int row_in_wave = lane / lpr, lane_in_row = lane % lpr;
+  const int rows_wave = kWave / lpr;
+  const uint8_t* ebase = codes + static_cast<int64_t>(e) * H * row_bytes;
+  const uint16_t* sbase = scales + static_cast<int64_t>(e) * H * nblk;
+
+  XFloats<UPL> hf[kDecodeMaxTokens];
+#pragma unroll
+  for (int t = 0; t < kDecodeMaxTokens; ++t) {
+    if (slot[t] < 0) continue;
+#pragma unroll
+    for (int i = 0; i < UPL; ++i) {
+      const int u = lane_in_row + lpr * i;
+      if (u >= units) continue;
+      const float4* src =
+          reinterpret_cast<const float4*>(h32 + static_cast<int64_t>(t * k + slot[t]) * I + 32 * u);
+      float s = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        float4 v = src[q];
+        hf[t].v[i][4 * q + 0] = v.x; hf[t].v[i][4 * q + 1] = v.y;
+        hf[t].v[i][4 * q + 2] = v.z; hf[t].v[i][4 * q + 3] = v.w;
+        s += (v.x + v.y) + (v.z + v.w);
+      }
+      hf[t].sum[i] = s;
+    }
+  }
+
+  const int rows_per_wave = rows_block / 4;
+  const int nsteps = rows_per_wave / rows_wave;
+  const int m0 = blockIdx.x * rows_block;
+  const int m_wave0 = m0 + wave * rows_per_wave + row_in_wave;
+  for (int step = 0; step < nsteps; ++step) {
+    const int m = m_wave0 + step * rows_wave;
+    const bool valid = m < H;
+    float y[kDecodeMaxTokens];
+#pragma unroll
+    for (int t = 0; t < kDecodeMaxTokens; ++t) y[t] = 0.0f;
+    if (valid) {
+      UnitWords<BITS> w[UPL];
+      float sc[UPL];
+#pragma unroll
+      for (int i = 0; i < UPL; ++i) {
+        const int u = lane_in_row + lpr * i;
+        if (u >= units) continue;
+        w[i] = load_unit<BITS>(ebase + static_cast<int64_t>(m) * row_bytes + u * (4 * BITS));
+        sc[i] = half_to_f32(sbase[static_cast<int64_t>(m) * nblk + (32 * u) / bs]);
+      }
+#pragma unroll
+      for (int i = 0; i < UPL; ++i) {
+        const int u = lane_in_row + lpr * i;
+        if (u >= units) continue;
+#pragma unroll
+        for (int t = 0; t < kDecodeMaxTokens; ++t) {
+          if (slot[t] < 0) continue;
+          const float d = unit_dot_f32<BITS>(w[i], hf[t].v[i]) - static_cast<float>(zp) * hf[t].sum[i];
+          y[t] = fmaf(sc[i], d, y[t]);
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < kDecodeMaxTokens; ++t) {
+      if (slot[t] < 0) continue;
+      const float yt = group_sum(y[t], lpr);
+      if (valid && lane_in_row == 0) y32[static_cast<int64_t>(t * k + slot[t]) * H + m] = yt;
+    }
+  }
+
+  // publish, then let the last workgroup of this row block combine
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int old = atomicAdd(&counters[blockIdx.x], 1);
+    s_last = (old == n_distinct - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  for (int idx = threadIdx.x; idx < T * rows_block; idx += 256) {
+    const int t = idx / rows_block;
+    const int mm = m0 + idx % rows_block;
+    if (mm >= H) continue;
+    float acc = 0.0f;
+    for (int j = 0; j < k; ++j)
+      acc = fmaf(R.w[t * k + j], __builtin_nontemporal_load(y32 + static_cast<int64_t>(t * k + j) * H + mm), acc);
+    if constexpr (OUT_BF16)
+      static_cast<uint16_t*>(out)[static_cast<int64_t>(t) * H + mm] = static_cast<uint16_t>(f32_to_bf16(acc));
+    else
+      static_cast<float*>(out)[static_cast<int64_t>(t) * H + mm] = acc;
+  }
+}
+
+namespace {
+
+template <int BITS, int UPL>
+hipError_t launch_decode_t(const Layer& L, const void* x, const void* logits, void* out, int64_t T,
+                           char* ws, const Workspace& W, hipStream_t s, const GemvShape& s1,
+                           const GemvShape& s2) {
+  const int Ti = static_cast<int>(T), k = L.k, E = static_cast<int>(L.E);
+  const int H = static_cast<int>(L.H), I = static_cast<int>(L.I);
+  int32_t* ids = reinterpret_cast<int32_t*>(ws + W.topk_id);
+  float* w = reinterpret_cast<float*>(ws + W.topk_w);
+  int32_t* counters = reinterpret_cast<int32_t*>(ws + W.counters);
+  float* h32 = reinterpret_cast<float*>(ws + W.h32);
+  float* y32 = reinterpret_cast<float*>(ws + W.y32);
+  dim3 g1((I + s1.rows_block - 1) / s1.rows_block, Ti * k);
+  if (L.act_bf16)
+    decode_fc1_kernel<BITS, UPL, true><<<g1, 256, 0, s>>>(
+        x, logits, Ti, E, k, L.fc1_codes, L.fc1_scales, H, I, L.bs, L.zp, L.fc1_row_bytes,
+        L.fc1_nblk, s1.lpr, s1.rows_block, ids, w, h32, counters, W.n_counters);
+  else
+    decode_fc1_kernel<BITS, UPL, false><<<g1, 256, 0, s>>>(
+        x, logits, Ti, E, k, L.fc1_codes, L.fc1_scales, H, I, L.bs, L.zp, L.fc1_row_bytes,
+        L.fc1_nblk, s1.lpr, s1.rows_block, ids, w, h32, counters, W.n_counters);
+  return hipGetLastError();
+}
+
+template <int BITS, int UPL>
+hipError_t launch_fc2_t(const Layer& L, void* out, int64_t T, char* ws, const Workspace& W,
+                        hipStream_t s, const GemvShape& s2) {
+  const int Ti = static_cast<int>(T), k = L.k;
+  const int H = static_cast<int>(L.H), I = static_cast<int>(L.I);
+  const int32_t* ids = reinterpret_cast<const int32_t*>(ws + W.topk_id);
+  const float* w = reinterpret_cast<const float*>(ws + W.topk_w);
+  int32_t* counters = reinterpret_cast<int32_t*>(ws + W.counters);
+  const float* h32 = reinterpret_cast<const float*>(ws + W.h32);
+  float* y32 = reinterpret_cast<float*>(ws + W.y32);
+  dim3 g2(W.n_counters, Ti * k);
+  if (L.act_bf16)
+    decode_fc2_kernel<BITS, UPL, true><<<g2, 256, 0, s>>>(
+        h32, ids, w, Ti, k, L.fc2_codes, L.fc2_scales, H, I, L.bs, L.zp, L.fc2_row_bytes,
+        L.fc2_nblk, s2.lpr, s2.rows_block, y32, counters, out);
+  else
+    decode_fc2_kernel<BITS, UPL, false><<<g2, 256, 0, s>>>(
+        h32, ids, w, Ti, k, L.fc2_codes, L.fc2_scales, H, I, L.bs, L.zp, L.fc2_row_bytes,
+        L.fc2_nblk, s2.lpr, s2.rows_block, y32, counters, out);
+  return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t launch_decode_bits(const Layer& L, const void* x, const void* logits, void* out,
+                              int64_t T, char* ws, const Workspace& W, hipStream_t s) {
+  const GemvShape s1 = gemv_shape(L.H, 16);
+  const GemvShape s2 = gemv_shape(L.I, 64);
+  hipError_t err;
+  switch (s1.upl) {
+    case 1: err = launch_decode_t<BITS, 1>(L, x, logits, out, T, ws, W, s, s1, s2); break;
+    case 2: err = launch_decode_t<BITS, 2>(L, x, logits, out, T, ws, W, s, s1, s2); break;
+    default: err = launch_decode_t<BITS, 4>(L, x, logits, out, T, ws, W, s, s1, s2); break;
+  }
+  if (err != hipSuccess) return err;
+  switch (s2.upl) {
+    case 1: return launch_fc2_t<BITS, 1>(L, out, T, ws, W, s, s2);
+    case 2: return launch_fc2_t<BITS, 2>(L, out, T, ws, W, s, s2);
+    default: return launch_fc2_t<BITS, 4>(L, out, T, ws, W, s, s2);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode(const Layer& L, const void* x, const void* logits, void* out, int64_t T,
+                         char* ws, const Workspace& W, hipStream_t s) {
+  switch (L.bits) {
+    case 4: return launch_decode_bits<4>(L, x, logits, out, T, ws, W, s);
+    case 3: return launch_decode_bits<3>(L, x, logits, out, T, ws, W, s);
+    default: return launch_decode_bits<2>(L, x, logits, out, T, ws, W, s);
+  }
+}
+
+}  // namespace qmoe

@@ -1,0 +1,197 @@
+// Device helpers for the gfx950 QMoE kernels: number formats, packed-code
+// unpacking and wavefront reductions. Wave64 throughout.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmoe {
+
+constexpr int kWave = 64;
+constexpr int kMaxTopK = 32;       // routing slots per token
+constexpr int kMaxExperts = 1024;  // 16 logits per lane in the top-k wave
+constexpr int kDecodeMaxTokens = 4;
+
+// ---------------------------------------------------------------- formats
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays NaN (quiet bit set).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ float half_to_f32(uint16_t h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+
+__device__ __forceinline__ float act_to_f32(float v) { return v; }
+__device__ __forceinline__ float act_to_f32(uint16_t b) { return bf16_to_f32(b); }
+
+// ---------------------------------------------------------------- packed codes
+//
+// A "unit" is 32 consecutive codes of one row. Every supported block size is
+// a multiple of 32, so a unit never straddles a scale block, and a unit is
+// exactly BITS dwords: INT4 16 B, INT3 12 B, INT2 8 B.
+
+template <int BITS>
+struct UnitWords {
+  uint32_t w[BITS];
+};
+
+template <int BITS>
+__device__ __forceinline__ UnitWords<BITS> load_unit(const uint8_t* p) {
+  UnitWords<BITS> u;
+  if constexpr (BITS == 4) {
+    uint4 v = *reinterpret_cast<const uint4*>(p);
+    u.w[0] = v.x; u.w[1] = v.y; u.w[2] = v.z; u.w[3] = v.w;
+  } else if constexpr (BITS == 2) {
+    uint2 v = *reinterpret_cast<const uint2*>(p);
+    u.w[0] = v.x; u.w[1] = v.y;
+  } else {
+    const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+    u.w[0] = q[0]; u.w[1] = q[1]; u.w[2] = q[2];
+  }
+  return u;
+}
+
+// Code i (0..31) of a unit, natural order. The packed stream is little-endian:
+// code i occupies bits [BITS*i, BITS*i + BITS) of the unit's 32*BITS bits.
+template <int BITS>
+__device__ __forceinline__ uint32_t unit_code(const UnitWords<BITS>& u, int i) {
+  const int bit = BITS * i;
+  const int d = bit >> 5, o = bit & 31;
+  constexpr uint32_t mask = (1u << BITS) - 1u;
+  if (o + BITS <= 32) return (u.w[d] >> o) & mask;
+  return ((u.w[d] >> o) | (u.w[d + 1] << (32 - o))) & mask;
+}
+
+// Pair p (0..15) of a unit, as two bf16 values 1 + q_a/128 (low half) and
+// 1 + q_b/128 (high half): the code is OR-ed into the low mantissa bits of
+// bf16 1.0 (0x3F80), which is exact for q < 128. pair_a/pair_b name the code
+// indices so the activations can be paired the same way. INT4 and INT2 pair
+// codes 16 bits apart so one shift and one AND-OR make a pair.
+__host__ __device__ constexpr int pair_a(int bits, int p) {
+  return bits == 4 ? 8 * (p / 4) + (p % 4) : bits == 2 ? 16 * (p / 8) + (p % 8) : 2 * p;
+}
+__host__ __device__ constexpr int pair_b(int bits, int p) {
+  return bits == 4 ? 8 * (p / 4) + (p % 4) + 4 : bits == 2 ? 16 * (p / 8) + (p % 8) + 8 : 2 * p + 1;
+}
+
+template <int BITS>
+__device__ __forceinline__ uint32_t unit_pair(const UnitWords<BITS>& u, int p) {
+  if constexpr (BITS == 4) {
+    return ((u.w[p >> 2] >> (4 * (p & 3))) & 0x000F000Fu) | 0x3F803F80u;
+  } else if constexpr (BITS == 2) {
+    return ((u.w[p >> 3] >> (2 * (p & 7))) & 0x00030003u) | 0x3F803F80u;
+  } else {
+    return unit_code<3>(u, 2 * p) | (unit_code<3>(u, 2 * p + 1) << 16) | 0x3F803F80u;
+  }
+}
+
+// The matrix-core operand value of code i: (q - zp) * s computed exactly in
+// fp32 (at most 11 + 3 significant bits) and rounded once to bf16. Writes the
+// unit's 32 values as 16 bf16 pairs in natural order (pair p = codes 2p, 2p+1).
+template <int BITS>
+__device__ __forceinline__ void dequant_unit_bf16(const UnitWords<BITS>& u, float s, int zp,
+                                                  uint32_t (&out)[16]) {
+#pragma unroll
+  for (int p = 0; p < 16; ++p) {
+    const float lo = static_cast<float>(static_cast<int>(unit_code<BITS>(u, 2 * p)) - zp) * s;
+    const float hi = static_cast<float>(static_cast<int>(unit_code<BITS>(u, 2 * p + 1)) - zp) * s;
+    out[p] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+  }
+}
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+// acc + a.lo*b.lo + a.hi*b.hi with bf16 inputs and fp32 accumulation.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), acc, false);
+}
+
+// ---------------------------------------------------------------- reductions
+
+__device__ __forceinline__ float group_sum(float v, int width) {
+  for (int off = width >> 1; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) { return group_sum(v, kWave); }
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int off) {
+  uint32_t lo = static_cast<uint32_t>(v), hi = static_cast<uint32_t>(v >> 32);
+  lo = __shfl_xor(lo, off, kWave);
+  hi = __shfl_xor(hi, off, kWave);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// ---------------------------------------------------------------- routing
+
+// Sortable key: larger key = larger logit, then lower expert index. -0 and +0
+// compare equal (both map to the +0 key) so ties between them go to the lower
+// index, as for any other equal logits.
+__device__ __forceinline__ uint64_t route_key(float v, uint32_t e) {
+  uint32_t u = __float_as_uint(v);
+  if (v == 0.0f) u = 0u;
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (static_cast<uint64_t>(u) << 32) | (0xFFFFFFFFu - e);
+}
+
+__device__ __forceinline__ float key_value(uint64_t key) {
+  uint32_t u = static_cast<uint32_t>(key >> 32);
+  u = (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u;
+  return __uint_as_float(u);
+}
+
+__device__ __forceinline__ int key_expert(uint64_t key) {
+  return static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(key));
+}
+
+// One wavefront selects the top-k experts of one token and computes the
+// softmax over the k selected logits. Slot j holds the j-th largest logit
+// (ties to the lower expert index). Lanes j < k write ids[j] and w[j].
+template <typename ACT>
+__device__ __forceinline__ void topk_softmax_wave(const ACT* logits, int E, int k, int lane,
+                                                  int32_t* ids, float* w) {
+  uint64_t keys[kMaxExperts / kWave];
+#pragma unroll
+  for (int i = 0; i < kMaxExperts / kWave; ++i) {
+    const int e = lane + kWave * i;
+    keys[i] = (e < E) ? route_key(act_to_f32(logits[e]), static_cast<uint32_t>(e)) : 0ull;
+  }
+  const int epl = (E + kWave - 1) / kWave;
+  int my_id = 0;
+  float my_v = 0.0f, v0 = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = 0ull;
+#pragma unroll
+    for (int i = 0; i < kMaxExperts / kWave; ++i)
+      if (i < epl && keys[i] > best) best = keys[i];
+#pragma unroll
+    for (int off = kWave / 2; off >= 1; off >>= 1) {
+      uint64_t o = shfl_xor_u64(best, off);
+      best = o > best ? o : best;
+    }
+    const int e = key_expert(best);
+    const float v = key_value(best);
+    if (j == 0) v0 = v;
+    if (lane == j) { my_id = e; my_v = v; }
+#pragma unroll
+    for (int i = 0; i < kMaxExperts / kWave; ++i)
+      if (lane == (e & (kWave - 1)) && i == (e / kWave)) keys[i] = 0ull;
+  }
+  const float ex = (lane < k) ? expf(my_v - v0) : 0.0f;
+  const float sum = wave_sum(ex);
+  if (lane < k) {
+    ids[lane] = my_id;
+    w[lane] = ex / sum;
+  }
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+}  // namespace qmoe

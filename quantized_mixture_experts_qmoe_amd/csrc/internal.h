@@ -1,0 +1,70 @@
+// Host-side internals of libqmoe: the validated layer description, the
+// workspace layout, and the kernel launchers each .hip file provides.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/qmoe.h"
+
+namespace qmoe {
+
+// Everything a launcher needs, resolved once at create time.
+struct Layer {
+  int64_t H, I, E;
+  int k, bits, bs, zp;
+  bool act_bf16;
+  int64_t max_tokens;
+  const uint8_t* fc1_codes;
+  const uint16_t* fc1_scales;
+  const uint8_t* fc2_codes;
+  const uint16_t* fc2_scales;
+  int64_t fc1_row_bytes, fc2_row_bytes;   // H*bits/8, I*bits/8
+  int64_t fc1_nblk, fc2_nblk;             // H/bs, I/bs
+};
+
+// Prefill GEMM tiling (rows = routes of one expert, cols = output features).
+constexpr int kTileM = 128;
+constexpr int kTileN = 128;
+constexpr int kRouteChunk = 256;           // routes per histogram/scatter chunk
+
+// Decode GEMV row blocking.
+struct GemvShape {
+  int units;       // K / 32
+  int lpr;         // lanes per row (power of two, <= 64)
+  int upl;         // units per lane (1, 2 or 4)
+  int rows_wave;   // rows one wave covers per step = 64 / lpr
+  int rows_block;  // rows one workgroup covers
+};
+GemvShape gemv_shape(int64_t K, int min_rows_block);
+
+// Workspace layout for one forward call on T tokens (byte offsets).
+struct Workspace {
+  size_t topk_id, topk_w;             // int32 / fp32 [R]
+  size_t counters;                    // int32 [n_counters] (decode combine)
+  size_t h32, y32;                    // decode: fp32 [R, I], fp32 [R, H]
+  size_t hist, chunk_base;            // prefill: int32 [nchunks, E] each
+  size_t counts, offsets;             // int32 [E], [E + 1]
+  size_t sorted_routes, inv_pos;      // int32 [R]
+  size_t tiles, num_tiles;            // int4 [max_tiles], int32 [1]
+  size_t xbf16;                       // prefill with fp32 activations: bf16 [T, H]
+  size_t hbf16, yf32;                 // prefill: bf16 [R, I], fp32 [R, H]
+  size_t total;
+  int64_t R, nchunks, max_tiles;
+  int n_counters;
+  bool decode;
+};
+bool use_decode_path(const Layer& L, bool force_prefill, int64_t T);
+
+// ---- launchers (each returns hipSuccess or the launch error)
+hipError_t launch_route(const Layer& L, const void* logits, int64_t T, char* ws, const Workspace& W,
+                        hipStream_t s);
+hipError_t launch_prefill(const Layer& L, const void* x, void* out, int64_t T, char* ws,
+                          const Workspace& W, hipStream_t s);
+hipError_t launch_decode(const Layer& L, const void* x, const void* logits, void* out, int64_t T,
+                         char* ws, const Workspace& W, hipStream_t s);
+hipError_t launch_dequant(const Layer& L, int fc, int64_t expert, float* out_f32,
+                          uint16_t* out_bf16, hipStream_t s);
+
+}  // namespace qmoe

@@ -1,0 +1,164 @@
+// Routing for the grouped (prefill) path: top-k + softmax over the selected
+// logits, a per-chunk expert histogram, one scan that yields expert offsets,
+// per-chunk scatter bases and the GEMM tile list, and a stable scatter of the
+// route ids into expert-sorted order.
+//
+// Semantics: top-k on the raw router logits with a softmax over the selected
+// k ("Document and test packed token inputs for MoE and QMoE", review of the
+// test harness); the expert-sorted route map with per-expert first offsets is
+// the grouped-GEMM input the tensor-core prefill path consumes ("[CUDA] Add
+// INT4 and INT3 QMoE CPU/GPU offload support", Description of #33731:
+// sorted_routes, tile descriptors, expert_first_token_offset).
+#include "device.h"
+#include "internal.h"
+
+namespace qmoe {
+
+template <typename ACT>
+__global__ __launch_bounds__(256) void route_topk_kernel(const ACT* __restrict__ logits, int64_t T,
+                                                         int E, int k, int32_t* __restrict__ topk_id,
+                                                         float* __restrict__ topk_w) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  topk_softmax_wave(logits + t * E, E, k, lane, topk_id + t * k, topk_w + t * k);
+}
+
+// hist[c][e] = number of routes of chunk c (routes [256c, 256c+256)) sent to e.
+__global__ __launch_bounds__(256) void route_hist_kernel(const int32_t* __restrict__ topk_id,
+                                                         int64_t R, int E,
+                                                         int32_t* __restrict__ hist) {
+  __shared__ int32_t s_hist[kMaxExperts];
+  for (int e = threadIdx.x; e < E; e += 256) s_hist[e] = 0;
+  __syncthreads();
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * kRouteChunk + threadIdx.x;
+  if (r < R) atomicAdd(&s_hist[topk_id[r]], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) hist[static_cast<int64_t>(blockIdx.x) * E + e] = s_hist[e];
+}
+
+// Inclusive scan of s[0..n) in place (n <= 1024, blockDim.x == 1024).
+__device__ void block_scan_inclusive(int32_t* s, int n) {
+  for (int off = 1; off < n; off <<= 1) {
+    int32_t v = 0;
+    if (threadIdx.x < n && threadIdx.x >= off) v = s[threadIdx.x - off];
+    __syncthreads();
+    if (threadIdx.x < n) s[threadIdx.x] += v;
+    __syncthreads();
+  }
+}
+
+// One workgroup of 1024 threads. Thread (e, p) owns expert e and the p-th
+// slice of the chunks.
+__global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restrict__ hist,
+                                                          int64_t nchunks, int E, int tile_m,
+                                                          int32_t* __restrict__ counts,
+                                                          int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ chunk_base,
+                                                          int4* __restrict__ tiles,
+                                                          int32_t* __restrict__ num_tiles) {
+  __shared__ int32_t s_part[1024];
+  __shared__ int32_t s_scan[1024];
+  __shared__ int32_t s_tiles[1024];
+  const int P = 1024 / E;  // E <= 1024
+  const int tid = threadIdx.x;
+  const int e = tid % E, p = tid / E;
+  const bool active = p < P;
+  int64_t c0 = 0, c1 = 0;
+  if (active) {
+    c0 = nchunks * p / P;
+    c1 = nchunks * (p + 1) / P;
+    int32_t sum = 0;
+    for (int64_t c = c0; c < c1; ++c) sum += hist[c * E + e];
+    s_part[p * E + e] = sum;
+  }
+  __syncthreads();
+  // per-expert totals and exclusive bases of each slice
+  if (tid < E) {
+    int32_t run = 0;
+    for (int q = 0; q < P; ++q) {
+      int32_t v = s_part[q * E + tid];
+      s_part[q * E + tid] = run;
+      run += v;
+    }
+    counts[tid] = run;
+    s_scan[tid] = run;
+    s_tiles[tid] = (run + tile_m - 1) / tile_m;
+  }
+  __syncthreads();
+  block_scan_inclusive(s_scan, E);
+  block_scan_inclusive(s_tiles, E);
+  if (tid < E) {
+    offsets[tid + 1] = s_scan[tid];
+    if (tid == 0) offsets[0] = 0;
+  }
+  if (tid == 0) num_tiles[0] = s_tiles[E - 1];
+  __syncthreads();
+  if (active) {
+    const int32_t expert_start = (e == 0) ? 0 : s_scan[e - 1];
+    int32_t run = expert_start + s_part[p * E + e];
+    for (int64_t c = c0; c < c1; ++c) {
+      chunk_base[c * E + e] = run;
+      run += hist[c * E + e];
+    }
+  }
+  if (tid < E) {
+    const int32_t expert_start = (tid == 0) ? 0 : s_scan[tid - 1];
+    const int32_t cnt = s_scan[tid] - expert_start;
+    const int32_t t0 = (tid == 0) ? 0 : s_tiles[tid - 1];
+    for (int32_t i = 0; i * tile_m < cnt; ++i) {
+      const int32_t rows = min(tile_m, cnt - i * tile_m);
+      tiles[t0 + i] = make_int4(tid, expert_start + i * tile_m, rows, 0);
+    }
+  }
+}
+
+// Stable scatter: a route's rank among the earlier routes of its chunk that
+// chose the same expert, added to the chunk's base for that expert.
+__global__ __launch_bounds__(256) void route_scatter_kernel(const int32_t* __restrict__ topk_id,
+                                                            int64_t R, int E,
+                                                            const int32_t* __restrict__ chunk_base,
+                                                            int32_t* __restrict__ sorted_routes,
+                                                            int32_t* __restrict__ inv_pos) {
+  __shared__ int32_t s_e[kRouteChunk];
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * kRouteChunk + threadIdx.x;
+  const int32_t e = (r < R) ? topk_id[r] : -1;
+  s_e[threadIdx.x] = e;
+  __syncthreads();
+  if (r >= R) return;
+  int32_t rank = 0;
+  for (int i = 0; i < static_cast<int>(threadIdx.x); ++i) rank += (s_e[i] == e);
+  const int32_t pos = chunk_base[static_cast<int64_t>(blockIdx.x) * E + e] + rank;
+  sorted_routes[pos] = static_cast<int32_t>(r);
+  inv_pos[r] = pos;
+}
+
+hipError_t launch_route(const Layer& L, const void* logits, int64_t T, char* ws, const Workspace& W,
+                        hipStream_t s) {
+  const int E = static_cast<int>(L.E), k = L.k;
+  int32_t* topk_id = reinterpret_cast<int32_t*>(ws + W.topk_id);
+  float* topk_w = reinterpret_cast<float*>(ws + W.topk_w);
+  const unsigned gt = static_cast<unsigned>((T + 3) / 4);
+  if (L.act_bf16)
+    route_topk_kernel<uint16_t><<<gt, 256, 0, s>>>(static_cast<const uint16_t*>(logits), T, E, k,
+                                                    topk_id, topk_w);
+  else
+    route_topk_kernel<float><<<gt, 256, 0, s>>>(static_cast<const float*>(logits), T, E, k, topk_id,
+                                                 topk_w);
+  const unsigned nc = static_cast<unsigned>(W.nchunks);
+  int32_t* hist = reinterpret_cast<int32_t*>(ws + W.hist);
+  route_hist_kernel<<<nc, 256, 0, s>>>(topk_id, W.R, E, hist);
+  route_scan_kernel<<<1, 1024, 0, s>>>(hist, W.nchunks, E, kTileM,
+                                       reinterpret_cast<int32_t*>(ws + W.counts),
+                                       reinterpret_cast<int32_t*>(ws + W.offsets),
+                                       reinterpret_cast<int32_t*>(ws + W.chunk_base),
+                                       reinterpret_cast<int4*>(ws + W.tiles),
+                                       reinterpret_cast<int32_t*>(ws + W.num_tiles));
+  route_scatter_kernel<<<nc, 256, 0, s>>>(topk_id, W.R, E,
+                                          reinterpret_cast<const int32_t*>(ws + W.chunk_base),
+                                          reinterpret_cast<int32_t*>(ws + W.sorted_routes),
+                                          reinterpret_cast<int32_t*>(ws + W.inv_pos));
+  return hipGetLastError();
+}
+
+}  // namespace qmoe

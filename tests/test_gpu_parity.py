@@ -1,0 +1,261 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle.
+
+Bit-exact: top-k ids, the permutation (expert offsets, sorted routes, inverse
+positions) and dequantized weight values. Routing weights: within 4 fp32 ulps
+of the oracle's softmax. Outputs: the G1-or-G2 tolerance of tests/tolerance.py.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import qmoe_inputs as qi
+from tests.gpu_util import DEV, fp32_ulps, layer_for, oracle_acc, run, sample_rows, say
+from tests.tolerance import compare
+
+pytestmark = pytest.mark.gpu
+
+FORMATS = [(b, bs) for b in (4, 3, 2) for bs in (32, 64, 128)]
+
+
+def small_spec(bits, bs, act="bf16", **kw):
+    d = dict(hidden=256, inter=128, num_experts=8, top_k=2, bits=bits, block_size=bs,
+             zero_point=1 << (bits - 1), scale_c=0.03, act_dtype=act)
+    d.update(kw)
+    return qi.LayerSpec(**d)
+
+
+# ------------------------------------------------------------------ dequant
+
+@pytest.mark.parametrize("bits,bs", FORMATS)
+def test_dequant_bit_exact_small(bits, bs):
+    wl = qi.make_layer(small_spec(bits, bs), T=1, seed=bits * 100 + bs)
+    layer = layer_for(wl, 16)
+    s = wl.spec
+    for fc, e in ((1, 0), (2, 7), (1, 5)):
+        f32, b16 = layer.dequant(fc, e)
+        torch.cuda.synchronize()
+        K = s.hidden if fc == 1 else s.inter
+        codes = wl.weights.fc1_codes[e] if fc == 1 else wl.weights.fc2_codes[e]
+        scales = wl.weights.fc1_scales[e] if fc == 1 else wl.weights.fc2_scales[e]
+        ref = oracle.dequant(codes, scales, bits, bs, s.zero_point, K)
+        assert np.array_equal(f32.cpu().numpy().astype(np.float64), ref)
+        ref_bf16 = oracle.f32_to_bf16_bits(ref.astype(np.float32))
+        got = b16.view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, ref_bf16)
+
+
+@pytest.mark.parametrize("name", ["decode", "int3", "stack"])
+def test_dequant_bit_exact_full_shape(name):
+    wl = qi.make_workload(name, T=1)
+    layer = layer_for(wl, 16)
+    s = wl.spec
+    for fc, e in ((1, 3), (2, 127)):
+        f32, b16 = layer.dequant(fc, e)
+        torch.cuda.synchronize()
+        K = s.hidden if fc == 1 else s.inter
+        codes = wl.weights.fc1_codes[e] if fc == 1 else wl.weights.fc2_codes[e]
+        scales = wl.weights.fc1_scales[e] if fc == 1 else wl.weights.fc2_scales[e]
+        ref = oracle.dequant(codes, scales, s.bits, s.block_size, s.zero_point, K)
+        assert np.array_equal(f32.cpu().numpy().astype(np.float64), ref)
+        got = b16.view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, oracle.f32_to_bf16_bits(ref.astype(np.float32)))
+
+
+# ------------------------------------------------------------------ routing
+
+def check_routing(wl, layer):
+    T, k, E = wl.tokens.x.shape[0], wl.spec.top_k, wl.spec.num_experts
+    ids, w, offs, srt, inv = layer.route(wl.tokens.logits.to(DEV))
+    torch.cuda.synchronize()
+    rid, rw = oracle.route(wl.tokens.logits, k)
+    assert np.array_equal(ids.cpu().numpy(), rid)
+    ulps = fp32_ulps(w.cpu().numpy(), rw.astype(np.float32))
+    assert ulps.max() <= 4, ulps.max()
+    counts, roffs, rsrt, rinv = oracle.permute(rid, E)
+    assert np.array_equal(offs.cpu().numpy(), roffs)
+    assert np.array_equal(srt.cpu().numpy(), rsrt)
+    assert np.array_equal(inv.cpu().numpy(), rinv)
+    return counts
+
+
+@pytest.mark.parametrize("name,T", [("tiny", 4), ("decode", 1), ("decode", 4), ("prefill", 8192),
+                                    ("int3", 2048), ("stack", 32768), ("prefill", 777)])
+def test_routing_bit_exact(name, T):
+    say(f"routing {name} T={T}")
+    wl = qi.make_workload(name, T=T)
+    layer = layer_for(wl, max(T, 8))
+    counts = check_routing(wl, layer)
+    assert counts.sum() == T * wl.spec.top_k
+
+
+def test_routing_constructed_ties():
+    wl = qi.make_workload("decode", T=64)
+    l = wl.tokens.logits.clone()
+    l[0, :] = 0.5                       # every logit equal: experts 0..7 in order
+    l[1, ::2] = 1.0                     # even experts tie at the top
+    l[2, :] = -0.0
+    l[2, 5] = 0.0                       # -0 and +0 compare equal: lowest indices win
+    l[3, :] = torch.arange(128).flip(0).to(l.dtype) * 0   # zeros
+    wl.tokens.logits = l
+    layer = layer_for(wl, 64)
+    check_routing(wl, layer)
+
+
+# ------------------------------------------------------------------ decode path
+
+def check_decode(wl, layer, min_g1_frac=0.999):
+    T = wl.tokens.x.shape[0]
+    out, ws = run(layer, wl.tokens.x, wl.tokens.logits)
+    ids, w = layer.routing_from_workspace(T, ws)
+    rid, rw = oracle.route(wl.tokens.logits, wl.spec.top_k)
+    assert np.array_equal(ids.cpu().numpy(), rid)
+    assert fp32_ulps(w.cpu().numpy(), rw.astype(np.float32)).max() <= 4
+    rep = compare(out, oracle_acc(wl))
+    say(f"decode {wl.name} T={T}: {rep}")
+    assert rep.ok, rep
+    assert rep.frac_within_ulp >= min_g1_frac, rep
+    return out
+
+
+@pytest.mark.parametrize("name,T", [("tiny", 4), ("tiny", 1), ("decode", 1), ("decode", 2),
+                                    ("decode", 4), ("int3", 4), ("stack", 1), ("stack", 4)])
+def test_decode_parity(name, T):
+    wl = qi.make_workload(name, T=T)
+    check_decode(wl, layer_for(wl, 16))
+
+
+@pytest.mark.parametrize("bits,bs", FORMATS)
+def test_decode_parity_formats(bits, bs):
+    wl = qi.make_layer(small_spec(bits, bs), T=3, seed=7 + bits + bs)
+    check_decode(wl, layer_for(wl, 16))
+
+
+def test_decode_fp32_activations_formats():
+    for bits, bs in ((3, 64), (2, 128)):
+        wl = qi.make_layer(small_spec(bits, bs, act="f32"), T=4, seed=3 + bits)
+        check_decode(wl, layer_for(wl, 16))
+
+
+def test_decode_repeated_experts_across_tokens():
+    """Four tokens with identical logits share all k experts: each expert is
+    streamed once and serves every token."""
+    wl = qi.make_workload("decode", T=4)
+    wl.tokens.logits = wl.tokens.logits[:1].repeat(4, 1).contiguous()
+    check_decode(wl, layer_for(wl, 16))
+
+
+# ------------------------------------------------------------------ prefill path
+
+def check_prefill(wl, layer, rows=None):
+    T = wl.tokens.x.shape[0]
+    out, ws = run(layer, wl.tokens.x, wl.tokens.logits)
+    ids, w = layer.routing_from_workspace(T, ws)
+    rid, _ = oracle.route(wl.tokens.logits, wl.spec.top_k)
+    assert np.array_equal(ids.cpu().numpy(), rid)
+    if rows is None:
+        rep = compare(out, oracle_acc(wl))
+    else:
+        rep = compare(out[torch.as_tensor(rows, device=DEV)], oracle_acc(wl, rows))
+    say(f"prefill {wl.name} T={T} rows={'all' if rows is None else len(rows)}: {rep}")
+    assert rep.ok, rep
+    return out
+
+
+@pytest.mark.parametrize("name,T", [("tiny", 5), ("tiny", 37), ("decode", 5), ("decode", 150),
+                                    ("int3", 67), ("stack", 129)])
+def test_prefill_parity_full(name, T):
+    wl = qi.make_workload(name, T=T)
+    check_prefill(wl, layer_for(wl, max(T, 8)))
+
+
+@pytest.mark.parametrize("name,T,n", [("prefill", 8192, 48), ("int3", 2048, 48), ("stack", 4096, 32)])
+def test_prefill_parity_sampled(name, T, n):
+    say(f"prefill sampled {name} T={T}")
+    wl = qi.make_workload(name, T=T)
+    check_prefill(wl, layer_for(wl, T), rows=sample_rows(T, n, seed=T))
+
+
+@pytest.mark.parametrize("bits,bs", FORMATS)
+def test_prefill_parity_formats(bits, bs):
+    wl = qi.make_layer(small_spec(bits, bs), T=300, seed=11 + bits + bs, nseq=3)
+    check_prefill(wl, layer_for(wl, 300))
+
+
+def test_prefill_fp32_activations():
+    wl = qi.make_layer(small_spec(4, 32, act="f32", hidden=192, inter=96), T=45, seed=5)
+    check_prefill(wl, layer_for(wl, 64))
+
+
+# ------------------------------------------------------------------ properties
+
+def test_decode_and_prefill_agree():
+    wl = qi.make_workload("decode", T=4)
+    a, _ = run(layer_for(wl, 16), wl.tokens.x, wl.tokens.logits)
+    os.environ["QMOE_FORCE_PATH"] = "prefill"
+    try:
+        lp = layer_for(wl, 16)
+    finally:
+        del os.environ["QMOE_FORCE_PATH"]
+    b, _ = run(lp, wl.tokens.x, wl.tokens.logits)
+    ref = oracle_acc(wl)
+    ra, rb = compare(a, ref), compare(b, ref)
+    assert ra.ok and rb.ok, (ra, rb)
+    d = (a.float() - b.float()).norm(dim=1) / a.float().norm(dim=1)
+    assert d.max().item() < 1e-2
+
+
+def test_packed_equals_per_sequence():
+    """Prefill rows are batch-invariant, so a sequence of >= 5 tokens run alone
+    reproduces its rows of the packed run bit for bit; shorter sequences take
+    the decode path and must agree within tolerance."""
+    wl = qi.make_workload("prefill", T=160)
+    layer = layer_for(wl, 160)
+    packed, _ = run(layer, wl.tokens.x, wl.tokens.logits)
+    s = 0
+    for n in wl.tokens.seq_lens:
+        part, _ = run(layer, wl.tokens.x[s:s + n].contiguous(), wl.tokens.logits[s:s + n].contiguous())
+        if n >= 5:
+            assert torch.equal(part, packed[s:s + n]), (s, n)
+        else:
+            sub = qi.Workload("seq", wl.spec, qi.Tokens(wl.tokens.x[s:s + n], wl.tokens.logits[s:s + n]),
+                              wl.weights)
+            assert compare(part, oracle_acc(sub)).ok
+        s += n
+
+
+@pytest.mark.parametrize("name,T", [("decode", 4), ("prefill", 1024)])
+def test_run_to_run_bitwise_deterministic(name, T):
+    wl = qi.make_workload(name, T=T)
+    layer = layer_for(wl, T)
+    a, _ = run(layer, wl.tokens.x, wl.tokens.logits)
+    b, _ = run(layer, wl.tokens.x, wl.tokens.logits)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_empty_input_is_a_noop():
+    wl = qi.make_workload("decode", T=4)
+    layer = layer_for(wl, 16)
+    out = torch.full((0, 2048), 7.0, dtype=torch.bfloat16, device=DEV)
+    res = layer(torch.empty((0, 2048), dtype=torch.bfloat16, device=DEV),
+                torch.empty((0, 128), dtype=torch.bfloat16, device=DEV), out=out)
+    torch.cuda.synchronize()
+    assert res.shape == (0, 2048)
+
+
+def test_forward_rejects_small_workspace_and_too_many_tokens():
+    import quantized_mixture_experts_qmoe_amd as q
+    wl = qi.make_workload("decode", T=4)
+    layer = layer_for(wl, 4)
+    x, l = wl.tokens.x.to(DEV), wl.tokens.logits.to(DEV)
+    ws = torch.empty(64, dtype=torch.uint8, device=DEV)
+    with pytest.raises(q.QMoEError) as ei:
+        layer(x, l, workspace=ws)
+    assert ei.value.status == 3
+    x5 = torch.zeros((5, 2048), dtype=torch.bfloat16, device=DEV)
+    l5 = torch.zeros((5, 128), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(q.QMoEError) as ei:
+        layer(x5, l5, workspace=layer.workspace(4))
+    assert ei.value.status == 1
