@@ -1,0 +1,323 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized MoE layer on one MI355X.
+
+Default run: the Qwen3-30B-A3B-shaped INT4 (block 32) layer, H=2048, I=768,
+E=128, top-8, bf16 activations, decoding M=4 tokens per step (the headline
+line), plus M=1 decode and the 8192-token packed prefill as extra entries.
+
+Timing. Every timed region is bracketed by torch.cuda.synchronize(). Inside,
+a short spin kernel first holds the stream while the host enqueues the K
+steps, then HIP events on that stream time exactly the K steps on the GPU, so
+host launch overhead is not mistaken for layer time. Decode steps rotate over
+NROT independently seeded layer instances (weights, activations, logits)
+whose combined active-expert bytes exceed the 256 MB MALL, so the weights
+come from HBM as they would in a deep model.
+
+Roofline. A second pass enables the library's stage hook, which records a
+HIP event on the stream after each kernel launch; the dominant kernel's
+average duration comes from those events. Algorithmic bytes (decode) and
+FLOPs (prefill) per launch are counted from the routing the call actually
+made (distinct experts per call).
+
+CPU baseline. The plain C oracle, timed on a bounded sample of tokens of the
+same workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import qmoe_inputs as qi  # noqa: E402
+import quantized_mixture_experts_qmoe_amd as q  # noqa: E402
+
+METRIC = "QMoE layer tokens/s: decode M=1..4 (%HBM peak), 8K prefill (%MFMA peak)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+NROT = 24
+DEV = torch.device("cuda:0")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------- instances
+
+def make_layer(spec: qi.LayerSpec, w: qi.LayerWeights, max_tokens: int) -> q.QMoELayer:
+    cfg = q.LayerConfig(spec.hidden, spec.inter, spec.num_experts, spec.top_k, spec.bits,
+                        spec.block_size, spec.zero_point, torch.bfloat16, max_tokens)
+    return q.QMoELayer(cfg, torch.from_numpy(w.fc1_codes).to(DEV),
+                       torch.from_numpy(w.fc1_scales).to(DEV),
+                       torch.from_numpy(w.fc2_codes).to(DEV),
+                       torch.from_numpy(w.fc2_scales).to(DEV))
+
+
+def device_instance(spec: qi.LayerSpec, T: int, seed: int, max_tokens: int):
+    """A layer instance drawn on the GPU (same distributions as qmoe_inputs)."""
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    E, H, I, bs, c = spec.num_experts, spec.hidden, spec.inter, spec.block_size, spec.scale_c
+
+    def codes(n, kk):
+        return torch.randint(0, 256, (E, n, kk * spec.bits // 8), generator=g, device=DEV,
+                             dtype=torch.uint8)
+
+    def scales(n, kk):
+        return (torch.randn((E, n, kk // bs), generator=g, device=DEV).abs() * c + 1e-3).half()
+
+    w = (codes(2 * I, H), scales(2 * I, H), codes(H, I), scales(H, I))
+    cfg = q.LayerConfig(spec.hidden, spec.inter, spec.num_experts, spec.top_k, spec.bits,
+                        spec.block_size, spec.zero_point, torch.bfloat16, max_tokens)
+    layer = q.QMoELayer(cfg, *w)
+    x = torch.randn((T, H), generator=g, device=DEV).bfloat16()
+    logits = torch.randn((T, E), generator=g, device=DEV).bfloat16()
+    return layer, x, logits
+
+
+def expert_bytes(spec: qi.LayerSpec):
+    H, I, bs, b = spec.hidden, spec.inter, spec.block_size, spec.bits
+    fc1 = 2 * I * H * b // 8 + 2 * I * (H // bs) * 2
+    fc2 = H * I * b // 8 + H * (I // bs) * 2
+    return fc1, fc2
+
+
+# ----------------------------------------------------------------- timing
+
+_SLEEP_CYCLES = None
+
+
+def _hold_stream(seconds: float):
+    """Enqueue a spin kernel that keeps the stream busy for about `seconds`."""
+    global _SLEEP_CYCLES
+    if _SLEEP_CYCLES is None:
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        torch.cuda._sleep(1_000_000)
+        b.record()
+        torch.cuda.synchronize()
+        _SLEEP_CYCLES = 1_000_000 / max(a.elapsed_time(b) / 1e3, 1e-6)   # cycles per second
+    torch.cuda._sleep(int(_SLEEP_CYCLES * seconds))
+
+
+def time_steps(step, K: int, hold_s: float):
+    """GPU time of exactly K calls of step(i), host enqueue hidden behind a spin kernel."""
+    torch.cuda.synchronize()
+    _hold_stream(hold_s)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(K):
+        step(i)
+    end.record()
+    enqueue_s = time.perf_counter() - t0
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t0
+    return start.elapsed_time(end) / K, enqueue_s, wall_s
+
+
+def kernel_times(layers, step, K: int, hold_s: float):
+    """Average duration (ms) per kernel role, from events the stage hook records."""
+    marks = []
+
+    def hook(stage, name):
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record()
+        marks.append((stage, name, ev))
+
+    for L in layers:
+        L.set_stage_hook(hook)
+    torch.cuda.synchronize()
+    _hold_stream(hold_s)
+    for i in range(K):
+        step(i)
+    torch.cuda.synchronize()
+    for L in layers:
+        L.set_stage_hook(None)
+    sums, counts = {}, {}
+    for a, b in zip(marks, marks[1:]):
+        if b[0] == 0:
+            continue            # next call starts
+        ms = a[2].elapsed_time(b[2])
+        sums[b[1]] = sums.get(b[1], 0.0) + ms
+        counts[b[1]] = counts.get(b[1], 0) + 1
+    return {k: sums[k] / counts[k] for k in sums}
+
+
+# ----------------------------------------------------------------- workloads
+
+def bench_decode(T: int, steps: int, warmup: int):
+    spec = qi.QWEN3_INT4
+    log(f"[bench] decode M={T}: building {NROT} layer instances")
+    wl0 = qi.make_workload("decode", T=T)
+    insts = [(make_layer(spec, wl0.weights, 4), wl0.tokens.x.to(DEV), wl0.tokens.logits.to(DEV))]
+    for i in range(1, NROT):
+        insts.append(device_instance(spec, T, 1000 * T + i, 4))
+    ws = insts[0][0].workspace(T)
+    out = torch.empty((T, spec.hidden), dtype=torch.bfloat16, device=DEV)
+
+    def step(i):
+        L, x, l = insts[i % NROT]
+        L.forward(x, l, out=out, workspace=ws)
+
+    # distinct experts of each instance (from the routing the layer computed)
+    distinct = []
+    for i in range(NROT):
+        step(i)
+        ids, _ = insts[i][0].routing_from_workspace(T, ws)
+        distinct.append(int(torch.unique(ids).numel()))
+    torch.cuda.synchronize()
+    for i in range(warmup):
+        step(i)
+    ms, enq, wall = time_steps(step, steps, hold_s=0.002 + steps * 1e-4)
+    log(f"[bench] decode M={T}: {ms * 1e3:.2f} us/step (enqueue {enq * 1e3:.1f} ms, wall {wall * 1e3:.1f} ms)")
+    kt = kernel_times([it[0] for it in insts], step, min(steps, 4 * NROT), hold_s=0.01)
+    log(f"[bench] decode M={T} kernels (us): " + ", ".join(f"{k}={v * 1e3:.2f}" for k, v in kt.items()))
+    fc1_b, fc2_b = expert_bytes(spec)
+    D = float(np.mean([distinct[i % NROT] for i in range(steps)]))
+    H, I, E, k = spec.hidden, spec.inter, spec.num_experts, spec.top_k
+    R = T * k
+    fc1_bytes = D * fc1_b + T * H * 2 + T * E * 2 + R * I * 4
+    layer_bytes = D * (fc1_b + fc2_b) + T * H * 2 * 2 + T * E * 2
+    t_fc1 = kt["decode_fc1_swiglu"] * 1e-3
+    t_fc2 = kt["decode_fc2_combine"] * 1e-3
+    fc2_bytes = D * fc2_b + R * I * 4 + 2 * R * H * 4 + T * H * 2
+    return {
+        "T": T, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
+        "distinct_experts": D,
+        "layer_GBs": layer_bytes / (ms * 1e-3) / 1e9,
+        "layer_frac_hbm": layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "kernels_us": {kk: v * 1e3 for kk, v in kt.items()},
+        "fc1": {"bytes": fc1_bytes, "s": t_fc1, "GBs": fc1_bytes / t_fc1 / 1e9},
+        "fc2": {"bytes": fc2_bytes, "s": t_fc2, "GBs": fc2_bytes / t_fc2 / 1e9},
+    }
+
+
+def bench_prefill(steps: int, warmup: int):
+    spec = qi.QWEN3_INT4
+    T = 8192
+    log("[bench] prefill 8K: building layer")
+    wl = qi.make_workload("prefill", T=T)
+    L = make_layer(spec, wl.weights, T)
+    x, l = wl.tokens.x.to(DEV), wl.tokens.logits.to(DEV)
+    ws = L.workspace(T)
+    out = torch.empty((T, spec.hidden), dtype=torch.bfloat16, device=DEV)
+
+    def step(i):
+        L.forward(x, l, out=out, workspace=ws)
+
+    for i in range(warmup):
+        step(i)
+    ms, enq, wall = time_steps(step, steps, hold_s=0.005)
+    kt = kernel_times([L], step, steps, hold_s=0.005)
+    log(f"[bench] prefill 8K: {ms:.3f} ms/step; kernels (us): "
+        + ", ".join(f"{k}={v * 1e3:.1f}" for k, v in kt.items()))
+    H, I, k = spec.hidden, spec.inter, spec.top_k
+    R = T * k
+    flops = 2.0 * R * (2 * I * H + H * I)
+    fc1_flops = 2.0 * R * 2 * I * H
+    t_fc1 = kt["gemm_fc1_swiglu"] * 1e-3
+    return {
+        "T": T, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
+        "layer_TFLOPs": flops / (ms * 1e-3) / 1e12,
+        "layer_frac_mfma": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+        "kernels_us": {kk: v * 1e3 for kk, v in kt.items()},
+        "fc1": {"flops": fc1_flops, "s": t_fc1, "TFLOPs": fc1_flops / t_fc1 / 1e12},
+    }
+
+
+def cpu_baseline(n_tokens: int):
+    """The oracle on a bounded sample of decode tokens, all host cores."""
+    import oracle
+    wl = qi.make_workload("decode", T=n_tokens)
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    oracle.forward(oracle.Layer.from_spec(wl.spec), wl.tokens.x, wl.tokens.logits, wl.weights,
+                   nthreads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_tokens} tokens of the decode workload (Qwen3-30B-A3B-shaped INT4 bs32 "
+                      f"layer, uniform routing), {dt:.1f} s wall on {threads} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--prefill-steps", type=int, default=20)
+    ap.add_argument("--no-extra", action="store_true", help="skip the M=1 and 8K prefill entries")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=48)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer is measured on one GPU's share)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    q.lib()   # fail loudly if the HIP library is missing
+
+    main_res = bench_decode(4, args.steps, args.warmup)
+    extra = []
+    if not args.no_extra:
+        m1 = bench_decode(1, args.steps, args.warmup)
+        pf = bench_prefill(args.prefill_steps, 3)
+        extra = [
+            {"workload": "decode M=1", "tokens_per_s": m1["tokens_per_s"],
+             "ms_per_step": m1["ms_per_step"], "layer_frac_hbm": m1["layer_frac_hbm"],
+             "distinct_experts": m1["distinct_experts"], "kernels_us": m1["kernels_us"],
+             "roofline": {"bound": "hbm", "kernel": "decode_fc1_swiglu",
+                          "achieved": m1["fc1"]["GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": m1["fc1"]["GBs"] / HBM_PEAK_GBS}},
+            {"workload": "prefill 8192 tokens (16 packed sequences, Zipf-skewed routing)",
+             "tokens_per_s": pf["tokens_per_s"], "ms_per_step": pf["ms_per_step"],
+             "layer_frac_mfma": pf["layer_frac_mfma"], "kernels_us": pf["kernels_us"],
+             "roofline": {"bound": "mfma", "kernel": "gemm_fc1_swiglu",
+                          "achieved": pf["fc1"]["TFLOPs"], "peak": BF16_PEAK_TFLOPS,
+                          "unit": "TFLOP/s", "frac": pf["fc1"]["TFLOPs"] / BF16_PEAK_TFLOPS}},
+        ]
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_tokens)
+
+    fc1 = main_res["fc1"]
+    line = {
+        "metric": METRIC,
+        "value": main_res["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "Qwen3-30B-A3B-shaped QMoE layer decode, M=4 tokens per step "
+                               "(INT4 bs32, H=2048, I=768, E=128, top-8, bf16 in/out)",
+                   "tokens_per_step": 4, "layer_instances_rotated": NROT,
+                   "distinct_experts_per_step": main_res["distinct_experts"],
+                   "layer_frac_hbm": main_res["layer_frac_hbm"],
+                   "kernels_us": main_res["kernels_us"]},
+        "roofline": {"bound": "hbm", "kernel": "decode_fc1_swiglu", "achieved": fc1["GBs"],
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": fc1["GBs"] / HBM_PEAK_GBS,
+                     "traffic": None},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

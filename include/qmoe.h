@@ -164,6 +164,17 @@ qmoe_status qmoe_dequant(qmoe_handle *handle, int fc, int64_t expert, float *out
 qmoe_status qmoe_workspace_routing(const qmoe_handle *handle, int64_t num_tokens,
                                    size_t *topk_id_offset, size_t *topk_w_offset);
 
+/*
+ * Profiling hook. When set, qmoe_forward calls fn(user, stage, name) on the
+ * host right after it enqueues each kernel (stage = 1, 2, ... in launch order,
+ * name = the kernel's role, a static string), and once with stage = 0 before
+ * the first launch. It lets a caller record events on the stream between the
+ * kernels of a real forward call. fn = NULL removes the hook. The hook must
+ * not call back into the library.
+ */
+typedef void (*qmoe_stage_fn)(void *user, int stage, const char *name);
+qmoe_status qmoe_set_stage_hook(qmoe_handle *handle, qmoe_stage_fn fn, void *user);
+
 #ifdef __cplusplus
 }
 #endif

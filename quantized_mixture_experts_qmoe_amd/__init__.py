@@ -22,7 +22,10 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration",
           3: "workspace missing or too small", 4: "HIP runtime error", 5: "out of host memory"}
 
 EXPORTS = ("qmoe_create", "qmoe_workspace_size", "qmoe_forward", "qmoe_destroy",
-           "qmoe_status_string", "qmoe_route", "qmoe_dequant", "qmoe_workspace_routing")
+           "qmoe_status_string", "qmoe_route", "qmoe_dequant", "qmoe_workspace_routing",
+           "qmoe_set_stage_hook")
+
+STAGE_FN = ctypes.CFUNCTYPE(None, ctypes.c_void_p, ctypes.c_int, ctypes.c_char_p)
 
 
 class QMoEError(RuntimeError):
@@ -67,8 +70,9 @@ def lib() -> ctypes.CDLL:
         L.qmoe_route.argtypes = [P, P, i64, P, P, P, P, P, P, sz, P]
         L.qmoe_dequant.argtypes = [P, ctypes.c_int, i64, P, P, P]
         L.qmoe_workspace_routing.argtypes = [P, i64, ctypes.POINTER(sz), ctypes.POINTER(sz)]
+        L.qmoe_set_stage_hook.argtypes = [P, STAGE_FN, P]
         for name in ("qmoe_create", "qmoe_workspace_size", "qmoe_forward", "qmoe_destroy",
-                     "qmoe_route", "qmoe_dequant", "qmoe_workspace_routing"):
+                     "qmoe_route", "qmoe_dequant", "qmoe_workspace_routing", "qmoe_set_stage_hook"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -192,6 +196,15 @@ class QMoELayer:
         ids = workspace[a.value:a.value + 4 * R].view(torch.int32).view(num_tokens, self.cfg.top_k)
         w = workspace[b.value:b.value + 4 * R].view(torch.float32).view(num_tokens, self.cfg.top_k)
         return ids, w
+
+    def set_stage_hook(self, fn):
+        """fn(stage: int, name: str) runs on the host after each kernel launch of
+        forward(); None removes it."""
+        if fn is None:
+            self._hook = STAGE_FN()
+        else:
+            self._hook = STAGE_FN(lambda _u, stage, name: fn(stage, name.decode()))
+        _check(lib().qmoe_set_stage_hook(self._h, self._hook, None), "qmoe_set_stage_hook")
 
     def route(self, logits: torch.Tensor):
         """Routing stage only: (topk_id, topk_w, expert_offsets, sorted_routes, inv_pos)."""

@@ -180,6 +180,8 @@ qmoe_status qmoe_create(const qmoe_config* c, const qmoe_weights* w, int device,
   L.fc2_row_bytes = L.I * L.bits / 8;
   L.fc1_nblk = L.H / L.bs;
   L.fc2_nblk = L.I / L.bs;
+  L.hook = nullptr;
+  L.hook_user = nullptr;
   h->device = device;
   const char* force = getenv("QMOE_FORCE_PATH");
   h->force_prefill = force && strcmp(force, "prefill") == 0;
@@ -213,6 +215,7 @@ qmoe_status qmoe_forward(qmoe_handle* h, const void* x, const void* logits, void
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(ws);
   hipError_t err;
+  stage_done(h->L, 0, "start");
   if (use_decode_path(h->L, h->force_prefill, T)) {
     const Workspace W = layout(h->L, T, true);
     err = launch_decode(h->L, x, logits, out, T, base, W, s);
@@ -256,6 +259,13 @@ qmoe_status qmoe_dequant(qmoe_handle* h, int fc, int64_t expert, float* out_f32,
   if (!guard.ok()) return QMOE_ERR_HIP;
   hipError_t err = launch_dequant(h->L, fc, expert, out_f32, out_bf16, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? QMOE_OK : QMOE_ERR_HIP;
+}
+
+qmoe_status qmoe_set_stage_hook(qmoe_handle* h, qmoe_stage_fn fn, void* user) {
+  if (!h) return QMOE_ERR_INVALID_ARG;
+  h->L.hook = fn;
+  h->L.hook_user = user;
+  return QMOE_OK;
 }
 
 qmoe_status qmoe_destroy(qmoe_handle* h) {

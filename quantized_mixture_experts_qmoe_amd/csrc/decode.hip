@@ -375,6 +375,7 @@ hipError_t launch_decode_t(const Layer& L, const void* x, const void* logits, vo
     decode_fc1_kernel<BITS, UPL, false><<<g1, 256, 0, s>>>(
         x, logits, Ti, E, k, L.fc1_codes, L.fc1_scales, H, I, L.bs, L.zp, L.fc1_row_bytes,
         L.fc1_nblk, s1.lpr, s1.rows_block, ids, w, h32, counters, W.n_counters);
+  stage_done(L, 1, "decode_fc1_swiglu");
   return hipGetLastError();
 }
 
@@ -397,6 +398,7 @@ hipError_t launch_fc2_t(const Layer& L, void* out, int64_t T, char* ws, const Wo
     decode_fc2_kernel<BITS, UPL, false><<<g2, 256, 0, s>>>(
         h32, ids, w, Ti, k, L.fc2_codes, L.fc2_scales, H, I, L.bs, L.zp, L.fc2_row_bytes,
         L.fc2_nblk, s2.lpr, s2.rows_block, y32, counters, out);
+  stage_done(L, 2, "decode_fc2_combine");
   return hipGetLastError();
 }
 

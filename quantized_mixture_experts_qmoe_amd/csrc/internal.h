@@ -22,7 +22,14 @@ struct Layer {
   const uint16_t* fc2_scales;
   int64_t fc1_row_bytes, fc2_row_bytes;   // H*bits/8, I*bits/8
   int64_t fc1_nblk, fc2_nblk;             // H/bs, I/bs
+  qmoe_stage_fn hook;                     // profiling hook (may be null)
+  void* hook_user;
 };
+
+// Report a finished launch to the profiling hook, if any.
+inline void stage_done(const Layer& L, int stage, const char* name) {
+  if (L.hook) L.hook(L.hook_user, stage, name);
+}
 
 // Prefill GEMM tiling (rows = routes of one expert, cols = output features).
 constexpr int kTileM = 128;

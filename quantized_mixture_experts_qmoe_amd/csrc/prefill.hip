@@ -246,9 +246,11 @@ hipError_t launch_gemms(const Layer& L, const uint16_t* xb, char* ws, const Work
   grouped_gemm_kernel<BITS, true><<<static_cast<unsigned>(g1), 256, 0, s>>>(
       xb, sorted, L.k, L.fc1_codes, L.fc1_scales, H, H, I, L.bs, L.zp, L.fc1_row_bytes, L.fc1_nblk,
       tiles, ntiles, nt1, hb, nullptr);
+  stage_done(L, 6, "gemm_fc1_swiglu");
   grouped_gemm_kernel<BITS, false><<<static_cast<unsigned>(g2), 256, 0, s>>>(
       hb, sorted, L.k, L.fc2_codes, L.fc2_scales, I, H, I, L.bs, L.zp, L.fc2_row_bytes, L.fc2_nblk,
       tiles, ntiles, nt2, nullptr, yf);
+  stage_done(L, 7, "gemm_fc2");
   return hipGetLastError();
 }
 
@@ -262,6 +264,7 @@ hipError_t launch_prefill(const Layer& L, const void* x, void* out, int64_t T, c
     const int64_t n = T * L.H;
     f32_to_bf16_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(
         static_cast<const float*>(x), n, staged);
+    stage_done(L, 5, "stage_x_bf16");
     xb = staged;
   }
   hipError_t err;
@@ -280,6 +283,7 @@ hipError_t launch_prefill(const Layer& L, const void* x, void* out, int64_t T, c
     combine_kernel<true><<<gc, 256, 0, s>>>(yf, inv, w, L.k, H, out);
   else
     combine_kernel<false><<<gc, 256, 0, s>>>(yf, inv, w, L.k, H, out);
+  stage_done(L, 8, "combine");
   return hipGetLastError();
 }
 

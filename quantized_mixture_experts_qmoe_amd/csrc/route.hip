@@ -145,19 +145,23 @@ hipError_t launch_route(const Layer& L, const void* logits, int64_t T, char* ws,
   else
     route_topk_kernel<float><<<gt, 256, 0, s>>>(static_cast<const float*>(logits), T, E, k, topk_id,
                                                  topk_w);
+  stage_done(L, 1, "route_topk");
   const unsigned nc = static_cast<unsigned>(W.nchunks);
   int32_t* hist = reinterpret_cast<int32_t*>(ws + W.hist);
   route_hist_kernel<<<nc, 256, 0, s>>>(topk_id, W.R, E, hist);
+  stage_done(L, 2, "route_hist");
   route_scan_kernel<<<1, 1024, 0, s>>>(hist, W.nchunks, E, kTileM,
                                        reinterpret_cast<int32_t*>(ws + W.counts),
                                        reinterpret_cast<int32_t*>(ws + W.offsets),
                                        reinterpret_cast<int32_t*>(ws + W.chunk_base),
                                        reinterpret_cast<int4*>(ws + W.tiles),
                                        reinterpret_cast<int32_t*>(ws + W.num_tiles));
+  stage_done(L, 3, "route_scan");
   route_scatter_kernel<<<nc, 256, 0, s>>>(topk_id, W.R, E,
                                           reinterpret_cast<const int32_t*>(ws + W.chunk_base),
                                           reinterpret_cast<int32_t*>(ws + W.sorted_routes),
                                           reinterpret_cast<int32_t*>(ws + W.inv_pos));
+  stage_done(L, 4, "route_scatter");
   return hipGetLastError();
 }
 
