@@ -189,17 +189,21 @@ def bench_decode(T: int, steps: int, warmup: int):
     R = T * k
     fc1_bytes = D * fc1_b + T * H * 2 + T * E * 2 + R * I * 4
     layer_bytes = D * (fc1_b + fc2_b) + T * H * 2 * 2 + T * E * 2
-    t_fc1 = kt["decode_fc1_swiglu"] * 1e-3
-    t_fc2 = kt["decode_fc2_combine"] * 1e-3
-    fc2_bytes = D * fc2_b + R * I * 4 + 2 * R * H * 4 + T * H * 2
+    if "decode_fused" in kt:
+        # one kernel computes the whole layer: its roofline is the whole layer's bytes
+        dom = "decode_fused"
+        dom_bytes = layer_bytes + R * I * 4 * 2 + R * H * 4 * 2
+    else:
+        dom = "decode_fc1_swiglu"
+        dom_bytes = fc1_bytes
+    t_dom = kt[dom] * 1e-3
     return {
         "T": T, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
         "distinct_experts": D,
         "layer_GBs": layer_bytes / (ms * 1e-3) / 1e9,
         "layer_frac_hbm": layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "kernels_us": {kk: v * 1e3 for kk, v in kt.items()},
-        "fc1": {"bytes": fc1_bytes, "s": t_fc1, "GBs": fc1_bytes / t_fc1 / 1e9},
-        "fc2": {"bytes": fc2_bytes, "s": t_fc2, "GBs": fc2_bytes / t_fc2 / 1e9},
+        "dominant": {"kernel": dom, "bytes": dom_bytes, "s": t_dom, "GBs": dom_bytes / t_dom / 1e9},
     }
 
 
@@ -278,9 +282,9 @@ def main():
             {"workload": "decode M=1", "tokens_per_s": m1["tokens_per_s"],
              "ms_per_step": m1["ms_per_step"], "layer_frac_hbm": m1["layer_frac_hbm"],
              "distinct_experts": m1["distinct_experts"], "kernels_us": m1["kernels_us"],
-             "roofline": {"bound": "hbm", "kernel": "decode_fc1_swiglu",
-                          "achieved": m1["fc1"]["GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                          "frac": m1["fc1"]["GBs"] / HBM_PEAK_GBS}},
+             "roofline": {"bound": "hbm", "kernel": m1["dominant"]["kernel"],
+                          "achieved": m1["dominant"]["GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": m1["dominant"]["GBs"] / HBM_PEAK_GBS}},
             {"workload": "prefill 8192 tokens (16 packed sequences, Zipf-skewed routing)",
              "tokens_per_s": pf["tokens_per_s"], "ms_per_step": pf["ms_per_step"],
              "layer_frac_mfma": pf["layer_frac_mfma"], "kernels_us": pf["kernels_us"],
@@ -290,7 +294,7 @@ def main():
         ]
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_tokens)
 
-    fc1 = main_res["fc1"]
+    dom = main_res["dominant"]
     line = {
         "metric": METRIC,
         "value": main_res["tokens_per_s"],
@@ -310,9 +314,9 @@ def main():
                    "distinct_experts_per_step": main_res["distinct_experts"],
                    "layer_frac_hbm": main_res["layer_frac_hbm"],
                    "kernels_us": main_res["kernels_us"]},
-        "roofline": {"bound": "hbm", "kernel": "decode_fc1_swiglu", "achieved": fc1["GBs"],
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": fc1["GBs"] / HBM_PEAK_GBS,
-                     "traffic": None},
+        "roofline": {"bound": "hbm", "kernel": dom["kernel"], "achieved": dom["GBs"],
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dom["GBs"] / HBM_PEAK_GBS,
+                     "bytes_per_launch": dom["bytes"], "traffic": None},
         "cpu_baseline": cpu,
         "extra": extra,
     }

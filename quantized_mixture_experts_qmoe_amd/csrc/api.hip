@@ -18,6 +18,11 @@ struct qmoe_handle {
   qmoe::Layer L;
   int device;
   bool force_prefill;
+  bool split_decode;      // use the two-kernel decode even where the fused one applies
+  bool fused_ok;          // fused single-launch decode applies to this layer
+  int fused_grid;         // resident workgroups for the fused decode
+  uint32_t epoch;         // fused decode calls so far, times 2 (barrier epochs)
+  uint32_t* sync;         // device: barrier flags, release word, error flag
 };
 
 namespace qmoe {
@@ -185,6 +190,25 @@ qmoe_status qmoe_create(const qmoe_config* c, const qmoe_weights* w, int device,
   h->device = device;
   const char* force = getenv("QMOE_FORCE_PATH");
   h->force_prefill = force && strcmp(force, "prefill") == 0;
+  h->split_decode = force && strcmp(force, "decode_split") == 0;
+  h->sync = nullptr;
+  h->epoch = 0;
+  h->fused_ok = false;
+  h->fused_grid = 0;
+  {
+    DeviceGuard guard(device);
+    if (!guard.ok()) { delete h; return QMOE_ERR_HIP; }
+    if (hipMalloc(reinterpret_cast<void**>(&h->sync), kSyncBytes) != hipSuccess ||
+        hipMemset(h->sync, 0, kSyncBytes) != hipSuccess) {
+      if (h->sync) (void)hipFree(h->sync);
+      delete h;
+      return QMOE_ERR_HIP;
+    }
+    if (fused_decode_supported(L)) {
+      h->fused_grid = fused_decode_grid(L, device);
+      h->fused_ok = h->fused_grid > 0;
+    }
+  }
   *out = h;
   return QMOE_OK;
 }
@@ -218,7 +242,13 @@ qmoe_status qmoe_forward(qmoe_handle* h, const void* x, const void* logits, void
   stage_done(h->L, 0, "start");
   if (use_decode_path(h->L, h->force_prefill, T)) {
     const Workspace W = layout(h->L, T, true);
-    err = launch_decode(h->L, x, logits, out, T, base, W, s);
+    if (h->fused_ok && !h->split_decode)
+    {
+      err = launch_decode_fused(h->L, x, logits, out, T, base, W, h->sync, h->epoch, h->fused_grid, s);
+      h->epoch += 2;
+    }
+    else
+      err = launch_decode(h->L, x, logits, out, T, base, W, s);
   } else {
     const Workspace W = layout(h->L, T, false);
     err = launch_route(h->L, logits, T, base, W, s);
@@ -269,6 +299,11 @@ qmoe_status qmoe_set_stage_hook(qmoe_handle* h, qmoe_stage_fn fn, void* user) {
 }
 
 qmoe_status qmoe_destroy(qmoe_handle* h) {
+  if (!h) return QMOE_OK;
+  if (h->sync) {
+    DeviceGuard guard(h->device);
+    (void)hipFree(h->sync);
+  }
   delete h;
   return QMOE_OK;
 }

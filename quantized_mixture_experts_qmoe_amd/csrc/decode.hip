@@ -40,29 +40,6 @@ struct XFloats {
   float sum[UPL];
 };
 
-// Activation unit (32 bf16 values at x) -> pairs matching unit_pair<BITS>.
-template <int BITS>
-__device__ __forceinline__ void load_x_pairs(const uint16_t* x, int zp, uint32_t (&pairs)[16],
-                                             float& corr) {
-  uint32_t v[16];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    uint4 c = reinterpret_cast<const uint4*>(x)[q];
-    v[4 * q + 0] = c.x; v[4 * q + 1] = c.y; v[4 * q + 2] = c.z; v[4 * q + 3] = c.w;
-  }
-  float sum = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) sum += bf16_to_f32((v[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
-#pragma unroll
-  for (int p = 0; p < 16; ++p) {
-    const int a = pair_a(BITS, p), b = pair_b(BITS, p);
-    const uint32_t xa = (v[a >> 1] >> (16 * (a & 1))) & 0xFFFFu;
-    const uint32_t xb = (v[b >> 1] >> (16 * (b & 1))) & 0xFFFFu;
-    pairs[p] = xa | (xb << 16);
-  }
-  corr = -(1.0f + static_cast<float>(zp) * (1.0f / 128.0f)) * sum;
-}
-
 // sum((q - zp) * x) / 128 over one unit, bf16 activations.
 template <int BITS>
 __device__ __forceinline__ float unit_dot_pairs(const uint32_t (&wp)[16], const uint32_t (&xp)[16],

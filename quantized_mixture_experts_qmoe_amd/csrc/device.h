@@ -23,6 +23,15 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
+// Two fp32 -> packed bf16 pair (low half = a) with the hardware conversion
+// (v_cvt_pk_bf16_f32, round to nearest even).
+typedef __bf16 bf16x2_hw_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_hw_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
+  const f32x2_hw_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_hw_t));
+}
+
 __device__ __forceinline__ float half_to_f32(uint16_t h) {
   return static_cast<float>(__builtin_bit_cast(_Float16, h));
 }
@@ -113,6 +122,29 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
                                          __builtin_bit_cast(bf16x2_t, b), acc, false);
 }
 
+// Activation unit (32 bf16 values at x) -> pairs matching unit_pair<BITS>.
+template <int BITS>
+__device__ __forceinline__ void load_x_pairs(const uint16_t* x, int zp, uint32_t (&pairs)[16],
+                                             float& corr) {
+  uint32_t v[16];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint4 c = reinterpret_cast<const uint4*>(x)[q];
+    v[4 * q + 0] = c.x; v[4 * q + 1] = c.y; v[4 * q + 2] = c.z; v[4 * q + 3] = c.w;
+  }
+  float sum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) sum += bf16_to_f32((v[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+#pragma unroll
+  for (int p = 0; p < 16; ++p) {
+    const int a = pair_a(BITS, p), b = pair_b(BITS, p);
+    const uint32_t xa = (v[a >> 1] >> (16 * (a & 1))) & 0xFFFFu;
+    const uint32_t xb = (v[b >> 1] >> (16 * (b & 1))) & 0xFFFFu;
+    pairs[p] = xa | (xb << 16);
+  }
+  corr = -(1.0f + static_cast<float>(zp) * (1.0f / 128.0f)) * sum;
+}
+
 // ---------------------------------------------------------------- reductions
 
 __device__ __forceinline__ float group_sum(float v, int width) {
@@ -149,6 +181,84 @@ __device__ __forceinline__ float key_value(uint64_t key) {
 
 __device__ __forceinline__ int key_expert(uint64_t key) {
   return static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(key));
+}
+
+// ---------------------------------------------------------------- DPP max
+//
+// Wave-wide maximum of 64-bit keys with DPP moves (no LDS traffic): rotate
+// within each row of 16 lanes by 8, 4, 2, 1, then fold rows with the row
+// broadcasts of lanes 15 and 31; lane 63 ends with the maximum, which is then
+// read as a uniform value.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ void dpp_max_step(uint32_t& hi, uint32_t& lo) {
+  const uint32_t phi = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+      static_cast<int>(hi), static_cast<int>(hi), CTRL, ROWS, 0xF, false));
+  const uint32_t plo = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+      static_cast<int>(lo), static_cast<int>(lo), CTRL, ROWS, 0xF, false));
+  const bool take = (phi > hi) | ((phi == hi) & (plo > lo));
+  hi = take ? phi : hi;
+  lo = take ? plo : lo;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t key) {
+  uint32_t hi = static_cast<uint32_t>(key >> 32), lo = static_cast<uint32_t>(key);
+  dpp_max_step<0x128, 0xF>(hi, lo);   // row_ror:8
+  dpp_max_step<0x124, 0xF>(hi, lo);   // row_ror:4
+  dpp_max_step<0x122, 0xF>(hi, lo);   // row_ror:2
+  dpp_max_step<0x121, 0xF>(hi, lo);   // row_ror:1
+  dpp_max_step<0x142, 0xA>(hi, lo);   // row_bcast:15 into rows 1 and 3
+  dpp_max_step<0x143, 0xC>(hi, lo);   // row_bcast:31 into rows 2 and 3
+  const uint32_t h = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(hi), 63));
+  const uint32_t l = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(lo), 63));
+  return (static_cast<uint64_t>(h) << 32) | l;
+}
+
+// Top-k of one token by one wavefront: k rounds of a DPP argmax over 64-bit
+// keys (ordered logit, then lower expert index), then the softmax over the k
+// selected logits. vals: the token's E logits (-0 folded into +0), e.g. in LDS.
+// Lanes j < k write ids[j] and w[j].
+template <int kC>
+__device__ __forceinline__ void topk_softmax_dpp_n(const float* vals, int E, int k, int lane,
+                                                   int32_t* ids, float* w) {
+  uint64_t keys[kC];
+  const int nc = (E + kWave - 1) / kWave;
+#pragma unroll
+  for (int c = 0; c < kC; ++c) {
+    const int e = lane + kWave * c;
+    keys[c] = (c < nc && e < E) ? route_key(vals[e], static_cast<uint32_t>(e)) : 0ull;
+  }
+  int my_id = 0;
+  float my_v = 0.0f, v0 = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = keys[0];
+#pragma unroll
+    for (int c = 1; c < kC; ++c) best = keys[c] > best ? keys[c] : best;
+    best = wave_max_u64(best);
+    const int e = key_expert(best);
+    const float v = key_value(best);
+    if (j == 0) v0 = v;
+    if (lane == j) { my_id = e; my_v = v; }
+#pragma unroll
+    for (int c = 0; c < kC; ++c)
+      if (keys[c] == best) keys[c] = 0ull;
+  }
+  const float ex = (lane < k) ? expf(my_v - v0) : 0.0f;
+  const float sum = wave_sum(ex);
+  if (lane < k) {
+    ids[lane] = my_id;
+    w[lane] = ex / sum;
+  }
+}
+
+// Dispatch on the expert count so each lane carries only the key slots it needs.
+__device__ __forceinline__ void topk_softmax_dpp(const float* vals, int E, int k, int lane,
+                                                 int32_t* ids, float* w) {
+  if (E <= 2 * kWave)
+    topk_softmax_dpp_n<2>(vals, E, k, lane, ids, w);
+  else if (E <= 4 * kWave)
+    topk_softmax_dpp_n<4>(vals, E, k, lane, ids, w);
+  else
+    topk_softmax_dpp_n<kMaxExperts / kWave>(vals, E, k, lane, ids, w);
 }
 
 // One wavefront selects the top-k experts of one token and computes the
@@ -190,6 +300,56 @@ __device__ __forceinline__ void topk_softmax_wave(const ACT* logits, int E, int 
     ids[lane] = my_id;
     w[lane] = ex / sum;
   }
+}
+
+// Top-k by rank, one wavefront per token, no serial dependency between
+// slots: rank(e) = #{e' : l[e'] > l[e] or (l[e'] == l[e] and e' < e)} over
+// the logits staged in LDS (vals, E floats, -0 already folded into +0); the
+// expert of rank j < k goes to slot j. Then the softmax over the k selected
+// logits. Lanes j < k write ids[j] and w[j].
+__device__ __forceinline__ float canon_logit(float v) { return v == 0.0f ? 0.0f : v; }
+
+__device__ __forceinline__ void topk_softmax_rank(const float* vals, int E, int k, int lane,
+                                                  int32_t* ids, float* w, float* selv) {
+  // E is padded to a multiple of 4 in LDS with -inf (never selected before a
+  // real expert because ties go to the lower index and every real logit is
+  // >= -inf). Each lane ranks up to kMaxExperts / 64 candidates at once.
+  constexpr int kC = kMaxExperts / kWave;
+  const int E4 = (E + 3) & ~3;
+  float v[kC];
+  int rank[kC];
+#pragma unroll
+  for (int c = 0; c < kC; ++c) {
+    const int e = lane + kWave * c;
+    v[c] = (e < E) ? vals[e] : 0.0f;
+    rank[c] = 0;
+  }
+  const int nc = (E + kWave - 1) / kWave;
+#pragma unroll 4
+  for (int q = 0; q < E4; q += 4) {
+    const float4 u = *reinterpret_cast<const float4*>(vals + q);
+#pragma unroll
+    for (int c = 0; c < kC; ++c) {
+      if (c >= nc) break;
+      const int e = lane + kWave * c;
+      rank[c] += ((u.x > v[c]) | ((u.x == v[c]) & (q < e))) + ((u.y > v[c]) | ((u.y == v[c]) & (q + 1 < e))) +
+                 ((u.z > v[c]) | ((u.z == v[c]) & (q + 2 < e))) + ((u.w > v[c]) | ((u.w == v[c]) & (q + 3 < e)));
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < kC; ++c) {
+    const int e = lane + kWave * c;
+    if (c < nc && e < E && rank[c] < k) {
+      ids[rank[c]] = e;
+      selv[rank[c]] = v[c];
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  const float v0 = selv[0];
+  const float ex = (lane < k) ? expf(selv[lane < k ? lane : 0] - v0) : 0.0f;
+  const float sum = wave_sum(ex);
+  if (lane < k) w[lane] = ex / sum;
 }
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }

@@ -71,6 +71,16 @@ hipError_t launch_prefill(const Layer& L, const void* x, void* out, int64_t T, c
                           const Workspace& W, hipStream_t s);
 hipError_t launch_decode(const Layer& L, const void* x, const void* logits, void* out, int64_t T,
                          char* ws, const Workspace& W, hipStream_t s);
+// Fused single-launch decode (bf16 activations, H <= 2048, I <= 1024). Its
+// grid barriers use a per-handle device buffer of flags (zeroed at create)
+// and a per-call epoch.
+constexpr int kFusedMaxWorkgroups = 1024;
+constexpr size_t kSyncBytes = 8192;                    // >= (64 + kFusedMaxWorkgroups) words
+bool fused_decode_supported(const Layer& L);
+int fused_decode_grid(const Layer& L, int device);
+hipError_t launch_decode_fused(const Layer& L, const void* x, const void* logits, void* out,
+                               int64_t T, char* ws, const Workspace& W, uint32_t* sync,
+                               uint32_t epoch, int grid, hipStream_t s);
 hipError_t launch_dequant(const Layer& L, int fc, int64_t expert, float* out_f32,
                           uint16_t* out_bf16, hipStream_t s);
 

@@ -139,6 +139,46 @@ def test_decode_fp32_activations_formats():
         check_decode(wl, layer_for(wl, 16))
 
 
+@pytest.mark.parametrize("name,T", [("decode", 1), ("decode", 4), ("int3", 4), ("stack", 1)])
+def test_fused_decode_matches_split_decode(name, T):
+    """The single-launch decode and the two-kernel decode compute the same
+    layer in fp32 with different summation orders."""
+    wl = qi.make_workload(name, T=T)
+    a = check_decode(wl, layer_for(wl, 16))
+    os.environ["QMOE_FORCE_PATH"] = "decode_split"
+    try:
+        ls = layer_for(wl, 16)
+    finally:
+        del os.environ["QMOE_FORCE_PATH"]
+    b = check_decode(wl, ls)
+    d = (a.float() - b.float()).abs().max().item()
+    scale = a.float().abs().max().item()
+    assert d <= 2 ** -7 * scale, (d, scale)
+
+
+def test_decode_back_to_back_calls_reuse_sync_state():
+    """The fused decode's barrier flags carry a per-call epoch and all data
+    crossing workgroups goes through coherent loads and stores: many calls in
+    a row, rotating over three layers with different token counts, must each
+    match that layer's first result bit for bit (stale data from the previous
+    call would show up as a mismatch)."""
+    cases = [qi.make_workload("decode", T=4), qi.make_workload("decode", T=1, seed=77),
+             qi.make_workload("decode", T=3, seed=78)]
+    layers = [layer_for(wl, 16) for wl in cases]
+    inputs = [(wl.tokens.x.to(DEV), wl.tokens.logits.to(DEV)) for wl in cases]
+    refs = []
+    for L, (x, g) in zip(layers, inputs):
+        refs.append(L(x, g).clone())
+        torch.cuda.synchronize()
+    outs = []
+    for r in range(60):
+        i = r % 3
+        outs.append((i, layers[i](inputs[i][0], inputs[i][1])))
+    torch.cuda.synchronize()
+    for i, o in outs:
+        assert torch.equal(o.view(torch.int16), refs[i].view(torch.int16)), i
+
+
 def test_decode_repeated_experts_across_tokens():
     """Four tokens with identical logits share all k experts: each expert is
     streamed once and serves every token."""
