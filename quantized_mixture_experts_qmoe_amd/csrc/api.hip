@@ -21,8 +21,8 @@ struct qmoe_handle {
   bool split_decode;      // use the two-kernel decode even where the fused one applies
   bool fused_ok;          // fused single-launch decode applies to this layer
   int fused_grid;         // resident workgroups for the fused decode
-  uint32_t epoch;         // fused decode calls so far, times 2 (barrier epochs)
-  uint32_t* sync;         // device: barrier flags, release word, error flag
+  uint32_t calls;         // epoch of the last fused decode call launched (0: none yet)
+  void* xbuf;             // device: fused decode exchange buffer (error bits, tagged h and y)
 };
 
 namespace qmoe {
@@ -191,22 +191,33 @@ qmoe_status qmoe_create(const qmoe_config* c, const qmoe_weights* w, int device,
   const char* force = getenv("QMOE_FORCE_PATH");
   h->force_prefill = force && strcmp(force, "prefill") == 0;
   h->split_decode = force && strcmp(force, "decode_split") == 0;
-  h->sync = nullptr;
-  h->epoch = 0;
+  h->xbuf = nullptr;
+  h->calls = 0;
   h->fused_ok = false;
   h->fused_grid = 0;
   {
     DeviceGuard guard(device);
     if (!guard.ok()) { delete h; return QMOE_ERR_HIP; }
-    if (hipMalloc(reinterpret_cast<void**>(&h->sync), kSyncBytes) != hipSuccess ||
-        hipMemset(h->sync, 0, kSyncBytes) != hipSuccess) {
-      if (h->sync) (void)hipFree(h->sync);
-      delete h;
-      return QMOE_ERR_HIP;
-    }
     if (fused_decode_supported(L)) {
+      const size_t xb = fused_exchange_bytes(L);
+      if (hipMalloc(&h->xbuf, xb) != hipSuccess || hipMemset(h->xbuf, 0, xb) != hipSuccess) {
+        if (h->xbuf) (void)hipFree(h->xbuf);
+        delete h;
+        return QMOE_ERR_HIP;
+      }
       h->fused_grid = fused_decode_grid(L, device);
+      // QMOE_FUSED_GRID=n caps the fused decode grid at n workgroups (n >= 1),
+      // e.g. to exercise its many-experts-per-workgroup schedule
+      const char* cap = getenv("QMOE_FUSED_GRID");
+      if (cap) {
+        const long n = strtol(cap, nullptr, 10);
+        if (n >= 1 && n < h->fused_grid) h->fused_grid = static_cast<int>(n);
+      }
       h->fused_ok = h->fused_grid > 0;
+      // QMOE_FUSED_EPOCH_START=n makes the first fused call use epoch n + 1
+      // (with n = 4294967295 the first call takes the wrap path)
+      const char* e0 = getenv("QMOE_FUSED_EPOCH_START");
+      if (e0) h->calls = static_cast<uint32_t>(strtoul(e0, nullptr, 10));
     }
   }
   *out = h;
@@ -242,13 +253,22 @@ qmoe_status qmoe_forward(qmoe_handle* h, const void* x, const void* logits, void
   stage_done(h->L, 0, "start");
   if (use_decode_path(h->L, h->force_prefill, T)) {
     const Workspace W = layout(h->L, T, true);
-    if (h->fused_ok && !h->split_decode)
-    {
-      err = launch_decode_fused(h->L, x, logits, out, T, base, W, h->sync, h->epoch, h->fused_grid, s);
-      h->epoch += 2;
-    }
-    else
+    if (h->fused_ok && !h->split_decode) {
+      // epochs 1, 2, ...; when the counter wraps the exchange buffer is
+      // zeroed again first, so no entry can carry a reused epoch. A call
+      // that did not launch does not use up its epoch.
+      uint32_t epoch = h->calls + 1u;
+      err = hipSuccess;
+      if (epoch == 0u) {
+        epoch = 1u;
+        err = clear_exchange(h->L, h->xbuf, s);
+      }
+      if (err == hipSuccess)
+        err = launch_decode_fused(h->L, x, logits, out, T, base, W, h->xbuf, epoch, h->fused_grid, s);
+      if (err == hipSuccess) h->calls = epoch;
+    } else {
       err = launch_decode(h->L, x, logits, out, T, base, W, s);
+    }
   } else {
     const Workspace W = layout(h->L, T, false);
     err = launch_route(h->L, logits, T, base, W, s);
@@ -300,9 +320,9 @@ qmoe_status qmoe_set_stage_hook(qmoe_handle* h, qmoe_stage_fn fn, void* user) {
 
 qmoe_status qmoe_destroy(qmoe_handle* h) {
   if (!h) return QMOE_OK;
-  if (h->sync) {
+  if (h->xbuf) {
     DeviceGuard guard(h->device);
-    (void)hipFree(h->sync);
+    (void)hipFree(h->xbuf);
   }
   delete h;
   return QMOE_OK;

@@ -1,35 +1,47 @@
-// Fused decode path (1..4 tokens, bf16 activations): one kernel launch.
+// Fused decode path (1..4 tokens, bf16 activations): one kernel launch with
+// no grid-wide barrier.
 //
 // Phases (one workgroup of 8 waves per CU; the grid is the number of
 // workgroups that fit on the device at once, so all are resident):
-//   0. routing of the <= 4 tokens, recomputed by every workgroup: a parallel
-//      rank-based top-k over raw logits and the softmax over the selected k;
-//      the list of distinct experts and, per expert, each token's slot;
+//   0. routing of the <= 4 tokens, recomputed by every workgroup: wave t
+//      takes token t's logits straight into registers as 32-bit keys
+//      (ordered bf16 logit, then the inverted expert index) and selects the
+//      k largest with DPP max reductions, then the softmax over the selected;
+//      the distinct experts, in ascending expert order, come from an LDS
+//      bitmask;
 //   1. FC1 + SwiGLU: items of two gate rows and the two matching up rows of
-//      one expert, dealt to the waves in contiguous ranges. Before computing,
-//      each wave issues the loads of its first two FC2 items;
-//   2. grid barrier;
-//   3. FC2: items of eight output rows of one expert, contiguous per wave.
-//      Each workgroup stages the h of the expert(s) its waves need in LDS as
-//      bf16 hi/lo pairs (converted once per workgroup);
-//   4. grid barrier;
-//   5. combine: every token's k slots summed in slot order (fp32), rounded
-//      once, spread over all threads of the grid.
+//      one expert, dealt to the waves in contiguous ranges. Each wave issues
+//      the loads of its first two FC1 items and its first two FC2 items
+//      before computing anything, keeps two items in flight, buffers its h
+//      values in LDS and writes them out once; right after its last FC1 item
+//      it issues the loads of its third and fourth FC2 items;
+//   2. FC2: a workgroup works on one expert (or, with more experts than
+//      workgroups, on whole experts in turn). It stages the expert's h in LDS
+//      as bf16 hi/lo pairs, waiting for each value to arrive, and its waves
+//      compute items of eight output rows, buffered in LDS and written once;
+//   3. combine: each group of eight output rows has one combining wave, which
+//      waits for the group's y values of every token slot, sums each token's
+//      k slots in slot order in fp32 and rounds once.
 //
-// Cross-workgroup data (h, y) moves only through agent-scope atomic loads and
-// stores (global_load/store with sc1), which are coherent per location at
-// device scope across the XCDs' separate L2 caches. A barrier arrival waits
-// for the workgroup's own stores to complete (s_waitcnt) before it publishes
-// its flag, so no cache write-back or invalidate is needed. Barriers are one
-// flag per workgroup plus a release word, tagged with a per-call epoch.
+// Cross-workgroup data (h, y) lives in a buffer the handle owns, as 64-bit
+// entries {fp32 value, epoch} written and read with single agent-scope atomic
+// stores and loads (global_store/load_dwordx2 with sc1), which are coherent
+// per location at device scope across the XCDs' separate L2 caches. A
+// consumer spins on the entries themselves until every one it needs carries
+// this call's epoch, so a value becomes usable one memory round trip after it
+// is stored: no flag, no fence, no read-modify-write atomic. Each call has a
+// new nonzero epoch; the buffer is zeroed at create and again when the epoch
+// counter wraps, so no entry can hold a matching epoch before this call's
+// producer writes it. Waits are bounded: a wait that runs out sets an error
+// bit and goes on.
 //
 // Matrix cores: v_mfma_f32_4x4x4_16b_bf16 works on 16 independent 4x4 blocks;
 // block b (lanes 4b..4b+3) multiplies A_b (lane 4b+i holds token i's four
 // k-values) by B_b (lane 4b+j holds four k-values of weight row j) and lane
 // 4b+j receives D_b[token i][row j] in element i, so with four tokens every
 // lane does useful work. FC1 gives the 16 blocks 16 different quant blocks of
-// four rows; FC2 gives them 8 quant blocks x 2 sets of four rows. One 16-byte
-// unit of 32 INT4 codes feeds eight consecutive MFMAs of one block.
+// four rows; FC2 gives them 8 quant blocks x 2 sets of four rows. One unit of
+// 32 codes feeds eight consecutive MFMAs of one block.
 //
 // Exactness: each code enters as the bf16 value 1 + q/128 (its bits OR-ed
 // into the mantissa of 1.0); the block sum is then
@@ -57,13 +69,13 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kFusedWaves = 8;
 constexpr int kFusedThreads = kFusedWaves * kWave;
-constexpr uint32_t kSpinLimit = 1u << 24;   // bounded barrier wait (then flag and go on)
-constexpr int kMaxI32 = 32;                  // FC2 quant blocks staged (I <= 1024)
-
-// sync buffer words
-constexpr int kSyncError = 0;
-constexpr int kSyncRelease = 32;
-constexpr int kSyncFlags = 64;
+constexpr int kKeySlots = kFusedMaxExperts / kWave;   // logits per lane in the top-k
+constexpr int kMaxRoutes = kDecodeMaxTokens * kMaxTopK;
+constexpr int kMaxGroups = 256;                       // output row groups of 8 (H <= 2048)
+constexpr int kMaxI32 = 32;                           // FC2 quant blocks staged (I <= 1024)
+constexpr int kCap1 = 32;                             // FC1 items buffered per wave (even)
+constexpr int kCap2 = 16;                             // FC2 items buffered per wave (multiple of 4)
+constexpr uint32_t kSpinLimit = 1u << 20;             // bounded wait for an exchange entry
 
 __device__ __forceinline__ f32x4_t mfma4(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1,
                                          f32x4_t c) {
@@ -72,26 +84,61 @@ __device__ __forceinline__ f32x4_t mfma4(uint32_t a0, uint32_t a1, uint32_t b0, 
   return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ void store_coherent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Exchange entries: {fp32 value (low word), epoch (high word)}.
+__device__ __forceinline__ void put_tagged(uint64_t* p, float v, uint32_t epoch) {
+  const uint64_t e = (static_cast<uint64_t>(epoch) << 32) | __float_as_uint(v);
+  __hip_atomic_store(p, e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float load_coherent(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ uint64_t get_tagged(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint32_t load_flag(const uint32_t* p) {
-  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ bool tag_is(uint64_t e, uint32_t epoch) {
+  return static_cast<uint32_t>(e >> 32) == epoch;
+}
+__device__ __forceinline__ float tag_value(uint64_t e) {
+  return __uint_as_float(static_cast<uint32_t>(e));
+}
+
+// Routing key of a bf16 logit: the order-preserving 16-bit image of the value
+// (-0 folded into +0) above the inverted expert index, so the largest key is
+// the largest logit and, among equal logits, the lowest expert index.
+__device__ __forceinline__ uint32_t logit_key(uint32_t b, int e) {
+  b = (b == 0x8000u) ? 0u : b;
+  const uint32_t ord = (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u);
+  return (ord << 16) | (0xFFFFu - static_cast<uint32_t>(e));
+}
+__device__ __forceinline__ float key_logit(uint32_t key) {
+  const uint32_t ord = key >> 16;
+  return bf16_to_f32((ord & 0x8000u) ? (ord & 0x7FFFu) : (~ord & 0xFFFFu));
+}
+__device__ __forceinline__ int key_to_expert(uint32_t key) {
+  return 0xFFFF - static_cast<int>(key & 0xFFFFu);
+}
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_umax(uint32_t v) {
+  const uint32_t p = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+      static_cast<int>(v), static_cast<int>(v), CTRL, ROWS, 0xF, false));
+  return p > v ? p : v;
+}
+
+// Maximum over the wavefront, returned uniformly.
+__device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
+  v = dpp_umax<0x128, 0xF>(v);   // row_ror:8
+  v = dpp_umax<0x124, 0xF>(v);   // row_ror:4
+  v = dpp_umax<0x122, 0xF>(v);   // row_ror:2
+  v = dpp_umax<0x121, 0xF>(v);   // row_ror:1
+  v = dpp_umax<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+  v = dpp_umax<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
 }
 
 struct FusedLds {
-  float logits[kDecodeMaxTokens][kMaxExperts + 4];
-  float selv[kDecodeMaxTokens][kMaxTopK];
-  int32_t ids[kDecodeMaxTokens * kMaxTopK];
-  float w[kDecodeMaxTokens * kMaxTopK];
-  int32_t firstr[kMaxExperts];                  // expert -> its first route
-  int nfirst[2];
-  int32_t dindex[kDecodeMaxTokens * kMaxTopK];  // first route -> distinct index
-  int32_t dlist[kDecodeMaxTokens * kMaxTopK];   // distinct index -> expert
-  int32_t dslot[kDecodeMaxTokens * kMaxTopK][kDecodeMaxTokens];
+  int32_t ids[kMaxRoutes];                            // route r = t*k + j -> expert
+  float w[kMaxRoutes];                                // routing weight of route r
+  uint32_t emask[kFusedMaxExperts / 32];              // experts selected by any token
+  int8_t slot[kDecodeMaxTokens][kFusedMaxExperts];    // (token, expert) -> slot, or -1
+  int32_t dlist[kMaxRoutes];                          // distinct index -> expert (ascending)
   int nd;
   // FC2 A operand of one expert, in register order: unit c, 16-byte chunk j
   // (pairs 4j..4j+3), lane l (token l & 3, quant block (l >> 2) + 8c; lanes
@@ -101,45 +148,10 @@ struct FusedLds {
   uint4 ahi[kMaxI32 / 8][4][32];
   uint4 alo[kMaxI32 / 8][4][32];
   float hsum[kDecodeMaxTokens][kMaxI32];
+  // per-wave result buffers: h [token][2 * item + row], y [token][8 * item + row]
+  float hbuf[kFusedWaves][kDecodeMaxTokens][2 * kCap1];
+  float ybuf[kFusedWaves][kDecodeMaxTokens][8 * kCap2];
 };
-
-// Grid barrier: every workgroup publishes `epoch` in its flag after its own
-// coherent stores have completed; workgroup 0 waits for all flags and then
-// publishes `epoch` in the release word, which the others wait for.
-__device__ void flag_barrier(uint32_t* sync, uint32_t epoch) {
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0)
-    __hip_atomic_store(sync + kSyncFlags + blockIdx.x, epoch, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-  if (blockIdx.x == 0) {
-    if (threadIdx.x < kWave) {
-      for (int i = threadIdx.x; i < static_cast<int>(gridDim.x); i += kWave) {
-        uint32_t spins = 0;
-        while (load_flag(sync + kSyncFlags + i) != epoch) {
-          if (++spins > kSpinLimit) {
-            atomicOr(sync + kSyncError, 1u);
-            break;
-          }
-          __builtin_amdgcn_s_sleep(1);
-        }
-      }
-    }
-    __syncthreads();
-    if (threadIdx.x == 0)
-      __hip_atomic_store(sync + kSyncRelease, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  } else if (threadIdx.x == 0) {
-    uint32_t spins = 0;
-    while (load_flag(sync + kSyncRelease) != epoch) {
-      if (++spins > kSpinLimit) {
-        atomicOr(sync + kSyncError, 2u);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-    }
-  }
-  __syncthreads();
-}
 
 // Share value v of lane (lane & ~3) | t with the four lanes of each block.
 __device__ __forceinline__ float quad_get(float v, int lane, int t) {
@@ -151,7 +163,7 @@ __device__ __forceinline__ float quad_get(float v, int lane, int t) {
 struct FusedArgs {
   const uint16_t* x;
   const uint16_t* logits;
-  void* out;
+  uint16_t* out;
   const uint8_t* c1;
   const uint16_t* s1;
   const uint8_t* c2;
@@ -160,37 +172,36 @@ struct FusedArgs {
   int64_t rb1, rb2, nb1, nb2;
   int32_t* ws_ids;
   float* ws_w;
-  float* h32;
-  float* y32;
-  uint32_t* sync;
-  uint32_t epoch;   // this call uses epoch + 1 and epoch + 2
+  uint64_t* hx;      // exchange: h [route][inter]
+  uint64_t* yx;      // exchange: y [route][hidden]
+  uint32_t* err;     // error bits (bounded waits that ran out)
+  uint32_t epoch;    // nonzero; no exchange entry holds it before this call writes it
 };
 
 // U1: FC1 quant blocks per lane (ceil(H/32 / 16)); U2: FC2 quant blocks per lane (ceil(I/32 / 8)).
 template <int BITS, int U1, int U2>
 __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a) {
   __shared__ FusedLds S;
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  // wave-uniform values go through readfirstlane so the compiler keeps them
+  // (and the loops over them) scalar
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int gw = blockIdx.x * kFusedWaves + wave, NW = gridDim.x * kFusedWaves;
   const int T = a.T, k = a.k, H = a.H, I = a.I, E = a.E, zp = a.zp, bs = a.bs;
   const int R = T * k;
   const int blk = lane >> 2, q4 = lane & 3;   // MFMA block and lane-in-block
   const float zc = 128.0f + static_cast<float>(zp);
 
-  // ---- logits to LDS and x for the FC1 A operand (neither needs routing)
-  // logits: loaded into registers first, written to LDS after the x loads are issued
-  const int E4 = (E + 3) & ~3;
-  constexpr int kLg = (kDecodeMaxTokens * (kMaxExperts + 4) + kFusedThreads - 1) / kFusedThreads;
-  uint16_t lg[kLg];
+  // ---- loads that need no routing: token `wave`'s logits, then x (FC1 A
+  // operand); all addresses clamped in range, values masked afterwards
+  uint16_t lg[kKeySlots];
+  if (wave < T) {
 #pragma unroll
-  for (int q = 0; q < kLg; ++q) {
-    const int i = threadIdx.x + q * kFusedThreads;
-    const int t = i / E4, e = i % E4;
-    const bool ok = i < T * E4 && e < E;
-    lg[q] = a.logits[ok ? static_cast<int64_t>(t) * E + e : 0];
+    for (int c = 0; c < kKeySlots; ++c) {
+      const int e = lane + kWave * c;
+      lg[c] = a.logits[static_cast<int64_t>(wave) * E + (e < E ? e : 0)];
+    }
   }
-  // x: every lane issues all of its loads before consuming any (clamped
-  // addresses, zeroed afterwards when out of range)
   const int nkb1 = H / 32;
   uint4 xraw[U1][4];
 #pragma unroll
@@ -201,50 +212,144 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
 #pragma unroll
     for (int q = 0; q < 4; ++q) xraw[c][q] = src[q];
   }
-#pragma unroll
-  for (int q = 0; q < kLg; ++q) {
-    const int i = threadIdx.x + q * kFusedThreads;
-    const int t = i / E4, e = i % E4;
-    if (i < T * E4) S.logits[t][e] = (e < E) ? canon_logit(bf16_to_f32(lg[q])) : -__builtin_inff();
-  }
-  for (int i = threadIdx.x; i < R; i += kFusedThreads)
-#pragma unroll
-    for (int t = 0; t < kDecodeMaxTokens; ++t) S.dslot[i][t] = -1;
+  if (threadIdx.x < kDecodeMaxTokens * kFusedMaxExperts / 4)
+    reinterpret_cast<uint32_t*>(&S.slot[0][0])[threadIdx.x] = 0xFFFFFFFFu;
+  if (threadIdx.x < kFusedMaxExperts / 32) S.emask[threadIdx.x] = 0u;
   __syncthreads();
 
   // ---- routing: wave t selects token t's experts
-  if (wave < T) topk_softmax_dpp(S.logits[wave], E, k, lane, S.ids + wave * k, S.w + wave * k);
-  __syncthreads();
-  // distinct experts in first-occurrence order: the first route of each
-  // expert from an LDS min table, its index from ballots over the (<= 128) routes
-  {
-    const int r = threadIdx.x;
-    const int e = (r < R) ? S.ids[r] : 0;
-    if (r < R) S.firstr[e] = R;
-    __syncthreads();
-    if (r < R) atomicMin(&S.firstr[e], r);
-    __syncthreads();
-    const bool is_first = (r < R) && (S.firstr[e] == r);
-    const uint64_t mask = __ballot(is_first);
-    if (lane == 0 && wave < 2) S.nfirst[wave] = __popcll(mask);
-    __syncthreads();
-    if (is_first) {
-      const int d = __popcll(mask & ((1ull << lane) - 1ull)) + (wave == 1 ? S.nfirst[0] : 0);
-      S.dindex[r] = d;
-      S.dlist[d] = e;
+  if (wave < T) {
+    uint32_t keys[kKeySlots];
+#pragma unroll
+    for (int c = 0; c < kKeySlots; ++c) {
+      const int e = lane + kWave * c;
+      keys[c] = (e < E) ? logit_key(lg[c], e) : 0u;
     }
-    __syncthreads();
-    if (r < R) S.dslot[S.dindex[S.firstr[e]]][r / k] = r % k;
-    if (threadIdx.x == 0) S.nd = S.nfirst[0] + (R > kWave ? S.nfirst[1] : 0);
+    uint32_t mine = 0u, first = 0u;
+    for (int j = 0; j < k; ++j) {
+      uint32_t b = keys[0];
+#pragma unroll
+      for (int c = 1; c < kKeySlots; ++c) b = keys[c] > b ? keys[c] : b;
+      b = wave_umax(b);
+      if (j == 0) first = b;
+      if (lane == j) mine = b;
+#pragma unroll
+      for (int c = 0; c < kKeySlots; ++c) keys[c] = (keys[c] == b) ? 0u : keys[c];
+    }
+    const float ex = (lane < k) ? expf(key_logit(mine) - key_logit(first)) : 0.0f;
+    const float sum = wave_sum(ex);
+    if (lane < k) {
+      const int e = key_to_expert(mine);
+      S.ids[wave * k + lane] = e;
+      S.w[wave * k + lane] = ex / sum;
+      S.slot[wave][e] = static_cast<int8_t>(lane);
+      atomicOr(&S.emask[e >> 5], 1u << (e & 31));
+    }
   }
   __syncthreads();
-  const int D = S.nd;
+  // distinct experts in ascending order: prefix of the mask words' popcounts
+  if (wave == 0) {
+    uint32_t m = (lane < (E + 31) / 32) ? S.emask[lane] : 0u;
+    const int pc = __popc(m);
+    int incl = pc;
+#pragma unroll
+    for (int off = 1; off < kFusedMaxExperts / 32; off <<= 1) {
+      const int o = __shfl_up(incl, off, kWave);
+      if (lane >= off) incl += o;
+    }
+    int pos = incl - pc;
+    while (m) {
+      S.dlist[pos++] = lane * 32 + (__ffs(m) - 1);
+      m &= m - 1u;
+    }
+    if (lane == kFusedMaxExperts / 32 - 1) S.nd = incl;
+  }
+  __syncthreads();
+  const int D = __builtin_amdgcn_readfirstlane(S.nd);
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i < R; i += kFusedThreads) {
       a.ws_ids[i] = S.ids[i];
       a.ws_w[i] = S.w[i];
     }
 
+  // ---- work ranges
+  // FC1: items (expert d, row pair p), contiguous per wave over the grid
+  const int g1 = I / 2;
+  const int n1 = D * g1;
+  const int i1_0 = static_cast<int>(static_cast<int64_t>(n1) * gw / NW);
+  const int i1_1 = static_cast<int>(static_cast<int64_t>(n1) * (gw + 1) / NW);
+  // FC2: items (expert d, group q of 8 output rows); a workgroup owns a slice
+  // of one expert when there are at least as many workgroups as experts,
+  // otherwise whole experts [dA, dB)
+  const int NG = gridDim.x;
+  const int g2 = H / 8;
+  int dA, dB, q0, q1;
+  if (D <= NG) {
+    dA = static_cast<int>(static_cast<int64_t>(blockIdx.x) * D / NG);
+    dB = dA + 1;
+    const int w_lo = static_cast<int>((static_cast<int64_t>(dA) * NG + D - 1) / D);
+    const int w_hi = static_cast<int>((static_cast<int64_t>(dA + 1) * NG + D - 1) / D);
+    const int nq = (w_hi - w_lo) * kFusedWaves, qw = (blockIdx.x - w_lo) * kFusedWaves + wave;
+    q0 = g2 * qw / nq;
+    q1 = g2 * (qw + 1) / nq;
+  } else {
+    dA = static_cast<int>(static_cast<int64_t>(blockIdx.x) * D / NG);
+    dB = static_cast<int>(static_cast<int64_t>(blockIdx.x + 1) * D / NG);
+    q0 = g2 * wave / kFusedWaves;
+    q1 = g2 * (wave + 1) / kFusedWaves;
+  }
+  const int nkb2 = I / 32;
+
+  // Loads of one item: branch-free (out-of-range quant blocks read unit 0 and
+  // get a zero scale when used); scales stay raw fp16 until used.
+  auto load_fc1 = [&](int it, UnitWords<BITS> (&wv)[U1], uint32_t (&sc)[U1]) {
+    const int e = S.dlist[it / g1];
+    const int n = 2 * (it % g1) + (q4 & 1);
+    const int row = (q4 < 2) ? n : I + n;
+    const uint8_t* rowp = a.c1 + (static_cast<int64_t>(e) * 2 * I + row) * a.rb1;
+    const uint16_t* srow = a.s1 + (static_cast<int64_t>(e) * 2 * I + row) * a.nb1;
+#pragma unroll
+    for (int c = 0; c < U1; ++c) {
+      const int kb = blk + 16 * c;
+      const int kbc = kb < nkb1 ? kb : 0;
+      wv[c] = load_unit<BITS>(rowp + kbc * (4 * BITS));
+      sc[c] = srow[(32 * kbc) / bs];
+    }
+  };
+  auto load_fc2 = [&](int d, int q, UnitWords<BITS> (&wv)[U2], uint32_t (&sc)[U2]) {
+    const int e = S.dlist[d];
+    const int m = q * 8 + (blk >= 8 ? 4 : 0) + q4;
+    const uint8_t* rowp = a.c2 + (static_cast<int64_t>(e) * H + m) * a.rb2;
+    const uint16_t* srow = a.s2 + (static_cast<int64_t>(e) * H + m) * a.nb2;
+#pragma unroll
+    for (int c = 0; c < U2; ++c) {
+      const int kb = (blk & 7) + 8 * c;
+      const int kbc = kb < nkb2 ? kb : 0;
+      wv[c] = load_unit<BITS>(rowp + kbc * (4 * BITS));
+      sc[c] = srow[(32 * kbc) / bs];
+    }
+  };
+
+  // ---- issue: the first two FC1 items, then the first two FC2 items. The
+  // loads are unconditional (a wave without items reads a valid item it
+  // never uses), so the compiler's wait counts stay exact.
+  UnitWords<BITS> w1A[U1], w1B[U1];
+  uint32_t s1A[U1], s1B[U1];   // raw fp16 scales, one per register
+  // (sched_barrier keeps the issue order A, B, FC2 A, FC2 B that the waits
+  // below count on)
+  const int last1 = max(i1_1 - 1, 0);
+  load_fc1(min(i1_0, last1), w1A, s1A);
+  __builtin_amdgcn_sched_barrier(0);
+  load_fc1(min(i1_0 + 1, last1), w1B, s1B);
+  __builtin_amdgcn_sched_barrier(0);
+  UnitWords<BITS> w2A[U2], w2B[U2];
+  uint32_t s2A[U2], s2B[U2];
+  const int last2 = max(q1 - 1, 0);
+  load_fc2(dA, min(q0, last2), w2A, s2A);
+  load_fc2(dA, min(q0 + 1, last2), w2B, s2B);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // x pairs and their sums (the x loads have long completed)
   uint32_t xp[U1][16];
   float sx[U1];
 #pragma unroll
@@ -272,77 +377,19 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
 #pragma unroll
     for (int t = 0; t < kDecodeMaxTokens; ++t) corr1[c][t] = zc * quad_get(sx[c], lane, t);
 
-  // ---- work ranges (contiguous per wave)
-  const int g1 = I / 2;
-  const int n1 = D * g1;
-  const int i1_0 = static_cast<int>(static_cast<int64_t>(n1) * gw / NW);
-  const int i1_1 = static_cast<int>(static_cast<int64_t>(n1) * (gw + 1) / NW);
-  const int g2 = H / 8;
-  const int n2 = D * g2;
-  const int i2_0 = static_cast<int>(static_cast<int64_t>(n2) * gw / NW);
-  const int i2_1 = static_cast<int>(static_cast<int64_t>(n2) * (gw + 1) / NW);
-  const int nkb2 = I / 32;
-
-  auto load_fc2 = [&](int it, UnitWords<BITS> (&wv)[U2], float (&sc)[U2]) {
-    const int e = S.dlist[it / g2];
-    const int m = (it % g2) * 8 + (blk >= 8 ? 4 : 0) + q4;
-    const uint8_t* rowp = a.c2 + (static_cast<int64_t>(e) * H + m) * a.rb2;
-    const uint16_t* srow = a.s2 + (static_cast<int64_t>(e) * H + m) * a.nb2;
-#pragma unroll
-    for (int c = 0; c < U2; ++c) {
-      const int kb = (blk & 7) + 8 * c;
-      if (kb < nkb2) {
-        wv[c] = load_unit<BITS>(rowp + kb * (4 * BITS));
-        sc[c] = half_to_f32(srow[(32 * kb) / bs]);
-      } else {
-#pragma unroll
-        for (int w = 0; w < BITS; ++w) wv[c].w[w] = 0u;
-        sc[c] = 0.0f;
-      }
-    }
-  };
-  auto load_fc1 = [&](int it, UnitWords<BITS> (&wv)[U1], float (&sc)[U1]) {
-    const int e = S.dlist[it / g1];
-    const int n = 2 * (it % g1) + (q4 & 1);
-    const int row = (q4 < 2) ? n : I + n;
-    const uint8_t* rowp = a.c1 + (static_cast<int64_t>(e) * 2 * I + row) * a.rb1;
-    const uint16_t* srow = a.s1 + (static_cast<int64_t>(e) * 2 * I + row) * a.nb1;
-#pragma unroll
-    for (int c = 0; c < U1; ++c) {
-      const int kb = blk + 16 * c;
-      if (kb < nkb1) {
-        wv[c] = load_unit<BITS>(rowp + kb * (4 * BITS));
-        sc[c] = half_to_f32(srow[(32 * kb) / bs]);
-      } else {
-#pragma unroll
-        for (int w = 0; w < BITS; ++w) wv[c].w[w] = 0u;
-        sc[c] = 0.0f;
-      }
-    }
-  };
-
-  // ---- loads: the first two FC1 items, then the first two FC2 items of this wave
-  UnitWords<BITS> w1a[U1], w1b[U1];
-  float s1a[U1], s1b[U1];
-  if (i1_0 < i1_1) load_fc1(i1_0, w1a, s1a);
-  if (i1_0 + 1 < i1_1) load_fc1(i1_0 + 1, w1b, s1b);
-  UnitWords<BITS> w2a[U2], w2b[U2];
-  float s2a[U2], s2b[U2];
-  if (i2_0 < i2_1) load_fc2(i2_0, w2a, s2a);
-  if (i2_0 + 1 < i2_1) load_fc2(i2_0 + 1, w2b, s2b);
-
-  // ---- phase 1: FC1 + SwiGLU
-  for (int it = i1_0; it < i1_1; ++it) {
+  // one FC1 item: gate/up sums of two rows for every token, SwiGLU, into hbuf
+  auto fc1_item = [&](const UnitWords<BITS> (&wv)[U1], const uint32_t (&sc)[U1], int li) {
     float acc[kDecodeMaxTokens] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < U1; ++c) {
       uint32_t wp[16];
 #pragma unroll
-      for (int p = 0; p < 16; ++p) wp[p] = unit_pair<BITS>(w1a[c], p);
+      for (int p = 0; p < 16; ++p) wp[p] = unit_pair<BITS>(wv[c], p);
       f32x4_t dv = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int m = 0; m < 8; ++m) dv = mfma4(xp[c][2 * m], xp[c][2 * m + 1], wp[2 * m], wp[2 * m + 1], dv);
-      const float s = s1a[c], s128 = 128.0f * s1a[c];
+      const float s = (blk + 16 * c) < nkb1 ? half_to_f32(static_cast<uint16_t>(sc[c])) : 0.0f;
+      const float s128 = 128.0f * s;
 #pragma unroll
       for (int t = 0; t < kDecodeMaxTokens; ++t)
         acc[t] = fmaf(s128, dv[t], fmaf(-s, corr1[c][t], acc[t]));
@@ -357,48 +404,81 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
     float up[kDecodeMaxTokens];
 #pragma unroll
     for (int t = 0; t < kDecodeMaxTokens; ++t) up[t] = __shfl_down(acc[t], 2, kWave);
-    if (lane < 2) {
-      const int d = it / g1;
-      const int n = 2 * (it % g1) + lane;
+    if (lane < 2)
 #pragma unroll
-      for (int t = 0; t < kDecodeMaxTokens; ++t) {
-        const int slot = (t < T) ? S.dslot[d][t] : -1;
-        if (slot >= 0)
-          store_coherent(a.h32 + static_cast<int64_t>(t * k + slot) * I + n, silu_mul(acc[t], up[t]));
-      }
+      for (int t = 0; t < kDecodeMaxTokens; ++t) S.hbuf[wave][t][2 * li + lane] = silu_mul(acc[t], up[t]);
+  };
+
+  // ---- phase 1: FC1 + SwiGLU, two items in flight, results flushed per chunk
+  for (int c0 = i1_0; c0 < i1_1; c0 += kCap1) {
+    const int c1 = min(c0 + kCap1, i1_1);
+    for (int it = c0; it < c1; it += 2) {
+      fc1_item(w1A, s1A, it - c0);
+      load_fc1(min(it + 2, last1), w1A, s1A);
+      if (it + 1 < c1) fc1_item(w1B, s1B, it + 1 - c0);
+      load_fc1(min(it + 3, last1), w1B, s1B);
     }
-#pragma unroll
-    for (int c = 0; c < U1; ++c) {
-      w1a[c] = w1b[c];
-      s1a[c] = s1b[c];
+    // write this chunk's h (coalesced along n per token)
+    const int ni2 = 2 * (c1 - c0);
+    for (int i = lane; i < T * ni2; i += kWave) {
+      const int t = i / ni2, nl = i % ni2;
+      const int it = c0 + nl / 2, d = it / g1;
+      const int slot = S.slot[t][S.dlist[d]];
+      if (slot >= 0)
+        put_tagged(a.hx + static_cast<int64_t>(t * k + slot) * I + 2 * (it % g1) + (nl & 1),
+                   S.hbuf[wave][t][nl], a.epoch);
     }
-    if (it + 2 < i1_1) load_fc1(it + 2, w1b, s1b);
   }
+  // the third and fourth FC2 items of this wave (FC1's registers are free now)
+  UnitWords<BITS> w2C[U2], w2D[U2];
+  uint32_t s2C[U2], s2D[U2];
+  load_fc2(dA, min(q0 + 2, last2), w2C, s2C);
+  load_fc2(dA, min(q0 + 3, last2), w2D, s2D);
 
-  // ---- phase 2
-  flag_barrier(a.sync, a.epoch + 1);
-
-  // ---- phase 3: FC2, one staged expert at a time
-  const int wg0 = static_cast<int>(static_cast<int64_t>(n2) * (blockIdx.x * kFusedWaves) / NW);
-  const int wg1 = static_cast<int>(static_cast<int64_t>(n2) * ((blockIdx.x + 1) * kFusedWaves) / NW);
-  const int d_lo = wg0 / g2, d_hi = (wg1 - 1) / g2;
-  int it = i2_0;
-  for (int d = d_lo; wg0 < wg1 && d <= d_hi; ++d) {
+  // ---- phase 2: FC2 of this workgroup's expert(s)
+  for (int d = dA; d < dB; ++d) {
+    __syncthreads();   // previous expert's staging area is free
+    const int e = S.dlist[d];
     // stage h of expert d in register order (see FusedLds)
-    __syncthreads();
     for (int i = threadIdx.x; i < U2 * 4 * 32; i += kFusedThreads) {
       const int c = i / 128, j = (i / 32) % 4, l = i % 32;
       const int t = l & 3, kb = (l >> 2) + 8 * c;
-      const int slot = (t < T) ? S.dslot[d][t] : -1;
+      const int slot = (t < T) ? S.slot[t][e] : -1;
       uint32_t hi[4] = {0u, 0u, 0u, 0u}, lo[4] = {0u, 0u, 0u, 0u};
       if (slot >= 0 && kb < nkb2) {
-        const float* hr = a.h32 + static_cast<int64_t>(t * k + slot) * I + 32 * kb;
+        // the h values of this (token, quant block, chunk), each waited for
+        // until it carries this call's epoch
+        const uint64_t* hr = a.hx + static_cast<int64_t>(t * k + slot) * I + 32 * kb;
+        uint64_t ea[4], eb[4];
+        uint32_t spins = 0;
+        bool ready;
+        do {
+          ready = true;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            ea[q] = get_tagged(hr + pair_a(BITS, 4 * j + q));
+            eb[q] = get_tagged(hr + pair_b(BITS, 4 * j + q));
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) ready = ready && tag_is(ea[q], a.epoch) && tag_is(eb[q], a.epoch);
+          if (!ready) {
+            if (++spins > kSpinLimit) {
+              atomicOr(a.err, 1u);
+              break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+          }
+        } while (!ready);
+        float va[4], vb[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int p = 4 * j + q;
-          const float va = load_coherent(hr + pair_a(BITS, p)), vb = load_coherent(hr + pair_b(BITS, p));
-          hi[q] = f32x2_to_bf16x2(va, vb);
-          lo[q] = f32x2_to_bf16x2(va - bf16_to_f32(hi[q] & 0xFFFFu), vb - bf16_to_f32(hi[q] >> 16));
+          va[q] = tag_value(ea[q]);
+          vb[q] = tag_value(eb[q]);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          hi[q] = f32x2_to_bf16x2(va[q], vb[q]);
+          lo[q] = f32x2_to_bf16x2(va[q] - bf16_to_f32(hi[q] & 0xFFFFu), vb[q] - bf16_to_f32(hi[q] >> 16));
         }
       }
       S.ahi[c][j][l] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
@@ -421,7 +501,7 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
       S.hsum[t][kb] = s;
     }
     __syncthreads();
-    if (it >= i2_1 || it / g2 != d) continue;
+    if (q0 >= q1) continue;
     // this wave's A operand for expert d
     uint32_t hhi[U2][16], hlo[U2][16];
     float corr2[U2][kDecodeMaxTokens];
@@ -438,58 +518,101 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
 #pragma unroll
       for (int t = 0; t < kDecodeMaxTokens; ++t) corr2[c][t] = ok ? zc * S.hsum[t][kb] : 0.0f;
     }
-    for (; it < i2_1 && it / g2 == d; ++it) {
+    if (d != dA) {
+      load_fc2(d, q0, w2A, s2A);
+      load_fc2(d, min(q0 + 1, last2), w2B, s2B);
+      load_fc2(d, min(q0 + 2, last2), w2C, s2C);
+      load_fc2(d, min(q0 + 3, last2), w2D, s2D);
+    }
+    auto fc2_item = [&](const UnitWords<BITS> (&wv)[U2], const uint32_t (&sc)[U2], int li) {
       float acc[kDecodeMaxTokens] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < U2; ++c) {
         uint32_t wp[16];
 #pragma unroll
-        for (int p = 0; p < 16; ++p) wp[p] = unit_pair<BITS>(w2a[c], p);
+        for (int p = 0; p < 16; ++p) wp[p] = unit_pair<BITS>(wv[c], p);
         f32x4_t dv = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
           dv = mfma4(hhi[c][2 * m], hhi[c][2 * m + 1], wp[2 * m], wp[2 * m + 1], dv);
           dv = mfma4(hlo[c][2 * m], hlo[c][2 * m + 1], wp[2 * m], wp[2 * m + 1], dv);
         }
-        const float s = s2a[c], s128 = 128.0f * s2a[c];
+        const float s = ((blk & 7) + 8 * c) < nkb2 ? half_to_f32(static_cast<uint16_t>(sc[c])) : 0.0f;
+        const float s128 = 128.0f * s;
 #pragma unroll
         for (int t = 0; t < kDecodeMaxTokens; ++t)
           acc[t] = fmaf(s128, dv[t], fmaf(-s, corr2[c][t], acc[t]));
       }
-#pragma unroll
-      for (int c = 0; c < U2; ++c) {
-        w2a[c] = w2b[c];
-        s2a[c] = s2b[c];
-      }
-      if (it + 2 < i2_1) load_fc2(it + 2, w2b, s2b);
 #pragma unroll
       for (int t = 0; t < kDecodeMaxTokens; ++t) {
         acc[t] += __shfl_xor(acc[t], 4, kWave);
         acc[t] += __shfl_xor(acc[t], 8, kWave);
         acc[t] += __shfl_xor(acc[t], 16, kWave);
       }
-      if ((lane & ~32) < 4) {
-        const int m = (it % g2) * 8 + (lane >= 32 ? 4 : 0) + q4;
+      if ((lane & ~32) < 4)
 #pragma unroll
-        for (int t = 0; t < kDecodeMaxTokens; ++t) {
-          const int slot = (t < T) ? S.dslot[d][t] : -1;
-          if (slot >= 0) store_coherent(a.y32 + static_cast<int64_t>(t * k + slot) * H + m, acc[t]);
-        }
+        for (int t = 0; t < kDecodeMaxTokens; ++t)
+          S.ybuf[wave][t][8 * li + (lane >= 32 ? 4 : 0) + q4] = acc[t];
+    };
+    for (int c0 = q0; c0 < q1; c0 += kCap2) {
+      const int c1 = min(c0 + kCap2, q1);
+      for (int q = c0; q < c1; q += 4) {
+        fc2_item(w2A, s2A, q - c0);
+        load_fc2(d, min(q + 4, last2), w2A, s2A);
+        if (q + 1 < c1) fc2_item(w2B, s2B, q + 1 - c0);
+        load_fc2(d, min(q + 5, last2), w2B, s2B);
+        if (q + 2 < c1) fc2_item(w2C, s2C, q + 2 - c0);
+        load_fc2(d, min(q + 6, last2), w2C, s2C);
+        if (q + 3 < c1) fc2_item(w2D, s2D, q + 3 - c0);
+        load_fc2(d, min(q + 7, last2), w2D, s2D);
+      }
+      // write this chunk's y (coalesced along m per token)
+      const int nm = 8 * (c1 - c0);
+      for (int i = lane; i < T * nm; i += kWave) {
+        const int t = i / nm, ml = i % nm;
+        const int slot = S.slot[t][e];
+        if (slot >= 0)
+          put_tagged(a.yx + static_cast<int64_t>(t * k + slot) * H + 8 * c0 + ml, S.ybuf[wave][t][ml],
+                     a.epoch);
       }
     }
   }
 
-  // ---- phase 4
-  flag_barrier(a.sync, a.epoch + 2);
-
-  // ---- phase 5: out[t][m] = round(sum_j w[t][j] * y[t*k + j][m]), slot order
-  for (int idx = blockIdx.x * kFusedThreads + threadIdx.x; idx < T * H;
-       idx += gridDim.x * kFusedThreads) {
-    const int t = idx / H, m = idx % H;
-    float o = 0.0f;
-    for (int j = 0; j < k; ++j)
-      o = fmaf(S.w[t * k + j], load_coherent(a.y32 + static_cast<int64_t>(t * k + j) * H + m), o);
-    static_cast<uint16_t*>(a.out)[idx] = static_cast<uint16_t>(f32_to_bf16(o));
+  // ---- phase 3: combine the row groups this wave owns
+  const int gc0 = static_cast<int>(static_cast<int64_t>(g2) * gw / NW);
+  const int gc1 = static_cast<int>(static_cast<int64_t>(g2) * (gw + 1) / NW);
+  for (int grp = gc0; grp < gc1; ++grp) {
+    if (lane < 8 * T) {
+      const int t = lane >> 3, m = 8 * grp + (lane & 7);
+      const uint64_t* yr = a.yx + static_cast<int64_t>(t * k) * H + m;
+      float o = 0.0f;
+      for (int j0 = 0; j0 < k; j0 += 8) {
+        // slots j0..j0+7 of token t at row m, each waited for until it
+        // carries this call's epoch
+        uint64_t v[8];
+        uint32_t spins = 0;
+        bool ready;
+        do {
+          ready = true;
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            v[j] = (j0 + j < k) ? get_tagged(yr + static_cast<int64_t>(j0 + j) * H) : 0ull;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) ready = ready && (j0 + j >= k || tag_is(v[j], a.epoch));
+          if (!ready) {
+            if (++spins > kSpinLimit) {
+              atomicOr(a.err, 2u);
+              break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+          }
+        } while (!ready);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (j0 + j < k) o = fmaf(S.w[t * k + j0 + j], tag_value(v[j]), o);
+      }
+      a.out[static_cast<int64_t>(t) * H + m] = static_cast<uint16_t>(f32_to_bf16(o));
+    }
   }
 }
 
@@ -538,7 +661,7 @@ const void* fused_kernel_for(const Layer& L) {
 
 bool fused_decode_supported(const Layer& L) {
   return L.act_bf16 && fused_u1(L) > 0 && fused_u2(L) > 0 && L.H % 8 == 0 && L.I % 2 == 0 &&
-         L.E <= kMaxExperts && fused_kernel_for(L) != nullptr;
+         L.E <= kFusedMaxExperts && L.k <= kMaxTopK && fused_kernel_for(L) != nullptr;
 }
 
 int fused_decode_grid(const Layer& L, int device) {
@@ -554,13 +677,32 @@ int fused_decode_grid(const Layer& L, int device) {
   return grid <= kFusedMaxWorkgroups ? grid : kFusedMaxWorkgroups;
 }
 
+size_t fused_exchange_bytes(const Layer& L) {
+  const size_t routes = static_cast<size_t>(kDecodeMaxTokens) * static_cast<size_t>(L.k);
+  return kExchangeHeader + routes * static_cast<size_t>(L.I + L.H) * sizeof(uint64_t);
+}
+
+namespace {
+__global__ void exchange_clear_kernel(uint4* p, size_t n16) {
+  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n16;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+}  // namespace
+
+hipError_t clear_exchange(const Layer& L, void* xbuf, hipStream_t s) {
+  const size_t n16 = fused_exchange_bytes(L) / 16;
+  hipLaunchKernelGGL(exchange_clear_kernel, dim3(256), dim3(256), 0, s, static_cast<uint4*>(xbuf), n16);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode_fused(const Layer& L, const void* x, const void* logits, void* out,
-                               int64_t T, char* ws, const Workspace& W, uint32_t* sync,
+                               int64_t T, char* ws, const Workspace& W, void* xbuf,
                                uint32_t epoch, int grid, hipStream_t s) {
   FusedArgs fa;
   fa.x = static_cast<const uint16_t*>(x);
   fa.logits = static_cast<const uint16_t*>(logits);
-  fa.out = out;
+  fa.out = static_cast<uint16_t*>(out);
   fa.c1 = L.fc1_codes;
   fa.s1 = L.fc1_scales;
   fa.c2 = L.fc2_codes;
@@ -578,9 +720,11 @@ hipError_t launch_decode_fused(const Layer& L, const void* x, const void* logits
   fa.nb2 = L.fc2_nblk;
   fa.ws_ids = reinterpret_cast<int32_t*>(ws + W.topk_id);
   fa.ws_w = reinterpret_cast<float*>(ws + W.topk_w);
-  fa.h32 = reinterpret_cast<float*>(ws + W.h32);
-  fa.y32 = reinterpret_cast<float*>(ws + W.y32);
-  fa.sync = sync;
+  char* xb = static_cast<char*>(xbuf);
+  const size_t routes = static_cast<size_t>(kDecodeMaxTokens) * static_cast<size_t>(L.k);
+  fa.err = reinterpret_cast<uint32_t*>(xb);
+  fa.hx = reinterpret_cast<uint64_t*>(xb + kExchangeHeader);
+  fa.yx = fa.hx + routes * static_cast<size_t>(L.I);
   fa.epoch = epoch;
   void* args[] = {&fa};
   const hipError_t err =

@@ -183,84 +183,6 @@ __device__ __forceinline__ int key_expert(uint64_t key) {
   return static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(key));
 }
 
-// ---------------------------------------------------------------- DPP max
-//
-// Wave-wide maximum of 64-bit keys with DPP moves (no LDS traffic): rotate
-// within each row of 16 lanes by 8, 4, 2, 1, then fold rows with the row
-// broadcasts of lanes 15 and 31; lane 63 ends with the maximum, which is then
-// read as a uniform value.
-template <int CTRL, int ROWS>
-__device__ __forceinline__ void dpp_max_step(uint32_t& hi, uint32_t& lo) {
-  const uint32_t phi = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
-      static_cast<int>(hi), static_cast<int>(hi), CTRL, ROWS, 0xF, false));
-  const uint32_t plo = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
-      static_cast<int>(lo), static_cast<int>(lo), CTRL, ROWS, 0xF, false));
-  const bool take = (phi > hi) | ((phi == hi) & (plo > lo));
-  hi = take ? phi : hi;
-  lo = take ? plo : lo;
-}
-
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t key) {
-  uint32_t hi = static_cast<uint32_t>(key >> 32), lo = static_cast<uint32_t>(key);
-  dpp_max_step<0x128, 0xF>(hi, lo);   // row_ror:8
-  dpp_max_step<0x124, 0xF>(hi, lo);   // row_ror:4
-  dpp_max_step<0x122, 0xF>(hi, lo);   // row_ror:2
-  dpp_max_step<0x121, 0xF>(hi, lo);   // row_ror:1
-  dpp_max_step<0x142, 0xA>(hi, lo);   // row_bcast:15 into rows 1 and 3
-  dpp_max_step<0x143, 0xC>(hi, lo);   // row_bcast:31 into rows 2 and 3
-  const uint32_t h = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(hi), 63));
-  const uint32_t l = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(lo), 63));
-  return (static_cast<uint64_t>(h) << 32) | l;
-}
-
-// Top-k of one token by one wavefront: k rounds of a DPP argmax over 64-bit
-// keys (ordered logit, then lower expert index), then the softmax over the k
-// selected logits. vals: the token's E logits (-0 folded into +0), e.g. in LDS.
-// Lanes j < k write ids[j] and w[j].
-template <int kC>
-__device__ __forceinline__ void topk_softmax_dpp_n(const float* vals, int E, int k, int lane,
-                                                   int32_t* ids, float* w) {
-  uint64_t keys[kC];
-  const int nc = (E + kWave - 1) / kWave;
-#pragma unroll
-  for (int c = 0; c < kC; ++c) {
-    const int e = lane + kWave * c;
-    keys[c] = (c < nc && e < E) ? route_key(vals[e], static_cast<uint32_t>(e)) : 0ull;
-  }
-  int my_id = 0;
-  float my_v = 0.0f, v0 = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    uint64_t best = keys[0];
-#pragma unroll
-    for (int c = 1; c < kC; ++c) best = keys[c] > best ? keys[c] : best;
-    best = wave_max_u64(best);
-    const int e = key_expert(best);
-    const float v = key_value(best);
-    if (j == 0) v0 = v;
-    if (lane == j) { my_id = e; my_v = v; }
-#pragma unroll
-    for (int c = 0; c < kC; ++c)
-      if (keys[c] == best) keys[c] = 0ull;
-  }
-  const float ex = (lane < k) ? expf(my_v - v0) : 0.0f;
-  const float sum = wave_sum(ex);
-  if (lane < k) {
-    ids[lane] = my_id;
-    w[lane] = ex / sum;
-  }
-}
-
-// Dispatch on the expert count so each lane carries only the key slots it needs.
-__device__ __forceinline__ void topk_softmax_dpp(const float* vals, int E, int k, int lane,
-                                                 int32_t* ids, float* w) {
-  if (E <= 2 * kWave)
-    topk_softmax_dpp_n<2>(vals, E, k, lane, ids, w);
-  else if (E <= 4 * kWave)
-    topk_softmax_dpp_n<4>(vals, E, k, lane, ids, w);
-  else
-    topk_softmax_dpp_n<kMaxExperts / kWave>(vals, E, k, lane, ids, w);
-}
-
 // One wavefront selects the top-k experts of one token and computes the
 // softmax over the k selected logits. Slot j holds the j-th largest logit
 // (ties to the lower expert index). Lanes j < k write ids[j] and w[j].
@@ -300,56 +222,6 @@ __device__ __forceinline__ void topk_softmax_wave(const ACT* logits, int E, int 
     ids[lane] = my_id;
     w[lane] = ex / sum;
   }
-}
-
-// Top-k by rank, one wavefront per token, no serial dependency between
-// slots: rank(e) = #{e' : l[e'] > l[e] or (l[e'] == l[e] and e' < e)} over
-// the logits staged in LDS (vals, E floats, -0 already folded into +0); the
-// expert of rank j < k goes to slot j. Then the softmax over the k selected
-// logits. Lanes j < k write ids[j] and w[j].
-__device__ __forceinline__ float canon_logit(float v) { return v == 0.0f ? 0.0f : v; }
-
-__device__ __forceinline__ void topk_softmax_rank(const float* vals, int E, int k, int lane,
-                                                  int32_t* ids, float* w, float* selv) {
-  // E is padded to a multiple of 4 in LDS with -inf (never selected before a
-  // real expert because ties go to the lower index and every real logit is
-  // >= -inf). Each lane ranks up to kMaxExperts / 64 candidates at once.
-  constexpr int kC = kMaxExperts / kWave;
-  const int E4 = (E + 3) & ~3;
-  float v[kC];
-  int rank[kC];
-#pragma unroll
-  for (int c = 0; c < kC; ++c) {
-    const int e = lane + kWave * c;
-    v[c] = (e < E) ? vals[e] : 0.0f;
-    rank[c] = 0;
-  }
-  const int nc = (E + kWave - 1) / kWave;
-#pragma unroll 4
-  for (int q = 0; q < E4; q += 4) {
-    const float4 u = *reinterpret_cast<const float4*>(vals + q);
-#pragma unroll
-    for (int c = 0; c < kC; ++c) {
-      if (c >= nc) break;
-      const int e = lane + kWave * c;
-      rank[c] += ((u.x > v[c]) | ((u.x == v[c]) & (q < e))) + ((u.y > v[c]) | ((u.y == v[c]) & (q + 1 < e))) +
-                 ((u.z > v[c]) | ((u.z == v[c]) & (q + 2 < e))) + ((u.w > v[c]) | ((u.w == v[c]) & (q + 3 < e)));
-    }
-  }
-#pragma unroll
-  for (int c = 0; c < kC; ++c) {
-    const int e = lane + kWave * c;
-    if (c < nc && e < E && rank[c] < k) {
-      ids[rank[c]] = e;
-      selv[rank[c]] = v[c];
-    }
-  }
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  const float v0 = selv[0];
-  const float ex = (lane < k) ? expf(selv[lane < k ? lane : 0] - v0) : 0.0f;
-  const float sum = wave_sum(ex);
-  if (lane < k) w[lane] = ex / sum;
 }
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }

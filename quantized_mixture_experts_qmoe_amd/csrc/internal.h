@@ -71,15 +71,20 @@ hipError_t launch_prefill(const Layer& L, const void* x, void* out, int64_t T, c
                           const Workspace& W, hipStream_t s);
 hipError_t launch_decode(const Layer& L, const void* x, const void* logits, void* out, int64_t T,
                          char* ws, const Workspace& W, hipStream_t s);
-// Fused single-launch decode (bf16 activations, H <= 2048, I <= 1024). Its
-// grid barriers use a per-handle device buffer of flags (zeroed at create)
-// and a per-call epoch.
+// Fused single-launch decode (bf16 activations, H <= 2048, I <= 1024,
+// E <= 256). Its workgroups exchange h and y through a per-handle device
+// buffer of epoch-tagged entries (fused_exchange_bytes, zeroed at create and
+// by clear_exchange whenever the epoch counter wraps); every call passes a
+// new nonzero epoch.
 constexpr int kFusedMaxWorkgroups = 1024;
-constexpr size_t kSyncBytes = 8192;                    // >= (64 + kFusedMaxWorkgroups) words
+constexpr int kFusedMaxExperts = 256;
+constexpr size_t kExchangeHeader = 256;                 // error bits, then the h and y entries
 bool fused_decode_supported(const Layer& L);
 int fused_decode_grid(const Layer& L, int device);
+size_t fused_exchange_bytes(const Layer& L);
+hipError_t clear_exchange(const Layer& L, void* xbuf, hipStream_t s);
 hipError_t launch_decode_fused(const Layer& L, const void* x, const void* logits, void* out,
-                               int64_t T, char* ws, const Workspace& W, uint32_t* sync,
+                               int64_t T, char* ws, const Workspace& W, void* xbuf,
                                uint32_t epoch, int grid, hipStream_t s);
 hipError_t launch_dequant(const Layer& L, int fc, int64_t expert, float* out_f32,
                           uint16_t* out_bf16, hipStream_t s);

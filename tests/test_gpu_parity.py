@@ -157,11 +157,11 @@ def test_fused_decode_matches_split_decode(name, T):
 
 
 def test_decode_back_to_back_calls_reuse_sync_state():
-    """The fused decode's barrier flags carry a per-call epoch and all data
-    crossing workgroups goes through coherent loads and stores: many calls in
-    a row, rotating over three layers with different token counts, must each
-    match that layer's first result bit for bit (stale data from the previous
-    call would show up as a mismatch)."""
+    """The fused decode's cross-workgroup flags carry a per-call epoch and all
+    data crossing workgroups goes through coherent loads and stores: many
+    calls in a row, rotating over three layers with different token counts,
+    must each match that layer's first result bit for bit (a flag or h/y
+    value left over from the previous call would show up as a mismatch)."""
     cases = [qi.make_workload("decode", T=4), qi.make_workload("decode", T=1, seed=77),
              qi.make_workload("decode", T=3, seed=78)]
     layers = [layer_for(wl, 16) for wl in cases]
@@ -177,6 +177,69 @@ def test_decode_back_to_back_calls_reuse_sync_state():
     torch.cuda.synchronize()
     for i, o in outs:
         assert torch.equal(o.view(torch.int16), refs[i].view(torch.int16)), i
+
+
+class _env:
+    """Set environment variables while a layer is created (the library reads
+    them once, at create)."""
+
+    def __init__(self, **kv):
+        self.kv = kv
+
+    def __enter__(self):
+        self.old = {k: os.environ.get(k) for k in self.kv}
+        os.environ.update({k: str(v) for k, v in self.kv.items()})
+
+    def __exit__(self, *exc):
+        for k, v in self.old.items():
+            if v is None:
+                del os.environ[k]
+            else:
+                os.environ[k] = v
+
+
+@pytest.mark.parametrize("name,T", [("decode", 4), ("int3", 4), ("stack", 1)])
+def test_fused_decode_schedule_independent(name, T):
+    """Every output element of the fused decode is computed by the same
+    arithmetic whatever the grid: with 1, 7, 16 or 40 workgroups (more
+    experts than workgroups, whole experts per workgroup, many FC1/FC2 chunks
+    per wave) the output equals the full-grid output bit for bit, twice in a
+    row on the same layer."""
+    wl = qi.make_workload(name, T=T)
+    ref = check_decode(wl, layer_for(wl, 16))
+    x, g = wl.tokens.x.to(DEV), wl.tokens.logits.to(DEV)
+    for grid in (1, 7, 16, 40):
+        with _env(QMOE_FUSED_GRID=grid):
+            L = layer_for(wl, 16)
+        for rep in range(2):
+            out = L(x, g)
+            torch.cuda.synchronize()
+            assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), (grid, rep)
+
+
+def test_fused_decode_epoch_wrap():
+    """The fused decode tags every exchanged value with the call's epoch. A
+    handle whose epoch counter starts just below the 32-bit wrap takes the
+    wrap path on its second call (the exchange buffer is zeroed again and
+    the epochs restart at 1); every call still equals the reference bit for
+    bit."""
+    wl = qi.make_workload("decode", T=4)
+    ref = check_decode(wl, layer_for(wl, 16))
+    x, g = wl.tokens.x.to(DEV), wl.tokens.logits.to(DEV)
+    with _env(QMOE_FUSED_EPOCH_START=2 ** 32 - 2):
+        L = layer_for(wl, 16)
+    for rep in range(4):
+        out = L(x, g)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), rep
+
+
+def test_decode_many_experts_uses_split_path():
+    """More experts than the fused kernel's routing holds (E = 320 > 256):
+    the forward takes the two-kernel decode and still matches the oracle."""
+    spec = small_spec(4, 32, num_experts=320, top_k=6)
+    wl = qi.make_layer(spec, T=4, seed=91)
+    check_decode(wl, layer_for(wl, 16))
 
 
 def test_decode_repeated_experts_across_tokens():
