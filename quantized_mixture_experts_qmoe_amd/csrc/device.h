@@ -101,16 +101,90 @@ __device__ __forceinline__ uint32_t unit_pair(const UnitWords<BITS>& u, int p) {
 }
 
 // The matrix-core operand value of code i: (q - zp) * s computed exactly in
-// fp32 (at most 11 + 3 significant bits) and rounded once to bf16. Writes the
-// unit's 32 values as 16 bf16 pairs in natural order (pair p = codes 2p, 2p+1).
+// fp32 and rounded once to bf16 (round to nearest even). Writes the unit's 32
+// values as 16 bf16 pairs in natural order (pair p = codes 2p, 2p+1).
+//
+// For a finite scale, q * s - zp * s is computed by one FMA: both products
+// and the result (at most 9 + 11 significant bits) are exact in fp32, so the
+// FMA's single rounding is exact. INT4 and INT2 codes are first spread into
+// bytes with masks so v_cvt_f32_ubyteN converts them without per-code
+// extraction. A non-finite scale takes the plain (q - zp) * s route so the
+// result stays bit-identical in every case.
+__device__ __forceinline__ float ubyte_f32(uint32_t w, int b) {
+  return static_cast<float>((w >> (8 * b)) & 0xFFu);   // selects v_cvt_f32_ubyteN
+}
+
+// v_and_b32 the compiler cannot fold into the byte conversions that follow
+// (otherwise it turns mask + byte select into a bit-field extract per code).
+__device__ __forceinline__ uint32_t and_opaque(uint32_t w, uint32_t m) {
+  uint32_t r;
+  asm("v_and_b32 %0, %1, %2" : "=v"(r) : "v"(m), "v"(w));
+  return r;
+}
+
+// Codes 16h .. 16h+15 of a unit as floats, natural order.
+template <int BITS>
+__device__ __forceinline__ void unit_half_codes(const UnitWords<BITS>& u, int h, float (&q)[16]) {
+  if constexpr (BITS == 4) {
+    // dwords 2h, 2h+1 hold codes 16h..16h+15 (nibbles); even codes -> bytes of lo, odd -> hi
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      const uint32_t w = h ? u.w[2 + d] : u.w[d];
+      const uint32_t lo = and_opaque(w, 0x0F0F0F0Fu), hi = and_opaque(w >> 4, 0x0F0F0F0Fu);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        q[8 * d + 2 * b] = ubyte_f32(lo, b);
+        q[8 * d + 2 * b + 1] = ubyte_f32(hi, b);
+      }
+    }
+  } else if constexpr (BITS == 2) {
+    // dword h holds codes 16h..16h+15; c_j's byte b holds code 16h + 4b + j
+    const uint32_t w = h ? u.w[1] : u.w[0];
+    uint32_t c[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c[j] = and_opaque(w >> (2 * j), 0x03030303u);
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) q[4 * b + j] = ubyte_f32(c[j], b);
+  } else {
+    // bits [48h, 48h + 48) of the 96-bit unit
+    const uint64_t w = h ? ((static_cast<uint64_t>(u.w[2]) << 32 | u.w[1]) >> 16)
+                         : (static_cast<uint64_t>(u.w[1]) << 32 | u.w[0]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) q[i] = static_cast<float>(static_cast<uint32_t>(w >> (3 * i)) & 7u);
+  }
+}
+
+// (q - zp) * s for codes as floats, rounded once to bf16 pairs. q - zp is an
+// exact small integer and its product with an fp16 scale has at most
+// 9 + 11 significant bits, so the fp32 product is exact for every scale
+// (infinities and NaN included) and the one rounding is the bf16 one.
+// Branch-free, so callers can interleave it with matrix work.
+template <int N>
+__device__ __forceinline__ void dequant_codes_bf16(const float (&q)[2 * N], float s, int zp,
+                                                   uint32_t (&out)[N]) {
+  const float zf = static_cast<float>(zp);
+#pragma unroll
+  for (int p = 0; p < N; ++p)
+    out[p] = f32x2_to_bf16x2((q[2 * p] - zf) * s, (q[2 * p + 1] - zf) * s);
+}
+
+// The matrix-core operand values of a whole unit: 16 bf16 pairs in natural
+// order (pair p = codes 2p, 2p+1).
 template <int BITS>
 __device__ __forceinline__ void dequant_unit_bf16(const UnitWords<BITS>& u, float s, int zp,
                                                   uint32_t (&out)[16]) {
+  float q0[16], q1[16];
+  unit_half_codes<BITS>(u, 0, q0);
+  unit_half_codes<BITS>(u, 1, q1);
+  uint32_t o0[8], o1[8];
+  dequant_codes_bf16<8>(q0, s, zp, o0);
+  dequant_codes_bf16<8>(q1, s, zp, o1);
 #pragma unroll
-  for (int p = 0; p < 16; ++p) {
-    const float lo = static_cast<float>(static_cast<int>(unit_code<BITS>(u, 2 * p)) - zp) * s;
-    const float hi = static_cast<float>(static_cast<int>(unit_code<BITS>(u, 2 * p + 1)) - zp) * s;
-    out[p] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+  for (int p = 0; p < 8; ++p) {
+    out[p] = o0[p];
+    out[8 + p] = o1[p];
   }
 }
 
@@ -225,5 +299,11 @@ __device__ __forceinline__ void topk_softmax_wave(const ACT* logits, int E, int 
 }
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+// silu(g) * u with the hardware exp2 and reciprocal (a few ulp in fp32), for
+// epilogues that round h to bf16 right after.
+__device__ __forceinline__ float silu_mul_fast(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
 
 }  // namespace qmoe

@@ -1,15 +1,23 @@
 // Prefill path (5+ tokens): expert-grouped GEMMs on the CDNA4 matrix cores.
 //
 // The routing stage leaves the routes sorted by expert and a tile list
-// (expert, first sorted row, rows). Each workgroup computes one 128 x 128
-// output tile of one expert:
+// (expert, first sorted row, rows <= 256). Each workgroup (8 waves, 4 x 2 of
+// 64 x 128) computes one 256 x 256 tile of one expert:
 //   FC1: A = x rows gathered through sorted_routes (bf16), B = the expert's
-//        gate rows [n0, n0+64) and up rows [I+n0, I+n0+64), dequantized into
-//        LDS as bf16; the epilogue applies h = silu(gate) * up and stores h
-//        as bf16 [R, I] in sorted order.
+//        gate rows [n0, n0+128) and up rows [I+n0, I+n0+128), dequantized to
+//        bf16 (round to nearest even of (q - zp) * s, exact in fp32) into
+//        LDS; each wave holds 64 gate and the 64 matching up columns, so the
+//        epilogue applies h = silu(gate) * up and stores h as bf16 [R, I] in
+//        sorted order.
 //   FC2: A = h rows of the tile (bf16), B = the expert's FC2 rows
-//        [n0, n0+128) dequantized into LDS; the epilogue stores fp32 y
+//        [n0, n0+256) dequantized into LDS; the epilogue stores fp32 y
 //        [R, H] in sorted order.
+// The tall tile shares each dequantized weight among 256 rows; a wave whose
+// 64 rows all lie past the expert's last route skips its matrix work.
+// The K loop runs in stages of 64 with two LDS buffers: while the waves run
+// the MFMAs of stage s, each thread dequantizes and stores stage s+1 from
+// registers and issues the global loads of stage s+2, so global latency is
+// covered by a whole stage of matrix work; one barrier per stage.
 // A combine kernel then sums each token's k slots in slot order and rounds
 // once.
 //
@@ -30,12 +38,17 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
 namespace {
 
-constexpr int kKT = 64;              // K per LDS stage (two 16x16x32 MFMA steps)
-constexpr int kLdsStride = kKT + 8;  // bf16 elements per LDS row (padding against bank conflicts)
+constexpr int kKT = 64;                 // K per stage (two 16x16x32 MFMA steps)
+constexpr int kLdsStride = kKT + 8;     // bf16 per LDS row (padding against bank conflicts)
+constexpr int kBM = kTileM;             // A rows per tile (256)
+constexpr int kBN = 256;                // B rows per tile
+constexpr int kGemmThreads = 512;       // 8 waves: 4 along M x 2 along N, 64 x 128 each
+static_assert(kBM == 256, "the staging below assumes 256-row tiles");
 
 // Logical tile index of this workgroup. Workgroups are dealt to the 8 XCDs
 // round-robin; consecutive logical tiles are kept on one XCD so the n-tiles
-// of one m-tile (which share their A rows) meet in the same L2.
+// of one m-tile (which share their A rows) and the m-tiles of one expert
+// (which share B) meet in the same L2.
 __device__ __forceinline__ int logical_tile(int active) {
   const int b = blockIdx.x;
   const int per_xcd = (active + 7) / 8;
@@ -45,18 +58,26 @@ __device__ __forceinline__ int logical_tile(int active) {
   return L < active ? L : -1;
 }
 
+int gemm_n_tiles(const Layer& L, bool fc1) {
+  return fc1 ? static_cast<int>((L.I + kBN / 2 - 1) / (kBN / 2))
+             : static_cast<int>((L.H + kBN - 1) / kBN);
+}
+
 }  // namespace
 
-// grid = 8 * ceil(max_tiles * n_tiles_n / 8), block = 256 (2 x 2 waves of 64 x 64)
+// grid = 8 * ceil(max_tiles * n_tiles_n / 8), block = 512
+// (one workgroup per CU: its LDS use limits each SIMD to two waves, so the
+// compiler may use the whole register file to keep fragments in flight)
 template <int BITS, bool FC1>
-__global__ __launch_bounds__(256) void grouped_gemm_kernel(
+__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void grouped_gemm_kernel(
     const uint16_t* __restrict__ a_src, const int32_t* __restrict__ sorted_routes, int k,
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales, int K, int H, int I,
-    int bs, int zp, int64_t row_bytes, int64_t nblk, const int4* __restrict__ tiles,
+    int bs_shift, int zp, int64_t row_bytes, int64_t nblk, const int4* __restrict__ tiles,
     const int32_t* __restrict__ num_tiles, int n_tiles_n, uint16_t* __restrict__ h_out,
     float* __restrict__ y_out) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[kTileM * kLdsStride];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[kTileN * kLdsStride];
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][kBM * kLdsStride];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kBN * kLdsStride];
 
   const int active = num_tiles[0] * n_tiles_n;
   const int L = logical_tile(active);
@@ -65,102 +86,140 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(
   const int4 td = tiles[m_tile];
   const int e = td.x, row0 = td.y, nrows = td.z;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
+  const bool wave_live = wm * 64 < nrows;   // uniform: this wave's rows hold routes
   const int n_rows_total = FC1 ? 2 * I : H;                    // rows of W
   const uint8_t* ebase = codes + static_cast<int64_t>(e) * n_rows_total * row_bytes;
   const uint16_t* sbase = scales + static_cast<int64_t>(e) * n_rows_total * nblk;
+  const int n0 = n_tile * (FC1 ? kBN / 2 : kBN);
 
-  // this thread's B row (one 32-code unit per K stage)
-  const int b_row = tid >> 1, b_half = tid & 1;
+  // this thread's B work: one unit (32 codes) per stage: row tid >> 1, K
+  // offset 32 * (tid & 1). Rows past the matrix read row 0 instead.
+  const int b_row = tid >> 1, b_kq = tid & 1;
   int w_row;
-  bool b_valid;
   if (FC1) {
-    const int n0 = n_tile * 64;
-    const int c = n0 + (b_row & 63);
-    b_valid = c < I;
-    w_row = (b_row < 64) ? c : I + c;
+    const int c = n0 + (b_row & (kBN / 2 - 1));
+    w_row = c < I ? ((b_row < kBN / 2) ? c : I + c) : 0;
   } else {
-    const int c = n_tile * kTileN + b_row;
-    b_valid = c < H;
-    w_row = c;
+    const int c = n0 + b_row;
+    w_row = c < H ? c : 0;
   }
+  const uint8_t* b_ptr = ebase + static_cast<int64_t>(w_row) * row_bytes;
+  const uint16_t* s_ptr = sbase + static_cast<int64_t>(w_row) * nblk;
 
-  // this thread's A rows: 4 chunks of 8 bf16 per stage
+  // this thread's A work: 32 bf16 (four 16-byte chunks) of row tid >> 1 per
+  // stage. Rows past the tile read the tile's first row: they only feed
+  // output rows that are never stored.
+  const int a_row = tid >> 1, a_col = (tid & 1) * 32;
+  const int a_src_row = a_row < nrows ? a_row : 0;
   const int64_t a_ld = FC1 ? H : I;
-  const uint16_t* a_ptr[4];
-  int a_row[4], a_col[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int c = tid + 256 * q;
-    a_row[q] = c >> 3;
-    a_col[q] = (c & 7) * 8;
-    if (a_row[q] < nrows) {
-      const int64_t src_row = FC1 ? (sorted_routes[row0 + a_row[q]] / k) : (row0 + a_row[q]);
-      a_ptr[q] = a_src + src_row * a_ld;
-    } else {
-      a_ptr[q] = nullptr;
-    }
-  }
+  const int64_t src_row = FC1 ? (sorted_routes[row0 + a_src_row] / k) : (row0 + a_src_row);
+  const uint16_t* a_ptr = a_src + src_row * a_ld + a_col;
 
-  f32x4_t acc[4][4];
+  // stage registers. Loads are unconditional (stages past K re-read a valid
+  // address, so the wait counts stay exact); a B unit past K gets a zero
+  // scale, which cancels whatever A holds there.
+  uint4 ra0, ra1, ra2, ra3;
+  UnitWords<BITS> rb;
+  uint32_t rs;
+  auto load_stage = [&](int st) {
+    const int k0 = st * kKT;
+    const uint16_t* ap = a_ptr + ((k0 + a_col < K) ? k0 : 0);
+    ra0 = *reinterpret_cast<const uint4*>(ap);
+    ra1 = *reinterpret_cast<const uint4*>(ap + 8);
+    ra2 = *reinterpret_cast<const uint4*>(ap + 16);
+    ra3 = *reinterpret_cast<const uint4*>(ap + 24);
+    const int kk = k0 + 32 * b_kq;
+    const int kb = (kk < K) ? kk : 0;
+    rb = load_unit<BITS>(b_ptr + (kb / 32) * (4 * BITS));
+    rs = s_ptr[kb >> bs_shift] | (kk < K ? 0u : 0x10000u);   // bit 16: past K
+  };
+  auto store_a = [&](int buf) {
+    uint4* ad = reinterpret_cast<uint4*>(&As[buf][a_row * kLdsStride + a_col]);
+    ad[0] = ra0;
+    ad[1] = ra1;
+    ad[2] = ra2;
+    ad[3] = ra3;
+  };
+  auto store_b = [&](int buf, const uint32_t (&pairs)[16]) {
+    uint4* bd = reinterpret_cast<uint4*>(&Bs[buf][b_row * kLdsStride + 32 * b_kq]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) bd[q] = make_uint4(pairs[4 * q], pairs[4 * q + 1], pairs[4 * q + 2], pairs[4 * q + 3]);
+  };
+  auto stage_scale = [&]() {
+    return (rs >> 16) ? 0.0f : half_to_f32(static_cast<uint16_t>(rs));
+  };
+  auto store_stage = [&](int buf) {
+    store_a(buf);
+    uint32_t pairs[16];
+    {
+      const float sc = stage_scale();
+      float q[16];
+      uint32_t p0[8];
+      unit_half_codes<BITS>(rb, 0, q);
+      dequant_codes_bf16<8>(q, sc, zp, p0);
+      for (int p = 0; p < 8; ++p) pairs[p] = p0[p];
+      unit_half_codes<BITS>(rb, 1, q);
+      dequant_codes_bf16<8>(q, sc, zp, p0);
+      for (int p = 0; p < 8; ++p) pairs[8 + p] = p0[p];
+    }
+    store_b(buf, pairs);
+  };
+
+  f32x4_t acc[4][8];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int quad = lane >> 4, l16 = lane & 15;
-  for (int k0 = 0; k0 < K; k0 += kKT) {
-    // ---- stage A
+  int b_frag_row[8];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (a_ptr[q] && k0 + a_col[q] < K) v = *reinterpret_cast<const uint4*>(a_ptr[q] + k0 + a_col[q]);
-      *reinterpret_cast<uint4*>(&As[a_row[q] * kLdsStride + a_col[q]]) = v;
-    }
-    // ---- stage B: dequantize one unit
-    {
-      uint32_t pairs[16];
-      const int kk = k0 + 32 * b_half;
-      if (b_valid && kk < K) {
-        const UnitWords<BITS> u =
-            load_unit<BITS>(ebase + static_cast<int64_t>(w_row) * row_bytes + (kk / 32) * (4 * BITS));
-        const float s = half_to_f32(sbase[static_cast<int64_t>(w_row) * nblk + kk / bs]);
-        dequant_unit_bf16<BITS>(u, s, zp, pairs);
-      } else {
+  for (int tn = 0; tn < 8; ++tn)
+    b_frag_row[tn] = FC1 ? (tn < 4 ? 0 : kBN / 2) + wn * 64 + (tn & 3) * 16 + l16
+                         : wn * 128 + tn * 16 + l16;
+  auto frag_a = [&](int buf, int ks, int tm) {
+    const int r = wm * 64 + tm * 16 + l16;
+    return *reinterpret_cast<const bf16x8_t*>(&As[buf][r * kLdsStride + ks * 32 + quad * 8]);
+  };
+  auto frag_b = [&](int buf, int ks, int tn) {
+    return *reinterpret_cast<const bf16x8_t*>(&Bs[buf][b_frag_row[tn] * kLdsStride + ks * 32 + quad * 8]);
+  };
+
+
+  const int ns = (K + kKT - 1) / kKT;
+  load_stage(0);
+  store_stage(0);
+  load_stage(ns > 1 ? 1 : 0);
+  __syncthreads();
+  for (int st = 0; st < ns; ++st) {
+    const int buf = st & 1;
+    // ---- MFMA on stage st: all fragments of the stage are read first, then
+    // the 32 MFMAs issue back to back
+    if (wave_live) {
 #pragma unroll
-        for (int p = 0; p < 16; ++p) pairs[p] = 0u;
+      for (int ks = 0; ks < kKT / 32; ++ks) {
+        bf16x8_t af[4], bfr[8];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) af[t] = frag_a(buf, ks, t);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) bfr[t] = frag_b(buf, ks, t);
+#pragma unroll
+        for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+          for (int tn = 0; tn < 8; ++tn)
+            acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[tm], bfr[tn], acc[tm][tn], 0, 0, 0);
       }
-      uint4* dst = reinterpret_cast<uint4*>(&Bs[b_row * kLdsStride + 32 * b_half]);
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        dst[q] = make_uint4(pairs[4 * q], pairs[4 * q + 1], pairs[4 * q + 2], pairs[4 * q + 3]);
     }
-    __syncthreads();
-    // ---- MFMA
-#pragma unroll
-    for (int ks = 0; ks < kKT / 32; ++ks) {
-      bf16x8_t af[4], bfr[4];
-#pragma unroll
-      for (int tm = 0; tm < 4; ++tm) {
-        const int r = wm * 64 + tm * 16 + l16;
-        af[tm] = *reinterpret_cast<const bf16x8_t*>(&As[r * kLdsStride + ks * 32 + quad * 8]);
-      }
-#pragma unroll
-      for (int tn = 0; tn < 4; ++tn) {
-        int r;
-        if (FC1) r = (tn < 2 ? 0 : 64) + wn * 32 + (tn & 1) * 16 + l16;
-        else r = wn * 64 + tn * 16 + l16;
-        bfr[tn] = *reinterpret_cast<const bf16x8_t*>(&Bs[r * kLdsStride + ks * 32 + quad * 8]);
-      }
-#pragma unroll
-      for (int tm = 0; tm < 4; ++tm)
-#pragma unroll
-        for (int tn = 0; tn < 4; ++tn)
-          acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[tm], bfr[tn], acc[tm][tn], 0, 0, 0);
-    }
+    // ---- stage st+1 into the other buffer (harmless after the last stage:
+    // it is never read), loads of stage st+2
+    store_stage(buf ^ 1);
+    load_stage(st + 2 < ns ? st + 2 : ns - 1);
     __syncthreads();
   }
+  if (!wave_live) return;
 
   // ---- epilogue: lane holds rows 4*quad + i, column l16 of each 16x16 tile
 #pragma unroll
@@ -172,17 +231,17 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(
       const int64_t orow = row0 + p;
       if (FC1) {
 #pragma unroll
-        for (int tn = 0; tn < 2; ++tn) {
-          const int c = n_tile * 64 + wn * 32 + tn * 16 + l16;
+        for (int tn = 0; tn < 4; ++tn) {
+          const int c = n0 + wn * 64 + tn * 16 + l16;
           if (c < I) {
-            const float hv = silu_mul(acc[tm][tn][i], acc[tm][tn + 2][i]);
+            const float hv = silu_mul_fast(acc[tm][tn][i], acc[tm][tn + 4][i]);
             h_out[orow * I + c] = static_cast<uint16_t>(f32_to_bf16(hv));
           }
         }
       } else {
 #pragma unroll
-        for (int tn = 0; tn < 4; ++tn) {
-          const int c = n_tile * kTileN + wn * 64 + tn * 16 + l16;
+        for (int tn = 0; tn < 8; ++tn) {
+          const int c = n0 + wn * 128 + tn * 16 + l16;
           if (c < H) y_out[orow * H + c] = acc[tm][tn][i];
         }
       }
@@ -239,16 +298,17 @@ hipError_t launch_gemms(const Layer& L, const uint16_t* xb, char* ws, const Work
   const int32_t* ntiles = reinterpret_cast<const int32_t*>(ws + W.num_tiles);
   uint16_t* hb = reinterpret_cast<uint16_t*>(ws + W.hbf16);
   float* yf = reinterpret_cast<float*>(ws + W.yf32);
-  const int nt1 = (I + 63) / 64;
-  const int nt2 = (H + kTileN - 1) / kTileN;
+  const int bs_shift = L.bs == 32 ? 5 : L.bs == 64 ? 6 : 7;   // block sizes are 32/64/128
+  const int nt1 = gemm_n_tiles(L, true);
+  const int nt2 = gemm_n_tiles(L, false);
   const int64_t g1 = 8 * ((W.max_tiles * nt1 + 7) / 8);
   const int64_t g2 = 8 * ((W.max_tiles * nt2 + 7) / 8);
-  grouped_gemm_kernel<BITS, true><<<static_cast<unsigned>(g1), 256, 0, s>>>(
-      xb, sorted, L.k, L.fc1_codes, L.fc1_scales, H, H, I, L.bs, L.zp, L.fc1_row_bytes, L.fc1_nblk,
+  grouped_gemm_kernel<BITS, true><<<static_cast<unsigned>(g1), kGemmThreads, 0, s>>>(
+      xb, sorted, L.k, L.fc1_codes, L.fc1_scales, H, H, I, bs_shift, L.zp, L.fc1_row_bytes, L.fc1_nblk,
       tiles, ntiles, nt1, hb, nullptr);
   stage_done(L, 6, "gemm_fc1_swiglu");
-  grouped_gemm_kernel<BITS, false><<<static_cast<unsigned>(g2), 256, 0, s>>>(
-      hb, sorted, L.k, L.fc2_codes, L.fc2_scales, I, H, I, L.bs, L.zp, L.fc2_row_bytes, L.fc2_nblk,
+  grouped_gemm_kernel<BITS, false><<<static_cast<unsigned>(g2), kGemmThreads, 0, s>>>(
+      hb, sorted, L.k, L.fc2_codes, L.fc2_scales, I, H, I, bs_shift, L.zp, L.fc2_row_bytes, L.fc2_nblk,
       tiles, ntiles, nt2, nullptr, yf);
   stage_done(L, 7, "gemm_fc2");
   return hipGetLastError();
