@@ -14,17 +14,30 @@ whose combined active-expert bytes exceed the 256 MB MALL, so the weights
 come from HBM as they would in a deep model.
 
 Roofline. A second pass enables the library's stage hook, which records a
-HIP event on the stream after each kernel launch; the dominant kernel's
-average duration comes from those events. Algorithmic bytes (decode) and
-FLOPs (prefill) per launch are counted from the routing the call actually
-made (distinct experts per call).
+HIP event on the stream after each kernel launch; per-kernel durations come
+from those events. The fused decode is a single launch per step, so its
+duration is the per-step time of the timed region itself. Algorithmic bytes
+(decode: active experts' codes and scales, x, logits, out) and FLOPs
+(prefill) per launch are counted from the routing the call actually made
+(distinct experts per call).
+
+HBM traffic. roofline.traffic is the dominant decode kernel's HBM bytes per
+launch as rocprofv3 counters measured them (FETCH_SIZE + WRITE_SIZE, each
+scaled by what the same counter reads for a plain copy of known size), read
+from the committed counter summary under profiles/ only if that summary was
+taken on the current kernel source (a digest of the sources is recorded with
+it); otherwise null.
 
 CPU baseline. The plain C oracle, timed on a bounded sample of tokens of the
 same workload on this host's cores.
+
+`--only decode4|decode1|prefill` runs one workload alone (for profiling) and
+prints its results instead of the benchmark line.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -45,6 +58,35 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 NROT = 24
 DEV = torch.device("cuda:0")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_fused_traffic_qwen3_int4_m4.txt")
+TRAFFIC_SOURCES = ["quantized_mixture_experts_qmoe_amd/csrc/decode_fused.hip",
+                   "quantized_mixture_experts_qmoe_amd/csrc/device.h",
+                   "quantized_mixture_experts_qmoe_amd/csrc/internal.h"]
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """Counter-measured HBM bytes per launch of the fused decode at M=4, or
+    None if there is no summary for the current kernel source."""
+    try:
+        with open(TRAFFIC_SUMMARY) as f:
+            kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith("#"))
+    except OSError:
+        return None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("source_digest") != kernel_source_digest():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def log(msg):
@@ -189,14 +231,18 @@ def bench_decode(T: int, steps: int, warmup: int):
     R = T * k
     fc1_bytes = D * fc1_b + T * H * 2 + T * E * 2 + R * I * 4
     layer_bytes = D * (fc1_b + fc2_b) + T * H * 2 * 2 + T * E * 2
-    if "decode_fused" in kt:
-        # one kernel computes the whole layer: its roofline is the whole layer's bytes
+    if list(kt) == ["decode_fused"]:
+        # one launch computes the whole layer, so a step is exactly one launch of
+        # it: its duration is the per-step time of the timed region (the stage
+        # hook's events would add the dispatch latency before the launch), and
+        # its algorithmic bytes are the layer's (active experts, x, logits, out)
         dom = "decode_fused"
-        dom_bytes = layer_bytes + R * I * 4 * 2 + R * H * 4 * 2
+        dom_bytes = layer_bytes
+        t_dom = ms * 1e-3
     else:
         dom = "decode_fc1_swiglu"
         dom_bytes = fc1_bytes
-    t_dom = kt[dom] * 1e-3
+        t_dom = kt[dom] * 1e-3
     return {
         "T": T, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
         "distinct_experts": D,
@@ -263,7 +309,14 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the M=1 and 8K prefill entries")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=48)
+    ap.add_argument("--only", choices=["decode4", "decode1", "prefill"], default=None,
+                    help="run one workload alone (profiling aid); prints its results")
+    ap.add_argument("--source-digest", action="store_true",
+                    help="print the digest of the fused decode sources and exit")
     args = ap.parse_args()
+    if args.source_digest:
+        print(kernel_source_digest())
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the layer is measured on one GPU's share)", file=sys.stderr)
@@ -272,6 +325,14 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     q.lib()   # fail loudly if the HIP library is missing
+
+    if args.only:
+        if args.only == "prefill":
+            res = bench_prefill(args.steps, args.warmup)
+        else:
+            res = bench_decode(4 if args.only == "decode4" else 1, args.steps, args.warmup)
+        print(json.dumps({"only": args.only, **res}), flush=True)
+        return
 
     main_res = bench_decode(4, args.steps, args.warmup)
     extra = []
@@ -316,7 +377,8 @@ def main():
                    "kernels_us": main_res["kernels_us"]},
         "roofline": {"bound": "hbm", "kernel": dom["kernel"], "achieved": dom["GBs"],
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dom["GBs"] / HBM_PEAK_GBS,
-                     "bytes_per_launch": dom["bytes"], "traffic": None},
+                     "bytes_per_launch": dom["bytes"],
+                     "traffic": measured_traffic() if dom["kernel"] == "decode_fused" else None},
         "cpu_baseline": cpu,
         "extra": extra,
     }
