@@ -308,7 +308,7 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--no-extra", action="store_true", help="skip the M=1 and 8K prefill entries")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=48)
+    ap.add_argument("--cpu-tokens", type=int, default=96)
     ap.add_argument("--only", choices=["decode4", "decode1", "prefill"], default=None,
                     help="run one workload alone (profiling aid); prints its results")
     ap.add_argument("--source-digest", action="store_true",
