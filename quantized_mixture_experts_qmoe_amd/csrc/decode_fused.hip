@@ -153,9 +153,31 @@ struct FusedLds {
   float ybuf[kFusedWaves][kDecodeMaxTokens][8 * kCap2];
 };
 
-// Share value v of lane (lane & ~3) | t with the four lanes of each block.
-__device__ __forceinline__ float quad_get(float v, int lane, int t) {
-  return __shfl(v, (lane & ~3) | t, kWave);
+// Cross-lane moves without the LDS crossbar (DPP and v_permlane*_swap).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// sum over lanes l, l-4, l-8, l-12 of each row of 16 (one residue class mod 4)
+__device__ __forceinline__ float row_class_sum(float v) {
+  v += dpp_f<0x124>(v);   // row_ror:4
+  v += dpp_f<0x128>(v);   // row_ror:8
+  return v;
+}
+// v of this lane plus v of the same lane in the paired row (rows 0+1, 2+3)
+__device__ __forceinline__ float row_pair_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// v of this lane plus v of the same lane in the other half of the wave
+__device__ __forceinline__ float half_pair_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// value of lane t of this lane's quad (DPP quad_perm [t, t, t, t])
+template <int T>
+__device__ __forceinline__ float quad_get(float v) {
+  return dpp_f<T * 0x55>(v);
 }
 
 }  // namespace
@@ -373,9 +395,12 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
   }
   float corr1[U1][kDecodeMaxTokens];
 #pragma unroll
-  for (int c = 0; c < U1; ++c)
-#pragma unroll
-    for (int t = 0; t < kDecodeMaxTokens; ++t) corr1[c][t] = zc * quad_get(sx[c], lane, t);
+  for (int c = 0; c < U1; ++c) {
+    corr1[c][0] = zc * quad_get<0>(sx[c]);
+    corr1[c][1] = zc * quad_get<1>(sx[c]);
+    corr1[c][2] = zc * quad_get<2>(sx[c]);
+    corr1[c][3] = zc * quad_get<3>(sx[c]);
+  }
 
   // one FC1 item: gate/up sums of two rows for every token, SwiGLU, into hbuf
   auto fc1_item = [&](const UnitWords<BITS> (&wv)[U1], const uint32_t (&sc)[U1], int li) {
@@ -394,16 +419,13 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
       for (int t = 0; t < kDecodeMaxTokens; ++t)
         acc[t] = fmaf(s128, dv[t], fmaf(-s, corr1[c][t], acc[t]));
     }
+    // sum over the 16 blocks: lanes 0..3 end with rows 0..3 (gate n, gate
+    // n+1, up n, up n+1); lanes 0 and 1 then take the up sums of lanes 2, 3
 #pragma unroll
-    for (int t = 0; t < kDecodeMaxTokens; ++t) {
-      acc[t] += __shfl_xor(acc[t], 4, kWave);
-      acc[t] += __shfl_xor(acc[t], 8, kWave);
-      acc[t] += __shfl_xor(acc[t], 16, kWave);
-      acc[t] += __shfl_xor(acc[t], 32, kWave);
-    }
+    for (int t = 0; t < kDecodeMaxTokens; ++t) acc[t] = half_pair_sum(row_pair_sum(row_class_sum(acc[t])));
     float up[kDecodeMaxTokens];
 #pragma unroll
-    for (int t = 0; t < kDecodeMaxTokens; ++t) up[t] = __shfl_down(acc[t], 2, kWave);
+    for (int t = 0; t < kDecodeMaxTokens; ++t) up[t] = dpp_f<0xEE>(acc[t]);   // quad_perm [2, 3, 2, 3]
     if (lane < 2)
 #pragma unroll
       for (int t = 0; t < kDecodeMaxTokens; ++t) S.hbuf[wave][t][2 * li + lane] = silu_mul(acc[t], up[t]);
@@ -543,12 +565,10 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
         for (int t = 0; t < kDecodeMaxTokens; ++t)
           acc[t] = fmaf(s128, dv[t], fmaf(-s, corr2[c][t], acc[t]));
       }
+      // sum over the 8 quant blocks of each half wave: lanes 0..3 end with
+      // rows 0..3 of the item, lanes 32..35 with rows 4..7
 #pragma unroll
-      for (int t = 0; t < kDecodeMaxTokens; ++t) {
-        acc[t] += __shfl_xor(acc[t], 4, kWave);
-        acc[t] += __shfl_xor(acc[t], 8, kWave);
-        acc[t] += __shfl_xor(acc[t], 16, kWave);
-      }
+      for (int t = 0; t < kDecodeMaxTokens; ++t) acc[t] = row_pair_sum(row_class_sum(acc[t]));
       if ((lane & ~32) < 4)
 #pragma unroll
         for (int t = 0; t < kDecodeMaxTokens; ++t)

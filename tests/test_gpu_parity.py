@@ -274,7 +274,8 @@ def test_prefill_parity_full(name, T):
     check_prefill(wl, layer_for(wl, max(T, 8)))
 
 
-@pytest.mark.parametrize("name,T,n", [("prefill", 8192, 48), ("int3", 2048, 48), ("stack", 4096, 32)])
+@pytest.mark.parametrize("name,T,n", [("prefill", 8192, 48), ("int3", 2048, 48), ("stack", 4096, 32),
+                                      ("stack", 32768, 24)])
 def test_prefill_parity_sampled(name, T, n):
     say(f"prefill sampled {name} T={T}")
     wl = qi.make_workload(name, T=T)
