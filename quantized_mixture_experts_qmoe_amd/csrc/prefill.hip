@@ -14,10 +14,13 @@
 //        [R, H] in sorted order.
 // The tall tile shares each dequantized weight among 256 rows; a wave whose
 // 64 rows all lie past the expert's last route skips its matrix work.
-// The K loop runs in stages of 64 with two LDS buffers: while the waves run
-// the MFMAs of stage s, each thread dequantizes and stores stage s+1 from
-// registers and issues the global loads of stage s+2, so global latency is
-// covered by a whole stage of matrix work; one barrier per stage.
+// The K loop runs in stages of 64 with two LDS buffers, ping-pong style: the
+// waves form two groups of four (rows 0-127 and 128-255 of the tile) that
+// run half a stage apart. In each phase between two barriers one group runs
+// the MFMAs of stage s while the other dequantizes and stores its share of
+// stage s+1 (its own A rows and half of B) and issues its global loads for
+// stage s+2; each SIMD holds one wave of each group, so its matrix and vector
+// work overlap.
 // A combine kernel then sums each token's k slots in slot order and rounds
 // once.
 //
@@ -42,7 +45,7 @@ constexpr int kKT = 64;                 // K per stage (two 16x16x32 MFMA steps)
 constexpr int kLdsStride = kKT + 8;     // bf16 per LDS row (padding against bank conflicts)
 constexpr int kBM = kTileM;             // A rows per tile (256)
 constexpr int kBN = 256;                // B rows per tile
-constexpr int kGemmThreads = 512;       // 8 waves: 4 along M x 2 along N, 64 x 128 each
+constexpr int kGemmThreads = 512;       // 8 waves: 2 groups of 2 x 2 waves of 64 x 128
 static_assert(kBM == 256, "the staging below assumes 256-row tiles");
 
 // Logical tile index of this workgroup. Workgroups are dealt to the 8 XCDs
@@ -88,16 +91,20 @@ void grouped_gemm_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
-  const bool wave_live = wm * 64 < nrows;   // uniform: this wave's rows hold routes
-  const int n_rows_total = FC1 ? 2 * I : H;                    // rows of W
+  // two groups of four waves, half a stage apart: group g owns rows
+  // [128 g, 128 g + 128) of the tile; in each phase one group runs its MFMAs
+  // while the other stores its share of the next stage
+  const int grp = wave >> 2, gw = wave & 3, gt = tid & 255;
+  const int wm = 2 * grp + (gw >> 1), wn = gw & 1;
+  const bool wave_live = wm * 64 < nrows;
+  const int n_rows_total = FC1 ? 2 * I : H;
   const uint8_t* ebase = codes + static_cast<int64_t>(e) * n_rows_total * row_bytes;
   const uint16_t* sbase = scales + static_cast<int64_t>(e) * n_rows_total * nblk;
   const int n0 = n_tile * (FC1 ? kBN / 2 : kBN);
 
-  // this thread's B work: one unit (32 codes) per stage: row tid >> 1, K
-  // offset 32 * (tid & 1). Rows past the matrix read row 0 instead.
-  const int b_row = tid >> 1, b_kq = tid & 1;
+  // this thread's B share: unit 256 grp + gt of the stage's 512 (row u >> 1,
+  // K offset 32 * (u & 1))
+  const int b_unit = 256 * grp + gt, b_row = b_unit >> 1, b_kq = b_unit & 1;
   int w_row;
   if (FC1) {
     const int c = n0 + (b_row & (kBN / 2 - 1));
@@ -109,18 +116,13 @@ void grouped_gemm_kernel(
   const uint8_t* b_ptr = ebase + static_cast<int64_t>(w_row) * row_bytes;
   const uint16_t* s_ptr = sbase + static_cast<int64_t>(w_row) * nblk;
 
-  // this thread's A work: 32 bf16 (four 16-byte chunks) of row tid >> 1 per
-  // stage. Rows past the tile read the tile's first row: they only feed
-  // output rows that are never stored.
-  const int a_row = tid >> 1, a_col = (tid & 1) * 32;
+  // this thread's A share: 32 bf16 of row 128 grp + (gt >> 1)
+  const int a_row = 128 * grp + (gt >> 1), a_col = (gt & 1) * 32;
   const int a_src_row = a_row < nrows ? a_row : 0;
   const int64_t a_ld = FC1 ? H : I;
   const int64_t src_row = FC1 ? (sorted_routes[row0 + a_src_row] / k) : (row0 + a_src_row);
   const uint16_t* a_ptr = a_src + src_row * a_ld + a_col;
 
-  // stage registers. Loads are unconditional (stages past K re-read a valid
-  // address, so the wait counts stay exact); a B unit past K gets a zero
-  // scale, which cancels whatever A holds there.
   uint4 ra0, ra1, ra2, ra3;
   UnitWords<BITS> rb;
   uint32_t rs;
@@ -136,26 +138,15 @@ void grouped_gemm_kernel(
     rb = load_unit<BITS>(b_ptr + (kb / 32) * (4 * BITS));
     rs = s_ptr[kb >> bs_shift] | (kk < K ? 0u : 0x10000u);   // bit 16: past K
   };
-  auto store_a = [&](int buf) {
+  auto store_stage = [&](int buf) {
     uint4* ad = reinterpret_cast<uint4*>(&As[buf][a_row * kLdsStride + a_col]);
     ad[0] = ra0;
     ad[1] = ra1;
     ad[2] = ra2;
     ad[3] = ra3;
-  };
-  auto store_b = [&](int buf, const uint32_t (&pairs)[16]) {
-    uint4* bd = reinterpret_cast<uint4*>(&Bs[buf][b_row * kLdsStride + 32 * b_kq]);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) bd[q] = make_uint4(pairs[4 * q], pairs[4 * q + 1], pairs[4 * q + 2], pairs[4 * q + 3]);
-  };
-  auto stage_scale = [&]() {
-    return (rs >> 16) ? 0.0f : half_to_f32(static_cast<uint16_t>(rs));
-  };
-  auto store_stage = [&](int buf) {
-    store_a(buf);
     uint32_t pairs[16];
     {
-      const float sc = stage_scale();
+      const float sc = (rs >> 16) ? 0.0f : half_to_f32(static_cast<uint16_t>(rs));
       float q[16];
       uint32_t p0[8];
       unit_half_codes<BITS>(rb, 0, q);
@@ -165,7 +156,9 @@ void grouped_gemm_kernel(
       dequant_codes_bf16<8>(q, sc, zp, p0);
       for (int p = 0; p < 8; ++p) pairs[8 + p] = p0[p];
     }
-    store_b(buf, pairs);
+    uint4* bd = reinterpret_cast<uint4*>(&Bs[buf][b_row * kLdsStride + 32 * b_kq]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) bd[q] = make_uint4(pairs[4 * q], pairs[4 * q + 1], pairs[4 * q + 2], pairs[4 * q + 3]);
   };
 
   f32x4_t acc[4][8];
@@ -187,37 +180,50 @@ void grouped_gemm_kernel(
   auto frag_b = [&](int buf, int ks, int tn) {
     return *reinterpret_cast<const bf16x8_t*>(&Bs[buf][b_frag_row[tn] * kLdsStride + ks * 32 + quad * 8]);
   };
-
+  auto mfma_stage = [&](int buf) {
+    if (!wave_live) return;
+#pragma unroll
+    for (int ks = 0; ks < kKT / 32; ++ks) {
+      bf16x8_t af[4], bfr[8];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) af[t] = frag_a(buf, ks, t);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) bfr[t] = frag_b(buf, ks, t);
+#pragma unroll
+      for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < 8; ++tn)
+          acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[tm], bfr[tn], acc[tm][tn], 0, 0, 0);
+    }
+  };
 
   const int ns = (K + kKT - 1) / kKT;
+  auto clampst = [&](int st) { return st < ns ? st : ns - 1; };
+  // prologue: stage 0 complete in buffer 0; registers hold stage 1
   load_stage(0);
   store_stage(0);
-  load_stage(ns > 1 ? 1 : 0);
+  load_stage(clampst(1));
   __syncthreads();
-  for (int st = 0; st < ns; ++st) {
-    const int buf = st & 1;
-    // ---- MFMA on stage st: all fragments of the stage are read first, then
-    // the 32 MFMAs issue back to back
-    if (wave_live) {
-#pragma unroll
-      for (int ks = 0; ks < kKT / 32; ++ks) {
-        bf16x8_t af[4], bfr[8];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) af[t] = frag_a(buf, ks, t);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) bfr[t] = frag_b(buf, ks, t);
-#pragma unroll
-        for (int tm = 0; tm < 4; ++tm)
-#pragma unroll
-          for (int tn = 0; tn < 8; ++tn)
-            acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[tm], bfr[tn], acc[tm][tn], 0, 0, 0);
-      }
+  // one loop per group (same barrier sequence), so each keeps only its own
+  // live registers
+  if (grp == 0) {
+    for (int st = 0; st < ns; ++st) {
+      const int buf = st & 1;
+      mfma_stage(buf);             // phase X
+      __syncthreads();
+      store_stage(buf ^ 1);        // phase Y
+      load_stage(clampst(st + 2));
+      __syncthreads();
     }
-    // ---- stage st+1 into the other buffer (harmless after the last stage:
-    // it is never read), loads of stage st+2
-    store_stage(buf ^ 1);
-    load_stage(st + 2 < ns ? st + 2 : ns - 1);
-    __syncthreads();
+  } else {
+    for (int st = 0; st < ns; ++st) {
+      const int buf = st & 1;
+      store_stage(buf ^ 1);        // phase X
+      load_stage(clampst(st + 2));
+      __syncthreads();
+      mfma_stage(buf);             // phase Y
+      __syncthreads();
+    }
   }
   if (!wave_live) return;
 
