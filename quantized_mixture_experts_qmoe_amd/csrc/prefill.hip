@@ -116,34 +116,42 @@ void grouped_gemm_kernel(
   const uint8_t* b_ptr = ebase + static_cast<int64_t>(w_row) * row_bytes;
   const uint16_t* s_ptr = sbase + static_cast<int64_t>(w_row) * nblk;
 
-  // this thread's A share: 32 bf16 of row 128 grp + (gt >> 1)
-  const int a_row = 128 * grp + (gt >> 1), a_col = (gt & 1) * 32;
-  const int a_src_row = a_row < nrows ? a_row : 0;
+  // this thread's A share: the 16-byte chunk (lane & 7) of rows
+  // 128 grp + 32 gw + 8 q + (lane >> 3), q = 0..3, so each load instruction
+  // reads whole 128-byte row segments (eight rows per instruction)
   const int64_t a_ld = FC1 ? H : I;
-  const int64_t src_row = FC1 ? (sorted_routes[row0 + a_src_row] / k) : (row0 + a_src_row);
-  const uint16_t* a_ptr = a_src + src_row * a_ld + a_col;
+  const int a_chunk = (lane & 7) * 8;
+  const int a_row0 = 128 * grp + 32 * gw + (lane >> 3);
+  const uint16_t* a_ptr[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = a_row0 + 8 * q;
+    const int rr = r < nrows ? r : 0;
+    const int64_t src_row = FC1 ? (sorted_routes[row0 + rr] / k) : (row0 + rr);
+    a_ptr[q] = a_src + src_row * a_ld + a_chunk;
+  }
 
   uint4 ra0, ra1, ra2, ra3;
   UnitWords<BITS> rb;
   uint32_t rs;
   auto load_stage = [&](int st) {
     const int k0 = st * kKT;
-    const uint16_t* ap = a_ptr + ((k0 + a_col < K) ? k0 : 0);
-    ra0 = *reinterpret_cast<const uint4*>(ap);
-    ra1 = *reinterpret_cast<const uint4*>(ap + 8);
-    ra2 = *reinterpret_cast<const uint4*>(ap + 16);
-    ra3 = *reinterpret_cast<const uint4*>(ap + 24);
+    const int ka = (k0 + a_chunk < K) ? k0 : 0;
+    ra0 = *reinterpret_cast<const uint4*>(a_ptr[0] + ka);
+    ra1 = *reinterpret_cast<const uint4*>(a_ptr[1] + ka);
+    ra2 = *reinterpret_cast<const uint4*>(a_ptr[2] + ka);
+    ra3 = *reinterpret_cast<const uint4*>(a_ptr[3] + ka);
     const int kk = k0 + 32 * b_kq;
     const int kb = (kk < K) ? kk : 0;
     rb = load_unit<BITS>(b_ptr + (kb / 32) * (4 * BITS));
     rs = s_ptr[kb >> bs_shift] | (kk < K ? 0u : 0x10000u);   // bit 16: past K
   };
   auto store_stage = [&](int buf) {
-    uint4* ad = reinterpret_cast<uint4*>(&As[buf][a_row * kLdsStride + a_col]);
-    ad[0] = ra0;
-    ad[1] = ra1;
-    ad[2] = ra2;
-    ad[3] = ra3;
+    uint16_t* ad = &As[buf][a_row0 * kLdsStride + a_chunk];
+    *reinterpret_cast<uint4*>(ad) = ra0;
+    *reinterpret_cast<uint4*>(ad + 8 * kLdsStride) = ra1;
+    *reinterpret_cast<uint4*>(ad + 16 * kLdsStride) = ra2;
+    *reinterpret_cast<uint4*>(ad + 24 * kLdsStride) = ra3;
     uint32_t pairs[16];
     {
       const float sc = (rs >> 16) ? 0.0f : half_to_f32(static_cast<uint16_t>(rs));
