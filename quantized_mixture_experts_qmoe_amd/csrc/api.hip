@@ -69,7 +69,7 @@ static Workspace layout(const Layer& L, int64_t T, bool decode) {
     W.h32 = take(static_cast<size_t>(R * L.I * 4));
     W.y32 = take(static_cast<size_t>(R * L.H * 4));
   } else {
-    W.nchunks = (R + kRouteChunk - 1) / kRouteChunk;
+    W.nchunks = (T + kChunkTokens - 1) / kChunkTokens;
     W.max_tiles = (R + kTileM - 1) / kTileM + L.E;
     W.hist = take(static_cast<size_t>(W.nchunks * L.E * 4));
     W.chunk_base = take(static_cast<size_t>(W.nchunks * L.E * 4));

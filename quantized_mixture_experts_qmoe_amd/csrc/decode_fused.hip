@@ -99,40 +99,6 @@ __device__ __forceinline__ float tag_value(uint64_t e) {
   return __uint_as_float(static_cast<uint32_t>(e));
 }
 
-// Routing key of a bf16 logit: the order-preserving 16-bit image of the value
-// (-0 folded into +0) above the inverted expert index, so the largest key is
-// the largest logit and, among equal logits, the lowest expert index.
-__device__ __forceinline__ uint32_t logit_key(uint32_t b, int e) {
-  b = (b == 0x8000u) ? 0u : b;
-  const uint32_t ord = (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u);
-  return (ord << 16) | (0xFFFFu - static_cast<uint32_t>(e));
-}
-__device__ __forceinline__ float key_logit(uint32_t key) {
-  const uint32_t ord = key >> 16;
-  return bf16_to_f32((ord & 0x8000u) ? (ord & 0x7FFFu) : (~ord & 0xFFFFu));
-}
-__device__ __forceinline__ int key_to_expert(uint32_t key) {
-  return 0xFFFF - static_cast<int>(key & 0xFFFFu);
-}
-
-template <int CTRL, int ROWS>
-__device__ __forceinline__ uint32_t dpp_umax(uint32_t v) {
-  const uint32_t p = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
-      static_cast<int>(v), static_cast<int>(v), CTRL, ROWS, 0xF, false));
-  return p > v ? p : v;
-}
-
-// Maximum over the wavefront, returned uniformly.
-__device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
-  v = dpp_umax<0x128, 0xF>(v);   // row_ror:8
-  v = dpp_umax<0x124, 0xF>(v);   // row_ror:4
-  v = dpp_umax<0x122, 0xF>(v);   // row_ror:2
-  v = dpp_umax<0x121, 0xF>(v);   // row_ror:1
-  v = dpp_umax<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
-  v = dpp_umax<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
-  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
-}
-
 struct FusedLds {
   int32_t ids[kMaxRoutes];                            // route r = t*k + j -> expert
   float w[kMaxRoutes];                                // routing weight of route r

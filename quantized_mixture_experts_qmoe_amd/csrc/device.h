@@ -257,12 +257,46 @@ __device__ __forceinline__ int key_expert(uint64_t key) {
   return static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(key));
 }
 
+// Routing key of a bf16 logit: the order-preserving 16-bit image of the value
+// (-0 folded into +0) above the inverted expert index, so the largest key is
+// the largest logit and, among equal logits, the lowest expert index.
+__device__ __forceinline__ uint32_t logit_key(uint32_t b, int e) {
+  b = (b == 0x8000u) ? 0u : b;
+  const uint32_t ord = (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u);
+  return (ord << 16) | (0xFFFFu - static_cast<uint32_t>(e));
+}
+__device__ __forceinline__ float key_logit(uint32_t key) {
+  const uint32_t ord = key >> 16;
+  return bf16_to_f32((ord & 0x8000u) ? (ord & 0x7FFFu) : (~ord & 0xFFFFu));
+}
+__device__ __forceinline__ int key_to_expert(uint32_t key) {
+  return 0xFFFF - static_cast<int>(key & 0xFFFFu);
+}
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_umax(uint32_t v) {
+  const uint32_t p = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+      static_cast<int>(v), static_cast<int>(v), CTRL, ROWS, 0xF, false));
+  return p > v ? p : v;
+}
+
+// Maximum over the wavefront, returned uniformly.
+__device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
+  v = dpp_umax<0x128, 0xF>(v);   // row_ror:8
+  v = dpp_umax<0x124, 0xF>(v);   // row_ror:4
+  v = dpp_umax<0x122, 0xF>(v);   // row_ror:2
+  v = dpp_umax<0x121, 0xF>(v);   // row_ror:1
+  v = dpp_umax<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+  v = dpp_umax<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
+}
+
 // One wavefront selects the top-k experts of one token and computes the
 // softmax over the k selected logits. Slot j holds the j-th largest logit
 // (ties to the lower expert index). Lanes j < k write ids[j] and w[j].
 template <typename ACT>
-__device__ __forceinline__ void topk_softmax_wave(const ACT* logits, int E, int k, int lane,
-                                                  int32_t* ids, float* w) {
+__device__ __forceinline__ void topk_softmax_wave_r(const ACT* logits, int E, int k, int lane,
+                                                    int& id, float& wt) {
   uint64_t keys[kMaxExperts / kWave];
 #pragma unroll
   for (int i = 0; i < kMaxExperts / kWave; ++i) {
@@ -292,10 +326,48 @@ __device__ __forceinline__ void topk_softmax_wave(const ACT* logits, int E, int 
   }
   const float ex = (lane < k) ? expf(my_v - v0) : 0.0f;
   const float sum = wave_sum(ex);
+  id = my_id;
+  wt = ex / sum;
+}
+template <typename ACT>
+__device__ __forceinline__ void topk_softmax_wave(const ACT* logits, int E, int k, int lane,
+                                                  int32_t* ids, float* w) {
+  int id;
+  float wt;
+  topk_softmax_wave_r(logits, E, k, lane, id, wt);
   if (lane < k) {
-    ids[lane] = my_id;
-    w[lane] = ex / sum;
+    ids[lane] = id;
+    w[lane] = wt;
   }
+}
+
+// The same selection for bf16 logits with 32-bit keys (logit_key) and DPP
+// reductions; SLOTS logits per lane (E <= 64 * SLOTS). Lanes j < k receive
+// slot j's expert and weight.
+template <int SLOTS>
+__device__ __forceinline__ void topk_softmax_bf16_wave(const uint16_t (&lg)[SLOTS], int E, int k,
+                                                       int lane, int& id, float& wt) {
+  uint32_t keys[SLOTS];
+#pragma unroll
+  for (int c = 0; c < SLOTS; ++c) {
+    const int e = lane + kWave * c;
+    keys[c] = (e < E) ? logit_key(lg[c], e) : 0u;
+  }
+  uint32_t mine = 0u, first = 0u;
+  for (int j = 0; j < k; ++j) {
+    uint32_t b = keys[0];
+#pragma unroll
+    for (int c = 1; c < SLOTS; ++c) b = keys[c] > b ? keys[c] : b;
+    b = wave_umax(b);
+    if (j == 0) first = b;
+    if (lane == j) mine = b;
+#pragma unroll
+    for (int c = 0; c < SLOTS; ++c) keys[c] = (keys[c] == b) ? 0u : keys[c];
+  }
+  const float ex = (lane < k) ? expf(key_logit(mine) - key_logit(first)) : 0.0f;
+  const float sum = wave_sum(ex);
+  id = key_to_expert(mine);
+  wt = ex / sum;
 }
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }

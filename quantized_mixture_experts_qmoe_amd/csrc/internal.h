@@ -34,7 +34,7 @@ inline void stage_done(const Layer& L, int stage, const char* name) {
 // Prefill GEMM tiling (rows = routes of one expert, cols = output features).
 constexpr int kTileM = 256;
 constexpr int kTileN = 128;
-constexpr int kRouteChunk = 256;           // routes per histogram/scatter chunk
+constexpr int kChunkTokens = 32;           // tokens per histogram/scatter chunk
 
 // Decode GEMV row blocking.
 struct GemvShape {

@@ -1,7 +1,7 @@
 // Routing for the grouped (prefill) path: top-k + softmax over the selected
-// logits, a per-chunk expert histogram, one scan that yields expert offsets,
-// per-chunk scatter bases and the GEMM tile list, and a stable scatter of the
-// route ids into expert-sorted order.
+// logits fused with a per-chunk expert histogram (chunks of 32 tokens), one
+// scan that yields expert offsets, per-chunk scatter bases and the GEMM tile
+// list, and a stable scatter of the route ids into expert-sorted order.
 //
 // Semantics: top-k on the raw router logits with a softmax over the selected
 // k ("Document and test packed token inputs for MoE and QMoE", review of the
@@ -14,25 +14,71 @@
 
 namespace qmoe {
 
-template <typename ACT>
-__global__ __launch_bounds__(256) void route_topk_kernel(const ACT* __restrict__ logits, int64_t T,
-                                                         int E, int k, int32_t* __restrict__ topk_id,
-                                                         float* __restrict__ topk_w) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  topk_softmax_wave(logits + t * E, E, k, lane, topk_id + t * k, topk_w + t * k);
-}
-
-// hist[c][e] = number of routes of chunk c (routes [256c, 256c+256)) sent to e.
-__global__ __launch_bounds__(256) void route_hist_kernel(const int32_t* __restrict__ topk_id,
-                                                         int64_t R, int E,
-                                                         int32_t* __restrict__ hist) {
+// Top-k + softmax of the chunk's tokens (chunk c = tokens [32c, 32c + 32);
+// wave w takes eight of them in turn, loading the next token's logits while
+// it selects the current one) and the chunk's expert histogram:
+// hist[c][e] = number of the chunk's routes sent to e.
+template <int SLOTS>
+__global__ __launch_bounds__(256) void route_topk_hist_bf16_kernel(
+    const uint16_t* __restrict__ logits, int64_t T, int E, int k, int32_t* __restrict__ topk_id,
+    float* __restrict__ topk_w, int32_t* __restrict__ hist) {
   __shared__ int32_t s_hist[kMaxExperts];
   for (int e = threadIdx.x; e < E; e += 256) s_hist[e] = 0;
   __syncthreads();
-  const int64_t r = static_cast<int64_t>(blockIdx.x) * kRouteChunk + threadIdx.x;
-  if (r < R) atomicAdd(&s_hist[topk_id[r]], 1);
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  constexpr int kPerWave = kChunkTokens / 4;
+  const int64_t tw = static_cast<int64_t>(blockIdx.x) * kChunkTokens + wave * kPerWave;
+  auto load = [&](int64_t t, uint16_t (&lg)[SLOTS]) {
+    const int64_t tc = t < T ? t : T - 1;
+#pragma unroll
+    for (int c = 0; c < SLOTS; ++c) {
+      const int e = lane + kWave * c;
+      lg[c] = logits[tc * E + (e < E ? e : 0)];
+    }
+  };
+  uint16_t cur[SLOTS], nxt[SLOTS];
+  load(tw, cur);
+  for (int i = 0; i < kPerWave; ++i) {
+    const int64_t t = tw + i;
+    if (t >= T) break;
+    load(t + 1, nxt);
+    int id;
+    float wt;
+    topk_softmax_bf16_wave<SLOTS>(cur, E, k, lane, id, wt);
+    if (lane < k) {
+      topk_id[t * k + lane] = id;
+      topk_w[t * k + lane] = wt;
+      atomicAdd(&s_hist[id], 1);
+    }
+#pragma unroll
+    for (int c = 0; c < SLOTS; ++c) cur[c] = nxt[c];
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) hist[static_cast<int64_t>(blockIdx.x) * E + e] = s_hist[e];
+}
+
+// The same for fp32 logits (64-bit keys: fp32 value, then the inverted index).
+__global__ __launch_bounds__(256) void route_topk_hist_f32_kernel(
+    const float* __restrict__ logits, int64_t T, int E, int k, int32_t* __restrict__ topk_id,
+    float* __restrict__ topk_w, int32_t* __restrict__ hist) {
+  __shared__ int32_t s_hist[kMaxExperts];
+  for (int e = threadIdx.x; e < E; e += 256) s_hist[e] = 0;
+  __syncthreads();
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  constexpr int kPerWave = kChunkTokens / 4;
+  const int64_t tw = static_cast<int64_t>(blockIdx.x) * kChunkTokens + wave * kPerWave;
+  for (int i = 0; i < kPerWave; ++i) {
+    const int64_t t = tw + i;
+    if (t >= T) break;
+    int id;
+    float wt;
+    topk_softmax_wave_r(logits + t * E, E, k, lane, id, wt);
+    if (lane < k) {
+      topk_id[t * k + lane] = id;
+      topk_w[t * k + lane] = wt;
+      atomicAdd(&s_hist[id], 1);
+    }
+  }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += 256) hist[static_cast<int64_t>(blockIdx.x) * E + e] = s_hist[e];
 }
@@ -68,8 +114,17 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restr
   if (active) {
     c0 = nchunks * p / P;
     c1 = nchunks * (p + 1) / P;
+    // (batches of eight independent loads)
     int32_t sum = 0;
-    for (int64_t c = c0; c < c1; ++c) sum += hist[c * E + e];
+    int64_t c = c0;
+    for (; c + 8 <= c1; c += 8) {
+      int32_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = hist[(c + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) sum += v[u];
+    }
+    for (; c < c1; ++c) sum += hist[c * E + e];
     s_part[p * E + e] = sum;
   }
   __syncthreads();
@@ -97,7 +152,18 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restr
   if (active) {
     const int32_t expert_start = (e == 0) ? 0 : s_scan[e - 1];
     int32_t run = expert_start + s_part[p * E + e];
-    for (int64_t c = c0; c < c1; ++c) {
+    int64_t c = c0;
+    for (; c + 8 <= c1; c += 8) {
+      int32_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = hist[(c + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        chunk_base[(c + u) * E + e] = run;
+        run += v[u];
+      }
+    }
+    for (; c < c1; ++c) {
       chunk_base[c * E + e] = run;
       run += hist[c * E + e];
     }
@@ -116,21 +182,23 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restr
 // Stable scatter: a route's rank among the earlier routes of its chunk that
 // chose the same expert, added to the chunk's base for that expert.
 __global__ __launch_bounds__(256) void route_scatter_kernel(const int32_t* __restrict__ topk_id,
-                                                            int64_t R, int E,
+                                                            int64_t R, int k, int E,
                                                             const int32_t* __restrict__ chunk_base,
                                                             int32_t* __restrict__ sorted_routes,
                                                             int32_t* __restrict__ inv_pos) {
-  __shared__ int32_t s_e[kRouteChunk];
-  const int64_t r = static_cast<int64_t>(blockIdx.x) * kRouteChunk + threadIdx.x;
-  const int32_t e = (r < R) ? topk_id[r] : -1;
-  s_e[threadIdx.x] = e;
+  __shared__ int32_t s_e[kChunkTokens * kMaxTopK];
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kChunkTokens * k;
+  const int n = static_cast<int>(min(static_cast<int64_t>(kChunkTokens) * k, R - r0));
+  for (int i = threadIdx.x; i < n; i += 256) s_e[i] = topk_id[r0 + i];
   __syncthreads();
-  if (r >= R) return;
-  int32_t rank = 0;
-  for (int i = 0; i < static_cast<int>(threadIdx.x); ++i) rank += (s_e[i] == e);
-  const int32_t pos = chunk_base[static_cast<int64_t>(blockIdx.x) * E + e] + rank;
-  sorted_routes[pos] = static_cast<int32_t>(r);
-  inv_pos[r] = pos;
+  for (int i = threadIdx.x; i < n; i += 256) {
+    const int32_t e = s_e[i];
+    int32_t rank = 0;
+    for (int j = 0; j < i; ++j) rank += (s_e[j] == e);
+    const int32_t pos = chunk_base[static_cast<int64_t>(blockIdx.x) * E + e] + rank;
+    sorted_routes[pos] = static_cast<int32_t>(r0 + i);
+    inv_pos[r0 + i] = pos;
+  }
 }
 
 hipError_t launch_route(const Layer& L, const void* logits, int64_t T, char* ws, const Workspace& W,
@@ -138,18 +206,25 @@ hipError_t launch_route(const Layer& L, const void* logits, int64_t T, char* ws,
   const int E = static_cast<int>(L.E), k = L.k;
   int32_t* topk_id = reinterpret_cast<int32_t*>(ws + W.topk_id);
   float* topk_w = reinterpret_cast<float*>(ws + W.topk_w);
-  const unsigned gt = static_cast<unsigned>((T + 3) / 4);
-  if (L.act_bf16)
-    route_topk_kernel<uint16_t><<<gt, 256, 0, s>>>(static_cast<const uint16_t*>(logits), T, E, k,
-                                                    topk_id, topk_w);
-  else
-    route_topk_kernel<float><<<gt, 256, 0, s>>>(static_cast<const float*>(logits), T, E, k, topk_id,
-                                                 topk_w);
-  stage_done(L, 1, "route_topk");
-  const unsigned nc = static_cast<unsigned>(W.nchunks);
   int32_t* hist = reinterpret_cast<int32_t*>(ws + W.hist);
-  route_hist_kernel<<<nc, 256, 0, s>>>(topk_id, W.R, E, hist);
-  stage_done(L, 2, "route_hist");
+  const unsigned nc = static_cast<unsigned>(W.nchunks);
+  if (L.act_bf16) {
+    const uint16_t* lg = static_cast<const uint16_t*>(logits);
+    if (E <= 64)
+      route_topk_hist_bf16_kernel<1><<<nc, 256, 0, s>>>(lg, T, E, k, topk_id, topk_w, hist);
+    else if (E <= 128)
+      route_topk_hist_bf16_kernel<2><<<nc, 256, 0, s>>>(lg, T, E, k, topk_id, topk_w, hist);
+    else if (E <= 256)
+      route_topk_hist_bf16_kernel<4><<<nc, 256, 0, s>>>(lg, T, E, k, topk_id, topk_w, hist);
+    else if (E <= 512)
+      route_topk_hist_bf16_kernel<8><<<nc, 256, 0, s>>>(lg, T, E, k, topk_id, topk_w, hist);
+    else
+      route_topk_hist_bf16_kernel<16><<<nc, 256, 0, s>>>(lg, T, E, k, topk_id, topk_w, hist);
+  } else {
+    route_topk_hist_f32_kernel<<<nc, 256, 0, s>>>(static_cast<const float*>(logits), T, E, k, topk_id,
+                                                   topk_w, hist);
+  }
+  stage_done(L, 1, "route_topk_hist");
   route_scan_kernel<<<1, 1024, 0, s>>>(hist, W.nchunks, E, kTileM,
                                        reinterpret_cast<int32_t*>(ws + W.counts),
                                        reinterpret_cast<int32_t*>(ws + W.offsets),
@@ -157,7 +232,7 @@ hipError_t launch_route(const Layer& L, const void* logits, int64_t T, char* ws,
                                        reinterpret_cast<int4*>(ws + W.tiles),
                                        reinterpret_cast<int32_t*>(ws + W.num_tiles));
   stage_done(L, 3, "route_scan");
-  route_scatter_kernel<<<nc, 256, 0, s>>>(topk_id, W.R, E,
+  route_scatter_kernel<<<nc, 256, 0, s>>>(topk_id, W.R, k, E,
                                           reinterpret_cast<const int32_t*>(ws + W.chunk_base),
                                           reinterpret_cast<int32_t*>(ws + W.sorted_routes),
                                           reinterpret_cast<int32_t*>(ws + W.inv_pos));
