@@ -15,18 +15,18 @@
 namespace qmoe {
 
 // Top-k + softmax of the chunk's tokens (chunk c = tokens [32c, 32c + 32);
-// wave w takes eight of them in turn, loading the next token's logits while
+// wave w of eight takes four of them in turn, loading the next token's logits while
 // it selects the current one) and the chunk's expert histogram:
 // hist[c][e] = number of the chunk's routes sent to e.
 template <int SLOTS>
-__global__ __launch_bounds__(256) void route_topk_hist_bf16_kernel(
+__global__ __launch_bounds__(512) void route_topk_hist_bf16_kernel(
     const uint16_t* __restrict__ logits, int64_t T, int E, int k, int32_t* __restrict__ topk_id,
     float* __restrict__ topk_w, int32_t* __restrict__ hist) {
   __shared__ int32_t s_hist[kMaxExperts];
-  for (int e = threadIdx.x; e < E; e += 256) s_hist[e] = 0;
+  for (int e = threadIdx.x; e < E; e += 512) s_hist[e] = 0;
   __syncthreads();
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-  constexpr int kPerWave = kChunkTokens / 4;
+  constexpr int kPerWave = kChunkTokens / 8;
   const int64_t tw = static_cast<int64_t>(blockIdx.x) * kChunkTokens + wave * kPerWave;
   auto load = [&](int64_t t, uint16_t (&lg)[SLOTS]) {
     const int64_t tc = t < T ? t : T - 1;
@@ -54,18 +54,18 @@ __global__ __launch_bounds__(256) void route_topk_hist_bf16_kernel(
     for (int c = 0; c < SLOTS; ++c) cur[c] = nxt[c];
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += 256) hist[static_cast<int64_t>(blockIdx.x) * E + e] = s_hist[e];
+  for (int e = threadIdx.x; e < E; e += 512) hist[static_cast<int64_t>(blockIdx.x) * E + e] = s_hist[e];
 }
 
 // The same for fp32 logits (64-bit keys: fp32 value, then the inverted index).
-__global__ __launch_bounds__(256) void route_topk_hist_f32_kernel(
+__global__ __launch_bounds__(512) void route_topk_hist_f32_kernel(
     const float* __restrict__ logits, int64_t T, int E, int k, int32_t* __restrict__ topk_id,
     float* __restrict__ topk_w, int32_t* __restrict__ hist) {
   __shared__ int32_t s_hist[kMaxExperts];
-  for (int e = threadIdx.x; e < E; e += 256) s_hist[e] = 0;
+  for (int e = threadIdx.x; e < E; e += 512) s_hist[e] = 0;
   __syncthreads();
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-  constexpr int kPerWave = kChunkTokens / 4;
+  constexpr int kPerWave = kChunkTokens / 8;
   const int64_t tw = static_cast<int64_t>(blockIdx.x) * kChunkTokens + wave * kPerWave;
   for (int i = 0; i < kPerWave; ++i) {
     const int64_t t = tw + i;
@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256) void route_topk_hist_f32_kernel(
     }
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += 256) hist[static_cast<int64_t>(blockIdx.x) * E + e] = s_hist[e];
+  for (int e = threadIdx.x; e < E; e += 512) hist[static_cast<int64_t>(blockIdx.x) * E + e] = s_hist[e];
 }
 
 // Inclusive scan of s[0..n) in place (n <= 1024, blockDim.x == 1024).
@@ -114,9 +114,16 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restr
   if (active) {
     c0 = nchunks * p / P;
     c1 = nchunks * (p + 1) / P;
-    // (batches of eight independent loads)
+    // (batches of 32, then 8, independent loads)
     int32_t sum = 0;
     int64_t c = c0;
+    for (; c + 32 <= c1; c += 32) {
+      int32_t v[32];
+#pragma unroll
+      for (int u = 0; u < 32; ++u) v[u] = hist[(c + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < 32; ++u) sum += v[u];
+    }
     for (; c + 8 <= c1; c += 8) {
       int32_t v[8];
 #pragma unroll
@@ -211,17 +218,17 @@ hipError_t launch_route(const Layer& L, const void* logits, int64_t T, char* ws,
   if (L.act_bf16) {
     const uint16_t* lg = static_cast<const uint16_t*>(logits);
     if (E <= 64)
-      route_topk_hist_bf16_kernel<1><<<nc, 256, 0, s>>>(lg, T, E, k, topk_id, topk_w, hist);
+      route_topk_hist_bf16_kernel<1><<<nc, 512, 0, s>>>(lg, T, E, k, topk_id, topk_w, hist);
     else if (E <= 128)
-      route_topk_hist_bf16_kernel<2><<<nc, 256, 0, s>>>(lg, T, E, k, topk_id, topk_w, hist);
+      route_topk_hist_bf16_kernel<2><<<nc, 512, 0, s>>>(lg, T, E, k, topk_id, topk_w, hist);
     else if (E <= 256)
-      route_topk_hist_bf16_kernel<4><<<nc, 256, 0, s>>>(lg, T, E, k, topk_id, topk_w, hist);
+      route_topk_hist_bf16_kernel<4><<<nc, 512, 0, s>>>(lg, T, E, k, topk_id, topk_w, hist);
     else if (E <= 512)
-      route_topk_hist_bf16_kernel<8><<<nc, 256, 0, s>>>(lg, T, E, k, topk_id, topk_w, hist);
+      route_topk_hist_bf16_kernel<8><<<nc, 512, 0, s>>>(lg, T, E, k, topk_id, topk_w, hist);
     else
-      route_topk_hist_bf16_kernel<16><<<nc, 256, 0, s>>>(lg, T, E, k, topk_id, topk_w, hist);
+      route_topk_hist_bf16_kernel<16><<<nc, 512, 0, s>>>(lg, T, E, k, topk_id, topk_w, hist);
   } else {
-    route_topk_hist_f32_kernel<<<nc, 256, 0, s>>>(static_cast<const float*>(logits), T, E, k, topk_id,
+    route_topk_hist_f32_kernel<<<nc, 512, 0, s>>>(static_cast<const float*>(logits), T, E, k, topk_id,
                                                    topk_w, hist);
   }
   stage_done(L, 1, "route_topk_hist");
