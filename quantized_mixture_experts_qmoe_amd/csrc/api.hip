@@ -44,8 +44,15 @@ GemvShape gemv_shape(int64_t K, int min_rows_block) {
   return s;
 }
 
-bool use_decode_path(const Layer& L, bool force_prefill, int64_t T) {
-  return !force_prefill && T >= 1 && T <= 4;
+// Small batches above the fused kernel's four tokens run it once per group of
+// up to four tokens: each launch streams only its group's experts, which up to
+// this many tokens beats the grouped GEMMs (whose 256-row tiles pay their
+// per-stage latency for a handful of rows).
+constexpr int64_t kGroupedDecodeMaxTokens = 24;
+
+bool use_decode_path(const Layer& L, bool force_prefill, bool grouped_ok, int64_t T) {
+  if (force_prefill || T < 1) return false;
+  return T <= kDecodeMaxTokens || (grouped_ok && T <= kGroupedDecodeMaxTokens);
 }
 
 static Workspace layout(const Layer& L, int64_t T, bool decode) {
@@ -114,7 +121,7 @@ class DeviceGuard {
 };
 
 size_t required_bytes(const qmoe_handle* h, int64_t T) {
-  if (use_decode_path(h->L, h->force_prefill, T)) {
+  if (use_decode_path(h->L, h->force_prefill, h->fused_ok && !h->split_decode, T)) {
     const size_t d = layout(h->L, T, true).total;
     const size_t p = layout(h->L, T, false).total;   // qmoe_route needs the routing layout
     return d > p ? d : p;
@@ -232,7 +239,8 @@ qmoe_status qmoe_workspace_size(const qmoe_handle* h, int64_t T, size_t* bytes) 
 
 qmoe_status qmoe_workspace_routing(const qmoe_handle* h, int64_t T, size_t* id_off, size_t* w_off) {
   if (!h || !id_off || !w_off || T < 0 || T > h->L.max_tokens) return QMOE_ERR_INVALID_ARG;
-  const Workspace W = layout(h->L, T, use_decode_path(h->L, h->force_prefill, T));
+  const Workspace W =
+      layout(h->L, T, use_decode_path(h->L, h->force_prefill, h->fused_ok && !h->split_decode, T));
   *id_off = W.topk_id;
   *w_off = W.topk_w;
   return QMOE_OK;
@@ -251,21 +259,33 @@ qmoe_status qmoe_forward(qmoe_handle* h, const void* x, const void* logits, void
   char* base = static_cast<char*>(ws);
   hipError_t err;
   stage_done(h->L, 0, "start");
-  if (use_decode_path(h->L, h->force_prefill, T)) {
+  const bool fused = h->fused_ok && !h->split_decode;
+  if (use_decode_path(h->L, h->force_prefill, fused, T)) {
     const Workspace W = layout(h->L, T, true);
-    if (h->fused_ok && !h->split_decode) {
-      // epochs 1, 2, ...; when the counter wraps the exchange buffer is
-      // zeroed again first, so no entry can carry a reused epoch. A call
-      // that did not launch does not use up its epoch.
-      uint32_t epoch = h->calls + 1u;
+    if (fused) {
+      // one launch per group of up to four tokens (bf16 rows), each with its
+      // own epoch: 1, 2, ...; when the counter wraps the exchange buffer is
+      // zeroed again first, so no entry can carry a reused epoch. A launch
+      // that did not happen does not use up its epoch.
       err = hipSuccess;
-      if (epoch == 0u) {
-        epoch = 1u;
-        err = clear_exchange(h->L, h->xbuf, s);
+      const int64_t H = h->L.H, E = h->L.E, k = h->L.k;
+      for (int64_t t0 = 0; t0 < T && err == hipSuccess; t0 += kDecodeMaxTokens) {
+        const int64_t tg = T - t0 < kDecodeMaxTokens ? T - t0 : kDecodeMaxTokens;
+        uint32_t epoch = h->calls + 1u;
+        if (epoch == 0u) {
+          epoch = 1u;
+          err = clear_exchange(h->L, h->xbuf, s);
+          if (err != hipSuccess) break;
+        }
+        Workspace Wg = W;   // this group's routing slots
+        Wg.topk_id += static_cast<size_t>(t0 * k * 4);
+        Wg.topk_w += static_cast<size_t>(t0 * k * 4);
+        err = launch_decode_fused(h->L, static_cast<const uint16_t*>(x) + t0 * H,
+                                  static_cast<const uint16_t*>(logits) + t0 * E,
+                                  static_cast<uint16_t*>(out) + t0 * H, tg, base, Wg, h->xbuf, epoch,
+                                  h->fused_grid, s);
+        if (err == hipSuccess) h->calls = epoch;
       }
-      if (err == hipSuccess)
-        err = launch_decode_fused(h->L, x, logits, out, T, base, W, h->xbuf, epoch, h->fused_grid, s);
-      if (err == hipSuccess) h->calls = epoch;
     } else {
       err = launch_decode(h->L, x, logits, out, T, base, W, s);
     }

@@ -267,11 +267,18 @@ def check_prefill(wl, layer, rows=None):
     return out
 
 
+def prefill_layer(wl, max_tokens):
+    """A layer whose calls all take the grouped-GEMM path (small batches of a
+    bf16 layer would otherwise run the fused decode per group of four)."""
+    with _env(QMOE_FORCE_PATH="prefill"):
+        return layer_for(wl, max_tokens)
+
+
 @pytest.mark.parametrize("name,T", [("tiny", 5), ("decode", 5), ("decode", 150),
                                     ("int3", 67), ("stack", 129)])
 def test_prefill_parity_full(name, T):
     wl = qi.make_workload(name, T=T)
-    check_prefill(wl, layer_for(wl, max(T, 8)))
+    check_prefill(wl, prefill_layer(wl, max(T, 8)))
 
 
 @pytest.mark.parametrize("name,T,n", [("prefill", 8192, 48), ("int3", 2048, 48), ("stack", 4096, 32),
@@ -285,7 +292,7 @@ def test_prefill_parity_sampled(name, T, n):
 @pytest.mark.parametrize("bits,bs", FORMATS)
 def test_prefill_parity_formats(bits, bs):
     wl = qi.make_layer(small_spec(bits, bs), T=300, seed=11 + bits + bs, nseq=3)
-    check_prefill(wl, layer_for(wl, 300))
+    check_prefill(wl, prefill_layer(wl, 300))
 
 
 @pytest.mark.parametrize("name,T", [("tiny", 37), ("tiny", 5), ("decode", 40), ("int3", 24)])
@@ -295,7 +302,7 @@ def test_prefill_matches_bf16_datapath_emulation(name, T):
     bf16. The oracle's emulation of those rounding points must agree to within
     fp32 summation noise (rare one-ulp flips of a bf16 h value)."""
     wl = qi.make_workload(name, T=T)
-    out, _ = run(layer_for(wl, max(T, 8)), wl.tokens.x, wl.tokens.logits)
+    out, _ = run(prefill_layer(wl, max(T, 8)), wl.tokens.x, wl.tokens.logits)
     xb = wl.tokens.x.to(torch.bfloat16).to(wl.tokens.x.dtype)
     emu = oracle.forward(oracle.Layer.from_spec(wl.spec), xb, wl.tokens.logits, wl.weights,
                          emulate=oracle.EMU_W_BF16 | oracle.EMU_H_BF16)
@@ -308,6 +315,27 @@ def test_prefill_matches_bf16_datapath_emulation(name, T):
 def test_prefill_fp32_activations():
     wl = qi.make_layer(small_spec(4, 32, act="f32", hidden=192, inter=96), T=45, seed=5)
     check_prefill(wl, layer_for(wl, 64))
+
+
+@pytest.mark.parametrize("name,T", [("decode", 5), ("decode", 8), ("decode", 13), ("int3", 24),
+                                    ("stack", 7)])
+def test_grouped_decode_parity(name, T):
+    """Batches of 5..24 tokens of a bf16 layer run the fused decode once per
+    group of up to four tokens: the routing of every token (read back from
+    the workspace) is bit-exact and every output row matches the oracle."""
+    wl = qi.make_workload(name, T=T)
+    check_decode(wl, layer_for(wl, 32))
+
+
+def test_grouped_decode_matches_prefill():
+    """The grouped decode and the grouped GEMMs compute the same 11-token
+    layer (fp32 h against bf16 h): both meet the tolerance and agree per
+    token to rel-L2 < 1e-2."""
+    wl = qi.make_workload("decode", T=11)
+    a = check_decode(wl, layer_for(wl, 16))
+    b = check_prefill(wl, prefill_layer(wl, 16))
+    d = (a.float() - b.float()).norm(dim=1) / a.float().norm(dim=1)
+    assert d.max().item() < 1e-2
 
 
 # ------------------------------------------------------------------ properties
@@ -329,21 +357,22 @@ def test_decode_and_prefill_agree():
 
 
 def test_packed_equals_per_sequence():
-    """Prefill rows are batch-invariant, so a sequence of >= 5 tokens run alone
-    reproduces its rows of the packed run bit for bit; shorter sequences take
-    the decode path and must agree within tolerance."""
+    """Prefill rows are batch-invariant: with every call on the grouped-GEMM
+    path, each sequence run alone reproduces its rows of the packed run bit
+    for bit. With the default dispatch, sequences of up to 24 tokens take the
+    fused decode (per group of four tokens) and must meet the tolerance."""
     wl = qi.make_workload("prefill", T=160)
-    layer = layer_for(wl, 160)
-    packed, _ = run(layer, wl.tokens.x, wl.tokens.logits)
+    lp = prefill_layer(wl, 160)
+    ld = layer_for(wl, 160)
+    packed, _ = run(lp, wl.tokens.x, wl.tokens.logits)
     s = 0
     for n in wl.tokens.seq_lens:
-        part, _ = run(layer, wl.tokens.x[s:s + n].contiguous(), wl.tokens.logits[s:s + n].contiguous())
-        if n >= 5:
-            assert torch.equal(part, packed[s:s + n]), (s, n)
-        else:
-            sub = qi.Workload("seq", wl.spec, qi.Tokens(wl.tokens.x[s:s + n], wl.tokens.logits[s:s + n]),
-                              wl.weights)
-            assert compare(part, oracle_acc(sub)).ok
+        xs, ls = wl.tokens.x[s:s + n].contiguous(), wl.tokens.logits[s:s + n].contiguous()
+        part, _ = run(lp, xs, ls)
+        assert torch.equal(part, packed[s:s + n]), (s, n)
+        dpart, _ = run(ld, xs, ls)
+        sub = qi.Workload("seq", wl.spec, qi.Tokens(xs, ls), wl.weights)
+        assert compare(dpart, oracle_acc(sub)).ok, (s, n)
         s += n
 
 
