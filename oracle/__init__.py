@@ -43,7 +43,7 @@ class _Layer(ctypes.Structure):
                 ("num_experts", ctypes.c_int64), ("top_k", ctypes.c_int32),
                 ("bits", ctypes.c_int32), ("block_size", ctypes.c_int32),
                 ("zero_point", ctypes.c_int32), ("emulate", ctypes.c_int32),
-                ("pad", ctypes.c_int32)]
+                ("normalize", ctypes.c_int32)]
 
 
 _lib = None
@@ -57,7 +57,7 @@ def lib():
         P = ctypes.c_void_p
         i64, i32 = ctypes.c_int64, ctypes.c_int32
         L.oracle_dequant.argtypes = [P, P, i64, i64, i32, i32, i32, P]
-        L.oracle_route.argtypes = [P, i64, i64, i32, P, P]
+        L.oracle_route.argtypes = [P, i64, i64, i32, i32, P, P]
         L.oracle_permute.argtypes = [P, i64, i64, P, P, P, P]
         L.oracle_forward.argtypes = [ctypes.POINTER(_Layer), P, P, P, P, P, P, i64, P, i32]
         L.oracle_round_output.argtypes = [P, i64, P, P]
@@ -119,13 +119,15 @@ def dequant(codes: np.ndarray, scales: np.ndarray, bits: int, block_size: int,
     return out
 
 
-def route(logits, k: int) -> Tuple[np.ndarray, np.ndarray]:
-    """Top-k ids (int32 [T, k]) and softmax weights over the selected (float64 [T, k])."""
+def route(logits, k: int, normalize: bool = True) -> Tuple[np.ndarray, np.ndarray]:
+    """Top-k ids (int32 [T, k]) and routing weights (float64 [T, k]): the
+    softmax over the selected logits, or with normalize=False each selected
+    expert's softmax probability over all E logits."""
     l64 = as_f64(logits)
     T, E = l64.shape
     ids = np.empty((T, k), dtype=np.int32)
     w = np.empty((T, k), dtype=np.float64)
-    _check(lib().oracle_route(_p(l64), T, E, k, _p(ids), _p(w)), "route")
+    _check(lib().oracle_route(_p(l64), T, E, k, int(bool(normalize)), _p(ids), _p(w)), "route")
     return ids, w
 
 
@@ -151,11 +153,12 @@ class Layer:
     bits: int
     block_size: int
     zero_point: int
+    normalize: bool = True   # routing weights over the selected k (else over all experts)
 
     @classmethod
-    def from_spec(cls, spec) -> "Layer":
+    def from_spec(cls, spec, normalize: bool = True) -> "Layer":
         return cls(spec.hidden, spec.inter, spec.num_experts, spec.top_k, spec.bits,
-                   spec.block_size, spec.zero_point)
+                   spec.block_size, spec.zero_point, normalize)
 
 
 def forward(layer: Layer, x, logits, weights, *, nthreads: Optional[int] = None,
@@ -173,7 +176,8 @@ def forward(layer: Layer, x, logits, weights, *, nthreads: Optional[int] = None,
     assert c1.shape == (E, 2 * I, H * layer.bits // 8) and s1.shape == (E, 2 * I, H // layer.block_size)
     assert c2.shape == (E, H, I * layer.bits // 8) and s2.shape == (E, H, I // layer.block_size)
     out = np.empty((T, H), dtype=np.float64)
-    L = _Layer(H, I, E, layer.top_k, layer.bits, layer.block_size, layer.zero_point, emulate, 0)
+    L = _Layer(H, I, E, layer.top_k, layer.bits, layer.block_size, layer.zero_point, emulate,
+               int(bool(layer.normalize)))
     if nthreads is None:
         nthreads = default_threads()
     _check(lib().oracle_forward(ctypes.byref(L), _p(x64), _p(l64), _p(c1), _p(s1), _p(c2), _p(s2),

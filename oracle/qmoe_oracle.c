@@ -29,7 +29,10 @@
  * Readings taken where the pages leave a step open:
  *  - top-k on raw logits, ties to the lower expert index, slots ordered by
  *    descending logit then ascending index;
- *  - softmax over the k selected logits (normalized routing weights);
+ *  - routing weights: with normalized routing, the softmax over the k
+ *    selected logits; without it, each selected expert's softmax probability
+ *    over all num_experts logits (the selection is the same top-k either
+ *    way, since the softmax is monotonic);
  *  - fc1 rows [0, I) are the gate, rows [I, 2I) the up projection, and
  *    h = silu(gate) * up with silu(g) = g / (1 + exp(-g)) and no clamp;
  *  - W[n][k] = (q[n][k] - zp) * s[n][k / block]; INT4 two codes per byte low
@@ -124,8 +127,9 @@ int oracle_dequant(const uint8_t *codes, const uint16_t *scales, int64_t N, int6
     return ORACLE_OK;
 }
 
-/* Top-k selection and softmax over the selected logits, per token. */
-int oracle_route(const double *logits, int64_t T, int64_t E, int k,
+/* Top-k selection and the routing weights, per token: the softmax over the
+ * selected logits (normalize != 0) or over all E logits (normalize == 0). */
+int oracle_route(const double *logits, int64_t T, int64_t E, int k, int normalize,
                  int32_t *topk_id, double *topk_w)
 {
     if (!logits || !topk_id || !topk_w || T < 0 || E < 1 || k < 1 || k > E) return ORACLE_BAD_ARG;
@@ -146,7 +150,10 @@ int oracle_route(const double *logits, int64_t T, int64_t E, int k,
         }
         double lmax = l[topk_id[t * k]];
         double denom = 0.0;
-        for (int j = 0; j < k; ++j) denom += exp(l[topk_id[t * k + j]] - lmax);
+        if (normalize)
+            for (int j = 0; j < k; ++j) denom += exp(l[topk_id[t * k + j]] - lmax);
+        else
+            for (int64_t e = 0; e < E; ++e) denom += exp(l[e] - lmax);
         for (int j = 0; j < k; ++j) topk_w[t * k + j] = exp(l[topk_id[t * k + j]] - lmax) / denom;
     }
     free(taken);
@@ -195,7 +202,7 @@ typedef struct {
     int64_t hidden, inter, num_experts;
     int32_t top_k, bits, block_size, zero_point;
     int32_t emulate;     /* EMU_* bitmask, 0 for the plain definition */
-    int32_t pad;
+    int32_t normalize;   /* routing weights: 1 over the selected k, 0 over all experts */
 } oracle_layer;
 
 typedef struct {
@@ -244,7 +251,7 @@ static void *run_tokens(void *arg)
     }
     for (int64_t t = jb->t0; t < jb->t1; ++t) {
         const double *xt = jb->x + t * H;
-        int st = oracle_route(jb->logits + t * E, 1, E, k, ids, w);
+        int st = oracle_route(jb->logits + t * E, 1, E, k, jb->L->normalize, ids, w);
         if (st != ORACLE_OK) { jb->status = st; break; }
         for (int64_t m = 0; m < H; ++m) acc[m] = 0.0;
         for (int j = 0; j < k; ++j) {

@@ -188,6 +188,49 @@ def test_softmax_selected_closed_form():
     np.testing.assert_allclose(w[0], [0.5, 1 / 3, 1 / 6], rtol=1e-15)
 
 
+def test_unnormalized_weights_are_full_softmax_at_selected():
+    """Without normalization a selected expert's weight is its probability
+    under the softmax over all experts (torch, fp64); the selection is the
+    same top-k as with normalization, and k = E gives identical weights."""
+    rng = np.random.default_rng(13)
+    logits = rng.standard_normal((200, 32)) * 3
+    ids0, w0 = oracle.route(logits, 6, normalize=False)
+    ids1, w1 = oracle.route(logits, 6)
+    assert np.array_equal(ids0, ids1)
+    ref = torch.softmax(torch.from_numpy(logits), dim=1).numpy()
+    np.testing.assert_allclose(w0, np.take_along_axis(ref, ids0.astype(np.int64), axis=1),
+                               rtol=1e-14, atol=0)
+    # the ratios between slots do not depend on the denominator
+    np.testing.assert_allclose(w0 / w0[:, :1], w1 / w1[:, :1], rtol=1e-14)
+    assert np.all(w0.sum(axis=1) < 1.0)
+    idsf, wf0 = oracle.route(logits, 32, normalize=False)
+    _, wf1 = oracle.route(logits, 32)
+    np.testing.assert_allclose(wf0, wf1, rtol=1e-14)
+
+
+def test_unnormalized_closed_form():
+    logits = np.array([[0.0, np.log(3.0), np.log(0.5), np.log(2.0)]])
+    ids, w = oracle.route(logits, 2, normalize=False)
+    assert ids.tolist() == [[1, 3]]
+    np.testing.assert_allclose(w[0], [3 / 6.5, 2 / 6.5], rtol=1e-15)
+
+
+def test_unnormalized_forward_scales_each_token():
+    """The layer output without normalization is, per token, the normalized
+    output times (sum over the selected of exp) / (sum over all of exp)."""
+    wl = qi.make_workload("tiny")
+    L1 = oracle.Layer.from_spec(wl.spec)
+    L0 = oracle.Layer.from_spec(wl.spec, normalize=False)
+    a1 = oracle.forward(L1, wl.tokens.x, wl.tokens.logits, wl.weights)
+    a0 = oracle.forward(L0, wl.tokens.x, wl.tokens.logits, wl.weights)
+    l = wl.tokens.logits.to(torch.float64).numpy()
+    ids, _ = oracle.route(l, wl.spec.top_k)
+    e = np.exp(l - l.max(axis=1, keepdims=True))
+    frac = np.take_along_axis(e, ids.astype(np.int64), axis=1).sum(axis=1) / e.sum(axis=1)
+    np.testing.assert_allclose(a0, a1 * frac[:, None], rtol=1e-12, atol=1e-300)
+    assert np.all(frac < 1.0)
+
+
 # ---------------------------------------------------------------- permutation
 
 @pytest.mark.parametrize("T,E,k,skew", [(0, 8, 2, False), (1, 128, 8, False), (4, 4, 2, False),
