@@ -75,7 +75,9 @@ typedef struct qmoe_config {
     int32_t block_size;         /* 32, 64 or 128 */
     int32_t zero_point;         /* 0 <= zp < 2^bits, or -1 for 2^(bits-1) */
     int32_t act_dtype;          /* qmoe_dtype */
-    int32_t normalize_routing;  /* must be 1: softmax over the selected k */
+    int32_t normalize_routing;  /* 1: routing weights are the softmax over the k selected
+                                   logits; 0: each selected expert's softmax probability
+                                   over all num_experts logits (same top-k either way) */
     int32_t reserved;           /* must be 0 */
     int64_t max_tokens;         /* largest T accepted by qmoe_forward (>= 0) */
 } qmoe_config;

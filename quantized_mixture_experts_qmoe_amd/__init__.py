@@ -106,6 +106,7 @@ class LayerConfig:
     zero_point: int = -1
     act_dtype: torch.dtype = torch.bfloat16
     max_tokens: int = 8192
+    normalize_routing: bool = True   # False: weights over all experts, not renormalized over the k
 
 
 class QMoELayer:
@@ -131,8 +132,8 @@ class QMoELayer:
         self.device = fc1_codes.device
         self._keep = (fc1_codes, fc1_scales, fc2_codes, fc2_scales)
         c = Config(ctypes.sizeof(Config), cfg.top_k, cfg.hidden, cfg.inter, cfg.num_experts,
-                   cfg.bits, cfg.block_size, cfg.zero_point, _ACT[cfg.act_dtype], 1, 0,
-                   cfg.max_tokens)
+                   cfg.bits, cfg.block_size, cfg.zero_point, _ACT[cfg.act_dtype],
+                   1 if cfg.normalize_routing else 0, 0, cfg.max_tokens)
         w = Weights(fc1_codes.data_ptr(), fc1_scales.data_ptr(), fc2_codes.data_ptr(),
                     fc2_scales.data_ptr())
         h = ctypes.c_void_p()

@@ -81,7 +81,7 @@ __device__ __forceinline__ void token_slots(const RoutingLds& R, int T, int k, i
 // grid = (ceil(I / rows_block), T * k), block = 256 (4 waves)
 template <int BITS, int UPL, bool BF16>
 __global__ __launch_bounds__(256) void decode_fc1_kernel(
-    const void* __restrict__ xv, const void* __restrict__ logitsv, int T, int E, int k,
+    const void* __restrict__ xv, const void* __restrict__ logitsv, int T, int E, int k, bool normalize,
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales, int H, int I, int bs,
     int zp, int64_t row_bytes, int64_t nblk, int lpr, int rows_block,
     int32_t* __restrict__ ws_ids, float* __restrict__ ws_w, float* __restrict__ h32,
@@ -91,10 +91,10 @@ __global__ __launch_bounds__(256) void decode_fc1_kernel(
   if (wave < T) {
     if constexpr (BF16)
       topk_softmax_wave(static_cast<const uint16_t*>(logitsv) + static_cast<int64_t>(wave) * E, E, k,
-                        lane, R.ids + wave * k, R.w + wave * k);
+                        normalize, lane, R.ids + wave * k, R.w + wave * k);
     else
       topk_softmax_wave(static_cast<const float*>(logitsv) + static_cast<int64_t>(wave) * E, E, k,
-                        lane, R.ids + wave * k, R.w + wave * k);
+                        normalize, lane, R.ids + wave * k, R.w + wave * k);
   }
   __syncthreads();
   const int nroutes = T * k;
@@ -346,11 +346,11 @@ hipError_t launch_decode_t(const Layer& L, const void* x, const void* logits, vo
   dim3 g1((I + s1.rows_block - 1) / s1.rows_block, Ti * k);
   if (L.act_bf16)
     decode_fc1_kernel<BITS, UPL, true><<<g1, 256, 0, s>>>(
-        x, logits, Ti, E, k, L.fc1_codes, L.fc1_scales, H, I, L.bs, L.zp, L.fc1_row_bytes,
+        x, logits, Ti, E, k, L.normalize, L.fc1_codes, L.fc1_scales, H, I, L.bs, L.zp, L.fc1_row_bytes,
         L.fc1_nblk, s1.lpr, s1.rows_block, ids, w, h32, counters, W.n_counters);
   else
     decode_fc1_kernel<BITS, UPL, false><<<g1, 256, 0, s>>>(
-        x, logits, Ti, E, k, L.fc1_codes, L.fc1_scales, H, I, L.bs, L.zp, L.fc1_row_bytes,
+        x, logits, Ti, E, k, L.normalize, L.fc1_codes, L.fc1_scales, H, I, L.bs, L.zp, L.fc1_row_bytes,
         L.fc1_nblk, s1.lpr, s1.rows_block, ids, w, h32, counters, W.n_counters);
   stage_done(L, 1, "decode_fc1_swiglu");
   return hipGetLastError();

@@ -6,7 +6,8 @@
 //   0. routing of the <= 4 tokens, recomputed by every workgroup: wave t
 //      takes token t's logits straight into registers as 32-bit keys
 //      (ordered bf16 logit, then the inverted expert index) and selects the
-//      k largest with DPP max reductions, then the softmax over the selected;
+//      k largest with DPP max reductions, then the routing weights (softmax
+//      over the selected, or without normalization over all experts);
 //      the distinct experts, in ascending expert order, come from an LDS
 //      bitmask;
 //   1. FC1 + SwiGLU: items of two gate rows and the two matching up rows of
@@ -157,6 +158,7 @@ struct FusedArgs {
   const uint8_t* c2;
   const uint16_t* s2;
   int T, E, k, H, I, bs, zp;
+  int normalize;     // routing weights over the selected k (1) or over all experts (0)
   int64_t rb1, rb2, nb1, nb2;
   int32_t* ws_ids;
   float* ws_w;
@@ -225,7 +227,12 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
       for (int c = 0; c < kKeySlots; ++c) keys[c] = (keys[c] == b) ? 0u : keys[c];
     }
     const float ex = (lane < k) ? expf(key_logit(mine) - key_logit(first)) : 0.0f;
-    const float sum = wave_sum(ex);
+    float all = 0.0f;   // sum over all experts (weights without normalization)
+    if (!a.normalize)
+#pragma unroll
+      for (int c = 0; c < kKeySlots; ++c)
+        if (lane + kWave * c < E) all += expf(bf16_to_f32(lg[c]) - key_logit(first));
+    const float sum = wave_sum(a.normalize ? ex : all);
     if (lane < k) {
       const int e = key_to_expert(mine);
       S.ids[wave * k + lane] = e;
@@ -700,6 +707,7 @@ hipError_t launch_decode_fused(const Layer& L, const void* x, const void* logits
   fa.I = static_cast<int>(L.I);
   fa.bs = L.bs;
   fa.zp = L.zp;
+  fa.normalize = L.normalize ? 1 : 0;
   fa.rb1 = L.fc1_row_bytes;
   fa.rb2 = L.fc2_row_bytes;
   fa.nb1 = L.fc1_nblk;

@@ -291,12 +291,14 @@ __device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
   return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
 }
 
-// One wavefront selects the top-k experts of one token and computes the
-// softmax over the k selected logits. Slot j holds the j-th largest logit
-// (ties to the lower expert index). Lanes j < k write ids[j] and w[j].
+// One wavefront selects the top-k experts of one token and computes their
+// routing weights: the softmax over the k selected logits (normalize), or each
+// selected expert's softmax probability over all E logits. Slot j holds the
+// j-th largest logit (ties to the lower expert index). Lanes j < k write
+// ids[j] and w[j].
 template <typename ACT>
-__device__ __forceinline__ void topk_softmax_wave_r(const ACT* logits, int E, int k, int lane,
-                                                    int& id, float& wt) {
+__device__ __forceinline__ void topk_softmax_wave_r(const ACT* logits, int E, int k, bool normalize,
+                                                    int lane, int& id, float& wt) {
   uint64_t keys[kMaxExperts / kWave];
 #pragma unroll
   for (int i = 0; i < kMaxExperts / kWave; ++i) {
@@ -325,16 +327,19 @@ __device__ __forceinline__ void topk_softmax_wave_r(const ACT* logits, int E, in
       if (lane == (e & (kWave - 1)) && i == (e / kWave)) keys[i] = 0ull;
   }
   const float ex = (lane < k) ? expf(my_v - v0) : 0.0f;
-  const float sum = wave_sum(ex);
+  float all = 0.0f;   // sum over all experts (weights without normalization)
+  if (!normalize)
+    for (int e = lane; e < E; e += kWave) all += expf(act_to_f32(logits[e]) - v0);
+  const float sum = wave_sum(normalize ? ex : all);
   id = my_id;
   wt = ex / sum;
 }
 template <typename ACT>
-__device__ __forceinline__ void topk_softmax_wave(const ACT* logits, int E, int k, int lane,
-                                                  int32_t* ids, float* w) {
+__device__ __forceinline__ void topk_softmax_wave(const ACT* logits, int E, int k, bool normalize,
+                                                  int lane, int32_t* ids, float* w) {
   int id;
   float wt;
-  topk_softmax_wave_r(logits, E, k, lane, id, wt);
+  topk_softmax_wave_r(logits, E, k, normalize, lane, id, wt);
   if (lane < k) {
     ids[lane] = id;
     w[lane] = wt;
@@ -346,7 +351,7 @@ __device__ __forceinline__ void topk_softmax_wave(const ACT* logits, int E, int 
 // slot j's expert and weight.
 template <int SLOTS>
 __device__ __forceinline__ void topk_softmax_bf16_wave(const uint16_t (&lg)[SLOTS], int E, int k,
-                                                       int lane, int& id, float& wt) {
+                                                       bool normalize, int lane, int& id, float& wt) {
   uint32_t keys[SLOTS];
 #pragma unroll
   for (int c = 0; c < SLOTS; ++c) {
@@ -365,7 +370,12 @@ __device__ __forceinline__ void topk_softmax_bf16_wave(const uint16_t (&lg)[SLOT
     for (int c = 0; c < SLOTS; ++c) keys[c] = (keys[c] == b) ? 0u : keys[c];
   }
   const float ex = (lane < k) ? expf(key_logit(mine) - key_logit(first)) : 0.0f;
-  const float sum = wave_sum(ex);
+  float all = 0.0f;   // sum over all experts (weights without normalization)
+  if (!normalize)
+#pragma unroll
+    for (int c = 0; c < SLOTS; ++c)
+      if (lane + kWave * c < E) all += expf(bf16_to_f32(lg[c]) - key_logit(first));
+  const float sum = wave_sum(normalize ? ex : all);
   id = key_to_expert(mine);
   wt = ex / sum;
 }

@@ -15,6 +15,7 @@ struct Layer {
   int64_t H, I, E;
   int k, bits, bs, zp;
   bool act_bf16;
+  bool normalize;   // routing weights: softmax over the selected k (else over all experts)
   int64_t max_tokens;
   const uint8_t* fc1_codes;
   const uint16_t* fc1_scales;

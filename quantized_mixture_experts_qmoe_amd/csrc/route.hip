@@ -20,8 +20,8 @@ namespace qmoe {
 // hist[c][e] = number of the chunk's routes sent to e.
 template <int SLOTS>
 __global__ __launch_bounds__(512) void route_topk_hist_bf16_kernel(
-    const uint16_t* __restrict__ logits, int64_t T, int E, int k, int32_t* __restrict__ topk_id,
-    float* __restrict__ topk_w, int32_t* __restrict__ hist) {
+    const uint16_t* __restrict__ logits, int64_t T, int E, int k, bool normalize,
+    int32_t* __restrict__ topk_id, float* __restrict__ topk_w, int32_t* __restrict__ hist) {
   __shared__ int32_t s_hist[kMaxExperts];
   for (int e = threadIdx.x; e < E; e += 512) s_hist[e] = 0;
   __syncthreads();
@@ -44,7 +44,7 @@ __global__ __launch_bounds__(512) void route_topk_hist_bf16_kernel(
     load(t + 1, nxt);
     int id;
     float wt;
-    topk_softmax_bf16_wave<SLOTS>(cur, E, k, lane, id, wt);
+    topk_softmax_bf16_wave<SLOTS>(cur, E, k, normalize, lane, id, wt);
     if (lane < k) {
       topk_id[t * k + lane] = id;
       topk_w[t * k + lane] = wt;
@@ -59,8 +59,8 @@ __global__ __launch_bounds__(512) void route_topk_hist_bf16_kernel(
 
 // The same for fp32 logits (64-bit keys: fp32 value, then the inverted index).
 __global__ __launch_bounds__(512) void route_topk_hist_f32_kernel(
-    const float* __restrict__ logits, int64_t T, int E, int k, int32_t* __restrict__ topk_id,
-    float* __restrict__ topk_w, int32_t* __restrict__ hist) {
+    const float* __restrict__ logits, int64_t T, int E, int k, bool normalize,
+    int32_t* __restrict__ topk_id, float* __restrict__ topk_w, int32_t* __restrict__ hist) {
   __shared__ int32_t s_hist[kMaxExperts];
   for (int e = threadIdx.x; e < E; e += 512) s_hist[e] = 0;
   __syncthreads();
@@ -72,7 +72,7 @@ __global__ __launch_bounds__(512) void route_topk_hist_f32_kernel(
     if (t >= T) break;
     int id;
     float wt;
-    topk_softmax_wave_r(logits + t * E, E, k, lane, id, wt);
+    topk_softmax_wave_r(logits + t * E, E, k, normalize, lane, id, wt);
     if (lane < k) {
       topk_id[t * k + lane] = id;
       topk_w[t * k + lane] = wt;
@@ -218,18 +218,18 @@ hipError_t launch_route(const Layer& L, const void* logits, int64_t T, char* ws,
   if (L.act_bf16) {
     const uint16_t* lg = static_cast<const uint16_t*>(logits);
     if (E <= 64)
-      route_topk_hist_bf16_kernel<1><<<nc, 512, 0, s>>>(lg, T, E, k, topk_id, topk_w, hist);
+      route_topk_hist_bf16_kernel<1><<<nc, 512, 0, s>>>(lg, T, E, k, L.normalize, topk_id, topk_w, hist);
     else if (E <= 128)
-      route_topk_hist_bf16_kernel<2><<<nc, 512, 0, s>>>(lg, T, E, k, topk_id, topk_w, hist);
+      route_topk_hist_bf16_kernel<2><<<nc, 512, 0, s>>>(lg, T, E, k, L.normalize, topk_id, topk_w, hist);
     else if (E <= 256)
-      route_topk_hist_bf16_kernel<4><<<nc, 512, 0, s>>>(lg, T, E, k, topk_id, topk_w, hist);
+      route_topk_hist_bf16_kernel<4><<<nc, 512, 0, s>>>(lg, T, E, k, L.normalize, topk_id, topk_w, hist);
     else if (E <= 512)
-      route_topk_hist_bf16_kernel<8><<<nc, 512, 0, s>>>(lg, T, E, k, topk_id, topk_w, hist);
+      route_topk_hist_bf16_kernel<8><<<nc, 512, 0, s>>>(lg, T, E, k, L.normalize, topk_id, topk_w, hist);
     else
-      route_topk_hist_bf16_kernel<16><<<nc, 512, 0, s>>>(lg, T, E, k, topk_id, topk_w, hist);
+      route_topk_hist_bf16_kernel<16><<<nc, 512, 0, s>>>(lg, T, E, k, L.normalize, topk_id, topk_w, hist);
   } else {
-    route_topk_hist_f32_kernel<<<nc, 512, 0, s>>>(static_cast<const float*>(logits), T, E, k, topk_id,
-                                                   topk_w, hist);
+    route_topk_hist_f32_kernel<<<nc, 512, 0, s>>>(static_cast<const float*>(logits), T, E, k,
+                                                   L.normalize, topk_id, topk_w, hist);
   }
   stage_done(L, 1, "route_topk_hist");
   route_scan_kernel<<<1, 1024, 0, s>>>(hist, W.nchunks, E, kTileM,

@@ -70,7 +70,7 @@ def _create(c, w=None):
     ({"block_size": 96}, 1), ({"hidden": 2048 + 32, "block_size": 64}, 1),
     ({"inter": 784}, 1), ({"zero_point": 16}, 1), ({"zero_point": -2}, 1),
     ({"act_dtype": 7}, 1), ({"reserved": 1}, 1), ({"max_tokens": -1}, 1),
-    ({"normalize_routing": 2}, 1), ({"normalize_routing": 0}, 2),
+    ({"normalize_routing": 2}, 1), ({"normalize_routing": -1}, 1),
     ({"num_experts": 2048, "top_k": 8}, 2), ({"top_k": 64}, 2), ({"hidden": 16384}, 2),
 ])
 def test_create_rejects_invalid_configs(kw, status):

@@ -338,6 +338,36 @@ def test_grouped_decode_matches_prefill():
     assert d.max().item() < 1e-2
 
 
+@pytest.mark.parametrize("name,T,force", [("decode", 4, None), ("decode", 8, None),
+                                          ("decode", 1, "decode_split"), ("tiny", 4, None),
+                                          ("prefill", 300, None), ("f32", 45, None),
+                                          ("stack", 129, "prefill")])
+def test_unnormalized_routing_parity(name, T, force):
+    """normalize_routing = 0 on every routing implementation (fused, grouped
+    and split decode, prefill routing; bf16 and fp32 logits): the same top-k
+    bit for bit, each weight the selected expert's softmax probability over
+    all experts (within 8 fp32 ulp: the denominator is a tree sum over all E
+    terms instead of k), and the layer output within the tolerance. "f32" is
+    the small fp32-activation layer of the fp32 prefill test."""
+    if name == "f32":
+        wl = qi.make_layer(small_spec(4, 32, act="f32", hidden=192, inter=96), T=T, seed=5)
+    else:
+        wl = qi.make_workload(name, T=T)
+    with _env(**({"QMOE_FORCE_PATH": force} if force else {})):
+        layer = layer_for(wl, max(T, 8), normalize=False)
+    out, ws = run(layer, wl.tokens.x, wl.tokens.logits)
+    ids, w = layer.routing_from_workspace(T, ws)
+    rid, rw = oracle.route(wl.tokens.logits, wl.spec.top_k, normalize=False)
+    assert np.array_equal(ids.cpu().numpy(), rid)
+    ulp = fp32_ulps(w.cpu().numpy(), rw.astype(np.float32)).max()
+    ref = oracle.forward(oracle.Layer.from_spec(wl.spec, normalize=False), wl.tokens.x,
+                         wl.tokens.logits, wl.weights)
+    rep = compare(out, ref)
+    say(f"unnormalized {name} T={T} path={force or 'default'}: weight ulp {ulp}, {rep}")
+    assert ulp <= 8
+    assert rep.ok, rep
+
+
 # ------------------------------------------------------------------ properties
 
 def test_decode_and_prefill_agree():
