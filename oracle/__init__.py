@@ -43,7 +43,8 @@ class _Layer(ctypes.Structure):
                 ("num_experts", ctypes.c_int64), ("top_k", ctypes.c_int32),
                 ("bits", ctypes.c_int32), ("block_size", ctypes.c_int32),
                 ("zero_point", ctypes.c_int32), ("emulate", ctypes.c_int32),
-                ("normalize", ctypes.c_int32)]
+                ("normalize", ctypes.c_int32), ("fc1_interleaved", ctypes.c_int32),
+                ("pad", ctypes.c_int32)]
 
 
 _lib = None
@@ -154,11 +155,12 @@ class Layer:
     block_size: int
     zero_point: int
     normalize: bool = True   # routing weights over the selected k (else over all experts)
+    fc1_interleaved: bool = False   # FC1 rows 2n / 2n+1 = gate n / up n (else two blocks)
 
     @classmethod
-    def from_spec(cls, spec, normalize: bool = True) -> "Layer":
+    def from_spec(cls, spec, normalize: bool = True, fc1_interleaved: bool = False) -> "Layer":
         return cls(spec.hidden, spec.inter, spec.num_experts, spec.top_k, spec.bits,
-                   spec.block_size, spec.zero_point, normalize)
+                   spec.block_size, spec.zero_point, normalize, fc1_interleaved)
 
 
 def forward(layer: Layer, x, logits, weights, *, nthreads: Optional[int] = None,
@@ -177,7 +179,7 @@ def forward(layer: Layer, x, logits, weights, *, nthreads: Optional[int] = None,
     assert c2.shape == (E, H, I * layer.bits // 8) and s2.shape == (E, H, I // layer.block_size)
     out = np.empty((T, H), dtype=np.float64)
     L = _Layer(H, I, E, layer.top_k, layer.bits, layer.block_size, layer.zero_point, emulate,
-               int(bool(layer.normalize)))
+               int(bool(layer.normalize)), int(bool(layer.fc1_interleaved)), 0)
     if nthreads is None:
         nthreads = default_threads()
     _check(lib().oracle_forward(ctypes.byref(L), _p(x64), _p(l64), _p(c1), _p(s1), _p(c2), _p(s2),

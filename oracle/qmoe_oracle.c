@@ -35,6 +35,10 @@
  *    way, since the softmax is monotonic);
  *  - fc1 rows [0, I) are the gate, rows [I, 2I) the up projection, and
  *    h = silu(gate) * up with silu(g) = g / (1 + exp(-g)) and no clamp;
+ *    with interleaved FC1 rows (the exporter layout named in the review of
+ *    "[CUDA] Add INT4 and INT3 QMoE CPU/GPU offload support", producer/
+ *    consumer contract) row 2n is gate n and row 2n+1 is up n, and the scale
+ *    rows follow the same order;
  *  - W[n][k] = (q[n][k] - zp) * s[n][k / block]; INT4 two codes per byte low
  *    nibble first, INT2 four per byte low bits first, INT3 eight codes per
  *    three bytes with code i at bits [3i, 3i+3) of the little-endian 24-bit
@@ -203,6 +207,8 @@ typedef struct {
     int32_t top_k, bits, block_size, zero_point;
     int32_t emulate;     /* EMU_* bitmask, 0 for the plain definition */
     int32_t normalize;   /* routing weights: 1 over the selected k, 0 over all experts */
+    int32_t fc1_interleaved;  /* FC1 rows: 0 gate block then up block, 1 interleaved */
+    int32_t pad;
 } oracle_layer;
 
 typedef struct {
@@ -261,8 +267,10 @@ static void *run_tokens(void *arg)
             const uint8_t *c2 = jb->fc2_codes + e * H * rb2;
             const uint16_t *s2 = jb->fc2_scales + e * H * nb2;
             for (int64_t n = 0; n < I; ++n) {
-                double g = row_dot(c1 + n * rb1, s1 + n * nb1, xt, H, bits, bs, zp, emu_w);
-                double u = row_dot(c1 + (I + n) * rb1, s1 + (I + n) * nb1, xt, H, bits, bs, zp, emu_w);
+                const int64_t gr = jb->L->fc1_interleaved ? 2 * n : n;
+                const int64_t ur = jb->L->fc1_interleaved ? 2 * n + 1 : I + n;
+                double g = row_dot(c1 + gr * rb1, s1 + gr * nb1, xt, H, bits, bs, zp, emu_w);
+                double u = row_dot(c1 + ur * rb1, s1 + ur * nb1, xt, H, bits, bs, zp, emu_w);
                 if (emu_gu) { g = to_bf16(g); u = to_bf16(u); }
                 double hv = g / (1.0 + exp(-g)) * u;
                 h[n] = emu_h ? to_bf16(hv) : hv;

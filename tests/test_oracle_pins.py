@@ -231,6 +231,30 @@ def test_unnormalized_forward_scales_each_token():
     assert np.all(frac < 1.0)
 
 
+def test_interleaved_fc1_rows_equal_block_layout():
+    """FC1 stored interleaved (row 2n = gate n, row 2n+1 = up n, scale rows in
+    the same order) gives exactly the layer of the block layout (gate rows,
+    then up rows) holding the same rows."""
+    wl = qi.make_workload("tiny")
+    w = wl.weights
+    I = wl.spec.inter
+
+    def interleave(a):
+        out = np.empty_like(a)
+        out[:, 0::2], out[:, 1::2] = a[:, :I], a[:, I:]
+        return out
+
+    wi = qi.LayerWeights(interleave(w.fc1_codes), interleave(w.fc1_scales), w.fc2_codes,
+                         w.fc2_scales)
+    a = oracle.forward(oracle.Layer.from_spec(wl.spec), wl.tokens.x, wl.tokens.logits, w)
+    b = oracle.forward(oracle.Layer.from_spec(wl.spec, fc1_interleaved=True), wl.tokens.x,
+                       wl.tokens.logits, wi)
+    assert np.array_equal(a, b)
+    # and reading the interleaved rows as blocks is a different layer
+    c = oracle.forward(oracle.Layer.from_spec(wl.spec), wl.tokens.x, wl.tokens.logits, wi)
+    assert not np.allclose(a, c)
+
+
 # ---------------------------------------------------------------- permutation
 
 @pytest.mark.parametrize("T,E,k,skew", [(0, 8, 2, False), (1, 128, 8, False), (4, 4, 2, False),
