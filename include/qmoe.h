@@ -64,6 +64,13 @@ typedef enum qmoe_dtype {
     QMOE_BF16 = 1               /* x, logits and out are bfloat16 */
 } qmoe_dtype;
 
+/* qmoe_config.flags: FC1 rows stored interleaved, row 2n = gate n and row
+ * 2n+1 = up n (scale rows in the same order), the exporter layout named in
+ * the review of "[CUDA] Add INT4 and INT3 QMoE CPU/GPU offload support"
+ * (producer/consumer contract). Without it rows [0, I) are the gate and rows
+ * [I, 2I) the up projection. */
+#define QMOE_FLAG_FC1_INTERLEAVED 1
+
 /* Layer description, passed by value into qmoe_create and validated once. */
 typedef struct qmoe_config {
     uint32_t struct_size;       /* sizeof(qmoe_config): ABI guard */
@@ -78,7 +85,7 @@ typedef struct qmoe_config {
     int32_t normalize_routing;  /* 1: routing weights are the softmax over the k selected
                                    logits; 0: each selected expert's softmax probability
                                    over all num_experts logits (same top-k either way) */
-    int32_t reserved;           /* must be 0 */
+    int32_t flags;              /* QMOE_FLAG_* bits; all others must be 0 */
     int64_t max_tokens;         /* largest T accepted by qmoe_forward (>= 0) */
 } qmoe_config;
 

@@ -40,7 +40,10 @@ class Config(ctypes.Structure):
                 ("num_experts", ctypes.c_int64), ("bits", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("zero_point", ctypes.c_int32),
                 ("act_dtype", ctypes.c_int32), ("normalize_routing", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("max_tokens", ctypes.c_int64)]
+                ("flags", ctypes.c_int32), ("max_tokens", ctypes.c_int64)]
+
+
+QMOE_FLAG_FC1_INTERLEAVED = 1   # qmoe_config.flags bit (include/qmoe.h)
 
 
 class Weights(ctypes.Structure):
@@ -107,6 +110,7 @@ class LayerConfig:
     act_dtype: torch.dtype = torch.bfloat16
     max_tokens: int = 8192
     normalize_routing: bool = True   # False: weights over all experts, not renormalized over the k
+    fc1_interleaved: bool = False    # FC1 rows 2n / 2n+1 = gate n / up n (else gate block, up block)
 
 
 class QMoELayer:
@@ -133,7 +137,8 @@ class QMoELayer:
         self._keep = (fc1_codes, fc1_scales, fc2_codes, fc2_scales)
         c = Config(ctypes.sizeof(Config), cfg.top_k, cfg.hidden, cfg.inter, cfg.num_experts,
                    cfg.bits, cfg.block_size, cfg.zero_point, _ACT[cfg.act_dtype],
-                   1 if cfg.normalize_routing else 0, 0, cfg.max_tokens)
+                   1 if cfg.normalize_routing else 0,
+                   QMOE_FLAG_FC1_INTERLEAVED if cfg.fc1_interleaved else 0, cfg.max_tokens)
         w = Weights(fc1_codes.data_ptr(), fc1_scales.data_ptr(), fc2_codes.data_ptr(),
                     fc2_scales.data_ptr())
         h = ctypes.c_void_p()

@@ -82,6 +82,7 @@ __device__ __forceinline__ void token_slots(const RoutingLds& R, int T, int k, i
 template <int BITS, int UPL, bool BF16>
 __global__ __launch_bounds__(256) void decode_fc1_kernel(
     const void* __restrict__ xv, const void* __restrict__ logitsv, int T, int E, int k, bool normalize,
+    bool fc1_il,
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales, int H, int I, int bs,
     int zp, int64_t row_bytes, int64_t nblk, int lpr, int rows_block,
     int32_t* __restrict__ ws_ids, float* __restrict__ ws_w, float* __restrict__ h32,
@@ -154,16 +155,19 @@ __global__ __launch_bounds__(256) void decode_fc1_kernel(
 #pragma unroll
     for (int t = 0; t < kDecodeMaxTokens; ++t) g[t] = up[t] = 0.0f;
     if (valid) {
+      // gate and up rows of n (interleaved FC1: rows 2n and 2n+1)
+      const int64_t gr = fc1_il ? 2 * static_cast<int64_t>(n) : n;
+      const int64_t ur = fc1_il ? gr + 1 : static_cast<int64_t>(I) + n;
       UnitWords<BITS> gw[UPL], uw[UPL];
       float gs[UPL], us[UPL];
 #pragma unroll
       for (int i = 0; i < UPL; ++i) {
         const int u = lane_in_row + lpr * i;
         if (u >= units) continue;
-        gw[i] = load_unit<BITS>(ebase + static_cast<int64_t>(n) * row_bytes + u * (4 * BITS));
-        uw[i] = load_unit<BITS>(ebase + static_cast<int64_t>(I + n) * row_bytes + u * (4 * BITS));
-        gs[i] = half_to_f32(sbase[static_cast<int64_t>(n) * nblk + (32 * u) / bs]);
-        us[i] = half_to_f32(sbase[static_cast<int64_t>(I + n) * nblk + (32 * u) / bs]);
+        gw[i] = load_unit<BITS>(ebase + gr * row_bytes + u * (4 * BITS));
+        uw[i] = load_unit<BITS>(ebase + ur * row_bytes + u * (4 * BITS));
+        gs[i] = half_to_f32(sbase[gr * nblk + (32 * u) / bs]);
+        us[i] = half_to_f32(sbase[ur * nblk + (32 * u) / bs]);
       }
 #pragma unroll
       for (int i = 0; i < UPL; ++i) {
@@ -346,11 +350,13 @@ hipError_t launch_decode_t(const Layer& L, const void* x, const void* logits, vo
   dim3 g1((I + s1.rows_block - 1) / s1.rows_block, Ti * k);
   if (L.act_bf16)
     decode_fc1_kernel<BITS, UPL, true><<<g1, 256, 0, s>>>(
-        x, logits, Ti, E, k, L.normalize, L.fc1_codes, L.fc1_scales, H, I, L.bs, L.zp, L.fc1_row_bytes,
+        x, logits, Ti, E, k, L.normalize, L.fc1_interleaved, L.fc1_codes, L.fc1_scales, H, I, L.bs,
+        L.zp, L.fc1_row_bytes,
         L.fc1_nblk, s1.lpr, s1.rows_block, ids, w, h32, counters, W.n_counters);
   else
     decode_fc1_kernel<BITS, UPL, false><<<g1, 256, 0, s>>>(
-        x, logits, Ti, E, k, L.normalize, L.fc1_codes, L.fc1_scales, H, I, L.bs, L.zp, L.fc1_row_bytes,
+        x, logits, Ti, E, k, L.normalize, L.fc1_interleaved, L.fc1_codes, L.fc1_scales, H, I, L.bs,
+        L.zp, L.fc1_row_bytes,
         L.fc1_nblk, s1.lpr, s1.rows_block, ids, w, h32, counters, W.n_counters);
   stage_done(L, 1, "decode_fc1_swiglu");
   return hipGetLastError();

@@ -159,6 +159,7 @@ struct FusedArgs {
   const uint16_t* s2;
   int T, E, k, H, I, bs, zp;
   int normalize;     // routing weights over the selected k (1) or over all experts (0)
+  int fc1_il;        // FC1 rows interleaved: 2n gate n, 2n+1 up n
   int64_t rb1, rb2, nb1, nb2;
   int32_t* ws_ids;
   float* ws_w;
@@ -300,7 +301,7 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
   auto load_fc1 = [&](int it, UnitWords<BITS> (&wv)[U1], uint32_t (&sc)[U1]) {
     const int e = S.dlist[it / g1];
     const int n = 2 * (it % g1) + (q4 & 1);
-    const int row = (q4 < 2) ? n : I + n;
+    const int row = a.fc1_il ? 2 * n + (q4 >> 1) : ((q4 < 2) ? n : I + n);
     const uint8_t* rowp = a.c1 + (static_cast<int64_t>(e) * 2 * I + row) * a.rb1;
     const uint16_t* srow = a.s1 + (static_cast<int64_t>(e) * 2 * I + row) * a.nb1;
 #pragma unroll
@@ -708,6 +709,7 @@ hipError_t launch_decode_fused(const Layer& L, const void* x, const void* logits
   fa.bs = L.bs;
   fa.zp = L.zp;
   fa.normalize = L.normalize ? 1 : 0;
+  fa.fc1_il = L.fc1_interleaved ? 1 : 0;
   fa.rb1 = L.fc1_row_bytes;
   fa.rb2 = L.fc2_row_bytes;
   fa.nb1 = L.fc1_nblk;

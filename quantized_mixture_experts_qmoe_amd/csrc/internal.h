@@ -16,6 +16,7 @@ struct Layer {
   int k, bits, bs, zp;
   bool act_bf16;
   bool normalize;   // routing weights: softmax over the selected k (else over all experts)
+  bool fc1_interleaved;   // FC1 row 2n = gate n, row 2n+1 = up n (else gate rows, then up rows)
   int64_t max_tokens;
   const uint8_t* fc1_codes;
   const uint16_t* fc1_scales;

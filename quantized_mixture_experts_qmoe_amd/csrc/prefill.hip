@@ -76,7 +76,7 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(2,
 void grouped_gemm_kernel(
     const uint16_t* __restrict__ a_src, const int32_t* __restrict__ sorted_routes, int k,
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales, int K, int H, int I,
-    int bs_shift, int zp, int64_t row_bytes, int64_t nblk, const int4* __restrict__ tiles,
+    int bs_shift, int zp, bool fc1_il, int64_t row_bytes, int64_t nblk, const int4* __restrict__ tiles,
     const int32_t* __restrict__ num_tiles, int n_tiles_n, uint16_t* __restrict__ h_out,
     float* __restrict__ y_out) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][kBM * kLdsStride];
@@ -108,7 +108,8 @@ void grouped_gemm_kernel(
   int w_row;
   if (FC1) {
     const int c = n0 + (b_row & (kBN / 2 - 1));
-    w_row = c < I ? ((b_row < kBN / 2) ? c : I + c) : 0;
+    const int up = b_row >= kBN / 2;   // gate rows of the tile first, then the matching up rows
+    w_row = c < I ? (fc1_il ? 2 * c + up : (up ? I + c : c)) : 0;
   } else {
     const int c = n0 + b_row;
     w_row = c < H ? c : 0;
@@ -318,11 +319,13 @@ hipError_t launch_gemms(const Layer& L, const uint16_t* xb, char* ws, const Work
   const int64_t g1 = 8 * ((W.max_tiles * nt1 + 7) / 8);
   const int64_t g2 = 8 * ((W.max_tiles * nt2 + 7) / 8);
   grouped_gemm_kernel<BITS, true><<<static_cast<unsigned>(g1), kGemmThreads, 0, s>>>(
-      xb, sorted, L.k, L.fc1_codes, L.fc1_scales, H, H, I, bs_shift, L.zp, L.fc1_row_bytes, L.fc1_nblk,
+      xb, sorted, L.k, L.fc1_codes, L.fc1_scales, H, H, I, bs_shift, L.zp, L.fc1_interleaved,
+      L.fc1_row_bytes, L.fc1_nblk,
       tiles, ntiles, nt1, hb, nullptr);
   stage_done(L, 6, "gemm_fc1_swiglu");
   grouped_gemm_kernel<BITS, false><<<static_cast<unsigned>(g2), kGemmThreads, 0, s>>>(
-      hb, sorted, L.k, L.fc2_codes, L.fc2_scales, I, H, I, bs_shift, L.zp, L.fc2_row_bytes, L.fc2_nblk,
+      hb, sorted, L.k, L.fc2_codes, L.fc2_scales, I, H, I, bs_shift, L.zp, false,
+      L.fc2_row_bytes, L.fc2_nblk,
       tiles, ntiles, nt2, nullptr, yf);
   stage_done(L, 7, "gemm_fc2");
   return hipGetLastError();

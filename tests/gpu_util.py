@@ -17,12 +17,13 @@ def say(msg: str):
     sys.stdout.flush()
 
 
-def layer_for(wl: qi.Workload, max_tokens: int = 8192, normalize: bool = True) -> q.QMoELayer:
+def layer_for(wl: qi.Workload, max_tokens: int = 8192, normalize: bool = True,
+              fc1_interleaved: bool = False) -> q.QMoELayer:
     s = wl.spec
     w = wl.weights
     cfg = q.LayerConfig(s.hidden, s.inter, s.num_experts, s.top_k, s.bits, s.block_size,
                         s.zero_point, torch.float32 if s.act_dtype == "f32" else torch.bfloat16,
-                        max_tokens, normalize)
+                        max_tokens, normalize, fc1_interleaved)
     return q.QMoELayer(cfg, torch.from_numpy(w.fc1_codes).to(DEV),
                        torch.from_numpy(w.fc1_scales).to(DEV), torch.from_numpy(w.fc2_codes).to(DEV),
                        torch.from_numpy(w.fc2_scales).to(DEV))

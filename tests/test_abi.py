@@ -44,12 +44,12 @@ def test_status_strings():
 
 def _cfg(**kw):
     base = dict(hidden=2048, inter=768, num_experts=128, top_k=8, bits=4, block_size=32,
-                zero_point=-1, act_dtype=q.QMOE_BF16, normalize_routing=1, reserved=0,
+                zero_point=-1, act_dtype=q.QMOE_BF16, normalize_routing=1, flags=0,
                 max_tokens=8192)
     base.update(kw)
     c = q.Config(ctypes.sizeof(q.Config), base["top_k"], base["hidden"], base["inter"],
                  base["num_experts"], base["bits"], base["block_size"], base["zero_point"],
-                 base["act_dtype"], base["normalize_routing"], base["reserved"], base["max_tokens"])
+                 base["act_dtype"], base["normalize_routing"], base["flags"], base["max_tokens"])
     return c
 
 
@@ -69,7 +69,7 @@ def _create(c, w=None):
     ({"inter": -768}, 1), ({"bits": 5}, 1), ({"bits": 1}, 1), ({"block_size": 16}, 1),
     ({"block_size": 96}, 1), ({"hidden": 2048 + 32, "block_size": 64}, 1),
     ({"inter": 784}, 1), ({"zero_point": 16}, 1), ({"zero_point": -2}, 1),
-    ({"act_dtype": 7}, 1), ({"reserved": 1}, 1), ({"max_tokens": -1}, 1),
+    ({"act_dtype": 7}, 1), ({"flags": 2}, 1), ({"flags": -1}, 1), ({"max_tokens": -1}, 1),
     ({"normalize_routing": 2}, 1), ({"normalize_routing": -1}, 1),
     ({"num_experts": 2048, "top_k": 8}, 2), ({"top_k": 64}, 2), ({"hidden": 16384}, 2),
 ])

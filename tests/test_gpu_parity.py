@@ -368,6 +368,46 @@ def test_unnormalized_routing_parity(name, T, force):
     assert rep.ok, rep
 
 
+def interleave_fc1(wl):
+    """The same layer with its FC1 rows (and scale rows) stored interleaved."""
+    w, I = wl.weights, wl.spec.inter
+
+    def il(a):
+        out = np.empty_like(a)
+        out[:, 0::2], out[:, 1::2] = a[:, :I], a[:, I:]
+        return out
+
+    return qi.Workload(wl.name, wl.spec, wl.tokens,
+                       qi.LayerWeights(il(w.fc1_codes), il(w.fc1_scales), w.fc2_codes, w.fc2_scales))
+
+
+@pytest.mark.parametrize("name,T,force", [("decode", 4, None), ("decode", 8, None),
+                                          ("decode", 2, "decode_split"), ("int3", 300, None),
+                                          ("tiny", 4, None), ("f32", 45, None)])
+def test_interleaved_fc1_rows(name, T, force):
+    """FC1 stored interleaved (row 2n gate n, row 2n+1 up n) on every FC1 path
+    (fused, grouped and split decode, prefill; bf16 and fp32): the output
+    equals, bit for bit, the block-layout run of the same rows (only the rows'
+    addresses differ), and matches the oracle on the interleaved layout."""
+    if name == "f32":
+        wl = qi.make_layer(small_spec(4, 32, act="f32", hidden=192, inter=96), T=T, seed=5)
+    else:
+        wl = qi.make_workload(name, T=T)
+    wi = interleave_fc1(wl)
+    with _env(**({"QMOE_FORCE_PATH": force} if force else {})):
+        lb = layer_for(wl, max(T, 8))
+        li = layer_for(wi, max(T, 8), fc1_interleaved=True)
+    a, _ = run(lb, wl.tokens.x, wl.tokens.logits)
+    b, _ = run(li, wl.tokens.x, wl.tokens.logits)
+    assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                       b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
+    ref = oracle.forward(oracle.Layer.from_spec(wl.spec, fc1_interleaved=True), wl.tokens.x,
+                         wl.tokens.logits, wi.weights)
+    rep = compare(b, ref)
+    say(f"interleaved FC1 {name} T={T} path={force or 'default'}: {rep}")
+    assert rep.ok, rep
+
+
 # ------------------------------------------------------------------ properties
 
 def test_decode_and_prefill_agree():
