@@ -182,10 +182,24 @@ class QMoELayer:
 
     def forward(self, x: torch.Tensor, logits: torch.Tensor, out: Optional[torch.Tensor] = None,
                 workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """x [T, hidden] or [batch, seq, hidden]; logits [T, num_experts], or for
+        3-D x [batch, seq, num_experts] or [batch * seq, num_experts]. A 3-D
+        input is the same packed token-major rows (batch * seq tokens, viewed
+        without a copy); the output has x's shape."""
+        shape = x.shape
+        if x.dim() == 3:
+            if not x.is_contiguous() or not logits.is_contiguous():
+                raise ValueError("x and logits must be contiguous")
+            if logits.dim() == 3 and logits.shape[:2] != x.shape[:2]:
+                raise ValueError("3-D logits must match x's [batch, seq]")
+            x = x.view(-1, x.shape[-1])
+            logits = logits.view(-1, logits.shape[-1])
         self._check_tokens(x, logits)
         T = x.shape[0]
         if out is None:
-            out = torch.empty_like(x)
+            out = torch.empty(shape, dtype=x.dtype, device=x.device)
+        elif out.shape != shape or out.dtype != x.dtype or not out.is_contiguous():
+            raise ValueError("out must be a contiguous tensor shaped and typed like x")
         ws = workspace if workspace is not None else self.workspace(T)
         _check(lib().qmoe_forward(self._h, _ptr(x), _ptr(logits), _ptr(out), T, _ptr(ws),
                                   ws.numel() * ws.element_size(), _stream()), "qmoe_forward")

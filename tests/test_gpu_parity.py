@@ -408,6 +408,25 @@ def test_interleaved_fc1_rows(name, T, force):
     assert rep.ok, rep
 
 
+def test_three_dimensional_input():
+    """x [batch, seq, hidden] is the packed token-major layout with a leading
+    dimension: the output (shaped like x) equals the 2-D run bit for bit, with
+    3-D and with flattened logits, on the decode and the prefill path."""
+    for T, B in ((4, 2), (40, 4)):
+        wl = qi.make_workload("decode", T=T)
+        layer = layer_for(wl, T)
+        x, l = wl.tokens.x.to(DEV), wl.tokens.logits.to(DEV)
+        ref = layer(x, l)
+        a = layer(x.view(B, T // B, -1), l.view(B, T // B, -1))
+        b = layer(x.view(B, T // B, -1), l)
+        torch.cuda.synchronize()
+        assert a.shape == (B, T // B, x.shape[1]) and b.shape == a.shape
+        assert torch.equal(a.view(T, -1).view(torch.int16), ref.view(torch.int16))
+        assert torch.equal(b.view(T, -1).view(torch.int16), ref.view(torch.int16))
+        with pytest.raises(ValueError):
+            layer(x.view(B, T // B, -1), l.view(1, T, -1))
+
+
 # ------------------------------------------------------------------ properties
 
 def test_decode_and_prefill_agree():
