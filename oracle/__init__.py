@@ -61,19 +61,24 @@ def lib():
         L.oracle_route.argtypes = [P, i64, i64, i32, i32, P, P]
         L.oracle_permute.argtypes = [P, i64, i64, P, P, P, P]
         L.oracle_forward.argtypes = [ctypes.POINTER(_Layer), P, P, P, P, P, P, i64, P, i32]
+        L.oracle_forward_bias.argtypes = [ctypes.POINTER(_Layer), P, P, P, P, P, P, P, P, i64, P, i32]
         L.oracle_round_output.argtypes = [P, i64, P, P]
         L.oracle_round_output.restype = None
         L.oracle_half_to_double_n.argtypes = [P, i64, P]
         L.oracle_half_to_double_n.restype = None
         L.oracle_f32_to_bf16_n.argtypes = [P, i64, P]
         L.oracle_f32_to_bf16_n.restype = None
-        for f in (L.oracle_dequant, L.oracle_route, L.oracle_permute, L.oracle_forward):
+        for f in (L.oracle_dequant, L.oracle_route, L.oracle_permute, L.oracle_forward,
+                  L.oracle_forward_bias):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
 
 
-def _p(a: np.ndarray):
+def _p(a: Optional[np.ndarray]):
+    """Pointer to a C-contiguous array (None for an absent optional input)."""
+    if a is None:
+        return None
     assert a.flags["C_CONTIGUOUS"]
     return a.ctypes.data_as(ctypes.c_void_p)
 
@@ -164,8 +169,11 @@ class Layer:
 
 
 def forward(layer: Layer, x, logits, weights, *, nthreads: Optional[int] = None,
-            emulate: int = 0) -> np.ndarray:
-    """Whole layer in double precision; returns the float64 accumulator [T, H]."""
+            emulate: int = 0, fc1_bias=None, fc2_bias=None) -> np.ndarray:
+    """Whole layer in double precision; returns the float64 accumulator [T, H].
+    fc1_bias [E, 2I] and fc2_bias [E, H] (optional, any float dtype, read as
+    exact values) are added to FC1 rows before SwiGLU and to y before the
+    routing-weighted sum."""
     x64 = as_f64(x)
     l64 = as_f64(logits)
     T = x64.shape[0]
@@ -182,8 +190,12 @@ def forward(layer: Layer, x, logits, weights, *, nthreads: Optional[int] = None,
                int(bool(layer.normalize)), int(bool(layer.fc1_interleaved)), 0)
     if nthreads is None:
         nthreads = default_threads()
-    _check(lib().oracle_forward(ctypes.byref(L), _p(x64), _p(l64), _p(c1), _p(s1), _p(c2), _p(s2),
-                                T, _p(out), nthreads), "forward")
+    b1 = None if fc1_bias is None else as_f64(fc1_bias)
+    b2 = None if fc2_bias is None else as_f64(fc2_bias)
+    assert b1 is None or b1.shape == (E, 2 * I)
+    assert b2 is None or b2.shape == (E, H)
+    _check(lib().oracle_forward_bias(ctypes.byref(L), _p(x64), _p(l64), _p(c1), _p(s1), _p(c2),
+                                     _p(s2), _p(b1), _p(b2), T, _p(out), nthreads), "forward")
     return out
 
 

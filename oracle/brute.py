@@ -72,7 +72,8 @@ def silu(v: np.ndarray) -> np.ndarray:
 
 def dense_masked_forward(x64: np.ndarray, logits64: np.ndarray, weights, spec,
                          *, swap_gate_up: bool = False, zp_delta: int = 0,
-                         softmax_all: bool = False) -> np.ndarray:
+                         softmax_all: bool = False, fc1_bias=None, fc2_bias=None,
+                         bias_after_silu: bool = False) -> np.ndarray:
     """Masked-mixture formulation of the layer in float64.
 
     The keyword switches plant deliberate mistakes; tests use them to show that
@@ -99,9 +100,16 @@ def dense_masked_forward(x64: np.ndarray, logits64: np.ndarray, weights, spec,
         W2 = dequant_dense(weights.fc2_codes[e], weights.fc2_scales[e], spec.bits,
                            spec.block_size, zp, I)                   # [H, I]
         gu = x64 @ W1.T                                             # [T, 2I]
+        if fc1_bias is not None and not bias_after_silu:
+            gu = gu + fc1_bias[e][None, :]
         g, u = gu[:, :I], gu[:, I:]
         if swap_gate_up:
             g, u = u, g
         h = silu(g) * u
-        out += gate[:, e:e + 1] * (h @ W2.T)
+        if fc1_bias is not None and bias_after_silu:
+            h = h + fc1_bias[e][None, :I]
+        y = h @ W2.T
+        if fc2_bias is not None:
+            y = y + fc2_bias[e][None, :]
+        out += gate[:, e:e + 1] * y
     return out

@@ -39,6 +39,12 @@
  *    "[CUDA] Add INT4 and INT3 QMoE CPU/GPU offload support", producer/
  *    consumer contract) row 2n is gate n and row 2n+1 is up n, and the scale
  *    rows follow the same order;
+ *  - optional biases ("[CUDA] Add INT4 and INT3 QMoE CPU/GPU offload
+ *    support", commit notes: FC1/FC2 biases [E, 2I] and [E, H] in the
+ *    activation dtype; the FC2 bias, indexed by the original expert, is added
+ *    before rounding): the FC1 bias of a row is added to that row's dot
+ *    product (gate and up, in the rows' storage order) before SwiGLU, and the
+ *    FC2 bias of output m to y[m] before the routing-weighted sum;
  *  - W[n][k] = (q[n][k] - zp) * s[n][k / block]; INT4 two codes per byte low
  *    nibble first, INT2 four per byte low bits first, INT3 eight codes per
  *    three bytes with code i at bits [3i, 3i+3) of the little-endian 24-bit
@@ -216,6 +222,7 @@ typedef struct {
     const double *x, *logits;
     const uint8_t *fc1_codes, *fc2_codes;
     const uint16_t *fc1_scales, *fc2_scales;
+    const double *fc1_bias, *fc2_bias;   /* [E, 2I] and [E, H], or NULL */
     double *out;
     int64_t t0, t1;
     int status;
@@ -271,12 +278,17 @@ static void *run_tokens(void *arg)
                 const int64_t ur = jb->L->fc1_interleaved ? 2 * n + 1 : I + n;
                 double g = row_dot(c1 + gr * rb1, s1 + gr * nb1, xt, H, bits, bs, zp, emu_w);
                 double u = row_dot(c1 + ur * rb1, s1 + ur * nb1, xt, H, bits, bs, zp, emu_w);
+                if (jb->fc1_bias) {
+                    g += jb->fc1_bias[e * 2 * I + gr];
+                    u += jb->fc1_bias[e * 2 * I + ur];
+                }
                 if (emu_gu) { g = to_bf16(g); u = to_bf16(u); }
                 double hv = g / (1.0 + exp(-g)) * u;
                 h[n] = emu_h ? to_bf16(hv) : hv;
             }
             for (int64_t m = 0; m < H; ++m) {
                 double y = row_dot(c2 + m * rb2, s2 + m * nb2, h, I, bits, bs, zp, emu_w);
+                if (jb->fc2_bias) y += jb->fc2_bias[e * H + m];
                 acc[m] += w[j] * y;
             }
         }
@@ -292,10 +304,11 @@ static void *run_tokens(void *arg)
  * x: [T, H] double, logits: [T, E] double, out: [T, H] double.
  * Tokens are split into contiguous ranges over nthreads POSIX threads.
  */
-int oracle_forward(const oracle_layer *L, const double *x, const double *logits,
-                   const uint8_t *fc1_codes, const uint16_t *fc1_scales,
-                   const uint8_t *fc2_codes, const uint16_t *fc2_scales,
-                   int64_t T, double *out, int nthreads)
+int oracle_forward_bias(const oracle_layer *L, const double *x, const double *logits,
+                        const uint8_t *fc1_codes, const uint16_t *fc1_scales,
+                        const uint8_t *fc2_codes, const uint16_t *fc2_scales,
+                        const double *fc1_bias, const double *fc2_bias,
+                        int64_t T, double *out, int nthreads)
 {
     if (!L || T < 0) return ORACLE_BAD_ARG;
     if (T == 0) return ORACLE_OK;
@@ -311,8 +324,8 @@ int oracle_forward(const oracle_layer *L, const double *x, const double *logits,
     pthread_t *th = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
     if (!jobs || !th) { free(jobs); free(th); return ORACLE_NO_MEM; }
     for (int i = 0; i < nthreads; ++i) {
-        jobs[i] = (job){L, x, logits, fc1_codes, fc2_codes, fc1_scales, fc2_scales, out,
-                        T * i / nthreads, T * (i + 1) / nthreads, ORACLE_OK};
+        jobs[i] = (job){L, x, logits, fc1_codes, fc2_codes, fc1_scales, fc2_scales, fc1_bias,
+                        fc2_bias, out, T * i / nthreads, T * (i + 1) / nthreads, ORACLE_OK};
     }
     int started = 0;
     for (int i = 1; i < nthreads; ++i) {
@@ -327,6 +340,15 @@ int oracle_forward(const oracle_layer *L, const double *x, const double *logits,
         if (jobs[i].status != ORACLE_OK) st = jobs[i].status;
     free(jobs); free(th);
     return st;
+}
+
+int oracle_forward(const oracle_layer *L, const double *x, const double *logits,
+                   const uint8_t *fc1_codes, const uint16_t *fc1_scales,
+                   const uint8_t *fc2_codes, const uint16_t *fc2_scales,
+                   int64_t T, double *out, int nthreads)
+{
+    return oracle_forward_bias(L, x, logits, fc1_codes, fc1_scales, fc2_codes, fc2_scales, NULL,
+                               NULL, T, out, nthreads);
 }
 
 /* Final rounding: double accumulator -> fp32 (one rounding) and -> bf16 of that fp32. */

@@ -297,6 +297,32 @@ def _close(a, b, rtol=1e-12):
     return np.abs(a - b).max() <= rtol * scale
 
 
+def test_biases_against_dense_masked():
+    """Optional FC1/FC2 biases: the oracle equals the dense masked mixture with
+    the FC1 bias added to the gate/up projections before SwiGLU and the FC2
+    bias to y before the routing weights; placing the FC1 bias after the
+    activation, or dropping either bias, would be noticed."""
+    wl = qi.make_workload("tiny")
+    rng = np.random.default_rng(21)
+    E, H, I = wl.spec.num_experts, wl.spec.hidden, wl.spec.inter
+    b1 = rng.standard_normal((E, 2 * I)) * 0.5
+    b2 = rng.standard_normal((E, H)) * 0.5
+    got = oracle.forward(oracle.Layer.from_spec(wl.spec), wl.tokens.x, wl.tokens.logits,
+                         wl.weights, fc1_bias=b1, fc2_bias=b2)
+    x64, l64 = oracle.as_f64(wl.tokens.x), oracle.as_f64(wl.tokens.logits)
+    ref = brute.dense_masked_forward(x64, l64, wl.weights, wl.spec, fc1_bias=b1, fc2_bias=b2)
+    assert _close(got, ref)
+    for kw in ({"fc1_bias": b1, "fc2_bias": b2, "bias_after_silu": True},
+               {"fc2_bias": b2}, {"fc1_bias": b1}):
+        assert not _close(got, brute.dense_masked_forward(x64, l64, wl.weights, wl.spec, **kw))
+    # the FC2 bias enters linearly: out(b2) - out(0) = sum_j w_j b2[e_j]
+    nob = oracle.forward(oracle.Layer.from_spec(wl.spec), wl.tokens.x, wl.tokens.logits,
+                         wl.weights, fc1_bias=b1)
+    ids, w = oracle.route(wl.tokens.logits, wl.spec.top_k)
+    lin = np.einsum("tj,tjm->tm", w, b2[ids])
+    assert _close(got - nob, lin)
+
+
 def test_tiny_layer_against_dense_masked():
     wl = qi.make_workload("tiny")
     acc = _run(wl)
