@@ -95,6 +95,14 @@ typedef struct qmoe_weights {
     const void *fc1_scales;
     const void *fc2_codes;
     const void *fc2_scales;
+    /* Optional biases in the activation dtype, or NULL: fc1_bias [E, 2I] is
+     * added to each FC1 row's output (gate and up rows, in their storage
+     * order) before SwiGLU, fc2_bias [E, H] to the expert's output before the
+     * routing-weighted combine ("[CUDA] Add INT4 and INT3 QMoE CPU/GPU
+     * offload support", commit notes). Layers with a bias run the split
+     * decode for T <= 4, not the fused one. */
+    const void *fc1_bias;
+    const void *fc2_bias;
 } qmoe_weights;
 
 typedef struct qmoe_handle qmoe_handle;

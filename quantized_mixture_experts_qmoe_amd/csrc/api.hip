@@ -163,6 +163,8 @@ qmoe_status qmoe_create(const qmoe_config* c, const qmoe_weights* w, int device,
   if (!aligned16(w->fc1_codes) || !aligned16(w->fc1_scales) || !aligned16(w->fc2_codes) ||
       !aligned16(w->fc2_scales))
     return QMOE_ERR_INVALID_ARG;
+  if ((w->fc1_bias && !aligned16(w->fc1_bias)) || (w->fc2_bias && !aligned16(w->fc2_bias)))
+    return QMOE_ERR_INVALID_ARG;
   // limits of this implementation
   if (c->num_experts > kMaxExperts || c->top_k > kMaxTopK) return QMOE_ERR_UNSUPPORTED;
   if (c->hidden > 8192 || c->inter > 8192) return QMOE_ERR_UNSUPPORTED;
@@ -189,6 +191,8 @@ qmoe_status qmoe_create(const qmoe_config* c, const qmoe_weights* w, int device,
   L.fc1_scales = static_cast<const uint16_t*>(w->fc1_scales);
   L.fc2_codes = static_cast<const uint8_t*>(w->fc2_codes);
   L.fc2_scales = static_cast<const uint16_t*>(w->fc2_scales);
+  L.fc1_bias = w->fc1_bias;
+  L.fc2_bias = w->fc2_bias;
   L.fc1_row_bytes = L.H * L.bits / 8;
   L.fc2_row_bytes = L.I * L.bits / 8;
   L.fc1_nblk = L.H / L.bs;

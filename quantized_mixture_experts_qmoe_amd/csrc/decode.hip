@@ -82,7 +82,7 @@ __device__ __forceinline__ void token_slots(const RoutingLds& R, int T, int k, i
 template <int BITS, int UPL, bool BF16>
 __global__ __launch_bounds__(256) void decode_fc1_kernel(
     const void* __restrict__ xv, const void* __restrict__ logitsv, int T, int E, int k, bool normalize,
-    bool fc1_il,
+    bool fc1_il, const void* __restrict__ fc1_bias,
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales, int H, int I, int bs,
     int zp, int64_t row_bytes, int64_t nblk, int lpr, int rows_block,
     int32_t* __restrict__ ws_ids, float* __restrict__ ws_w, float* __restrict__ h32,
@@ -154,10 +154,10 @@ __global__ __launch_bounds__(256) void decode_fc1_kernel(
     float g[kDecodeMaxTokens], up[kDecodeMaxTokens];
 #pragma unroll
     for (int t = 0; t < kDecodeMaxTokens; ++t) g[t] = up[t] = 0.0f;
+    // gate and up rows of n (interleaved FC1: rows 2n and 2n+1)
+    const int64_t gr = fc1_il ? 2 * static_cast<int64_t>(n) : n;
+    const int64_t ur = fc1_il ? gr + 1 : static_cast<int64_t>(I) + n;
     if (valid) {
-      // gate and up rows of n (interleaved FC1: rows 2n and 2n+1)
-      const int64_t gr = fc1_il ? 2 * static_cast<int64_t>(n) : n;
-      const int64_t ur = fc1_il ? gr + 1 : static_cast<int64_t>(I) + n;
       UnitWords<BITS> gw[UPL], uw[UPL];
       float gs[UPL], us[UPL];
 #pragma unroll
@@ -201,8 +201,8 @@ __global__ __launch_bounds__(256) void decode_fc1_kernel(
 #pragma unroll
     for (int t = 0; t < kDecodeMaxTokens; ++t) {
       if (slot[t] < 0) continue;
-      const float gt = group_sum(g[t], lpr);
-      const float ut = group_sum(up[t], lpr);
+      const float gt = group_sum(g[t], lpr) + (valid ? bias_at(fc1_bias, BF16, e * 2LL * I + gr) : 0.0f);
+      const float ut = group_sum(up[t], lpr) + (valid ? bias_at(fc1_bias, BF16, e * 2LL * I + ur) : 0.0f);
       if (valid && lane_in_row == 0)
         h32[static_cast<int64_t>(t * k + slot[t]) * I + n] = silu_mul(gt, ut);
     }
@@ -215,8 +215,8 @@ __global__ __launch_bounds__(256) void decode_fc2_kernel(
     const float* __restrict__ h32, const int32_t* __restrict__ ws_ids,
     const float* __restrict__ ws_w, int T, int k, const uint8_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, int H, int I, int bs, int zp, int64_t row_bytes,
-    int64_t nblk, int lpr, int rows_block, float* __restrict__ y32,
-    int32_t* __restrict__ counters, void* __restrict__ out) {
+    int64_t nblk, int lpr, int rows_block, const void* __restrict__ fc2_bias,
+    float* __restrict__ y32, int32_t* __restrict__ counters, void* __restrict__ out) {
   __shared__ RoutingLds R;
   __shared__ int s_last;
   const int nroutes = T * k;
@@ -305,7 +305,7 @@ __global__ __launch_bounds__(256) void decode_fc2_kernel(
 #pragma unroll
     for (int t = 0; t < kDecodeMaxTokens; ++t) {
       if (slot[t] < 0) continue;
-      const float yt = group_sum(y[t], lpr);
+      const float yt = group_sum(y[t], lpr) + (valid ? bias_at(fc2_bias, OUT_BF16, e * static_cast<int64_t>(H) + m) : 0.0f);
       if (valid && lane_in_row == 0) y32[static_cast<int64_t>(t * k + slot[t]) * H + m] = yt;
     }
   }
@@ -350,12 +350,14 @@ hipError_t launch_decode_t(const Layer& L, const void* x, const void* logits, vo
   dim3 g1((I + s1.rows_block - 1) / s1.rows_block, Ti * k);
   if (L.act_bf16)
     decode_fc1_kernel<BITS, UPL, true><<<g1, 256, 0, s>>>(
-        x, logits, Ti, E, k, L.normalize, L.fc1_interleaved, L.fc1_codes, L.fc1_scales, H, I, L.bs,
+        x, logits, Ti, E, k, L.normalize, L.fc1_interleaved, L.fc1_bias, L.fc1_codes, L.fc1_scales, H,
+        I, L.bs,
         L.zp, L.fc1_row_bytes,
         L.fc1_nblk, s1.lpr, s1.rows_block, ids, w, h32, counters, W.n_counters);
   else
     decode_fc1_kernel<BITS, UPL, false><<<g1, 256, 0, s>>>(
-        x, logits, Ti, E, k, L.normalize, L.fc1_interleaved, L.fc1_codes, L.fc1_scales, H, I, L.bs,
+        x, logits, Ti, E, k, L.normalize, L.fc1_interleaved, L.fc1_bias, L.fc1_codes, L.fc1_scales, H,
+        I, L.bs,
         L.zp, L.fc1_row_bytes,
         L.fc1_nblk, s1.lpr, s1.rows_block, ids, w, h32, counters, W.n_counters);
   stage_done(L, 1, "decode_fc1_swiglu");
@@ -376,11 +378,11 @@ hipError_t launch_fc2_t(const Layer& L, void* out, int64_t T, char* ws, const Wo
   if (L.act_bf16)
     decode_fc2_kernel<BITS, UPL, true><<<g2, 256, 0, s>>>(
         h32, ids, w, Ti, k, L.fc2_codes, L.fc2_scales, H, I, L.bs, L.zp, L.fc2_row_bytes,
-        L.fc2_nblk, s2.lpr, s2.rows_block, y32, counters, out);
+        L.fc2_nblk, s2.lpr, s2.rows_block, L.fc2_bias, y32, counters, out);
   else
     decode_fc2_kernel<BITS, UPL, false><<<g2, 256, 0, s>>>(
         h32, ids, w, Ti, k, L.fc2_codes, L.fc2_scales, H, I, L.bs, L.zp, L.fc2_row_bytes,
-        L.fc2_nblk, s2.lpr, s2.rows_block, y32, counters, out);
+        L.fc2_nblk, s2.lpr, s2.rows_block, L.fc2_bias, y32, counters, out);
   stage_done(L, 2, "decode_fc2_combine");
   return hipGetLastError();
 }

@@ -380,6 +380,12 @@ __device__ __forceinline__ void topk_softmax_bf16_wave(const uint16_t (&lg)[SLOT
   wt = ex / sum;
 }
 
+// Element i of an optional bias in the activation dtype (0 when absent).
+__device__ __forceinline__ float bias_at(const void* b, bool bf16, int64_t i) {
+  if (!b) return 0.0f;
+  return bf16 ? bf16_to_f32(static_cast<const uint16_t*>(b)[i]) : static_cast<const float*>(b)[i];
+}
+
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 
 // silu(g) * u with the hardware exp2 and reciprocal (a few ulp in fp32), for

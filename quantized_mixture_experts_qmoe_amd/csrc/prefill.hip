@@ -76,7 +76,8 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(2,
 void grouped_gemm_kernel(
     const uint16_t* __restrict__ a_src, const int32_t* __restrict__ sorted_routes, int k,
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales, int K, int H, int I,
-    int bs_shift, int zp, bool fc1_il, int64_t row_bytes, int64_t nblk, const int4* __restrict__ tiles,
+    int bs_shift, int zp, bool fc1_il, const void* __restrict__ bias, bool bias_bf16,
+    int64_t row_bytes, int64_t nblk, const int4* __restrict__ tiles,
     const int32_t* __restrict__ num_tiles, int n_tiles_n, uint16_t* __restrict__ h_out,
     float* __restrict__ y_out) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][kBM * kLdsStride];
@@ -236,7 +237,20 @@ void grouped_gemm_kernel(
   }
   if (!wave_live) return;
 
-  // ---- epilogue: lane holds rows 4*quad + i, column l16 of each 16x16 tile
+  // ---- epilogue: lane holds rows 4*quad + i, column l16 of each 16x16 tile;
+  // the optional bias is per column (FC1: the gate and up rows' biases)
+  float bcol[8];
+#pragma unroll
+  for (int tn = 0; tn < 8; ++tn) {
+    if (FC1) {
+      const int c = n0 + wn * 64 + (tn & 3) * 16 + l16, up = tn >> 2;
+      const int64_t r = fc1_il ? 2 * c + up : (up ? I + c : c);
+      bcol[tn] = c < I ? bias_at(bias, bias_bf16, static_cast<int64_t>(e) * 2 * I + r) : 0.0f;
+    } else {
+      const int c = n0 + wn * 128 + tn * 16 + l16;
+      bcol[tn] = c < H ? bias_at(bias, bias_bf16, static_cast<int64_t>(e) * H + c) : 0.0f;
+    }
+  }
 #pragma unroll
   for (int tm = 0; tm < 4; ++tm) {
 #pragma unroll
@@ -249,7 +263,7 @@ void grouped_gemm_kernel(
         for (int tn = 0; tn < 4; ++tn) {
           const int c = n0 + wn * 64 + tn * 16 + l16;
           if (c < I) {
-            const float hv = silu_mul_fast(acc[tm][tn][i], acc[tm][tn + 4][i]);
+            const float hv = silu_mul_fast(acc[tm][tn][i] + bcol[tn], acc[tm][tn + 4][i] + bcol[tn + 4]);
             h_out[orow * I + c] = static_cast<uint16_t>(f32_to_bf16(hv));
           }
         }
@@ -257,7 +271,7 @@ void grouped_gemm_kernel(
 #pragma unroll
         for (int tn = 0; tn < 8; ++tn) {
           const int c = n0 + wn * 128 + tn * 16 + l16;
-          if (c < H) y_out[orow * H + c] = acc[tm][tn][i];
+          if (c < H) y_out[orow * H + c] = acc[tm][tn][i] + bcol[tn];
         }
       }
     }
@@ -320,11 +334,13 @@ hipError_t launch_gemms(const Layer& L, const uint16_t* xb, char* ws, const Work
   const int64_t g2 = 8 * ((W.max_tiles * nt2 + 7) / 8);
   grouped_gemm_kernel<BITS, true><<<static_cast<unsigned>(g1), kGemmThreads, 0, s>>>(
       xb, sorted, L.k, L.fc1_codes, L.fc1_scales, H, H, I, bs_shift, L.zp, L.fc1_interleaved,
+      L.fc1_bias, L.act_bf16,
       L.fc1_row_bytes, L.fc1_nblk,
       tiles, ntiles, nt1, hb, nullptr);
   stage_done(L, 6, "gemm_fc1_swiglu");
   grouped_gemm_kernel<BITS, false><<<static_cast<unsigned>(g2), kGemmThreads, 0, s>>>(
-      hb, sorted, L.k, L.fc2_codes, L.fc2_scales, I, H, I, bs_shift, L.zp, false,
+      hb, sorted, L.k, L.fc2_codes, L.fc2_scales, I, H, I, bs_shift, L.zp, false, L.fc2_bias,
+      L.act_bf16,
       L.fc2_row_bytes, L.fc2_nblk,
       tiles, ntiles, nt2, nullptr, yf);
   stage_done(L, 7, "gemm_fc2");

@@ -18,7 +18,7 @@ def say(msg: str):
 
 
 def layer_for(wl: qi.Workload, max_tokens: int = 8192, normalize: bool = True,
-              fc1_interleaved: bool = False) -> q.QMoELayer:
+              fc1_interleaved: bool = False, fc1_bias=None, fc2_bias=None) -> q.QMoELayer:
     s = wl.spec
     w = wl.weights
     cfg = q.LayerConfig(s.hidden, s.inter, s.num_experts, s.top_k, s.bits, s.block_size,
@@ -26,7 +26,9 @@ def layer_for(wl: qi.Workload, max_tokens: int = 8192, normalize: bool = True,
                         max_tokens, normalize, fc1_interleaved)
     return q.QMoELayer(cfg, torch.from_numpy(w.fc1_codes).to(DEV),
                        torch.from_numpy(w.fc1_scales).to(DEV), torch.from_numpy(w.fc2_codes).to(DEV),
-                       torch.from_numpy(w.fc2_scales).to(DEV))
+                       torch.from_numpy(w.fc2_scales).to(DEV),
+                       None if fc1_bias is None else fc1_bias.to(DEV),
+                       None if fc2_bias is None else fc2_bias.to(DEV))
 
 
 def run(layer: q.QMoELayer, x: torch.Tensor, logits: torch.Tensor):

@@ -427,6 +427,36 @@ def test_three_dimensional_input():
             layer(x.view(B, T // B, -1), l.view(1, T, -1))
 
 
+@pytest.mark.parametrize("name,T,il", [("decode", 4, False), ("decode", 2, True),
+                                       ("decode", 12, False), ("int3", 300, False),
+                                       ("prefill", 300, True), ("tiny", 4, False), ("f32", 45, False)])
+def test_biases_parity(name, T, il):
+    """Optional FC1/FC2 biases in the activation dtype, on the split decode
+    (which layers with a bias take for T <= 4) and on the prefill path, with
+    block and interleaved FC1 rows: the output matches the oracle given the
+    same biases, and differs from the run without them."""
+    if name == "f32":
+        wl = qi.make_layer(small_spec(4, 32, act="f32", hidden=192, inter=96), T=T, seed=5)
+    else:
+        wl = qi.make_workload(name, T=T)
+    if il:
+        wl = interleave_fc1(wl)
+    spec = wl.spec
+    rng = np.random.default_rng(T + 7)
+    dt = torch.float32 if spec.act_dtype == "f32" else torch.bfloat16
+    b1 = torch.from_numpy(rng.standard_normal((spec.num_experts, 2 * spec.inter)) * 0.25).to(dt)
+    b2 = torch.from_numpy(rng.standard_normal((spec.num_experts, spec.hidden)) * 0.1).to(dt)
+    layer = layer_for(wl, max(T, 8), fc1_interleaved=il, fc1_bias=b1, fc2_bias=b2)
+    out, _ = run(layer, wl.tokens.x, wl.tokens.logits)
+    ref = oracle.forward(oracle.Layer.from_spec(spec, fc1_interleaved=il), wl.tokens.x,
+                         wl.tokens.logits, wl.weights, fc1_bias=b1, fc2_bias=b2)
+    rep = compare(out, ref)
+    say(f"biases {name} T={T} interleaved={il}: {rep}")
+    assert rep.ok, rep
+    nob, _ = run(layer_for(wl, max(T, 8), fc1_interleaved=il), wl.tokens.x, wl.tokens.logits)
+    assert not torch.equal(out, nob)
+
+
 # ------------------------------------------------------------------ properties
 
 def test_decode_and_prefill_agree():
