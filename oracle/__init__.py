@@ -61,7 +61,9 @@ def lib():
         L.oracle_route.argtypes = [P, i64, i64, i32, i32, P, P]
         L.oracle_permute.argtypes = [P, i64, i64, P, P, P, P]
         L.oracle_forward.argtypes = [ctypes.POINTER(_Layer), P, P, P, P, P, P, i64, P, i32]
-        L.oracle_forward_bias.argtypes = [ctypes.POINTER(_Layer), P, P, P, P, P, P, P, P, i64, P, i32]
+        L.oracle_forward_ext.argtypes = [ctypes.POINTER(_Layer), P, P, P, P, P, P, P, P, P, P, i64, P,
+                                         i32]
+        L.oracle_dequant_zp.argtypes = [P, P, P, i64, i64, i32, i32, i32, P]
         L.oracle_round_output.argtypes = [P, i64, P, P]
         L.oracle_round_output.restype = None
         L.oracle_half_to_double_n.argtypes = [P, i64, P]
@@ -69,7 +71,7 @@ def lib():
         L.oracle_f32_to_bf16_n.argtypes = [P, i64, P]
         L.oracle_f32_to_bf16_n.restype = None
         for f in (L.oracle_dequant, L.oracle_route, L.oracle_permute, L.oracle_forward,
-                  L.oracle_forward_bias):
+                  L.oracle_forward_ext, L.oracle_dequant_zp):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -114,14 +116,17 @@ def f32_to_bf16_bits(f: np.ndarray) -> np.ndarray:
 
 
 def dequant(codes: np.ndarray, scales: np.ndarray, bits: int, block_size: int,
-            zero_point: int, K: int) -> np.ndarray:
-    """(q - zp) * s for one [N, K] matrix of packed codes -> float64 [N, K]."""
+            zero_point: int, K: int, zero_points: Optional[np.ndarray] = None) -> np.ndarray:
+    """(q - zp) * s for one [N, K] matrix of packed codes -> float64 [N, K];
+    zero_points (uint8 [N, K/bs]) replaces the scalar zero point when given."""
     codes = np.ascontiguousarray(codes, dtype=np.uint8)
     sc = np.ascontiguousarray(scales).view(np.uint16)
+    zps = None if zero_points is None else np.ascontiguousarray(zero_points, dtype=np.uint8)
     N = codes.shape[0]
+    assert zps is None or zps.shape == sc.shape
     out = np.empty((N, K), dtype=np.float64)
-    _check(lib().oracle_dequant(_p(codes), _p(sc), N, K, bits, block_size, zero_point, _p(out)),
-           "dequant")
+    _check(lib().oracle_dequant_zp(_p(codes), _p(sc), _p(zps), N, K, bits, block_size, zero_point,
+                                   _p(out)), "dequant")
     return out
 
 
@@ -169,11 +174,13 @@ class Layer:
 
 
 def forward(layer: Layer, x, logits, weights, *, nthreads: Optional[int] = None,
-            emulate: int = 0, fc1_bias=None, fc2_bias=None) -> np.ndarray:
+            emulate: int = 0, fc1_bias=None, fc2_bias=None, fc1_zero_points=None,
+            fc2_zero_points=None) -> np.ndarray:
     """Whole layer in double precision; returns the float64 accumulator [T, H].
     fc1_bias [E, 2I] and fc2_bias [E, H] (optional, any float dtype, read as
     exact values) are added to FC1 rows before SwiGLU and to y before the
-    routing-weighted sum."""
+    routing-weighted sum. fc1_zero_points / fc2_zero_points (uint8, shaped
+    like the scales) replace the scalar zero point per row and quant block."""
     x64 = as_f64(x)
     l64 = as_f64(logits)
     T = x64.shape[0]
@@ -194,8 +201,13 @@ def forward(layer: Layer, x, logits, weights, *, nthreads: Optional[int] = None,
     b2 = None if fc2_bias is None else as_f64(fc2_bias)
     assert b1 is None or b1.shape == (E, 2 * I)
     assert b2 is None or b2.shape == (E, H)
-    _check(lib().oracle_forward_bias(ctypes.byref(L), _p(x64), _p(l64), _p(c1), _p(s1), _p(c2),
-                                     _p(s2), _p(b1), _p(b2), T, _p(out), nthreads), "forward")
+    z1 = None if fc1_zero_points is None else np.ascontiguousarray(fc1_zero_points, dtype=np.uint8)
+    z2 = None if fc2_zero_points is None else np.ascontiguousarray(fc2_zero_points, dtype=np.uint8)
+    assert z1 is None or z1.shape == s1.shape
+    assert z2 is None or z2.shape == s2.shape
+    _check(lib().oracle_forward_ext(ctypes.byref(L), _p(x64), _p(l64), _p(c1), _p(s1), _p(c2),
+                                    _p(s2), _p(b1), _p(b2), _p(z1), _p(z2), T, _p(out), nthreads),
+           "forward")
     return out
 
 

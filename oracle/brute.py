@@ -43,10 +43,14 @@ def pack_codes(q: np.ndarray, bits: int) -> np.ndarray:
 
 
 def dequant_dense(codes: np.ndarray, scales: np.ndarray, bits: int, block_size: int,
-                  zero_point: int, K: int) -> np.ndarray:
+                  zero_point, K: int) -> np.ndarray:
+    """zero_point: a scalar code, or an array of codes shaped like scales."""
     q = unpack_codes(codes, bits, K)
     s = np.repeat(np.asarray(scales, dtype=np.float16).astype(np.float64), block_size, axis=-1)
-    return (q - zero_point).astype(np.float64) * s
+    z = zero_point
+    if isinstance(z, np.ndarray):
+        z = np.repeat(z.astype(np.int64), block_size, axis=-1)
+    return (q.astype(np.int64) - z).astype(np.float64) * s
 
 
 def topk_brute(logits64: np.ndarray, k: int) -> np.ndarray:
@@ -73,7 +77,8 @@ def silu(v: np.ndarray) -> np.ndarray:
 def dense_masked_forward(x64: np.ndarray, logits64: np.ndarray, weights, spec,
                          *, swap_gate_up: bool = False, zp_delta: int = 0,
                          softmax_all: bool = False, fc1_bias=None, fc2_bias=None,
-                         bias_after_silu: bool = False) -> np.ndarray:
+                         bias_after_silu: bool = False, fc1_zero_points=None,
+                         fc2_zero_points=None) -> np.ndarray:
     """Masked-mixture formulation of the layer in float64.
 
     The keyword switches plant deliberate mistakes; tests use them to show that
@@ -95,10 +100,12 @@ def dense_masked_forward(x64: np.ndarray, logits64: np.ndarray, weights, spec,
     for e in range(E):
         if not gate[:, e].any():
             continue
+        z1 = zp if fc1_zero_points is None else fc1_zero_points[e].astype(np.int64) + zp_delta
+        z2 = zp if fc2_zero_points is None else fc2_zero_points[e].astype(np.int64) + zp_delta
         W1 = dequant_dense(weights.fc1_codes[e], weights.fc1_scales[e], spec.bits,
-                           spec.block_size, zp, H)                   # [2I, H]
+                           spec.block_size, z1, H)                   # [2I, H]
         W2 = dequant_dense(weights.fc2_codes[e], weights.fc2_scales[e], spec.bits,
-                           spec.block_size, zp, I)                   # [H, I]
+                           spec.block_size, z2, I)                   # [H, I]
         gu = x64 @ W1.T                                             # [T, 2I]
         if fc1_bias is not None and not bias_after_silu:
             gu = gu + fc1_bias[e][None, :]

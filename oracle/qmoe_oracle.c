@@ -45,7 +45,10 @@
  *    before rounding): the FC1 bias of a row is added to that row's dot
  *    product (gate and up, in the rows' storage order) before SwiGLU, and the
  *    FC2 bias of output m to y[m] before the routing-weighted sum;
- *  - W[n][k] = (q[n][k] - zp) * s[n][k / block]; INT4 two codes per byte low
+ *  - W[n][k] = (q[n][k] - zp) * s[n][k / block], where zp is the layer's
+ *    scalar zero-point code or, when a zero-point tensor is given, its code
+ *    zp[n][k / block] (one unsigned byte per row and quant block, laid out
+ *    like the scales); INT4 two codes per byte low
  *    nibble first, INT2 four per byte low bits first, INT3 eight codes per
  *    three bytes with code i at bits [3i, 3i+3) of the little-endian 24-bit
  *    word;
@@ -122,8 +125,9 @@ static int valid_format(int64_t K, int bits, int bs)
 }
 
 /* W[n][kk] = (q - zp) * s for one [N, K] matrix; out is [N, K] double. */
-int oracle_dequant(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
-                   int bits, int bs, int zp, double *out)
+/* (q - zp) * s for one [N, K] matrix; zps [N, K/bs] or NULL for the scalar zp. */
+int oracle_dequant_zp(const uint8_t *codes, const uint16_t *scales, const uint8_t *zps, int64_t N,
+                      int64_t K, int bits, int bs, int zp, double *out)
 {
     if (!codes || !scales || !out || N < 0 || !valid_format(K, bits, bs)) return ORACLE_BAD_ARG;
     int64_t rb = row_bytes(K, bits), nblk = K / bs;
@@ -131,10 +135,17 @@ int oracle_dequant(const uint8_t *codes, const uint16_t *scales, int64_t N, int6
         const uint8_t *row = codes + n * rb;
         for (int64_t kk = 0; kk < K; ++kk) {
             double s = oracle_half_to_double(scales[n * nblk + kk / bs]);
-            out[n * K + kk] = (double)(code_at(row, kk, bits) - zp) * s;
+            int z = zps ? (int)zps[n * nblk + kk / bs] : zp;
+            out[n * K + kk] = (double)(code_at(row, kk, bits) - z) * s;
         }
     }
     return ORACLE_OK;
+}
+
+int oracle_dequant(const uint8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
+                   int bits, int bs, int zp, double *out)
+{
+    return oracle_dequant_zp(codes, scales, NULL, N, K, bits, bs, zp, out);
 }
 
 /* Top-k selection and the routing weights, per token: the softmax over the
@@ -223,18 +234,20 @@ typedef struct {
     const uint8_t *fc1_codes, *fc2_codes;
     const uint16_t *fc1_scales, *fc2_scales;
     const double *fc1_bias, *fc2_bias;   /* [E, 2I] and [E, H], or NULL */
+    const uint8_t *fc1_zp, *fc2_zp;      /* [E, 2I, H/bs] and [E, H, I/bs], or NULL */
     double *out;
     int64_t t0, t1;
     int status;
 } job;
 
 /* dot of one dequantized weight row with a double vector */
-static double row_dot(const uint8_t *row, const uint16_t *srow, const double *v, int64_t K,
-                      int bits, int bs, int zp, int emu_w)
+static double row_dot(const uint8_t *row, const uint16_t *srow, const uint8_t *zrow,
+                      const double *v, int64_t K, int bits, int bs, int zp, int emu_w)
 {
     double acc = 0.0;
     for (int64_t kk = 0; kk < K; ++kk) {
-        double w = (double)(code_at(row, kk, bits) - zp) * oracle_half_to_double(srow[kk / bs]);
+        int z = zrow ? (int)zrow[kk / bs] : zp;
+        double w = (double)(code_at(row, kk, bits) - z) * oracle_half_to_double(srow[kk / bs]);
         if (emu_w) w = to_bf16(w);
         acc += w * v[kk];
     }
@@ -276,8 +289,11 @@ static void *run_tokens(void *arg)
             for (int64_t n = 0; n < I; ++n) {
                 const int64_t gr = jb->L->fc1_interleaved ? 2 * n : n;
                 const int64_t ur = jb->L->fc1_interleaved ? 2 * n + 1 : I + n;
-                double g = row_dot(c1 + gr * rb1, s1 + gr * nb1, xt, H, bits, bs, zp, emu_w);
-                double u = row_dot(c1 + ur * rb1, s1 + ur * nb1, xt, H, bits, bs, zp, emu_w);
+                const uint8_t *z1 = jb->fc1_zp ? jb->fc1_zp + e * (2 * I) * nb1 : NULL;
+                double g = row_dot(c1 + gr * rb1, s1 + gr * nb1, z1 ? z1 + gr * nb1 : NULL, xt, H,
+                                   bits, bs, zp, emu_w);
+                double u = row_dot(c1 + ur * rb1, s1 + ur * nb1, z1 ? z1 + ur * nb1 : NULL, xt, H,
+                                   bits, bs, zp, emu_w);
                 if (jb->fc1_bias) {
                     g += jb->fc1_bias[e * 2 * I + gr];
                     u += jb->fc1_bias[e * 2 * I + ur];
@@ -287,7 +303,8 @@ static void *run_tokens(void *arg)
                 h[n] = emu_h ? to_bf16(hv) : hv;
             }
             for (int64_t m = 0; m < H; ++m) {
-                double y = row_dot(c2 + m * rb2, s2 + m * nb2, h, I, bits, bs, zp, emu_w);
+                const uint8_t *z2 = jb->fc2_zp ? jb->fc2_zp + (e * H + m) * nb2 : NULL;
+                double y = row_dot(c2 + m * rb2, s2 + m * nb2, z2, h, I, bits, bs, zp, emu_w);
                 if (jb->fc2_bias) y += jb->fc2_bias[e * H + m];
                 acc[m] += w[j] * y;
             }
@@ -304,11 +321,12 @@ static void *run_tokens(void *arg)
  * x: [T, H] double, logits: [T, E] double, out: [T, H] double.
  * Tokens are split into contiguous ranges over nthreads POSIX threads.
  */
-int oracle_forward_bias(const oracle_layer *L, const double *x, const double *logits,
-                        const uint8_t *fc1_codes, const uint16_t *fc1_scales,
-                        const uint8_t *fc2_codes, const uint16_t *fc2_scales,
-                        const double *fc1_bias, const double *fc2_bias,
-                        int64_t T, double *out, int nthreads)
+int oracle_forward_ext(const oracle_layer *L, const double *x, const double *logits,
+                       const uint8_t *fc1_codes, const uint16_t *fc1_scales,
+                       const uint8_t *fc2_codes, const uint16_t *fc2_scales,
+                       const double *fc1_bias, const double *fc2_bias,
+                       const uint8_t *fc1_zp, const uint8_t *fc2_zp,
+                       int64_t T, double *out, int nthreads)
 {
     if (!L || T < 0) return ORACLE_BAD_ARG;
     if (T == 0) return ORACLE_OK;
@@ -325,7 +343,8 @@ int oracle_forward_bias(const oracle_layer *L, const double *x, const double *lo
     if (!jobs || !th) { free(jobs); free(th); return ORACLE_NO_MEM; }
     for (int i = 0; i < nthreads; ++i) {
         jobs[i] = (job){L, x, logits, fc1_codes, fc2_codes, fc1_scales, fc2_scales, fc1_bias,
-                        fc2_bias, out, T * i / nthreads, T * (i + 1) / nthreads, ORACLE_OK};
+                        fc2_bias, fc1_zp, fc2_zp, out, T * i / nthreads, T * (i + 1) / nthreads,
+                        ORACLE_OK};
     }
     int started = 0;
     for (int i = 1; i < nthreads; ++i) {
@@ -347,8 +366,8 @@ int oracle_forward(const oracle_layer *L, const double *x, const double *logits,
                    const uint8_t *fc2_codes, const uint16_t *fc2_scales,
                    int64_t T, double *out, int nthreads)
 {
-    return oracle_forward_bias(L, x, logits, fc1_codes, fc1_scales, fc2_codes, fc2_scales, NULL,
-                               NULL, T, out, nthreads);
+    return oracle_forward_ext(L, x, logits, fc1_codes, fc1_scales, fc2_codes, fc2_scales, NULL,
+                              NULL, NULL, NULL, T, out, nthreads);
 }
 
 /* Final rounding: double accumulator -> fp32 (one rounding) and -> bf16 of that fp32. */

@@ -323,6 +323,46 @@ def test_biases_against_dense_masked():
     assert _close(got - nob, lin)
 
 
+@pytest.mark.parametrize("bits,bs", [(4, 32), (3, 64), (2, 128)])
+def test_dequant_zero_point_tensor(bits, bs):
+    """A zero-point tensor (one code per row and quant block) gives, exactly,
+    (q - zp[n][k/bs]) * s; filled with the scalar zero point it reproduces the
+    scalar-zero-point dequant bit for bit."""
+    rng = np.random.default_rng(bits * 100 + bs)
+    N, K = 24, 4 * bs
+    q = rng.integers(0, 1 << bits, size=(N, K))
+    codes = brute.pack_codes(q, bits)
+    scales = (np.abs(rng.standard_normal((N, K // bs))) * 0.05 + 1e-3).astype(np.float16)
+    zps = rng.integers(0, 1 << bits, size=(N, K // bs)).astype(np.uint8)
+    got = oracle.dequant(codes, scales, bits, bs, 0, K, zero_points=zps)
+    ref = (q - np.repeat(zps.astype(np.int64), bs, axis=1)) * np.repeat(
+        scales.astype(np.float64), bs, axis=1)
+    assert np.array_equal(got, ref)
+    assert np.array_equal(got, brute.dequant_dense(codes, scales, bits, bs, zps, K))
+    zc = 1 << (bits - 1)
+    full = np.full_like(zps, zc)
+    assert np.array_equal(oracle.dequant(codes, scales, bits, bs, 0, K, zero_points=full),
+                          oracle.dequant(codes, scales, bits, bs, zc, K))
+
+
+def test_zero_point_tensors_against_dense_masked():
+    """Per-block zero points in both FC1 and FC2: the oracle equals the dense
+    masked mixture; an off-by-one zero point would be noticed."""
+    wl = qi.make_workload("tiny")
+    rng = np.random.default_rng(31)
+    z1 = rng.integers(0, 16, size=wl.weights.fc1_scales.shape).astype(np.uint8)
+    z2 = rng.integers(0, 16, size=wl.weights.fc2_scales.shape).astype(np.uint8)
+    got = oracle.forward(oracle.Layer.from_spec(wl.spec), wl.tokens.x, wl.tokens.logits,
+                         wl.weights, fc1_zero_points=z1, fc2_zero_points=z2)
+    x64, l64 = oracle.as_f64(wl.tokens.x), oracle.as_f64(wl.tokens.logits)
+    ref = brute.dense_masked_forward(x64, l64, wl.weights, wl.spec, fc1_zero_points=z1,
+                                     fc2_zero_points=z2)
+    assert _close(got, ref)
+    assert not _close(got, brute.dense_masked_forward(x64, l64, wl.weights, wl.spec,
+                                                      fc1_zero_points=z1, fc2_zero_points=z2,
+                                                      zp_delta=1))
+
+
 def test_tiny_layer_against_dense_masked():
     wl = qi.make_workload("tiny")
     acc = _run(wl)
