@@ -103,6 +103,12 @@ typedef struct qmoe_weights {
      * decode for T <= 4, not the fused one. */
     const void *fc1_bias;
     const void *fc2_bias;
+    /* Optional zero-point tensors, or NULL: one unsigned code per row and
+     * quant block (uint8 [E, 2I, H/bs] and [E, H, I/bs], laid out like the
+     * scales) replacing the scalar zero_point, so W = (q - zp[n][k/bs]) * s.
+     * Layers with one run the split decode for T <= 4, not the fused one. */
+    const void *fc1_zero_points;
+    const void *fc2_zero_points;
 } qmoe_weights;
 
 typedef struct qmoe_handle qmoe_handle;

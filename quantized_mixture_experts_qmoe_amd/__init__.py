@@ -49,7 +49,8 @@ QMOE_FLAG_FC1_INTERLEAVED = 1   # qmoe_config.flags bit (include/qmoe.h)
 class Weights(ctypes.Structure):
     _fields_ = [("fc1_codes", ctypes.c_void_p), ("fc1_scales", ctypes.c_void_p),
                 ("fc2_codes", ctypes.c_void_p), ("fc2_scales", ctypes.c_void_p),
-                ("fc1_bias", ctypes.c_void_p), ("fc2_bias", ctypes.c_void_p)]
+                ("fc1_bias", ctypes.c_void_p), ("fc2_bias", ctypes.c_void_p),
+                ("fc1_zero_points", ctypes.c_void_p), ("fc2_zero_points", ctypes.c_void_p)]
 
 
 _lib = None
@@ -120,12 +121,15 @@ class QMoELayer:
     Weight tensors (on the GPU, contiguous, owned by the caller and kept alive
     by this object): fc1_codes uint8 [E, 2I, H*bits/8], fc1_scales fp16
     [E, 2I, H/bs], fc2_codes uint8 [E, H, I*bits/8], fc2_scales fp16 [E, H, I/bs];
-    optional fc1_bias [E, 2I] and fc2_bias [E, H] in the activation dtype.
+    optional fc1_bias [E, 2I] and fc2_bias [E, H] in the activation dtype, and
+    optional uint8 zero-point tensors shaped like the scales.
     """
 
     def __init__(self, cfg: LayerConfig, fc1_codes: torch.Tensor, fc1_scales: torch.Tensor,
                  fc2_codes: torch.Tensor, fc2_scales: torch.Tensor,
-                 fc1_bias: Optional[torch.Tensor] = None, fc2_bias: Optional[torch.Tensor] = None):
+                 fc1_bias: Optional[torch.Tensor] = None, fc2_bias: Optional[torch.Tensor] = None,
+                 fc1_zero_points: Optional[torch.Tensor] = None,
+                 fc2_zero_points: Optional[torch.Tensor] = None):
         for t in (fc1_codes, fc1_scales, fc2_codes, fc2_scales):
             if not t.is_cuda or not t.is_contiguous():
                 raise ValueError("weights must be contiguous GPU tensors")
@@ -135,6 +139,11 @@ class QMoELayer:
                                   or tuple(t.shape) != shape):
                 raise ValueError(f"biases must be contiguous GPU tensors of the activation dtype, "
                                  f"shaped {shape}")
+        for t, sc in ((fc1_zero_points, fc1_scales), (fc2_zero_points, fc2_scales)):
+            if t is not None and (not t.is_cuda or not t.is_contiguous() or t.dtype != torch.uint8
+                                  or t.shape != sc.shape):
+                raise ValueError("zero points must be contiguous uint8 GPU tensors shaped like "
+                                 "the scales")
         if fc1_codes.dtype != torch.uint8 or fc2_codes.dtype != torch.uint8:
             raise ValueError("codes must be uint8")
         if fc1_scales.dtype != torch.float16 or fc2_scales.dtype != torch.float16:
@@ -143,14 +152,17 @@ class QMoELayer:
             raise ValueError("act_dtype must be torch.bfloat16 or torch.float32")
         self.cfg = cfg
         self.device = fc1_codes.device
-        self._keep = (fc1_codes, fc1_scales, fc2_codes, fc2_scales, fc1_bias, fc2_bias)
+        self._keep = (fc1_codes, fc1_scales, fc2_codes, fc2_scales, fc1_bias, fc2_bias,
+                      fc1_zero_points, fc2_zero_points)
         c = Config(ctypes.sizeof(Config), cfg.top_k, cfg.hidden, cfg.inter, cfg.num_experts,
                    cfg.bits, cfg.block_size, cfg.zero_point, _ACT[cfg.act_dtype],
                    1 if cfg.normalize_routing else 0,
                    QMOE_FLAG_FC1_INTERLEAVED if cfg.fc1_interleaved else 0, cfg.max_tokens)
         w = Weights(fc1_codes.data_ptr(), fc1_scales.data_ptr(), fc2_codes.data_ptr(),
                     fc2_scales.data_ptr(), None if fc1_bias is None else fc1_bias.data_ptr(),
-                    None if fc2_bias is None else fc2_bias.data_ptr())
+                    None if fc2_bias is None else fc2_bias.data_ptr(),
+                    None if fc1_zero_points is None else fc1_zero_points.data_ptr(),
+                    None if fc2_zero_points is None else fc2_zero_points.data_ptr())
         h = ctypes.c_void_p()
         _check(lib().qmoe_create(ctypes.byref(c), ctypes.byref(w), self.device.index or 0,
                                  ctypes.byref(h)), "qmoe_create")

@@ -193,6 +193,8 @@ qmoe_status qmoe_create(const qmoe_config* c, const qmoe_weights* w, int device,
   L.fc2_scales = static_cast<const uint16_t*>(w->fc2_scales);
   L.fc1_bias = w->fc1_bias;
   L.fc2_bias = w->fc2_bias;
+  L.fc1_zp = static_cast<const uint8_t*>(w->fc1_zero_points);
+  L.fc2_zp = static_cast<const uint8_t*>(w->fc2_zero_points);
   L.fc1_row_bytes = L.H * L.bits / 8;
   L.fc2_row_bytes = L.I * L.bits / 8;
   L.fc1_nblk = L.H / L.bs;

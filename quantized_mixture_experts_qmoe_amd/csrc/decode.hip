@@ -31,7 +31,7 @@ namespace {
 template <int BITS, int UPL>
 struct XPairs {
   uint32_t p[UPL][16];
-  float corr[UPL];
+  float sum[UPL];   // sum of the unit's 32 x values
 };
 
 template <int UPL>
@@ -82,7 +82,7 @@ __device__ __forceinline__ void token_slots(const RoutingLds& R, int T, int k, i
 template <int BITS, int UPL, bool BF16>
 __global__ __launch_bounds__(256) void decode_fc1_kernel(
     const void* __restrict__ xv, const void* __restrict__ logitsv, int T, int E, int k, bool normalize,
-    bool fc1_il, const void* __restrict__ fc1_bias,
+    bool fc1_il, const void* __restrict__ fc1_bias, const uint8_t* __restrict__ fc1_zp,
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales, int H, int I, int bs,
     int zp, int64_t row_bytes, int64_t nblk, int lpr, int rows_block,
     int32_t* __restrict__ ws_ids, float* __restrict__ ws_w, float* __restrict__ h32,
@@ -118,6 +118,7 @@ __global__ __launch_bounds__(256) void decode_fc1_kernel(
   const int rows_wave = kWave / lpr;
   const uint8_t* ebase = codes + static_cast<int64_t>(e) * (2 * I) * row_bytes;
   const uint16_t* sbase = scales + static_cast<int64_t>(e) * (2 * I) * nblk;
+  const uint8_t* zbase = fc1_zp ? fc1_zp + static_cast<int64_t>(e) * (2 * I) * nblk : nullptr;
 
   // activations of the tokens that use e, for this lane's units
   XPairs<BITS, UPL> xp[kDecodeMaxTokens];
@@ -130,8 +131,8 @@ __global__ __launch_bounds__(256) void decode_fc1_kernel(
       const int u = lane_in_row + lpr * i;
       if (u >= units) continue;
       if constexpr (BF16) {
-        load_x_pairs<BITS>(static_cast<const uint16_t*>(xv) + static_cast<int64_t>(t) * H + 32 * u, zp,
-                           xp[t].p[i], xp[t].corr[i]);
+        load_x_pairs<BITS>(static_cast<const uint16_t*>(xv) + static_cast<int64_t>(t) * H + 32 * u,
+                           xp[t].p[i], xp[t].sum[i]);
       } else {
         const float* xs = static_cast<const float*>(xv) + static_cast<int64_t>(t) * H + 32 * u;
         float s = 0.0f;
@@ -160,6 +161,7 @@ __global__ __launch_bounds__(256) void decode_fc1_kernel(
     if (valid) {
       UnitWords<BITS> gw[UPL], uw[UPL];
       float gs[UPL], us[UPL];
+      int gz[UPL], uz[UPL];   // zero points of the gate and up rows' blocks
 #pragma unroll
       for (int i = 0; i < UPL; ++i) {
         const int u = lane_in_row + lpr * i;
@@ -168,6 +170,8 @@ __global__ __launch_bounds__(256) void decode_fc1_kernel(
         uw[i] = load_unit<BITS>(ebase + ur * row_bytes + u * (4 * BITS));
         gs[i] = half_to_f32(sbase[gr * nblk + (32 * u) / bs]);
         us[i] = half_to_f32(sbase[ur * nblk + (32 * u) / bs]);
+        gz[i] = zbase ? static_cast<int>(zbase[gr * nblk + (32 * u) / bs]) : zp;
+        uz[i] = zbase ? static_cast<int>(zbase[ur * nblk + (32 * u) / bs]) : zp;
       }
 #pragma unroll
       for (int i = 0; i < UPL; ++i) {
@@ -184,16 +188,19 @@ __global__ __launch_bounds__(256) void decode_fc1_kernel(
 #pragma unroll
           for (int t = 0; t < kDecodeMaxTokens; ++t) {
             if (slot[t] < 0) continue;
-            g[t] = fmaf(gsc, unit_dot_pairs<BITS>(gp, xp[t].p[i], xp[t].corr[i]), g[t]);
-            up[t] = fmaf(usc, unit_dot_pairs<BITS>(upp, xp[t].p[i], xp[t].corr[i]), up[t]);
+            const float gc = -(1.0f + static_cast<float>(gz[i]) * (1.0f / 128.0f)) * xp[t].sum[i];
+            const float uc = -(1.0f + static_cast<float>(uz[i]) * (1.0f / 128.0f)) * xp[t].sum[i];
+            g[t] = fmaf(gsc, unit_dot_pairs<BITS>(gp, xp[t].p[i], gc), g[t]);
+            up[t] = fmaf(usc, unit_dot_pairs<BITS>(upp, xp[t].p[i], uc), up[t]);
           }
         } else {
 #pragma unroll
           for (int t = 0; t < kDecodeMaxTokens; ++t) {
             if (slot[t] < 0) continue;
-            const float zs = static_cast<float>(zp) * xf[t].sum[i];
-            g[t] = fmaf(gs[i], unit_dot_f32<BITS>(gw[i], xf[t].v[i]) - zs, g[t]);
-            up[t] = fmaf(us[i], unit_dot_f32<BITS>(uw[i], xf[t].v[i]) - zs, up[t]);
+            const float gzs = static_cast<float>(gz[i]) * xf[t].sum[i];
+            const float uzs = static_cast<float>(uz[i]) * xf[t].sum[i];
+            g[t] = fmaf(gs[i], unit_dot_f32<BITS>(gw[i], xf[t].v[i]) - gzs, g[t]);
+            up[t] = fmaf(us[i], unit_dot_f32<BITS>(uw[i], xf[t].v[i]) - uzs, up[t]);
           }
         }
       }
@@ -216,6 +223,7 @@ __global__ __launch_bounds__(256) void decode_fc2_kernel(
     const float* __restrict__ ws_w, int T, int k, const uint8_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, int H, int I, int bs, int zp, int64_t row_bytes,
     int64_t nblk, int lpr, int rows_block, const void* __restrict__ fc2_bias,
+    const uint8_t* __restrict__ fc2_zp,
     float* __restrict__ y32, int32_t* __restrict__ counters, void* __restrict__ out) {
   __shared__ RoutingLds R;
   __shared__ int s_last;
@@ -247,6 +255,7 @@ __global__ __launch_bounds__(256) void decode_fc2_kernel(
   const int rows_wave = kWave / lpr;
   const uint8_t* ebase = codes + static_cast<int64_t>(e) * H * row_bytes;
   const uint16_t* sbase = scales + static_cast<int64_t>(e) * H * nblk;
+  const uint8_t* zbase = fc2_zp ? fc2_zp + static_cast<int64_t>(e) * H * nblk : nullptr;
 
   XFloats<UPL> hf[kDecodeMaxTokens];
 #pragma unroll
@@ -283,12 +292,14 @@ __global__ __launch_bounds__(256) void decode_fc2_kernel(
     if (valid) {
       UnitWords<BITS> w[UPL];
       float sc[UPL];
+      int zz[UPL];
 #pragma unroll
       for (int i = 0; i < UPL; ++i) {
         const int u = lane_in_row + lpr * i;
         if (u >= units) continue;
         w[i] = load_unit<BITS>(ebase + static_cast<int64_t>(m) * row_bytes + u * (4 * BITS));
         sc[i] = half_to_f32(sbase[static_cast<int64_t>(m) * nblk + (32 * u) / bs]);
+        zz[i] = zbase ? static_cast<int>(zbase[static_cast<int64_t>(m) * nblk + (32 * u) / bs]) : zp;
       }
 #pragma unroll
       for (int i = 0; i < UPL; ++i) {
@@ -297,7 +308,7 @@ __global__ __launch_bounds__(256) void decode_fc2_kernel(
 #pragma unroll
         for (int t = 0; t < kDecodeMaxTokens; ++t) {
           if (slot[t] < 0) continue;
-          const float d = unit_dot_f32<BITS>(w[i], hf[t].v[i]) - static_cast<float>(zp) * hf[t].sum[i];
+          const float d = unit_dot_f32<BITS>(w[i], hf[t].v[i]) - static_cast<float>(zz[i]) * hf[t].sum[i];
           y[t] = fmaf(sc[i], d, y[t]);
         }
       }
@@ -350,13 +361,15 @@ hipError_t launch_decode_t(const Layer& L, const void* x, const void* logits, vo
   dim3 g1((I + s1.rows_block - 1) / s1.rows_block, Ti * k);
   if (L.act_bf16)
     decode_fc1_kernel<BITS, UPL, true><<<g1, 256, 0, s>>>(
-        x, logits, Ti, E, k, L.normalize, L.fc1_interleaved, L.fc1_bias, L.fc1_codes, L.fc1_scales, H,
+        x, logits, Ti, E, k, L.normalize, L.fc1_interleaved, L.fc1_bias, L.fc1_zp, L.fc1_codes,
+        L.fc1_scales, H,
         I, L.bs,
         L.zp, L.fc1_row_bytes,
         L.fc1_nblk, s1.lpr, s1.rows_block, ids, w, h32, counters, W.n_counters);
   else
     decode_fc1_kernel<BITS, UPL, false><<<g1, 256, 0, s>>>(
-        x, logits, Ti, E, k, L.normalize, L.fc1_interleaved, L.fc1_bias, L.fc1_codes, L.fc1_scales, H,
+        x, logits, Ti, E, k, L.normalize, L.fc1_interleaved, L.fc1_bias, L.fc1_zp, L.fc1_codes,
+        L.fc1_scales, H,
         I, L.bs,
         L.zp, L.fc1_row_bytes,
         L.fc1_nblk, s1.lpr, s1.rows_block, ids, w, h32, counters, W.n_counters);
@@ -378,11 +391,11 @@ hipError_t launch_fc2_t(const Layer& L, void* out, int64_t T, char* ws, const Wo
   if (L.act_bf16)
     decode_fc2_kernel<BITS, UPL, true><<<g2, 256, 0, s>>>(
         h32, ids, w, Ti, k, L.fc2_codes, L.fc2_scales, H, I, L.bs, L.zp, L.fc2_row_bytes,
-        L.fc2_nblk, s2.lpr, s2.rows_block, L.fc2_bias, y32, counters, out);
+        L.fc2_nblk, s2.lpr, s2.rows_block, L.fc2_bias, L.fc2_zp, y32, counters, out);
   else
     decode_fc2_kernel<BITS, UPL, false><<<g2, 256, 0, s>>>(
         h32, ids, w, Ti, k, L.fc2_codes, L.fc2_scales, H, I, L.bs, L.zp, L.fc2_row_bytes,
-        L.fc2_nblk, s2.lpr, s2.rows_block, L.fc2_bias, y32, counters, out);
+        L.fc2_nblk, s2.lpr, s2.rows_block, L.fc2_bias, L.fc2_zp, y32, counters, out);
   stage_done(L, 2, "decode_fc2_combine");
   return hipGetLastError();
 }

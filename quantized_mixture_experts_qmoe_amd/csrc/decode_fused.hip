@@ -654,7 +654,8 @@ const void* fused_kernel_for(const Layer& L) {
 }  // namespace
 
 bool fused_decode_supported(const Layer& L) {
-  return L.act_bf16 && !L.fc1_bias && !L.fc2_bias && fused_u1(L) > 0 && fused_u2(L) > 0 &&
+  return L.act_bf16 && !L.fc1_bias && !L.fc2_bias && !L.fc1_zp && !L.fc2_zp && fused_u1(L) > 0 &&
+         fused_u2(L) > 0 &&
          L.H % 8 == 0 && L.I % 2 == 0 &&
          L.E <= kFusedMaxExperts && L.k <= kMaxTopK && fused_kernel_for(L) != nullptr;
 }

@@ -1,6 +1,7 @@
 // Test export: materialize one expert matrix with the kernels' own unpacking.
 //
-//   out_f32[n][k]  = (q - zp) * s as the decode GEMV reads it: the code comes
+//   out_f32[n][k]  = (q - zp) * s as the decode GEMV reads it (zp the scalar
+//                    zero point or the row's per-block code): the code comes
 //                    back out of the bf16 pair 1 + q/128 that unit_pair builds
 //                    (exact), placed at the code index pair_a/pair_b name;
 //   out_bf16[n][k] = the bf16 operand the prefill GEMM stages in LDS
@@ -17,7 +18,8 @@ namespace qmoe {
 // one thread per 32-code unit; grid = ceil(N * K/32 / 256)
 template <int BITS>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ codes,
-                                                      const uint16_t* __restrict__ scales, int64_t N,
+                                                      const uint16_t* __restrict__ scales,
+                                                      const uint8_t* __restrict__ zps, int64_t N,
                                                       int64_t K, int bs, int zp, int64_t row_bytes,
                                                       int64_t nblk, float* __restrict__ out_f32,
                                                       uint16_t* __restrict__ out_bf16) {
@@ -27,6 +29,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
   const int64_t n = gid / units, u = gid % units;
   const UnitWords<BITS> w = load_unit<BITS>(codes + n * row_bytes + u * (4 * BITS));
   const float s = half_to_f32(scales[n * nblk + (32 * u) / bs]);
+  if (zps) zp = zps[n * nblk + (32 * u) / bs];   // per-block zero point
   const int64_t base = n * K + 32 * u;
   if (out_f32) {
 #pragma unroll
@@ -57,12 +60,14 @@ hipError_t launch_dequant(const Layer& L, int fc, int64_t expert, float* out_f32
   const int64_t nb = fc == 1 ? L.fc1_nblk : L.fc2_nblk;
   const uint8_t* c = (fc == 1 ? L.fc1_codes : L.fc2_codes) + expert * N * rb;
   const uint16_t* sc = (fc == 1 ? L.fc1_scales : L.fc2_scales) + expert * N * nb;
+  const uint8_t* zb = fc == 1 ? L.fc1_zp : L.fc2_zp;
+  const uint8_t* z = zb ? zb + expert * N * nb : nullptr;
   const int64_t threads = N * (K / 32);
   const unsigned grid = static_cast<unsigned>((threads + 255) / 256);
   switch (L.bits) {
-    case 4: dequant_kernel<4><<<grid, 256, 0, s>>>(c, sc, N, K, L.bs, L.zp, rb, nb, out_f32, out_bf16); break;
-    case 3: dequant_kernel<3><<<grid, 256, 0, s>>>(c, sc, N, K, L.bs, L.zp, rb, nb, out_f32, out_bf16); break;
-    default: dequant_kernel<2><<<grid, 256, 0, s>>>(c, sc, N, K, L.bs, L.zp, rb, nb, out_f32, out_bf16); break;
+    case 4: dequant_kernel<4><<<grid, 256, 0, s>>>(c, sc, z, N, K, L.bs, L.zp, rb, nb, out_f32, out_bf16); break;
+    case 3: dequant_kernel<3><<<grid, 256, 0, s>>>(c, sc, z, N, K, L.bs, L.zp, rb, nb, out_f32, out_bf16); break;
+    default: dequant_kernel<2><<<grid, 256, 0, s>>>(c, sc, z, N, K, L.bs, L.zp, rb, nb, out_f32, out_bf16); break;
   }
   return hipGetLastError();
 }

@@ -198,15 +198,15 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
 
 // Activation unit (32 bf16 values at x) -> pairs matching unit_pair<BITS>.
 template <int BITS>
-__device__ __forceinline__ void load_x_pairs(const uint16_t* x, int zp, uint32_t (&pairs)[16],
-                                             float& corr) {
+__device__ __forceinline__ void load_x_pairs(const uint16_t* x, uint32_t (&pairs)[16],
+                                             float& sum) {
   uint32_t v[16];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     uint4 c = reinterpret_cast<const uint4*>(x)[q];
     v[4 * q + 0] = c.x; v[4 * q + 1] = c.y; v[4 * q + 2] = c.z; v[4 * q + 3] = c.w;
   }
-  float sum = 0.0f;
+  sum = 0.0f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) sum += bf16_to_f32((v[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
 #pragma unroll
@@ -216,7 +216,6 @@ __device__ __forceinline__ void load_x_pairs(const uint16_t* x, int zp, uint32_t
     const uint32_t xb = (v[b >> 1] >> (16 * (b & 1))) & 0xFFFFu;
     pairs[p] = xa | (xb << 16);
   }
-  corr = -(1.0f + static_cast<float>(zp) * (1.0f / 128.0f)) * sum;
 }
 
 // ---------------------------------------------------------------- reductions

@@ -24,6 +24,8 @@ struct Layer {
   const uint16_t* fc2_scales;
   const void* fc1_bias;   // [E, 2I] in the activation dtype, or null
   const void* fc2_bias;   // [E, H] in the activation dtype, or null
+  const uint8_t* fc1_zp;  // [E, 2I, H/bs] zero-point codes, or null (scalar zp)
+  const uint8_t* fc2_zp;  // [E, H, I/bs] zero-point codes, or null (scalar zp)
   int64_t fc1_row_bytes, fc2_row_bytes;   // H*bits/8, I*bits/8
   int64_t fc1_nblk, fc2_nblk;             // H/bs, I/bs
   qmoe_stage_fn hook;                     // profiling hook (may be null)

@@ -71,12 +71,13 @@ int gemm_n_tiles(const Layer& L, bool fc1) {
 // grid = 8 * ceil(max_tiles * n_tiles_n / 8), block = 512
 // (one workgroup per CU: its LDS use limits each SIMD to two waves, so the
 // compiler may use the whole register file to keep fragments in flight)
-template <int BITS, bool FC1>
+template <int BITS, bool FC1, bool HAS_ZP>
 __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void grouped_gemm_kernel(
     const uint16_t* __restrict__ a_src, const int32_t* __restrict__ sorted_routes, int k,
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales, int K, int H, int I,
-    int bs_shift, int zp, bool fc1_il, const void* __restrict__ bias, bool bias_bf16,
+    int bs_shift, int zp, const uint8_t* __restrict__ zps, bool fc1_il,
+    const void* __restrict__ bias, bool bias_bf16,
     int64_t row_bytes, int64_t nblk, const int4* __restrict__ tiles,
     const int32_t* __restrict__ num_tiles, int n_tiles_n, uint16_t* __restrict__ h_out,
     float* __restrict__ y_out) {
@@ -117,6 +118,9 @@ void grouped_gemm_kernel(
   }
   const uint8_t* b_ptr = ebase + static_cast<int64_t>(w_row) * row_bytes;
   const uint16_t* s_ptr = sbase + static_cast<int64_t>(w_row) * nblk;
+  // per-block zero points of this thread's B row (when the layer has them)
+  const uint8_t* z_ptr =
+      HAS_ZP ? zps + (static_cast<int64_t>(e) * n_rows_total + w_row) * nblk : nullptr;
 
   // this thread's A share: the 16-byte chunk (lane & 7) of rows
   // 128 grp + 32 gw + 8 q + (lane >> 3), q = 0..3, so each load instruction
@@ -136,6 +140,7 @@ void grouped_gemm_kernel(
   uint4 ra0, ra1, ra2, ra3;
   UnitWords<BITS> rb;
   uint32_t rs;
+  int rz = zp;   // this stage's zero point (the scalar one without a tensor)
   auto load_stage = [&](int st) {
     const int k0 = st * kKT;
     const int ka = (k0 + a_chunk < K) ? k0 : 0;
@@ -147,6 +152,7 @@ void grouped_gemm_kernel(
     const int kb = (kk < K) ? kk : 0;
     rb = load_unit<BITS>(b_ptr + (kb / 32) * (4 * BITS));
     rs = s_ptr[kb >> bs_shift] | (kk < K ? 0u : 0x10000u);   // bit 16: past K
+    if constexpr (HAS_ZP) rz = z_ptr[kb >> bs_shift];
   };
   auto store_stage = [&](int buf) {
     uint16_t* ad = &As[buf][a_row0 * kLdsStride + a_chunk];
@@ -160,10 +166,10 @@ void grouped_gemm_kernel(
       float q[16];
       uint32_t p0[8];
       unit_half_codes<BITS>(rb, 0, q);
-      dequant_codes_bf16<8>(q, sc, zp, p0);
+      dequant_codes_bf16<8>(q, sc, rz, p0);
       for (int p = 0; p < 8; ++p) pairs[p] = p0[p];
       unit_half_codes<BITS>(rb, 1, q);
-      dequant_codes_bf16<8>(q, sc, zp, p0);
+      dequant_codes_bf16<8>(q, sc, rz, p0);
       for (int p = 0; p < 8; ++p) pairs[8 + p] = p0[p];
     }
     uint4* bd = reinterpret_cast<uint4*>(&Bs[buf][b_row * kLdsStride + 32 * b_kq]);
@@ -332,14 +338,16 @@ hipError_t launch_gemms(const Layer& L, const uint16_t* xb, char* ws, const Work
   const int nt2 = gemm_n_tiles(L, false);
   const int64_t g1 = 8 * ((W.max_tiles * nt1 + 7) / 8);
   const int64_t g2 = 8 * ((W.max_tiles * nt2 + 7) / 8);
-  grouped_gemm_kernel<BITS, true><<<static_cast<unsigned>(g1), kGemmThreads, 0, s>>>(
-      xb, sorted, L.k, L.fc1_codes, L.fc1_scales, H, H, I, bs_shift, L.zp, L.fc1_interleaved,
+  auto fc1 = L.fc1_zp ? grouped_gemm_kernel<BITS, true, true> : grouped_gemm_kernel<BITS, true, false>;
+  auto fc2 = L.fc2_zp ? grouped_gemm_kernel<BITS, false, true> : grouped_gemm_kernel<BITS, false, false>;
+  fc1<<<static_cast<unsigned>(g1), kGemmThreads, 0, s>>>(
+      xb, sorted, L.k, L.fc1_codes, L.fc1_scales, H, H, I, bs_shift, L.zp, L.fc1_zp, L.fc1_interleaved,
       L.fc1_bias, L.act_bf16,
       L.fc1_row_bytes, L.fc1_nblk,
       tiles, ntiles, nt1, hb, nullptr);
   stage_done(L, 6, "gemm_fc1_swiglu");
-  grouped_gemm_kernel<BITS, false><<<static_cast<unsigned>(g2), kGemmThreads, 0, s>>>(
-      hb, sorted, L.k, L.fc2_codes, L.fc2_scales, I, H, I, bs_shift, L.zp, false, L.fc2_bias,
+  fc2<<<static_cast<unsigned>(g2), kGemmThreads, 0, s>>>(
+      hb, sorted, L.k, L.fc2_codes, L.fc2_scales, I, H, I, bs_shift, L.zp, L.fc2_zp, false, L.fc2_bias,
       L.act_bf16,
       L.fc2_row_bytes, L.fc2_nblk,
       tiles, ntiles, nt2, nullptr, yf);

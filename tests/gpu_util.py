@@ -18,7 +18,8 @@ def say(msg: str):
 
 
 def layer_for(wl: qi.Workload, max_tokens: int = 8192, normalize: bool = True,
-              fc1_interleaved: bool = False, fc1_bias=None, fc2_bias=None) -> q.QMoELayer:
+              fc1_interleaved: bool = False, fc1_bias=None, fc2_bias=None,
+              fc1_zero_points=None, fc2_zero_points=None) -> q.QMoELayer:
     s = wl.spec
     w = wl.weights
     cfg = q.LayerConfig(s.hidden, s.inter, s.num_experts, s.top_k, s.bits, s.block_size,
@@ -28,7 +29,9 @@ def layer_for(wl: qi.Workload, max_tokens: int = 8192, normalize: bool = True,
                        torch.from_numpy(w.fc1_scales).to(DEV), torch.from_numpy(w.fc2_codes).to(DEV),
                        torch.from_numpy(w.fc2_scales).to(DEV),
                        None if fc1_bias is None else fc1_bias.to(DEV),
-                       None if fc2_bias is None else fc2_bias.to(DEV))
+                       None if fc2_bias is None else fc2_bias.to(DEV),
+                       None if fc1_zero_points is None else torch.from_numpy(fc1_zero_points).to(DEV),
+                       None if fc2_zero_points is None else torch.from_numpy(fc2_zero_points).to(DEV))
 
 
 def run(layer: q.QMoELayer, x: torch.Tensor, logits: torch.Tensor):

@@ -64,6 +64,34 @@ def test_dequant_bit_exact_full_shape(name):
         assert np.array_equal(got, oracle.f32_to_bf16_bits(ref.astype(np.float32)))
 
 
+def random_zero_points(wl, seed):
+    rng = np.random.default_rng(seed)
+    hi = 1 << wl.spec.bits
+    return (rng.integers(0, hi, size=wl.weights.fc1_scales.shape).astype(np.uint8),
+            rng.integers(0, hi, size=wl.weights.fc2_scales.shape).astype(np.uint8))
+
+
+@pytest.mark.parametrize("bits,bs", FORMATS)
+def test_dequant_zero_point_tensor_bit_exact(bits, bs):
+    """With per-block zero-point tensors the exported dequantized weights are
+    (q - zp[n][k/bs]) * s exactly, in fp32 and as the RNE bf16 operand."""
+    wl = qi.make_layer(small_spec(bits, bs), T=1, seed=bits * 10 + bs)
+    z1, z2 = random_zero_points(wl, bits + bs)
+    layer = layer_for(wl, 16, fc1_zero_points=z1, fc2_zero_points=z2)
+    s = wl.spec
+    for fc, e in ((1, 0), (2, 7), (1, 5)):
+        f32, b16 = layer.dequant(fc, e)
+        torch.cuda.synchronize()
+        K = s.hidden if fc == 1 else s.inter
+        codes = wl.weights.fc1_codes[e] if fc == 1 else wl.weights.fc2_codes[e]
+        scales = wl.weights.fc1_scales[e] if fc == 1 else wl.weights.fc2_scales[e]
+        z = z1[e] if fc == 1 else z2[e]
+        ref = oracle.dequant(codes, scales, bits, bs, s.zero_point, K, zero_points=z)
+        assert np.array_equal(f32.cpu().numpy().astype(np.float64), ref)
+        got = b16.view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, oracle.f32_to_bf16_bits(ref.astype(np.float32)))
+
+
 # ------------------------------------------------------------------ routing
 
 def check_routing(wl, layer):
@@ -455,6 +483,40 @@ def test_biases_parity(name, T, il):
     assert rep.ok, rep
     nob, _ = run(layer_for(wl, max(T, 8), fc1_interleaved=il), wl.tokens.x, wl.tokens.logits)
     assert not torch.equal(out, nob)
+
+
+@pytest.mark.parametrize("name,T", [("decode", 4), ("decode", 300), ("int3", 67), ("stack", 129),
+                                    ("tiny", 4), ("f32", 45)])
+def test_zero_point_tensors_parity(name, T):
+    """Per-block zero-point tensors in FC1 and FC2, on the split decode (which
+    such layers take for T <= 4) and the prefill path, every format and both
+    activation dtypes: the output matches the oracle given the same tensors."""
+    if name == "f32":
+        wl = qi.make_layer(small_spec(4, 32, act="f32", hidden=192, inter=96), T=T, seed=5)
+    else:
+        wl = qi.make_workload(name, T=T)
+    z1, z2 = random_zero_points(wl, T)
+    out, _ = run(layer_for(wl, max(T, 8), fc1_zero_points=z1, fc2_zero_points=z2),
+                 wl.tokens.x, wl.tokens.logits)
+    ref = oracle.forward(oracle.Layer.from_spec(wl.spec), wl.tokens.x, wl.tokens.logits,
+                         wl.weights, fc1_zero_points=z1, fc2_zero_points=z2)
+    rep = compare(out, ref)
+    say(f"zero-point tensors {name} T={T}: {rep}")
+    assert rep.ok, rep
+
+
+@pytest.mark.parametrize("T", [3, 200])
+def test_zero_point_tensor_of_the_scalar_is_bitwise_same(T):
+    """A zero-point tensor filled with the layer's scalar zero point gives the
+    output of the scalar zero point bit for bit (split decode and prefill)."""
+    wl = qi.make_workload("decode", T=T)
+    z1 = np.full(wl.weights.fc1_scales.shape, wl.spec.zero_point, np.uint8)
+    z2 = np.full(wl.weights.fc2_scales.shape, wl.spec.zero_point, np.uint8)
+    with _env(**({"QMOE_FORCE_PATH": "decode_split"} if T <= 4 else {})):
+        a, _ = run(layer_for(wl, max(T, 8)), wl.tokens.x, wl.tokens.logits)
+    b, _ = run(layer_for(wl, max(T, 8), fc1_zero_points=z1, fc2_zero_points=z2), wl.tokens.x,
+               wl.tokens.logits)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
 # ------------------------------------------------------------------ properties
