@@ -61,7 +61,8 @@ typedef enum qmoe_status {
 
 typedef enum qmoe_dtype {
     QMOE_F32 = 0,               /* x, logits and out are float32 */
-    QMOE_BF16 = 1               /* x, logits and out are bfloat16 */
+    QMOE_BF16 = 1,              /* x, logits and out are bfloat16 */
+    QMOE_F16 = 2                /* x, logits and out are float16 */
 } qmoe_dtype;
 
 /* qmoe_config.flags: FC1 rows stored interleaved, row 2n = gate n and row

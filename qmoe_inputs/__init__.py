@@ -35,7 +35,7 @@ class LayerSpec:
     block_size: int
     zero_point: int
     scale_c: float          # scales = fp16(|N(0,1)| * scale_c + 1e-3)
-    act_dtype: str          # "f32" or "bf16"
+    act_dtype: str          # "f32", "bf16" or "f16"
 
     @property
     def fc1_rows(self) -> int:
@@ -60,7 +60,7 @@ class Tokens:
     seq_lens: List[int] = field(default_factory=list)
 
 
-TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
+TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 # The five workloads. Names say what they are.
 TINY = LayerSpec(hidden=64, inter=32, num_experts=4, top_k=2, bits=4,

@@ -17,7 +17,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqmoe.so")
 
-QMOE_F32, QMOE_BF16 = 0, 1
+QMOE_F32, QMOE_BF16, QMOE_F16 = 0, 1, 2
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration",
           3: "workspace missing or too small", 4: "HIP runtime error", 5: "out of host memory"}
 
@@ -97,7 +97,7 @@ def _stream(stream: Optional[torch.cuda.Stream] = None) -> ctypes.c_void_p:
     return ctypes.c_void_p(s.cuda_stream)
 
 
-_ACT = {torch.bfloat16: QMOE_BF16, torch.float32: QMOE_F32}
+_ACT = {torch.bfloat16: QMOE_BF16, torch.float32: QMOE_F32, torch.float16: QMOE_F16}
 
 
 @dataclass
@@ -149,7 +149,7 @@ class QMoELayer:
         if fc1_scales.dtype != torch.float16 or fc2_scales.dtype != torch.float16:
             raise ValueError("scales must be float16")
         if cfg.act_dtype not in _ACT:
-            raise ValueError("act_dtype must be torch.bfloat16 or torch.float32")
+            raise ValueError("act_dtype must be torch.bfloat16, torch.float16 or torch.float32")
         self.cfg = cfg
         self.device = fc1_codes.device
         self._keep = (fc1_codes, fc1_scales, fc2_codes, fc2_scales, fc1_bias, fc2_bias,

@@ -156,7 +156,8 @@ qmoe_status qmoe_create(const qmoe_config* c, const qmoe_weights* w, int device,
   if (c->block_size != 32 && c->block_size != 64 && c->block_size != 128) return QMOE_ERR_INVALID_ARG;
   if (c->hidden % c->block_size != 0 || c->inter % c->block_size != 0) return QMOE_ERR_INVALID_ARG;
   if (c->zero_point < -1 || c->zero_point >= (1 << c->bits)) return QMOE_ERR_INVALID_ARG;
-  if (c->act_dtype != QMOE_F32 && c->act_dtype != QMOE_BF16) return QMOE_ERR_INVALID_ARG;
+  if (c->act_dtype != QMOE_F32 && c->act_dtype != QMOE_BF16 && c->act_dtype != QMOE_F16)
+    return QMOE_ERR_INVALID_ARG;
   if ((c->flags & ~QMOE_FLAG_FC1_INTERLEAVED) != 0 || c->max_tokens < 0) return QMOE_ERR_INVALID_ARG;
   if (c->normalize_routing != 0 && c->normalize_routing != 1) return QMOE_ERR_INVALID_ARG;
   if (!w->fc1_codes || !w->fc1_scales || !w->fc2_codes || !w->fc2_scales) return QMOE_ERR_INVALID_ARG;
@@ -183,7 +184,8 @@ qmoe_status qmoe_create(const qmoe_config* c, const qmoe_weights* w, int device,
   L.bits = c->bits;
   L.bs = c->block_size;
   L.zp = c->zero_point < 0 ? (1 << (c->bits - 1)) : c->zero_point;
-  L.act_bf16 = c->act_dtype == QMOE_BF16;
+  L.act = c->act_dtype == QMOE_BF16 ? kActBF16 : c->act_dtype == QMOE_F16 ? kActF16 : kActF32;
+  L.act_bf16 = L.act == kActBF16;
   L.normalize = c->normalize_routing == 1;
   L.fc1_interleaved = (c->flags & QMOE_FLAG_FC1_INTERLEAVED) != 0;
   L.max_tokens = c->max_tokens;

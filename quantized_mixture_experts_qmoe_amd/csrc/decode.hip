@@ -79,7 +79,7 @@ __device__ __forceinline__ void token_slots(const RoutingLds& R, int T, int k, i
 }  // namespace
 
 // grid = (ceil(I / rows_block), T * k), block = 256 (4 waves)
-template <int BITS, int UPL, bool BF16>
+template <int BITS, int UPL, int ACT>
 __global__ __launch_bounds__(256) void decode_fc1_kernel(
     const void* __restrict__ xv, const void* __restrict__ logitsv, int T, int E, int k, bool normalize,
     bool fc1_il, const void* __restrict__ fc1_bias, const uint8_t* __restrict__ fc1_zp,
@@ -90,8 +90,11 @@ __global__ __launch_bounds__(256) void decode_fc1_kernel(
   __shared__ RoutingLds R;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
   if (wave < T) {
-    if constexpr (BF16)
+    if constexpr (ACT == kActBF16)
       topk_softmax_wave(static_cast<const uint16_t*>(logitsv) + static_cast<int64_t>(wave) * E, E, k,
+                        normalize, lane, R.ids + wave * k, R.w + wave * k);
+    else if constexpr (ACT == kActF16)
+      topk_softmax_wave(static_cast<const _Float16*>(logitsv) + static_cast<int64_t>(wave) * E, E, k,
                         normalize, lane, R.ids + wave * k, R.w + wave * k);
     else
       topk_softmax_wave(static_cast<const float*>(logitsv) + static_cast<int64_t>(wave) * E, E, k,
@@ -130,16 +133,17 @@ __global__ __launch_bounds__(256) void decode_fc1_kernel(
     for (int i = 0; i < UPL; ++i) {
       const int u = lane_in_row + lpr * i;
       if (u >= units) continue;
-      if constexpr (BF16) {
+      if constexpr (ACT == kActBF16) {
         load_x_pairs<BITS>(static_cast<const uint16_t*>(xv) + static_cast<int64_t>(t) * H + 32 * u,
                            xp[t].p[i], xp[t].sum[i]);
       } else {
-        const float* xs = static_cast<const float*>(xv) + static_cast<int64_t>(t) * H + 32 * u;
+        // fp32 or fp16 activations, widened to fp32 (exact)
+        const int64_t x0 = static_cast<int64_t>(t) * H + 32 * u;
         float s = 0.0f;
 #pragma unroll
         for (int c = 0; c < 32; ++c) {
-          xf[t].v[i][c] = xs[c];
-          s += xs[c];
+          xf[t].v[i][c] = load_act(xv, ACT, x0 + c);
+          s += xf[t].v[i][c];
         }
         xf[t].sum[i] = s;
       }
@@ -177,7 +181,7 @@ __global__ __launch_bounds__(256) void decode_fc1_kernel(
       for (int i = 0; i < UPL; ++i) {
         const int u = lane_in_row + lpr * i;
         if (u >= units) continue;
-        if constexpr (BF16) {
+        if constexpr (ACT == kActBF16) {
           uint32_t gp[16], upp[16];
 #pragma unroll
           for (int p = 0; p < 16; ++p) {
@@ -208,8 +212,8 @@ __global__ __launch_bounds__(256) void decode_fc1_kernel(
 #pragma unroll
     for (int t = 0; t < kDecodeMaxTokens; ++t) {
       if (slot[t] < 0) continue;
-      const float gt = group_sum(g[t], lpr) + (valid ? bias_at(fc1_bias, BF16, e * 2LL * I + gr) : 0.0f);
-      const float ut = group_sum(up[t], lpr) + (valid ? bias_at(fc1_bias, BF16, e * 2LL * I + ur) : 0.0f);
+      const float gt = group_sum(g[t], lpr) + (valid ? bias_at(fc1_bias, ACT, e * 2LL * I + gr) : 0.0f);
+      const float ut = group_sum(up[t], lpr) + (valid ? bias_at(fc1_bias, ACT, e * 2LL * I + ur) : 0.0f);
       if (valid && lane_in_row == 0)
         h32[static_cast<int64_t>(t * k + slot[t]) * I + n] = silu_mul(gt, ut);
     }
@@ -217,7 +221,7 @@ __global__ __launch_bounds__(256) void decode_fc1_kernel(
 }
 
 // grid = (n_counters = ceil(H / rows_block), T * k), block = 256
-template <int BITS, int UPL, bool OUT_BF16>
+template <int BITS, int UPL, int ACT>
 __global__ __launch_bounds__(256) void decode_fc2_kernel(
     const float* __restrict__ h32, const int32_t* __restrict__ ws_ids,
     const float* __restrict__ ws_w, int T, int k, const uint8_t* __restrict__ codes,
@@ -316,7 +320,7 @@ __global__ __launch_bounds__(256) void decode_fc2_kernel(
 #pragma unroll
     for (int t = 0; t < kDecodeMaxTokens; ++t) {
       if (slot[t] < 0) continue;
-      const float yt = group_sum(y[t], lpr) + (valid ? bias_at(fc2_bias, OUT_BF16, e * static_cast<int64_t>(H) + m) : 0.0f);
+      const float yt = group_sum(y[t], lpr) + (valid ? bias_at(fc2_bias, ACT, e * static_cast<int64_t>(H) + m) : 0.0f);
       if (valid && lane_in_row == 0) y32[static_cast<int64_t>(t * k + slot[t]) * H + m] = yt;
     }
   }
@@ -338,10 +342,7 @@ __global__ __launch_bounds__(256) void decode_fc2_kernel(
     float acc = 0.0f;
     for (int j = 0; j < k; ++j)
       acc = fmaf(R.w[t * k + j], __builtin_nontemporal_load(y32 + static_cast<int64_t>(t * k + j) * H + mm), acc);
-    if constexpr (OUT_BF16)
-      static_cast<uint16_t*>(out)[static_cast<int64_t>(t) * H + mm] = static_cast<uint16_t>(f32_to_bf16(acc));
-    else
-      static_cast<float*>(out)[static_cast<int64_t>(t) * H + mm] = acc;
+    store_act(out, ACT, static_cast<int64_t>(t) * H + mm, acc);
   }
 }
 
@@ -359,20 +360,12 @@ hipError_t launch_decode_t(const Layer& L, const void* x, const void* logits, vo
   float* h32 = reinterpret_cast<float*>(ws + W.h32);
   float* y32 = reinterpret_cast<float*>(ws + W.y32);
   dim3 g1((I + s1.rows_block - 1) / s1.rows_block, Ti * k);
-  if (L.act_bf16)
-    decode_fc1_kernel<BITS, UPL, true><<<g1, 256, 0, s>>>(
-        x, logits, Ti, E, k, L.normalize, L.fc1_interleaved, L.fc1_bias, L.fc1_zp, L.fc1_codes,
-        L.fc1_scales, H,
-        I, L.bs,
-        L.zp, L.fc1_row_bytes,
-        L.fc1_nblk, s1.lpr, s1.rows_block, ids, w, h32, counters, W.n_counters);
-  else
-    decode_fc1_kernel<BITS, UPL, false><<<g1, 256, 0, s>>>(
-        x, logits, Ti, E, k, L.normalize, L.fc1_interleaved, L.fc1_bias, L.fc1_zp, L.fc1_codes,
-        L.fc1_scales, H,
-        I, L.bs,
-        L.zp, L.fc1_row_bytes,
-        L.fc1_nblk, s1.lpr, s1.rows_block, ids, w, h32, counters, W.n_counters);
+  auto fc1 = L.act == kActBF16 ? decode_fc1_kernel<BITS, UPL, kActBF16>
+             : L.act == kActF16 ? decode_fc1_kernel<BITS, UPL, kActF16>
+                                : decode_fc1_kernel<BITS, UPL, kActF32>;
+  fc1<<<g1, 256, 0, s>>>(x, logits, Ti, E, k, L.normalize, L.fc1_interleaved, L.fc1_bias, L.fc1_zp,
+                         L.fc1_codes, L.fc1_scales, H, I, L.bs, L.zp, L.fc1_row_bytes, L.fc1_nblk,
+                         s1.lpr, s1.rows_block, ids, w, h32, counters, W.n_counters);
   stage_done(L, 1, "decode_fc1_swiglu");
   return hipGetLastError();
 }
@@ -388,14 +381,12 @@ hipError_t launch_fc2_t(const Layer& L, void* out, int64_t T, char* ws, const Wo
   const float* h32 = reinterpret_cast<const float*>(ws + W.h32);
   float* y32 = reinterpret_cast<float*>(ws + W.y32);
   dim3 g2(W.n_counters, Ti * k);
-  if (L.act_bf16)
-    decode_fc2_kernel<BITS, UPL, true><<<g2, 256, 0, s>>>(
-        h32, ids, w, Ti, k, L.fc2_codes, L.fc2_scales, H, I, L.bs, L.zp, L.fc2_row_bytes,
-        L.fc2_nblk, s2.lpr, s2.rows_block, L.fc2_bias, L.fc2_zp, y32, counters, out);
-  else
-    decode_fc2_kernel<BITS, UPL, false><<<g2, 256, 0, s>>>(
-        h32, ids, w, Ti, k, L.fc2_codes, L.fc2_scales, H, I, L.bs, L.zp, L.fc2_row_bytes,
-        L.fc2_nblk, s2.lpr, s2.rows_block, L.fc2_bias, L.fc2_zp, y32, counters, out);
+  auto fc2 = L.act == kActBF16 ? decode_fc2_kernel<BITS, UPL, kActBF16>
+             : L.act == kActF16 ? decode_fc2_kernel<BITS, UPL, kActF16>
+                                : decode_fc2_kernel<BITS, UPL, kActF32>;
+  fc2<<<g2, 256, 0, s>>>(h32, ids, w, Ti, k, L.fc2_codes, L.fc2_scales, H, I, L.bs, L.zp,
+                         L.fc2_row_bytes, L.fc2_nblk, s2.lpr, s2.rows_block, L.fc2_bias, L.fc2_zp,
+                         y32, counters, out);
   stage_done(L, 2, "decode_fc2_combine");
   return hipGetLastError();
 }

@@ -38,6 +38,28 @@ __device__ __forceinline__ float half_to_f32(uint16_t h) {
 
 __device__ __forceinline__ float act_to_f32(float v) { return v; }
 __device__ __forceinline__ float act_to_f32(uint16_t b) { return bf16_to_f32(b); }
+__device__ __forceinline__ float act_to_f32(_Float16 h) { return static_cast<float>(h); }
+
+// Activation dtypes of x, logits, out and the biases.
+constexpr int kActF32 = 0, kActBF16 = 1, kActF16 = 2;
+
+// Store v into element i of an activation-dtype array, rounding once (round
+// to nearest even; NaN stays NaN).
+__device__ __forceinline__ void store_act(void* p, int act, int64_t i, float v) {
+  if (act == kActBF16)
+    static_cast<uint16_t*>(p)[i] = static_cast<uint16_t>(f32_to_bf16(v));
+  else if (act == kActF16)
+    static_cast<_Float16*>(p)[i] = static_cast<_Float16>(v);
+  else
+    static_cast<float*>(p)[i] = v;
+}
+
+// Element i of an activation-dtype array as fp32 (exact).
+__device__ __forceinline__ float load_act(const void* p, int act, int64_t i) {
+  if (act == kActBF16) return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
+  if (act == kActF16) return static_cast<float>(static_cast<const _Float16*>(p)[i]);
+  return static_cast<const float*>(p)[i];
+}
 
 // ---------------------------------------------------------------- packed codes
 //
@@ -380,9 +402,8 @@ __device__ __forceinline__ void topk_softmax_bf16_wave(const uint16_t (&lg)[SLOT
 }
 
 // Element i of an optional bias in the activation dtype (0 when absent).
-__device__ __forceinline__ float bias_at(const void* b, bool bf16, int64_t i) {
-  if (!b) return 0.0f;
-  return bf16 ? bf16_to_f32(static_cast<const uint16_t*>(b)[i]) : static_cast<const float*>(b)[i];
+__device__ __forceinline__ float bias_at(const void* b, int act, int64_t i) {
+  return b ? load_act(b, act, i) : 0.0f;
 }
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }

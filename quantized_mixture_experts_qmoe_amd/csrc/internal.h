@@ -14,7 +14,8 @@ namespace qmoe {
 struct Layer {
   int64_t H, I, E;
   int k, bits, bs, zp;
-  bool act_bf16;
+  int act;        // kActF32, kActBF16 or kActF16 (x, logits, out and biases)
+  bool act_bf16;  // act == kActBF16
   bool normalize;   // routing weights: softmax over the selected k (else over all experts)
   bool fc1_interleaved;   // FC1 row 2n = gate n, row 2n+1 = up n (else gate rows, then up rows)
   int64_t max_tokens;

@@ -77,7 +77,7 @@ void grouped_gemm_kernel(
     const uint16_t* __restrict__ a_src, const int32_t* __restrict__ sorted_routes, int k,
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales, int K, int H, int I,
     int bs_shift, int zp, const uint8_t* __restrict__ zps, bool fc1_il,
-    const void* __restrict__ bias, bool bias_bf16,
+    const void* __restrict__ bias, int act,
     int64_t row_bytes, int64_t nblk, const int4* __restrict__ tiles,
     const int32_t* __restrict__ num_tiles, int n_tiles_n, uint16_t* __restrict__ h_out,
     float* __restrict__ y_out) {
@@ -251,10 +251,10 @@ void grouped_gemm_kernel(
     if (FC1) {
       const int c = n0 + wn * 64 + (tn & 3) * 16 + l16, up = tn >> 2;
       const int64_t r = fc1_il ? 2 * c + up : (up ? I + c : c);
-      bcol[tn] = c < I ? bias_at(bias, bias_bf16, static_cast<int64_t>(e) * 2 * I + r) : 0.0f;
+      bcol[tn] = c < I ? bias_at(bias, act, static_cast<int64_t>(e) * 2 * I + r) : 0.0f;
     } else {
       const int c = n0 + wn * 128 + tn * 16 + l16;
-      bcol[tn] = c < H ? bias_at(bias, bias_bf16, static_cast<int64_t>(e) * H + c) : 0.0f;
+      bcol[tn] = c < H ? bias_at(bias, act, static_cast<int64_t>(e) * H + c) : 0.0f;
     }
   }
 #pragma unroll
@@ -286,7 +286,7 @@ void grouped_gemm_kernel(
 
 // out[t][m] = round(sum_j w[t][j] * y[inv_pos[t*k + j]][m]), slot order j = 0..k-1.
 // grid = (ceil(H / 1024), T), block = 256, 4 columns per thread.
-template <bool OUT_BF16>
+template <int ACT>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
                                                       const int32_t* __restrict__ inv_pos,
                                                       const float* __restrict__ topk_w, int k,
@@ -304,22 +304,28 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     acc.z = fmaf(w, v.z, acc.z);
     acc.w = fmaf(w, v.w, acc.w);
   }
-  if constexpr (OUT_BF16) {
+  if constexpr (ACT == kActBF16) {
     uint2 o;
     o.x = f32_to_bf16(acc.x) | (f32_to_bf16(acc.y) << 16);
     o.y = f32_to_bf16(acc.z) | (f32_to_bf16(acc.w) << 16);
     *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + t * H + m) = o;
+  } else if constexpr (ACT == kActF16) {
+    const int64_t o = t * H + m;
+    store_act(out, kActF16, o, acc.x);
+    store_act(out, kActF16, o + 1, acc.y);
+    store_act(out, kActF16, o + 2, acc.z);
+    store_act(out, kActF16, o + 3, acc.w);
   } else {
     *reinterpret_cast<float4*>(static_cast<float*>(out) + t * H + m) = acc;
   }
 }
 
-// fp32 activations are staged for the matrix cores as bf16 (round to nearest
-// even) once per call.
-__global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float* __restrict__ in, int64_t n,
-                                                          uint16_t* __restrict__ out) {
+// fp32 and fp16 activations are staged for the matrix cores as bf16 (round
+// to nearest even) once per call.
+__global__ __launch_bounds__(256) void act_to_bf16_kernel(const void* __restrict__ in, int act,
+                                                          int64_t n, uint16_t* __restrict__ out) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i < n) out[i] = static_cast<uint16_t>(f32_to_bf16(in[i]));
+  if (i < n) out[i] = static_cast<uint16_t>(f32_to_bf16(load_act(in, act, i)));
 }
 
 namespace {
@@ -342,13 +348,13 @@ hipError_t launch_gemms(const Layer& L, const uint16_t* xb, char* ws, const Work
   auto fc2 = L.fc2_zp ? grouped_gemm_kernel<BITS, false, true> : grouped_gemm_kernel<BITS, false, false>;
   fc1<<<static_cast<unsigned>(g1), kGemmThreads, 0, s>>>(
       xb, sorted, L.k, L.fc1_codes, L.fc1_scales, H, H, I, bs_shift, L.zp, L.fc1_zp, L.fc1_interleaved,
-      L.fc1_bias, L.act_bf16,
+      L.fc1_bias, L.act,
       L.fc1_row_bytes, L.fc1_nblk,
       tiles, ntiles, nt1, hb, nullptr);
   stage_done(L, 6, "gemm_fc1_swiglu");
   fc2<<<static_cast<unsigned>(g2), kGemmThreads, 0, s>>>(
       hb, sorted, L.k, L.fc2_codes, L.fc2_scales, I, H, I, bs_shift, L.zp, L.fc2_zp, false, L.fc2_bias,
-      L.act_bf16,
+      L.act,
       L.fc2_row_bytes, L.fc2_nblk,
       tiles, ntiles, nt2, nullptr, yf);
   stage_done(L, 7, "gemm_fc2");
@@ -363,8 +369,7 @@ hipError_t launch_prefill(const Layer& L, const void* x, void* out, int64_t T, c
   if (!L.act_bf16) {
     uint16_t* staged = reinterpret_cast<uint16_t*>(ws + W.xbf16);
     const int64_t n = T * L.H;
-    f32_to_bf16_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(
-        static_cast<const float*>(x), n, staged);
+    act_to_bf16_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(x, L.act, n, staged);
     stage_done(L, 5, "stage_x_bf16");
     xb = staged;
   }
@@ -380,10 +385,12 @@ hipError_t launch_prefill(const Layer& L, const void* x, void* out, int64_t T, c
   const float* yf = reinterpret_cast<const float*>(ws + W.yf32);
   const int32_t* inv = reinterpret_cast<const int32_t*>(ws + W.inv_pos);
   const float* w = reinterpret_cast<const float*>(ws + W.topk_w);
-  if (L.act_bf16)
-    combine_kernel<true><<<gc, 256, 0, s>>>(yf, inv, w, L.k, H, out);
+  if (L.act == kActBF16)
+    combine_kernel<kActBF16><<<gc, 256, 0, s>>>(yf, inv, w, L.k, H, out);
+  else if (L.act == kActF16)
+    combine_kernel<kActF16><<<gc, 256, 0, s>>>(yf, inv, w, L.k, H, out);
   else
-    combine_kernel<false><<<gc, 256, 0, s>>>(yf, inv, w, L.k, H, out);
+    combine_kernel<kActF32><<<gc, 256, 0, s>>>(yf, inv, w, L.k, H, out);
   stage_done(L, 8, "combine");
   return hipGetLastError();
 }

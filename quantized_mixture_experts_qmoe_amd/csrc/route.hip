@@ -57,9 +57,11 @@ __global__ __launch_bounds__(512) void route_topk_hist_bf16_kernel(
   for (int e = threadIdx.x; e < E; e += 512) hist[static_cast<int64_t>(blockIdx.x) * E + e] = s_hist[e];
 }
 
-// The same for fp32 logits (64-bit keys: fp32 value, then the inverted index).
-__global__ __launch_bounds__(512) void route_topk_hist_f32_kernel(
-    const float* __restrict__ logits, int64_t T, int E, int k, bool normalize,
+// The same for fp32 or fp16 logits (64-bit keys: the value widened to fp32,
+// then the inverted index).
+template <typename ACT>
+__global__ __launch_bounds__(512) void route_topk_hist_wide_kernel(
+    const ACT* __restrict__ logits, int64_t T, int E, int k, bool normalize,
     int32_t* __restrict__ topk_id, float* __restrict__ topk_w, int32_t* __restrict__ hist) {
   __shared__ int32_t s_hist[kMaxExperts];
   for (int e = threadIdx.x; e < E; e += 512) s_hist[e] = 0;
@@ -227,9 +229,12 @@ hipError_t launch_route(const Layer& L, const void* logits, int64_t T, char* ws,
       route_topk_hist_bf16_kernel<8><<<nc, 512, 0, s>>>(lg, T, E, k, L.normalize, topk_id, topk_w, hist);
     else
       route_topk_hist_bf16_kernel<16><<<nc, 512, 0, s>>>(lg, T, E, k, L.normalize, topk_id, topk_w, hist);
+  } else if (L.act == kActF16) {
+    route_topk_hist_wide_kernel<_Float16><<<nc, 512, 0, s>>>(static_cast<const _Float16*>(logits), T,
+                                                              E, k, L.normalize, topk_id, topk_w, hist);
   } else {
-    route_topk_hist_f32_kernel<<<nc, 512, 0, s>>>(static_cast<const float*>(logits), T, E, k,
-                                                   L.normalize, topk_id, topk_w, hist);
+    route_topk_hist_wide_kernel<float><<<nc, 512, 0, s>>>(static_cast<const float*>(logits), T, E, k,
+                                                           L.normalize, topk_id, topk_w, hist);
   }
   stage_done(L, 1, "route_topk_hist");
   route_scan_kernel<<<1, 1024, 0, s>>>(hist, W.nchunks, E, kTileM,

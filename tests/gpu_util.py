@@ -23,7 +23,7 @@ def layer_for(wl: qi.Workload, max_tokens: int = 8192, normalize: bool = True,
     s = wl.spec
     w = wl.weights
     cfg = q.LayerConfig(s.hidden, s.inter, s.num_experts, s.top_k, s.bits, s.block_size,
-                        s.zero_point, torch.float32 if s.act_dtype == "f32" else torch.bfloat16,
+                        s.zero_point, qi.TORCH_DTYPE[s.act_dtype],
                         max_tokens, normalize, fc1_interleaved)
     return q.QMoELayer(cfg, torch.from_numpy(w.fc1_codes).to(DEV),
                        torch.from_numpy(w.fc1_scales).to(DEV), torch.from_numpy(w.fc2_codes).to(DEV),

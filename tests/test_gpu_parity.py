@@ -519,6 +519,33 @@ def test_zero_point_tensor_of_the_scalar_is_bitwise_same(T):
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+@pytest.mark.parametrize("T,extras", [(1, False), (4, False), (4, True), (37, False), (300, True)])
+def test_fp16_activations_parity(T, extras):
+    """fp16 x, logits and out on the Qwen3-shaped INT4 layer: T <= 4 runs the
+    split decode (x widened to fp32), larger T the prefill path (x staged as
+    bf16 once per call). The routing of the fp16 logits is bit-exact and the
+    output (rounded once to fp16) matches the oracle; with extras, fp16
+    biases and unnormalized routing too."""
+    spec = qi.spec_with(qi.QWEN3_INT4, act_dtype="f16")
+    wl = qi.make_layer(spec, T=T, seed=41 + T, nseq=max(1, T // 40))
+    b1 = b2 = None
+    if extras:
+        rng = np.random.default_rng(T)
+        b1 = torch.from_numpy(rng.standard_normal((spec.num_experts, 2 * spec.inter)) * 0.25).half()
+        b2 = torch.from_numpy(rng.standard_normal((spec.num_experts, spec.hidden)) * 0.1).half()
+    layer = layer_for(wl, max(T, 8), normalize=not extras, fc1_bias=b1, fc2_bias=b2)
+    out, ws = run(layer, wl.tokens.x, wl.tokens.logits)
+    assert out.dtype == torch.float16
+    ids, _ = layer.routing_from_workspace(T, ws)
+    rid, _ = oracle.route(wl.tokens.logits, spec.top_k, normalize=not extras)
+    assert np.array_equal(ids.cpu().numpy(), rid)
+    ref = oracle.forward(oracle.Layer.from_spec(spec, normalize=not extras), wl.tokens.x,
+                         wl.tokens.logits, wl.weights, fc1_bias=b1, fc2_bias=b2)
+    rep = compare(out, ref)
+    say(f"fp16 activations T={T} extras={extras}: {rep}")
+    assert rep.ok, rep
+
+
 # ------------------------------------------------------------------ properties
 
 def test_decode_and_prefill_agree():

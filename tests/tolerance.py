@@ -54,11 +54,12 @@ class Report:
 
 
 def compare(gpu_out: torch.Tensor, ref_acc: np.ndarray) -> Report:
-    """gpu_out: [T, H] bf16 or fp32 tensor; ref_acc: the oracle's float64 accumulator."""
+    """gpu_out: [T, H] bf16, fp16 or fp32 tensor; ref_acc: the oracle's float64
+    accumulator. Bound G1 is counted in bf16 ulps of the output widened to fp32."""
     ref32, ref_bits = oracle.round_output(ref_acc)
     g = gpu_out.detach().cpu()
-    if g.dtype == torch.float32:
-        gpu32 = g.numpy()
+    if g.dtype in (torch.float32, torch.float16):
+        gpu32 = g.to(torch.float32).numpy()
         gbits = oracle.f32_to_bf16_bits(gpu32)
     else:
         gbits = bf16_bits(g)
