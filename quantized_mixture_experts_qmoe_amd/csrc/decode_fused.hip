@@ -272,8 +272,11 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
   // FC1: items (expert d, row pair p), contiguous per wave over the grid
   const int g1 = I / 2;
   const int n1 = D * g1;
-  const int i1_0 = static_cast<int>(static_cast<int64_t>(n1) * gw / NW);
-  const int i1_1 = static_cast<int>(static_cast<int64_t>(n1) * (gw + 1) / NW);
+  // (unsigned 32-bit range arithmetic: n1 <= 128 * 512 and gw < 8192, so
+  // every product fits, and the divisions stay short scalar sequences)
+  const uint32_t un1 = static_cast<uint32_t>(n1), ugw = static_cast<uint32_t>(gw), uNW = static_cast<uint32_t>(NW);
+  const int i1_0 = static_cast<int>(un1 * ugw / uNW);
+  const int i1_1 = static_cast<int>(un1 * (ugw + 1) / uNW);
   // FC2: items (expert d, group q of 8 output rows); a workgroup owns a slice
   // of one expert when there are at least as many workgroups as experts,
   // otherwise whole experts [dA, dB)
@@ -281,16 +284,16 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
   const int g2 = H / 8;
   int dA, dB, q0, q1;
   if (D <= NG) {
-    dA = static_cast<int>(static_cast<int64_t>(blockIdx.x) * D / NG);
+    dA = static_cast<int>(blockIdx.x * static_cast<uint32_t>(D) / static_cast<uint32_t>(NG));
     dB = dA + 1;
-    const int w_lo = static_cast<int>((static_cast<int64_t>(dA) * NG + D - 1) / D);
-    const int w_hi = static_cast<int>((static_cast<int64_t>(dA + 1) * NG + D - 1) / D);
+    const int w_lo = static_cast<int>(static_cast<uint32_t>(dA * NG + D - 1) / static_cast<uint32_t>(D));
+    const int w_hi = static_cast<int>(static_cast<uint32_t>((dA + 1) * NG + D - 1) / static_cast<uint32_t>(D));
     const int nq = (w_hi - w_lo) * kFusedWaves, qw = (blockIdx.x - w_lo) * kFusedWaves + wave;
-    q0 = g2 * qw / nq;
-    q1 = g2 * (qw + 1) / nq;
+    q0 = static_cast<int>(static_cast<uint32_t>(g2 * qw) / static_cast<uint32_t>(nq));
+    q1 = static_cast<int>(static_cast<uint32_t>(g2 * (qw + 1)) / static_cast<uint32_t>(nq));
   } else {
-    dA = static_cast<int>(static_cast<int64_t>(blockIdx.x) * D / NG);
-    dB = static_cast<int>(static_cast<int64_t>(blockIdx.x + 1) * D / NG);
+    dA = static_cast<int>(blockIdx.x * static_cast<uint32_t>(D) / static_cast<uint32_t>(NG));
+    dB = static_cast<int>((blockIdx.x + 1) * static_cast<uint32_t>(D) / static_cast<uint32_t>(NG));
     q0 = g2 * wave / kFusedWaves;
     q1 = g2 * (wave + 1) / kFusedWaves;
   }
@@ -573,8 +576,8 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
   }
 
   // ---- phase 3: combine the row groups this wave owns
-  const int gc0 = static_cast<int>(static_cast<int64_t>(g2) * gw / NW);
-  const int gc1 = static_cast<int>(static_cast<int64_t>(g2) * (gw + 1) / NW);
+  const int gc0 = static_cast<int>(static_cast<uint32_t>(g2 * gw) / static_cast<uint32_t>(NW));
+  const int gc1 = static_cast<int>(static_cast<uint32_t>(g2 * (gw + 1)) / static_cast<uint32_t>(NW));
   for (int grp = gc0; grp < gc1; ++grp) {
     if (lane < 8 * T) {
       const int t = lane >> 3, m = 8 * grp + (lane & 7);
