@@ -299,6 +299,7 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
   }
   const int nkb2 = I / 32;
 
+  const int bsh = (bs == 32) ? 0 : (bs == 64) ? 1 : 2;   // bs = 32 << bsh: block of unit kb
   // Loads of one item: branch-free (out-of-range quant blocks read unit 0 and
   // get a zero scale when used); scales stay raw fp16 until used.
   auto load_fc1 = [&](int it, UnitWords<BITS> (&wv)[U1], uint32_t (&sc)[U1]) {
@@ -312,7 +313,7 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
       const int kb = blk + 16 * c;
       const int kbc = kb < nkb1 ? kb : 0;
       wv[c] = load_unit<BITS>(rowp + kbc * (4 * BITS));
-      sc[c] = srow[(32 * kbc) / bs];
+      sc[c] = srow[kbc >> bsh];
     }
   };
   auto load_fc2 = [&](int d, int q, UnitWords<BITS> (&wv)[U2], uint32_t (&sc)[U2]) {
@@ -325,7 +326,7 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
       const int kb = (blk & 7) + 8 * c;
       const int kbc = kb < nkb2 ? kb : 0;
       wv[c] = load_unit<BITS>(rowp + kbc * (4 * BITS));
-      sc[c] = srow[(32 * kbc) / bs];
+      sc[c] = srow[kbc >> bsh];
     }
   };
 
