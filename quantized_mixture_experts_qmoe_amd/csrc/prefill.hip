@@ -31,6 +31,8 @@
 // short-circuit for QMoE offload", Motivation & Summary item 3); fp32
 // combine rounded once ("[CUDA] Add MoEPacked CPU/GPU hybrid offload and
 // consolidate QMoE/GGUF offload optimizations", Key Changes item 4).
+#include <utility>
+
 #include "device.h"
 #include "internal.h"
 
@@ -42,11 +44,17 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 namespace {
 
 constexpr int kKT = 64;                 // K per stage (two 16x16x32 MFMA steps)
-constexpr int kLdsStride = kKT + 8;     // bf16 per LDS row (padding against bank conflicts)
+constexpr int kLdsStride = kKT + 16;    // bf16 per LDS row (padding against bank conflicts)
 constexpr int kBM = kTileM;             // A rows per tile (256)
 constexpr int kBN = 256;                // B rows per tile
 constexpr int kGemmThreads = 512;       // 8 waves: 2 groups of 2 x 2 waves of 64 x 128
 static_assert(kBM == 256, "the staging below assumes 256-row tiles");
+static_assert(2 * (kBM + kBN) * kLdsStride * 2 <= 160 * 1024, "LDS of one workgroup");
+// epilogue staging: per wave, 16 output rows of its 64 x 128 block at a time,
+// in a private slice of the A buffers (fp32 y: 128 + 4 columns; bf16 h: 64 + 8)
+constexpr int kStgY = 16 * (128 + 4);
+constexpr int kStgH = 16 * (64 + 8);
+static_assert(8 * kStgY * 4 <= 2 * kBM * kLdsStride * 2, "epilogue staging fits in the A buffers");
 
 // Logical tile index of this workgroup. Workgroups are dealt to the 8 XCDs
 // round-robin; consecutive logical tiles are kept on one XCD so the n-tiles
@@ -59,6 +67,17 @@ __device__ __forceinline__ int logical_tile(int active) {
   if (j >= per_xcd) return -1;
   const int L = (b % 8) * per_xcd + j;
   return L < active ? L : -1;
+}
+
+// Calls f(std::integral_constant<int, J>) for J = 0..N-1, so that each step's
+// counts are compile-time constants (the scheduling hints below need them).
+template <typename F, int... J>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, J...>) {
+  (f(std::integral_constant<int, J>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 int gemm_n_tiles(const Layer& L, bool fc1) {
@@ -196,21 +215,32 @@ void grouped_gemm_kernel(
   auto frag_b = [&](int buf, int ks, int tn) {
     return *reinterpret_cast<const bf16x8_t*>(&Bs[buf][b_frag_row[tn] * kLdsStride + ks * 32 + quad * 8]);
   };
+  // The stage's 16 steps (2 K halves x 8 B fragments) each run 4 MFMAs that
+  // share one B fragment. Fragment reads run ahead of their use: B two steps
+  // ahead through a ring of three registers, the second K half's A fragments
+  // during the first half's last four steps, so the LDS latency hides behind
+  // the matrix work instead of stalling it.
   auto mfma_stage = [&](int buf) {
     if (!wave_live) return;
+    bf16x8_t af[2][4], bfr[3];
 #pragma unroll
-    for (int ks = 0; ks < kKT / 32; ++ks) {
-      bf16x8_t af[4], bfr[8];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) af[t] = frag_a(buf, ks, t);
-#pragma unroll
-      for (int t = 0; t < 8; ++t) bfr[t] = frag_b(buf, ks, t);
+    for (int t = 0; t < 4; ++t) af[0][t] = frag_a(buf, 0, t);
+    bfr[0] = frag_b(buf, 0, 0);
+    bfr[1] = frag_b(buf, 0, 1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+    static_for<16>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      constexpr int ks = j >> 3, tn = j & 7;
+      constexpr int nreads = (j + 2 < 16 ? 1 : 0) + (ks == 0 && tn >= 4 ? 1 : 0);
+      if constexpr (j + 2 < 16) bfr[(j + 2) % 3] = frag_b(buf, (j + 2) >> 3, (j + 2) & 7);
+      if constexpr (ks == 0 && tn >= 4) af[1][tn - 4] = frag_a(buf, 1, tn - 4);
 #pragma unroll
       for (int tm = 0; tm < 4; ++tm)
-#pragma unroll
-        for (int tn = 0; tn < 8; ++tn)
-          acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[tm], bfr[tn], acc[tm][tn], 0, 0, 0);
-    }
+        acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks][tm], bfr[j % 3], acc[tm][tn], 0, 0, 0);
+      // keep the issue order: this step's reads, then its four MFMAs
+      if constexpr (nreads > 0) __builtin_amdgcn_sched_group_barrier(0x100, nreads, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    });
   };
 
   const int ns = (K + kKT - 1) / kKT;
@@ -257,28 +287,42 @@ void grouped_gemm_kernel(
       bcol[tn] = c < H ? bias_at(bias, act, static_cast<int64_t>(e) * H + c) : 0.0f;
     }
   }
+  // Results go out through a private LDS slice of this wave, 16 rows at a
+  // time, so that each row segment is written with whole 16-byte stores
+  // (the loop's last barrier has retired every LDS access of the K loop).
+  float* stg_y = reinterpret_cast<float*>(&As[0][0]) + wave * kStgY;
+  uint16_t* stg_h = &As[0][0] + wave * kStgH;
 #pragma unroll
   for (int tm = 0; tm < 4; ++tm) {
+    const int prow = wm * 64 + tm * 16;   // first tile row of this block
+    if (FC1) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int p = wm * 64 + tm * 16 + quad * 4 + i;
-      if (p >= nrows) continue;
-      const int64_t orow = row0 + p;
-      if (FC1) {
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int tn = 0; tn < 4; ++tn) {
-          const int c = n0 + wn * 64 + tn * 16 + l16;
-          if (c < I) {
-            const float hv = silu_mul_fast(acc[tm][tn][i] + bcol[tn], acc[tm][tn + 4][i] + bcol[tn + 4]);
-            h_out[orow * I + c] = static_cast<uint16_t>(f32_to_bf16(hv));
-          }
+          const float hv = silu_mul_fast(acc[tm][tn][i] + bcol[tn], acc[tm][tn + 4][i] + bcol[tn + 4]);
+          stg_h[(quad * 4 + i) * 72 + tn * 16 + l16] = static_cast<uint16_t>(f32_to_bf16(hv));
         }
-      } else {
+      // 16 rows x 64 columns: eight 16-byte chunks per row, two per lane
 #pragma unroll
-        for (int tn = 0; tn < 8; ++tn) {
-          const int c = n0 + wn * 128 + tn * 16 + l16;
-          if (c < H) y_out[orow * H + c] = acc[tm][tn][i] + bcol[tn];
-        }
+      for (int j = 0; j < 2; ++j) {
+        const int idx = lane + 64 * j, row = idx >> 3, c8 = idx & 7;
+        const int p = prow + row, c = n0 + wn * 64 + c8 * 8;
+        const uint4 v = *reinterpret_cast<const uint4*>(&stg_h[row * 72 + c8 * 8]);
+        if (p < nrows && c < I) *reinterpret_cast<uint4*>(&h_out[static_cast<int64_t>(row0 + p) * I + c]) = v;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int tn = 0; tn < 8; ++tn) stg_y[(quad * 4 + i) * 132 + tn * 16 + l16] = acc[tm][tn][i] + bcol[tn];
+      // 16 rows x 128 columns: 32 float4 per row, eight per lane
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int idx = lane + 64 * j, row = idx >> 5, c4 = idx & 31;
+        const int p = prow + row, c = n0 + wn * 128 + c4 * 4;
+        const float4 v = *reinterpret_cast<const float4*>(&stg_y[row * 132 + c4 * 4]);
+        if (p < nrows && c < H) *reinterpret_cast<float4*>(&y_out[static_cast<int64_t>(row0 + p) * H + c]) = v;
       }
     }
   }
