@@ -31,8 +31,13 @@ it); otherwise null.
 CPU baseline. The plain C oracle, timed on a bounded sample of tokens of the
 same workload on this host's cores.
 
-`--only decode4|decode1|prefill` runs one workload alone (for profiling) and
-prints its results instead of the benchmark line.
+Extra entries: M=1 decode and the 8192-token prefill of the same layer; the
+INT3 (block 64) layer at M=4 decode and as a 2048-token prefill; one pass over
+a stack of 48 independent INT2 (block 32) layers with Zipf routing drawn per
+layer, at M=1 decode and as a 32768-token packed prefill.
+
+`--only <workload>` runs one workload alone (for profiling) and prints its
+results instead of the benchmark line.
 """
 from __future__ import annotations
 
@@ -104,8 +109,9 @@ def make_layer(spec: qi.LayerSpec, w: qi.LayerWeights, max_tokens: int) -> q.QMo
                        torch.from_numpy(w.fc2_scales).to(DEV))
 
 
-def device_instance(spec: qi.LayerSpec, T: int, seed: int, max_tokens: int):
-    """A layer instance drawn on the GPU (same distributions as qmoe_inputs)."""
+def device_instance(spec: qi.LayerSpec, T: int, seed: int, max_tokens: int, zipf_s=None):
+    """A layer instance drawn on the GPU (same distributions as qmoe_inputs;
+    with zipf_s, the logits carry that layer's Zipf popularity bias)."""
     g = torch.Generator(device=DEV)
     g.manual_seed(seed)
     E, H, I, bs, c = spec.num_experts, spec.hidden, spec.inter, spec.block_size, spec.scale_c
@@ -122,8 +128,11 @@ def device_instance(spec: qi.LayerSpec, T: int, seed: int, max_tokens: int):
                         spec.block_size, spec.zero_point, torch.bfloat16, max_tokens)
     layer = q.QMoELayer(cfg, *w)
     x = torch.randn((T, H), generator=g, device=DEV).bfloat16()
-    logits = torch.randn((T, E), generator=g, device=DEV).bfloat16()
-    return layer, x, logits
+    logits = torch.randn((T, E), generator=g, device=DEV, dtype=torch.float64)
+    if zipf_s is not None:
+        bias = qi.zipf_bias(E, zipf_s, np.random.default_rng(seed))
+        logits = logits + torch.from_numpy(bias).to(DEV)[None, :]
+    return layer, x, logits.bfloat16()
 
 
 def expert_bytes(spec: qi.LayerSpec):
@@ -198,13 +207,13 @@ def kernel_times(layers, step, K: int, hold_s: float):
 
 # ----------------------------------------------------------------- workloads
 
-def bench_decode(T: int, steps: int, warmup: int):
-    spec = qi.QWEN3_INT4
-    log(f"[bench] decode M={T}: building {NROT} layer instances")
-    wl0 = qi.make_workload("decode", T=T)
+def bench_decode(T: int, steps: int, warmup: int, name: str = "decode"):
+    spec = qi.QWEN3_INT4 if name == "decode" else qi.QWEN3_INT3
+    log(f"[bench] {name} M={T}: building {NROT} layer instances")
+    wl0 = qi.make_workload(name, T=T)
     insts = [(make_layer(spec, wl0.weights, 4), wl0.tokens.x.to(DEV), wl0.tokens.logits.to(DEV))]
     for i in range(1, NROT):
-        insts.append(device_instance(spec, T, 1000 * T + i, 4))
+        insts.append(device_instance(spec, T, 1000 * T + i + (0 if name == "decode" else 500), 4))
     ws = insts[0][0].workspace(T)
     out = torch.empty((T, spec.hidden), dtype=torch.bfloat16, device=DEV)
 
@@ -222,9 +231,9 @@ def bench_decode(T: int, steps: int, warmup: int):
     for i in range(warmup):
         step(i)
     ms, enq, wall = time_steps(step, steps, hold_s=0.002 + steps * 1e-4)
-    log(f"[bench] decode M={T}: {ms * 1e3:.2f} us/step (enqueue {enq * 1e3:.1f} ms, wall {wall * 1e3:.1f} ms)")
+    log(f"[bench] {name} M={T}: {ms * 1e3:.2f} us/step (enqueue {enq * 1e3:.1f} ms, wall {wall * 1e3:.1f} ms)")
     kt = kernel_times([it[0] for it in insts], step, min(steps, 4 * NROT), hold_s=0.01)
-    log(f"[bench] decode M={T} kernels (us): " + ", ".join(f"{k}={v * 1e3:.2f}" for k, v in kt.items()))
+    log(f"[bench] {name} M={T} kernels (us): " + ", ".join(f"{k}={v * 1e3:.2f}" for k, v in kt.items()))
     fc1_b, fc2_b = expert_bytes(spec)
     D = float(np.mean([distinct[i % NROT] for i in range(steps)]))
     H, I, E, k = spec.hidden, spec.inter, spec.num_experts, spec.top_k
@@ -253,11 +262,10 @@ def bench_decode(T: int, steps: int, warmup: int):
     }
 
 
-def bench_prefill(steps: int, warmup: int):
-    spec = qi.QWEN3_INT4
-    T = 8192
-    log("[bench] prefill 8K: building layer")
-    wl = qi.make_workload("prefill", T=T)
+def bench_prefill(steps: int, warmup: int, name: str = "prefill", T: int = 8192):
+    spec = qi.QWEN3_INT4 if name == "prefill" else qi.QWEN3_INT3
+    log(f"[bench] {name} {T}: building layer")
+    wl = qi.make_workload(name, T=T)
     L = make_layer(spec, wl.weights, T)
     x, l = wl.tokens.x.to(DEV), wl.tokens.logits.to(DEV)
     ws = L.workspace(T)
@@ -270,7 +278,7 @@ def bench_prefill(steps: int, warmup: int):
         step(i)
     ms, enq, wall = time_steps(step, steps, hold_s=0.005)
     kt = kernel_times([L], step, steps, hold_s=0.005)
-    log(f"[bench] prefill 8K: {ms:.3f} ms/step; kernels (us): "
+    log(f"[bench] {name} {T}: {ms:.3f} ms/step; kernels (us): "
         + ", ".join(f"{k}={v * 1e3:.1f}" for k, v in kt.items()))
     H, I, k = spec.hidden, spec.inter, spec.top_k
     R = T * k
@@ -284,6 +292,51 @@ def bench_prefill(steps: int, warmup: int):
         "kernels_us": {kk: v * 1e3 for kk, v in kt.items()},
         "fc1": {"flops": fc1_flops, "s": t_fc1, "TFLOPs": fc1_flops / t_fc1 / 1e12},
     }
+
+
+def bench_stack(T: int, steps: int, warmup: int):
+    """One pass over the 48 independent INT2 layers (Qwen3-30B-A3B shape,
+    Zipf(1.1) routing drawn per layer), layers back to back on one stream.
+    T=1 decodes one token per layer; T=32768 is the packed prefill."""
+    spec = qi.QWEN3_INT2
+    nl = 48
+    log(f"[bench] stack T={T}: building {nl} layers")
+    layers = [device_instance(spec, T, 5 + l, T, zipf_s=1.1) for l in range(nl)]
+    ws = layers[0][0].workspace(T)
+    out = torch.empty((T, spec.hidden), dtype=torch.bfloat16, device=DEV)
+
+    def step(i):
+        for L, x, lg in layers:
+            L.forward(x, lg, out=out, workspace=ws)
+
+    distinct = []
+    if T == 1:
+        for L, x, lg in layers:
+            L.forward(x, lg, out=out, workspace=ws)
+            ids, _ = L.routing_from_workspace(T, ws)
+            distinct.append(int(torch.unique(ids).numel()))
+    torch.cuda.synchronize()
+    for i in range(warmup):
+        step(i)
+    ms, enq, wall = time_steps(step, steps, hold_s=0.002 + steps * nl * (2e-5 if T == 1 else 1e-4))
+    log(f"[bench] stack T={T}: {ms:.3f} ms/pass of {nl} layers")
+    H, I, k = spec.hidden, spec.inter, spec.top_k
+    res = {"T": T, "layers": nl, "ms_per_pass": ms, "tokens_per_s": T / (ms * 1e-3),
+           "layer_us": ms * 1e3 / nl}
+    if T == 1:
+        fc1_b, fc2_b = expert_bytes(spec)
+        nbytes = sum(distinct) * (fc1_b + fc2_b) + nl * (H * 2 * 2 + spec.num_experts * 2)
+        res["bytes_per_pass"] = nbytes
+        res["frac_hbm"] = nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS
+    else:
+        flops = nl * 2.0 * T * k * (2 * I * H + H * I)
+        res["flops_per_pass"] = flops
+        res["frac_mfma"] = flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS
+    for L, _, _ in layers:
+        L.close()
+    del layers, ws
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(n_tokens: int):
@@ -309,7 +362,9 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the M=1 and 8K prefill entries")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=96)
-    ap.add_argument("--only", choices=["decode4", "decode1", "prefill"], default=None,
+    ap.add_argument("--only", choices=["decode4", "decode1", "prefill", "int3_decode4",
+                                       "int3_prefill", "stack_decode1", "stack_prefill"],
+                    default=None,
                     help="run one workload alone (profiling aid); prints its results")
     ap.add_argument("--source-digest", action="store_true",
                     help="print the digest of the fused decode sources and exit")
@@ -329,6 +384,12 @@ def main():
     if args.only:
         if args.only == "prefill":
             res = bench_prefill(args.steps, args.warmup)
+        elif args.only == "int3_prefill":
+            res = bench_prefill(args.steps, args.warmup, "int3", 2048)
+        elif args.only == "int3_decode4":
+            res = bench_decode(4, args.steps, args.warmup, "int3")
+        elif args.only.startswith("stack"):
+            res = bench_stack(1 if args.only == "stack_decode1" else 32768, args.steps, args.warmup)
         else:
             res = bench_decode(4 if args.only == "decode4" else 1, args.steps, args.warmup)
         print(json.dumps({"only": args.only, **res}), flush=True)
@@ -339,6 +400,10 @@ def main():
     if not args.no_extra:
         m1 = bench_decode(1, args.steps, args.warmup)
         pf = bench_prefill(args.prefill_steps, 3)
+        i3d = bench_decode(4, args.steps, args.warmup, "int3")
+        i3p = bench_prefill(args.prefill_steps, 3, "int3", 2048)
+        sd = bench_stack(1, 20, 3)
+        sp = bench_stack(32768, 3, 1)
         extra = [
             {"workload": "decode M=1", "tokens_per_s": m1["tokens_per_s"],
              "ms_per_step": m1["ms_per_step"], "layer_frac_hbm": m1["layer_frac_hbm"],
@@ -352,6 +417,27 @@ def main():
              "roofline": {"bound": "mfma", "kernel": "gemm_fc1_swiglu",
                           "achieved": pf["fc1"]["TFLOPs"], "peak": BF16_PEAK_TFLOPS,
                           "unit": "TFLOP/s", "frac": pf["fc1"]["TFLOPs"] / BF16_PEAK_TFLOPS}},
+            {"workload": "INT3 bs64 layer decode M=4 (uniform routing)",
+             "tokens_per_s": i3d["tokens_per_s"], "ms_per_step": i3d["ms_per_step"],
+             "layer_frac_hbm": i3d["layer_frac_hbm"], "distinct_experts": i3d["distinct_experts"],
+             "kernels_us": i3d["kernels_us"],
+             "roofline": {"bound": "hbm", "kernel": i3d["dominant"]["kernel"],
+                          "achieved": i3d["dominant"]["GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": i3d["dominant"]["GBs"] / HBM_PEAK_GBS}},
+            {"workload": "INT3 bs64 layer prefill 2048 tokens (8 packed sequences)",
+             "tokens_per_s": i3p["tokens_per_s"], "ms_per_step": i3p["ms_per_step"],
+             "layer_frac_mfma": i3p["layer_frac_mfma"], "kernels_us": i3p["kernels_us"],
+             "roofline": {"bound": "mfma", "kernel": "gemm_fc1_swiglu",
+                          "achieved": i3p["fc1"]["TFLOPs"], "peak": BF16_PEAK_TFLOPS,
+                          "unit": "TFLOP/s", "frac": i3p["fc1"]["TFLOPs"] / BF16_PEAK_TFLOPS}},
+            {"workload": "48-layer INT2 bs32 stack, M=1 decode pass (Zipf routing per layer)",
+             "tokens_per_s": sd["tokens_per_s"], "ms_per_pass": sd["ms_per_pass"],
+             "layer_us": sd["layer_us"], "bytes_per_pass": sd["bytes_per_pass"],
+             "frac_hbm": sd["frac_hbm"]},
+            {"workload": "48-layer INT2 bs32 stack, 32768-token packed prefill pass",
+             "tokens_per_s": sp["tokens_per_s"], "ms_per_pass": sp["ms_per_pass"],
+             "layer_us": sp["layer_us"], "flops_per_pass": sp["flops_per_pass"],
+             "frac_mfma": sp["frac_mfma"]},
         ]
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_tokens)
 
