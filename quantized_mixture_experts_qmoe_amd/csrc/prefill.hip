@@ -116,7 +116,12 @@ void grouped_gemm_kernel(
   // [128 g, 128 g + 128) of the tile; in each phase one group runs its MFMAs
   // while the other stores its share of the next stage
   const int grp = wave >> 2, gw = wave & 3, gt = tid & 255;
-  const int wm = 2 * grp + (gw >> 1), wn = gw & 1;
+  // A tile of at most 128 rows runs in half mode: both groups compute rows
+  // 0-127 (stored by group 0), each for half of the tile's columns, so the
+  // matrix cores stay busy in both phases; each wave then holds 64 x 64.
+  const bool half = nrows <= kBM / 2;
+  const int wm = half ? (gw >> 1) : 2 * grp + (gw >> 1), wn = gw & 1;
+  const int cg = half ? grp : 0;   // column half of this group in half mode
   const bool wave_live = wm * 64 < nrows;
   const int n_rows_total = FC1 ? 2 * I : H;
   const uint8_t* ebase = codes + static_cast<int64_t>(e) * n_rows_total * row_bytes;
@@ -158,7 +163,8 @@ void grouped_gemm_kernel(
 
   uint4 ra0, ra1, ra2, ra3;
   UnitWords<BITS> rb;
-  uint32_t rs;
+  uint16_t rs;      // raw fp16 scale of this stage's B unit
+  bool rpast;       // the unit lies past K (its scale is taken as zero)
   int rz = zp;   // this stage's zero point (the scalar one without a tensor)
   auto load_stage = [&](int st) {
     const int k0 = st * kKT;
@@ -170,7 +176,10 @@ void grouped_gemm_kernel(
     const int kk = k0 + 32 * b_kq;
     const int kb = (kk < K) ? kk : 0;
     rb = load_unit<BITS>(b_ptr + (kb / 32) * (4 * BITS));
-    rs = s_ptr[kb >> bs_shift] | (kk < K ? 0u : 0x10000u);   // bit 16: past K
+    // (the flag is kept apart from the loaded value, so nothing waits for
+    // the load before the store phase that consumes it)
+    rs = s_ptr[kb >> bs_shift];
+    rpast = kk >= K;
     if constexpr (HAS_ZP) rz = z_ptr[kb >> bs_shift];
   };
   auto store_stage = [&](int buf) {
@@ -181,7 +190,7 @@ void grouped_gemm_kernel(
     *reinterpret_cast<uint4*>(ad + 24 * kLdsStride) = ra3;
     uint32_t pairs[16];
     {
-      const float sc = (rs >> 16) ? 0.0f : half_to_f32(static_cast<uint16_t>(rs));
+      const float sc = rpast ? 0.0f : half_to_f32(rs);
       float q[16];
       uint32_t p0[8];
       unit_half_codes<BITS>(rb, 0, q);
@@ -203,11 +212,18 @@ void grouped_gemm_kernel(
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int quad = lane >> 4, l16 = lane & 15;
+  // B rows (output columns) of fragment tn: FC1 pairs gate fragment tn with
+  // up fragment tn + NT/2 (NT = 8 fragments per wave, 4 in half mode)
   int b_frag_row[8];
 #pragma unroll
-  for (int tn = 0; tn < 8; ++tn)
-    b_frag_row[tn] = FC1 ? (tn < 4 ? 0 : kBN / 2) + wn * 64 + (tn & 3) * 16 + l16
-                         : wn * 128 + tn * 16 + l16;
+  for (int tn = 0; tn < 8; ++tn) {
+    if (half)
+      b_frag_row[tn] = FC1 ? ((tn & 2) ? kBN / 2 : 0) + cg * 64 + wn * 32 + (tn & 1) * 16 + l16
+                           : cg * 128 + wn * 64 + (tn & 3) * 16 + l16;
+    else
+      b_frag_row[tn] = FC1 ? (tn < 4 ? 0 : kBN / 2) + wn * 64 + (tn & 3) * 16 + l16
+                           : wn * 128 + tn * 16 + l16;
+  }
   auto frag_a = [&](int buf, int ks, int tm) {
     const int r = wm * 64 + tm * 16 + l16;
     return *reinterpret_cast<const bf16x8_t*>(&As[buf][r * kLdsStride + ks * 32 + quad * 8]);
@@ -215,25 +231,26 @@ void grouped_gemm_kernel(
   auto frag_b = [&](int buf, int ks, int tn) {
     return *reinterpret_cast<const bf16x8_t*>(&Bs[buf][b_frag_row[tn] * kLdsStride + ks * 32 + quad * 8]);
   };
-  // The stage's 16 steps (2 K halves x 8 B fragments) each run 4 MFMAs that
-  // share one B fragment. Fragment reads run ahead of their use: B two steps
-  // ahead through a ring of three registers, the second K half's A fragments
-  // during the first half's last four steps, so the LDS latency hides behind
-  // the matrix work instead of stalling it.
-  auto mfma_stage = [&](int buf) {
-    if (!wave_live) return;
+  // A stage is 2 K halves x NT B fragments (NT = 8, or 4 in half mode); each
+  // step runs 4 MFMAs that share one B fragment. Fragment reads run ahead of
+  // their use: B two steps ahead through a ring of three registers, the
+  // second K half's A fragments during the first half's last four steps, so
+  // the LDS latency hides behind the matrix work instead of stalling it.
+  auto mfma_steps = [&](int buf, auto ntc) {
+    constexpr int NT = decltype(ntc)::value, NS = 2 * NT;
     bf16x8_t af[2][4], bfr[3];
 #pragma unroll
     for (int t = 0; t < 4; ++t) af[0][t] = frag_a(buf, 0, t);
     bfr[0] = frag_b(buf, 0, 0);
     bfr[1] = frag_b(buf, 0, 1);
     __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-    static_for<16>([&](auto jc) {
+    static_for<NS>([&](auto jc) {
       constexpr int j = decltype(jc)::value;
-      constexpr int ks = j >> 3, tn = j & 7;
-      constexpr int nreads = (j + 2 < 16 ? 1 : 0) + (ks == 0 && tn >= 4 ? 1 : 0);
-      if constexpr (j + 2 < 16) bfr[(j + 2) % 3] = frag_b(buf, (j + 2) >> 3, (j + 2) & 7);
-      if constexpr (ks == 0 && tn >= 4) af[1][tn - 4] = frag_a(buf, 1, tn - 4);
+      constexpr int ks = j / NT, tn = j % NT;
+      constexpr bool rd_a = ks == 0 && tn >= NT - 4;
+      constexpr int nreads = (j + 2 < NS ? 1 : 0) + (rd_a ? 1 : 0);
+      if constexpr (j + 2 < NS) bfr[(j + 2) % 3] = frag_b(buf, (j + 2) / NT, (j + 2) % NT);
+      if constexpr (rd_a) af[1][tn - (NT - 4)] = frag_a(buf, 1, tn - (NT - 4));
 #pragma unroll
       for (int tm = 0; tm < 4; ++tm)
         acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks][tm], bfr[j % 3], acc[tm][tn], 0, 0, 0);
@@ -242,7 +259,6 @@ void grouped_gemm_kernel(
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     });
   };
-
   const int ns = (K + kKT - 1) / kKT;
   auto clampst = [&](int st) { return st < ns ? st : ns - 1; };
   // prologue: stage 0 complete in buffer 0; registers hold stage 1
@@ -250,82 +266,104 @@ void grouped_gemm_kernel(
   store_stage(0);
   load_stage(clampst(1));
   __syncthreads();
-  // one loop per group (same barrier sequence), so each keeps only its own
-  // live registers
-  if (grp == 0) {
-    for (int st = 0; st < ns; ++st) {
-      const int buf = st & 1;
-      mfma_stage(buf);             // phase X
-      __syncthreads();
-      store_stage(buf ^ 1);        // phase Y
-      load_stage(clampst(st + 2));
-      __syncthreads();
+  // The K loop, instantiated once per fragment count (the mode is uniform
+  // over the tile, so each instance keeps its own register allocation); one
+  // loop per group (same barrier sequence), so each keeps only its own live
+  // registers.
+  auto kloop = [&](auto ntc) {
+    auto mfma_stage = [&](int buf) {
+      if (wave_live) mfma_steps(buf, ntc);
+    };
+    if (grp == 0) {
+      for (int st = 0; st < ns; ++st) {
+        const int buf = st & 1;
+        mfma_stage(buf);             // phase X
+        __syncthreads();
+        store_stage(buf ^ 1);        // phase Y
+        load_stage(clampst(st + 2));
+        __syncthreads();
+      }
+    } else {
+      for (int st = 0; st < ns; ++st) {
+        const int buf = st & 1;
+        store_stage(buf ^ 1);        // phase X
+        load_stage(clampst(st + 2));
+        __syncthreads();
+        mfma_stage(buf);             // phase Y
+        __syncthreads();
+      }
     }
-  } else {
-    for (int st = 0; st < ns; ++st) {
-      const int buf = st & 1;
-      store_stage(buf ^ 1);        // phase X
-      load_stage(clampst(st + 2));
-      __syncthreads();
-      mfma_stage(buf);             // phase Y
-      __syncthreads();
-    }
-  }
+  };
+  if (half)
+    kloop(std::integral_constant<int, 4>{});
+  else
+    kloop(std::integral_constant<int, 8>{});
   if (!wave_live) return;
 
-  // ---- epilogue: lane holds rows 4*quad + i, column l16 of each 16x16 tile;
-  // the optional bias is per column (FC1: the gate and up rows' biases)
-  float bcol[8];
-#pragma unroll
-  for (int tn = 0; tn < 8; ++tn) {
-    if (FC1) {
-      const int c = n0 + wn * 64 + (tn & 3) * 16 + l16, up = tn >> 2;
-      const int64_t r = fc1_il ? 2 * c + up : (up ? I + c : c);
-      bcol[tn] = c < I ? bias_at(bias, act, static_cast<int64_t>(e) * 2 * I + r) : 0.0f;
-    } else {
-      const int c = n0 + wn * 128 + tn * 16 + l16;
-      bcol[tn] = c < H ? bias_at(bias, act, static_cast<int64_t>(e) * H + c) : 0.0f;
-    }
-  }
-  // Results go out through a private LDS slice of this wave, 16 rows at a
-  // time, so that each row segment is written with whole 16-byte stores
-  // (the loop's last barrier has retired every LDS access of the K loop).
+  // ---- epilogue: lane holds rows 4*quad + i, column l16 of each 16x16
+  // fragment. Results go out through a private LDS slice of this wave, 16
+  // rows at a time, so that each row segment is written with whole 16-byte
+  // stores (the loop's last barrier has retired every LDS access of the K
+  // loop). The optional bias is per column (FC1: the gate and up rows').
   float* stg_y = reinterpret_cast<float*>(&As[0][0]) + wave * kStgY;
   uint16_t* stg_h = &As[0][0] + wave * kStgH;
+  auto epilogue = [&](auto ntc) {
+    constexpr int NT = decltype(ntc)::value, NH = NT / 2;
+    // first output column of this wave (FC1: h columns, NH * 16 of them;
+    // FC2: y columns, NT * 16 of them)
+    const int cb = FC1 ? n0 + (half ? cg * 64 + wn * 32 : wn * 64)
+                       : n0 + (half ? cg * 128 + wn * 64 : wn * 128);
+    float bcol[NT];
 #pragma unroll
-  for (int tm = 0; tm < 4; ++tm) {
-    const int prow = wm * 64 + tm * 16;   // first tile row of this block
-    if (FC1) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int tn = 0; tn < 4; ++tn) {
-          const float hv = silu_mul_fast(acc[tm][tn][i] + bcol[tn], acc[tm][tn + 4][i] + bcol[tn + 4]);
-          stg_h[(quad * 4 + i) * 72 + tn * 16 + l16] = static_cast<uint16_t>(f32_to_bf16(hv));
-        }
-      // 16 rows x 64 columns: eight 16-byte chunks per row, two per lane
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int idx = lane + 64 * j, row = idx >> 3, c8 = idx & 7;
-        const int p = prow + row, c = n0 + wn * 64 + c8 * 8;
-        const uint4 v = *reinterpret_cast<const uint4*>(&stg_h[row * 72 + c8 * 8]);
-        if (p < nrows && c < I) *reinterpret_cast<uint4*>(&h_out[static_cast<int64_t>(row0 + p) * I + c]) = v;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int tn = 0; tn < 8; ++tn) stg_y[(quad * 4 + i) * 132 + tn * 16 + l16] = acc[tm][tn][i] + bcol[tn];
-      // 16 rows x 128 columns: 32 float4 per row, eight per lane
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int idx = lane + 64 * j, row = idx >> 5, c4 = idx & 31;
-        const int p = prow + row, c = n0 + wn * 128 + c4 * 4;
-        const float4 v = *reinterpret_cast<const float4*>(&stg_y[row * 132 + c4 * 4]);
-        if (p < nrows && c < H) *reinterpret_cast<float4*>(&y_out[static_cast<int64_t>(row0 + p) * H + c]) = v;
+    for (int tn = 0; tn < NT; ++tn) {
+      if (FC1) {
+        const int c = cb + (tn % NH) * 16 + l16, up = tn >= NH;
+        const int64_t r = fc1_il ? 2 * c + up : (up ? I + c : c);
+        bcol[tn] = c < I ? bias_at(bias, act, static_cast<int64_t>(e) * 2 * I + r) : 0.0f;
+      } else {
+        const int c = cb + tn * 16 + l16;
+        bcol[tn] = c < H ? bias_at(bias, act, static_cast<int64_t>(e) * H + c) : 0.0f;
       }
     }
-  }
+#pragma unroll
+    for (int tm = 0; tm < 4; ++tm) {
+      const int prow = wm * 64 + tm * 16;   // first tile row of this block
+      if (FC1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int tn = 0; tn < NH; ++tn) {
+            const float hv = silu_mul_fast(acc[tm][tn][i] + bcol[tn], acc[tm][tn + NH][i] + bcol[tn + NH]);
+            stg_h[(quad * 4 + i) * 72 + tn * 16 + l16] = static_cast<uint16_t>(f32_to_bf16(hv));
+          }
+        // 16 rows x NH*16 columns: NT 16-byte chunks per row
+#pragma unroll
+        for (int j = 0; j < NT / 4; ++j) {
+          const int idx = lane + 64 * j, row = idx / NT, c8 = idx % NT;
+          const int p = prow + row, c = cb + c8 * 8;
+          const uint4 v = *reinterpret_cast<const uint4*>(&stg_h[row * 72 + c8 * 8]);
+          if (p < nrows && c < I) *reinterpret_cast<uint4*>(&h_out[static_cast<int64_t>(row0 + p) * I + c]) = v;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int tn = 0; tn < NT; ++tn) stg_y[(quad * 4 + i) * 132 + tn * 16 + l16] = acc[tm][tn][i] + bcol[tn];
+        // 16 rows x NT*16 columns: NT*4 float4 per row
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          const int idx = lane + 64 * j, row = idx / (NT * 4), c4 = idx % (NT * 4);
+          const int p = prow + row, c = cb + c4 * 4;
+          const float4 v = *reinterpret_cast<const float4*>(&stg_y[row * 132 + c4 * 4]);
+          if (p < nrows && c < H) *reinterpret_cast<float4*>(&y_out[static_cast<int64_t>(row0 + p) * H + c]) = v;
+        }
+      }
+    }
+  };
+  if (half)
+    epilogue(std::integral_constant<int, 4>{});
+  else
+    epilogue(std::integral_constant<int, 8>{});
 }
 
 // out[t][m] = round(sum_j w[t][j] * y[inv_pos[t*k + j]][m]), slot order j = 0..k-1.
