@@ -170,11 +170,18 @@ __device__ __forceinline__ void unit_half_codes(const UnitWords<BITS>& u, int h,
 #pragma unroll
       for (int j = 0; j < 4; ++j) q[4 * b + j] = ubyte_f32(c[j], b);
   } else {
-    // bits [48h, 48h + 48) of the 96-bit unit
-    const uint64_t w = h ? ((static_cast<uint64_t>(u.w[2]) << 32 | u.w[1]) >> 16)
-                         : (static_cast<uint64_t>(u.w[1]) << 32 | u.w[0]);
+    // bits [48h, 48h + 48) of the 96-bit unit as two 32-bit words (a: the
+    // low 32 bits, b: the next 16), kept in registers: code i sits at bit 3i
+    // of b:a, and code 10 straddles the two words
+    const uint32_t a = h ? __builtin_amdgcn_alignbit(u.w[2], u.w[1], 16) : u.w[0];
+    const uint32_t b = h ? (u.w[2] >> 16) : u.w[1];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) q[i] = static_cast<float>(static_cast<uint32_t>(w >> (3 * i)) & 7u);
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t c = (3 * i + 3 <= 32) ? (a >> (3 * i)) & 7u
+                         : (3 * i >= 32)   ? (b >> (3 * i - 32)) & 7u
+                                           : __builtin_amdgcn_alignbit(b, a, 3 * i) & 7u;
+      q[i] = static_cast<float>(c);
+    }
   }
 }
 
