@@ -192,13 +192,16 @@ void grouped_gemm_kernel(
     {
       const float sc = rpast ? 0.0f : half_to_f32(rs);
       float q[16];
-      uint32_t p0[8];
+      // (q - zp) * s as one fma: q * s and zp * s are exact in fp32 (at most
+      // 8 + 11 significant bits), so the fused result is the exact product,
+      // bit for bit what subtracting first and then multiplying gives
+      const float nzs = -static_cast<float>(rz) * sc;
       unit_half_codes<BITS>(rb, 0, q);
-      dequant_codes_bf16<8>(q, sc, rz, p0);
-      for (int p = 0; p < 8; ++p) pairs[p] = p0[p];
+#pragma unroll
+      for (int p = 0; p < 8; ++p) pairs[p] = f32x2_to_bf16x2(fmaf(q[2 * p], sc, nzs), fmaf(q[2 * p + 1], sc, nzs));
       unit_half_codes<BITS>(rb, 1, q);
-      dequant_codes_bf16<8>(q, sc, rz, p0);
-      for (int p = 0; p < 8; ++p) pairs[8 + p] = p0[p];
+#pragma unroll
+      for (int p = 0; p < 8; ++p) pairs[8 + p] = f32x2_to_bf16x2(fmaf(q[2 * p], sc, nzs), fmaf(q[2 * p + 1], sc, nzs));
     }
     uint4* bd = reinterpret_cast<uint4*>(&Bs[buf][b_row * kLdsStride + 32 * b_kq]);
 #pragma unroll
