@@ -1,6 +1,10 @@
 // Fused decode path (1..4 tokens, bf16 activations): one kernel launch with
 // no grid-wide barrier.
 //
+// Layers with FC1/FC2 biases or per-block zero-point tensors run an instance
+// that also loads, per weight row, the row's bias and its blocks' zero points
+// (EX below).
+//
 // Phases (one workgroup of 8 waves per CU; the grid is the number of
 // workgroups that fit on the device at once, so all are resident):
 //   0. routing of the <= 4 tokens, recomputed by every workgroup: wave t
@@ -167,10 +171,22 @@ struct FusedArgs {
   uint64_t* yx;      // exchange: y [route][hidden]
   uint32_t* err;     // error bits (bounded waits that ran out)
   uint32_t epoch;    // nonzero; no exchange entry holds it before this call writes it
+  // optional: FC1/FC2 biases (bf16, [E][2I] / [E][H]) and per-block
+  // zero-point codes (uint8, laid out like the scales); read only by the
+  // instance built for layers that have any of them
+  const uint16_t* b1;
+  const uint16_t* b2;
+  const uint8_t* z1;
+  const uint8_t* z2;
 };
 
 // U1: FC1 quant blocks per lane (ceil(H/32 / 16)); U2: FC2 quant blocks per lane (ceil(I/32 / 8)).
-template <int BITS, int U1, int U2>
+// EX: the layer has biases or zero-point tensors. Each lane then also loads,
+// with an item's codes and scales, the bias of its weight row and the zero
+// point of each of its quant blocks; the block correction becomes
+// (128 + zp) * sum(x) per block, and the bias is added to the row's sum
+// before SwiGLU (FC1) or before the combine (FC2).
+template <int BITS, int U1, int U2, bool EX>
 __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a) {
   __shared__ FusedLds S;
   // wave-uniform values go through readfirstlane so the compiler keeps them
@@ -302,7 +318,8 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
   const int bsh = (bs == 32) ? 0 : (bs == 64) ? 1 : 2;   // bs = 32 << bsh: block of unit kb
   // Loads of one item: branch-free (out-of-range quant blocks read unit 0 and
   // get a zero scale when used); scales stay raw fp16 until used.
-  auto load_fc1 = [&](int it, UnitWords<BITS> (&wv)[U1], uint32_t (&sc)[U1]) {
+  auto load_fc1 = [&](int it, UnitWords<BITS> (&wv)[U1], uint32_t (&sc)[U1], uint32_t& bv,
+                      uint32_t (&zv)[U1]) {
     const int e = S.dlist[it / g1];
     const int n = 2 * (it % g1) + (q4 & 1);
     const int row = a.fc1_il ? 2 * n + (q4 >> 1) : ((q4 < 2) ? n : I + n);
@@ -315,8 +332,18 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
       wv[c] = load_unit<BITS>(rowp + kbc * (4 * BITS));
       sc[c] = srow[kbc >> bsh];
     }
+    if constexpr (EX) {
+      bv = a.b1 ? a.b1[static_cast<int64_t>(e) * 2 * I + row] : 0u;
+      const uint8_t* zrow = a.z1 ? a.z1 + (static_cast<int64_t>(e) * 2 * I + row) * a.nb1 : nullptr;
+#pragma unroll
+      for (int c = 0; c < U1; ++c) {
+        const int kb = blk + 16 * c;
+        zv[c] = zrow ? zrow[(kb < nkb1 ? kb : 0) >> bsh] : static_cast<uint32_t>(zp);
+      }
+    }
   };
-  auto load_fc2 = [&](int d, int q, UnitWords<BITS> (&wv)[U2], uint32_t (&sc)[U2]) {
+  auto load_fc2 = [&](int d, int q, UnitWords<BITS> (&wv)[U2], uint32_t (&sc)[U2], uint32_t& bv,
+                      uint32_t (&zv)[U2]) {
     const int e = S.dlist[d];
     const int m = q * 8 + (blk >= 8 ? 4 : 0) + q4;
     const uint8_t* rowp = a.c2 + (static_cast<int64_t>(e) * H + m) * a.rb2;
@@ -328,6 +355,15 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
       wv[c] = load_unit<BITS>(rowp + kbc * (4 * BITS));
       sc[c] = srow[kbc >> bsh];
     }
+    if constexpr (EX) {
+      bv = a.b2 ? a.b2[static_cast<int64_t>(e) * H + m] : 0u;
+      const uint8_t* zrow = a.z2 ? a.z2 + (static_cast<int64_t>(e) * H + m) * a.nb2 : nullptr;
+#pragma unroll
+      for (int c = 0; c < U2; ++c) {
+        const int kb = (blk & 7) + 8 * c;
+        zv[c] = zrow ? zrow[(kb < nkb2 ? kb : 0) >> bsh] : static_cast<uint32_t>(zp);
+      }
+    }
   };
 
   // ---- issue: the first two FC1 items, then the first two FC2 items. The
@@ -335,18 +371,20 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
   // never uses), so the compiler's wait counts stay exact.
   UnitWords<BITS> w1A[U1], w1B[U1];
   uint32_t s1A[U1], s1B[U1];   // raw fp16 scales, one per register
+  uint32_t b1A = 0u, b1B = 0u, z1A[U1], z1B[U1];   // raw bias and zero points (EX)
   // (sched_barrier keeps the issue order A, B, FC2 A, FC2 B that the waits
   // below count on)
   const int last1 = max(i1_1 - 1, 0);
-  load_fc1(min(i1_0, last1), w1A, s1A);
+  load_fc1(min(i1_0, last1), w1A, s1A, b1A, z1A);
   __builtin_amdgcn_sched_barrier(0);
-  load_fc1(min(i1_0 + 1, last1), w1B, s1B);
+  load_fc1(min(i1_0 + 1, last1), w1B, s1B, b1B, z1B);
   __builtin_amdgcn_sched_barrier(0);
   UnitWords<BITS> w2A[U2], w2B[U2];
   uint32_t s2A[U2], s2B[U2];
+  uint32_t b2A = 0u, b2B = 0u, z2A[U2], z2B[U2];
   const int last2 = max(q1 - 1, 0);
-  load_fc2(dA, min(q0, last2), w2A, s2A);
-  load_fc2(dA, min(q0 + 1, last2), w2B, s2B);
+  load_fc2(dA, min(q0, last2), w2A, s2A, b2A, z2A);
+  load_fc2(dA, min(q0 + 1, last2), w2B, s2B, b2B, z2B);
   __builtin_amdgcn_sched_barrier(0);
 
   // x pairs and their sums (the x loads have long completed)
@@ -374,14 +412,18 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
   float corr1[U1][kDecodeMaxTokens];
 #pragma unroll
   for (int c = 0; c < U1; ++c) {
-    corr1[c][0] = zc * quad_get<0>(sx[c]);
-    corr1[c][1] = zc * quad_get<1>(sx[c]);
-    corr1[c][2] = zc * quad_get<2>(sx[c]);
-    corr1[c][3] = zc * quad_get<3>(sx[c]);
+    // (with EX the zero point varies per block: the sums stay raw here and
+    // the item scales them by 128 + zp)
+    const float zcc = EX ? 1.0f : zc;
+    corr1[c][0] = zcc * quad_get<0>(sx[c]);
+    corr1[c][1] = zcc * quad_get<1>(sx[c]);
+    corr1[c][2] = zcc * quad_get<2>(sx[c]);
+    corr1[c][3] = zcc * quad_get<3>(sx[c]);
   }
 
   // one FC1 item: gate/up sums of two rows for every token, SwiGLU, into hbuf
-  auto fc1_item = [&](const UnitWords<BITS> (&wv)[U1], const uint32_t (&sc)[U1], int li) {
+  auto fc1_item = [&](const UnitWords<BITS> (&wv)[U1], const uint32_t (&sc)[U1], uint32_t bv,
+                      const uint32_t (&zv)[U1], int li) {
     float acc[kDecodeMaxTokens] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < U1; ++c) {
@@ -393,14 +435,23 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
       for (int m = 0; m < 8; ++m) dv = mfma4(xp[c][2 * m], xp[c][2 * m + 1], wp[2 * m], wp[2 * m + 1], dv);
       const float s = (blk + 16 * c) < nkb1 ? half_to_f32(static_cast<uint16_t>(sc[c])) : 0.0f;
       const float s128 = 128.0f * s;
+      // (with EX: the same product (128 + zp) * sum(x) as the scalar path
+      // forms once, so a tensor holding the scalar gives identical bits)
+      const float zcl = 128.0f + static_cast<float>(zv[c]);
 #pragma unroll
       for (int t = 0; t < kDecodeMaxTokens; ++t)
-        acc[t] = fmaf(s128, dv[t], fmaf(-s, corr1[c][t], acc[t]));
+        acc[t] = fmaf(s128, dv[t], fmaf(-s, EX ? zcl * corr1[c][t] : corr1[c][t], acc[t]));
     }
     // sum over the 16 blocks: lanes 0..3 end with rows 0..3 (gate n, gate
     // n+1, up n, up n+1); lanes 0 and 1 then take the up sums of lanes 2, 3
 #pragma unroll
     for (int t = 0; t < kDecodeMaxTokens; ++t) acc[t] = half_pair_sum(row_pair_sum(row_class_sum(acc[t])));
+    if (EX && a.b1) {
+      // every lane now holds the total of its row: add that row's bias
+      const float b = bf16_to_f32(bv);
+#pragma unroll
+      for (int t = 0; t < kDecodeMaxTokens; ++t) acc[t] += b;
+    }
     float up[kDecodeMaxTokens];
 #pragma unroll
     for (int t = 0; t < kDecodeMaxTokens; ++t) up[t] = dpp_f<0xEE>(acc[t]);   // quad_perm [2, 3, 2, 3]
@@ -413,10 +464,10 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
   for (int c0 = i1_0; c0 < i1_1; c0 += kCap1) {
     const int c1 = min(c0 + kCap1, i1_1);
     for (int it = c0; it < c1; it += 2) {
-      fc1_item(w1A, s1A, it - c0);
-      load_fc1(min(it + 2, last1), w1A, s1A);
-      if (it + 1 < c1) fc1_item(w1B, s1B, it + 1 - c0);
-      load_fc1(min(it + 3, last1), w1B, s1B);
+      fc1_item(w1A, s1A, b1A, z1A, it - c0);
+      load_fc1(min(it + 2, last1), w1A, s1A, b1A, z1A);
+      if (it + 1 < c1) fc1_item(w1B, s1B, b1B, z1B, it + 1 - c0);
+      load_fc1(min(it + 3, last1), w1B, s1B, b1B, z1B);
     }
     // write this chunk's h (coalesced along n per token)
     const int ni2 = 2 * (c1 - c0);
@@ -432,8 +483,9 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
   // the third and fourth FC2 items of this wave (FC1's registers are free now)
   UnitWords<BITS> w2C[U2], w2D[U2];
   uint32_t s2C[U2], s2D[U2];
-  load_fc2(dA, min(q0 + 2, last2), w2C, s2C);
-  load_fc2(dA, min(q0 + 3, last2), w2D, s2D);
+  uint32_t b2C = 0u, b2D = 0u, z2C[U2], z2D[U2];
+  load_fc2(dA, min(q0 + 2, last2), w2C, s2C, b2C, z2C);
+  load_fc2(dA, min(q0 + 3, last2), w2D, s2D, b2D, z2D);
 
   // ---- phase 2: FC2 of this workgroup's expert(s)
   for (int d = dA; d < dB; ++d) {
@@ -516,15 +568,16 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
         hlo[c][4 * j] = l4.x; hlo[c][4 * j + 1] = l4.y; hlo[c][4 * j + 2] = l4.z; hlo[c][4 * j + 3] = l4.w;
       }
 #pragma unroll
-      for (int t = 0; t < kDecodeMaxTokens; ++t) corr2[c][t] = ok ? zc * S.hsum[t][kb] : 0.0f;
+      for (int t = 0; t < kDecodeMaxTokens; ++t) corr2[c][t] = ok ? (EX ? 1.0f : zc) * S.hsum[t][kb] : 0.0f;
     }
     if (d != dA) {
-      load_fc2(d, q0, w2A, s2A);
-      load_fc2(d, min(q0 + 1, last2), w2B, s2B);
-      load_fc2(d, min(q0 + 2, last2), w2C, s2C);
-      load_fc2(d, min(q0 + 3, last2), w2D, s2D);
+      load_fc2(d, q0, w2A, s2A, b2A, z2A);
+      load_fc2(d, min(q0 + 1, last2), w2B, s2B, b2B, z2B);
+      load_fc2(d, min(q0 + 2, last2), w2C, s2C, b2C, z2C);
+      load_fc2(d, min(q0 + 3, last2), w2D, s2D, b2D, z2D);
     }
-    auto fc2_item = [&](const UnitWords<BITS> (&wv)[U2], const uint32_t (&sc)[U2], int li) {
+    auto fc2_item = [&](const UnitWords<BITS> (&wv)[U2], const uint32_t (&sc)[U2], uint32_t bv,
+                        const uint32_t (&zv)[U2], int li) {
       float acc[kDecodeMaxTokens] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < U2; ++c) {
@@ -539,14 +592,21 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
         }
         const float s = ((blk & 7) + 8 * c) < nkb2 ? half_to_f32(static_cast<uint16_t>(sc[c])) : 0.0f;
         const float s128 = 128.0f * s;
+        const float zcl = 128.0f + static_cast<float>(zv[c]);
 #pragma unroll
         for (int t = 0; t < kDecodeMaxTokens; ++t)
-          acc[t] = fmaf(s128, dv[t], fmaf(-s, corr2[c][t], acc[t]));
+          acc[t] = fmaf(s128, dv[t], fmaf(-s, EX ? zcl * corr2[c][t] : corr2[c][t], acc[t]));
       }
       // sum over the 8 quant blocks of each half wave: lanes 0..3 end with
       // rows 0..3 of the item, lanes 32..35 with rows 4..7
 #pragma unroll
       for (int t = 0; t < kDecodeMaxTokens; ++t) acc[t] = row_pair_sum(row_class_sum(acc[t]));
+      if (EX && a.b2) {
+        // lanes holding a row's total add that row's bias
+        const float b = bf16_to_f32(bv);
+#pragma unroll
+        for (int t = 0; t < kDecodeMaxTokens; ++t) acc[t] += b;
+      }
       if ((lane & ~32) < 4)
 #pragma unroll
         for (int t = 0; t < kDecodeMaxTokens; ++t)
@@ -555,14 +615,14 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
     for (int c0 = q0; c0 < q1; c0 += kCap2) {
       const int c1 = min(c0 + kCap2, q1);
       for (int q = c0; q < c1; q += 4) {
-        fc2_item(w2A, s2A, q - c0);
-        load_fc2(d, min(q + 4, last2), w2A, s2A);
-        if (q + 1 < c1) fc2_item(w2B, s2B, q + 1 - c0);
-        load_fc2(d, min(q + 5, last2), w2B, s2B);
-        if (q + 2 < c1) fc2_item(w2C, s2C, q + 2 - c0);
-        load_fc2(d, min(q + 6, last2), w2C, s2C);
-        if (q + 3 < c1) fc2_item(w2D, s2D, q + 3 - c0);
-        load_fc2(d, min(q + 7, last2), w2D, s2D);
+        fc2_item(w2A, s2A, b2A, z2A, q - c0);
+        load_fc2(d, min(q + 4, last2), w2A, s2A, b2A, z2A);
+        if (q + 1 < c1) fc2_item(w2B, s2B, b2B, z2B, q + 1 - c0);
+        load_fc2(d, min(q + 5, last2), w2B, s2B, b2B, z2B);
+        if (q + 2 < c1) fc2_item(w2C, s2C, b2C, z2C, q + 2 - c0);
+        load_fc2(d, min(q + 6, last2), w2C, s2C, b2C, z2C);
+        if (q + 3 < c1) fc2_item(w2D, s2D, b2D, z2D, q + 3 - c0);
+        load_fc2(d, min(q + 7, last2), w2D, s2D, b2D, z2D);
       }
       // write this chunk's y (coalesced along m per token)
       const int nm = 8 * (c1 - c0);
@@ -617,14 +677,15 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
 namespace {
 
 template <int BITS, int U1, int U2>
-const void* fused_fn() {
-  return reinterpret_cast<const void*>(&decode_fused_kernel<BITS, U1, U2>);
+const void* fused_fn(bool ex) {
+  return ex ? reinterpret_cast<const void*>(&decode_fused_kernel<BITS, U1, U2, true>)
+            : reinterpret_cast<const void*>(&decode_fused_kernel<BITS, U1, U2, false>);
 }
 
 template <int BITS>
-const void* fused_fn_bits(int u1, int u2) {
+const void* fused_fn_bits(int u1, int u2, bool ex) {
 #define QMOE_FUSED_CASE(A, B) \
-  if (u1 == A && u2 == B) return fused_fn<BITS, A, B>();
+  if (u1 == A && u2 == B) return fused_fn<BITS, A, B>(ex);
   QMOE_FUSED_CASE(1, 1)
   QMOE_FUSED_CASE(1, 2)
   QMOE_FUSED_CASE(2, 1)
@@ -646,19 +707,26 @@ int fused_u2(const Layer& L) {
   return nkb <= 8 ? 1 : nkb <= 16 ? 2 : nkb <= 24 ? 3 : nkb <= 32 ? 4 : 0;
 }
 
+bool fused_extras(const Layer& L) {
+  return L.fc1_bias || L.fc2_bias || L.fc1_zp || L.fc2_zp;
+}
+
 const void* fused_kernel_for(const Layer& L) {
   const int u1 = fused_u1(L), u2 = fused_u2(L);
+  const bool ex = fused_extras(L);
   switch (L.bits) {
-    case 4: return fused_fn_bits<4>(u1, u2);
-    case 3: return fused_fn_bits<3>(u1, u2);
-    default: return fused_fn_bits<2>(u1, u2);
+    case 4: return fused_fn_bits<4>(u1, u2, ex);
+    case 3: return fused_fn_bits<3>(u1, u2, ex);
+    default: return fused_fn_bits<2>(u1, u2, ex);
   }
 }
 
 }  // namespace
 
 bool fused_decode_supported(const Layer& L) {
-  return L.act_bf16 && !L.fc1_bias && !L.fc2_bias && !L.fc1_zp && !L.fc2_zp && fused_u1(L) > 0 &&
+  // (with biases or zero-point tensors, I > 768 runs the split decode: that
+  // instance would keep its extra operands in scratch memory)
+  return L.act_bf16 && fused_u1(L) > 0 && (!fused_extras(L) || fused_u2(L) <= 3) &&
          fused_u2(L) > 0 &&
          L.H % 8 == 0 && L.I % 2 == 0 &&
          L.E <= kFusedMaxExperts && L.k <= kMaxTopK && fused_kernel_for(L) != nullptr;
@@ -720,6 +788,10 @@ hipError_t launch_decode_fused(const Layer& L, const void* x, const void* logits
   fa.rb2 = L.fc2_row_bytes;
   fa.nb1 = L.fc1_nblk;
   fa.nb2 = L.fc2_nblk;
+  fa.b1 = static_cast<const uint16_t*>(L.fc1_bias);
+  fa.b2 = static_cast<const uint16_t*>(L.fc2_bias);
+  fa.z1 = L.fc1_zp;
+  fa.z2 = L.fc2_zp;
   fa.ws_ids = reinterpret_cast<int32_t*>(ws + W.topk_id);
   fa.ws_w = reinterpret_cast<float*>(ws + W.topk_w);
   char* xb = static_cast<char*>(xbuf);

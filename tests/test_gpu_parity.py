@@ -459,8 +459,9 @@ def test_three_dimensional_input():
                                        ("decode", 12, False), ("int3", 300, False),
                                        ("prefill", 300, True), ("tiny", 4, False), ("f32", 45, False)])
 def test_biases_parity(name, T, il):
-    """Optional FC1/FC2 biases in the activation dtype, on the split decode
-    (which layers with a bias take for T <= 4) and on the prefill path, with
+    """Optional FC1/FC2 biases in the activation dtype, on the decode (the
+    fused kernel for bf16 layers, the split decode otherwise) and on the
+    prefill path, with
     block and interleaved FC1 rows: the output matches the oracle given the
     same biases, and differs from the run without them."""
     if name == "f32":
@@ -488,9 +489,10 @@ def test_biases_parity(name, T, il):
 @pytest.mark.parametrize("name,T", [("decode", 4), ("decode", 300), ("int3", 67), ("stack", 129),
                                     ("tiny", 4), ("f32", 45)])
 def test_zero_point_tensors_parity(name, T):
-    """Per-block zero-point tensors in FC1 and FC2, on the split decode (which
-    such layers take for T <= 4) and the prefill path, every format and both
-    activation dtypes: the output matches the oracle given the same tensors."""
+    """Per-block zero-point tensors in FC1 and FC2, on the decode (the fused
+    kernel for bf16 layers, the split decode otherwise) and the prefill path,
+    every format and both activation dtypes: the output matches the oracle
+    given the same tensors."""
     if name == "f32":
         wl = qi.make_layer(small_spec(4, 32, act="f32", hidden=192, inter=96), T=T, seed=5)
     else:
@@ -505,18 +507,53 @@ def test_zero_point_tensors_parity(name, T):
     assert rep.ok, rep
 
 
+@pytest.mark.parametrize("name,T,bias,zps", [("decode", 4, True, True), ("decode", 1, True, False),
+                                             ("int3", 4, False, True), ("stack", 2, True, True)])
+def test_fused_decode_with_extras_matches_split(name, T, bias, zps):
+    """Layers with biases or zero-point tensors run the fused decode's instance
+    that loads them; it computes the same layer as the two-kernel decode (fp32
+    throughout, different summation orders), and both match the oracle."""
+    wl = qi.make_workload(name, T=T)
+    spec = wl.spec
+    rng = np.random.default_rng(T + 11)
+    b1 = b2 = z1 = z2 = None
+    if bias:
+        b1 = torch.from_numpy(rng.standard_normal((spec.num_experts, 2 * spec.inter)) * 0.25).to(torch.bfloat16)
+        b2 = torch.from_numpy(rng.standard_normal((spec.num_experts, spec.hidden)) * 0.1).to(torch.bfloat16)
+    if zps:
+        z1, z2 = random_zero_points(wl, T)
+    kw = dict(fc1_bias=b1, fc2_bias=b2, fc1_zero_points=z1, fc2_zero_points=z2)
+    say(f"fused decode with extras {name} T={T} bias={bias} zps={zps}")
+    a, _ = run(layer_for(wl, 16, **kw), wl.tokens.x, wl.tokens.logits)
+    with _env(QMOE_FORCE_PATH="decode_split"):
+        ls = layer_for(wl, 16, **kw)
+    b, _ = run(ls, wl.tokens.x, wl.tokens.logits)
+    ref = oracle.forward(oracle.Layer.from_spec(spec), wl.tokens.x, wl.tokens.logits, wl.weights,
+                         fc1_bias=b1, fc2_bias=b2, fc1_zero_points=z1, fc2_zero_points=z2)
+    for out in (a, b):
+        rep = compare(out, ref)
+        assert rep.ok, rep
+    d = (a.float() - b.float()).abs().max().item()
+    scale = a.float().abs().max().item()
+    assert d <= 2 ** -7 * scale, (d, scale)
+
+
 @pytest.mark.parametrize("T", [3, 200])
 def test_zero_point_tensor_of_the_scalar_is_bitwise_same(T):
     """A zero-point tensor filled with the layer's scalar zero point gives the
-    output of the scalar zero point bit for bit (split decode and prefill)."""
+    output of the scalar zero point bit for bit, on each path: the fused and
+    the split decode (T <= 4) and the prefill."""
     wl = qi.make_workload("decode", T=T)
     z1 = np.full(wl.weights.fc1_scales.shape, wl.spec.zero_point, np.uint8)
     z2 = np.full(wl.weights.fc2_scales.shape, wl.spec.zero_point, np.uint8)
-    with _env(**({"QMOE_FORCE_PATH": "decode_split"} if T <= 4 else {})):
-        a, _ = run(layer_for(wl, max(T, 8)), wl.tokens.x, wl.tokens.logits)
-    b, _ = run(layer_for(wl, max(T, 8), fc1_zero_points=z1, fc2_zero_points=z2), wl.tokens.x,
-               wl.tokens.logits)
-    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    for force in ((None, "decode_split") if T <= 4 else (None,)):
+        with _env(**({"QMOE_FORCE_PATH": force} if force else {})):
+            la = layer_for(wl, max(T, 8))
+            lb = layer_for(wl, max(T, 8), fc1_zero_points=z1, fc2_zero_points=z2)
+        a, _ = run(la, wl.tokens.x, wl.tokens.logits)
+        b, _ = run(lb, wl.tokens.x, wl.tokens.logits)
+        say(f"scalar zero point vs tensor T={T} path={force or 'default'}")
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), force
 
 
 @pytest.mark.parametrize("T,extras", [(1, False), (4, False), (4, True), (37, False), (300, True)])
