@@ -1,4 +1,4 @@
-// Fused decode path (1..4 tokens, bf16 activations): one kernel launch with
+// Fused decode path (1..4 tokens, bf16 or fp16 activations): one kernel launch with
 // no grid-wide barrier.
 //
 // Layers with FC1/FC2 biases or per-block zero-point tensors run an instance
@@ -87,6 +87,48 @@ __device__ __forceinline__ f32x4_t mfma4(uint32_t a0, uint32_t a1, uint32_t b0, 
   const short4_t a = __builtin_bit_cast(short4_t, u32x2_t{a0, a1});
   const short4_t b = __builtin_bit_cast(short4_t, u32x2_t{b0, b1});
   return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// fp16 activations: the same 4x4x4 block product on fp16 operands (x is exact
+// in fp16, and so is 1 + q/128 for q < 128).
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4_t mfma4_f16(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1,
+                                             f32x4_t c) {
+  const half4_t a = __builtin_bit_cast(half4_t, u32x2_t{a0, a1});
+  const half4_t b = __builtin_bit_cast(half4_t, u32x2_t{b0, b1});
+  return __builtin_amdgcn_mfma_f32_4x4x4f16(a, b, c, 0, 0, 0);
+}
+
+// A 16-bit activation value (bf16, or fp16 when F16) as fp32, exactly.
+template <bool F16>
+__device__ __forceinline__ float act16(uint32_t bits) {
+  return F16 ? half_to_f32(static_cast<uint16_t>(bits)) : bf16_to_f32(bits);
+}
+// The logit a routing key was made from (logit_key orders the 16-bit
+// patterns of bf16 and fp16 alike: both are sign-magnitude).
+template <bool F16>
+__device__ __forceinline__ float key_value(uint32_t key) {
+  const uint32_t ord = key >> 16;
+  return act16<F16>((ord & 0x8000u) ? (ord & 0x7FFFu) : (~ord & 0xFFFFu));
+}
+
+// Pair p of a unit as two fp16 values 1 + q/128: the code sits at bit 3 of
+// the fp16 mantissa of 1.0 (0x3C00); same pairing as unit_pair.
+template <int BITS>
+__device__ __forceinline__ uint32_t unit_pair_f16(const UnitWords<BITS>& u, int p) {
+  if constexpr (BITS == 4) {
+    const uint32_t w = u.w[p >> 2];
+    const int sh = 4 * (p & 3);
+    const uint32_t v = sh >= 3 ? (w >> (sh - 3)) : (w << (3 - sh));
+    return (v & 0x00780078u) | 0x3C003C00u;
+  } else if constexpr (BITS == 2) {
+    const uint32_t w = u.w[p >> 3];
+    const int sh = 2 * (p & 7);
+    const uint32_t v = sh >= 3 ? (w >> (sh - 3)) : (w << (3 - sh));
+    return (v & 0x00180018u) | 0x3C003C00u;
+  } else {
+    return ((unit_code<3>(u, 2 * p) | (unit_code<3>(u, 2 * p + 1) << 16)) << 3) | 0x3C003C00u;
+  }
 }
 
 // Exchange entries: {fp32 value (low word), epoch (high word)}.
@@ -186,7 +228,9 @@ struct FusedArgs {
 // point of each of its quant blocks; the block correction becomes
 // (128 + zp) * sum(x) per block, and the bias is added to the row's sum
 // before SwiGLU (FC1) or before the combine (FC2).
-template <int BITS, int U1, int U2, bool EX>
+// F16: fp16 x, logits, biases and out (with EX): FC1 runs on fp16 operands;
+// FC2's operands are built from the fp32 h as in the bf16 case.
+template <int BITS, int U1, int U2, bool EX, bool F16>
 __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a) {
   __shared__ FusedLds S;
   // wave-uniform values go through readfirstlane so the compiler keeps them
@@ -243,12 +287,12 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
 #pragma unroll
       for (int c = 0; c < kKeySlots; ++c) keys[c] = (keys[c] == b) ? 0u : keys[c];
     }
-    const float ex = (lane < k) ? expf(key_logit(mine) - key_logit(first)) : 0.0f;
+    const float ex = (lane < k) ? expf(key_value<F16>(mine) - key_value<F16>(first)) : 0.0f;
     float all = 0.0f;   // sum over all experts (weights without normalization)
     if (!a.normalize)
 #pragma unroll
       for (int c = 0; c < kKeySlots; ++c)
-        if (lane + kWave * c < E) all += expf(bf16_to_f32(lg[c]) - key_logit(first));
+        if (lane + kWave * c < E) all += expf(act16<F16>(lg[c]) - key_value<F16>(first));
     const float sum = wave_sum(a.normalize ? ex : all);
     if (lane < k) {
       const int e = key_to_expert(mine);
@@ -401,7 +445,7 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
     }
     float sum = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) sum += bf16_to_f32((v[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+    for (int i = 0; i < 32; ++i) sum += act16<F16>((v[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
 #pragma unroll
     for (int p = 0; p < 16; ++p) {
       const int pa = pair_a(BITS, p), pb = pair_b(BITS, p);
@@ -429,10 +473,12 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
     for (int c = 0; c < U1; ++c) {
       uint32_t wp[16];
 #pragma unroll
-      for (int p = 0; p < 16; ++p) wp[p] = unit_pair<BITS>(wv[c], p);
+      for (int p = 0; p < 16; ++p) wp[p] = F16 ? unit_pair_f16<BITS>(wv[c], p) : unit_pair<BITS>(wv[c], p);
       f32x4_t dv = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int m = 0; m < 8; ++m) dv = mfma4(xp[c][2 * m], xp[c][2 * m + 1], wp[2 * m], wp[2 * m + 1], dv);
+      for (int m = 0; m < 8; ++m)
+        dv = F16 ? mfma4_f16(xp[c][2 * m], xp[c][2 * m + 1], wp[2 * m], wp[2 * m + 1], dv)
+                 : mfma4(xp[c][2 * m], xp[c][2 * m + 1], wp[2 * m], wp[2 * m + 1], dv);
       const float s = (blk + 16 * c) < nkb1 ? half_to_f32(static_cast<uint16_t>(sc[c])) : 0.0f;
       const float s128 = 128.0f * s;
       // (with EX: the same product (128 + zp) * sum(x) as the scalar path
@@ -448,7 +494,7 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
     for (int t = 0; t < kDecodeMaxTokens; ++t) acc[t] = half_pair_sum(row_pair_sum(row_class_sum(acc[t])));
     if (EX && a.b1) {
       // every lane now holds the total of its row: add that row's bias
-      const float b = bf16_to_f32(bv);
+      const float b = act16<F16>(bv);
 #pragma unroll
       for (int t = 0; t < kDecodeMaxTokens; ++t) acc[t] += b;
     }
@@ -603,7 +649,7 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
       for (int t = 0; t < kDecodeMaxTokens; ++t) acc[t] = row_pair_sum(row_class_sum(acc[t]));
       if (EX && a.b2) {
         // lanes holding a row's total add that row's bias
-        const float b = bf16_to_f32(bv);
+        const float b = act16<F16>(bv);
 #pragma unroll
         for (int t = 0; t < kDecodeMaxTokens; ++t) acc[t] += b;
       }
@@ -669,21 +715,25 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
         for (int j = 0; j < 8; ++j)
           if (j0 + j < k) o = fmaf(S.w[t * k + j0 + j], tag_value(v[j]), o);
       }
-      a.out[static_cast<int64_t>(t) * H + m] = static_cast<uint16_t>(f32_to_bf16(o));
+      a.out[static_cast<int64_t>(t) * H + m] =
+          F16 ? __builtin_bit_cast(uint16_t, static_cast<_Float16>(o)) : static_cast<uint16_t>(f32_to_bf16(o));
     }
   }
 }
 
 namespace {
 
+// variant 0: bf16; 1: bf16 with biases or zero-point tensors; 2: fp16 (with
+// the same extras machinery, which costs nothing when a layer has none)
 template <int BITS, int U1, int U2>
-const void* fused_fn(bool ex) {
-  return ex ? reinterpret_cast<const void*>(&decode_fused_kernel<BITS, U1, U2, true>)
-            : reinterpret_cast<const void*>(&decode_fused_kernel<BITS, U1, U2, false>);
+const void* fused_fn(int variant) {
+  if (variant == 2) return reinterpret_cast<const void*>(&decode_fused_kernel<BITS, U1, U2, true, true>);
+  if (variant == 1) return reinterpret_cast<const void*>(&decode_fused_kernel<BITS, U1, U2, true, false>);
+  return reinterpret_cast<const void*>(&decode_fused_kernel<BITS, U1, U2, false, false>);
 }
 
 template <int BITS>
-const void* fused_fn_bits(int u1, int u2, bool ex) {
+const void* fused_fn_bits(int u1, int u2, int ex) {
 #define QMOE_FUSED_CASE(A, B) \
   if (u1 == A && u2 == B) return fused_fn<BITS, A, B>(ex);
   QMOE_FUSED_CASE(1, 1)
@@ -713,7 +763,7 @@ bool fused_extras(const Layer& L) {
 
 const void* fused_kernel_for(const Layer& L) {
   const int u1 = fused_u1(L), u2 = fused_u2(L);
-  const bool ex = fused_extras(L);
+  const int ex = L.act == kActF16 ? 2 : fused_extras(L) ? 1 : 0;
   switch (L.bits) {
     case 4: return fused_fn_bits<4>(u1, u2, ex);
     case 3: return fused_fn_bits<3>(u1, u2, ex);
@@ -726,7 +776,8 @@ const void* fused_kernel_for(const Layer& L) {
 bool fused_decode_supported(const Layer& L) {
   // (with biases or zero-point tensors, I > 768 runs the split decode: that
   // instance would keep its extra operands in scratch memory)
-  return L.act_bf16 && fused_u1(L) > 0 && (!fused_extras(L) || fused_u2(L) <= 3) &&
+  const bool ex = fused_extras(L) || L.act == kActF16;
+  return (L.act_bf16 || L.act == kActF16) && fused_u1(L) > 0 && (!ex || fused_u2(L) <= 3) &&
          fused_u2(L) > 0 &&
          L.H % 8 == 0 && L.I % 2 == 0 &&
          L.E <= kFusedMaxExperts && L.k <= kMaxTopK && fused_kernel_for(L) != nullptr;

@@ -559,7 +559,7 @@ def test_zero_point_tensor_of_the_scalar_is_bitwise_same(T):
 @pytest.mark.parametrize("T,extras", [(1, False), (4, False), (4, True), (37, False), (300, True)])
 def test_fp16_activations_parity(T, extras):
     """fp16 x, logits and out on the Qwen3-shaped INT4 layer: T <= 4 runs the
-    split decode (x widened to fp32), larger T the prefill path (x staged as
+    fused decode on fp16 operands, larger T the prefill path (x staged as
     bf16 once per call). The routing of the fp16 logits is bit-exact and the
     output (rounded once to fp16) matches the oracle; with extras, fp16
     biases and unnormalized routing too."""
@@ -581,6 +581,38 @@ def test_fp16_activations_parity(T, extras):
     rep = compare(out, ref)
     say(f"fp16 activations T={T} extras={extras}: {rep}")
     assert rep.ok, rep
+
+
+@pytest.mark.parametrize("name,T,extras", [("decode", 4, False), ("decode", 1, True), ("int3", 3, False),
+                                            ("stack", 4, True)])
+def test_fused_decode_fp16_matches_split(name, T, extras):
+    """fp16 layers run the fused decode's fp16 instance (FC1 on fp16 operands);
+    it computes the same layer as the two-kernel decode, which widens x to
+    fp32, and both match the oracle. With extras: fp16 biases and zero-point
+    tensors as well."""
+    spec = qi.spec_with(qi.make_workload(name, T=1).spec, act_dtype="f16")
+    wl = qi.make_layer(spec, T=T, seed=61 + T)
+    b1 = b2 = z1 = z2 = None
+    if extras:
+        rng = np.random.default_rng(T + 3)
+        b1 = torch.from_numpy(rng.standard_normal((spec.num_experts, 2 * spec.inter)) * 0.25).half()
+        b2 = torch.from_numpy(rng.standard_normal((spec.num_experts, spec.hidden)) * 0.1).half()
+        z1, z2 = random_zero_points(wl, T)
+    kw = dict(fc1_bias=b1, fc2_bias=b2, fc1_zero_points=z1, fc2_zero_points=z2)
+    say(f"fused fp16 decode {name} T={T} extras={extras}")
+    a, _ = run(layer_for(wl, 16, **kw), wl.tokens.x, wl.tokens.logits)
+    with _env(QMOE_FORCE_PATH="decode_split"):
+        ls = layer_for(wl, 16, **kw)
+    b, _ = run(ls, wl.tokens.x, wl.tokens.logits)
+    assert a.dtype == torch.float16 and b.dtype == torch.float16
+    ref = oracle.forward(oracle.Layer.from_spec(spec), wl.tokens.x, wl.tokens.logits, wl.weights,
+                         fc1_bias=b1, fc2_bias=b2, fc1_zero_points=z1, fc2_zero_points=z2)
+    for out in (a, b):
+        rep = compare(out, ref)
+        assert rep.ok, rep
+    d = (a.float() - b.float()).abs().max().item()
+    scale = a.float().abs().max().item()
+    assert d <= 2 ** -9 * scale, (d, scale)
 
 
 # ------------------------------------------------------------------ properties
