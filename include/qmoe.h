@@ -100,14 +100,16 @@ typedef struct qmoe_weights {
      * added to each FC1 row's output (gate and up rows, in their storage
      * order) before SwiGLU, fc2_bias [E, H] to the expert's output before the
      * routing-weighted combine ("[CUDA] Add INT4 and INT3 QMoE CPU/GPU
-     * offload support", commit notes). Layers with a bias run the split
-     * decode for T <= 4, not the fused one. */
+     * offload support", commit notes). For T <= 4 such layers run the fused
+     * decode (its instance that also loads biases and zero points) when
+     * inter <= 768, else the split decode. */
     const void *fc1_bias;
     const void *fc2_bias;
     /* Optional zero-point tensors, or NULL: one unsigned code per row and
      * quant block (uint8 [E, 2I, H/bs] and [E, H, I/bs], laid out like the
      * scales) replacing the scalar zero_point, so W = (q - zp[n][k/bs]) * s.
-     * Layers with one run the split decode for T <= 4, not the fused one. */
+     * For T <= 4 such layers run the fused decode when inter <= 768, else
+     * the split decode. */
     const void *fc1_zero_points;
     const void *fc2_zero_points;
 } qmoe_weights;

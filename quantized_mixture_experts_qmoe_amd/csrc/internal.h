@@ -78,8 +78,9 @@ hipError_t launch_prefill(const Layer& L, const void* x, void* out, int64_t T, c
                           const Workspace& W, hipStream_t s);
 hipError_t launch_decode(const Layer& L, const void* x, const void* logits, void* out, int64_t T,
                          char* ws, const Workspace& W, hipStream_t s);
-// Fused single-launch decode (bf16 activations, H <= 2048, I <= 1024,
-// E <= 256). Its workgroups exchange h and y through a per-handle device
+// Fused single-launch decode (bf16 or fp16 activations, H <= 2048,
+// I <= 1024, or I <= 768 with fp16, biases or zero-point tensors; E <= 256).
+// Its workgroups exchange h and y through a per-handle device
 // buffer of epoch-tagged entries (fused_exchange_bytes, zeroed at create and
 // by clear_exchange whenever the epoch counter wraps); every call passes a
 // new nonzero epoch.

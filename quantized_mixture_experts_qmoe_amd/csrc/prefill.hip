@@ -161,6 +161,10 @@ void grouped_gemm_kernel(
     a_ptr[q] = a_src + src_row * a_ld + a_chunk;
   }
 
+  // a wave whose 32 A rows all lie past the tile's routes neither loads nor
+  // stores them: no stored output row reads them (row m of a product depends
+  // on row m of A only)
+  const bool a_live = 128 * grp + 32 * gw < nrows;
   uint4 ra0, ra1, ra2, ra3;
   UnitWords<BITS> rb;
   uint16_t rs;      // raw fp16 scale of this stage's B unit
@@ -169,10 +173,12 @@ void grouped_gemm_kernel(
   auto load_stage = [&](int st) {
     const int k0 = st * kKT;
     const int ka = (k0 + a_chunk < K) ? k0 : 0;
-    ra0 = *reinterpret_cast<const uint4*>(a_ptr[0] + ka);
-    ra1 = *reinterpret_cast<const uint4*>(a_ptr[1] + ka);
-    ra2 = *reinterpret_cast<const uint4*>(a_ptr[2] + ka);
-    ra3 = *reinterpret_cast<const uint4*>(a_ptr[3] + ka);
+    if (a_live) {
+      ra0 = *reinterpret_cast<const uint4*>(a_ptr[0] + ka);
+      ra1 = *reinterpret_cast<const uint4*>(a_ptr[1] + ka);
+      ra2 = *reinterpret_cast<const uint4*>(a_ptr[2] + ka);
+      ra3 = *reinterpret_cast<const uint4*>(a_ptr[3] + ka);
+    }
     const int kk = k0 + 32 * b_kq;
     const int kb = (kk < K) ? kk : 0;
     rb = load_unit<BITS>(b_ptr + (kb / 32) * (4 * BITS));
@@ -183,11 +189,13 @@ void grouped_gemm_kernel(
     if constexpr (HAS_ZP) rz = z_ptr[kb >> bs_shift];
   };
   auto store_stage = [&](int buf) {
-    uint16_t* ad = &As[buf][a_row0 * kLdsStride + a_chunk];
-    *reinterpret_cast<uint4*>(ad) = ra0;
-    *reinterpret_cast<uint4*>(ad + 8 * kLdsStride) = ra1;
-    *reinterpret_cast<uint4*>(ad + 16 * kLdsStride) = ra2;
-    *reinterpret_cast<uint4*>(ad + 24 * kLdsStride) = ra3;
+    if (a_live) {
+      uint16_t* ad = &As[buf][a_row0 * kLdsStride + a_chunk];
+      *reinterpret_cast<uint4*>(ad) = ra0;
+      *reinterpret_cast<uint4*>(ad + 8 * kLdsStride) = ra1;
+      *reinterpret_cast<uint4*>(ad + 16 * kLdsStride) = ra2;
+      *reinterpret_cast<uint4*>(ad + 24 * kLdsStride) = ra3;
+    }
     uint32_t pairs[16];
     {
       const float sc = rpast ? 0.0f : half_to_f32(rs);
