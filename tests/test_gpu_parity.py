@@ -355,6 +355,50 @@ def test_grouped_decode_parity(name, T):
     check_decode(wl, layer_for(wl, 32))
 
 
+@pytest.mark.parametrize("T,f16,extras", [(9, True, False), (7, False, True), (13, True, True)])
+def test_grouped_decode_fp16_and_extras(T, f16, extras):
+    """Batches of 5..24 tokens of fp16 layers or layers with biases and
+    zero-point tensors run the fused decode's matching instance once per group
+    of up to four tokens: every output row matches the oracle."""
+    spec = qi.QWEN3_INT4 if not f16 else qi.spec_with(qi.QWEN3_INT4, act_dtype="f16")
+    wl = qi.make_layer(spec, T=T, seed=71 + T)
+    dt = torch.float16 if f16 else torch.bfloat16
+    b1 = b2 = z1 = z2 = None
+    if extras:
+        rng = np.random.default_rng(T + 5)
+        b1 = torch.from_numpy(rng.standard_normal((spec.num_experts, 2 * spec.inter)) * 0.25).to(dt)
+        b2 = torch.from_numpy(rng.standard_normal((spec.num_experts, spec.hidden)) * 0.1).to(dt)
+        z1, z2 = random_zero_points(wl, T)
+    say(f"grouped fused decode T={T} f16={f16} extras={extras}")
+    out, _ = run(layer_for(wl, 32, fc1_bias=b1, fc2_bias=b2, fc1_zero_points=z1, fc2_zero_points=z2),
+                 wl.tokens.x, wl.tokens.logits)
+    assert out.dtype == dt
+    ref = oracle.forward(oracle.Layer.from_spec(spec), wl.tokens.x, wl.tokens.logits, wl.weights,
+                         fc1_bias=b1, fc2_bias=b2, fc1_zero_points=z1, fc2_zero_points=z2)
+    rep = compare(out, ref)
+    assert rep.ok, rep
+
+
+@pytest.mark.parametrize("f16", [False, True])
+def test_wide_inter_with_extras_takes_split_decode(f16):
+    """With inter > 768, layers with fp16 activations or biases take the split
+    decode (the fused instances for them would spill); the result still
+    matches the oracle."""
+    spec = small_spec(4, 32, act="f16" if f16 else "bf16", hidden=512, inter=1024, num_experts=16,
+                      top_k=4)
+    wl = qi.make_layer(spec, T=4, seed=83)
+    dt = torch.float16 if f16 else torch.bfloat16
+    rng = np.random.default_rng(9)
+    b1 = torch.from_numpy(rng.standard_normal((spec.num_experts, 2 * spec.inter)) * 0.25).to(dt)
+    b2 = torch.from_numpy(rng.standard_normal((spec.num_experts, spec.hidden)) * 0.1).to(dt)
+    out, _ = run(layer_for(wl, 8, fc1_bias=b1, fc2_bias=b2), wl.tokens.x, wl.tokens.logits)
+    ref = oracle.forward(oracle.Layer.from_spec(spec), wl.tokens.x, wl.tokens.logits, wl.weights,
+                         fc1_bias=b1, fc2_bias=b2)
+    rep = compare(out, ref)
+    say(f"wide inter with biases f16={f16}: {rep}")
+    assert rep.ok, rep
+
+
 def test_grouped_decode_matches_prefill():
     """The grouped decode and the grouped GEMMs compute the same 11-token
     layer (fp32 h against bf16 h): both meet the tolerance and agree per
