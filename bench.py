@@ -339,18 +339,38 @@ def bench_stack(T: int, steps: int, warmup: int):
     return res
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(n_tokens: int):
-    """The oracle on a bounded sample of decode tokens, all host cores."""
+    """The oracle on a bounded sample of decode tokens: all host cores (the
+    reported value), and one thread on an eighth of the sample."""
     import oracle
     wl = qi.make_workload("decode", T=n_tokens)
     threads = oracle.default_threads()
+    layer = oracle.Layer.from_spec(wl.spec)
     t0 = time.perf_counter()
-    oracle.forward(oracle.Layer.from_spec(wl.spec), wl.tokens.x, wl.tokens.logits, wl.weights,
-                   nthreads=threads)
+    oracle.forward(layer, wl.tokens.x, wl.tokens.logits, wl.weights, nthreads=threads)
     dt = time.perf_counter() - t0
+    n1 = max(1, n_tokens // 8)
+    t0 = time.perf_counter()
+    oracle.forward(layer, wl.tokens.x[:n1], wl.tokens.logits[:n1], wl.weights, nthreads=1)
+    dt1 = time.perf_counter() - t0
+    log(f"[bench] cpu baseline: {threads} threads {n_tokens / dt:.1f} tokens/s, "
+        f"1 thread {n1 / dt1:.2f} tokens/s ({cpu_model()})")
     return {"value": n_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{n_tokens} tokens of the decode workload (Qwen3-30B-A3B-shaped INT4 bs32 "
-                      f"layer, uniform routing), {dt:.1f} s wall on {threads} threads"}
+                      f"layer, uniform routing), {dt:.1f} s wall on {threads} threads",
+            "single_thread": {"value": n1 / dt1, "unit": "tokens/s", "sample": f"{n1} tokens"},
+            "cpu_model": cpu_model()}
 
 
 def main():
