@@ -659,6 +659,34 @@ def test_fused_decode_fp16_matches_split(name, T, extras):
     assert d <= 2 ** -9 * scale, (d, scale)
 
 
+@pytest.mark.parametrize("name,T,force", [("decode", 4, None), ("decode", 9, None), ("decode", 300, None),
+                                           ("tiny", 4, None), ("decode", 4, "decode_split")])
+def test_nan_and_inf_inputs_stay_local(name, T, force):
+    """NaN and infinite values in x or the logits of some tokens (the pages
+    leave their result open): the call completes, every token still gets k
+    distinct valid experts, and the tokens with clean inputs match the oracle
+    (each token's output depends on its own inputs only)."""
+    wl = qi.make_workload(name, T=T)
+    E, k = wl.spec.num_experts, wl.spec.top_k
+    x, lg = wl.tokens.x.clone(), wl.tokens.logits.clone()
+    x[1, 5] = float("nan")
+    lg[2, 3 % E] = float("inf")
+    lg[0, 1 % E] = float("nan")
+    dirty = [0, 1, 2]
+    say(f"nan/inf inputs {name} T={T} path={force or 'default'}")
+    with _env(**({"QMOE_FORCE_PATH": force} if force else {})):
+        layer = layer_for(wl, max(T, 16))
+    out, ws = run(layer, x, lg)
+    ids, _ = layer.routing_from_workspace(T, ws)
+    ids = ids.cpu().numpy()
+    assert ids.min() >= 0 and ids.max() < E
+    assert all(len(set(row)) == k for row in ids.tolist())
+    clean = [t for t in range(T) if t not in dirty]
+    ref = oracle.forward(oracle.Layer.from_spec(wl.spec), x[clean], lg[clean], wl.weights)
+    rep = compare(out[torch.as_tensor(clean, device=DEV)], ref)
+    assert rep.ok, rep
+
+
 # ------------------------------------------------------------------ properties
 
 def test_decode_and_prefill_agree():
