@@ -11,9 +11,14 @@
 //        sorted order.
 //   FC2: A = h rows of the tile (bf16), B = the expert's FC2 rows
 //        [n0, n0+256) dequantized into LDS; the epilogue stores fp32 y
-//        [R, H] in sorted order.
+//        [R, H] in sorted order (non-temporal: the combine reads it once).
+// Both epilogues stage each wave's results in LDS, 16 rows at a time, and
+// write whole 16-byte row segments.
 // The tall tile shares each dequantized weight among 256 rows; a wave whose
-// 64 rows all lie past the expert's last route skips its matrix work.
+// 64 rows all lie past the expert's last route skips its matrix work, and a
+// wave whose 32 rows of the A share do neither loads nor stores them. A tile
+// of at most 128 rows runs in half mode: both wave groups compute rows
+// 0-127, each for half of the columns.
 // The K loop runs in stages of 64 with two LDS buffers, ping-pong style: the
 // waves form two groups of four (rows 0-127 and 128-255 of the tile) that
 // run half a stage apart. In each phase between two barriers one group runs
