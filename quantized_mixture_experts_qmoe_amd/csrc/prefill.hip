@@ -16,7 +16,8 @@
 // write whole 16-byte row segments.
 // The tall tile shares each dequantized weight among 256 rows; a wave whose
 // 64 rows all lie past the expert's last route skips its matrix work, and a
-// wave whose 32 rows of the A share do neither loads nor stores them. A tile
+// wave whose 32 rows of the A share all lie past it neither loads nor stores
+// them. A tile
 // of at most 128 rows runs in half mode: both wave groups compute rows
 // 0-127, each for half of the columns.
 // The K loop runs in stages of 64 with two LDS buffers, ping-pong style: the
