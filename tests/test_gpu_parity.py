@@ -355,6 +355,17 @@ def test_grouped_decode_parity(name, T):
     check_decode(wl, layer_for(wl, 32))
 
 
+@pytest.mark.parametrize("T,k", [(8, 10), (8, 16), (3, 10)])
+def test_speculative_decode_shape(T, k):
+    """Eight draft tokens with top-10 routing (80 routes), the speculative
+    decode shape the pages measure, and the largest top-k (16): the grouped
+    fused decode's routing is bit-exact and the output matches the oracle."""
+    spec = qi.spec_with(qi.QWEN3_INT4, top_k=k)
+    wl = qi.make_layer(spec, T=T, seed=91 + T + k)
+    say(f"speculative decode shape T={T} k={k}")
+    check_decode(wl, layer_for(wl, 32))
+
+
 @pytest.mark.parametrize("T,f16,extras", [(9, True, False), (7, False, True), (13, True, True)])
 def test_grouped_decode_fp16_and_extras(T, f16, extras):
     """Batches of 5..24 tokens of fp16 layers or layers with biases and
