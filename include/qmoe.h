@@ -191,6 +191,23 @@ qmoe_status qmoe_workspace_routing(const qmoe_handle *handle, int64_t num_tokens
                                    size_t *topk_id_offset, size_t *topk_w_offset);
 
 /*
+ * Error bits of the fused decode's bounded waits. A workgroup of the fused
+ * decode that waits for another's FC1 result (h) or FC2 result (y) gives up
+ * after a fixed number of polls, sets a bit and goes on, so a stalled
+ * producer cannot hang the device. bit 0: an h wait ran out; bit 1: a y
+ * wait ran out. Either means some output since the last query may be wrong.
+ *
+ * The bits accumulate over every qmoe_forward call on the handle since it
+ * was created or last queried. This call waits for `stream` (the stream the
+ * forward calls ran on; NULL = the null stream) to finish, copies the bits
+ * to *bits and clears them: it is synchronous and meant for checks, not for
+ * the hot loop. A handle whose layer never takes the fused decode reports 0.
+ * Errors: QMOE_ERR_INVALID_ARG for a NULL handle or `bits`; QMOE_ERR_HIP if
+ * the synchronisation or a copy fails (*bits is then 0).
+ */
+qmoe_status qmoe_decode_errors(qmoe_handle *handle, void *stream, uint32_t *bits);
+
+/*
  * Profiling hook. When set, qmoe_forward calls fn(user, stage, name) on the
  * host right after it enqueues each kernel (stage = 1, 2, ... in launch order,
  * name = the kernel's role, a static string), and once with stage = 0 before

@@ -23,7 +23,7 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration",
 
 EXPORTS = ("qmoe_create", "qmoe_workspace_size", "qmoe_forward", "qmoe_destroy",
            "qmoe_status_string", "qmoe_route", "qmoe_dequant", "qmoe_workspace_routing",
-           "qmoe_set_stage_hook")
+           "qmoe_set_stage_hook", "qmoe_decode_errors")
 
 STAGE_FN = ctypes.CFUNCTYPE(None, ctypes.c_void_p, ctypes.c_int, ctypes.c_char_p)
 
@@ -76,8 +76,10 @@ def lib() -> ctypes.CDLL:
         L.qmoe_dequant.argtypes = [P, ctypes.c_int, i64, P, P, P]
         L.qmoe_workspace_routing.argtypes = [P, i64, ctypes.POINTER(sz), ctypes.POINTER(sz)]
         L.qmoe_set_stage_hook.argtypes = [P, STAGE_FN, P]
+        L.qmoe_decode_errors.argtypes = [P, P, ctypes.POINTER(ctypes.c_uint32)]
         for name in ("qmoe_create", "qmoe_workspace_size", "qmoe_forward", "qmoe_destroy",
-                     "qmoe_route", "qmoe_dequant", "qmoe_workspace_routing", "qmoe_set_stage_hook"):
+                     "qmoe_route", "qmoe_dequant", "qmoe_workspace_routing", "qmoe_set_stage_hook",
+                     "qmoe_decode_errors"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -238,6 +240,15 @@ class QMoELayer:
         ids = workspace[a.value:a.value + 4 * R].view(torch.int32).view(num_tokens, self.cfg.top_k)
         w = workspace[b.value:b.value + 4 * R].view(torch.float32).view(num_tokens, self.cfg.top_k)
         return ids, w
+
+    def decode_errors(self, stream: Optional[torch.cuda.Stream] = None) -> int:
+        """Error bits of the fused decode's bounded waits since the last query
+        (bit 0: an FC1 result wait ran out, bit 1: an FC2 result wait); waits
+        for the stream, then clears them. 0 means every wait was met."""
+        bits = ctypes.c_uint32()
+        _check(lib().qmoe_decode_errors(self._h, _stream(stream), ctypes.byref(bits)),
+               "qmoe_decode_errors")
+        return bits.value
 
     def set_stage_hook(self, fn):
         """fn(stage: int, name: str) runs on the host after each kernel launch of

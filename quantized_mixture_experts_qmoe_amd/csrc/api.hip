@@ -21,6 +21,7 @@ struct qmoe_handle {
   bool split_decode;      // use the two-kernel decode even where the fused one applies
   bool fused_ok;          // fused single-launch decode applies to this layer
   int fused_grid;         // resident workgroups for the fused decode
+  uint32_t spin_limit;    // fused decode wait bound in polls (0: the library default)
   uint32_t calls;         // epoch of the last fused decode call launched (0: none yet)
   void* xbuf;             // device: fused decode exchange buffer (error bits, tagged h and y)
 };
@@ -211,6 +212,7 @@ qmoe_status qmoe_create(const qmoe_config* c, const qmoe_weights* w, int device,
   h->calls = 0;
   h->fused_ok = false;
   h->fused_grid = 0;
+  h->spin_limit = 0;
   {
     DeviceGuard guard(device);
     if (!guard.ok()) { delete h; return QMOE_ERR_HIP; }
@@ -234,6 +236,13 @@ qmoe_status qmoe_create(const qmoe_config* c, const qmoe_weights* w, int device,
       // (with n = 4294967295 the first call takes the wrap path)
       const char* e0 = getenv("QMOE_FUSED_EPOCH_START");
       if (e0) h->calls = static_cast<uint32_t>(strtoul(e0, nullptr, 10));
+      // QMOE_FUSED_SPIN_LIMIT=n (n >= 1) bounds each wait at n polls, so a
+      // test can make waits run out and check that the error bits report it
+      const char* sl = getenv("QMOE_FUSED_SPIN_LIMIT");
+      if (sl) {
+        const long n = strtol(sl, nullptr, 10);
+        if (n >= 1) h->spin_limit = static_cast<uint32_t>(n);
+      }
     }
   }
   *out = h;
@@ -292,7 +301,7 @@ qmoe_status qmoe_forward(qmoe_handle* h, const void* x, const void* logits, void
         err = launch_decode_fused(h->L, static_cast<const uint16_t*>(x) + t0 * H,
                                   static_cast<const uint16_t*>(logits) + t0 * E,
                                   static_cast<uint16_t*>(out) + t0 * H, tg, base, Wg, h->xbuf, epoch,
-                                  h->fused_grid, s);
+                                  h->fused_grid, h->spin_limit, s);
         if (err == hipSuccess) h->calls = epoch;
       }
     } else {
@@ -344,6 +353,26 @@ qmoe_status qmoe_set_stage_hook(qmoe_handle* h, qmoe_stage_fn fn, void* user) {
   if (!h) return QMOE_ERR_INVALID_ARG;
   h->L.hook = fn;
   h->L.hook_user = user;
+  return QMOE_OK;
+}
+
+qmoe_status qmoe_decode_errors(qmoe_handle* h, void* stream, uint32_t* bits) {
+  if (!h || !bits) return QMOE_ERR_INVALID_ARG;
+  *bits = 0;
+  if (!h->xbuf) return QMOE_OK;
+  DeviceGuard guard(h->device);
+  if (!guard.ok()) return QMOE_ERR_HIP;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t v = 0;
+  // the error word is the first word of the exchange buffer's header
+  if (hipStreamSynchronize(s) != hipSuccess ||
+      hipMemcpy(&v, h->xbuf, sizeof v, hipMemcpyDeviceToHost) != hipSuccess)
+    return QMOE_ERR_HIP;
+  if (v != 0) {
+    const uint32_t zero = 0;
+    if (hipMemcpy(h->xbuf, &zero, sizeof zero, hipMemcpyHostToDevice) != hipSuccess) return QMOE_ERR_HIP;
+  }
+  *bits = v;
   return QMOE_OK;
 }
 

@@ -80,7 +80,7 @@ constexpr int kMaxGroups = 256;                       // output row groups of 8 
 constexpr int kMaxI32 = 32;                           // FC2 quant blocks staged (I <= 1024)
 constexpr int kCap1 = 32;                             // FC1 items buffered per wave (even)
 constexpr int kCap2 = 16;                             // FC2 items buffered per wave (multiple of 4)
-constexpr uint32_t kSpinLimit = 1u << 20;             // bounded wait for an exchange entry
+constexpr uint32_t kSpinLimit = 1u << 20;             // default bound of a wait for an exchange entry
 
 __device__ __forceinline__ f32x4_t mfma4(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1,
                                          f32x4_t c) {
@@ -220,6 +220,7 @@ struct FusedArgs {
   const uint16_t* b2;
   const uint8_t* z1;
   const uint8_t* z2;
+  uint32_t spin_limit;   // polls before a wait for an exchange entry gives up
 };
 
 // U1: FC1 quant blocks per lane (ceil(H/32 / 16)); U2: FC2 quant blocks per lane (ceil(I/32 / 8)).
@@ -560,7 +561,7 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
 #pragma unroll
           for (int q = 0; q < 4; ++q) ready = ready && tag_is(ea[q], a.epoch) && tag_is(eb[q], a.epoch);
           if (!ready) {
-            if (++spins > kSpinLimit) {
+            if (++spins > a.spin_limit) {
               atomicOr(a.err, 1u);
               break;
             }
@@ -704,7 +705,7 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
 #pragma unroll
           for (int j = 0; j < 8; ++j) ready = ready && (j0 + j >= k || tag_is(v[j], a.epoch));
           if (!ready) {
-            if (++spins > kSpinLimit) {
+            if (++spins > a.spin_limit) {
               atomicOr(a.err, 2u);
               break;
             }
@@ -817,7 +818,7 @@ hipError_t clear_exchange(const Layer& L, void* xbuf, hipStream_t s) {
 
 hipError_t launch_decode_fused(const Layer& L, const void* x, const void* logits, void* out,
                                int64_t T, char* ws, const Workspace& W, void* xbuf,
-                               uint32_t epoch, int grid, hipStream_t s) {
+                               uint32_t epoch, int grid, uint32_t spin_limit, hipStream_t s) {
   FusedArgs fa;
   fa.x = static_cast<const uint16_t*>(x);
   fa.logits = static_cast<const uint16_t*>(logits);
@@ -851,6 +852,7 @@ hipError_t launch_decode_fused(const Layer& L, const void* x, const void* logits
   fa.hx = reinterpret_cast<uint64_t*>(xb + kExchangeHeader);
   fa.yx = fa.hx + routes * static_cast<size_t>(L.I);
   fa.epoch = epoch;
+  fa.spin_limit = spin_limit ? spin_limit : kSpinLimit;
   void* args[] = {&fa};
   const hipError_t err =
       hipLaunchKernel(fused_kernel_for(L), dim3(grid), dim3(kFusedThreads), args, 0, s);

@@ -93,7 +93,7 @@ size_t fused_exchange_bytes(const Layer& L);
 hipError_t clear_exchange(const Layer& L, void* xbuf, hipStream_t s);
 hipError_t launch_decode_fused(const Layer& L, const void* x, const void* logits, void* out,
                                int64_t T, char* ws, const Workspace& W, void* xbuf,
-                               uint32_t epoch, int grid, hipStream_t s);
+                               uint32_t epoch, int grid, uint32_t spin_limit, hipStream_t s);
 hipError_t launch_dequant(const Layer& L, int fc, int64_t expert, float* out_f32,
                           uint16_t* out_bf16, hipStream_t s);
 

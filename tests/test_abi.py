@@ -100,6 +100,8 @@ def test_null_handles_and_outputs():
     assert L.qmoe_dequant(None, 1, 0, None, None, None) == 1
     a, b = ctypes.c_size_t(), ctypes.c_size_t()
     assert L.qmoe_workspace_routing(None, 4, ctypes.byref(a), ctypes.byref(b)) == 1
+    bits = ctypes.c_uint32(7)
+    assert L.qmoe_decode_errors(None, None, ctypes.byref(bits)) == 1
     c = _cfg()
     w = q.Weights(FAKE, FAKE, FAKE, FAKE)
     assert L.qmoe_create(ctypes.byref(c), ctypes.byref(w), 0, None) == 1

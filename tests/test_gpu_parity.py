@@ -205,6 +205,8 @@ def test_decode_back_to_back_calls_reuse_sync_state():
     torch.cuda.synchronize()
     for i, o in outs:
         assert torch.equal(o.view(torch.int16), refs[i].view(torch.int16)), i
+    # no bounded wait of the fused decode ran out in any of these calls
+    assert [L.decode_errors() for L in layers] == [0, 0, 0]
 
 
 class _env:
@@ -243,6 +245,7 @@ def test_fused_decode_schedule_independent(name, T):
             out = L(x, g)
             torch.cuda.synchronize()
             assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), (grid, rep)
+        assert L.decode_errors() == 0, grid
 
 
 def test_fused_decode_epoch_wrap():
@@ -260,14 +263,38 @@ def test_fused_decode_epoch_wrap():
         out = L(x, g)
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), rep
+    assert L.decode_errors() == 0
+
+
+def test_fused_decode_reports_waits_that_run_out():
+    """The fused decode's waits for another workgroup's h or y are bounded.
+    With the bound set from the host to one poll, consumers give up on
+    results that have not arrived yet: every kernel still finishes, and the
+    handle reports the waits that ran out in its error bits (bit 0: h,
+    bit 1: y), which the query clears. The outputs of such calls are not
+    checked (they read values that were not ready)."""
+    wl = qi.make_workload("decode", T=4)
+    x, g = wl.tokens.x.to(DEV), wl.tokens.logits.to(DEV)
+    with _env(QMOE_FUSED_SPIN_LIMIT=1):
+        L = layer_for(wl, 16)
+    for _ in range(3):
+        L(x, g)
+    bits = L.decode_errors()
+    assert bits != 0 and bits & ~3 == 0, bits
+    assert L.decode_errors() == 0
+    # a handle with the default bound, on the same inputs, meets every wait
+    check_decode(wl, layer_for(wl, 16))
 
 
 def test_decode_many_experts_uses_split_path():
     """More experts than the fused kernel's routing holds (E = 320 > 256):
-    the forward takes the two-kernel decode and still matches the oracle."""
+    the forward takes the two-kernel decode and still matches the oracle. A
+    handle without the fused decode reports no wait errors."""
     spec = small_spec(4, 32, num_experts=320, top_k=6)
     wl = qi.make_layer(spec, T=4, seed=91)
-    check_decode(wl, layer_for(wl, 16))
+    L = layer_for(wl, 16)
+    check_decode(wl, L)
+    assert L.decode_errors() == 0
 
 
 def test_decode_repeated_experts_across_tokens():
