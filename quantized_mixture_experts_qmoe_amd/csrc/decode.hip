@@ -287,41 +287,55 @@ __global__ __launch_bounds__(256) void decode_fc2_kernel(
   const int nsteps = rows_per_wave / rows_wave;
   const int m0 = blockIdx.x * rows_block;
   const int m_wave0 = m0 + wave * rows_per_wave + row_in_wave;
-  for (int step = 0; step < nsteps; ++step) {
-    const int m = m_wave0 + step * rows_wave;
-    const bool valid = m < H;
-    float y[kDecodeMaxTokens];
+  // Rows are taken in batches whose weight loads are all issued before any
+  // of them is used, so their HBM latencies overlap instead of adding up
+  // (with four units per lane the registers allow no batching).
+  constexpr int kBatch = UPL == 1 ? 8 : UPL == 2 ? 4 : 1;
+  for (int s0 = 0; s0 < nsteps; s0 += kBatch) {
+    UnitWords<BITS> w[kBatch][UPL];
+    float sc[kBatch][UPL];
+    int zz[kBatch][UPL];
 #pragma unroll
-    for (int t = 0; t < kDecodeMaxTokens; ++t) y[t] = 0.0f;
-    if (valid) {
-      UnitWords<BITS> w[UPL];
-      float sc[UPL];
-      int zz[UPL];
-#pragma unroll
-      for (int i = 0; i < UPL; ++i) {
-        const int u = lane_in_row + lpr * i;
-        if (u >= units) continue;
-        w[i] = load_unit<BITS>(ebase + static_cast<int64_t>(m) * row_bytes + u * (4 * BITS));
-        sc[i] = half_to_f32(sbase[static_cast<int64_t>(m) * nblk + (32 * u) / bs]);
-        zz[i] = zbase ? static_cast<int>(zbase[static_cast<int64_t>(m) * nblk + (32 * u) / bs]) : zp;
-      }
+    for (int b = 0; b < kBatch; ++b) {
+      const int m = m_wave0 + (s0 + b) * rows_wave;
+      if (s0 + b >= nsteps || m >= H) continue;
 #pragma unroll
       for (int i = 0; i < UPL; ++i) {
         const int u = lane_in_row + lpr * i;
         if (u >= units) continue;
-#pragma unroll
-        for (int t = 0; t < kDecodeMaxTokens; ++t) {
-          if (slot[t] < 0) continue;
-          const float d = unit_dot_f32<BITS>(w[i], hf[t].v[i]) - static_cast<float>(zz[i]) * hf[t].sum[i];
-          y[t] = fmaf(sc[i], d, y[t]);
-        }
+        w[b][i] = load_unit<BITS>(ebase + static_cast<int64_t>(m) * row_bytes + u * (4 * BITS));
+        sc[b][i] = half_to_f32(sbase[static_cast<int64_t>(m) * nblk + (32 * u) / bs]);
+        zz[b][i] = zbase ? static_cast<int>(zbase[static_cast<int64_t>(m) * nblk + (32 * u) / bs]) : zp;
       }
     }
 #pragma unroll
-    for (int t = 0; t < kDecodeMaxTokens; ++t) {
-      if (slot[t] < 0) continue;
-      const float yt = group_sum(y[t], lpr) + (valid ? bias_at(fc2_bias, ACT, e * static_cast<int64_t>(H) + m) : 0.0f);
-      if (valid && lane_in_row == 0) y32[static_cast<int64_t>(t * k + slot[t]) * H + m] = yt;
+    for (int b = 0; b < kBatch; ++b) {
+      if (s0 + b >= nsteps) break;
+      const int m = m_wave0 + (s0 + b) * rows_wave;
+      const bool valid = m < H;
+      float y[kDecodeMaxTokens];
+#pragma unroll
+      for (int t = 0; t < kDecodeMaxTokens; ++t) y[t] = 0.0f;
+      if (valid) {
+#pragma unroll
+        for (int i = 0; i < UPL; ++i) {
+          const int u = lane_in_row + lpr * i;
+          if (u >= units) continue;
+#pragma unroll
+          for (int t = 0; t < kDecodeMaxTokens; ++t) {
+            if (slot[t] < 0) continue;
+            const float d =
+                unit_dot_f32<BITS>(w[b][i], hf[t].v[i]) - static_cast<float>(zz[b][i]) * hf[t].sum[i];
+            y[t] = fmaf(sc[b][i], d, y[t]);
+          }
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < kDecodeMaxTokens; ++t) {
+        if (slot[t] < 0) continue;
+        const float yt = group_sum(y[t], lpr) + (valid ? bias_at(fc2_bias, ACT, e * static_cast<int64_t>(H) + m) : 0.0f);
+        if (valid && lane_in_row == 0) y32[static_cast<int64_t>(t * k + slot[t]) * H + m] = yt;
+      }
     }
   }
 
