@@ -21,8 +21,9 @@ duration is the per-step time of the timed region itself. Algorithmic bytes
 (prefill) per launch are counted from the routing the call actually made
 (distinct experts per call).
 
-HBM traffic. roofline.traffic is the dominant decode kernel's HBM bytes per
-launch as rocprofv3 counters measured them (FETCH_SIZE + WRITE_SIZE, each
+HBM traffic. roofline.traffic is the dominant kernel's HBM bytes per launch
+(the fused decode; for the 8K prefill entry, the FC1 GEMM) as rocprofv3
+counters measured them (FETCH_SIZE + WRITE_SIZE, each
 scaled by what the same counter reads for a plain copy of known size), read
 from the committed counter summary under profiles/ only if that summary was
 taken on the current kernel source (a digest of the sources is recorded with
@@ -67,29 +68,34 @@ TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_fused_traffic_qwen3_int
 TRAFFIC_SOURCES = ["quantized_mixture_experts_qmoe_amd/csrc/decode_fused.hip",
                    "quantized_mixture_experts_qmoe_amd/csrc/device.h",
                    "quantized_mixture_experts_qmoe_amd/csrc/internal.h"]
+PREFILL_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "prefill_traffic_qwen3_int4_8k.txt")
+PREFILL_SOURCES = ["quantized_mixture_experts_qmoe_amd/csrc/prefill.hip",
+                   "quantized_mixture_experts_qmoe_amd/csrc/device.h",
+                   "quantized_mixture_experts_qmoe_amd/csrc/internal.h"]
 
 
-def kernel_source_digest() -> str:
+def kernel_source_digest(sources=None) -> str:
     h = hashlib.sha256()
-    for rel in TRAFFIC_SOURCES:
+    for rel in (TRAFFIC_SOURCES if sources is None else sources):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """Counter-measured HBM bytes per launch of the fused decode at M=4, or
-    None if there is no summary for the current kernel source."""
+def measured_traffic(path=None, sources=None, key="hbm_bytes_per_launch"):
+    """Counter-measured HBM bytes per launch from a committed counter summary
+    (default: the fused decode at M=4), or None if there is no summary taken
+    on the current kernel source."""
     try:
-        with open(TRAFFIC_SUMMARY) as f:
-            kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith("#"))
+        with open(TRAFFIC_SUMMARY if path is None else path) as f:
+            kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith(("#", "|", "-")))
     except OSError:
         return None
     kv = {k.strip(): v.strip() for k, v in kv.items()}
-    if kv.get("source_digest") != kernel_source_digest():
+    if kv.get("source_digest") != kernel_source_digest(sources):
         return None
     try:
-        return float(kv["hbm_bytes_per_launch"])
+        return float(kv[key])
     except (KeyError, ValueError):
         return None
 
@@ -436,7 +442,9 @@ def main():
              "layer_frac_mfma": pf["layer_frac_mfma"], "kernels_us": pf["kernels_us"],
              "roofline": {"bound": "mfma", "kernel": "gemm_fc1_swiglu",
                           "achieved": pf["fc1"]["TFLOPs"], "peak": BF16_PEAK_TFLOPS,
-                          "unit": "TFLOP/s", "frac": pf["fc1"]["TFLOPs"] / BF16_PEAK_TFLOPS}},
+                          "unit": "TFLOP/s", "frac": pf["fc1"]["TFLOPs"] / BF16_PEAK_TFLOPS,
+                          "traffic": measured_traffic(PREFILL_TRAFFIC_SUMMARY, PREFILL_SOURCES,
+                                                      "fc1_hbm_bytes_per_launch")}},
             {"workload": "INT3 bs64 layer decode M=4 (uniform routing)",
              "tokens_per_s": i3d["tokens_per_s"], "ms_per_step": i3d["ms_per_step"],
              "layer_frac_hbm": i3d["layer_frac_hbm"], "distinct_experts": i3d["distinct_experts"],

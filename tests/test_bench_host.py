@@ -51,6 +51,34 @@ def test_source_digest_covers_every_fused_decode_source(tmp_path, monkeypatch):
     assert bench.kernel_source_digest() == base
 
 
+def test_prefill_traffic_uses_its_own_sources_and_key(tmp_path):
+    """The prefill summary is keyed on the prefill sources' digest, and the
+    figure is looked up by name (table and note lines are not read)."""
+    p = tmp_path / "pf.txt"
+    dig = bench.kernel_source_digest(bench.PREFILL_SOURCES)
+    assert dig != bench.kernel_source_digest()
+    with open(p, "w") as f:
+        f.write("| kernel | read: MB |\n- note: text\n")
+        f.write(f"fc1_hbm_bytes_per_launch: 677620306\nsource_digest: {dig}\n")
+    got = bench.measured_traffic(str(p), bench.PREFILL_SOURCES, "fc1_hbm_bytes_per_launch")
+    assert got == 677620306.0
+    assert bench.measured_traffic(str(p), None, "fc1_hbm_bytes_per_launch") is None
+    assert bench.measured_traffic(str(p), bench.PREFILL_SOURCES, "fc2_hbm_bytes_per_launch") is None
+
+
+def test_committed_summaries_parse():
+    """Both committed counter summaries carry a digest and their figures."""
+    for path, key in ((bench.TRAFFIC_SUMMARY, "hbm_bytes_per_launch"),
+                      (bench.PREFILL_TRAFFIC_SUMMARY, "fc1_hbm_bytes_per_launch")):
+        kv = {}
+        for line in open(path):
+            if ":" in line and not line.startswith(("#", "|", "-")):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+        assert len(kv["source_digest"]) == 16
+        assert float(kv[key]) > 0
+
+
 @pytest.mark.parametrize("n", [2, 8])
 def test_more_than_one_gpu_is_refused(n):
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", str(n)],
