@@ -72,8 +72,7 @@ static Workspace layout(const Layer& L, int64_t T, bool decode) {
   W.topk_w = take(R * 4);
   if (decode) {
     const GemvShape s2 = gemv_shape(L.I, 64);
-    W.n_counters = static_cast<int>((L.H + s2.rows_block - 1) / s2.rows_block);
-    W.counters = take(static_cast<size_t>(W.n_counters) * 4);
+    W.fc2_row_blocks = static_cast<int>((L.H + s2.rows_block - 1) / s2.rows_block);
     W.h32 = take(static_cast<size_t>(R * L.I * 4));
     W.y32 = take(static_cast<size_t>(R * L.H * 4));
   } else {

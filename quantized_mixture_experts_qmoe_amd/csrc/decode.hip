@@ -1,14 +1,16 @@
 // Decode path (1..4 tokens): memory-bound dequant-GEMVs.
 //
 // Every active expert's weights are streamed from HBM once and applied to
-// all (at most four) tokens that selected it. Two launches:
+// all (at most four) tokens that selected it. Three launches:
 //   1. decode_fc1: each workgroup recomputes the top-k routing of the <= 4
 //      tokens in its prologue (a few hundred logits), owns one (expert, block
 //      of gate rows) pair, and writes h = silu(gate) * up in fp32 per route;
 //   2. decode_fc2: each workgroup owns one (expert, block of output rows)
-//      pair and writes the per-route fp32 FC2 rows; the last workgroup to
-//      finish a block of output rows combines the k slots of every token in
-//      slot order and rounds once.
+//      pair and writes the per-route fp32 FC2 rows;
+//   3. decode_combine: sums the k slots of every token in slot order and
+//      rounds once. (A separate launch: having the last FC2 workgroup of a
+//      row block combine needed a device-scope fence in every workgroup,
+//      which cost more than the launch.)
 //
 // Semantics: SwiGLU experts with fc1 rows = 2 * inter ("[CUDA/CPU] Add AVX2
 // INT4 cold-expert kernel and zero-cold doorbell short-circuit for QMoE
@@ -85,8 +87,7 @@ __global__ __launch_bounds__(256) void decode_fc1_kernel(
     bool fc1_il, const void* __restrict__ fc1_bias, const uint8_t* __restrict__ fc1_zp,
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales, int H, int I, int bs,
     int zp, int64_t row_bytes, int64_t nblk, int lpr, int rows_block,
-    int32_t* __restrict__ ws_ids, float* __restrict__ ws_w, float* __restrict__ h32,
-    int32_t* __restrict__ counters, int n_counters) {
+    int32_t* __restrict__ ws_ids, float* __restrict__ ws_w, float* __restrict__ h32) {
   __shared__ RoutingLds R;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
   if (wave < T) {
@@ -107,7 +108,6 @@ __global__ __launch_bounds__(256) void decode_fc1_kernel(
       ws_ids[i] = R.ids[i];
       ws_w[i] = R.w[i];
     }
-    for (int i = threadIdx.x; i < n_counters; i += 256) counters[i] = 0;
   }
   const int r = blockIdx.y;
   const int e = R.ids[r];
@@ -220,7 +220,7 @@ __global__ __launch_bounds__(256) void decode_fc1_kernel(
   }
 }
 
-// grid = (n_counters = ceil(H / rows_block), T * k), block = 256
+// grid = (fc2_row_blocks = ceil(H / rows_block), T * k), block = 256
 template <int BITS, int UPL, int ACT>
 __global__ __launch_bounds__(256) void decode_fc2_kernel(
     const float* __restrict__ h32, const int32_t* __restrict__ ws_ids,
@@ -228,23 +228,14 @@ __global__ __launch_bounds__(256) void decode_fc2_kernel(
     const uint16_t* __restrict__ scales, int H, int I, int bs, int zp, int64_t row_bytes,
     int64_t nblk, int lpr, int rows_block, const void* __restrict__ fc2_bias,
     const uint8_t* __restrict__ fc2_zp,
-    float* __restrict__ y32, int32_t* __restrict__ counters, void* __restrict__ out) {
+    float* __restrict__ y32) {
   __shared__ RoutingLds R;
-  __shared__ int s_last;
   const int nroutes = T * k;
   for (int i = threadIdx.x; i < nroutes; i += 256) {
     R.ids[i] = ws_ids[i];
     R.w[i] = ws_w[i];
   }
   __syncthreads();
-  // number of distinct experts = number of workgroups per row block that work
-  bool first = false;
-  if (static_cast<int>(threadIdx.x) < nroutes) {
-    first = true;
-    for (int q = 0; q < static_cast<int>(threadIdx.x); ++q)
-      if (R.ids[q] == R.ids[threadIdx.x]) first = false;
-  }
-  const int n_distinct = __syncthreads_count(first);
 
   const int r = blockIdx.y;
   const int e = R.ids[r];
@@ -339,25 +330,21 @@ __global__ __launch_bounds__(256) void decode_fc2_kernel(
     }
   }
 
-  // publish, then let the last workgroup of this row block combine
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int old = atomicAdd(&counters[blockIdx.x], 1);
-    s_last = (old == n_distinct - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  for (int idx = threadIdx.x; idx < T * rows_block; idx += 256) {
-    const int t = idx / rows_block;
-    const int mm = m0 + idx % rows_block;
-    if (mm >= H) continue;
-    float acc = 0.0f;
-    for (int j = 0; j < k; ++j)
-      acc = fmaf(R.w[t * k + j], __builtin_nontemporal_load(y32 + static_cast<int64_t>(t * k + j) * H + mm), acc);
-    store_act(out, ACT, static_cast<int64_t>(t) * H + mm, acc);
-  }
+}
+
+// out[t][m] = round(sum_j w[t][j] * y32[t*k + j][m]), slot order j = 0..k-1,
+// one fp32 accumulator rounded once. grid = (ceil(H / 256), T), block = 256.
+template <int ACT>
+__global__ __launch_bounds__(256) void decode_combine_kernel(const float* __restrict__ y32,
+                                                             const float* __restrict__ ws_w, int k,
+                                                             int H, void* __restrict__ out) {
+  const int t = blockIdx.y;
+  const int m = blockIdx.x * 256 + threadIdx.x;
+  if (m >= H) return;
+  float acc = 0.0f;
+  for (int j = 0; j < k; ++j)
+    acc = fmaf(ws_w[t * k + j], __builtin_nontemporal_load(y32 + static_cast<int64_t>(t * k + j) * H + m), acc);
+  store_act(out, ACT, static_cast<int64_t>(t) * H + m, acc);
 }
 
 namespace {
@@ -370,16 +357,14 @@ hipError_t launch_decode_t(const Layer& L, const void* x, const void* logits, vo
   const int H = static_cast<int>(L.H), I = static_cast<int>(L.I);
   int32_t* ids = reinterpret_cast<int32_t*>(ws + W.topk_id);
   float* w = reinterpret_cast<float*>(ws + W.topk_w);
-  int32_t* counters = reinterpret_cast<int32_t*>(ws + W.counters);
   float* h32 = reinterpret_cast<float*>(ws + W.h32);
-  float* y32 = reinterpret_cast<float*>(ws + W.y32);
   dim3 g1((I + s1.rows_block - 1) / s1.rows_block, Ti * k);
   auto fc1 = L.act == kActBF16 ? decode_fc1_kernel<BITS, UPL, kActBF16>
              : L.act == kActF16 ? decode_fc1_kernel<BITS, UPL, kActF16>
                                 : decode_fc1_kernel<BITS, UPL, kActF32>;
   fc1<<<g1, 256, 0, s>>>(x, logits, Ti, E, k, L.normalize, L.fc1_interleaved, L.fc1_bias, L.fc1_zp,
                          L.fc1_codes, L.fc1_scales, H, I, L.bs, L.zp, L.fc1_row_bytes, L.fc1_nblk,
-                         s1.lpr, s1.rows_block, ids, w, h32, counters, W.n_counters);
+                         s1.lpr, s1.rows_block, ids, w, h32);
   stage_done(L, 1, "decode_fc1_swiglu");
   return hipGetLastError();
 }
@@ -391,17 +376,24 @@ hipError_t launch_fc2_t(const Layer& L, void* out, int64_t T, char* ws, const Wo
   const int H = static_cast<int>(L.H), I = static_cast<int>(L.I);
   const int32_t* ids = reinterpret_cast<const int32_t*>(ws + W.topk_id);
   const float* w = reinterpret_cast<const float*>(ws + W.topk_w);
-  int32_t* counters = reinterpret_cast<int32_t*>(ws + W.counters);
   const float* h32 = reinterpret_cast<const float*>(ws + W.h32);
   float* y32 = reinterpret_cast<float*>(ws + W.y32);
-  dim3 g2(W.n_counters, Ti * k);
+  dim3 g2(W.fc2_row_blocks, Ti * k);
   auto fc2 = L.act == kActBF16 ? decode_fc2_kernel<BITS, UPL, kActBF16>
              : L.act == kActF16 ? decode_fc2_kernel<BITS, UPL, kActF16>
                                 : decode_fc2_kernel<BITS, UPL, kActF32>;
   fc2<<<g2, 256, 0, s>>>(h32, ids, w, Ti, k, L.fc2_codes, L.fc2_scales, H, I, L.bs, L.zp,
                          L.fc2_row_bytes, L.fc2_nblk, s2.lpr, s2.rows_block, L.fc2_bias, L.fc2_zp,
-                         y32, counters, out);
-  stage_done(L, 2, "decode_fc2_combine");
+                         y32);
+  stage_done(L, 2, "decode_fc2");
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  dim3 g3((H + 255) / 256, Ti);
+  auto comb = L.act == kActBF16 ? decode_combine_kernel<kActBF16>
+              : L.act == kActF16 ? decode_combine_kernel<kActF16>
+                                 : decode_combine_kernel<kActF32>;
+  comb<<<g3, 256, 0, s>>>(y32, w, k, H, out);
+  stage_done(L, 3, "decode_combine");
   return hipGetLastError();
 }
 

@@ -56,7 +56,6 @@ GemvShape gemv_shape(int64_t K, int min_rows_block);
 // Workspace layout for one forward call on T tokens (byte offsets).
 struct Workspace {
   size_t topk_id, topk_w;             // int32 / fp32 [R]
-  size_t counters;                    // int32 [n_counters] (decode combine)
   size_t h32, y32;                    // decode: fp32 [R, I], fp32 [R, H]
   size_t hist, chunk_base;            // prefill: int32 [nchunks, E] each
   size_t counts, offsets;             // int32 [E], [E + 1]
@@ -66,7 +65,7 @@ struct Workspace {
   size_t hbf16, yf32;                 // prefill: bf16 [R, I], fp32 [R, H]
   size_t total;
   int64_t R, nchunks, max_tiles;
-  int n_counters;
+  int fc2_row_blocks;                 // decode: FC2 workgroups per route
   bool decode;
 };
 bool use_decode_path(const Layer& L, bool force_prefill, int64_t T);
