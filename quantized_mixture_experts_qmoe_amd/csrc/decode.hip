@@ -400,7 +400,13 @@ hipError_t launch_fc2_t(const Layer& L, void* out, int64_t T, char* ws, const Wo
 template <int BITS>
 hipError_t launch_decode_bits(const Layer& L, const void* x, const void* logits, void* out,
                               int64_t T, char* ws, const Workspace& W, hipStream_t s) {
-  const GemvShape s1 = gemv_shape(L.H, 16);
+  // FC1 workgroups cover 32 gate rows each when that still leaves at least
+  // two workgroups per CU of a 256-CU part (ceil(I / 32) * T * k >= 512), else
+  // 16: larger blocks recompute the routing prologue in fewer workgroups
+  // (4 tokens: FC1 52 -> 41 us), smaller ones fill the chip when few routes
+  // are active (1 token: 22 us at 16 rows, 28 us at 32).
+  const int64_t wg32 = (L.I + 31) / 32 * T * L.k;
+  const GemvShape s1 = gemv_shape(L.H, wg32 >= 512 ? 32 : 16);
   const GemvShape s2 = gemv_shape(L.I, 64);
   hipError_t err;
   switch (s1.upl) {
