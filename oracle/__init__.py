@@ -22,9 +22,14 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "qmoe_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle_qmoe.so")
 
-EMU_W_BF16 = 1
-EMU_H_BF16 = 2
-EMU_GU_BF16 = 4
+# Rounding points of the fp16 matrix-core datapath (qmoe_oracle.c describes
+# each): activations, dequantized weights, SwiGLU output.
+EMU_X_F16 = 1
+EMU_W_F16 = 2
+EMU_H_F16 = 4
+EMU_F16_DATAPATH = EMU_X_F16 | EMU_W_F16 | EMU_H_F16
+EMU_W_BF16 = 8      # the earlier bf16 datapath: weights and h rounded to bf16
+EMU_H_BF16 = 16
 
 
 def build(force: bool = False) -> str:
@@ -64,6 +69,13 @@ def lib():
         L.oracle_forward_ext.argtypes = [ctypes.POINTER(_Layer), P, P, P, P, P, P, P, P, P, P, i64, P,
                                          i32]
         L.oracle_dequant_zp.argtypes = [P, P, P, i64, i64, i32, i32, i32, P]
+        L.oracle_dequant_f16.argtypes = [P, P, P, i64, i64, i32, i32, i32, P]
+        L.oracle_double_to_half_n.argtypes = [P, i64, P]
+        L.oracle_double_to_half_n.restype = None
+        L.oracle_emulate_x_rows.argtypes = [P, i64, i64, P]
+        L.oracle_emulate_x_rows.restype = None
+        L.oracle_emulate_h_rows.argtypes = [P, i64, i64]
+        L.oracle_emulate_h_rows.restype = None
         L.oracle_round_output.argtypes = [P, i64, P, P]
         L.oracle_round_output.restype = None
         L.oracle_half_to_double_n.argtypes = [P, i64, P]
@@ -71,7 +83,7 @@ def lib():
         L.oracle_f32_to_bf16_n.argtypes = [P, i64, P]
         L.oracle_f32_to_bf16_n.restype = None
         for f in (L.oracle_dequant, L.oracle_route, L.oracle_permute, L.oracle_forward,
-                  L.oracle_forward_ext, L.oracle_dequant_zp):
+                  L.oracle_forward_ext, L.oracle_dequant_zp, L.oracle_dequant_f16):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -112,6 +124,44 @@ def f32_to_bf16_bits(f: np.ndarray) -> np.ndarray:
     f = np.ascontiguousarray(f, dtype=np.float32)
     out = np.empty(f.shape, dtype=np.uint16)
     lib().oracle_f32_to_bf16_n(_p(f), f.size, _p(out))
+    return out
+
+
+def double_to_half_bits(v: np.ndarray) -> np.ndarray:
+    """Nearest fp16 (ties to even, gradual underflow) of float64 values, as bits."""
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    out = np.empty(v.shape, dtype=np.uint16)
+    lib().oracle_double_to_half_n(_p(v), v.size, _p(out))
+    return out
+
+
+def emulate_x_rows(x: np.ndarray) -> np.ndarray:
+    """Rows of activations as the fp16 datapath's FC1 reads them (EMU_X_F16)."""
+    x = np.array(x, dtype=np.float64, order="C", copy=True)
+    tmp = np.empty(x.shape[-1], dtype=np.float64)
+    lib().oracle_emulate_x_rows(_p(x), x.size // x.shape[-1], x.shape[-1], _p(tmp))
+    return x
+
+
+def emulate_h_rows(h: np.ndarray) -> np.ndarray:
+    """Rows of SwiGLU outputs as the fp16 datapath's FC2 reads them (EMU_H_F16)."""
+    h = np.array(h, dtype=np.float64, order="C", copy=True)
+    lib().oracle_emulate_h_rows(_p(h), h.size // h.shape[-1], h.shape[-1])
+    return h
+
+
+def dequant_f16(codes: np.ndarray, scales: np.ndarray, bits: int, block_size: int,
+                zero_point: int, K: int, zero_points: Optional[np.ndarray] = None) -> np.ndarray:
+    """fp16((q - zp) * s) bit patterns (uint16 [N, K]): the weight operand of
+    the fp16 datapath."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    sc = np.ascontiguousarray(scales).view(np.uint16)
+    zps = None if zero_points is None else np.ascontiguousarray(zero_points, dtype=np.uint8)
+    N = codes.shape[0]
+    assert zps is None or zps.shape == sc.shape
+    out = np.empty((N, K), dtype=np.uint16)
+    _check(lib().oracle_dequant_f16(_p(codes), _p(sc), _p(zps), N, K, bits, block_size,
+                                    zero_point, _p(out)), "dequant_f16")
     return out
 
 
@@ -180,7 +230,8 @@ def forward(layer: Layer, x, logits, weights, *, nthreads: Optional[int] = None,
     fc1_bias [E, 2I] and fc2_bias [E, H] (optional, any float dtype, read as
     exact values) are added to FC1 rows before SwiGLU and to y before the
     routing-weighted sum. fc1_zero_points / fc2_zero_points (uint8, shaped
-    like the scales) replace the scalar zero point per row and quant block."""
+    like the scales) replace the scalar zero point per row and quant block.
+    emulate: a bitmask of EMU_* rounding points (0: the plain definition)."""
     x64 = as_f64(x)
     l64 = as_f64(logits)
     T = x64.shape[0]

@@ -14,7 +14,11 @@ mistake cannot hide in both:
 - top-k is a full stable sort by (-logit, expert index) (``np.lexsort``);
 - the layer is computed densely: every expert runs on every token through
   BLAS matmuls, and a [T, E] gate matrix that is zero off the top-k selects
-  and weights the results (a masked mixture), instead of per-route loops.
+  and weights the results (a masked mixture), instead of per-route loops;
+- the fp16 rounding points of the emulated datapath use numpy's own float64
+  -> float16 conversion and whole-array exponent arithmetic (``np.frexp``,
+  ``np.ldexp``) over reshaped chunks, instead of the C oracle's hand-written
+  rounding and per-element loops.
 """
 from __future__ import annotations
 
@@ -70,6 +74,48 @@ def softmax_selected(logits64: np.ndarray, ids: np.ndarray) -> np.ndarray:
     return z / z.sum(axis=1, keepdims=True)
 
 
+def f16(v: np.ndarray) -> np.ndarray:
+    """Nearest float16 value (numpy's conversion), back in float64."""
+    with np.errstate(over="ignore"):
+        return np.asarray(v, dtype=np.float64).astype(np.float16).astype(np.float64)
+
+
+def _range_exponent(M: np.ndarray) -> np.ndarray:
+    """e with M * 2^-e in [2^14, 2^15)."""
+    return np.frexp(M)[1].astype(np.int64) - 15
+
+
+def f16_rows_scaled(x: np.ndarray) -> np.ndarray:
+    """Each row rounded to fp16 after an exact scaling that puts its largest
+    magnitude in [2^14, 2^15) (rows that are zero or not finite: no scaling)."""
+    finite = np.isfinite(x).all(axis=-1, keepdims=True)
+    M = np.where(finite, np.abs(np.where(np.isfinite(x), x, 0.0)).max(axis=-1, keepdims=True), 0.0)
+    e = np.where(M > 0, _range_exponent(np.where(M > 0, M, 1.0)), 0)
+    return np.ldexp(f16(np.ldexp(x, -e)), e)
+
+
+def f16_chunks_scaled(h: np.ndarray, chunk: int = 32, *, plant_no_chunk_exponent: bool = False,
+                      plant_no_common_exponent: bool = False) -> np.ndarray:
+    """h [..., I] as FC2 of the fp16 datapath reads it: per chunk of 32 values,
+    an exponent only when the chunk's largest magnitude M is nonzero, finite
+    and outside [2^-10, 2^15]; each chunk stored as fp16 at its exponent, then
+    brought to the row's largest chunk exponent E with a second fp16
+    rounding. The plant_* switches drop one step (for the pin tests)."""
+    lead, I = h.shape[:-1], h.shape[-1]
+    c = h.reshape(*lead, I // chunk, chunk)
+    finite = np.isfinite(c).all(axis=-1, keepdims=True)
+    M = np.where(finite, np.abs(np.where(np.isfinite(c), c, 0.0)).max(axis=-1, keepdims=True), 0.0)
+    out_of_range = (M > 0) & ((M > 2.0 ** 15) | (M < 2.0 ** -10))
+    e = np.where(out_of_range, _range_exponent(np.where(M > 0, M, 1.0)), 0)
+    if plant_no_chunk_exponent:
+        e = np.zeros_like(e)
+    stored = f16(np.ldexp(c, -e))
+    E = e.max(axis=-2, keepdims=True)
+    if plant_no_common_exponent:
+        return np.ldexp(stored, e).reshape(h.shape)
+    return np.ldexp(f16(np.ldexp(stored, e - E)), E).reshape(h.shape)
+
+
 def silu(v: np.ndarray) -> np.ndarray:
     return v * (0.5 * (1.0 + np.tanh(0.5 * v)))      # sigmoid via tanh identity
 
@@ -78,14 +124,22 @@ def dense_masked_forward(x64: np.ndarray, logits64: np.ndarray, weights, spec,
                          *, swap_gate_up: bool = False, zp_delta: int = 0,
                          softmax_all: bool = False, fc1_bias=None, fc2_bias=None,
                          bias_after_silu: bool = False, fc1_zero_points=None,
-                         fc2_zero_points=None) -> np.ndarray:
+                         fc2_zero_points=None, emu_x: bool = False, emu_w: bool = False,
+                         emu_h: bool = False, plant_h_unrounded: bool = False,
+                         plant_h_no_chunk_exponent: bool = False,
+                         plant_h_no_common_exponent: bool = False,
+                         plant_x_unscaled: bool = False) -> np.ndarray:
     """Masked-mixture formulation of the layer in float64.
 
-    The keyword switches plant deliberate mistakes; tests use them to show that
-    the comparison against the oracle would notice each one.
+    emu_x / emu_w / emu_h apply the fp16 datapath's rounding points to the
+    activations, the dequantized weights and the SwiGLU output.
+    The other keyword switches plant deliberate mistakes; tests use them to
+    show that the comparison against the oracle would notice each one.
     """
     T = x64.shape[0]
     E, H, I, k = spec.num_experts, spec.hidden, spec.inter, spec.top_k
+    if emu_x:
+        x64 = f16(x64) if plant_x_unscaled else f16_rows_scaled(x64)
     ids = topk_brute(logits64, k)
     if softmax_all:
         z = np.exp(logits64 - logits64.max(axis=1, keepdims=True))
@@ -106,6 +160,8 @@ def dense_masked_forward(x64: np.ndarray, logits64: np.ndarray, weights, spec,
                            spec.block_size, z1, H)                   # [2I, H]
         W2 = dequant_dense(weights.fc2_codes[e], weights.fc2_scales[e], spec.bits,
                            spec.block_size, z2, I)                   # [H, I]
+        if emu_w:
+            W1, W2 = f16(W1), f16(W2)
         gu = x64 @ W1.T                                             # [T, 2I]
         if fc1_bias is not None and not bias_after_silu:
             gu = gu + fc1_bias[e][None, :]
@@ -115,6 +171,9 @@ def dense_masked_forward(x64: np.ndarray, logits64: np.ndarray, weights, spec,
         h = silu(g) * u
         if fc1_bias is not None and bias_after_silu:
             h = h + fc1_bias[e][None, :I]
+        if emu_h and not plant_h_unrounded:
+            h = f16_chunks_scaled(h, plant_no_chunk_exponent=plant_h_no_chunk_exponent,
+                                  plant_no_common_exponent=plant_h_no_common_exponent)
         y = h @ W2.T
         if fc2_bias is not None:
             y = y + fc2_bias[e][None, :]

@@ -56,6 +56,14 @@
  *    expert;
  *  - the output is the double accumulator rounded once to fp32 and, for bf16
  *    outputs, that fp32 rounded to bf16 (round to nearest even).
+ *
+ * An optional emulation mode (EMU_* flags, off by default) applies the
+ * rounding points of the GPU's fp16 matrix-core datapath to the activations,
+ * the dequantized weights and the SwiGLU output (described where the flags
+ * are defined). It is pinned, like the plain definition, by the tests:
+ * against numpy's float16 conversion (every fp16 value, every tie, the
+ * range edges) and against an independent vectorized twin of each rounding
+ * point and of the whole layer.
  */
 #include <math.h>
 #include <pthread.h>
@@ -95,6 +103,36 @@ uint16_t oracle_f32_to_bf16(float f)
     return (uint16_t)(u >> 16);
 }
 
+/* IEEE binary16 nearest to a double (round to nearest, ties to even, with
+ * gradual underflow), as a bit pattern. NaN keeps its sign and becomes the
+ * quiet NaN 0x7E00; magnitudes from 65520 up round to infinity (65520 lies
+ * half way between 65504 and 2^16, and the tie goes to the even pattern).
+ * Every finite value is rounded on the grid of its binade: steps of 2^-24
+ * below 2^-14, else 2^(E-10) for values in [2^E, 2^(E+1)). */
+uint16_t oracle_double_to_half(double v)
+{
+    uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    if (isnan(v)) return (uint16_t)(sign | 0x7E00u);
+    double a = fabs(v);
+    if (a >= 65520.0) return (uint16_t)(sign | 0x7C00u);
+    if (a == 0.0) return sign;
+    int ex;
+    (void)frexp(a, &ex);                 /* a = f * 2^ex, f in [0.5, 1) */
+    int E = ex - 1;                      /* a in [2^E, 2^(E+1)) */
+    if (E < -14) E = -14;
+    double step = ldexp(1.0, E - 10);
+    double r = nearbyint(a / step) * step;   /* exact scaling; ties to even */
+    if (r == 0.0) return sign;
+    if (r < ldexp(1.0, -14))                 /* subnormal: r = m * 2^-24 */
+        return (uint16_t)(sign | (uint16_t)ldexp(r, 24));
+    (void)frexp(r, &ex);                     /* the rounding may reach the next binade */
+    E = ex - 1;
+    int mant = (int)(ldexp(r, 10 - E)) - 1024;
+    return (uint16_t)(sign | (uint16_t)((E + 15) << 10) | (uint16_t)mant);
+}
+
+static double round_half(double v) { return oracle_half_to_double(oracle_double_to_half(v)); }
+
 /* Unsigned code number kk of one packed row. */
 static int code_at(const uint8_t *row, int64_t kk, int bits)
 {
@@ -124,7 +162,6 @@ static int valid_format(int64_t K, int bits, int bs)
     return 1;
 }
 
-/* W[n][kk] = (q - zp) * s for one [N, K] matrix; out is [N, K] double. */
 /* (q - zp) * s for one [N, K] matrix; zps [N, K/bs] or NULL for the scalar zp. */
 int oracle_dequant_zp(const uint8_t *codes, const uint16_t *scales, const uint8_t *zps, int64_t N,
                       int64_t K, int bits, int bs, int zp, double *out)
@@ -137,6 +174,23 @@ int oracle_dequant_zp(const uint8_t *codes, const uint16_t *scales, const uint8_
             double s = oracle_half_to_double(scales[n * nblk + kk / bs]);
             int z = zps ? (int)zps[n * nblk + kk / bs] : zp;
             out[n * K + kk] = (double)(code_at(row, kk, bits) - z) * s;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* The fp16 operand of the emulated datapath: fp16((q - zp) * s) bit patterns. */
+int oracle_dequant_f16(const uint8_t *codes, const uint16_t *scales, const uint8_t *zps, int64_t N,
+                       int64_t K, int bits, int bs, int zp, uint16_t *out)
+{
+    if (!codes || !scales || !out || N < 0 || !valid_format(K, bits, bs)) return ORACLE_BAD_ARG;
+    int64_t rb = row_bytes(K, bits), nblk = K / bs;
+    for (int64_t n = 0; n < N; ++n) {
+        const uint8_t *row = codes + n * rb;
+        for (int64_t kk = 0; kk < K; ++kk) {
+            double s = oracle_half_to_double(scales[n * nblk + kk / bs]);
+            int z = zps ? (int)zps[n * nblk + kk / bs] : zp;
+            out[n * K + kk] = oracle_double_to_half((double)(code_at(row, kk, bits) - z) * s);
         }
     }
     return ORACLE_OK;
@@ -206,17 +260,82 @@ int oracle_permute(const int32_t *topk_id, int64_t R, int64_t E, int32_t *counts
     return ORACLE_OK;
 }
 
-/* Rounding-point emulation (off by default). Each flag rounds one
- * intermediate to bf16, to measure what a bf16 datapath costs. */
-#define EMU_W_BF16 1       /* dequantized weight (q - zp) * s */
-#define EMU_H_BF16 2       /* SwiGLU output h */
-#define EMU_GU_BF16 4      /* gate and up dot products */
+/* Rounding-point emulation of the fp16 matrix-core datapath of the grouped
+ * (prefill) path (off by default; each flag rounds one operand):
+ *  EMU_X_F16: token t's activations x enter as fp16 after an exact scaling by
+ *    2^-e_t, where M = max |x_t| and e_t = (exponent of M) - 15, so the
+ *    scaled maximum lies in [2^14, 2^15): x' = fp16(x * 2^-e_t) * 2^e_t
+ *    (e_t = 0 for a zero or non-finite M);
+ *  EMU_W_F16: each dequantized weight is fp16((q - zp) * s);
+ *  EMU_H_F16: each route's SwiGLU output h enters FC2 as fp16 in chunks of
+ *    32 consecutive values n: a chunk whose maximum magnitude M lies outside
+ *    [2^-10, 2^15] (and is nonzero, finite) gets the exponent
+ *    e_c = (exponent of M) - 15, else e_c = 0, and is stored as
+ *    fp16(h * 2^-e_c); the route's exponent is E = max_c e_c and FC2 reads
+ *    fp16(stored * 2^(e_c - E)) * 2^E.
+ * fp16() is oracle_double_to_half: nearest, ties to even, gradual underflow. */
+#define EMU_X_F16 1
+#define EMU_W_F16 2
+#define EMU_H_F16 4
+#define EMU_H_CHUNK 32
+/* The earlier bf16 datapath's rounding points (x is rounded by the caller):
+ * weights and h rounded to bf16, nearest even. */
+#define EMU_W_BF16 8
+#define EMU_H_BF16 16
 
-static double to_bf16(double v) {
+static double to_bf16(double v)
+{
     uint32_t u = (uint32_t)oracle_f32_to_bf16((float)v) << 16;
     float f;
     memcpy(&f, &u, sizeof f);
     return (double)f;
+}
+
+/* Exponent of the power of two that puts M in [2^14, 2^15). */
+static int range_exponent(double M)
+{
+    int ex;
+    (void)frexp(M, &ex);       /* M = f * 2^ex, f in [0.5, 1): M * 2^-(ex-15) in [2^14, 2^15) */
+    return ex - 15;
+}
+
+static void emulate_x(const double *x, int64_t H, double *out)
+{
+    double M = 0.0;
+    int finite = 1;
+    for (int64_t i = 0; i < H; ++i) {
+        if (!isfinite(x[i])) finite = 0;
+        else if (fabs(x[i]) > M) M = fabs(x[i]);
+    }
+    int e = (finite && M > 0.0) ? range_exponent(M) : 0;
+    for (int64_t i = 0; i < H; ++i) out[i] = ldexp(round_half(ldexp(x[i], -e)), e);
+}
+
+static void emulate_h(double *h, int64_t I)
+{
+    int64_t nc = I / EMU_H_CHUNK;
+    int E = INT32_MIN;
+    /* first pass: chunk exponents and the stored fp16 values */
+    int *ec = (int *)malloc((size_t)nc * sizeof(int));
+    if (!ec) return;   /* unreachable in practice; leaves h unrounded */
+    for (int64_t c = 0; c < nc; ++c) {
+        double M = 0.0;
+        int finite = 1;
+        for (int64_t n = c * EMU_H_CHUNK; n < (c + 1) * EMU_H_CHUNK; ++n) {
+            if (!isfinite(h[n])) finite = 0;
+            else if (fabs(h[n]) > M) M = fabs(h[n]);
+        }
+        int e = 0;
+        if (finite && M > 0.0 && (M > 32768.0 || M < ldexp(1.0, -10))) e = range_exponent(M);
+        ec[c] = e;
+        if (e > E) E = e;
+        for (int64_t n = c * EMU_H_CHUNK; n < (c + 1) * EMU_H_CHUNK; ++n) h[n] = round_half(ldexp(h[n], -e));
+    }
+    /* second pass: every chunk brought to the route's exponent */
+    for (int64_t c = 0; c < nc; ++c)
+        for (int64_t n = c * EMU_H_CHUNK; n < (c + 1) * EMU_H_CHUNK; ++n)
+            h[n] = ldexp(round_half(ldexp(h[n], ec[c] - E)), E);
+    free(ec);
 }
 
 typedef struct {
@@ -242,13 +361,14 @@ typedef struct {
 
 /* dot of one dequantized weight row with a double vector */
 static double row_dot(const uint8_t *row, const uint16_t *srow, const uint8_t *zrow,
-                      const double *v, int64_t K, int bits, int bs, int zp, int emu_w)
+                      const double *v, int64_t K, int bits, int bs, int zp, int emu_w, int emu_wb)
 {
     double acc = 0.0;
     for (int64_t kk = 0; kk < K; ++kk) {
         int z = zrow ? (int)zrow[kk / bs] : zp;
         double w = (double)(code_at(row, kk, bits) - z) * oracle_half_to_double(srow[kk / bs]);
-        if (emu_w) w = to_bf16(w);
+        if (emu_w) w = round_half(w);
+        if (emu_wb) w = to_bf16(w);
         acc += w * v[kk];
     }
     return acc;
@@ -262,21 +382,28 @@ static void *run_tokens(void *arg)
     int k = L->top_k, bits = L->bits, bs = L->block_size, zp = L->zero_point;
     int64_t rb1 = row_bytes(H, bits), rb2 = row_bytes(I, bits);
     int64_t nb1 = H / bs, nb2 = I / bs;
-    int emu_w = (L->emulate & EMU_W_BF16) != 0;
-    int emu_h = (L->emulate & EMU_H_BF16) != 0;
-    int emu_gu = (L->emulate & EMU_GU_BF16) != 0;
+    int emu_x = (L->emulate & EMU_X_F16) != 0;
+    int emu_w = (L->emulate & EMU_W_F16) != 0;
+    int emu_h = (L->emulate & EMU_H_F16) != 0;
+    int emu_wb = (L->emulate & EMU_W_BF16) != 0;
+    int emu_hb = (L->emulate & EMU_H_BF16) != 0;
 
     double *h = (double *)malloc((size_t)I * sizeof(double));
     double *acc = (double *)malloc((size_t)H * sizeof(double));
+    double *xe = (double *)malloc((size_t)H * sizeof(double));
     int32_t *ids = (int32_t *)malloc((size_t)k * sizeof(int32_t));
     double *w = (double *)malloc((size_t)k * sizeof(double));
-    if (!h || !acc || !ids || !w) {
+    if (!h || !acc || !xe || !ids || !w) {
         jb->status = ORACLE_NO_MEM;
-        free(h); free(acc); free(ids); free(w);
+        free(h); free(acc); free(xe); free(ids); free(w);
         return NULL;
     }
     for (int64_t t = jb->t0; t < jb->t1; ++t) {
         const double *xt = jb->x + t * H;
+        if (emu_x) {
+            emulate_x(xt, H, xe);
+            xt = xe;
+        }
         int st = oracle_route(jb->logits + t * E, 1, E, k, jb->L->normalize, ids, w);
         if (st != ORACLE_OK) { jb->status = st; break; }
         for (int64_t m = 0; m < H; ++m) acc[m] = 0.0;
@@ -291,27 +418,27 @@ static void *run_tokens(void *arg)
                 const int64_t ur = jb->L->fc1_interleaved ? 2 * n + 1 : I + n;
                 const uint8_t *z1 = jb->fc1_zp ? jb->fc1_zp + e * (2 * I) * nb1 : NULL;
                 double g = row_dot(c1 + gr * rb1, s1 + gr * nb1, z1 ? z1 + gr * nb1 : NULL, xt, H,
-                                   bits, bs, zp, emu_w);
+                                   bits, bs, zp, emu_w, emu_wb);
                 double u = row_dot(c1 + ur * rb1, s1 + ur * nb1, z1 ? z1 + ur * nb1 : NULL, xt, H,
-                                   bits, bs, zp, emu_w);
+                                   bits, bs, zp, emu_w, emu_wb);
                 if (jb->fc1_bias) {
                     g += jb->fc1_bias[e * 2 * I + gr];
                     u += jb->fc1_bias[e * 2 * I + ur];
                 }
-                if (emu_gu) { g = to_bf16(g); u = to_bf16(u); }
-                double hv = g / (1.0 + exp(-g)) * u;
-                h[n] = emu_h ? to_bf16(hv) : hv;
+                h[n] = g / (1.0 + exp(-g)) * u;
+                if (emu_hb) h[n] = to_bf16(h[n]);
             }
+            if (emu_h) emulate_h(h, I);
             for (int64_t m = 0; m < H; ++m) {
                 const uint8_t *z2 = jb->fc2_zp ? jb->fc2_zp + (e * H + m) * nb2 : NULL;
-                double y = row_dot(c2 + m * rb2, s2 + m * nb2, z2, h, I, bits, bs, zp, emu_w);
+                double y = row_dot(c2 + m * rb2, s2 + m * nb2, z2, h, I, bits, bs, zp, emu_w, emu_wb);
                 if (jb->fc2_bias) y += jb->fc2_bias[e * H + m];
                 acc[m] += w[j] * y;
             }
         }
         for (int64_t m = 0; m < H; ++m) jb->out[t * H + m] = acc[m];
     }
-    free(h); free(acc); free(ids); free(w);
+    free(h); free(acc); free(xe); free(ids); free(w);
     return NULL;
 }
 
@@ -389,4 +516,24 @@ void oracle_half_to_double_n(const uint16_t *h, int64_t n, double *out)
 void oracle_f32_to_bf16_n(const float *f, int64_t n, uint16_t *out)
 {
     for (int64_t i = 0; i < n; ++i) out[i] = oracle_f32_to_bf16(f[i]);
+}
+
+/* The datapath emulation's activation and SwiGLU-output rounding points,
+ * applied in place to `rows` rows (for the pin tests). */
+void oracle_emulate_x_rows(double *x, int64_t rows, int64_t H, double *tmp)
+{
+    for (int64_t r = 0; r < rows; ++r) {
+        emulate_x(x + r * H, H, tmp);
+        memcpy(x + r * H, tmp, (size_t)H * sizeof(double));
+    }
+}
+
+void oracle_emulate_h_rows(double *h, int64_t rows, int64_t I)
+{
+    for (int64_t r = 0; r < rows; ++r) emulate_h(h + r * I, I);
+}
+
+void oracle_double_to_half_n(const double *v, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_double_to_half(v[i]);
 }

@@ -480,12 +480,164 @@ def test_zipf_skew_present():
     assert (counts == 0).sum() > 10           # a long tail of idle experts
 
 
-def test_emulated_bf16_points_stay_close():
-    """The bf16 datapath reading (bf16 weights and bf16 h) moves the result by
-    well under the 1e-2 per-token relative-L2 bound on a Qwen3-shaped slice."""
-    wl = qi.make_workload("decode", T=4)
-    exact = _run(wl)
-    emu = _run(wl, emulate=oracle.EMU_W_BF16 | oracle.EMU_H_BF16)
-    rel = np.linalg.norm(emu - exact, axis=1) / np.linalg.norm(exact, axis=1)
-    assert rel.max() < 5e-3
-    assert rel.max() > 1e-5          # the emulation really changes something
+# ---------------------------------------------------------------- fp16 datapath emulation
+#
+# The grouped (prefill) path feeds fp16 operands to the matrix cores. The
+# oracle's emulation of those rounding points (EMU_*) is pinned against
+# numpy's own float16 conversion and an independent vectorized twin in
+# oracle/brute.py, and each plausible slip in it is shown to be visible.
+
+def _half_bits_numpy(v):
+    with np.errstate(over="ignore"):
+        return np.asarray(v, dtype=np.float64).astype(np.float16).view(np.uint16)
+
+
+def test_double_to_half_against_numpy():
+    """Nearest fp16 of float64 values against numpy's conversion: every fp16
+    value, every exact tie between neighbours (and a hair either side of
+    it), the overflow and underflow edges, and random values over the whole
+    range, both signs."""
+    allh = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    fin = allh[np.isfinite(allh.view(np.float16))].view(np.float16).astype(np.float64)
+    pos = np.unique(fin[fin >= 0])
+    mids = (pos[:-1] + pos[1:]) / 2                       # exact ties (float64 holds them)
+    hair = np.concatenate([np.nextafter(mids, 0), np.nextafter(mids, np.inf)])
+    edges = np.array([65504.0, 65519.99, 65520.0, 65535.0, 1e6, 2.0 ** -24, 2.0 ** -25,
+                      3 * 2.0 ** -26, 2.0 ** -26, 2.0 ** -14 - 2.0 ** -25, 0.0, np.inf])
+    rng = np.random.default_rng(3)
+    rnd = np.ldexp(rng.random(200000) + 0.5, rng.integers(-30, 18, 200000))
+    v = np.concatenate([fin, mids, hair, edges, rnd])
+    v = np.concatenate([v, -v])
+    got = oracle.double_to_half_bits(v)
+    assert np.array_equal(got, _half_bits_numpy(v))
+    nan = oracle.double_to_half_bits(np.array([np.nan, -np.nan]))
+    assert all((b & 0x7C00) == 0x7C00 and (b & 0x3FF) != 0 for b in nan)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_dequant_f16_exhaustive_codes_times_scales(bits):
+    """Every code times every fp16 scale (infinities and NaN included), for
+    every zero point: the fp16 operand is numpy's float16 of the exact
+    product (q - zp) * s."""
+    ncodes = 1 << bits
+    allh = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    K = 8 * ncodes
+    q = np.tile(np.arange(ncodes), K // ncodes)
+    packed = np.broadcast_to(brute.pack_codes(q[None], bits), (allh.size, K * bits // 8)).copy()
+    scales = allh.view(np.float16)[:, None]
+    s64 = scales.astype(np.float64)
+    for zp in range(ncodes):
+        got = oracle.dequant_f16(packed, scales, bits, K, zp, K)
+        with np.errstate(invalid="ignore"):
+            exact = (q[None, :] - zp).astype(np.float64) * s64
+        ref = _half_bits_numpy(exact)
+        nan = np.isnan(exact)
+        assert np.array_equal(np.isnan(got.view(np.float16)), nan)
+        assert np.array_equal(got[~nan], ref[~nan])
+
+
+def _emu_rows():
+    """Rows that exercise every branch of the range scaling: ordinary values,
+    rows far above and far below the fp16 range, zero rows, a row with an
+    infinity, and rows whose 32-wide chunks differ by many binades (so the
+    common exponent pushes some chunks into the fp16 subnormals)."""
+    rng = np.random.default_rng(11)
+    rows = [rng.standard_normal(256), rng.standard_normal(256) * 2.0 ** 20,
+            rng.standard_normal(256) * 2.0 ** -20, np.zeros(256),
+            np.r_[rng.standard_normal(255), np.inf]]
+    mixed = rng.standard_normal(256) * 3
+    mixed[:32] *= 2.0 ** 30
+    mixed[64:96] *= 2.0 ** -14
+    rows.append(mixed)
+    for shift in (12, 16, 17, 24, 40):
+        r = rng.standard_normal(256)
+        r[32:64] *= 2.0 ** shift
+        rows.append(r)
+    return np.stack(rows)
+
+
+def test_emulated_activation_rounding_matches_numpy_twin():
+    rows = _emu_rows()
+    got = oracle.emulate_x_rows(rows)
+    ref = brute.f16_rows_scaled(rows)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    # ordinary bf16 activations pass through exactly
+    x = torch.randn(16, 256).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(oracle.emulate_x_rows(x), x)
+    # without the scaling, large rows would overflow fp16 and tiny ones lose bits
+    plant = brute.f16(rows[1:3])
+    assert not np.array_equal(plant, ref[1:3])
+
+
+def test_emulated_h_rounding_matches_numpy_twin():
+    rows = _emu_rows()
+    got = oracle.emulate_h_rows(rows)
+    ref = brute.f16_chunks_scaled(rows)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    # ordinary values: plain fp16 rounding, no exponent anywhere
+    assert np.array_equal(got[0], brute.f16(rows[0]))
+    # each slip in the chunk logic changes some row
+    for kw in ({"plant_no_chunk_exponent": True}, {"plant_no_common_exponent": True}):
+        bad = brute.f16_chunks_scaled(rows, **kw)
+        assert not np.array_equal(bad[ok], ref[ok]), kw
+
+
+def _emu_forward(wl, x=None):
+    x = wl.tokens.x if x is None else x
+    return oracle.forward(oracle.Layer.from_spec(wl.spec), x, wl.tokens.logits, wl.weights,
+                          nthreads=4, emulate=oracle.EMU_F16_DATAPATH)
+
+
+def _emu_brute(wl, x=None, **kw):
+    x = wl.tokens.x if x is None else x
+    return brute.dense_masked_forward(oracle.as_f64(x), oracle.as_f64(wl.tokens.logits),
+                                      wl.weights, wl.spec, emu_x=True, emu_w=True, emu_h=True, **kw)
+
+
+@pytest.mark.parametrize("name,T,xscale", [("tiny", 9, 1.0), ("decode", 2, 1.0), ("int3", 2, 1.0),
+                                           ("stack", 2, 1.0), ("decode", 2, 2.0 ** 9),
+                                           ("tiny", 6, 2.0 ** -16)])
+def test_emulated_datapath_against_dense_masked(name, T, xscale):
+    """The whole layer with the fp16 datapath's rounding points, against the
+    dense masked twin with the same points: fp32 activations (tiny), bf16
+    activations at every format, activations large enough that h leaves the
+    fp16 range (its chunk exponents engage) and activations so small that
+    they would fall into the fp16 subnormals without the per-token scaling."""
+    wl = qi.make_workload(name, T=T)
+    x = (wl.tokens.x.to(torch.float64) * xscale).to(wl.tokens.x.dtype)
+    acc = _emu_forward(wl, x)
+    ref = _emu_brute(wl, x)
+    assert np.isfinite(ref).all()
+    assert _close(acc, ref, rtol=1e-10)
+    plain = _brute(qi.Workload(wl.name, wl.spec, qi.Tokens(x, wl.tokens.logits), wl.weights))
+    # the rounding points move the result, but only by fp16 rounding noise
+    rel = np.linalg.norm(acc - plain, axis=1) / np.linalg.norm(plain, axis=1)
+    assert 1e-6 < rel.max() < 5e-3, rel.max()
+
+
+def test_emulated_datapath_planted_mistakes_are_visible():
+    """Each slip in the emulated rounding points moves the layer output far
+    beyond the agreement of the two emulations (1e-10 relative)."""
+    wl = qi.make_workload("decode", T=2)
+    acc = _emu_forward(wl)
+    for kw in ({"plant_h_unrounded": True},):
+        assert not _close(acc, _emu_brute(wl, **kw), rtol=1e-8), kw
+    w_plain = brute.dense_masked_forward(oracle.as_f64(wl.tokens.x), oracle.as_f64(wl.tokens.logits),
+                                         wl.weights, wl.spec, emu_x=True, emu_h=True)
+    assert not _close(acc, w_plain, rtol=1e-8)
+    big = (wl.tokens.x.to(torch.float64) * 2.0 ** 9).to(torch.bfloat16)
+    acc_big = _emu_forward(wl, big)
+    bad = _emu_brute(wl, big, plant_h_no_chunk_exponent=True)
+    assert not np.isfinite(bad).all() or not _close(acc_big, bad, rtol=1e-8)
+    wt = qi.make_workload("tiny", T=6)      # fp32 activations: x rounding matters
+    x_plain = brute.dense_masked_forward(oracle.as_f64(wt.tokens.x), oracle.as_f64(wt.tokens.logits),
+                                         wt.weights, wt.spec, emu_w=True, emu_h=True)
+    assert not _close(_emu_forward(wt), x_plain, rtol=1e-8)
+    huge = (wt.tokens.x.to(torch.float64) * 2.0 ** 20).to(torch.float32)
+    acc_h = _emu_forward(wt, huge)
+    bad = _emu_brute(wt, huge, plant_x_unscaled=True)
+    assert not np.isfinite(bad).all() or not _close(acc_h, bad, rtol=1e-8)
