@@ -80,33 +80,34 @@ def f16(v: np.ndarray) -> np.ndarray:
         return np.asarray(v, dtype=np.float64).astype(np.float16).astype(np.float64)
 
 
-def _range_exponent(M: np.ndarray) -> np.ndarray:
-    """e with M * 2^-e in [2^14, 2^15)."""
-    return np.frexp(M)[1].astype(np.int64) - 15
+def _range_exponent(M: np.ndarray, lo: float) -> np.ndarray:
+    """0 where M (finite, >= 0) is 0 or lies in [lo, 2^15], else the e with
+    M * 2^-e in [2^14, 2^15), clamped to [-120, 120]."""
+    e = np.clip(np.frexp(np.where(M > 0, M, 1.0))[1].astype(np.int64) - 15, -120, 120)
+    return np.where((M == 0) | ((M >= lo) & (M <= 32768.0)), 0, e)
 
 
 def f16_rows_scaled(x: np.ndarray) -> np.ndarray:
-    """Each row rounded to fp16 after an exact scaling that puts its largest
-    magnitude in [2^14, 2^15) (rows that are zero or not finite: no scaling)."""
+    """Each row rounded to fp16 after an exact scaling by its range exponent
+    (lower bound 2^-3; rows with a non-finite value: no scaling)."""
     finite = np.isfinite(x).all(axis=-1, keepdims=True)
     M = np.where(finite, np.abs(np.where(np.isfinite(x), x, 0.0)).max(axis=-1, keepdims=True), 0.0)
-    e = np.where(M > 0, _range_exponent(np.where(M > 0, M, 1.0)), 0)
+    e = _range_exponent(M, 2.0 ** -3)
     return np.ldexp(f16(np.ldexp(x, -e)), e)
 
 
 def f16_chunks_scaled(h: np.ndarray, chunk: int = 32, *, plant_no_chunk_exponent: bool = False,
                       plant_no_common_exponent: bool = False) -> np.ndarray:
     """h [..., I] as FC2 of the fp16 datapath reads it: per chunk of 32 values,
-    an exponent only when the chunk's largest magnitude M is nonzero, finite
-    and outside [2^-10, 2^15]; each chunk stored as fp16 at its exponent, then
-    brought to the row's largest chunk exponent E with a second fp16
-    rounding. The plant_* switches drop one step (for the pin tests)."""
+    the range exponent of the chunk (lower bound 2^-14; none for a chunk
+    with a non-finite value); each chunk stored as fp16 at its exponent, then brought to the
+    row's largest chunk exponent E with a second fp16 rounding. The plant_*
+    switches drop one step (for the pin tests)."""
     lead, I = h.shape[:-1], h.shape[-1]
     c = h.reshape(*lead, I // chunk, chunk)
     finite = np.isfinite(c).all(axis=-1, keepdims=True)
     M = np.where(finite, np.abs(np.where(np.isfinite(c), c, 0.0)).max(axis=-1, keepdims=True), 0.0)
-    out_of_range = (M > 0) & ((M > 2.0 ** 15) | (M < 2.0 ** -10))
-    e = np.where(out_of_range, _range_exponent(np.where(M > 0, M, 1.0)), 0)
+    e = _range_exponent(M, 2.0 ** -14)
     if plant_no_chunk_exponent:
         e = np.zeros_like(e)
     stored = f16(np.ldexp(c, -e))

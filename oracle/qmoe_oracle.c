@@ -262,17 +262,18 @@ int oracle_permute(const int32_t *topk_id, int64_t R, int64_t E, int32_t *counts
 
 /* Rounding-point emulation of the fp16 matrix-core datapath of the grouped
  * (prefill) path (off by default; each flag rounds one operand):
- *  EMU_X_F16: token t's activations x enter as fp16 after an exact scaling by
- *    2^-e_t, where M = max |x_t| and e_t = (exponent of M) - 15, so the
- *    scaled maximum lies in [2^14, 2^15): x' = fp16(x * 2^-e_t) * 2^e_t
- *    (e_t = 0 for a zero or non-finite M);
+ * A range exponent e of a set of values with largest magnitude M, for a
+ * lower bound lo, is 0 while M lies in [lo, 2^15] (or M is 0 or the set holds
+ * a non-finite value), else (exponent of M) - 15, which puts M * 2^-e in
+ * [2^14, 2^15), clamped to [-120, 120]; values v are then stored as
+ * fp16(v * 2^-e).
+ *  EMU_X_F16: token t's activations enter as fp16(x * 2^-e_t) * 2^e_t, e_t
+ *    the range exponent (lo = 2^-3) of the token's row;
  *  EMU_W_F16: each dequantized weight is fp16((q - zp) * s);
  *  EMU_H_F16: each route's SwiGLU output h enters FC2 as fp16 in chunks of
- *    32 consecutive values n: a chunk whose maximum magnitude M lies outside
- *    [2^-10, 2^15] (and is nonzero, finite) gets the exponent
- *    e_c = (exponent of M) - 15, else e_c = 0, and is stored as
- *    fp16(h * 2^-e_c); the route's exponent is E = max_c e_c and FC2 reads
- *    fp16(stored * 2^(e_c - E)) * 2^E.
+ *    32 consecutive values n: chunk c is stored as fp16(h * 2^-e_c), e_c its
+ *    range exponent (lo = 2^-14); the route's exponent is E = max_c e_c and
+ *    FC2 reads fp16(stored * 2^(e_c - E)) * 2^E.
  * fp16() is oracle_double_to_half: nearest, ties to even, gradual underflow. */
 #define EMU_X_F16 1
 #define EMU_W_F16 2
@@ -291,12 +292,15 @@ static double to_bf16(double v)
     return (double)f;
 }
 
-/* Exponent of the power of two that puts M in [2^14, 2^15). */
-static int range_exponent(double M)
+/* The range exponent of a set of values with largest magnitude M (finite),
+ * for the lower bound lo. */
+static int range_exponent(double M, double lo)
 {
+    if (M == 0.0 || (M >= lo && M <= 32768.0)) return 0;
     int ex;
     (void)frexp(M, &ex);       /* M = f * 2^ex, f in [0.5, 1): M * 2^-(ex-15) in [2^14, 2^15) */
-    return ex - 15;
+    int e = ex - 15;
+    return e < -120 ? -120 : e > 120 ? 120 : e;
 }
 
 static void emulate_x(const double *x, int64_t H, double *out)
@@ -307,7 +311,7 @@ static void emulate_x(const double *x, int64_t H, double *out)
         if (!isfinite(x[i])) finite = 0;
         else if (fabs(x[i]) > M) M = fabs(x[i]);
     }
-    int e = (finite && M > 0.0) ? range_exponent(M) : 0;
+    int e = finite ? range_exponent(M, 0.125) : 0;
     for (int64_t i = 0; i < H; ++i) out[i] = ldexp(round_half(ldexp(x[i], -e)), e);
 }
 
@@ -325,8 +329,7 @@ static void emulate_h(double *h, int64_t I)
             if (!isfinite(h[n])) finite = 0;
             else if (fabs(h[n]) > M) M = fabs(h[n]);
         }
-        int e = 0;
-        if (finite && M > 0.0 && (M > 32768.0 || M < ldexp(1.0, -10))) e = range_exponent(M);
+        int e = finite ? range_exponent(M, ldexp(1.0, -14)) : 0;
         ec[c] = e;
         if (e > E) E = e;
         for (int64_t n = c * EMU_H_CHUNK; n < (c + 1) * EMU_H_CHUNK; ++n) h[n] = round_half(ldexp(h[n], -e));
