@@ -35,7 +35,10 @@ same workload on this host's cores.
 Extra entries: M=1 decode and the 8192-token prefill of the same layer; the
 INT3 (block 64) layer at M=4 decode and as a 2048-token prefill; one pass over
 a stack of 48 independent INT2 (block 32) layers with Zipf routing drawn per
-layer, at M=1 decode and as a 32768-token packed prefill.
+layer, at M=1 decode and as a 32768-token packed prefill; batches of 32 and
+64 tokens of the INT4 layer (the small-batch path). Each entry reports the
+per-step min / median / max over its timed steps; prefill entries the load
+skew of their routing (routes per expert).
 
 `--only <workload>` runs one workload alone (for profiling) and prints its
 results instead of the benchmark line.
@@ -167,6 +170,21 @@ def _hold_stream(seconds: float):
     torch.cuda._sleep(int(_SLEEP_CYCLES * seconds))
 
 
+def step_spread(step, K: int, hold_s: float):
+    """Per-step GPU times (us) of K calls, each bracketed by events on the
+    stream while a spin kernel holds it: min, median and max."""
+    torch.cuda.synchronize()
+    _hold_stream(hold_s)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    evs[0].record()
+    for i in range(K):
+        step(i)
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    us = np.array([evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(K)])
+    return {"min": float(us.min()), "median": float(np.median(us)), "max": float(us.max())}
+
+
 def time_steps(step, K: int, hold_s: float):
     """GPU time of exactly K calls of step(i), host enqueue hidden behind a spin kernel."""
     torch.cuda.synchronize()
@@ -237,7 +255,9 @@ def bench_decode(T: int, steps: int, warmup: int, name: str = "decode"):
     for i in range(warmup):
         step(i)
     ms, enq, wall = time_steps(step, steps, hold_s=0.002 + steps * 1e-4)
-    log(f"[bench] {name} M={T}: {ms * 1e3:.2f} us/step (enqueue {enq * 1e3:.1f} ms, wall {wall * 1e3:.1f} ms)")
+    spread = step_spread(step, steps, hold_s=0.002 + steps * 1e-4)
+    log(f"[bench] {name} M={T}: {ms * 1e3:.2f} us/step (enqueue {enq * 1e3:.1f} ms, wall {wall * 1e3:.1f} ms); "
+        f"per step min {spread['min']:.2f} median {spread['median']:.2f} max {spread['max']:.2f} us")
     kt = kernel_times([it[0] for it in insts], step, min(steps, 4 * NROT), hold_s=0.01)
     log(f"[bench] {name} M={T} kernels (us): " + ", ".join(f"{k}={v * 1e3:.2f}" for k, v in kt.items()))
     fc1_b, fc2_b = expert_bytes(spec)
@@ -254,6 +274,7 @@ def bench_decode(T: int, steps: int, warmup: int, name: str = "decode"):
         dom = "decode_fused"
         dom_bytes = layer_bytes
         t_dom = ms * 1e-3
+        kt = {"decode_fused": ms}
     else:
         dom = "decode_fc1_swiglu"
         dom_bytes = fc1_bytes
@@ -264,6 +285,7 @@ def bench_decode(T: int, steps: int, warmup: int, name: str = "decode"):
         "layer_GBs": layer_bytes / (ms * 1e-3) / 1e9,
         "layer_frac_hbm": layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "kernels_us": {kk: v * 1e3 for kk, v in kt.items()},
+        "step_us": spread,
         "dominant": {"kernel": dom, "bytes": dom_bytes, "s": t_dom, "GBs": dom_bytes / t_dom / 1e9},
     }
 
@@ -282,7 +304,13 @@ def bench_prefill(steps: int, warmup: int, name: str = "prefill", T: int = 8192)
 
     for i in range(warmup):
         step(i)
+    ids, _ = L.routing_from_workspace(T, ws)
+    per_expert = torch.bincount(ids.reshape(-1).long(), minlength=spec.num_experts).float()
+    skew = {"max_routes_per_expert": int(per_expert.max().item()),
+            "mean_routes_per_active_expert": float(per_expert[per_expert > 0].mean().item()),
+            "active_experts": int((per_expert > 0).sum().item())}
     ms, enq, wall = time_steps(step, steps, hold_s=0.005)
+    spread = step_spread(step, steps, hold_s=0.005)
     kt = kernel_times([L], step, steps, hold_s=0.005)
     log(f"[bench] {name} {T}: {ms:.3f} ms/step; kernels (us): "
         + ", ".join(f"{k}={v * 1e3:.1f}" for k, v in kt.items()))
@@ -296,8 +324,48 @@ def bench_prefill(steps: int, warmup: int, name: str = "prefill", T: int = 8192)
         "layer_TFLOPs": flops / (ms * 1e-3) / 1e12,
         "layer_frac_mfma": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
         "kernels_us": {kk: v * 1e3 for kk, v in kt.items()},
+        "step_us": spread, "load_skew": skew,
         "fc1": {"flops": fc1_flops, "s": t_fc1, "TFLOPs": fc1_flops / t_fc1 / 1e12},
     }
+
+
+def bench_small(T: int, steps: int, warmup: int):
+    """Batches between decode and prefill (the small-batch path): one layer
+    call on T tokens, rotating NROT / 4 seeded instances so the MALL holds
+    none of the active experts' weights. Roofline: the active experts'
+    weight bytes (each streamed once per call) over the call's time."""
+    spec = qi.QWEN3_INT4
+    n = NROT // 4
+    log(f"[bench] small batch T={T}: building {n} layer instances")
+    insts = [device_instance(spec, T, 7000 + T + i, T) for i in range(n)]
+    ws = insts[0][0].workspace(T)
+    out = torch.empty((T, spec.hidden), dtype=torch.bfloat16, device=DEV)
+
+    def step(i):
+        L, x, l = insts[i % n]
+        L.forward(x, l, out=out, workspace=ws)
+
+    distinct = []
+    for i in range(n):
+        step(i)
+        ids, _ = insts[i][0].routing_from_workspace(T, ws)
+        distinct.append(int(torch.unique(ids).numel()))
+    for i in range(warmup):
+        step(i)
+    ms, enq, wall = time_steps(step, steps, hold_s=0.002 + steps * 2e-4)
+    spread = step_spread(step, steps, hold_s=0.002 + steps * 2e-4)
+    kt = kernel_times([it[0] for it in insts], step, min(steps, 4 * n), hold_s=0.01)
+    fc1_b, fc2_b = expert_bytes(spec)
+    D = float(np.mean([distinct[i % n] for i in range(steps)]))
+    H, E = spec.hidden, spec.num_experts
+    layer_bytes = D * (fc1_b + fc2_b) + T * H * 2 * 2 + T * E * 2
+    log(f"[bench] small batch T={T}: {ms * 1e3:.1f} us/step, {D:.1f} experts, kernels (us): "
+        + ", ".join(f"{k}={v * 1e3:.1f}" for k, v in kt.items()))
+    for L, _, _ in insts:
+        L.close()
+    return {"T": T, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3), "distinct_experts": D,
+            "layer_frac_hbm": layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "kernels_us": {kk: v * 1e3 for kk, v in kt.items()}, "step_us": spread}
 
 
 def bench_stack(T: int, steps: int, warmup: int):
@@ -346,36 +414,61 @@ def bench_stack(T: int, steps: int, warmup: int):
 
 
 def cpu_model() -> str:
+    """The host CPU's model name, as /proc/cpuinfo and lscpu give it."""
+    names = []
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
                 if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                    names.append(line.split(":", 1)[1].strip())
+                    break
     except OSError:
         pass
-    return "unknown"
+    try:
+        import subprocess
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith(("Model name", "Vendor ID", "Socket(s)", "Core(s) per socket")):
+                names.append(" ".join(line.split()))
+    except Exception:
+        pass
+    return "; ".join(names) if names else "unknown"
 
 
 def cpu_baseline(n_tokens: int):
-    """The oracle on a bounded sample of decode tokens: all host cores (the
-    reported value), and one thread on an eighth of the sample."""
+    """The oracle, as it stands, on bounded samples of each workload: all
+    host cores (the reported value is the decode workload's), and one thread
+    on a smaller sample. The 48 layers of the stack are independent and of
+    one shape, so one layer's sampled per-token cost stands for each."""
     import oracle
-    wl = qi.make_workload("decode", T=n_tokens)
     threads = oracle.default_threads()
-    layer = oracle.Layer.from_spec(wl.spec)
-    t0 = time.perf_counter()
-    oracle.forward(layer, wl.tokens.x, wl.tokens.logits, wl.weights, nthreads=threads)
-    dt = time.perf_counter() - t0
+
+    def timed(name, T, nthreads, **kw):
+        wl = qi.make_workload(name, T=T, **kw)
+        layer = oracle.Layer.from_spec(wl.spec)
+        t0 = time.perf_counter()
+        oracle.forward(layer, wl.tokens.x, wl.tokens.logits, wl.weights, nthreads=nthreads)
+        return time.perf_counter() - t0
+
+    dt = timed("decode", n_tokens, threads)
     n1 = max(1, n_tokens // 8)
-    t0 = time.perf_counter()
-    oracle.forward(layer, wl.tokens.x[:n1], wl.tokens.logits[:n1], wl.weights, nthreads=1)
-    dt1 = time.perf_counter() - t0
+    dt1 = timed("decode", n1, 1)
+    others = {}
+    for label, name, T in (("prefill_8k_sample", "prefill", 128), ("int3_sample", "int3", 64),
+                           ("stack_layer_sample", "stack", 256)):
+        d = timed(name, T, threads)
+        others[label] = {"value": T / d, "unit": "tokens/s per layer", "tokens": T, "wall_s": d}
     log(f"[bench] cpu baseline: {threads} threads {n_tokens / dt:.1f} tokens/s, "
-        f"1 thread {n1 / dt1:.2f} tokens/s ({cpu_model()})")
+        f"1 thread {n1 / dt1:.2f} tokens/s; " + ", ".join(f"{k} {v['value']:.1f}" for k, v in others.items()))
     return {"value": n_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{n_tokens} tokens of the decode workload (Qwen3-30B-A3B-shaped INT4 bs32 "
                       f"layer, uniform routing), {dt:.1f} s wall on {threads} threads",
             "single_thread": {"value": n1 / dt1, "unit": "tokens/s", "sample": f"{n1} tokens"},
+            "other_workloads": {
+                **others,
+                "note": "prefill: the first 128 tokens of the 8192-token Zipf workload; int3: 64 tokens "
+                        "of the INT3 bs64 layer; stack: 256 tokens of layer 0 of the 48-layer INT2 "
+                        "stack (every layer has this shape and cost; a pass costs 48 times a layer)"},
             "cpu_model": cpu_model()}
 
 
@@ -389,7 +482,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=96)
     ap.add_argument("--only", choices=["decode4", "decode1", "prefill", "int3_decode4",
-                                       "int3_prefill", "stack_decode1", "stack_prefill"],
+                                       "int3_prefill", "stack_decode1", "stack_prefill",
+                                       "small32", "small64"],
                     default=None,
                     help="run one workload alone (profiling aid); prints its results")
     ap.add_argument("--source-digest", action="store_true",
@@ -414,6 +508,8 @@ def main():
             res = bench_prefill(args.steps, args.warmup, "int3", 2048)
         elif args.only == "int3_decode4":
             res = bench_decode(4, args.steps, args.warmup, "int3")
+        elif args.only.startswith("small"):
+            res = bench_small(int(args.only[5:]), args.steps, args.warmup)
         elif args.only.startswith("stack"):
             res = bench_stack(1 if args.only == "stack_decode1" else 32768, args.steps, args.warmup)
         else:
@@ -430,16 +526,19 @@ def main():
         i3p = bench_prefill(args.prefill_steps, 3, "int3", 2048)
         sd = bench_stack(1, 20, 3)
         sp = bench_stack(32768, 3, 1)
+        smalls = [bench_small(T, args.steps // 2, args.warmup) for T in (32, 64)]
         extra = [
             {"workload": "decode M=1", "tokens_per_s": m1["tokens_per_s"],
              "ms_per_step": m1["ms_per_step"], "layer_frac_hbm": m1["layer_frac_hbm"],
              "distinct_experts": m1["distinct_experts"], "kernels_us": m1["kernels_us"],
+             "step_us": m1["step_us"],
              "roofline": {"bound": "hbm", "kernel": m1["dominant"]["kernel"],
                           "achieved": m1["dominant"]["GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": m1["dominant"]["GBs"] / HBM_PEAK_GBS}},
             {"workload": "prefill 8192 tokens (16 packed sequences, Zipf-skewed routing)",
              "tokens_per_s": pf["tokens_per_s"], "ms_per_step": pf["ms_per_step"],
              "layer_frac_mfma": pf["layer_frac_mfma"], "kernels_us": pf["kernels_us"],
+             "step_us": pf["step_us"], "load_skew": pf["load_skew"],
              "roofline": {"bound": "mfma", "kernel": "gemm_fc1_swiglu",
                           "achieved": pf["fc1"]["TFLOPs"], "peak": BF16_PEAK_TFLOPS,
                           "unit": "TFLOP/s", "frac": pf["fc1"]["TFLOPs"] / BF16_PEAK_TFLOPS,
@@ -455,6 +554,7 @@ def main():
             {"workload": "INT3 bs64 layer prefill 2048 tokens (8 packed sequences)",
              "tokens_per_s": i3p["tokens_per_s"], "ms_per_step": i3p["ms_per_step"],
              "layer_frac_mfma": i3p["layer_frac_mfma"], "kernels_us": i3p["kernels_us"],
+             "step_us": i3p["step_us"], "load_skew": i3p["load_skew"],
              "roofline": {"bound": "mfma", "kernel": "gemm_fc1_swiglu",
                           "achieved": i3p["fc1"]["TFLOPs"], "peak": BF16_PEAK_TFLOPS,
                           "unit": "TFLOP/s", "frac": i3p["fc1"]["TFLOPs"] / BF16_PEAK_TFLOPS}},
@@ -466,6 +566,12 @@ def main():
              "tokens_per_s": sp["tokens_per_s"], "ms_per_pass": sp["ms_per_pass"],
              "layer_us": sp["layer_us"], "flops_per_pass": sp["flops_per_pass"],
              "frac_mfma": sp["frac_mfma"]},
+        ] + [
+            {"workload": f"small batch {r['T']} tokens (uniform routing, small-batch path)",
+             "tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"],
+             "distinct_experts": r["distinct_experts"], "layer_frac_hbm": r["layer_frac_hbm"],
+             "kernels_us": r["kernels_us"], "step_us": r["step_us"]}
+            for r in smalls
         ]
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_tokens)
 
@@ -488,7 +594,7 @@ def main():
                    "tokens_per_step": 4, "layer_instances_rotated": NROT,
                    "distinct_experts_per_step": main_res["distinct_experts"],
                    "layer_frac_hbm": main_res["layer_frac_hbm"],
-                   "kernels_us": main_res["kernels_us"]},
+                   "kernels_us": main_res["kernels_us"], "step_us": main_res["step_us"]},
         "roofline": {"bound": "hbm", "kernel": dom["kernel"], "achieved": dom["GBs"],
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dom["GBs"] / HBM_PEAK_GBS,
                      "bytes_per_launch": dom["bytes"],

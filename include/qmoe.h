@@ -38,7 +38,13 @@
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream);
  *    work is enqueued asynchronously and the call returns without
  *    synchronizing; only launch errors are reported (QMOE_ERR_HIP);
- *  - a handle may be used from one stream at a time.
+ *  - a handle may be used from one stream at a time (see qmoe_create);
+ *  - environment variables read once, by qmoe_create, change nothing unless
+ *    set: QMOE_FORCE_PATH=prefill|decode_split forces one path (debugging and
+ *    tests); QMOE_FUSED_GRID, QMOE_FUSED_EPOCH_START and QMOE_FUSED_SPIN_LIMIT
+ *    are test hooks of the fused decode (a smaller grid, the epoch counter's
+ *    start, the bound of its waits) that exist so the tests can reach its
+ *    rare schedules and error paths.
  */
 #ifndef QMOE_H
 #define QMOE_H
@@ -121,6 +127,25 @@ typedef struct qmoe_handle qmoe_handle;
  * stores them; the weights are neither copied nor freed and must outlive the
  * handle. `device` is the HIP device ordinal the weights live on.
  * On success *out receives the handle; on error *out is set to NULL.
+ *
+ * Validation follows the pages' fail-closed admission: dimensions must be
+ * positive and representable, the expert count nonzero, and enums in range
+ * ("[CUDA] Add INT4 and INT3 QMoE CPU/GPU offload support", review-fix
+ * commits on weights_prepacked normalization and E = 0 rejection).
+ *
+ * Besides host state, a handle whose layer the fused decode serves (bf16 or
+ * fp16 activations, E <= 256, H <= 2048, I <= 1024) owns one device buffer
+ * on `device`: the exchange area the fused decode's workgroups pass h and y
+ * through, 256 + 4 * top_k * (inter + hidden) * 8 bytes (about 3 MB at the
+ * Qwen3-30B-A3B shape), allocated and zeroed here and freed by
+ * qmoe_destroy. Its entries carry a per-call epoch that the handle counts
+ * on the host, so one handle must be used from one stream at a time: two
+ * streams driving one handle concurrently race on that buffer. (Calls
+ * under HIP graph capture never use it: see qmoe_forward.)
+ * Errors: QMOE_ERR_INVALID_ARG for a bad config, pointer or device ordinal;
+ * QMOE_ERR_UNSUPPORTED beyond this implementation's limits (E > 1024,
+ * top_k > 32, hidden or inter > 8192); QMOE_ERR_HIP if a device call fails;
+ * QMOE_ERR_OOM if the host allocation fails.
  */
 qmoe_status qmoe_create(const qmoe_config *config, const qmoe_weights *weights, int device,
                         qmoe_handle **out);
@@ -128,8 +153,16 @@ qmoe_status qmoe_create(const qmoe_config *config, const qmoe_weights *weights, 
 /*
  * Bytes of device workspace qmoe_forward needs for `num_tokens` tokens
  * (0 <= num_tokens <= max_tokens). The workspace holds the routing arrays,
- * the permutation, the per-route intermediate activations and per-route fp32
- * FC2 outputs; it carries no state between calls.
+ * the expert-sorted permutation and tile list, the per-route intermediate
+ * activations and the per-route fp32 FC2 outputs; it carries no state
+ * between calls and needs no initialisation. The size is computed from the
+ * shapes and checked by qmoe_forward, never assumed: a review on the pages
+ * asks that the prefill scratch, computed by a workspace-size function, be
+ * checked against every resolved device budget ("[CUDA] Add MoEPacked
+ * CPU/GPU hybrid offload and consolidate QMoE/GGUF offload optimizations",
+ * review comment on the device working budget).
+ * Errors: QMOE_ERR_INVALID_ARG for a NULL handle or `bytes`, or num_tokens
+ * outside [0, max_tokens].
  */
 qmoe_status qmoe_workspace_size(const qmoe_handle *handle, int64_t num_tokens, size_t *bytes);
 
@@ -140,30 +173,66 @@ qmoe_status qmoe_workspace_size(const qmoe_handle *handle, int64_t num_tokens, s
  *  out     device [num_tokens, hidden]       act_dtype (written)
  *  workspace / workspace_bytes: caller-owned device scratch of at least
  *          qmoe_workspace_size(num_tokens) bytes.
- * num_tokens == 0 returns QMOE_OK and launches nothing. Tokens 1..4 take the
- * memory-bound decode path; larger counts take the grouped-GEMM prefill path.
+ * num_tokens == 0 returns QMOE_OK and launches nothing.
+ *
+ * The method: top-k of the raw router logits, softmax over the selected k,
+ * the expert FFNs on dequantized weights W = (q - zp) * s with SwiGLU, and a
+ * routing-weighted sum in fp32 rounded once ("Document and test packed token
+ * inputs for MoE and QMoE", Description and review of the test harness;
+ * "[CUDA/CPU] Add AVX2 INT4 cold-expert kernel and zero-cold doorbell
+ * short-circuit for QMoE offload", Motivation & Summary item 3; "[CUDA] Add
+ * MoEPacked CPU/GPU hybrid offload and consolidate QMoE/GGUF offload
+ * optimizations", Key Changes item 4).
+ *
+ * Dispatch:
+ *  - 1..4 tokens: the fused single-launch decode where it applies (see
+ *    qmoe_create), else the split decode (three launches);
+ *  - 5..24 tokens on layers the fused decode serves: the fused decode once
+ *    per group of up to four tokens;
+ *  - otherwise: routing, then the grouped fp16 matrix-core GEMMs over
+ *    expert-sorted routes, then the combine.
+ * A call made while `stream` is being captured into a HIP graph takes the
+ * split decode (1..4 tokens) or the grouped GEMMs (above): the fused
+ * decode's per-call epoch cannot be replayed.
+ *
+ * The fused decode's workgroups exchange results through the handle's
+ * buffer and each needs the others resident at once; its grid is one
+ * workgroup per compute unit, so it assumes the device is otherwise idle
+ * while it runs. A wait that runs out (a workgroup that could not start,
+ * for instance) sets an error bit instead of hanging; outputs of the calls
+ * since the last qmoe_decode_errors query may then be wrong, and that query
+ * reports it.
  */
 qmoe_status qmoe_forward(qmoe_handle *handle, const void *x, const void *logits, void *out,
                          int64_t num_tokens, void *workspace, size_t workspace_bytes,
                          void *stream);
 
-/* Release a handle (host state only). qmoe_destroy(NULL) returns QMOE_OK. */
+/* Release a handle: its host state and, when it has one, its device
+ * exchange buffer (after which no call may be in flight on it).
+ * qmoe_destroy(NULL) returns QMOE_OK. */
 qmoe_status qmoe_destroy(qmoe_handle *handle);
 
 /* Static, human-readable text for a status code. */
-const char *qmoe_status_string(qmoe_status status);
+const char *qmoe_status_string(int status);
 
 /*
  * Test exports. Same conventions as above.
  *
  * qmoe_route runs only the routing stage of the prefill path on `num_tokens`
- * tokens (any count 1..max_tokens) and copies its results out:
+ * tokens (any count 1..max_tokens) and copies its results out. The
+ * expert-sorted route map with per-expert first offsets is the grouped
+ * GEMMs' input ("[CUDA] Add INT4 and INT3 QMoE CPU/GPU offload support",
+ * Description: sorted routes, tile descriptors, expert first-token offsets);
+ * the order within an expert is the stable order of the route ids:
  *   topk_id        int32 [T, top_k]   selected experts, slot order
  *   topk_w         fp32  [T, top_k]   softmax over the selected logits
  *   expert_offsets int32 [E + 1]      exclusive prefix sum of routes per expert
  *   sorted_routes  int32 [T * top_k]  route ids r = t*top_k + j, stably sorted by expert
  *   inv_pos        int32 [T * top_k]  position of route r in sorted_routes
  * All output pointers are device pointers; any of them may be NULL to skip it.
+ * Errors: QMOE_ERR_INVALID_ARG for a bad handle, count or logits pointer;
+ * QMOE_ERR_WORKSPACE if the workspace is smaller than
+ * qmoe_workspace_size(num_tokens) of the grouped path.
  */
 qmoe_status qmoe_route(qmoe_handle *handle, const void *logits, int64_t num_tokens,
                        int32_t *topk_id, float *topk_w, int32_t *expert_offsets,
@@ -173,19 +242,30 @@ qmoe_status qmoe_route(qmoe_handle *handle, const void *logits, int64_t num_toke
 /*
  * qmoe_dequant writes the dequantized matrix of one expert of FC1 (fc = 1,
  * [2*inter, hidden]) or FC2 (fc = 2, [hidden, inter]) using the kernels' own
- * unpacking routines:
- *   out_f32  device fp32 [N, K]: (q - zp) * scale as read by the decode path
- *   out_bf16 device bf16 bits [N, K]: the round-to-nearest-even bf16 value the
- *            prefill path stages for the matrix cores
- * Either output may be NULL.
+ * routines, for W = (q - zp) * s ("[CUDA] Add INT4 and INT3 QMoE CPU/GPU
+ * offload support", Description: raw integer experts, block sizes
+ * 32/64/128, scales [N, K/block]; "[CUDA/CPU] Add AVX2 INT4 cold-expert
+ * kernel and zero-cold doorbell short-circuit for QMoE offload",
+ * Motivation & Summary item 3: unsigned codes with a zero point):
+ *   out_f32  device fp32 [N, K]: (q - zp) * s, exact, from the codes the
+ *            decode paths' matrix operands carry (each code as 1 + q/128)
+ *   out_f16  device fp16 bits [N, K]: fp16((q - zp) * s), rounded once to
+ *            nearest even, from the same routine the grouped GEMMs' staging
+ *            calls
+ * Either output may be NULL. Errors: QMOE_ERR_INVALID_ARG for a bad handle,
+ * fc or expert.
  */
 qmoe_status qmoe_dequant(qmoe_handle *handle, int fc, int64_t expert, float *out_f32,
-                         uint16_t *out_bf16, void *stream);
+                         uint16_t *out_f16, void *stream);
 
 /*
  * Byte offsets, inside the workspace of a qmoe_forward call on `num_tokens`
  * tokens, of the routing results that call leaves behind: topk_id (int32
- * [T, top_k]) and topk_w (fp32 [T, top_k]). Both paths write them.
+ * [T, top_k]) and topk_w (fp32 [T, top_k]), the top-k over raw logits and
+ * the softmax over the selected ("Document and test packed token inputs for
+ * MoE and QMoE", review of the test harness). Both paths write them.
+ * Errors: QMOE_ERR_INVALID_ARG for a NULL argument or a count outside
+ * [0, max_tokens].
  */
 qmoe_status qmoe_workspace_routing(const qmoe_handle *handle, int64_t num_tokens,
                                    size_t *topk_id_offset, size_t *topk_w_offset);
@@ -208,7 +288,9 @@ qmoe_status qmoe_workspace_routing(const qmoe_handle *handle, int64_t num_tokens
 qmoe_status qmoe_decode_errors(qmoe_handle *handle, void *stream, uint32_t *bits);
 
 /*
- * Profiling hook. When set, qmoe_forward calls fn(user, stage, name) on the
+ * Profiling hook, for per-kernel time per layer as the pages measure it
+ * ("[CUDA] Add INT4 and INT3 QMoE CPU/GPU offload support", GPU kernel time
+ * per layer). When set, qmoe_forward calls fn(user, stage, name) on the
  * host right after it enqueues each kernel (stage = 1, 2, ... in launch order,
  * name = the kernel's role, a static string), and once with stage = 0 before
  * the first launch. It lets a caller record events on the stream between the

@@ -117,6 +117,25 @@ class LayerConfig:
     fc1_interleaved: bool = False    # FC1 rows 2n / 2n+1 = gate n / up n (else gate block, up block)
 
 
+def check_weight_shapes(cfg: LayerConfig, fc1_codes, fc1_scales, fc2_codes, fc2_scales):
+    """Raise ValueError unless the four weight tensors have the layout the
+    library reads: codes uint8 [E, N, K*bits/8] and scales fp16 [E, N, K/bs],
+    N x K = 2I x H for FC1 and H x I for FC2. The library cannot check sizes
+    behind raw pointers, and a tensor that is too small would be read out of
+    bounds on the GPU."""
+    E, H, I, b, bs = cfg.num_experts, cfg.hidden, cfg.inter, cfg.bits, cfg.block_size
+    if b not in (2, 3, 4) or bs not in (32, 64, 128) or H <= 0 or I <= 0 or H % bs or I % bs:
+        raise ValueError("bits must be 2, 3 or 4 and block_size 32, 64 or 128, dividing hidden "
+                         "and inter")
+    want = (("fc1_codes", fc1_codes, (E, 2 * I, H * b // 8)),
+            ("fc1_scales", fc1_scales, (E, 2 * I, H // bs)),
+            ("fc2_codes", fc2_codes, (E, H, I * b // 8)),
+            ("fc2_scales", fc2_scales, (E, H, I // bs)))
+    for name, t, shape in want:
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} must be shaped {shape}, got {tuple(t.shape)}")
+
+
 class QMoELayer:
     """One quantized MoE layer resident on a GPU.
 
@@ -132,6 +151,7 @@ class QMoELayer:
                  fc1_bias: Optional[torch.Tensor] = None, fc2_bias: Optional[torch.Tensor] = None,
                  fc1_zero_points: Optional[torch.Tensor] = None,
                  fc2_zero_points: Optional[torch.Tensor] = None):
+        check_weight_shapes(cfg, fc1_codes, fc1_scales, fc2_codes, fc2_scales)
         for t in (fc1_codes, fc1_scales, fc2_codes, fc2_scales):
             if not t.is_cuda or not t.is_contiguous():
                 raise ValueError("weights must be contiguous GPU tensors")
@@ -278,10 +298,10 @@ class QMoELayer:
         return ids, w, offs, srt, inv
 
     def dequant(self, fc: int, expert: int):
-        """(fp32 [N, K] as the decode path reads it, bf16 [N, K] as the prefill path stages it)."""
+        """(fp32 [N, K] as the decode path reads it, fp16 [N, K] as the prefill path stages it)."""
         c = self.cfg
         N, K = (2 * c.inter, c.hidden) if fc == 1 else (c.hidden, c.inter)
         f = torch.empty((N, K), dtype=torch.float32, device=self.device)
         b = torch.empty((N, K), dtype=torch.int16, device=self.device)
         _check(lib().qmoe_dequant(self._h, fc, expert, _ptr(f), _ptr(b), _stream()), "qmoe_dequant")
-        return f, b.view(torch.bfloat16)
+        return f, b.view(torch.float16)

@@ -14,7 +14,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(os.path.dirname(HERE), "_build")
 LIB = os.path.join(HERE, "libqmoe.so")
-SOURCES = ["api.hip", "route.hip", "decode.hip", "decode_fused.hip", "prefill.hip", "dequant.hip"]
+SOURCES = ["api.hip", "route.hip", "decode.hip", "decode_fused.hip", "prefill.hip", "small.hip",
+           "dequant.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -17,9 +17,10 @@
 struct qmoe_handle {
   qmoe::Layer L;
   int device;
-  bool force_prefill;
+  int force;              // QMOE_FORCE_PATH: one of the kForce* values below
   bool split_decode;      // use the two-kernel decode even where the fused one applies
   bool fused_ok;          // fused single-launch decode applies to this layer
+  bool small_ok;          // the small-batch path applies to this layer
   int fused_grid;         // resident workgroups for the fused decode
   uint32_t spin_limit;    // fused decode wait bound in polls (0: the library default)
   uint32_t calls;         // epoch of the last fused decode call launched (0: none yet)
@@ -45,23 +46,41 @@ GemvShape gemv_shape(int64_t K, int min_rows_block) {
   return s;
 }
 
-// Small batches above the fused kernel's four tokens run it once per group of
-// up to four tokens: each launch streams only its group's experts, which up to
-// this many tokens beats the grouped GEMMs (whose 256-row tiles pay their
-// per-stage latency for a handful of rows).
-constexpr int64_t kGroupedDecodeMaxTokens = 24;
+// Paths forced from the environment (QMOE_FORCE_PATH, read at create).
+constexpr int kForceNone = 0, kForcePrefill = 1, kForceSmall = 2, kForceGrouped = 3;
 
-bool use_decode_path(const Layer& L, bool force_prefill, bool grouped_ok, int64_t T) {
-  if (force_prefill || T < 1) return false;
-  return T <= kDecodeMaxTokens || (grouped_ok && T <= kGroupedDecodeMaxTokens);
+// Batches above the decode's four tokens. On layers the fused decode serves,
+// up to kGroupedDecodeMaxTokens run it once per group of four tokens (each
+// launch streams only its group's experts). Up to kSmallMaxTokens run the
+// small-batch path, which streams each active expert's weights once per
+// call; larger batches run the grouped GEMMs on 256-row tiles. Measured on
+// the Qwen3-30B-A3B-shaped INT4 layer (us per call, cold weights):
+//   tokens          5     8    12    16    24    32    64   128   256
+//   grouped decode 54    65    96   125   186
+//   small path     81   101   112   115   144   148   161   176   235
+//   grouped GEMMs 114   158   177   179   241   244   251   258   265
+// QMOE_FORCE_PATH=grouped extends the grouped decode to 24 tokens.
+constexpr int64_t kGroupedDecodeMaxTokens = 12;
+constexpr int64_t kGroupedDecodeForcedMax = 24;
+constexpr int64_t kSmallMaxTokens = 256;
+
+Path choose_path(const Layer& L, int force, bool small_ok, bool fused, int64_t T) {
+  (void)L;
+  if (force == kForcePrefill) return Path::kPrefill;
+  if (force == kForceSmall && small_ok) return Path::kSmall;
+  if (T <= kDecodeMaxTokens) return Path::kDecode;
+  const int64_t grouped_max = force == kForceGrouped ? kGroupedDecodeForcedMax : kGroupedDecodeMaxTokens;
+  if (fused && T <= grouped_max) return Path::kDecode;
+  if (small_ok && T <= kSmallMaxTokens) return Path::kSmall;
+  return Path::kPrefill;
 }
 
-static Workspace layout(const Layer& L, int64_t T, bool decode) {
+static Workspace layout(const Layer& L, int64_t T, Path path) {
   Workspace W;
   memset(&W, 0, sizeof W);
   const int64_t R = T * L.k;
   W.R = R;
-  W.decode = decode;
+  W.decode = path == Path::kDecode;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -70,14 +89,15 @@ static Workspace layout(const Layer& L, int64_t T, bool decode) {
   };
   W.topk_id = take(R * 4);
   W.topk_w = take(R * 4);
-  if (decode) {
+  if (path == Path::kDecode) {
     const GemvShape s2 = gemv_shape(L.I, 64);
     W.fc2_row_blocks = static_cast<int>((L.H + s2.rows_block - 1) / s2.rows_block);
     W.h32 = take(static_cast<size_t>(R * L.I * 4));
     W.y32 = take(static_cast<size_t>(R * L.H * 4));
   } else {
+    W.tile_m = path == Path::kSmall ? kSmallRows : kTileM;
     W.nchunks = (T + kChunkTokens - 1) / kChunkTokens;
-    W.max_tiles = (R + kTileM - 1) / kTileM + L.E;
+    W.max_tiles = (R + W.tile_m - 1) / W.tile_m + L.E;
     W.hist = take(static_cast<size_t>(W.nchunks * L.E * 4));
     W.chunk_base = take(static_cast<size_t>(W.nchunks * L.E * 4));
     W.counts = take(static_cast<size_t>(L.E * 4));
@@ -86,8 +106,15 @@ static Workspace layout(const Layer& L, int64_t T, bool decode) {
     W.inv_pos = take(static_cast<size_t>(R * 4));
     W.tiles = take(static_cast<size_t>(W.max_tiles * 16));
     W.num_tiles = take(4);
-    W.xbf16 = L.act_bf16 ? 0 : take(static_cast<size_t>(T * L.H * 2));
-    W.hbf16 = take(static_cast<size_t>(R * L.I * 2));
+    W.x16 = L.act == kActF16 ? 0 : take(static_cast<size_t>(T * L.H * 2));
+    W.xexp = L.act == kActF16 ? 0 : take(static_cast<size_t>(T));
+    if (path == Path::kSmall) {
+      W.h32 = take(static_cast<size_t>(R * L.I * 4));
+    } else {
+      W.h16 = take(static_cast<size_t>(R * L.I * 2));
+      W.hexp = take(static_cast<size_t>(R * h_exp_stride(L.I)));
+      W.rexp = take(static_cast<size_t>(R));
+    }
     W.yf32 = take(static_cast<size_t>(R * L.H * 4));
   }
   W.total = off;
@@ -120,20 +147,32 @@ class DeviceGuard {
   bool ok_ = false;
 };
 
+// Workspace for a forward call on T tokens: enough for the path it takes,
+// with or without the fused decode (a call under graph capture does without
+// it), and for qmoe_route, which runs the grouped GEMMs' routing.
 size_t required_bytes(const qmoe_handle* h, int64_t T) {
-  if (use_decode_path(h->L, h->force_prefill, h->fused_ok && !h->split_decode, T)) {
-    const size_t d = layout(h->L, T, true).total;
-    const size_t p = layout(h->L, T, false).total;   // qmoe_route needs the routing layout
-    return d > p ? d : p;
+  size_t need = layout(h->L, T, Path::kPrefill).total;
+  for (bool fused : {false, true}) {
+    const Path p = choose_path(h->L, h->force, h->small_ok, fused && h->fused_ok && !h->split_decode, T);
+    const size_t b = layout(h->L, T, p).total;
+    need = b > need ? b : need;
   }
-  return layout(h->L, T, false).total;
+  return need;
 }
+
+// The dispatch behind qmoe_forward; the caller
+// has validated the arguments, checked that `ws` holds required_bytes(h, T)
+// bytes and made the handle's device current.
+qmoe_status forward_impl(qmoe_handle* h, const void* x, const void* logits, void* out, int64_t T,
+                         void* ws, hipStream_t s);
 
 }  // namespace
 
 extern "C" {
 
-const char* qmoe_status_string(qmoe_status st) {
+const char* qmoe_status_string(int st) {
+  // an int, not the enum: callers may pass any value, and a C++ enum object
+  // holding a value outside its enumerators' range is undefined behaviour
   switch (st) {
     case QMOE_OK: return "ok";
     case QMOE_ERR_INVALID_ARG: return "invalid argument";
@@ -205,8 +244,13 @@ qmoe_status qmoe_create(const qmoe_config* c, const qmoe_weights* w, int device,
   L.hook_user = nullptr;
   h->device = device;
   const char* force = getenv("QMOE_FORCE_PATH");
-  h->force_prefill = force && strcmp(force, "prefill") == 0;
+  h->force = !force                           ? kForceNone
+             : strcmp(force, "prefill") == 0  ? kForcePrefill
+             : strcmp(force, "small") == 0    ? kForceSmall
+             : strcmp(force, "grouped") == 0  ? kForceGrouped
+                                              : kForceNone;
   h->split_decode = force && strcmp(force, "decode_split") == 0;
+  h->small_ok = small_path_supported(L);
   h->xbuf = nullptr;
   h->calls = 0;
   h->fused_ok = false;
@@ -214,7 +258,11 @@ qmoe_status qmoe_create(const qmoe_config* c, const qmoe_weights* w, int device,
   h->spin_limit = 0;
   {
     DeviceGuard guard(device);
-    if (!guard.ok()) { delete h; return QMOE_ERR_HIP; }
+    if (!guard.ok() ||
+        (h->small_ok && prepare_small(L) != hipSuccess)) {
+      delete h;
+      return QMOE_ERR_HIP;
+    }
     if (fused_decode_supported(L)) {
       const size_t xb = fused_exchange_bytes(L);
       if (hipMalloc(&h->xbuf, xb) != hipSuccess || hipMemset(h->xbuf, 0, xb) != hipSuccess) {
@@ -257,7 +305,7 @@ qmoe_status qmoe_workspace_size(const qmoe_handle* h, int64_t T, size_t* bytes) 
 qmoe_status qmoe_workspace_routing(const qmoe_handle* h, int64_t T, size_t* id_off, size_t* w_off) {
   if (!h || !id_off || !w_off || T < 0 || T > h->L.max_tokens) return QMOE_ERR_INVALID_ARG;
   const Workspace W =
-      layout(h->L, T, use_decode_path(h->L, h->force_prefill, h->fused_ok && !h->split_decode, T));
+      layout(h->L, T, choose_path(h->L, h->force, h->small_ok, h->fused_ok && !h->split_decode, T));
   *id_off = W.topk_id;
   *w_off = W.topk_w;
   return QMOE_OK;
@@ -272,46 +320,7 @@ qmoe_status qmoe_forward(qmoe_handle* h, const void* x, const void* logits, void
   if (!ws || !aligned16(ws) || ws_bytes < required_bytes(h, T)) return QMOE_ERR_WORKSPACE;
   DeviceGuard guard(h->device);
   if (!guard.ok()) return QMOE_ERR_HIP;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  char* base = static_cast<char*>(ws);
-  hipError_t err;
-  stage_done(h->L, 0, "start");
-  const bool fused = h->fused_ok && !h->split_decode;
-  if (use_decode_path(h->L, h->force_prefill, fused, T)) {
-    const Workspace W = layout(h->L, T, true);
-    if (fused) {
-      // one launch per group of up to four tokens (bf16 rows), each with its
-      // own epoch: 1, 2, ...; when the counter wraps the exchange buffer is
-      // zeroed again first, so no entry can carry a reused epoch. A launch
-      // that did not happen does not use up its epoch.
-      err = hipSuccess;
-      const int64_t H = h->L.H, E = h->L.E, k = h->L.k;
-      for (int64_t t0 = 0; t0 < T && err == hipSuccess; t0 += kDecodeMaxTokens) {
-        const int64_t tg = T - t0 < kDecodeMaxTokens ? T - t0 : kDecodeMaxTokens;
-        uint32_t epoch = h->calls + 1u;
-        if (epoch == 0u) {
-          epoch = 1u;
-          err = clear_exchange(h->L, h->xbuf, s);
-          if (err != hipSuccess) break;
-        }
-        Workspace Wg = W;   // this group's routing slots
-        Wg.topk_id += static_cast<size_t>(t0 * k * 4);
-        Wg.topk_w += static_cast<size_t>(t0 * k * 4);
-        err = launch_decode_fused(h->L, static_cast<const uint16_t*>(x) + t0 * H,
-                                  static_cast<const uint16_t*>(logits) + t0 * E,
-                                  static_cast<uint16_t*>(out) + t0 * H, tg, base, Wg, h->xbuf, epoch,
-                                  h->fused_grid, h->spin_limit, s);
-        if (err == hipSuccess) h->calls = epoch;
-      }
-    } else {
-      err = launch_decode(h->L, x, logits, out, T, base, W, s);
-    }
-  } else {
-    const Workspace W = layout(h->L, T, false);
-    err = launch_route(h->L, logits, T, base, W, s);
-    if (err == hipSuccess) err = launch_prefill(h->L, x, out, T, base, W, s);
-  }
-  return err == hipSuccess ? QMOE_OK : QMOE_ERR_HIP;
+  return forward_impl(h, x, logits, out, T, ws, static_cast<hipStream_t>(stream));
 }
 
 qmoe_status qmoe_route(qmoe_handle* h, const void* logits, int64_t T, int32_t* topk_id, float* topk_w,
@@ -319,7 +328,7 @@ qmoe_status qmoe_route(qmoe_handle* h, const void* logits, int64_t T, int32_t* t
                        size_t ws_bytes, void* stream) {
   if (!h || T < 1 || T > h->L.max_tokens) return QMOE_ERR_INVALID_ARG;
   if (!logits || !aligned16(logits)) return QMOE_ERR_INVALID_ARG;
-  const Workspace W = layout(h->L, T, false);
+  const Workspace W = layout(h->L, T, Path::kPrefill);
   if (!ws || !aligned16(ws) || ws_bytes < W.total) return QMOE_ERR_WORKSPACE;
   DeviceGuard guard(h->device);
   if (!guard.ok()) return QMOE_ERR_HIP;
@@ -338,13 +347,13 @@ qmoe_status qmoe_route(qmoe_handle* h, const void* logits, int64_t T, int32_t* t
   return err == hipSuccess ? QMOE_OK : QMOE_ERR_HIP;
 }
 
-qmoe_status qmoe_dequant(qmoe_handle* h, int fc, int64_t expert, float* out_f32, uint16_t* out_bf16,
+qmoe_status qmoe_dequant(qmoe_handle* h, int fc, int64_t expert, float* out_f32, uint16_t* out_f16,
                          void* stream) {
   if (!h || (fc != 1 && fc != 2) || expert < 0 || expert >= h->L.E) return QMOE_ERR_INVALID_ARG;
-  if (!out_f32 && !out_bf16) return QMOE_OK;
+  if (!out_f32 && !out_f16) return QMOE_OK;
   DeviceGuard guard(h->device);
   if (!guard.ok()) return QMOE_ERR_HIP;
-  hipError_t err = launch_dequant(h->L, fc, expert, out_f32, out_bf16, static_cast<hipStream_t>(stream));
+  hipError_t err = launch_dequant(h->L, fc, expert, out_f32, out_f16, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? QMOE_OK : QMOE_ERR_HIP;
 }
 
@@ -386,3 +395,63 @@ qmoe_status qmoe_destroy(qmoe_handle* h) {
 }
 
 }  // extern "C"
+
+namespace {
+
+qmoe_status forward_impl(qmoe_handle* h, const void* x, const void* logits, void* out, int64_t T,
+                         void* ws, hipStream_t s) {
+  char* base = static_cast<char*>(ws);
+  hipError_t err;
+  bool fused = h->fused_ok && !h->split_decode;
+  if (fused) {
+    // The fused decode tags its exchange entries with an epoch the host
+    // picks per call; a captured graph would replay one epoch forever, so a
+    // call under stream capture takes the paths without cross-workgroup
+    // exchange (split decode up to four tokens, grouped GEMMs above).
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess) return QMOE_ERR_HIP;
+    if (cs != hipStreamCaptureStatusNone) fused = false;
+  }
+  stage_done(h->L, 0, "start");
+  const Path path = choose_path(h->L, h->force, h->small_ok, fused, T);
+  if (path == Path::kDecode) {
+    const Workspace W = layout(h->L, T, Path::kDecode);
+    if (fused) {
+      // one launch per group of up to four tokens (bf16 rows), each with its
+      // own epoch: 1, 2, ...; when the counter wraps the exchange buffer is
+      // zeroed again first, so no entry can carry a reused epoch. A launch
+      // that did not happen does not use up its epoch.
+      err = hipSuccess;
+      const int64_t H = h->L.H, E = h->L.E, k = h->L.k;
+      for (int64_t t0 = 0; t0 < T && err == hipSuccess; t0 += kDecodeMaxTokens) {
+        const int64_t tg = T - t0 < kDecodeMaxTokens ? T - t0 : kDecodeMaxTokens;
+        uint32_t epoch = h->calls + 1u;
+        if (epoch == 0u) {
+          epoch = 1u;
+          err = clear_exchange(h->L, h->xbuf, s);
+          if (err != hipSuccess) break;
+        }
+        Workspace Wg = W;   // this group's routing slots
+        Wg.topk_id += static_cast<size_t>(t0 * k * 4);
+        Wg.topk_w += static_cast<size_t>(t0 * k * 4);
+        err = launch_decode_fused(h->L, static_cast<const uint16_t*>(x) + t0 * H,
+                                  static_cast<const uint16_t*>(logits) + t0 * E,
+                                  static_cast<uint16_t*>(out) + t0 * H, tg, base, Wg, h->xbuf, epoch,
+                                  h->fused_grid, h->spin_limit, s);
+        if (err == hipSuccess) h->calls = epoch;
+      }
+    } else {
+      err = launch_decode(h->L, x, logits, out, T, base, W, s);
+    }
+  } else {
+    const Workspace W = layout(h->L, T, path);
+    err = launch_route(h->L, logits, T, base, W, s);
+    if (err == hipSuccess)
+      err = path == Path::kSmall ? launch_small(h->L, x, out, T, base, W, s)
+                                 : launch_prefill(h->L, x, out, T, base, W, s);
+  }
+  return err == hipSuccess ? QMOE_OK : QMOE_ERR_HIP;
+}
+
+}  // namespace
+

@@ -4,8 +4,8 @@
 //                    zero point or the row's per-block code): the code comes
 //                    back out of the bf16 pair 1 + q/128 that unit_pair builds
 //                    (exact), placed at the code index pair_a/pair_b name;
-//   out_bf16[n][k] = the bf16 operand the prefill GEMM stages in LDS
-//                    (dequant_unit_bf16).
+//   out_f16[n][k]  = the fp16 operand fp16((q - zp) * s) the prefill GEMM
+//                    stages in LDS, from the same routine (dequant_unit_f16).
 //
 // Dequantization W = (q - zp) * s[n][k / block] ("[CUDA] Add INT4 and INT3
 // QMoE CPU/GPU offload support", Description: raw integer experts, block
@@ -22,13 +22,14 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
                                                       const uint8_t* __restrict__ zps, int64_t N,
                                                       int64_t K, int bs, int zp, int64_t row_bytes,
                                                       int64_t nblk, float* __restrict__ out_f32,
-                                                      uint16_t* __restrict__ out_bf16) {
+                                                      uint16_t* __restrict__ out_f16) {
   const int64_t units = K / 32;
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (gid >= N * units) return;
   const int64_t n = gid / units, u = gid % units;
   const UnitWords<BITS> w = load_unit<BITS>(codes + n * row_bytes + u * (4 * BITS));
-  const float s = half_to_f32(scales[n * nblk + (32 * u) / bs]);
+  const uint16_t sbits = scales[n * nblk + (32 * u) / bs];
+  const float s = half_to_f32(sbits);
   if (zps) zp = zps[n * nblk + (32 * u) / bs];   // per-block zero point
   const int64_t base = n * K + 32 * u;
   if (out_f32) {
@@ -41,19 +42,19 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
       out_f32[base + pair_b(BITS, p)] = (qb - static_cast<float>(zp)) * s;
     }
   }
-  if (out_bf16) {
+  if (out_f16) {
     uint32_t pairs[16];
-    dequant_unit_bf16<BITS>(w, s, zp, pairs);
+    dequant_unit_f16<BITS>(w, sbits, zp, pairs);
 #pragma unroll
     for (int p = 0; p < 16; ++p) {
-      out_bf16[base + 2 * p] = static_cast<uint16_t>(pairs[p] & 0xFFFFu);
-      out_bf16[base + 2 * p + 1] = static_cast<uint16_t>(pairs[p] >> 16);
+      out_f16[base + 2 * p] = static_cast<uint16_t>(pairs[p] & 0xFFFFu);
+      out_f16[base + 2 * p + 1] = static_cast<uint16_t>(pairs[p] >> 16);
     }
   }
 }
 
 hipError_t launch_dequant(const Layer& L, int fc, int64_t expert, float* out_f32,
-                          uint16_t* out_bf16, hipStream_t s) {
+                          uint16_t* out_f16, hipStream_t s) {
   const int64_t N = fc == 1 ? 2 * L.I : L.H;
   const int64_t K = fc == 1 ? L.H : L.I;
   const int64_t rb = fc == 1 ? L.fc1_row_bytes : L.fc2_row_bytes;
@@ -65,9 +66,9 @@ hipError_t launch_dequant(const Layer& L, int fc, int64_t expert, float* out_f32
   const int64_t threads = N * (K / 32);
   const unsigned grid = static_cast<unsigned>((threads + 255) / 256);
   switch (L.bits) {
-    case 4: dequant_kernel<4><<<grid, 256, 0, s>>>(c, sc, z, N, K, L.bs, L.zp, rb, nb, out_f32, out_bf16); break;
-    case 3: dequant_kernel<3><<<grid, 256, 0, s>>>(c, sc, z, N, K, L.bs, L.zp, rb, nb, out_f32, out_bf16); break;
-    default: dequant_kernel<2><<<grid, 256, 0, s>>>(c, sc, z, N, K, L.bs, L.zp, rb, nb, out_f32, out_bf16); break;
+    case 4: dequant_kernel<4><<<grid, 256, 0, s>>>(c, sc, z, N, K, L.bs, L.zp, rb, nb, out_f32, out_f16); break;
+    case 3: dequant_kernel<3><<<grid, 256, 0, s>>>(c, sc, z, N, K, L.bs, L.zp, rb, nb, out_f32, out_f16); break;
+    default: dequant_kernel<2><<<grid, 256, 0, s>>>(c, sc, z, N, K, L.bs, L.zp, rb, nb, out_f32, out_f16); break;
   }
   return hipGetLastError();
 }

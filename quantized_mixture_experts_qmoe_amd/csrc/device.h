@@ -122,98 +122,86 @@ __device__ __forceinline__ uint32_t unit_pair(const UnitWords<BITS>& u, int p) {
   }
 }
 
-// The matrix-core operand value of code i: (q - zp) * s computed exactly in
-// fp32 and rounded once to bf16 (round to nearest even). Writes the unit's 32
-// values as 16 bf16 pairs in natural order (pair p = codes 2p, 2p+1).
+// ---------------------------------------------------------------- fp16 operands
 //
-// For a finite scale, q * s - zp * s is computed by one FMA: both products
-// and the result (at most 9 + 11 significant bits) are exact in fp32, so the
-// FMA's single rounding is exact. INT4 and INT2 codes are first spread into
-// bytes with masks so v_cvt_f32_ubyteN converts them without per-code
-// extraction. A non-finite scale takes the plain (q - zp) * s route so the
-// result stays bit-identical in every case.
-__device__ __forceinline__ float ubyte_f32(uint32_t w, int b) {
-  return static_cast<float>((w >> (8 * b)) & 0xFFu);   // selects v_cvt_f32_ubyteN
+// The grouped (prefill) GEMMs feed the matrix cores fp16 operands. A weight
+// enters as fp16((q - zp) * s): round to nearest even of the exact product,
+// with gradual underflow. dequant_unit_f16 forms it for the 32 codes of a
+// unit, as 16 packed pairs in natural order (pair p = codes 2p, 2p+1):
+//   1. each pair of codes becomes the fp16 pair (1024 + q_a, 1024 + q_b): the
+//      code is OR-ed into the mantissa of 1024.0 (0x6400), exact for q < 1024;
+//   2. adding -(1024 + zp) gives q - zp exactly (small integers);
+//   3. one packed fp16 multiply by (s, s) rounds the exact product once.
+// Step 3 is an IEEE product, so the result is fp16((q - zp) * s) for every
+// scale pattern, infinities and NaN included (q = zp and s = inf gives NaN,
+// as (q - zp) * s does).
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t f16_pair_scale(uint32_t biased_pair, f16x2_t off, f16x2_t sv) {
+  const f16x2_t v = __builtin_bit_cast(f16x2_t, biased_pair);
+  return __builtin_bit_cast(uint32_t, (v + off) * sv);
 }
 
-// v_and_b32 the compiler cannot fold into the byte conversions that follow
-// (otherwise it turns mask + byte select into a bit-field extract per code).
-__device__ __forceinline__ uint32_t and_opaque(uint32_t w, uint32_t m) {
-  uint32_t r;
-  asm("v_and_b32 %0, %1, %2" : "=v"(r) : "v"(m), "v"(w));
-  return r;
+// Range exponents. A row or chunk of values with largest magnitude m is
+// stored as fp16(v * 2^-e): e = 0 while m lies in [lo, 2^15] (or m is 0 or
+// not finite), else the e that puts m in [2^14, 2^15), clamped to
+// [-120, 120]. Activations use lo = 2^-3 (so every value at least 2^-14 of
+// the row's largest stays a normal fp16 number), h chunks lo = 2^-14 (the
+// smallest normal fp16 number; a chunk's values below it carry less than
+// 2^-14 of the row's weight), which keeps ordinary chunks unscaled.
+template <int LO_EXP>
+__device__ __forceinline__ int range_exponent_lo(float m) {
+  const bool out = (m > 32768.0f || (m > 0.0f && m < __builtin_ldexpf(1.0f, LO_EXP))) && m <= 3.4028235e38f;
+  int ex = 0;
+  (void)frexpf(m, &ex);
+  return out ? min(max(ex - 15, -120), 120) : 0;
 }
+__device__ __forceinline__ int range_exponent(float m) { return range_exponent_lo<-3>(m); }
+__device__ __forceinline__ int h_chunk_exponent(float m) { return range_exponent_lo<-14>(m); }
 
-// Codes 16h .. 16h+15 of a unit as floats, natural order.
 template <int BITS>
-__device__ __forceinline__ void unit_half_codes(const UnitWords<BITS>& u, int h, float (&q)[16]) {
+__device__ __forceinline__ void dequant_unit_f16(const UnitWords<BITS>& u, uint32_t scale_bits, int zp,
+                                                 uint32_t (&out)[16]) {
+  const _Float16 s = __builtin_bit_cast(_Float16, static_cast<uint16_t>(scale_bits));
+  const f16x2_t sv = {s, s};
+  const _Float16 o = static_cast<_Float16>(-(1024 + zp));
+  const f16x2_t off = {o, o};
+  constexpr uint32_t kBias = 0x64006400u;   // fp16 1024.0 in both halves
   if constexpr (BITS == 4) {
-    // dwords 2h, 2h+1 hold codes 16h..16h+15 (nibbles); even codes -> bytes of lo, odd -> hi
+    // dword d holds codes 8d..8d+7 as nibbles; byte b of lo / hi holds
+    // codes 8d + 2b / 8d + 2b + 1
 #pragma unroll
-    for (int d = 0; d < 2; ++d) {
-      const uint32_t w = h ? u.w[2 + d] : u.w[d];
-      const uint32_t lo = and_opaque(w, 0x0F0F0F0Fu), hi = and_opaque(w >> 4, 0x0F0F0F0Fu);
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t w = u.w[d];
+      const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        q[8 * d + 2 * b] = ubyte_f32(lo, b);
-        q[8 * d + 2 * b + 1] = ubyte_f32(hi, b);
+        const uint32_t pr = ((lo >> (8 * b)) & 0xFFu) | (((hi >> (8 * b)) & 0xFFu) << 16);
+        out[4 * d + b] = f16_pair_scale(pr | kBias, off, sv);
       }
     }
   } else if constexpr (BITS == 2) {
-    // dword h holds codes 16h..16h+15; c_j's byte b holds code 16h + 4b + j
-    const uint32_t w = h ? u.w[1] : u.w[0];
-    uint32_t c[4];
+    // dword d holds codes 16d..16d+15, two bits each; pair p = nibble p
 #pragma unroll
-    for (int j = 0; j < 4; ++j) c[j] = and_opaque(w >> (2 * j), 0x03030303u);
+    for (int d = 0; d < 2; ++d) {
+      const uint32_t w = u.w[d];
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) q[4 * b + j] = ubyte_f32(c[j], b);
-  } else {
-    // bits [48h, 48h + 48) of the 96-bit unit as two 32-bit words (a: the
-    // low 32 bits, b: the next 16), kept in registers: code i sits at bit 3i
-    // of b:a, and code 10 straddles the two words
-    const uint32_t a = h ? __builtin_amdgcn_alignbit(u.w[2], u.w[1], 16) : u.w[0];
-    const uint32_t b = h ? (u.w[2] >> 16) : u.w[1];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t c = (3 * i + 3 <= 32) ? (a >> (3 * i)) & 7u
-                         : (3 * i >= 32)   ? (b >> (3 * i - 32)) & 7u
-                                           : __builtin_amdgcn_alignbit(b, a, 3 * i) & 7u;
-      q[i] = static_cast<float>(c);
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t nib = (w >> (4 * j)) & 0xFu;
+        const uint32_t pr = (nib & 3u) | ((nib >> 2) << 16);
+        out[8 * d + j] = f16_pair_scale(pr | kBias, off, sv);
+      }
     }
-  }
-}
-
-// (q - zp) * s for codes as floats, rounded once to bf16 pairs. q - zp is an
-// exact small integer and its product with an fp16 scale has at most
-// 9 + 11 significant bits, so the fp32 product is exact for every scale
-// (infinities and NaN included) and the one rounding is the bf16 one.
-// Branch-free, so callers can interleave it with matrix work.
-template <int N>
-__device__ __forceinline__ void dequant_codes_bf16(const float (&q)[2 * N], float s, int zp,
-                                                   uint32_t (&out)[N]) {
-  const float zf = static_cast<float>(zp);
+  } else {
+    // pair p = the six bits [6p, 6p + 6) of the 96-bit unit
 #pragma unroll
-  for (int p = 0; p < N; ++p)
-    out[p] = f32x2_to_bf16x2((q[2 * p] - zf) * s, (q[2 * p + 1] - zf) * s);
-}
-
-// The matrix-core operand values of a whole unit: 16 bf16 pairs in natural
-// order (pair p = codes 2p, 2p+1).
-template <int BITS>
-__device__ __forceinline__ void dequant_unit_bf16(const UnitWords<BITS>& u, float s, int zp,
-                                                  uint32_t (&out)[16]) {
-  float q0[16], q1[16];
-  unit_half_codes<BITS>(u, 0, q0);
-  unit_half_codes<BITS>(u, 1, q1);
-  uint32_t o0[8], o1[8];
-  dequant_codes_bf16<8>(q0, s, zp, o0);
-  dequant_codes_bf16<8>(q1, s, zp, o1);
-#pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    out[p] = o0[p];
-    out[8 + p] = o1[p];
+    for (int p = 0; p < 16; ++p) {
+      const int bit = 6 * p, d = bit >> 5, o6 = bit & 31;
+      const uint32_t f = (o6 <= 26) ? (u.w[d] >> o6) & 63u
+                                    : __builtin_amdgcn_alignbit(u.w[d + 1], u.w[d], o6) & 63u;
+      const uint32_t pr = (f & 7u) | ((f >> 3) << 16);
+      out[p] = f16_pair_scale(pr | kBias, off, sv);
+    }
   }
 }
 

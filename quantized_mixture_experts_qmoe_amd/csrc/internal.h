@@ -40,8 +40,16 @@ inline void stage_done(const Layer& L, int stage, const char* name) {
 
 // Prefill GEMM tiling (rows = routes of one expert, cols = output features).
 constexpr int kTileM = 256;
+// Small-batch path: routes of one expert per tile (one MFMA row block).
+constexpr int kSmallRows = 16;
 constexpr int kTileN = 128;
 constexpr int kChunkTokens = 32;           // tokens per histogram/scatter chunk
+
+// Bytes per route of the prefill's h exponents (one per 32 columns of h),
+// padded to whole 16-byte rows.
+__host__ __device__ constexpr int h_exp_stride(int64_t I) {
+  return static_cast<int>((I / 32 + 15) / 16 * 16);
+}
 
 // Decode GEMV row blocking.
 struct GemvShape {
@@ -61,20 +69,35 @@ struct Workspace {
   size_t counts, offsets;             // int32 [E], [E + 1]
   size_t sorted_routes, inv_pos;      // int32 [R]
   size_t tiles, num_tiles;            // int4 [max_tiles], int32 [1]
-  size_t xbf16;                       // prefill with fp32 activations: bf16 [T, H]
-  size_t hbf16, yf32;                 // prefill: bf16 [R, I], fp32 [R, H]
+  size_t x16, xexp;                   // prefill, bf16/fp32 activations: fp16 [T, H], int8 [T]
+  size_t h16, hexp, rexp, yf32;       // prefill: fp16 [R, I], int8 [R, h_exp_stride(I)], int8 [R],
+                                      // fp32 [R, H]
   size_t total;
   int64_t R, nchunks, max_tiles;
+  int tile_m;                         // routes per tile of the grouped paths
   int fc2_row_blocks;                 // decode: FC2 workgroups per route
   bool decode;
 };
-bool use_decode_path(const Layer& L, bool force_prefill, int64_t T);
+
+// The path a forward call takes.
+enum class Path { kDecode, kSmall, kPrefill };
 
 // ---- launchers (each returns hipSuccess or the launch error)
 hipError_t launch_route(const Layer& L, const void* logits, int64_t T, char* ws, const Workspace& W,
                         hipStream_t s);
 hipError_t launch_prefill(const Layer& L, const void* x, void* out, int64_t T, char* ws,
                           const Workspace& W, hipStream_t s);
+// Staging of FC1's activations (fp16 with a per-token exponent; fp16 inputs
+// pass through) and the routing-weighted combine, shared by the grouped paths.
+hipError_t launch_stage_x(const Layer& L, const void* x, int64_t T, char* ws, const Workspace& W,
+                          hipStream_t s, const uint16_t** xa, const int8_t** xexp);
+hipError_t launch_combine(const Layer& L, void* out, int64_t T, char* ws, const Workspace& W,
+                          hipStream_t s);
+// Small-batch path: grouped GEMMs streaming each expert's weights once.
+bool small_path_supported(const Layer& L);
+hipError_t prepare_small(const Layer& L);
+hipError_t launch_small(const Layer& L, const void* x, void* out, int64_t T, char* ws,
+                        const Workspace& W, hipStream_t s);
 hipError_t launch_decode(const Layer& L, const void* x, const void* logits, void* out, int64_t T,
                          char* ws, const Workspace& W, hipStream_t s);
 // Fused single-launch decode (bf16 or fp16 activations, H <= 2048,
@@ -94,6 +117,6 @@ hipError_t launch_decode_fused(const Layer& L, const void* x, const void* logits
                                int64_t T, char* ws, const Workspace& W, void* xbuf,
                                uint32_t epoch, int grid, uint32_t spin_limit, hipStream_t s);
 hipError_t launch_dequant(const Layer& L, int fc, int64_t expert, float* out_f32,
-                          uint16_t* out_bf16, hipStream_t s);
+                          uint16_t* out_f16, hipStream_t s);
 
 }  // namespace qmoe

@@ -1,15 +1,16 @@
-// Prefill path (5+ tokens): expert-grouped GEMMs on the CDNA4 matrix cores.
+// Prefill path (5+ tokens): expert-grouped GEMMs on the CDNA4 matrix cores
+// with fp16 operands.
 //
 // The routing stage leaves the routes sorted by expert and a tile list
 // (expert, first sorted row, rows <= 256). Each workgroup (8 waves, 4 x 2 of
 // 64 x 128) computes one 256 x 256 tile of one expert:
-//   FC1: A = x rows gathered through sorted_routes (bf16), B = the expert's
-//        gate rows [n0, n0+128) and up rows [I+n0, I+n0+128), dequantized to
-//        bf16 (round to nearest even of (q - zp) * s, exact in fp32) into
-//        LDS; each wave holds 64 gate and the 64 matching up columns, so the
-//        epilogue applies h = silu(gate) * up and stores h as bf16 [R, I] in
-//        sorted order.
-//   FC2: A = h rows of the tile (bf16), B = the expert's FC2 rows
+//   FC1: A = x rows gathered through sorted_routes (fp16, each token scaled
+//        by its power of two), B = the expert's gate rows [n0, n0+128) and up
+//        rows [I+n0, I+n0+128), dequantized to fp16((q - zp) * s) into LDS;
+//        each wave holds 64 gate and the 64 matching up columns, so the
+//        epilogue applies h = silu(gate) * up and stores h as fp16 [R, I] in
+//        sorted order (with per-chunk exponents, see below).
+//   FC2: A = h rows of the tile (fp16), B = the expert's FC2 rows
 //        [n0, n0+256) dequantized into LDS; the epilogue stores fp32 y
 //        [R, H] in sorted order (non-temporal: the combine reads it once).
 // Both epilogues stage each wave's results in LDS, 16 rows at a time, and
@@ -44,7 +45,7 @@
 
 namespace qmoe {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
 namespace {
@@ -75,6 +76,12 @@ __device__ __forceinline__ int logical_tile(int active) {
   return L < active ? L : -1;
 }
 
+// v of lane (l + N) mod 16 within this lane's row of 16 (DPP row_ror).
+template <int N>
+__device__ __forceinline__ float row_rotate(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + N, 0xF, 0xF, false));
+}
+
 // Calls f(std::integral_constant<int, J>) for J = 0..N-1, so that each step's
 // counts are compile-time constants (the scheduling hints below need them).
 template <typename F, int... J>
@@ -96,6 +103,16 @@ int gemm_n_tiles(const Layer& L, bool fc1) {
 // grid = 8 * ceil(max_tiles * n_tiles_n / 8), block = 512
 // (one workgroup per CU: its LDS use limits each SIMD to two waves, so the
 // compiler may use the whole register file to keep fragments in flight)
+//
+// Operand ranges: FC1's A rows are a token's activations scaled by 2^-e_t
+// (a per-token exponent from the staging pass, or none for fp16 inputs),
+// undone on the accumulators in the epilogue. FC1 stores h as fp16 in chunks
+// of 32 columns with an exponent per (route, chunk), nonzero only for chunks
+// whose largest magnitude lies outside [2^-14, 2^15]; a pass between the two
+// GEMMs brings each route's chunks to the route's largest exponent E, and
+// FC2 scales its accumulators by 2^E. A row's exponent sits in the unused
+// padding of its row in the first B buffer from the prologue to the
+// epilogue.
 template <int BITS, bool FC1, bool HAS_ZP>
 __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void grouped_gemm_kernel(
@@ -105,7 +122,7 @@ void grouped_gemm_kernel(
     const void* __restrict__ bias, int act,
     int64_t row_bytes, int64_t nblk, const int4* __restrict__ tiles,
     const int32_t* __restrict__ num_tiles, int n_tiles_n, uint16_t* __restrict__ h_out,
-    float* __restrict__ y_out) {
+    float* __restrict__ y_out, const int8_t* __restrict__ a_exp, int8_t* __restrict__ h_exp) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][kBM * kLdsStride];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kBN * kLdsStride];
 
@@ -171,6 +188,27 @@ void grouped_gemm_kernel(
   // stores them: no stored output row reads them (row m of a product depends
   // on row m of A only)
   const bool a_live = 128 * grp + 32 * gw < nrows;
+  // this thread's rows' exponents (FC1: the token's activation exponent;
+  // FC2: the route's h exponent), issued now and stored to LDS after the
+  // first stage's loads are on their way
+  int row_e[4] = {0, 0, 0, 0};
+  if (a_exp != nullptr && a_live) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = a_row0 + 8 * q;
+      const int rr = r < nrows ? r : 0;
+      row_e[q] = FC1 ? a_exp[sorted_routes[row0 + rr] / k] : a_exp[row0 + rr];
+    }
+  }
+  auto store_row_exponents = [&]() {
+    if ((lane & 7) == 0 && a_live) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        Bs[0][(a_row0 + 8 * q) * kLdsStride + kKT] = static_cast<uint16_t>(static_cast<int16_t>(row_e[q]));
+    }
+  };
+  const int hstride = h_exp_stride(I);
+
   uint4 ra0, ra1, ra2, ra3;
   UnitWords<BITS> rb;
   uint16_t rs;      // raw fp16 scale of this stage's B unit
@@ -178,7 +216,9 @@ void grouped_gemm_kernel(
   int rz = zp;   // this stage's zero point (the scalar one without a tensor)
   auto load_stage = [&](int st) {
     const int k0 = st * kKT;
-    const int ka = (k0 + a_chunk < K) ? k0 : 0;
+    // (a chunk past K reads its row's first columns instead: always inside
+    // the row; the zero scales of the B units past K cancel it)
+    const int ka = (k0 + a_chunk < K) ? k0 : -a_chunk;
     if (a_live) {
       ra0 = *reinterpret_cast<const uint4*>(a_ptr[0] + ka);
       ra1 = *reinterpret_cast<const uint4*>(a_ptr[1] + ka);
@@ -202,21 +242,9 @@ void grouped_gemm_kernel(
       *reinterpret_cast<uint4*>(ad + 16 * kLdsStride) = ra2;
       *reinterpret_cast<uint4*>(ad + 24 * kLdsStride) = ra3;
     }
+    // the fp16 operand fp16((q - zp) * s) (a unit past K gets a zero scale)
     uint32_t pairs[16];
-    {
-      const float sc = rpast ? 0.0f : half_to_f32(rs);
-      float q[16];
-      // (q - zp) * s as one fma: q * s and zp * s are exact in fp32 (at most
-      // 8 + 11 significant bits), so the fused result is the exact product,
-      // bit for bit what subtracting first and then multiplying gives
-      const float nzs = -static_cast<float>(rz) * sc;
-      unit_half_codes<BITS>(rb, 0, q);
-#pragma unroll
-      for (int p = 0; p < 8; ++p) pairs[p] = f32x2_to_bf16x2(fmaf(q[2 * p], sc, nzs), fmaf(q[2 * p + 1], sc, nzs));
-      unit_half_codes<BITS>(rb, 1, q);
-#pragma unroll
-      for (int p = 0; p < 8; ++p) pairs[8 + p] = f32x2_to_bf16x2(fmaf(q[2 * p], sc, nzs), fmaf(q[2 * p + 1], sc, nzs));
-    }
+    dequant_unit_f16<BITS>(rb, rpast ? 0u : static_cast<uint32_t>(rs), rz, pairs);
     uint4* bd = reinterpret_cast<uint4*>(&Bs[buf][b_row * kLdsStride + 32 * b_kq]);
 #pragma unroll
     for (int q = 0; q < 4; ++q) bd[q] = make_uint4(pairs[4 * q], pairs[4 * q + 1], pairs[4 * q + 2], pairs[4 * q + 3]);
@@ -243,10 +271,10 @@ void grouped_gemm_kernel(
   }
   auto frag_a = [&](int buf, int ks, int tm) {
     const int r = wm * 64 + tm * 16 + l16;
-    return *reinterpret_cast<const bf16x8_t*>(&As[buf][r * kLdsStride + ks * 32 + quad * 8]);
+    return *reinterpret_cast<const f16x8_t*>(&As[buf][r * kLdsStride + ks * 32 + quad * 8]);
   };
   auto frag_b = [&](int buf, int ks, int tn) {
-    return *reinterpret_cast<const bf16x8_t*>(&Bs[buf][b_frag_row[tn] * kLdsStride + ks * 32 + quad * 8]);
+    return *reinterpret_cast<const f16x8_t*>(&Bs[buf][b_frag_row[tn] * kLdsStride + ks * 32 + quad * 8]);
   };
   // A stage is 2 K halves x NT B fragments (NT = 8, or 4 in half mode); each
   // step runs 4 MFMAs that share one B fragment. Fragment reads run ahead of
@@ -255,7 +283,7 @@ void grouped_gemm_kernel(
   // the LDS latency hides behind the matrix work instead of stalling it.
   auto mfma_steps = [&](int buf, auto ntc) {
     constexpr int NT = decltype(ntc)::value, NS = 2 * NT;
-    bf16x8_t af[2][4], bfr[3];
+    f16x8_t af[2][4], bfr[3];
 #pragma unroll
     for (int t = 0; t < 4; ++t) af[0][t] = frag_a(buf, 0, t);
     bfr[0] = frag_b(buf, 0, 0);
@@ -270,7 +298,7 @@ void grouped_gemm_kernel(
       if constexpr (rd_a) af[1][tn - (NT - 4)] = frag_a(buf, 1, tn - (NT - 4));
 #pragma unroll
       for (int tm = 0; tm < 4; ++tm)
-        acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks][tm], bfr[j % 3], acc[tm][tn], 0, 0, 0);
+        acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[ks][tm], bfr[j % 3], acc[tm][tn], 0, 0, 0);
       // keep the issue order: this step's reads, then its four MFMAs
       if constexpr (nreads > 0) __builtin_amdgcn_sched_group_barrier(0x100, nreads, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
@@ -282,6 +310,7 @@ void grouped_gemm_kernel(
   load_stage(0);
   store_stage(0);
   load_stage(clampst(1));
+  store_row_exponents();
   __syncthreads();
   // The K loop, instantiated once per fragment count (the mode is uniform
   // over the tile, so each instance keeps its own register allocation); one
@@ -345,14 +374,72 @@ void grouped_gemm_kernel(
 #pragma unroll
     for (int tm = 0; tm < 4; ++tm) {
       const int prow = wm * 64 + tm * 16;   // first tile row of this block
+      // this lane's rows' exponents (prologue, padding of the first B buffer)
+      int re[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        re[i] = static_cast<int16_t>(Bs[0][(prow + quad * 4 + i) * kLdsStride + kKT]);
+      const bool scaled = __ballot((re[0] | re[1] | re[2] | re[3]) != 0) != 0;
       if (FC1) {
+        // h of this lane's 4 rows x NH columns, then per (row, 32-column
+        // chunk of fragments 2c, 2c+1) the exponent that keeps the chunk in
+        // fp16 range (0 unless its largest magnitude lies outside
+        // [2^-10, 2^15]); the 16 lanes of a DPP row hold one row's columns
+        float hv[4][NH];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int tn = 0; tn < NH; ++tn) {
-            const float hv = silu_mul_fast(acc[tm][tn][i] + bcol[tn], acc[tm][tn + NH][i] + bcol[tn + NH]);
-            stg_h[(quad * 4 + i) * 72 + tn * 16 + l16] = static_cast<uint16_t>(f32_to_bf16(hv));
+          for (int tn = 0; tn < NH; ++tn)
+            hv[i][tn] = scaled ? silu_mul_fast(ldexpf(acc[tm][tn][i], re[i]) + bcol[tn],
+                                               ldexpf(acc[tm][tn + NH][i], re[i]) + bcol[tn + NH])
+                               : silu_mul_fast(acc[tm][tn][i] + bcol[tn], acc[tm][tn + NH][i] + bcol[tn + NH]);
+        constexpr int NC = NH / 2;
+        int ce[4][NC];
+        // a chunk needs an exponent only if its maximum leaves [2^-14, 2^15]:
+        // a lane whose own values of the chunk are all inside that range (or
+        // hold one at least 2^-14 and none above 2^15) settles it for its
+        // row, so the chunk maxima are formed only in the rare waves where
+        // some lane cannot tell
+        float lm[4][NC];
+        bool unsure = false;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int c = 0; c < NC; ++c) {
+            lm[i][c] = fmaxf(fabsf(hv[i][2 * c]), fabsf(hv[i][2 * c + 1]));
+            unsure = unsure || !(lm[i][c] >= 0x1p-14f && lm[i][c] <= 32768.0f);
+            ce[i][c] = 0;
           }
+        if (__ballot(unsure) != 0) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+              float m = lm[i][c];
+              m = fmaxf(m, row_rotate<8>(m));
+              m = fmaxf(m, row_rotate<4>(m));
+              m = fmaxf(m, row_rotate<2>(m));
+              m = fmaxf(m, row_rotate<1>(m));
+              ce[i][c] = h_chunk_exponent(m);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int tn = 0; tn < NH; ++tn)
+            stg_h[(quad * 4 + i) * 72 + tn * 16 + l16] =
+                __builtin_bit_cast(uint16_t, static_cast<_Float16>(ldexpf(hv[i][tn], -ce[i][tn / 2])));
+        if (l16 == 0) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int p = prow + quad * 4 + i;
+            if (p < nrows)
+#pragma unroll
+              for (int c = 0; c < NC; ++c)
+                if (cb + 32 * c < I)
+                  h_exp[static_cast<int64_t>(row0 + p) * hstride + (cb >> 5) + c] = static_cast<int8_t>(ce[i][c]);
+          }
+        }
         // 16 rows x NH*16 columns: NT 16-byte chunks per row
 #pragma unroll
         for (int j = 0; j < NT / 4; ++j) {
@@ -365,7 +452,9 @@ void grouped_gemm_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int tn = 0; tn < NT; ++tn) stg_y[(quad * 4 + i) * 132 + tn * 16 + l16] = acc[tm][tn][i] + bcol[tn];
+          for (int tn = 0; tn < NT; ++tn)
+            stg_y[(quad * 4 + i) * 132 + tn * 16 + l16] =
+                (scaled ? ldexpf(acc[tm][tn][i], re[i]) : acc[tm][tn][i]) + bcol[tn];
         // 16 rows x NT*16 columns: NT*4 float4 per row
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
@@ -424,24 +513,120 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
 }
 
-// fp32 and fp16 activations are staged for the matrix cores as bf16 (round
-// to nearest even) once per call.
-__global__ __launch_bounds__(256) void act_to_bf16_kernel(const void* __restrict__ in, int act,
-                                                          int64_t n, uint16_t* __restrict__ out) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i < n) out[i] = static_cast<uint16_t>(f32_to_bf16(load_act(in, act, i)));
+// FC1's activations: each token's row scaled by 2^-e_t and rounded once to
+// fp16, e_t = range_exponent of the row's largest magnitude (0 for a row
+// with a non-finite value); e_t goes to xexp.
+// bf16 rows come through exactly (8 significant bits), fp32 rows are
+// rounded to 11. One wave per token, 8 consecutive values per lane.
+template <int ACT>
+__global__ __launch_bounds__(256) void stage_x_f16_kernel(const void* __restrict__ x, int64_t T, int H,
+                                                          uint16_t* __restrict__ x16,
+                                                          int8_t* __restrict__ xexp) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int lane = threadIdx.x & (kWave - 1);
+  auto load8 = [&](int i, float (&v)[8]) {
+    if constexpr (ACT == kActBF16) {
+      const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + t * H + i);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[2 * j] = bf16_to_f32(w[j] & 0xFFFFu);
+        v[2 * j + 1] = bf16_to_f32(w[j] >> 16);
+      }
+    } else {
+      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(x) + t * H + i);
+      const float4 a = p[0], b = p[1];
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+  };
+  float m = 0.0f;
+  bool finite = true;
+  for (int i = lane * 8; i < H; i += kWave * 8) {
+    float v[8];
+    load8(i, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      finite = finite && (fabsf(v[j]) <= 3.4028235e38f);
+      m = fmaxf(m, fabsf(v[j]));
+    }
+  }
+#pragma unroll
+  for (int off = kWave / 2; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+  finite = __all(finite);
+  const int e = finite ? range_exponent(m) : 0;
+  for (int i = lane * 8; i < H; i += kWave * 8) {
+    float v[8];
+    load8(i, v);
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      o[j] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(ldexpf(v[2 * j], -e)))) |
+             (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(ldexpf(v[2 * j + 1], -e))))
+              << 16);
+    *reinterpret_cast<uint4*>(x16 + t * H + i) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+  if (lane == 0) xexp[t] = static_cast<int8_t>(e);
+}
+
+// Between the GEMMs: each route's h chunks brought to the route's largest
+// chunk exponent E (a chunk stored at e < E is multiplied by 2^(e - E), one
+// more fp16 rounding), and E written to rexp[route] for FC2. Chunks are
+// rewritten only in the rare routes whose exponents differ. One wave per
+// route; lane c reads chunk c's exponent.
+__global__ __launch_bounds__(256) void h_common_exponent_kernel(uint16_t* __restrict__ h16,
+                                                               const int8_t* __restrict__ hexp,
+                                                               int8_t* __restrict__ rexp, int64_t R,
+                                                               int I) {
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (r >= R) return;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int nchk = I / 32, hs = h_exp_stride(I);
+  const int8_t* er = hexp + r * hs;
+  int emax = -128, emin = 127;
+  for (int c = lane; c < nchk; c += kWave) {
+    const int e = er[c];
+    emax = max(emax, e);
+    emin = min(emin, e);
+  }
+#pragma unroll
+  for (int off = kWave / 2; off >= 1; off >>= 1) {
+    emax = max(emax, __shfl_xor(emax, off, kWave));
+    emin = min(emin, __shfl_xor(emin, off, kWave));
+  }
+  if (lane == 0) rexp[r] = static_cast<int8_t>(emax);
+  if (emin == emax) return;
+  // rare: rescale the chunks below E (8 fp16 values per lane and step)
+  for (int i = lane * 8; i < I; i += kWave * 8) {
+    const int d = er[i >> 5] - emax;
+    if (d == 0) continue;
+    const uint16_t fb = d >= -14 ? static_cast<uint16_t>((d + 15) << 10)
+                        : d >= -24 ? static_cast<uint16_t>(1u << (d + 24)) : uint16_t{0};
+    const _Float16 f = __builtin_bit_cast(_Float16, fb);
+    const f16x2_t fv = {f, f};
+    uint4* p = reinterpret_cast<uint4*>(h16 + r * I + i);
+    uint4 v = *p;
+    v.x = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, v.x) * fv);
+    v.y = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, v.y) * fv);
+    v.z = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, v.z) * fv);
+    v.w = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, v.w) * fv);
+    *p = v;
+  }
 }
 
 namespace {
 
 template <int BITS>
-hipError_t launch_gemms(const Layer& L, const uint16_t* xb, char* ws, const Workspace& W,
-                        hipStream_t s) {
+hipError_t launch_gemms(const Layer& L, const uint16_t* xa, const int8_t* xexp, char* ws,
+                        const Workspace& W, hipStream_t s) {
   const int H = static_cast<int>(L.H), I = static_cast<int>(L.I);
   const int32_t* sorted = reinterpret_cast<const int32_t*>(ws + W.sorted_routes);
   const int4* tiles = reinterpret_cast<const int4*>(ws + W.tiles);
   const int32_t* ntiles = reinterpret_cast<const int32_t*>(ws + W.num_tiles);
-  uint16_t* hb = reinterpret_cast<uint16_t*>(ws + W.hbf16);
+  uint16_t* hb = reinterpret_cast<uint16_t*>(ws + W.h16);
+  int8_t* hexp = reinterpret_cast<int8_t*>(ws + W.hexp);
+  int8_t* rexp = reinterpret_cast<int8_t*>(ws + W.rexp);
   float* yf = reinterpret_cast<float*>(ws + W.yf32);
   const int bs_shift = L.bs == 32 ? 5 : L.bs == 64 ? 6 : 7;   // block sizes are 32/64/128
   const int nt1 = gemm_n_tiles(L, true);
@@ -451,39 +636,46 @@ hipError_t launch_gemms(const Layer& L, const uint16_t* xb, char* ws, const Work
   auto fc1 = L.fc1_zp ? grouped_gemm_kernel<BITS, true, true> : grouped_gemm_kernel<BITS, true, false>;
   auto fc2 = L.fc2_zp ? grouped_gemm_kernel<BITS, false, true> : grouped_gemm_kernel<BITS, false, false>;
   fc1<<<static_cast<unsigned>(g1), kGemmThreads, 0, s>>>(
-      xb, sorted, L.k, L.fc1_codes, L.fc1_scales, H, H, I, bs_shift, L.zp, L.fc1_zp, L.fc1_interleaved,
+      xa, sorted, L.k, L.fc1_codes, L.fc1_scales, H, H, I, bs_shift, L.zp, L.fc1_zp, L.fc1_interleaved,
       L.fc1_bias, L.act,
       L.fc1_row_bytes, L.fc1_nblk,
-      tiles, ntiles, nt1, hb, nullptr);
+      tiles, ntiles, nt1, hb, nullptr, xexp, hexp);
   stage_done(L, 6, "gemm_fc1_swiglu");
+  h_common_exponent_kernel<<<static_cast<unsigned>((W.R + 3) / 4), 256, 0, s>>>(hb, hexp, rexp, W.R, I);
+  stage_done(L, 9, "h_common_exponent");
   fc2<<<static_cast<unsigned>(g2), kGemmThreads, 0, s>>>(
       hb, sorted, L.k, L.fc2_codes, L.fc2_scales, I, H, I, bs_shift, L.zp, L.fc2_zp, false, L.fc2_bias,
       L.act,
       L.fc2_row_bytes, L.fc2_nblk,
-      tiles, ntiles, nt2, nullptr, yf);
+      tiles, ntiles, nt2, nullptr, yf, rexp, nullptr);
   stage_done(L, 7, "gemm_fc2");
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_prefill(const Layer& L, const void* x, void* out, int64_t T, char* ws,
-                          const Workspace& W, hipStream_t s) {
-  const uint16_t* xb = static_cast<const uint16_t*>(x);
-  if (!L.act_bf16) {
-    uint16_t* staged = reinterpret_cast<uint16_t*>(ws + W.xbf16);
-    const int64_t n = T * L.H;
-    act_to_bf16_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(x, L.act, n, staged);
-    stage_done(L, 5, "stage_x_bf16");
-    xb = staged;
-  }
-  hipError_t err;
-  switch (L.bits) {
-    case 4: err = launch_gemms<4>(L, xb, ws, W, s); break;
-    case 3: err = launch_gemms<3>(L, xb, ws, W, s); break;
-    default: err = launch_gemms<2>(L, xb, ws, W, s); break;
-  }
-  if (err != hipSuccess) return err;
+hipError_t launch_stage_x(const Layer& L, const void* x, int64_t T, char* ws, const Workspace& W,
+                          hipStream_t s, const uint16_t** xa, const int8_t** xexp) {
+  // fp16 activations go to the matrix cores as they are; bf16 and fp32
+  // ones are staged as fp16 with a per-token exponent
+  *xa = static_cast<const uint16_t*>(x);
+  *xexp = nullptr;
+  if (L.act == kActF16) return hipSuccess;
+  uint16_t* staged = reinterpret_cast<uint16_t*>(ws + W.x16);
+  int8_t* e = reinterpret_cast<int8_t*>(ws + W.xexp);
+  const unsigned grid = static_cast<unsigned>((T + 3) / 4);
+  if (L.act == kActBF16)
+    stage_x_f16_kernel<kActBF16><<<grid, 256, 0, s>>>(x, T, static_cast<int>(L.H), staged, e);
+  else
+    stage_x_f16_kernel<kActF32><<<grid, 256, 0, s>>>(x, T, static_cast<int>(L.H), staged, e);
+  stage_done(L, 5, "stage_x_f16");
+  *xa = staged;
+  *xexp = e;
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const Layer& L, void* out, int64_t T, char* ws, const Workspace& W,
+                          hipStream_t s) {
   const int H = static_cast<int>(L.H);
   dim3 gc((H / 4 + 255) / 256, static_cast<unsigned>(T));
   const float* yf = reinterpret_cast<const float*>(ws + W.yf32);
@@ -497,6 +689,21 @@ hipError_t launch_prefill(const Layer& L, const void* x, void* out, int64_t T, c
     combine_kernel<kActF32><<<gc, 256, 0, s>>>(yf, inv, w, L.k, H, out);
   stage_done(L, 8, "combine");
   return hipGetLastError();
+}
+
+hipError_t launch_prefill(const Layer& L, const void* x, void* out, int64_t T, char* ws,
+                          const Workspace& W, hipStream_t s) {
+  const uint16_t* xa = nullptr;
+  const int8_t* xexp = nullptr;
+  hipError_t err = launch_stage_x(L, x, T, ws, W, s, &xa, &xexp);
+  if (err != hipSuccess) return err;
+  switch (L.bits) {
+    case 4: err = launch_gemms<4>(L, xa, xexp, ws, W, s); break;
+    case 3: err = launch_gemms<3>(L, xa, xexp, ws, W, s); break;
+    default: err = launch_gemms<2>(L, xa, xexp, ws, W, s); break;
+  }
+  if (err != hipSuccess) return err;
+  return launch_combine(L, out, T, ws, W, s);
 }
 
 }  // namespace qmoe

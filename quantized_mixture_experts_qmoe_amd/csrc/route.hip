@@ -237,7 +237,7 @@ hipError_t launch_route(const Layer& L, const void* logits, int64_t T, char* ws,
                                                            L.normalize, topk_id, topk_w, hist);
   }
   stage_done(L, 1, "route_topk_hist");
-  route_scan_kernel<<<1, 1024, 0, s>>>(hist, W.nchunks, E, kTileM,
+  route_scan_kernel<<<1, 1024, 0, s>>>(hist, W.nchunks, E, W.tile_m,
                                        reinterpret_cast<int32_t*>(ws + W.counts),
                                        reinterpret_cast<int32_t*>(ws + W.offsets),
                                        reinterpret_cast<int32_t*>(ws + W.chunk_base),

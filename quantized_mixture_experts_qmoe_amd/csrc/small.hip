@@ -1,0 +1,371 @@
+// Small-batch path (5 to a few hundred tokens): expert-grouped GEMMs whose
+// weights stream from HBM straight into the matrix cores.
+//
+// Between four tokens and a few hundred, each active expert serves only a
+// handful of routes. The grouped GEMMs of the prefill path stage every
+// weight tile through LDS for 256-row tiles that are nearly empty; here each
+// expert's weights are read once per call and go from registers to the
+// matrix cores.
+//
+// Routing is the prefill path's (top-k, histogram, scan, stable scatter)
+// with tiles of at most 16 routes of one expert. Each workgroup (8 waves)
+// takes one tile and a block of output columns:
+//   FC1: the tile's activation rows (fp16, staged per token as for the
+//        prefill GEMMs) go to LDS once; each wave owns 16 h columns, streams
+//        the matching 16 gate and 16 up weight rows, dequantizes each
+//        32-code unit to fp16((q - zp) * s) in registers (the routine the
+//        prefill GEMMs and the export use) and feeds
+//        v_mfma_f32_16x16x32_f16; the epilogue applies SwiGLU and stores h
+//        in fp32 [R, I] in sorted order;
+//   FC2: the tile's h rows go to LDS as fp16 with a per-route exponent (the
+//        range exponent of the row, so no value leaves fp16 range); each
+//        wave owns 32 output columns; the epilogue stores y in fp32 [R, H],
+//        which the prefill path's combine sums per token in slot order and
+//        rounds once.
+// Lane (q, n) of a wave (q = lane / 16, n = lane % 16) loads, for each block
+// of 128 K values, unit 4j + q of its weight row (32 codes, 16 B for INT4):
+// its 32 values are the B operand of the block's four MFMA steps, K values
+// 32(4j + q) + 8t + 0..7 at step t, and the A operand of step t is read from
+// the same K range of the staged rows. So every weight byte is loaded once,
+// by one lane, in 64-byte row segments.
+//
+// Semantics: grouped experts over expert-sorted routes ("[CUDA] Add INT4 and
+// INT3 QMoE CPU/GPU offload support", Description of the grouped prefill
+// path); SwiGLU contract ("[CUDA/CPU] Add AVX2 INT4 cold-expert kernel and
+// zero-cold doorbell short-circuit for QMoE offload", Motivation & Summary
+// item 3); fp32 partial sums rounded once ("[CUDA] Add MoEPacked CPU/GPU
+// hybrid offload and consolidate QMoE/GGUF offload optimizations", Key
+// Changes item 4).
+#include "device.h"
+#include "internal.h"
+
+namespace qmoe {
+
+namespace {
+
+typedef _Float16 sf16x8_t __attribute__((ext_vector_type(8)));
+typedef float sf32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kSmallWaves = 8;
+constexpr int kSmallThreads = kSmallWaves * kWave;
+constexpr int kFc1Cols = kSmallWaves * 16;   // h columns per FC1 workgroup
+constexpr int kFc2Cols = kSmallWaves * 32;   // output columns per FC2 workgroup
+constexpr int kDepth = 4;                    // 128-K blocks of weights in flight per wave
+
+// Logical index of this workgroup: the column blocks of one tile (which
+// share its staged rows) are dealt to one XCD.
+__device__ __forceinline__ int small_logical(int active) {
+  const int b = blockIdx.x;
+  const int per_xcd = (active + 7) / 8;
+  const int j = b / 8;
+  if (j >= per_xcd) return -1;
+  const int L = (b % 8) * per_xcd + j;
+  return L < active ? L : -1;
+}
+
+// One weight row's view for the streaming loop.
+template <int BITS, bool HAS_ZP>
+struct RowStream {
+  const uint8_t* codes;
+  const uint16_t* scales;
+  const uint8_t* zps;
+  int zp, ushift, nunits;   // ushift: log2(block / 32); nunits = K / 32
+  __device__ __forceinline__ void load(int u, UnitWords<BITS>& w, uint32_t& s, int& z) const {
+    const int uc = u < nunits ? u : 0;
+    w = load_unit<BITS>(codes + uc * (4 * BITS));
+    s = u < nunits ? scales[uc >> ushift] : 0u;   // a unit past K weighs zero
+    z = HAS_ZP ? zps[uc >> ushift] : zp;
+  }
+};
+
+// Staged rows are K fp16 values each, in 16-byte pieces: piece c of row r
+// sits at piece c ^ (r mod 16) of the row (K is a multiple of 128, so the
+// swizzle stays inside the row), so the 16 rows an MFMA step reads at one
+// column fall in 16 different pieces of LDS.
+__device__ __forceinline__ int swz(int r, int piece) { return 8 * (piece ^ (r & 15)); }
+
+// acc += A(rows of the block) x B(one unit of one weight row), four steps;
+// arow is this lane's row (l16), col0 the unit's first column.
+__device__ __forceinline__ sf32x4_t mfma_unit(const uint16_t* arow, int l16, int col0,
+                                              const uint32_t (&pairs)[16], sf32x4_t acc) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const sf16x8_t a = *reinterpret_cast<const sf16x8_t*>(arow + swz(l16, (col0 >> 3) + t));
+    const uint4 b4 = make_uint4(pairs[4 * t], pairs[4 * t + 1], pairs[4 * t + 2], pairs[4 * t + 3]);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(sf16x8_t, b4), acc, 0, 0, 0);
+  }
+  return acc;
+}
+
+}  // namespace
+
+// FC1 + SwiGLU over one tile (<= 16 routes of expert e) and 128 h columns.
+// grid = 8 * ceil(max_tiles * n_blocks / 8), block = 512, dynamic LDS =
+// 16 * H * 2 bytes.
+template <int BITS, bool HAS_ZP>
+__global__ __launch_bounds__(kSmallThreads) void small_fc1_kernel(
+    const uint16_t* __restrict__ xa, const int8_t* __restrict__ xexp,
+    const int32_t* __restrict__ sorted_routes, int k, const int4* __restrict__ tiles,
+    const int32_t* __restrict__ num_tiles, const uint8_t* __restrict__ codes,
+    const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zps, int zp, int ushift,
+    int64_t row_bytes, int64_t nblk, int H, int I, bool fc1_il, const void* __restrict__ bias,
+    int act, int n_blocks, float* __restrict__ h32) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  __shared__ int s_exp[kSmallRows];
+  const int active = num_tiles[0] * n_blocks;
+  const int L = small_logical(active);
+  if (L < 0) return;
+  const int4 td = tiles[L / n_blocks];
+  const int e = td.x, row0 = td.y, nrows = td.z, nb = L % n_blocks;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  const int q = lane >> 4, l16 = lane & 15;
+  const int ld = H;
+
+  // stage the tile's activation rows (and their exponents)
+  const int upr = H / 8;   // 16-byte pieces per row
+  for (int i = threadIdx.x; i < nrows * upr; i += kSmallThreads) {
+    const int r = i / upr, c = i % upr;
+    const int64_t tok = sorted_routes[row0 + r] / k;
+    *reinterpret_cast<uint4*>(smem + r * ld + swz(r, c)) =
+        *reinterpret_cast<const uint4*>(xa + tok * H + 8 * c);
+  }
+  if (threadIdx.x < kSmallRows) {
+    const int r = threadIdx.x;
+    s_exp[r] = (xexp != nullptr && r < nrows) ? xexp[sorted_routes[row0 + r] / k] : 0;
+  }
+
+  // this lane's weight rows: gate and up rows of h column n
+  const int n = nb * kFc1Cols + wave * 16 + l16;
+  const int nc = n < I ? n : 0;
+  const int gr = fc1_il ? 2 * nc : nc, ur = fc1_il ? 2 * nc + 1 : I + nc;
+  const int64_t ebase = static_cast<int64_t>(e) * 2 * I;
+  const int nunits = H / 32;
+  RowStream<BITS, HAS_ZP> g{codes + (ebase + gr) * row_bytes, scales + (ebase + gr) * nblk,
+                            HAS_ZP ? zps + (ebase + gr) * nblk : nullptr, zp, ushift, nunits};
+  RowStream<BITS, HAS_ZP> u{codes + (ebase + ur) * row_bytes, scales + (ebase + ur) * nblk,
+                            HAS_ZP ? zps + (ebase + ur) * nblk : nullptr, zp, ushift, nunits};
+  const int nj = (nunits + 3) / 4;
+
+  UnitWords<BITS> wg[kDepth], wu[kDepth];
+  uint32_t sg[kDepth], su[kDepth];
+  int zg[kDepth], zu[kDepth];
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d) {
+    g.load(4 * d + q, wg[d], sg[d], zg[d]);
+    u.load(4 * d + q, wu[d], su[d], zu[d]);
+  }
+  __syncthreads();
+
+  sf32x4_t accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
+  const uint16_t* arow = smem + l16 * ld;
+  for (int j0 = 0; j0 < nj; j0 += kDepth) {
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) {
+      const int j = j0 + d;
+      if (j < nj) {
+        uint32_t pg[16], pu[16];
+        dequant_unit_f16<BITS>(wg[d], sg[d], zg[d], pg);
+        dequant_unit_f16<BITS>(wu[d], su[d], zu[d], pu);
+        const int col0 = 128 * j + 32 * q;
+        accg = mfma_unit(arow, l16, col0, pg, accg);
+        accu = mfma_unit(arow, l16, col0, pu, accu);
+        g.load(4 * (j + kDepth) + q, wg[d], sg[d], zg[d]);
+        u.load(4 * (j + kDepth) + q, wu[d], su[d], zu[d]);
+      }
+    }
+  }
+
+  // epilogue: lane holds rows 4q + i, column n
+  if (n >= I) return;
+  const float bg = bias_at(bias, act, ebase + (fc1_il ? 2 * n : n));
+  const float bu = bias_at(bias, act, ebase + (fc1_il ? 2 * n + 1 : I + n));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * q + i;
+    if (r < nrows) {
+      const int ex = s_exp[r];
+      const float gv = ldexpf(accg[i], ex) + bg, uv = ldexpf(accu[i], ex) + bu;
+      h32[static_cast<int64_t>(row0 + r) * I + n] = silu_mul(gv, uv);
+    }
+  }
+}
+
+// FC2 over one tile and 256 output columns. grid as FC1, block = 512,
+// dynamic LDS = 16 * I * 2 bytes.
+template <int BITS, bool HAS_ZP>
+__global__ __launch_bounds__(kSmallThreads) void small_fc2_kernel(
+    const float* __restrict__ h32, const int4* __restrict__ tiles,
+    const int32_t* __restrict__ num_tiles, const uint8_t* __restrict__ codes,
+    const uint16_t* __restrict__ scales, const uint8_t* __restrict__ zps, int zp, int ushift,
+    int64_t row_bytes, int64_t nblk, int H, int I, const void* __restrict__ bias, int act,
+    int n_blocks, float* __restrict__ y32) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  __shared__ int s_exp[kSmallRows];
+  const int active = num_tiles[0] * n_blocks;
+  const int L = small_logical(active);
+  if (L < 0) return;
+  const int4 td = tiles[L / n_blocks];
+  const int e = td.x, row0 = td.y, nrows = td.z, nb = L % n_blocks;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  const int q = lane >> 4, l16 = lane & 15;
+  const int ld = I;
+
+  // stage h rows as fp16 with the row's range exponent; wave w takes rows
+  // w and w + 8 (rows past the tile are left unset: no stored output reads
+  // them, since row m of a product depends on row m of A only)
+  for (int r = wave; r < nrows; r += kSmallWaves) {
+    const float* hr = h32 + static_cast<int64_t>(row0 + r) * I;
+    float m = 0.0f;
+    bool finite = true;
+    for (int c = lane; c < I; c += kWave) {
+      const float v = hr[c];
+      finite = finite && fabsf(v) <= 3.4028235e38f;
+      m = fmaxf(m, fabsf(v));
+    }
+#pragma unroll
+    for (int off = kWave / 2; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+    const int ex = __all(finite) ? range_exponent(m) : 0;
+    for (int c = 2 * lane; c < I; c += 2 * kWave) {
+      const float2 v = *reinterpret_cast<const float2*>(hr + c);
+      const f16x2_t hv = {static_cast<_Float16>(ldexpf(v.x, -ex)), static_cast<_Float16>(ldexpf(v.y, -ex))};
+      *reinterpret_cast<f16x2_t*>(smem + r * ld + swz(r, c >> 3) + (c & 7)) = hv;
+    }
+    if (lane == 0) s_exp[r] = ex;
+  }
+
+  const int nunits = I / 32;
+  const int nj = (nunits + 3) / 4;
+  const int64_t ebase = static_cast<int64_t>(e) * H;
+  int cols[2];
+  RowStream<BITS, HAS_ZP> w2[2];
+#pragma unroll
+  for (int sidx = 0; sidx < 2; ++sidx) {
+    cols[sidx] = nb * kFc2Cols + wave * 32 + 16 * sidx + l16;
+    const int mc = cols[sidx] < H ? cols[sidx] : 0;
+    w2[sidx] = RowStream<BITS, HAS_ZP>{codes + (ebase + mc) * row_bytes, scales + (ebase + mc) * nblk,
+                                       HAS_ZP ? zps + (ebase + mc) * nblk : nullptr, zp, ushift,
+                                       nunits};
+  }
+  UnitWords<BITS> wv[2][kDepth];
+  uint32_t sv[2][kDepth];
+  int zv[2][kDepth];
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d)
+#pragma unroll
+    for (int sidx = 0; sidx < 2; ++sidx) w2[sidx].load(4 * d + q, wv[sidx][d], sv[sidx][d], zv[sidx][d]);
+  __syncthreads();
+
+  sf32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  const uint16_t* arow = smem + l16 * ld;
+  for (int j0 = 0; j0 < nj; j0 += kDepth) {
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) {
+      const int j = j0 + d;
+      if (j < nj) {
+        const int col0 = 128 * j + 32 * q;
+#pragma unroll
+        for (int sidx = 0; sidx < 2; ++sidx) {
+          uint32_t p[16];
+          dequant_unit_f16<BITS>(wv[sidx][d], sv[sidx][d], zv[sidx][d], p);
+          acc[sidx] = mfma_unit(arow, l16, col0, p, acc[sidx]);
+          w2[sidx].load(4 * (j + kDepth) + q, wv[sidx][d], sv[sidx][d], zv[sidx][d]);
+        }
+      }
+    }
+  }
+
+#pragma unroll
+  for (int sidx = 0; sidx < 2; ++sidx) {
+    const int m = cols[sidx];
+    if (m >= H) continue;
+    const float b = bias_at(bias, act, ebase + m);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * q + i;
+      if (r < nrows)
+        __builtin_nontemporal_store(ldexpf(acc[sidx][i], s_exp[r]) + b,
+                                    &y32[static_cast<int64_t>(row0 + r) * H + m]);
+    }
+  }
+}
+
+namespace {
+
+template <int BITS>
+hipError_t launch_small_gemms(const Layer& L, const uint16_t* xa, const int8_t* xexp, char* ws,
+                              const Workspace& W, hipStream_t s) {
+  const int H = static_cast<int>(L.H), I = static_cast<int>(L.I);
+  const int32_t* sorted = reinterpret_cast<const int32_t*>(ws + W.sorted_routes);
+  const int4* tiles = reinterpret_cast<const int4*>(ws + W.tiles);
+  const int32_t* ntiles = reinterpret_cast<const int32_t*>(ws + W.num_tiles);
+  float* h32 = reinterpret_cast<float*>(ws + W.h32);
+  float* y32 = reinterpret_cast<float*>(ws + W.yf32);
+  const int ushift = L.bs == 32 ? 0 : L.bs == 64 ? 1 : 2;
+  const int nb1 = (I + kFc1Cols - 1) / kFc1Cols, nb2 = (H + kFc2Cols - 1) / kFc2Cols;
+  const int64_t g1 = 8 * ((W.max_tiles * nb1 + 7) / 8), g2 = 8 * ((W.max_tiles * nb2 + 7) / 8);
+  const size_t lds1 = static_cast<size_t>(kSmallRows) * H * 2;
+  const size_t lds2 = static_cast<size_t>(kSmallRows) * I * 2;
+  auto fc1 = L.fc1_zp ? small_fc1_kernel<BITS, true> : small_fc1_kernel<BITS, false>;
+  auto fc2 = L.fc2_zp ? small_fc2_kernel<BITS, true> : small_fc2_kernel<BITS, false>;
+  fc1<<<static_cast<unsigned>(g1), kSmallThreads, lds1, s>>>(
+      xa, xexp, sorted, L.k, tiles, ntiles, L.fc1_codes, L.fc1_scales, L.fc1_zp, L.zp, ushift,
+      L.fc1_row_bytes, L.fc1_nblk, H, I, L.fc1_interleaved, L.fc1_bias, L.act, nb1, h32);
+  stage_done(L, 6, "small_fc1_swiglu");
+  fc2<<<static_cast<unsigned>(g2), kSmallThreads, lds2, s>>>(
+      h32, tiles, ntiles, L.fc2_codes, L.fc2_scales, L.fc2_zp, L.zp, ushift, L.fc2_row_bytes,
+      L.fc2_nblk, H, I, L.fc2_bias, L.act, nb2, y32);
+  stage_done(L, 7, "small_fc2");
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool small_path_supported(const Layer& L) {
+  // K values in whole 128-wide blocks (four units per lane and block), and a
+  // tile's staged rows (16 x K fp16) within 128 KB of LDS
+  return L.H % 128 == 0 && L.I % 128 == 0 && L.H <= 4096 && L.I <= 4096;
+}
+
+// Allow each instance the dynamic LDS its largest layer needs (beyond the
+// 64 KB default of a launch).
+hipError_t prepare_small(const Layer& L) {
+  const int b1 = static_cast<int>(kSmallRows * L.H * 2), b2 = static_cast<int>(kSmallRows * L.I * 2);
+  const void* f1[] = {reinterpret_cast<const void*>(&small_fc1_kernel<4, false>),
+                      reinterpret_cast<const void*>(&small_fc1_kernel<4, true>),
+                      reinterpret_cast<const void*>(&small_fc1_kernel<3, false>),
+                      reinterpret_cast<const void*>(&small_fc1_kernel<3, true>),
+                      reinterpret_cast<const void*>(&small_fc1_kernel<2, false>),
+                      reinterpret_cast<const void*>(&small_fc1_kernel<2, true>)};
+  const void* f2[] = {reinterpret_cast<const void*>(&small_fc2_kernel<4, false>),
+                      reinterpret_cast<const void*>(&small_fc2_kernel<4, true>),
+                      reinterpret_cast<const void*>(&small_fc2_kernel<3, false>),
+                      reinterpret_cast<const void*>(&small_fc2_kernel<3, true>),
+                      reinterpret_cast<const void*>(&small_fc2_kernel<2, false>),
+                      reinterpret_cast<const void*>(&small_fc2_kernel<2, true>)};
+  for (const void* f : f1) {
+    const hipError_t err = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, b1);
+    if (err != hipSuccess) return err;
+  }
+  for (const void* f : f2) {
+    const hipError_t err = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, b2);
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_small(const Layer& L, const void* x, void* out, int64_t T, char* ws,
+                        const Workspace& W, hipStream_t s) {
+  const uint16_t* xa = nullptr;
+  const int8_t* xexp = nullptr;
+  hipError_t err = launch_stage_x(L, x, T, ws, W, s, &xa, &xexp);
+  if (err != hipSuccess) return err;
+  switch (L.bits) {
+    case 4: err = launch_small_gemms<4>(L, xa, xexp, ws, W, s); break;
+    case 3: err = launch_small_gemms<3>(L, xa, xexp, ws, W, s); break;
+    default: err = launch_small_gemms<2>(L, xa, xexp, ws, W, s); break;
+  }
+  if (err != hipSuccess) return err;
+  return launch_combine(L, out, T, ws, W, s);
+}
+
+}  // namespace qmoe

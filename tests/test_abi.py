@@ -117,3 +117,37 @@ def test_product_path_has_no_cpu_fallback():
             assert "import oracle" not in src and "from oracle" not in src, path
             assert "qmoe_oracle" not in src and "liboracle" not in src, path
     assert "raise ImportError" in open(q.__file__).read()
+
+
+def _weights(E=4, H=64, I=32, bits=4, bs=32):
+    import torch
+    return [torch.zeros((E, 2 * I, H * bits // 8), dtype=torch.uint8),
+            torch.zeros((E, 2 * I, H // bs), dtype=torch.float16),
+            torch.zeros((E, H, I * bits // 8), dtype=torch.uint8),
+            torch.zeros((E, H, I // bs), dtype=torch.float16)]
+
+
+@pytest.mark.parametrize("which,bad", [(0, (4, 64, 31)), (1, (4, 64, 3)), (2, (4, 64, 15)),
+                                       (3, (3, 64, 1)), (0, (4, 32, 32)), (2, (4, 63, 16))])
+def test_binding_rejects_weight_shapes(which, bad):
+    """QMoELayer checks the four weight tensors against the layer's shapes
+    before anything reaches the library (a short tensor would be read out of
+    bounds on the GPU)."""
+    import torch
+    cfg = q.LayerConfig(64, 32, 4, 2, 4, 32)
+    w = _weights()
+    w[which] = torch.zeros(bad, dtype=w[which].dtype)
+    with pytest.raises(ValueError, match="must be shaped"):
+        q.QMoELayer(cfg, *w)
+
+
+@pytest.mark.parametrize("bits,bs", [(3, 64), (2, 128), (4, 32)])
+def test_binding_accepts_weight_shapes(bits, bs):
+    """Correct shapes pass the shape check (the next check, on the device,
+    rejects these CPU tensors)."""
+    H, I = 256, 128
+    cfg = q.LayerConfig(H, I, 4, 2, bits, bs)
+    w = _weights(4, H, I, bits, bs)
+    q.check_weight_shapes(cfg, *w)
+    with pytest.raises(ValueError, match="GPU tensors"):
+        q.QMoELayer(cfg, *w)
