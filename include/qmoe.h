@@ -40,9 +40,10 @@
  *    synchronizing; only launch errors are reported (QMOE_ERR_HIP);
  *  - a handle may be used from one stream at a time (see qmoe_create);
  *  - environment variables read once, by qmoe_create, change nothing unless
- *    set: QMOE_FORCE_PATH=prefill|decode_split forces one path (debugging and
- *    tests); QMOE_FUSED_GRID, QMOE_FUSED_EPOCH_START and QMOE_FUSED_SPIN_LIMIT
- *    are test hooks of the fused decode (a smaller grid, the epoch counter's
+ *    set: QMOE_FORCE_PATH=prefill|small|grouped|decode_split forces one
+ *    path (grouped: the fused decode in groups of four up to 24 tokens;
+ *    debugging, tests and measurement); QMOE_FUSED_GRID,
+ *    QMOE_FUSED_EPOCH_START and QMOE_FUSED_SPIN_LIMIT are test hooks of the fused decode (a smaller grid, the epoch counter's
  *    start, the bound of its waits) that exist so the tests can reach its
  *    rare schedules and error paths.
  */
@@ -187,12 +188,15 @@ qmoe_status qmoe_workspace_size(const qmoe_handle *handle, int64_t num_tokens, s
  * Dispatch:
  *  - 1..4 tokens: the fused single-launch decode where it applies (see
  *    qmoe_create), else the split decode (three launches);
- *  - 5..24 tokens on layers the fused decode serves: the fused decode once
+ *  - 5..12 tokens on layers the fused decode serves: the fused decode once
  *    per group of up to four tokens;
- *  - otherwise: routing, then the grouped fp16 matrix-core GEMMs over
- *    expert-sorted routes, then the combine.
+ *  - up to 256 tokens: routing, then the small-batch GEMMs (each active
+ *    expert's weights streamed once per call into the fp16 matrix cores for
+ *    up to 16 of its routes at a time), then the combine;
+ *  - more tokens: routing, then the grouped fp16 matrix-core GEMMs over
+ *    expert-sorted routes in tiles of 256, then the combine.
  * A call made while `stream` is being captured into a HIP graph takes the
- * split decode (1..4 tokens) or the grouped GEMMs (above): the fused
+ * split decode (1..4 tokens) or the batched paths (above): the fused
  * decode's per-call epoch cannot be replayed.
  *
  * The fused decode's workgroups exchange results through the handle's
