@@ -43,9 +43,10 @@
  *    set: QMOE_FORCE_PATH=prefill|small|grouped|decode_split forces one
  *    path (grouped: the fused decode in groups of four up to 24 tokens;
  *    debugging, tests and measurement); QMOE_FUSED_GRID,
- *    QMOE_FUSED_EPOCH_START and QMOE_FUSED_SPIN_LIMIT are test hooks of the fused decode (a smaller grid, the epoch counter's
- *    start, the bound of its waits) that exist so the tests can reach its
- *    rare schedules and error paths.
+ *    QMOE_FUSED_EPOCH_START and QMOE_FUSED_SPIN_LIMIT are test hooks of the
+ *    fused decode (a smaller grid, the epoch counter's start, the bound of
+ *    its waits) that exist so the tests can reach its rare schedules and
+ *    error paths.
  */
 #ifndef QMOE_H
 #define QMOE_H
