@@ -212,6 +212,30 @@ qmoe_status qmoe_forward(qmoe_handle *handle, const void *x, const void *logits,
                          int64_t num_tokens, void *workspace, size_t workspace_bytes,
                          void *stream);
 
+/*
+ * Size in bytes of the device array qmoe_forward_noalloc uses as its
+ * workspace (one array per GPU the library runs on, held until the process
+ * ends).
+ */
+#define QMOE_NOALLOC_WORKSPACE_BYTES (32u << 20)
+
+/*
+ * qmoe_forward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments, result and dispatch as qmoe_forward, without the workspace:
+ * the call uses the library's own device array of
+ * QMOE_NOALLOC_WORKSPACE_BYTES bytes on the handle's device and allocates
+ * nothing. Calls whose workspace (qmoe_workspace_size) would exceed that size
+ * return QMOE_ERR_WORKSPACE and enqueue nothing; at the Qwen3-30B-A3B layer
+ * shape that allows every decode size and packed batches of about 400
+ * tokens. Every handle on one GPU shares that GPU's array: calls on the same
+ * GPU whose work overlaps in time (different streams, different threads)
+ * race on it, and must be ordered by the caller. Nothing in it needs to
+ * start at zero. QMOE_ERR_UNSUPPORTED for device ordinals of 64 and above.
+ */
+qmoe_status qmoe_forward_noalloc(qmoe_handle *handle, const void *x, const void *logits, void *out,
+                                 int64_t num_tokens, void *stream);
+
 /* Release a handle: its host state and, when it has one, its device
  * exchange buffer (after which no call may be in flight on it).
  * qmoe_destroy(NULL) returns QMOE_OK. */

@@ -23,7 +23,8 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration",
 
 EXPORTS = ("qmoe_create", "qmoe_workspace_size", "qmoe_forward", "qmoe_destroy",
            "qmoe_status_string", "qmoe_route", "qmoe_dequant", "qmoe_workspace_routing",
-           "qmoe_set_stage_hook", "qmoe_decode_errors")
+           "qmoe_set_stage_hook", "qmoe_decode_errors", "qmoe_forward_noalloc")
+NOALLOC_WORKSPACE_BYTES = 32 << 20   # QMOE_NOALLOC_WORKSPACE_BYTES (include/qmoe.h)
 
 STAGE_FN = ctypes.CFUNCTYPE(None, ctypes.c_void_p, ctypes.c_int, ctypes.c_char_p)
 
@@ -77,9 +78,10 @@ def lib() -> ctypes.CDLL:
         L.qmoe_workspace_routing.argtypes = [P, i64, ctypes.POINTER(sz), ctypes.POINTER(sz)]
         L.qmoe_set_stage_hook.argtypes = [P, STAGE_FN, P]
         L.qmoe_decode_errors.argtypes = [P, P, ctypes.POINTER(ctypes.c_uint32)]
+        L.qmoe_forward_noalloc.argtypes = [P, P, P, P, i64, P]
         for name in ("qmoe_create", "qmoe_workspace_size", "qmoe_forward", "qmoe_destroy",
                      "qmoe_route", "qmoe_dequant", "qmoe_workspace_routing", "qmoe_set_stage_hook",
-                     "qmoe_decode_errors"):
+                     "qmoe_decode_errors", "qmoe_forward_noalloc"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib

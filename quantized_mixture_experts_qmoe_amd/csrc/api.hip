@@ -9,6 +9,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 
 #include "device.h"
@@ -160,7 +161,34 @@ size_t required_bytes(const qmoe_handle* h, int64_t T) {
   return need;
 }
 
-// The dispatch behind qmoe_forward; the caller
+// Workspace of qmoe_forward_noalloc: a file-scope device array, one copy per
+// GPU the library runs on, held until the process ends. In host code the
+// symbol's name is no device address: qmoe_create resolves each device's
+// copy once (with that device current) and every use goes through the
+// pointer kept here.
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[QMOE_NOALLOC_WORKSPACE_BYTES];
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];
+
+// Resolve the calling thread's current device's copy of `scratch`, once.
+hipError_t resolve_scratch(int device) {
+  if (device >= kMaxDevices) return hipSuccess;   // qmoe_forward_noalloc refuses such devices
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[device]) return hipSuccess;
+  void* p = nullptr;
+  const hipError_t err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (err == hipSuccess) g_scratch[device] = p;
+  return err;
+}
+
+void* scratch_for(int device) {
+  if (device < 0 || device >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  return g_scratch[device];
+}
+
+// The dispatch shared by qmoe_forward and qmoe_forward_noalloc; the caller
 // has validated the arguments, checked that `ws` holds required_bytes(h, T)
 // bytes and made the handle's device current.
 qmoe_status forward_impl(qmoe_handle* h, const void* x, const void* logits, void* out, int64_t T,
@@ -258,7 +286,7 @@ qmoe_status qmoe_create(const qmoe_config* c, const qmoe_weights* w, int device,
   h->spin_limit = 0;
   {
     DeviceGuard guard(device);
-    if (!guard.ok() ||
+    if (!guard.ok() || resolve_scratch(device) != hipSuccess ||
         (h->small_ok && prepare_small(L) != hipSuccess)) {
       delete h;
       return QMOE_ERR_HIP;
@@ -318,6 +346,20 @@ qmoe_status qmoe_forward(qmoe_handle* h, const void* x, const void* logits, void
   if (!x || !logits || !out || !aligned16(x) || !aligned16(logits) || !aligned16(out))
     return QMOE_ERR_INVALID_ARG;
   if (!ws || !aligned16(ws) || ws_bytes < required_bytes(h, T)) return QMOE_ERR_WORKSPACE;
+  DeviceGuard guard(h->device);
+  if (!guard.ok()) return QMOE_ERR_HIP;
+  return forward_impl(h, x, logits, out, T, ws, static_cast<hipStream_t>(stream));
+}
+
+qmoe_status qmoe_forward_noalloc(qmoe_handle* h, const void* x, const void* logits, void* out,
+                                 int64_t T, void* stream) {
+  if (!h || T < 0 || T > h->L.max_tokens) return QMOE_ERR_INVALID_ARG;
+  if (T == 0) return QMOE_OK;
+  if (!x || !logits || !out || !aligned16(x) || !aligned16(logits) || !aligned16(out))
+    return QMOE_ERR_INVALID_ARG;
+  if (required_bytes(h, T) > QMOE_NOALLOC_WORKSPACE_BYTES) return QMOE_ERR_WORKSPACE;
+  void* ws = scratch_for(h->device);
+  if (!ws) return QMOE_ERR_UNSUPPORTED;
   DeviceGuard guard(h->device);
   if (!guard.ok()) return QMOE_ERR_HIP;
   return forward_impl(h, x, logits, out, T, ws, static_cast<hipStream_t>(stream));

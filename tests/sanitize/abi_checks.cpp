@@ -115,6 +115,8 @@ int main() {
   CHECK(qmoe_workspace_size(nullptr, 4, &n) == QMOE_ERR_INVALID_ARG, "workspace_size NULL");
   CHECK(qmoe_forward(nullptr, nullptr, nullptr, nullptr, 4, nullptr, 0, nullptr) == QMOE_ERR_INVALID_ARG,
         "forward NULL");
+  CHECK(qmoe_forward_noalloc(nullptr, nullptr, nullptr, nullptr, 4, nullptr) == QMOE_ERR_INVALID_ARG,
+        "forward_noalloc NULL");
   CHECK(qmoe_route(nullptr, nullptr, 4, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, nullptr) ==
             QMOE_ERR_INVALID_ARG,
         "route NULL");
