@@ -247,8 +247,11 @@ const char *qmoe_status_string(int status);
 /*
  * Test exports. Same conventions as above.
  *
- * qmoe_route runs only the routing stage of the prefill path on `num_tokens`
- * tokens (any count 1..max_tokens) and copies its results out. The
+ * qmoe_route runs only the routing stage of the batched paths on
+ * `num_tokens` tokens (any count 1..max_tokens) and copies its results out:
+ * the one-launch routing of the small-batch path when a forward of that
+ * many tokens would take that path and its route list fits the launch, else
+ * the chunked routing of the grouped GEMMs. The
  * expert-sorted route map with per-expert first offsets is the grouped
  * GEMMs' input ("[CUDA] Add INT4 and INT3 QMoE CPU/GPU offload support",
  * Description: sorted routes, tile descriptors, expert first-token offsets);
@@ -261,7 +264,7 @@ const char *qmoe_status_string(int status);
  * All output pointers are device pointers; any of them may be NULL to skip it.
  * Errors: QMOE_ERR_INVALID_ARG for a bad handle, count or logits pointer;
  * QMOE_ERR_WORKSPACE if the workspace is smaller than
- * qmoe_workspace_size(num_tokens) of the grouped path.
+ * qmoe_workspace_size(num_tokens).
  */
 qmoe_status qmoe_route(qmoe_handle *handle, const void *logits, int64_t num_tokens,
                        int32_t *topk_id, float *topk_w, int32_t *expert_offsets,

@@ -56,10 +56,10 @@ constexpr int kForceNone = 0, kForcePrefill = 1, kForceSmall = 2, kForceGrouped 
 // small-batch path, which streams each active expert's weights once per
 // call; larger batches run the grouped GEMMs on 256-row tiles. Measured on
 // the Qwen3-30B-A3B-shaped INT4 layer (us per call, cold weights):
-//   tokens          5     8    12    16    24    32    64   128   256
-//   grouped decode 54    65    96   125   186
-//   small path     81   101   112   115   144   148   161   176   235
-//   grouped GEMMs 114   158   177   179   241   244   251   258   265
+//   tokens          5     8    12    13    16    24    32    64   128   256
+//   grouped decode 53    65    96   116   125   186
+//   small path     64    83    95    96    97   124   128   146   170   240
+//   grouped GEMMs 114   158   177         179   241   244   251   258   265
 // QMOE_FORCE_PATH=grouped extends the grouped decode to 24 tokens.
 constexpr int64_t kGroupedDecodeMaxTokens = 12;
 constexpr int64_t kGroupedDecodeForcedMax = 24;
@@ -107,7 +107,9 @@ static Workspace layout(const Layer& L, int64_t T, Path path) {
     W.inv_pos = take(static_cast<size_t>(R * 4));
     W.tiles = take(static_cast<size_t>(W.max_tiles * 16));
     W.num_tiles = take(4);
-    W.x16 = L.act == kActF16 ? 0 : take(static_cast<size_t>(T * L.H * 2));
+    // fp16 activations are staged only to put them in operand order
+    const bool staged = L.act != kActF16 || operand_perm(L.bits) != 0;
+    W.x16 = staged ? take(static_cast<size_t>(T * L.H * 2)) : 0;
     W.xexp = L.act == kActF16 ? 0 : take(static_cast<size_t>(T));
     if (path == Path::kSmall) {
       W.h32 = take(static_cast<size_t>(R * L.I * 4));
@@ -370,13 +372,17 @@ qmoe_status qmoe_route(qmoe_handle* h, const void* logits, int64_t T, int32_t* t
                        size_t ws_bytes, void* stream) {
   if (!h || T < 1 || T > h->L.max_tokens) return QMOE_ERR_INVALID_ARG;
   if (!logits || !aligned16(logits)) return QMOE_ERR_INVALID_ARG;
-  const Workspace W = layout(h->L, T, Path::kPrefill);
+  // the routing a forward of T tokens runs on the batched paths
+  const Path path = choose_path(h->L, h->force, h->small_ok, h->fused_ok && !h->split_decode, T);
+  const bool small = path == Path::kSmall && route_small_fits(h->L, T);
+  const Workspace W = layout(h->L, T, small ? Path::kSmall : Path::kPrefill);
   if (!ws || !aligned16(ws) || ws_bytes < W.total) return QMOE_ERR_WORKSPACE;
   DeviceGuard guard(h->device);
   if (!guard.ok()) return QMOE_ERR_HIP;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(ws);
-  hipError_t err = launch_route(h->L, logits, T, base, W, s);
+  hipError_t err = small ? launch_route_small(h->L, logits, nullptr, T, base, W, s, nullptr, nullptr)
+                         : launch_route(h->L, logits, T, base, W, s);
   const size_t R = static_cast<size_t>(W.R);
   auto copy = [&](void* dst, size_t off, size_t bytes) {
     if (dst && err == hipSuccess) err = hipMemcpyAsync(dst, base + off, bytes, hipMemcpyDeviceToDevice, s);
@@ -487,10 +493,12 @@ qmoe_status forward_impl(qmoe_handle* h, const void* x, const void* logits, void
     }
   } else {
     const Workspace W = layout(h->L, T, path);
-    err = launch_route(h->L, logits, T, base, W, s);
-    if (err == hipSuccess)
-      err = path == Path::kSmall ? launch_small(h->L, x, out, T, base, W, s)
-                                 : launch_prefill(h->L, x, out, T, base, W, s);
+    if (path == Path::kSmall) {
+      err = launch_small(h->L, x, logits, out, T, base, W, s);
+    } else {
+      err = launch_route(h->L, logits, T, base, W, s);
+      if (err == hipSuccess) err = launch_prefill(h->L, x, out, T, base, W, s);
+    }
   }
   return err == hipSuccess ? QMOE_OK : QMOE_ERR_HIP;
 }

@@ -4,8 +4,9 @@
 //                    zero point or the row's per-block code): the code comes
 //                    back out of the bf16 pair 1 + q/128 that unit_pair builds
 //                    (exact), placed at the code index pair_a/pair_b name;
-//   out_f16[n][k]  = the fp16 operand fp16((q - zp) * s) the prefill GEMM
-//                    stages in LDS, from the same routine (dequant_unit_f16).
+//   out_f16[n][k]  = the fp16 operand fp16((q - zp) * s) the batched paths
+//                    feed the matrix cores, from the same routine
+//                    (dequant_unit_f16), moved from operand order to K order.
 //
 // Dequantization W = (q - zp) * s[n][k / block] ("[CUDA] Add INT4 and INT3
 // QMoE CPU/GPU offload support", Description: raw integer experts, block
@@ -43,12 +44,14 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
     }
   }
   if (out_f16) {
+    // pairs in operand order, written back to their K positions
     uint32_t pairs[16];
     dequant_unit_f16<BITS>(w, sbits, zp, pairs);
+    constexpr int P = operand_perm(BITS);
 #pragma unroll
     for (int p = 0; p < 16; ++p) {
-      out_f16[base + 2 * p] = static_cast<uint16_t>(pairs[p] & 0xFFFFu);
-      out_f16[base + 2 * p + 1] = static_cast<uint16_t>(pairs[p] >> 16);
+      out_f16[base + operand_k(P, 2 * p)] = static_cast<uint16_t>(pairs[p] & 0xFFFFu);
+      out_f16[base + operand_k(P, 2 * p + 1)] = static_cast<uint16_t>(pairs[p] >> 16);
     }
   }
 }

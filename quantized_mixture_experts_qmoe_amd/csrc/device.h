@@ -127,7 +127,7 @@ __device__ __forceinline__ uint32_t unit_pair(const UnitWords<BITS>& u, int p) {
 // The grouped (prefill) GEMMs feed the matrix cores fp16 operands. A weight
 // enters as fp16((q - zp) * s): round to nearest even of the exact product,
 // with gradual underflow. dequant_unit_f16 forms it for the 32 codes of a
-// unit, as 16 packed pairs in natural order (pair p = codes 2p, 2p+1):
+// unit, as 16 packed pairs in operand order (defined with it below):
 //   1. each pair of codes becomes the fp16 pair (1024 + q_a, 1024 + q_b): the
 //      code is OR-ed into the mantissa of 1024.0 (0x6400), exact for q < 1024;
 //   2. adding -(1024 + zp) gives q - zp exactly (small integers);
@@ -159,6 +159,34 @@ __device__ __forceinline__ int range_exponent_lo(float m) {
 __device__ __forceinline__ int range_exponent(float m) { return range_exponent_lo<-3>(m); }
 __device__ __forceinline__ int h_chunk_exponent(float m) { return range_exponent_lo<-14>(m); }
 
+// The fp16 matrix operands of the batched paths hold their K values in an
+// order of their own ("operand order") that lets the dequantization build a
+// pair of codes with one shift and one mask: within each group of 8 (INT4)
+// or 16 (INT2) K values, position 2j holds K value j and position 2j + 1 K
+// value j + 4 (INT4) or j + 8 (INT2); INT3 keeps K order. Every operand of a
+// dot product uses the same order (the activation rows and h are written in
+// it), so the products are unchanged; only the order of the additions inside
+// a matrix-core step differs.
+__host__ __device__ constexpr int operand_perm(int bits) { return bits == 4 ? 8 : bits == 2 ? 16 : 0; }
+// K value held at operand position pos
+__host__ __device__ constexpr int operand_k(int perm, int pos) {
+  return perm == 8    ? (pos & ~7) + ((pos & 7) >> 1) + 4 * (pos & 1)
+         : perm == 16 ? (pos & ~15) + ((pos & 15) >> 1) + 8 * (pos & 1)
+                      : pos;
+}
+// operand position of K value k
+__host__ __device__ constexpr int operand_pos(int perm, int k) {
+  return perm == 8    ? (k & ~7) + 2 * (k & 3) + ((k >> 2) & 1)
+         : perm == 16 ? (k & ~15) + 2 * (k & 7) + ((k >> 3) & 1)
+                      : k;
+}
+
+// One 32-code unit dequantized to the fp16 operand fp16((q - zp) * s), as
+// 16 pairs in operand order (pair p = operand positions 2p, 2p + 1). Each
+// pair is built exactly as the fp16 numbers 1024 + q (the code OR-ed into
+// the mantissa of 1024.0), then a packed add of -(1024 + zp) (exact: small
+// integers) and a packed multiply by the scale, the only rounding. Shared by
+// both batched paths and the export of qmoe_dequant.
 template <int BITS>
 __device__ __forceinline__ void dequant_unit_f16(const UnitWords<BITS>& u, uint32_t scale_bits, int zp,
                                                  uint32_t (&out)[16]) {
@@ -166,43 +194,119 @@ __device__ __forceinline__ void dequant_unit_f16(const UnitWords<BITS>& u, uint3
   const f16x2_t sv = {s, s};
   const _Float16 o = static_cast<_Float16>(-(1024 + zp));
   const f16x2_t off = {o, o};
-  constexpr uint32_t kBias = 0x64006400u;   // fp16 1024.0 in both halves
+  // v_perm_b32 picks bytes of {0x64646464 (bytes 4-7), codes (bytes 0-3)}:
+  // selector kSelEven builds (0x64 | byte 0, 0x64 | byte 2) as the fp16
+  // pair (1024 + byte 0, 1024 + byte 2), kSelOdd the same from bytes 1, 3
+  constexpr uint32_t kHigh = 0x64646464u, kSelEven = 0x04020400u, kSelOdd = 0x04030401u;
   if constexpr (BITS == 4) {
-    // dword d holds codes 8d..8d+7 as nibbles; byte b of lo / hi holds
-    // codes 8d + 2b / 8d + 2b + 1
+    // dword d holds codes 8d..8d+7 as nibbles; the low nibbles of its bytes
+    // are codes 8d + {0, 2, 4, 6}, the high ones 8d + {1, 3, 5, 7}: pair
+    // 4d + j = codes (8d + j, 8d + j + 4)
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      const uint32_t w = u.w[d];
-      const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const uint32_t pr = ((lo >> (8 * b)) & 0xFFu) | (((hi >> (8 * b)) & 0xFFu) << 16);
-        out[4 * d + b] = f16_pair_scale(pr | kBias, off, sv);
-      }
+      const uint32_t lo = u.w[d] & 0x0F0F0F0Fu, hi = (u.w[d] >> 4) & 0x0F0F0F0Fu;
+      out[4 * d + 0] = f16_pair_scale(__builtin_amdgcn_perm(kHigh, lo, kSelEven), off, sv);
+      out[4 * d + 1] = f16_pair_scale(__builtin_amdgcn_perm(kHigh, hi, kSelEven), off, sv);
+      out[4 * d + 2] = f16_pair_scale(__builtin_amdgcn_perm(kHigh, lo, kSelOdd), off, sv);
+      out[4 * d + 3] = f16_pair_scale(__builtin_amdgcn_perm(kHigh, hi, kSelOdd), off, sv);
     }
   } else if constexpr (BITS == 2) {
-    // dword d holds codes 16d..16d+15, two bits each; pair p = nibble p
+    // dword d holds codes 16d..16d+15, two bits each; bits [2i, 2i+2) of
+    // its bytes are codes 16d + i + {0, 4, 8, 12}: pair 8d + j = codes
+    // (16d + j, 16d + j + 8)
 #pragma unroll
     for (int d = 0; d < 2; ++d) {
-      const uint32_t w = u.w[d];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t nib = (w >> (4 * j)) & 0xFu;
-        const uint32_t pr = (nib & 3u) | ((nib >> 2) << 16);
-        out[8 * d + j] = f16_pair_scale(pr | kBias, off, sv);
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t c = (u.w[d] >> (2 * i)) & 0x03030303u;
+        out[8 * d + i] = f16_pair_scale(__builtin_amdgcn_perm(kHigh, c, kSelEven), off, sv);
+        out[8 * d + 4 + i] = f16_pair_scale(__builtin_amdgcn_perm(kHigh, c, kSelOdd), off, sv);
       }
     }
   } else {
-    // pair p = the six bits [6p, 6p + 6) of the 96-bit unit
+    // pair p = codes (2p, 2p + 1), the six bits [6p, 6p + 6) of the 96-bit unit
 #pragma unroll
     for (int p = 0; p < 16; ++p) {
       const int bit = 6 * p, d = bit >> 5, o6 = bit & 31;
       const uint32_t f = (o6 <= 26) ? (u.w[d] >> o6) & 63u
                                     : __builtin_amdgcn_alignbit(u.w[d + 1], u.w[d], o6) & 63u;
       const uint32_t pr = (f & 7u) | ((f >> 3) << 16);
-      out[p] = f16_pair_scale(pr | kBias, off, sv);
+      out[p] = f16_pair_scale(pr | 0x64006400u, off, sv);
     }
   }
+}
+
+// ---------------------------------------------------------------- activation staging
+
+// The batched paths' activations, in operand order (P = operand_perm of the
+// layer's bits), for token t, by one wave: bf16 and fp32 rows scaled by
+// 2^-e_t and rounded once to fp16, e_t = range_exponent of the row's largest
+// magnitude (0 for a row with a non-finite value), e_t to xexp[t]; fp16 rows
+// copied as they are (no exponent). bf16 rows come through exactly (8
+// significant bits), fp32 rows are rounded to 11. 16 consecutive values per
+// lane.
+template <int ACT, int P>
+__device__ __forceinline__ void stage_x_row(const void* __restrict__ x, int64_t t, int H,
+                                            uint16_t* __restrict__ x16, int8_t* __restrict__ xexp,
+                                            int lane) {
+  auto load16 = [&](int i, float (&v)[16]) {
+    if constexpr (ACT == kActF32) {
+      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(x) + t * H + i);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 a = p[q];
+        v[4 * q] = a.x; v[4 * q + 1] = a.y; v[4 * q + 2] = a.z; v[4 * q + 3] = a.w;
+      }
+    } else {
+      const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + t * H + i);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const uint4 u = p[q];
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint16_t lo = static_cast<uint16_t>(w[j] & 0xFFFFu), hi = static_cast<uint16_t>(w[j] >> 16);
+          v[8 * q + 2 * j] = ACT == kActBF16 ? bf16_to_f32(lo) : half_to_f32(lo);
+          v[8 * q + 2 * j + 1] = ACT == kActBF16 ? bf16_to_f32(hi) : half_to_f32(hi);
+        }
+      }
+    }
+  };
+  int e = 0;
+  if constexpr (ACT != kActF16) {
+    float m = 0.0f;
+    bool finite = true;
+    for (int i = lane * 16; i < H; i += kWave * 16) {
+      float v[16];
+      load16(i, v);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        finite = finite && (fabsf(v[j]) <= 3.4028235e38f);
+        m = fmaxf(m, fabsf(v[j]));
+      }
+    }
+#pragma unroll
+    for (int off = kWave / 2; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+    finite = __all(finite);
+    e = finite ? range_exponent(m) : 0;
+  }
+  for (int i = lane * 16; i < H; i += kWave * 16) {
+    float v[16];
+    load16(i, v);
+    uint32_t o[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float lo = v[operand_k(P, 2 * j)], hi = v[operand_k(P, 2 * j + 1)];
+      const _Float16 a = static_cast<_Float16>(ACT == kActF16 ? lo : ldexpf(lo, -e));
+      const _Float16 b = static_cast<_Float16>(ACT == kActF16 ? hi : ldexpf(hi, -e));
+      o[j] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
+             (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
+    }
+    uint4* dst = reinterpret_cast<uint4*>(x16 + t * H + i);
+    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+  }
+  if (ACT != kActF16 && lane == 0) xexp[t] = static_cast<int8_t>(e);
 }
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;

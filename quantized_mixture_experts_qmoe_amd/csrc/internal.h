@@ -85,19 +85,28 @@ enum class Path { kDecode, kSmall, kPrefill };
 // ---- launchers (each returns hipSuccess or the launch error)
 hipError_t launch_route(const Layer& L, const void* logits, int64_t T, char* ws, const Workspace& W,
                         hipStream_t s);
+// One-launch routing of a small batch (with the activation staging when x is
+// not null; *xa and *xexp, when not null, receive FC1's operand rows and
+// exponents), usable while route_small_fits.
+bool route_small_fits(const Layer& L, int64_t T);
+hipError_t launch_route_small(const Layer& L, const void* logits, const void* x, int64_t T, char* ws,
+                              const Workspace& W, hipStream_t s, const uint16_t** xa,
+                              const int8_t** xexp);
 hipError_t launch_prefill(const Layer& L, const void* x, void* out, int64_t T, char* ws,
                           const Workspace& W, hipStream_t s);
-// Staging of FC1's activations (fp16 with a per-token exponent; fp16 inputs
-// pass through) and the routing-weighted combine, shared by the grouped paths.
+// Staging of FC1's activations (fp16 in operand order, with a per-token
+// exponent for bf16/fp32 inputs) and the routing-weighted combine, shared by
+// the grouped paths.
 hipError_t launch_stage_x(const Layer& L, const void* x, int64_t T, char* ws, const Workspace& W,
                           hipStream_t s, const uint16_t** xa, const int8_t** xexp);
 hipError_t launch_combine(const Layer& L, void* out, int64_t T, char* ws, const Workspace& W,
                           hipStream_t s);
-// Small-batch path: grouped GEMMs streaming each expert's weights once.
+// Small-batch path (routing included): grouped GEMMs streaming each
+// expert's weights once.
 bool small_path_supported(const Layer& L);
 hipError_t prepare_small(const Layer& L);
-hipError_t launch_small(const Layer& L, const void* x, void* out, int64_t T, char* ws,
-                        const Workspace& W, hipStream_t s);
+hipError_t launch_small(const Layer& L, const void* x, const void* logits, void* out, int64_t T,
+                        char* ws, const Workspace& W, hipStream_t s);
 hipError_t launch_decode(const Layer& L, const void* x, const void* logits, void* out, int64_t T,
                          char* ws, const Workspace& W, hipStream_t s);
 // Fused single-launch decode (bf16 or fp16 activations, H <= 2048,

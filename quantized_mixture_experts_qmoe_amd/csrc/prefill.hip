@@ -423,11 +423,13 @@ void grouped_gemm_kernel(
               ce[i][c] = h_chunk_exponent(m);
             }
         }
+        // h goes out in operand order, the order FC2's A rows need
+        const int hpos = operand_pos(operand_perm(BITS), l16);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int tn = 0; tn < NH; ++tn)
-            stg_h[(quad * 4 + i) * 72 + tn * 16 + l16] =
+            stg_h[(quad * 4 + i) * 72 + tn * 16 + hpos] =
                 __builtin_bit_cast(uint16_t, static_cast<_Float16>(ldexpf(hv[i][tn], -ce[i][tn / 2])));
         if (l16 == 0) {
 #pragma unroll
@@ -513,61 +515,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
 }
 
-// FC1's activations: each token's row scaled by 2^-e_t and rounded once to
-// fp16, e_t = range_exponent of the row's largest magnitude (0 for a row
-// with a non-finite value); e_t goes to xexp.
-// bf16 rows come through exactly (8 significant bits), fp32 rows are
-// rounded to 11. One wave per token, 8 consecutive values per lane.
-template <int ACT>
+// FC1's activations in operand order (stage_x_row), one wave per token.
+template <int ACT, int P>
 __global__ __launch_bounds__(256) void stage_x_f16_kernel(const void* __restrict__ x, int64_t T, int H,
                                                           uint16_t* __restrict__ x16,
                                                           int8_t* __restrict__ xexp) {
   const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const int lane = threadIdx.x & (kWave - 1);
-  auto load8 = [&](int i, float (&v)[8]) {
-    if constexpr (ACT == kActBF16) {
-      const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + t * H + i);
-      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v[2 * j] = bf16_to_f32(w[j] & 0xFFFFu);
-        v[2 * j + 1] = bf16_to_f32(w[j] >> 16);
-      }
-    } else {
-      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(x) + t * H + i);
-      const float4 a = p[0], b = p[1];
-      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-    }
-  };
-  float m = 0.0f;
-  bool finite = true;
-  for (int i = lane * 8; i < H; i += kWave * 8) {
-    float v[8];
-    load8(i, v);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      finite = finite && (fabsf(v[j]) <= 3.4028235e38f);
-      m = fmaxf(m, fabsf(v[j]));
-    }
-  }
-#pragma unroll
-  for (int off = kWave / 2; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
-  finite = __all(finite);
-  const int e = finite ? range_exponent(m) : 0;
-  for (int i = lane * 8; i < H; i += kWave * 8) {
-    float v[8];
-    load8(i, v);
-    uint32_t o[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      o[j] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(ldexpf(v[2 * j], -e)))) |
-             (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(ldexpf(v[2 * j + 1], -e))))
-              << 16);
-    *reinterpret_cast<uint4*>(x16 + t * H + i) = make_uint4(o[0], o[1], o[2], o[3]);
-  }
-  if (lane == 0) xexp[t] = static_cast<int8_t>(e);
+  stage_x_row<ACT, P>(x, t, H, x16, xexp, threadIdx.x & (kWave - 1));
 }
 
 // Between the GEMMs: each route's h chunks brought to the route's largest
@@ -656,18 +611,31 @@ hipError_t launch_gemms(const Layer& L, const uint16_t* xa, const int8_t* xexp, 
 
 hipError_t launch_stage_x(const Layer& L, const void* x, int64_t T, char* ws, const Workspace& W,
                           hipStream_t s, const uint16_t** xa, const int8_t** xexp) {
-  // fp16 activations go to the matrix cores as they are; bf16 and fp32
-  // ones are staged as fp16 with a per-token exponent
+  // the matrix operands hold K values in operand order; fp16 activations of
+  // a layer whose order is K order go to the matrix cores as they are
+  const int P = operand_perm(L.bits);
   *xa = static_cast<const uint16_t*>(x);
   *xexp = nullptr;
-  if (L.act == kActF16) return hipSuccess;
+  if (L.act == kActF16 && P == 0) return hipSuccess;
   uint16_t* staged = reinterpret_cast<uint16_t*>(ws + W.x16);
-  int8_t* e = reinterpret_cast<int8_t*>(ws + W.xexp);
+  int8_t* e = L.act == kActF16 ? nullptr : reinterpret_cast<int8_t*>(ws + W.xexp);
   const unsigned grid = static_cast<unsigned>((T + 3) / 4);
-  if (L.act == kActBF16)
-    stage_x_f16_kernel<kActBF16><<<grid, 256, 0, s>>>(x, T, static_cast<int>(L.H), staged, e);
+  const int H = static_cast<int>(L.H);
+  auto go = [&](auto pc) {
+    constexpr int PP = decltype(pc)::value;
+    if (L.act == kActBF16)
+      stage_x_f16_kernel<kActBF16, PP><<<grid, 256, 0, s>>>(x, T, H, staged, e);
+    else if (L.act == kActF16)
+      stage_x_f16_kernel<kActF16, PP><<<grid, 256, 0, s>>>(x, T, H, staged, e);
+    else
+      stage_x_f16_kernel<kActF32, PP><<<grid, 256, 0, s>>>(x, T, H, staged, e);
+  };
+  if (P == 8)
+    go(std::integral_constant<int, 8>{});
+  else if (P == 16)
+    go(std::integral_constant<int, 16>{});
   else
-    stage_x_f16_kernel<kActF32><<<grid, 256, 0, s>>>(x, T, static_cast<int>(L.H), staged, e);
+    go(std::integral_constant<int, 0>{});
   stage_done(L, 5, "stage_x_f16");
   *xa = staged;
   *xexp = e;

@@ -9,6 +9,8 @@
 // the grouped-GEMM input the tensor-core prefill path consumes ("[CUDA] Add
 // INT4 and INT3 QMoE CPU/GPU offload support", Description of #33731:
 // sorted_routes, tile descriptors, expert_first_token_offset).
+#include <utility>
+
 #include "device.h"
 #include "internal.h"
 
@@ -208,6 +210,173 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(const int32_t* __res
     sorted_routes[pos] = static_cast<int32_t>(r0 + i);
     inv_pos[r0 + i] = pos;
   }
+}
+
+// Routing of a small batch in one launch, together with the activation
+// staging. Workgroup 0 (16 waves) routes every token: top-k + softmax (wave
+// w takes tokens w, w + 16, ...), then, over the route list in chunks of 64
+// routes, each route's rank among the earlier routes of its chunk with the
+// same expert and the per-(chunk, expert) counts, a per-expert scan over the
+// chunks, the expert offsets and the tile list (tiles of tile_m routes), and
+// the stable scatter. Workgroups 1.. stage the activations, one token per
+// wave (stage_x_row). Used while the route list and the (chunk, expert)
+// table fit in LDS (route_small_fits).
+constexpr int kSmallRouteMax = 4096;        // routes of one call
+constexpr int kSmallRouteTable = 8192;      // (64-route chunk, expert) counters
+
+bool route_small_fits(const Layer& L, int64_t T) {
+  const int64_t R = T * L.k;
+  return R <= kSmallRouteMax && ((R + 63) / 64) * L.E <= kSmallRouteTable;
+}
+
+template <int SLOTS, typename LG, int ACT, int P>
+__global__ __launch_bounds__(1024) void route_small_kernel(
+    const LG* __restrict__ logits, int64_t T, int E, int k, bool normalize, int tile_m,
+    int32_t* __restrict__ topk_id, float* __restrict__ topk_w, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_routes, int32_t* __restrict__ inv_pos,
+    int4* __restrict__ tiles, int32_t* __restrict__ num_tiles, const void* __restrict__ x, int H,
+    uint16_t* __restrict__ x16, int8_t* __restrict__ xexp) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6, tid = threadIdx.x;
+  if (blockIdx.x > 0) {
+    const int64_t t = static_cast<int64_t>(blockIdx.x - 1) * 16 + wave;
+    if (t < T) stage_x_row<ACT, P>(x, t, H, x16, xexp, lane);
+    return;
+  }
+  __shared__ int32_t s_id[kSmallRouteMax];
+  __shared__ uint8_t s_rank[kSmallRouteMax];
+  __shared__ int32_t s_tab[kSmallRouteTable];
+  __shared__ int32_t s_scan[1024];
+  __shared__ int32_t s_tiles[1024];
+  const int R = static_cast<int>(T) * k;
+  const int nch = (R + 63) / 64;
+  for (int i = tid; i < nch * E; i += 1024) s_tab[i] = 0;
+  // top-k + softmax, one token per wave at a time
+  for (int64_t t = wave; t < T; t += 16) {
+    int id;
+    float wt;
+    if constexpr (SLOTS > 0) {
+      uint16_t lg[SLOTS];
+#pragma unroll
+      for (int c = 0; c < SLOTS; ++c) {
+        const int e = lane + kWave * c;
+        lg[c] = reinterpret_cast<const uint16_t*>(logits)[t * E + (e < E ? e : 0)];
+      }
+      topk_softmax_bf16_wave<SLOTS>(lg, E, k, normalize, lane, id, wt);
+    } else {
+      topk_softmax_wave_r(logits + t * E, E, k, normalize, lane, id, wt);
+    }
+    if (lane < k) {
+      topk_id[t * k + lane] = id;
+      topk_w[t * k + lane] = wt;
+      s_id[t * k + lane] = id;
+    }
+  }
+  __syncthreads();
+  // per chunk of 64 routes: each route's rank among the chunk's earlier
+  // routes with its expert, and the chunk's count per expert (written by
+  // the expert's last route in the chunk)
+  for (int c = wave; c < nch; c += 16) {
+    const int r = 64 * c + lane;
+    const int e = r < R ? s_id[r] : -1;
+    int rank = 0;
+    bool later = false;
+    for (int j = 0; j < kWave; ++j) {
+      const int ej = __shfl(e, j, kWave);
+      rank += (j < lane && ej == e) ? 1 : 0;
+      later = later || (j > lane && ej == e);
+    }
+    if (r < R) {
+      s_rank[r] = static_cast<uint8_t>(rank);
+      if (!later) s_tab[c * E + e] = rank + 1;
+    }
+  }
+  __syncthreads();
+  // per expert: exclusive bases of the chunks, the total, its tile count
+  if (tid < E) {
+    int32_t run = 0;
+    for (int c = 0; c < nch; ++c) {
+      const int32_t v = s_tab[c * E + tid];
+      s_tab[c * E + tid] = run;
+      run += v;
+    }
+    counts[tid] = run;
+    s_scan[tid] = run;
+    s_tiles[tid] = (run + tile_m - 1) / tile_m;
+  }
+  __syncthreads();
+  block_scan_inclusive(s_scan, E);
+  block_scan_inclusive(s_tiles, E);
+  if (tid < E) {
+    offsets[tid + 1] = s_scan[tid];
+    if (tid == 0) offsets[0] = 0;
+    const int32_t start = tid == 0 ? 0 : s_scan[tid - 1];
+    const int32_t cnt = s_scan[tid] - start;
+    const int32_t t0 = tid == 0 ? 0 : s_tiles[tid - 1];
+    for (int32_t i = 0; i * tile_m < cnt; ++i)
+      tiles[t0 + i] = make_int4(tid, start + i * tile_m, min(tile_m, cnt - i * tile_m), 0);
+  }
+  if (tid == 0) num_tiles[0] = s_tiles[E - 1];
+  // stable scatter
+  for (int r = tid; r < R; r += 1024) {
+    const int e = s_id[r];
+    const int32_t pos = (e == 0 ? 0 : s_scan[e - 1]) + s_tab[(r >> 6) * E + e] + s_rank[r];
+    sorted_routes[pos] = r;
+    inv_pos[r] = pos;
+  }
+}
+
+hipError_t launch_route_small(const Layer& L, const void* logits, const void* x, int64_t T, char* ws,
+                              const Workspace& W, hipStream_t s, const uint16_t** xa,
+                              const int8_t** xexp) {
+  const int E = static_cast<int>(L.E), k = L.k, H = static_cast<int>(L.H);
+  const int P = operand_perm(L.bits);
+  const bool stage = x != nullptr && (L.act != kActF16 || P != 0);
+  uint16_t* x16 = stage ? reinterpret_cast<uint16_t*>(ws + W.x16) : nullptr;
+  int8_t* xe = L.act != kActF16 ? reinterpret_cast<int8_t*>(ws + W.xexp) : nullptr;
+  if (xa) *xa = stage ? x16 : static_cast<const uint16_t*>(x);
+  if (xexp) *xexp = stage ? xe : nullptr;
+  const unsigned grid = 1 + (stage ? static_cast<unsigned>((T + 15) / 16) : 0u);
+  int32_t* topk_id = reinterpret_cast<int32_t*>(ws + W.topk_id);
+  float* topk_w = reinterpret_cast<float*>(ws + W.topk_w);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + W.counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + W.offsets);
+  int32_t* srt = reinterpret_cast<int32_t*>(ws + W.sorted_routes);
+  int32_t* inv = reinterpret_cast<int32_t*>(ws + W.inv_pos);
+  int4* tiles = reinterpret_cast<int4*>(ws + W.tiles);
+  int32_t* ntiles = reinterpret_cast<int32_t*>(ws + W.num_tiles);
+  auto go = [&](auto slots, auto lgt, auto actc, auto pc) {
+    constexpr int SL = decltype(slots)::value, AC = decltype(actc)::value, PP = decltype(pc)::value;
+    using LT = typename decltype(lgt)::type;
+    route_small_kernel<SL, LT, AC, PP><<<grid, 1024, 0, s>>>(
+        static_cast<const LT*>(logits), T, E, k, L.normalize, W.tile_m, topk_id, topk_w, counts, offsets,
+        srt, inv, tiles, ntiles, x, H, x16, xe);
+  };
+  auto with_perm = [&](auto slots, auto lgt, auto actc) {
+    if (P == 8)
+      go(slots, lgt, actc, std::integral_constant<int, 8>{});
+    else if (P == 16)
+      go(slots, lgt, actc, std::integral_constant<int, 16>{});
+    else
+      go(slots, lgt, actc, std::integral_constant<int, 0>{});
+  };
+  using I0 = std::integral_constant<int, 0>;
+  if (L.act_bf16) {
+    using A = std::integral_constant<int, kActBF16>;
+    struct U16 { using type = uint16_t; };
+    if (E <= 64) with_perm(std::integral_constant<int, 1>{}, U16{}, A{});
+    else if (E <= 128) with_perm(std::integral_constant<int, 2>{}, U16{}, A{});
+    else if (E <= 256) with_perm(std::integral_constant<int, 4>{}, U16{}, A{});
+    else if (E <= 512) with_perm(std::integral_constant<int, 8>{}, U16{}, A{});
+    else with_perm(std::integral_constant<int, 16>{}, U16{}, A{});
+  } else if (L.act == kActF16) {
+    struct F16 { using type = _Float16; };
+    with_perm(I0{}, F16{}, std::integral_constant<int, kActF16>{});
+  } else {
+    struct F32 { using type = float; };
+    with_perm(I0{}, F32{}, std::integral_constant<int, kActF32>{});
+  }
+  stage_done(L, 1, "route_small");
+  return hipGetLastError();
 }
 
 hipError_t launch_route(const Layer& L, const void* logits, int64_t T, char* ws, const Workspace& W,

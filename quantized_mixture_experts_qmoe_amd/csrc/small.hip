@@ -7,8 +7,9 @@
 // expert's weights are read once per call and go from registers to the
 // matrix cores.
 //
-// Routing is the prefill path's (top-k, histogram, scan, stable scatter)
-// with tiles of at most 16 routes of one expert. Each workgroup (8 waves)
+// Routing (top-k, histogram, scan, stable scatter) and the activation
+// staging run in one launch while the route list fits in LDS (else the
+// prefill path's launches), with tiles of at most 16 routes of one expert. Each workgroup (8 waves)
 // takes one tile and a block of output columns:
 //   FC1: the tile's activation rows (fp16, staged per token as for the
 //        prefill GEMMs) go to LDS once; each wave owns 16 h columns, streams
@@ -225,10 +226,24 @@ __global__ __launch_bounds__(kSmallThreads) void small_fc2_kernel(
 #pragma unroll
     for (int off = kWave / 2; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
     const int ex = __all(finite) ? range_exponent(m) : 0;
-    for (int c = 2 * lane; c < I; c += 2 * kWave) {
-      const float2 v = *reinterpret_cast<const float2*>(hr + c);
-      const f16x2_t hv = {static_cast<_Float16>(ldexpf(v.x, -ex)), static_cast<_Float16>(ldexpf(v.y, -ex))};
-      *reinterpret_cast<f16x2_t*>(smem + r * ld + swz(r, c >> 3) + (c & 7)) = hv;
+    // 16 values per lane, placed in operand order
+    constexpr int P = operand_perm(BITS);
+    for (int c = 16 * lane; c < I; c += 16 * kWave) {
+      float v[16];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 f = *reinterpret_cast<const float4*>(hr + c + 4 * q4);
+        v[4 * q4] = f.x; v[4 * q4 + 1] = f.y; v[4 * q4 + 2] = f.z; v[4 * q4 + 3] = f.w;
+      }
+      uint32_t o[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const f16x2_t hv = {static_cast<_Float16>(ldexpf(v[operand_k(P, 2 * j)], -ex)),
+                            static_cast<_Float16>(ldexpf(v[operand_k(P, 2 * j + 1)], -ex))};
+        o[j] = __builtin_bit_cast(uint32_t, hv);
+      }
+      *reinterpret_cast<uint4*>(smem + r * ld + swz(r, c >> 3)) = make_uint4(o[0], o[1], o[2], o[3]);
+      *reinterpret_cast<uint4*>(smem + r * ld + swz(r, (c >> 3) + 1)) = make_uint4(o[4], o[5], o[6], o[7]);
     }
     if (lane == 0) s_exp[r] = ex;
   }
@@ -353,11 +368,17 @@ hipError_t prepare_small(const Layer& L) {
   return hipSuccess;
 }
 
-hipError_t launch_small(const Layer& L, const void* x, void* out, int64_t T, char* ws,
-                        const Workspace& W, hipStream_t s) {
+hipError_t launch_small(const Layer& L, const void* x, const void* logits, void* out, int64_t T,
+                        char* ws, const Workspace& W, hipStream_t s) {
   const uint16_t* xa = nullptr;
   const int8_t* xexp = nullptr;
-  hipError_t err = launch_stage_x(L, x, T, ws, W, s, &xa, &xexp);
+  hipError_t err;
+  if (route_small_fits(L, T)) {
+    err = launch_route_small(L, logits, x, T, ws, W, s, &xa, &xexp);
+  } else {
+    err = launch_route(L, logits, T, ws, W, s);
+    if (err == hipSuccess) err = launch_stage_x(L, x, T, ws, W, s, &xa, &xexp);
+  }
   if (err != hipSuccess) return err;
   switch (L.bits) {
     case 4: err = launch_small_gemms<4>(L, xa, xexp, ws, W, s); break;

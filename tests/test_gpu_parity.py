@@ -142,13 +142,43 @@ def check_routing(wl, layer):
 
 
 @pytest.mark.parametrize("name,T", [("tiny", 4), ("decode", 1), ("decode", 4), ("prefill", 8192),
-                                    ("int3", 2048), ("stack", 32768), ("prefill", 777)])
+                                    ("int3", 2048), ("stack", 32768), ("prefill", 777),
+                                    ("decode", 13), ("decode", 32), ("prefill", 256), ("stack", 100)])
 def test_routing_bit_exact(name, T):
+    """qmoe_route runs the routing a forward of T tokens would run: the
+    chunked launches of the grouped GEMMs, or (13 to 256 tokens here) the
+    small-batch path's one-launch routing."""
     say(f"routing {name} T={T}")
     wl = qi.make_workload(name, T=T)
     layer = layer_for(wl, max(T, 8))
     counts = check_routing(wl, layer)
     assert counts.sum() == T * wl.spec.top_k
+
+
+@pytest.mark.parametrize("kw,T", [
+    (dict(act="f16"), 40), (dict(act="f32"), 8), (dict(num_experts=1024, top_k=8), 40),
+    (dict(num_experts=1024, top_k=8), 100), (dict(num_experts=128, top_k=32), 100),
+    (dict(num_experts=64, top_k=1), 256), (dict(num_experts=300, top_k=5), 77)])
+def test_small_routing_bit_exact(kw, T):
+    """The small-batch path's one-launch routing (and, where the route list
+    outgrows it, E = 1024 at 100 tokens, the chunked routing) for fp16 and
+    fp32 logits, up to 1024 experts and top-32: ids, offsets, sorted routes
+    and inverse positions bit-exact, weights within 4 ulp; the layer's output
+    matches the oracle on sampled rows."""
+    d = dict(num_experts=8, top_k=2)
+    d.update(kw)
+    act = d.pop("act", "bf16")
+    spec = small_spec(4, 32, act=act, **d)
+    wl = qi.make_layer(spec, T=T, seed=1000 + T + spec.num_experts + spec.top_k)
+    say(f"small routing E={spec.num_experts} k={spec.top_k} act={act} T={T}")
+    with _env(QMOE_FORCE_PATH="small"):
+        layer = layer_for(wl, 256)
+    check_routing(wl, layer)
+    rows = sample_rows(T, 12, seed=T)
+    out, _ = run(layer, wl.tokens.x, wl.tokens.logits)
+    rep = compare(out[torch.as_tensor(rows, device=DEV)], oracle_acc(wl, rows))
+    say(f"  output on {len(rows)} rows: {rep}")
+    assert rep.ok, rep
 
 
 def test_routing_constructed_ties():
