@@ -189,7 +189,7 @@ qmoe_status qmoe_workspace_size(const qmoe_handle *handle, int64_t num_tokens, s
  * Dispatch:
  *  - 1..4 tokens: the fused single-launch decode where it applies (see
  *    qmoe_create), else the split decode (three launches);
- *  - 5..12 tokens on layers the fused decode serves: the fused decode once
+ *  - 5..8 tokens on layers the fused decode serves: the fused decode once
  *    per group of up to four tokens;
  *  - up to 256 tokens: routing, then the small-batch GEMMs (each active
  *    expert's weights streamed once per call into the fp16 matrix cores for

@@ -23,12 +23,13 @@
 //        wave owns 32 output columns; the epilogue stores y in fp32 [R, H],
 //        which the prefill path's combine sums per token in slot order and
 //        rounds once.
-// Lane (q, n) of a wave (q = lane / 16, n = lane % 16) loads, for each block
-// of 128 K values, unit 4j + q of its weight row (32 codes, 16 B for INT4):
-// its 32 values are the B operand of the block's four MFMA steps, K values
-// 32(4j + q) + 8t + 0..7 at step t, and the A operand of step t is read from
-// the same K range of the staged rows. So every weight byte is loaded once,
-// by one lane, in 64-byte row segments.
+// Lane (q, n) of a wave (q = lane / 16, n = lane % 16) feeds the matrix
+// cores, for each 128-K sub-block, unit 4s + q (32 codes) of weight row n:
+// its 32 values are the B operand of the sub-block's four MFMA steps, K
+// values 32(4s + q) + 8t + 0..7 at step t, and the A operand of step t is
+// read from the same K range of the staged rows. The weights are loaded in
+// whole row segments (RowBlockStream) and handed to that layout across
+// lanes, so every weight byte is loaded once per call, by one lane.
 //
 // Semantics: grouped experts over expert-sorted routes ("[CUDA] Add INT4 and
 // INT3 QMoE CPU/GPU offload support", Description of the grouped prefill
@@ -51,7 +52,7 @@ constexpr int kSmallWaves = 8;
 constexpr int kSmallThreads = kSmallWaves * kWave;
 constexpr int kFc1Cols = kSmallWaves * 16;   // h columns per FC1 workgroup
 constexpr int kFc2Cols = kSmallWaves * 32;   // output columns per FC2 workgroup
-constexpr int kDepth = 4;                    // 128-K blocks of weights in flight per wave
+constexpr int kDepthB = 2;                   // row blocks of weights in flight per wave
 
 // Logical index of this workgroup: the column blocks of one tile (which
 // share its staged rows) are dealt to one XCD.
@@ -64,19 +65,88 @@ __device__ __forceinline__ int small_logical(int active) {
   return L < active ? L : -1;
 }
 
-// One weight row's view for the streaming loop.
+// Sixteen weight rows (row n of the group is the MFMA column of the lanes
+// with l16 = n), streamed in blocks of UB units per row. Each load
+// instruction reads UB consecutive units (128 bytes for INT4 and INT2, 96
+// for INT3) of each of RPI rows: lane l loads unit (l mod UB) of row
+// RPI * m + l / UB in instruction m. Rows read in such whole segments keep
+// HBM streaming at full rate, where 64-byte pieces of 16 rows at a time
+// fall to about two thirds of it. ds_bpermute then hands lane (q, n) the
+// unit 4s + q of its own row n for each 128-K sub-block s, the layout the
+// matrix cores' B operand takes. Units past K get a zero scale (their
+// addresses are clamped to the row's first unit).
 template <int BITS, bool HAS_ZP>
-struct RowStream {
+struct RowBlockStream {
+  static constexpr int UB = BITS == 2 ? 16 : 8;   // units per row per block
+  static constexpr int RPI = kWave / UB;          // rows per load instruction
+  static constexpr int NI = 16 / RPI;             // load instructions per block
+  static constexpr int SB = UB / 4;               // 128-K sub-blocks per block
+  struct Block {
+    UnitWords<BITS> raw[NI];
+    uint32_t s[SB];
+    int z[SB];
+  };
+  const uint8_t* row_ld[NI];   // row this lane loads in instruction m
+  const uint16_t* srow;        // this lane's own row: scales
+  const uint8_t* zrow;         // and zero points
+  int zp, ushift, nunits, lu, q, msel;
+  int src[SB];                 // ds_bpermute byte address per sub-block
+
+  // rows(r) = pointers to row r (0..15) of the group: codes, scales, zero points
+  template <typename RowFn>
+  __device__ __forceinline__ void init(RowFn rows, int lane, int zp_, int ushift_, int nunits_) {
+    zp = zp_;
+    ushift = ushift_;
+    nunits = nunits_;
+    lu = lane % UB;
+    q = lane >> 4;
+    const int n = lane & 15;
+#pragma unroll
+    for (int m = 0; m < NI; ++m) row_ld[m] = rows(RPI * m + lane / UB).codes;
+    const auto own = rows(n);
+    srow = own.scales;
+    zrow = own.zps;
+    msel = n / RPI;
+#pragma unroll
+    for (int sb = 0; sb < SB; ++sb) src[sb] = 4 * ((n % RPI) * UB + 4 * sb + q);
+  }
+
+  __device__ __forceinline__ void load(int b, Block& blk) const {
+    const int u = b * UB + lu;
+    const int uc = u < nunits ? u : 0;
+#pragma unroll
+    for (int m = 0; m < NI; ++m) blk.raw[m] = load_unit<BITS>(row_ld[m] + uc * (4 * BITS));
+#pragma unroll
+    for (int sb = 0; sb < SB; ++sb) {
+      const int v = b * UB + 4 * sb + q;
+      const int vc = v < nunits ? v : 0;
+      blk.s[sb] = v < nunits ? srow[vc >> ushift] : 0u;   // a unit past K weighs zero
+      blk.z[sb] = HAS_ZP ? zrow[vc >> ushift] : zp;
+    }
+  }
+
+  // unit 4 * sb + q of this lane's row, from the lanes that loaded it
+  __device__ __forceinline__ UnitWords<BITS> unit(const Block& blk, int sb) const {
+    UnitWords<BITS> w;
+#pragma unroll
+    for (int d = 0; d < BITS; ++d) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int m = 0; m < NI; ++m) {
+        const uint32_t t = static_cast<uint32_t>(
+            __builtin_amdgcn_ds_bpermute(src[sb], static_cast<int>(blk.raw[m].w[d])));
+        v = msel == m ? t : v;
+      }
+      w.w[d] = v;
+    }
+    return w;
+  }
+};
+
+struct RowPtrs {
   const uint8_t* codes;
   const uint16_t* scales;
   const uint8_t* zps;
-  int zp, ushift, nunits;   // ushift: log2(block / 32); nunits = K / 32
-  __device__ __forceinline__ void load(int u, UnitWords<BITS>& w, uint32_t& s, int& z) const {
-    const int uc = u < nunits ? u : 0;
-    w = load_unit<BITS>(codes + uc * (4 * BITS));
-    s = u < nunits ? scales[uc >> ushift] : 0u;   // a unit past K weighs zero
-    z = HAS_ZP ? zps[uc >> ushift] : zp;
-  }
 };
 
 // Staged rows are K fp16 values each, in 16-byte pieces: piece c of row r
@@ -122,7 +192,34 @@ __global__ __launch_bounds__(kSmallThreads) void small_fc1_kernel(
   const int q = lane >> 4, l16 = lane & 15;
   const int ld = H;
 
-  // stage the tile's activation rows (and their exponents)
+  // this lane's h column n; the wave's gate rows and up rows stream as two
+  // groups of 16
+  const int n = nb * kFc1Cols + wave * 16 + l16;
+  const int64_t ebase = static_cast<int64_t>(e) * 2 * I;
+  const int nunits = H / 32;
+  using Stream = RowBlockStream<BITS, HAS_ZP>;
+  Stream sg, su;
+  auto rows_of = [&](bool up) {
+    return [=](int r) {
+      const int c0 = nb * kFc1Cols + wave * 16 + r;
+      const int c = c0 < I ? c0 : 0;
+      const int64_t row = ebase + (fc1_il ? 2 * c + (up ? 1 : 0) : (up ? I + c : c));
+      return RowPtrs{codes + row * row_bytes, scales + row * nblk, HAS_ZP ? zps + row * nblk : nullptr};
+    };
+  };
+  sg.init(rows_of(false), lane, zp, ushift, nunits);
+  su.init(rows_of(true), lane, zp, ushift, nunits);
+  const int nbk = (nunits + Stream::UB - 1) / Stream::UB;
+
+  typename Stream::Block kg[kDepthB], ku[kDepthB];
+#pragma unroll
+  for (int d = 0; d < kDepthB; ++d) {
+    sg.load(d, kg[d]);
+    su.load(d, ku[d]);
+  }
+
+  // stage the tile's activation rows (and their exponents) while the first
+  // blocks' loads are in flight
   const int upr = H / 8;   // 16-byte pieces per row
   for (int i = threadIdx.x; i < nrows * upr; i += kSmallThreads) {
     const int r = i / upr, c = i % upr;
@@ -135,43 +232,29 @@ __global__ __launch_bounds__(kSmallThreads) void small_fc1_kernel(
     s_exp[r] = (xexp != nullptr && r < nrows) ? xexp[sorted_routes[row0 + r] / k] : 0;
   }
 
-  // this lane's weight rows: gate and up rows of h column n
-  const int n = nb * kFc1Cols + wave * 16 + l16;
-  const int nc = n < I ? n : 0;
-  const int gr = fc1_il ? 2 * nc : nc, ur = fc1_il ? 2 * nc + 1 : I + nc;
-  const int64_t ebase = static_cast<int64_t>(e) * 2 * I;
-  const int nunits = H / 32;
-  RowStream<BITS, HAS_ZP> g{codes + (ebase + gr) * row_bytes, scales + (ebase + gr) * nblk,
-                            HAS_ZP ? zps + (ebase + gr) * nblk : nullptr, zp, ushift, nunits};
-  RowStream<BITS, HAS_ZP> u{codes + (ebase + ur) * row_bytes, scales + (ebase + ur) * nblk,
-                            HAS_ZP ? zps + (ebase + ur) * nblk : nullptr, zp, ushift, nunits};
-  const int nj = (nunits + 3) / 4;
-
-  UnitWords<BITS> wg[kDepth], wu[kDepth];
-  uint32_t sg[kDepth], su[kDepth];
-  int zg[kDepth], zu[kDepth];
-#pragma unroll
-  for (int d = 0; d < kDepth; ++d) {
-    g.load(4 * d + q, wg[d], sg[d], zg[d]);
-    u.load(4 * d + q, wu[d], su[d], zu[d]);
-  }
   __syncthreads();
 
   sf32x4_t accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
   const uint16_t* arow = smem + l16 * ld;
-  for (int j0 = 0; j0 < nj; j0 += kDepth) {
+  for (int b0 = 0; b0 < nbk; b0 += kDepthB) {
 #pragma unroll
-    for (int d = 0; d < kDepth; ++d) {
-      const int j = j0 + d;
-      if (j < nj) {
-        uint32_t pg[16], pu[16];
-        dequant_unit_f16<BITS>(wg[d], sg[d], zg[d], pg);
-        dequant_unit_f16<BITS>(wu[d], su[d], zu[d], pu);
-        const int col0 = 128 * j + 32 * q;
-        accg = mfma_unit(arow, l16, col0, pg, accg);
-        accu = mfma_unit(arow, l16, col0, pu, accu);
-        g.load(4 * (j + kDepth) + q, wg[d], sg[d], zg[d]);
-        u.load(4 * (j + kDepth) + q, wu[d], su[d], zu[d]);
+    for (int d = 0; d < kDepthB; ++d) {
+      const int bk = b0 + d;
+      if (bk < nbk) {
+#pragma unroll
+        for (int sb = 0; sb < Stream::SB; ++sb) {
+          // K is a multiple of 128, so a sub-block lies wholly inside or
+          // wholly past it; one past it has no staged A columns to read
+          if (bk * Stream::UB + 4 * sb >= nunits) break;
+          uint32_t pg[16], pu[16];
+          dequant_unit_f16<BITS>(sg.unit(kg[d], sb), kg[d].s[sb], kg[d].z[sb], pg);
+          dequant_unit_f16<BITS>(su.unit(ku[d], sb), ku[d].s[sb], ku[d].z[sb], pu);
+          const int col0 = 32 * (bk * Stream::UB + 4 * sb + q);
+          accg = mfma_unit(arow, l16, col0, pg, accg);
+          accu = mfma_unit(arow, l16, col0, pu, accu);
+        }
+        sg.load(bk + kDepthB, kg[d]);
+        su.load(bk + kDepthB, ku[d]);
       }
     }
   }
@@ -211,7 +294,31 @@ __global__ __launch_bounds__(kSmallThreads) void small_fc2_kernel(
   const int q = lane >> 4, l16 = lane & 15;
   const int ld = I;
 
-  // stage h rows as fp16 with the row's range exponent; wave w takes rows
+  const int nunits = I / 32;
+  const int64_t ebase = static_cast<int64_t>(e) * H;
+  using Stream = RowBlockStream<BITS, HAS_ZP>;
+  int cols[2];
+  Stream w2[2];
+#pragma unroll
+  for (int sidx = 0; sidx < 2; ++sidx) {
+    cols[sidx] = nb * kFc2Cols + wave * 32 + 16 * sidx + l16;
+    w2[sidx].init(
+        [=](int r) {
+          const int c0 = nb * kFc2Cols + wave * 32 + 16 * sidx + r;
+          const int64_t row = ebase + (c0 < H ? c0 : 0);
+          return RowPtrs{codes + row * row_bytes, scales + row * nblk, HAS_ZP ? zps + row * nblk : nullptr};
+        },
+        lane, zp, ushift, nunits);
+  }
+  const int nbk = (nunits + Stream::UB - 1) / Stream::UB;
+  typename Stream::Block bv[2][kDepthB];
+#pragma unroll
+  for (int d = 0; d < kDepthB; ++d)
+#pragma unroll
+    for (int sidx = 0; sidx < 2; ++sidx) w2[sidx].load(d, bv[sidx][d]);
+
+  // stage h rows as fp16 with the row's range exponent (while the first
+  // blocks' loads are in flight); wave w takes rows
   // w and w + 8 (rows past the tile are left unset: no stored output reads
   // them, since row m of a product depends on row m of A only)
   for (int r = wave; r < nrows; r += kSmallWaves) {
@@ -248,42 +355,25 @@ __global__ __launch_bounds__(kSmallThreads) void small_fc2_kernel(
     if (lane == 0) s_exp[r] = ex;
   }
 
-  const int nunits = I / 32;
-  const int nj = (nunits + 3) / 4;
-  const int64_t ebase = static_cast<int64_t>(e) * H;
-  int cols[2];
-  RowStream<BITS, HAS_ZP> w2[2];
-#pragma unroll
-  for (int sidx = 0; sidx < 2; ++sidx) {
-    cols[sidx] = nb * kFc2Cols + wave * 32 + 16 * sidx + l16;
-    const int mc = cols[sidx] < H ? cols[sidx] : 0;
-    w2[sidx] = RowStream<BITS, HAS_ZP>{codes + (ebase + mc) * row_bytes, scales + (ebase + mc) * nblk,
-                                       HAS_ZP ? zps + (ebase + mc) * nblk : nullptr, zp, ushift,
-                                       nunits};
-  }
-  UnitWords<BITS> wv[2][kDepth];
-  uint32_t sv[2][kDepth];
-  int zv[2][kDepth];
-#pragma unroll
-  for (int d = 0; d < kDepth; ++d)
-#pragma unroll
-    for (int sidx = 0; sidx < 2; ++sidx) w2[sidx].load(4 * d + q, wv[sidx][d], sv[sidx][d], zv[sidx][d]);
   __syncthreads();
 
   sf32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   const uint16_t* arow = smem + l16 * ld;
-  for (int j0 = 0; j0 < nj; j0 += kDepth) {
+  for (int b0 = 0; b0 < nbk; b0 += kDepthB) {
 #pragma unroll
-    for (int d = 0; d < kDepth; ++d) {
-      const int j = j0 + d;
-      if (j < nj) {
-        const int col0 = 128 * j + 32 * q;
+    for (int d = 0; d < kDepthB; ++d) {
+      const int bk = b0 + d;
+      if (bk < nbk) {
 #pragma unroll
         for (int sidx = 0; sidx < 2; ++sidx) {
-          uint32_t p[16];
-          dequant_unit_f16<BITS>(wv[sidx][d], sv[sidx][d], zv[sidx][d], p);
-          acc[sidx] = mfma_unit(arow, l16, col0, p, acc[sidx]);
-          w2[sidx].load(4 * (j + kDepth) + q, wv[sidx][d], sv[sidx][d], zv[sidx][d]);
+#pragma unroll
+          for (int sb = 0; sb < Stream::SB; ++sb) {
+            if (bk * Stream::UB + 4 * sb >= nunits) break;   // past K (K % 128 == 0)
+            uint32_t p[16];
+            dequant_unit_f16<BITS>(w2[sidx].unit(bv[sidx][d], sb), bv[sidx][d].s[sb], bv[sidx][d].z[sb], p);
+            acc[sidx] = mfma_unit(arow, l16, 32 * (bk * Stream::UB + 4 * sb + q), p, acc[sidx]);
+          }
+          w2[sidx].load(bk + kDepthB, bv[sidx][d]);
         }
       }
     }

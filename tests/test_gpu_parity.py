@@ -576,7 +576,7 @@ def test_grouped_decode_parity(name, T):
 def test_speculative_decode_shape(T, k):
     """Eight draft tokens with top-10 routing (80 routes), the speculative
     decode shape the pages measure, and the largest top-k (16): on the grouped
-    fused decode (the default up to 12 tokens) and on the small-batch path,
+    fused decode (the default up to 8 tokens) and on the small-batch path,
     the routing is bit-exact and the output matches the oracle (and the
     small-batch path the fp16-datapath emulation)."""
     spec = qi.spec_with(qi.QWEN3_INT4, top_k=k)
@@ -931,18 +931,18 @@ def small_layer(wl, max_tokens, **kw):
                                     ("decode", 64), ("decode", 128), ("int3", 40), ("stack", 64),
                                     ("prefill", 100)])
 def test_small_path_parity(name, T):
-    """The small-batch path (the default from 13 to 256 tokens; forced here for
+    """The small-batch path (the default from 9 to 256 tokens; forced here for
     every size): routing bit-exact, every row against the plain oracle (4x
     margin) and per element against the fp16-datapath emulation."""
     wl = qi.make_workload(name, T=T)
     check_prefill(wl, small_layer(wl, max(T, 8)), emulation=True)
 
 
-@pytest.mark.parametrize("T,path", [(4, "decode"), (12, "decode"), (13, "small"), (256, "small"),
+@pytest.mark.parametrize("T,path", [(4, "decode"), (8, "decode"), (9, "small"), (256, "small"),
                                     (257, "prefill")])
 def test_default_dispatch(T, path):
     """The default dispatch of the Qwen3-shaped bf16 layer: the fused decode up
-    to 12 tokens (groups of four above four), the small-batch path up to 256,
+    to 8 tokens (groups of four above four), the small-batch path up to 256,
     the grouped GEMMs above; each call's stage names show the path taken, and
     the output matches the oracle on sampled rows."""
     wl = qi.make_workload("decode", T=T)
