@@ -64,17 +64,25 @@ import quantized_mixture_experts_qmoe_amd as q  # noqa: E402
 
 METRIC = "QMoE layer tokens/s: decode M=1..4 (%HBM peak), 8K prefill (%MFMA peak)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
-BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+F16_PEAK_TFLOPS = 2500.0       # MI355X dense fp16 (and bf16) MFMA, TFLOP/s
 NROT = 24
 DEV = torch.device("cuda:0")
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_fused_traffic_qwen3_int4_m4.txt")
-TRAFFIC_SOURCES = ["quantized_mixture_experts_qmoe_amd/csrc/decode_fused.hip",
-                   "quantized_mixture_experts_qmoe_amd/csrc/device.h",
-                   "quantized_mixture_experts_qmoe_amd/csrc/internal.h"]
-PREFILL_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "prefill_traffic_qwen3_int4_8k.txt")
-PREFILL_SOURCES = ["quantized_mixture_experts_qmoe_amd/csrc/prefill.hip",
-                   "quantized_mixture_experts_qmoe_amd/csrc/device.h",
-                   "quantized_mixture_experts_qmoe_amd/csrc/internal.h"]
+_CSRC = "quantized_mixture_experts_qmoe_amd/csrc/"
+_COMMON = [_CSRC + "device.h", _CSRC + "internal.h"]
+# Committed counter summaries (profiles/) and the sources each was taken on:
+# a summary's figures are reported only while the digest recorded in it
+# matches the digest of those sources now.
+TRAFFIC = {
+    "decode4": ("decode_fused_traffic_qwen3_int4_m4.txt", [_CSRC + "decode_fused.hip"] + _COMMON),
+    "decode1": ("decode_fused_traffic_qwen3_int4_m1.txt", [_CSRC + "decode_fused.hip"] + _COMMON),
+    "int3_decode4": ("decode_fused_traffic_qwen3_int3_m4.txt", [_CSRC + "decode_fused.hip"] + _COMMON),
+    "stack_decode1": ("decode_fused_traffic_int2_stack_m1.txt", [_CSRC + "decode_fused.hip"] + _COMMON),
+    "prefill": ("prefill_traffic_qwen3_int4_8k.txt", [_CSRC + "prefill.hip"] + _COMMON),
+    "small32": ("small_traffic_qwen3_int4_t32.txt", [_CSRC + "small.hip", _CSRC + "route.hip",
+                                                     _CSRC + "prefill.hip"] + _COMMON),
+}
+TRAFFIC_SOURCES = TRAFFIC["decode4"][1]
+PREFILL_SOURCES = TRAFFIC["prefill"][1]
 
 
 def kernel_source_digest(sources=None) -> str:
@@ -85,12 +93,13 @@ def kernel_source_digest(sources=None) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(path=None, sources=None, key="hbm_bytes_per_launch"):
-    """Counter-measured HBM bytes per launch from a committed counter summary
-    (default: the fused decode at M=4), or None if there is no summary taken
-    on the current kernel source."""
+def measured_traffic(workload="decode4", key="hbm_bytes_per_launch"):
+    """Counter-measured HBM bytes per launch of a workload's dominant kernel
+    from its committed counter summary, or None if there is none taken on
+    the current kernel sources."""
+    name, sources = TRAFFIC[workload]
     try:
-        with open(TRAFFIC_SUMMARY if path is None else path) as f:
+        with open(os.path.join(ROOT, "profiles", name)) as f:
             kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith(("#", "|", "-")))
     except OSError:
         return None
@@ -322,7 +331,7 @@ def bench_prefill(steps: int, warmup: int, name: str = "prefill", T: int = 8192)
     return {
         "T": T, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
         "layer_TFLOPs": flops / (ms * 1e-3) / 1e12,
-        "layer_frac_mfma": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+        "layer_frac_mfma": flops / (ms * 1e-3) / 1e12 / F16_PEAK_TFLOPS,
         "kernels_us": {kk: v * 1e3 for kk, v in kt.items()},
         "step_us": spread, "load_skew": skew,
         "fc1": {"flops": fc1_flops, "s": t_fc1, "TFLOPs": fc1_flops / t_fc1 / 1e12},
@@ -405,7 +414,7 @@ def bench_stack(T: int, steps: int, warmup: int):
     else:
         flops = nl * 2.0 * T * k * (2 * I * H + H * I)
         res["flops_per_pass"] = flops
-        res["frac_mfma"] = flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS
+        res["frac_mfma"] = flops / (ms * 1e-3) / 1e12 / F16_PEAK_TFLOPS
     for L, _, _ in layers:
         L.close()
     del layers, ws
@@ -534,34 +543,36 @@ def main():
              "step_us": m1["step_us"],
              "roofline": {"bound": "hbm", "kernel": m1["dominant"]["kernel"],
                           "achieved": m1["dominant"]["GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                          "frac": m1["dominant"]["GBs"] / HBM_PEAK_GBS}},
+                          "frac": m1["dominant"]["GBs"] / HBM_PEAK_GBS,
+                          "traffic": measured_traffic("decode1")}},
             {"workload": "prefill 8192 tokens (16 packed sequences, Zipf-skewed routing)",
              "tokens_per_s": pf["tokens_per_s"], "ms_per_step": pf["ms_per_step"],
              "layer_frac_mfma": pf["layer_frac_mfma"], "kernels_us": pf["kernels_us"],
              "step_us": pf["step_us"], "load_skew": pf["load_skew"],
              "roofline": {"bound": "mfma", "kernel": "gemm_fc1_swiglu",
-                          "achieved": pf["fc1"]["TFLOPs"], "peak": BF16_PEAK_TFLOPS,
-                          "unit": "TFLOP/s", "frac": pf["fc1"]["TFLOPs"] / BF16_PEAK_TFLOPS,
-                          "traffic": measured_traffic(PREFILL_TRAFFIC_SUMMARY, PREFILL_SOURCES,
-                                                      "fc1_hbm_bytes_per_launch")}},
+                          "achieved": pf["fc1"]["TFLOPs"], "peak": F16_PEAK_TFLOPS,
+                          "unit": "TFLOP/s", "frac": pf["fc1"]["TFLOPs"] / F16_PEAK_TFLOPS,
+                          "traffic": measured_traffic("prefill", "fc1_hbm_bytes_per_launch")}},
             {"workload": "INT3 bs64 layer decode M=4 (uniform routing)",
              "tokens_per_s": i3d["tokens_per_s"], "ms_per_step": i3d["ms_per_step"],
              "layer_frac_hbm": i3d["layer_frac_hbm"], "distinct_experts": i3d["distinct_experts"],
              "kernels_us": i3d["kernels_us"],
              "roofline": {"bound": "hbm", "kernel": i3d["dominant"]["kernel"],
                           "achieved": i3d["dominant"]["GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                          "frac": i3d["dominant"]["GBs"] / HBM_PEAK_GBS}},
+                          "frac": i3d["dominant"]["GBs"] / HBM_PEAK_GBS,
+                          "traffic": measured_traffic("int3_decode4")}},
             {"workload": "INT3 bs64 layer prefill 2048 tokens (8 packed sequences)",
              "tokens_per_s": i3p["tokens_per_s"], "ms_per_step": i3p["ms_per_step"],
              "layer_frac_mfma": i3p["layer_frac_mfma"], "kernels_us": i3p["kernels_us"],
              "step_us": i3p["step_us"], "load_skew": i3p["load_skew"],
              "roofline": {"bound": "mfma", "kernel": "gemm_fc1_swiglu",
-                          "achieved": i3p["fc1"]["TFLOPs"], "peak": BF16_PEAK_TFLOPS,
-                          "unit": "TFLOP/s", "frac": i3p["fc1"]["TFLOPs"] / BF16_PEAK_TFLOPS}},
+                          "achieved": i3p["fc1"]["TFLOPs"], "peak": F16_PEAK_TFLOPS,
+                          "unit": "TFLOP/s", "frac": i3p["fc1"]["TFLOPs"] / F16_PEAK_TFLOPS}},
             {"workload": "48-layer INT2 bs32 stack, M=1 decode pass (Zipf routing per layer)",
              "tokens_per_s": sd["tokens_per_s"], "ms_per_pass": sd["ms_per_pass"],
              "layer_us": sd["layer_us"], "bytes_per_pass": sd["bytes_per_pass"],
-             "frac_hbm": sd["frac_hbm"]},
+             "frac_hbm": sd["frac_hbm"],
+             "traffic_per_layer": measured_traffic("stack_decode1")},
             {"workload": "48-layer INT2 bs32 stack, 32768-token packed prefill pass",
              "tokens_per_s": sp["tokens_per_s"], "ms_per_pass": sp["ms_per_pass"],
              "layer_us": sp["layer_us"], "flops_per_pass": sp["flops_per_pass"],
@@ -570,7 +581,9 @@ def main():
             {"workload": f"small batch {r['T']} tokens (uniform routing, small-batch path)",
              "tokens_per_s": r["tokens_per_s"], "ms_per_step": r["ms_per_step"],
              "distinct_experts": r["distinct_experts"], "layer_frac_hbm": r["layer_frac_hbm"],
-             "kernels_us": r["kernels_us"], "step_us": r["step_us"]}
+             "kernels_us": r["kernels_us"], "step_us": r["step_us"],
+             "fc1_traffic": measured_traffic("small32", "fc1_hbm_bytes_per_launch")
+             if r["T"] == 32 else None}
             for r in smalls
         ]
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_tokens)
@@ -598,7 +611,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": dom["kernel"], "achieved": dom["GBs"],
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dom["GBs"] / HBM_PEAK_GBS,
                      "bytes_per_launch": dom["bytes"],
-                     "traffic": measured_traffic() if dom["kernel"] == "decode_fused" else None},
+                     "traffic": measured_traffic("decode4") if dom["kernel"] == "decode_fused" else None},
         "cpu_baseline": cpu,
         "extra": extra,
     }

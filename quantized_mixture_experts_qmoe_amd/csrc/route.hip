@@ -250,25 +250,42 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
   const int R = static_cast<int>(T) * k;
   const int nch = (R + 63) / 64;
   for (int i = tid; i < nch * E; i += 1024) s_tab[i] = 0;
-  // top-k + softmax, one token per wave at a time
-  for (int64_t t = wave; t < T; t += 16) {
-    int id;
-    float wt;
-    if constexpr (SLOTS > 0) {
-      uint16_t lg[SLOTS];
+  // top-k + softmax, one token per wave at a time (bf16 logits: the next
+  // token's logits load while the current one is selected)
+  if constexpr (SLOTS > 0) {
+    auto load = [&](int64_t t, uint16_t (&lg)[SLOTS]) {
+      const int64_t tc = t < T ? t : T - 1;
 #pragma unroll
       for (int c = 0; c < SLOTS; ++c) {
         const int e = lane + kWave * c;
-        lg[c] = reinterpret_cast<const uint16_t*>(logits)[t * E + (e < E ? e : 0)];
+        lg[c] = reinterpret_cast<const uint16_t*>(logits)[tc * E + (e < E ? e : 0)];
       }
-      topk_softmax_bf16_wave<SLOTS>(lg, E, k, normalize, lane, id, wt);
-    } else {
-      topk_softmax_wave_r(logits + t * E, E, k, normalize, lane, id, wt);
+    };
+    uint16_t cur[SLOTS], nxt[SLOTS];
+    load(wave, cur);
+    for (int64_t t = wave; t < T; t += 16) {
+      load(t + 16, nxt);
+      int id;
+      float wt;
+      topk_softmax_bf16_wave<SLOTS>(cur, E, k, normalize, lane, id, wt);
+      if (lane < k) {
+        topk_id[t * k + lane] = id;
+        topk_w[t * k + lane] = wt;
+        s_id[t * k + lane] = id;
+      }
+#pragma unroll
+      for (int c = 0; c < SLOTS; ++c) cur[c] = nxt[c];
     }
-    if (lane < k) {
-      topk_id[t * k + lane] = id;
-      topk_w[t * k + lane] = wt;
-      s_id[t * k + lane] = id;
+  } else {
+    for (int64_t t = wave; t < T; t += 16) {
+      int id;
+      float wt;
+      topk_softmax_wave_r(logits + t * E, E, k, normalize, lane, id, wt);
+      if (lane < k) {
+        topk_id[t * k + lane] = id;
+        topk_w[t * k + lane] = wt;
+        s_id[t * k + lane] = id;
+      }
     }
   }
   __syncthreads();
