@@ -56,10 +56,10 @@ constexpr int kForceNone = 0, kForcePrefill = 1, kForceSmall = 2, kForceGrouped 
 // small-batch path, which streams each active expert's weights once per
 // call; larger batches run the grouped GEMMs on 256-row tiles. Measured on
 // the Qwen3-30B-A3B-shaped INT4 layer (us per call, cold weights):
-//   tokens          5     8     9    12    16    24    32    64   128   256
+//   tokens          5     8     9    12    16    24    32    64   128   256   384
 //   grouped decode 53    65    85    95   125   185
-//   small path     61    72    75    84    87   110   113   131   158   216
-//   grouped GEMMs 114   158         177   179   241   244   251   258   265
+//   small path           75    75    84    87         110   128   148   214   276
+//   grouped GEMMs 114   158         177   179   241   244   251   258   265   238
 // QMOE_FORCE_PATH=grouped extends the grouped decode to 24 tokens.
 constexpr int64_t kGroupedDecodeMaxTokens = 8;
 constexpr int64_t kGroupedDecodeForcedMax = 24;

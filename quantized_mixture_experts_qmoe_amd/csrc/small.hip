@@ -28,7 +28,7 @@
 // its 32 values are the B operand of the sub-block's four MFMA steps, K
 // values 32(4s + q) + 8t + 0..7 at step t, and the A operand of step t is
 // read from the same K range of the staged rows. The weights are loaded in
-// whole row segments (RowBlockStream) and handed to that layout across
+// whole row segments (StreamLanes, RowGroup) and handed to that layout across
 // lanes, so every weight byte is loaded once per call, by one lane.
 //
 // Semantics: grouped experts over expert-sorted routes ("[CUDA] Add INT4 and
@@ -50,9 +50,12 @@ typedef float sf32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kSmallWaves = 8;
 constexpr int kSmallThreads = kSmallWaves * kWave;
-constexpr int kFc1Cols = kSmallWaves * 16;   // h columns per FC1 workgroup
-constexpr int kFc2Cols = kSmallWaves * 32;   // output columns per FC2 workgroup
-constexpr int kDepthB = 2;                   // row blocks of weights in flight per wave
+constexpr int kFc1Groups = 1;                        // 16-column groups of h per FC1 wave
+constexpr int kFc2Groups = 4;                        // 16-row groups of outputs per FC2 wave
+constexpr int kFc1Depth = 2;                         // row blocks in flight per FC1 row group
+constexpr int kFc2Depth = 1;                         // and per FC2 row group
+constexpr int kFc1Cols = kSmallWaves * 16 * kFc1Groups;   // h columns per FC1 workgroup
+constexpr int kFc2Cols = kSmallWaves * 16 * kFc2Groups;   // output columns per FC2 workgroup
 
 // Logical index of this workgroup: the column blocks of one tile (which
 // share its staged rows) are dealt to one XCD.
@@ -65,89 +68,93 @@ __device__ __forceinline__ int small_logical(int active) {
   return L < active ? L : -1;
 }
 
-// Sixteen weight rows (row n of the group is the MFMA column of the lanes
-// with l16 = n), streamed in blocks of UB units per row. Each load
-// instruction reads UB consecutive units (128 bytes for INT4 and INT2, 96
-// for INT3) of each of RPI rows: lane l loads unit (l mod UB) of row
+// Weight rows stream in groups of sixteen (row n of a group is the MFMA
+// column of the lanes with l16 = n), in blocks of UB units per row. Each
+// load instruction reads UB consecutive units (128 bytes for INT4 and INT2,
+// 96 for INT3) of each of RPI rows: lane l loads unit (l mod UB) of row
 // RPI * m + l / UB in instruction m. Rows read in such whole segments keep
 // HBM streaming at full rate, where 64-byte pieces of 16 rows at a time
 // fall to about two thirds of it. ds_bpermute then hands lane (q, n) the
 // unit 4s + q of its own row n for each 128-K sub-block s, the layout the
 // matrix cores' B operand takes. Units past K get a zero scale (their
 // addresses are clamped to the row's first unit).
-template <int BITS, bool HAS_ZP>
-struct RowBlockStream {
+template <int BITS>
+struct StreamLanes {
   static constexpr int UB = BITS == 2 ? 16 : 8;   // units per row per block
   static constexpr int RPI = kWave / UB;          // rows per load instruction
   static constexpr int NI = 16 / RPI;             // load instructions per block
   static constexpr int SB = UB / 4;               // 128-K sub-blocks per block
-  struct Block {
-    UnitWords<BITS> raw[NI];
-    uint32_t s[SB];
-    int z[SB];
-  };
-  const uint8_t* row_ld[NI];   // row this lane loads in instruction m
-  const uint16_t* srow;        // this lane's own row: scales
-  const uint8_t* zrow;         // and zero points
-  int zp, ushift, nunits, lu, q, msel;
-  int src[SB];                 // ds_bpermute byte address per sub-block
-
-  // rows(r) = pointers to row r (0..15) of the group: codes, scales, zero points
-  template <typename RowFn>
-  __device__ __forceinline__ void init(RowFn rows, int lane, int zp_, int ushift_, int nunits_) {
-    zp = zp_;
-    ushift = ushift_;
-    nunits = nunits_;
+  int lu, q, msel;
+  int64_t cofs[NI];   // byte offset (from the group's first row) of the row this lane
+                      // loads in instruction m
+  int64_t sofs;       // element offset of this lane's own row's scales
+  int src[SB];        // ds_bpermute byte address of the lane holding its unit
+  // rows of every group a wave streams lie rstride bytes apart (their
+  // scales and zero points sstride elements apart)
+  __device__ __forceinline__ StreamLanes(int lane, int64_t rstride, int64_t sstride) {
     lu = lane % UB;
     q = lane >> 4;
     const int n = lane & 15;
-#pragma unroll
-    for (int m = 0; m < NI; ++m) row_ld[m] = rows(RPI * m + lane / UB).codes;
-    const auto own = rows(n);
-    srow = own.scales;
-    zrow = own.zps;
     msel = n / RPI;
+#pragma unroll
+    for (int m = 0; m < NI; ++m) cofs[m] = (RPI * m + lane / UB) * rstride;
+    sofs = n * sstride;
 #pragma unroll
     for (int sb = 0; sb < SB; ++sb) src[sb] = 4 * ((n % RPI) * UB + 4 * sb + q);
   }
-
-  __device__ __forceinline__ void load(int b, Block& blk) const {
-    const int u = b * UB + lu;
-    const int uc = u < nunits ? u : 0;
-#pragma unroll
-    for (int m = 0; m < NI; ++m) blk.raw[m] = load_unit<BITS>(row_ld[m] + uc * (4 * BITS));
-#pragma unroll
-    for (int sb = 0; sb < SB; ++sb) {
-      const int v = b * UB + 4 * sb + q;
-      const int vc = v < nunits ? v : 0;
-      blk.s[sb] = v < nunits ? srow[vc >> ushift] : 0u;   // a unit past K weighs zero
-      blk.z[sb] = HAS_ZP ? zrow[vc >> ushift] : zp;
-    }
-  }
-
-  // unit 4 * sb + q of this lane's row, from the lanes that loaded it
-  __device__ __forceinline__ UnitWords<BITS> unit(const Block& blk, int sb) const {
-    UnitWords<BITS> w;
-#pragma unroll
-    for (int d = 0; d < BITS; ++d) {
-      uint32_t v = 0;
-#pragma unroll
-      for (int m = 0; m < NI; ++m) {
-        const uint32_t t = static_cast<uint32_t>(
-            __builtin_amdgcn_ds_bpermute(src[sb], static_cast<int>(blk.raw[m].w[d])));
-        v = msel == m ? t : v;
-      }
-      w.w[d] = v;
-    }
-    return w;
-  }
 };
 
-struct RowPtrs {
+// Sixteen rows: the codes, scales and zero points of the group's first row
+// (the same pointers for every lane of a wave).
+struct RowGroup {
   const uint8_t* codes;
   const uint16_t* scales;
   const uint8_t* zps;
 };
+
+template <int BITS>
+struct RowBlock {
+  UnitWords<BITS> raw[StreamLanes<BITS>::NI];
+  uint32_t s[StreamLanes<BITS>::SB];
+  int z[StreamLanes<BITS>::SB];
+};
+
+template <int BITS, bool HAS_ZP>
+__device__ __forceinline__ void load_block(const StreamLanes<BITS>& ln, const RowGroup& g, int b, int nunits,
+                                           int ushift, int zp, RowBlock<BITS>& blk) {
+  using SL = StreamLanes<BITS>;
+  // a unit past K reads the row's first unit (unused: its scale is zero)
+  const int u = b * SL::UB + ln.lu;
+  const int uc = u < nunits ? u : 0;
+#pragma unroll
+  for (int m = 0; m < SL::NI; ++m) blk.raw[m] = load_unit<BITS>(g.codes + ln.cofs[m] + uc * (4 * BITS));
+#pragma unroll
+  for (int sb = 0; sb < SL::SB; ++sb) {
+    const int v = b * SL::UB + 4 * sb + ln.q;
+    const int vc = v < nunits ? v : 0;
+    blk.s[sb] = v < nunits ? g.scales[ln.sofs + (vc >> ushift)] : 0u;   // past K weighs zero
+    blk.z[sb] = HAS_ZP ? g.zps[ln.sofs + (vc >> ushift)] : zp;
+  }
+}
+
+// unit 4 * sb + q of this lane's row, from the lanes that loaded it
+template <int BITS>
+__device__ __forceinline__ UnitWords<BITS> gather_unit(const StreamLanes<BITS>& ln, const RowBlock<BITS>& blk,
+                                                       int sb) {
+  UnitWords<BITS> w;
+#pragma unroll
+  for (int d = 0; d < BITS; ++d) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int m = 0; m < StreamLanes<BITS>::NI; ++m) {
+      const uint32_t t = static_cast<uint32_t>(
+          __builtin_amdgcn_ds_bpermute(ln.src[sb], static_cast<int>(blk.raw[m].w[d])));
+      v = ln.msel == m ? t : v;
+    }
+    w.w[d] = v;
+  }
+  return w;
+}
 
 // Staged rows are K fp16 values each, in 16-byte pieces: piece c of row r
 // sits at piece c ^ (r mod 16) of the row (K is a multiple of 128, so the
@@ -170,7 +177,7 @@ __device__ __forceinline__ sf32x4_t mfma_unit(const uint16_t* arow, int l16, int
 
 }  // namespace
 
-// FC1 + SwiGLU over one tile (<= 16 routes of expert e) and 128 h columns.
+// FC1 + SwiGLU over one tile (<= 16 routes of expert e) and kFc1Cols h columns.
 // grid = 8 * ceil(max_tiles * n_blocks / 8), block = 512, dynamic LDS =
 // 16 * H * 2 bytes.
 template <int BITS, bool HAS_ZP>
@@ -192,31 +199,31 @@ __global__ __launch_bounds__(kSmallThreads) void small_fc1_kernel(
   const int q = lane >> 4, l16 = lane & 15;
   const int ld = H;
 
-  // this lane's h column n; the wave's gate rows and up rows stream as two
-  // groups of 16
-  const int n = nb * kFc1Cols + wave * 16 + l16;
+  // the wave's h columns: kFc1Groups groups of 16, each streaming its 16
+  // gate rows (group 2c) and 16 up rows (group 2c + 1)
+  constexpr int NG = 2 * kFc1Groups;
+  using SL = StreamLanes<BITS>;
+  const int64_t step = fc1_il ? 2 : 1;   // interleaved FC1: gate and up rows alternate
+  const SL ln(lane, step * row_bytes, step * nblk);
   const int64_t ebase = static_cast<int64_t>(e) * 2 * I;
   const int nunits = H / 32;
-  using Stream = RowBlockStream<BITS, HAS_ZP>;
-  Stream sg, su;
-  auto rows_of = [&](bool up) {
-    return [=](int r) {
-      const int c0 = nb * kFc1Cols + wave * 16 + r;
-      const int c = c0 < I ? c0 : 0;
-      const int64_t row = ebase + (fc1_il ? 2 * c + (up ? 1 : 0) : (up ? I + c : c));
-      return RowPtrs{codes + row * row_bytes, scales + row * nblk, HAS_ZP ? zps + row * nblk : nullptr};
-    };
-  };
-  sg.init(rows_of(false), lane, zp, ushift, nunits);
-  su.init(rows_of(true), lane, zp, ushift, nunits);
-  const int nbk = (nunits + Stream::UB - 1) / Stream::UB;
-
-  typename Stream::Block kg[kDepthB], ku[kDepthB];
+  const int col_w = nb * kFc1Cols + __builtin_amdgcn_readfirstlane(wave) * 16 * kFc1Groups;
+  RowGroup grp[NG];
 #pragma unroll
-  for (int d = 0; d < kDepthB; ++d) {
-    sg.load(d, kg[d]);
-    su.load(d, ku[d]);
+  for (int g = 0; g < NG; ++g) {
+    const int c0 = col_w + 16 * (g >> 1), up = g & 1;
+    const int cc = c0 < I ? c0 : 0;
+    const int64_t row = ebase + (fc1_il ? 2 * cc + up : (up ? I + cc : cc));
+    grp[g] = RowGroup{codes + row * row_bytes, scales + row * nblk, HAS_ZP ? zps + row * nblk : nullptr};
   }
+  const int nbk = (nunits + SL::UB - 1) / SL::UB;
+  constexpr int D = kFc1Depth;
+  RowBlock<BITS> blk[NG][D];
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+      load_block<BITS, HAS_ZP>(ln, grp[g], d < nbk ? d : nbk - 1, nunits, ushift, zp, blk[g][d]);
 
   // stage the tile's activation rows (and their exponents) while the first
   // blocks' loads are in flight
@@ -231,50 +238,76 @@ __global__ __launch_bounds__(kSmallThreads) void small_fc1_kernel(
     const int r = threadIdx.x;
     s_exp[r] = (xexp != nullptr && r < nrows) ? xexp[sorted_routes[row0 + r] / k] : 0;
   }
-
   __syncthreads();
 
-  sf32x4_t accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
+  sf32x4_t acc[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) acc[g] = sf32x4_t{0.f, 0.f, 0.f, 0.f};
   const uint16_t* arow = smem + l16 * ld;
-  for (int b0 = 0; b0 < nbk; b0 += kDepthB) {
+  int bk = 0;
+  for (; bk + D <= nbk; bk += D) {
 #pragma unroll
-    for (int d = 0; d < kDepthB; ++d) {
-      const int bk = b0 + d;
-      if (bk < nbk) {
+    for (int d = 0; d < D; ++d) {
+      const int bb = bk + d;
 #pragma unroll
-        for (int sb = 0; sb < Stream::SB; ++sb) {
+      for (int g = 0; g < NG; ++g) {
+        // (a group past I computes on clamped rows; its results are not stored)
+#pragma unroll
+        for (int sb = 0; sb < SL::SB; ++sb) {
           // K is a multiple of 128, so a sub-block lies wholly inside or
           // wholly past it; one past it has no staged A columns to read
-          if (bk * Stream::UB + 4 * sb >= nunits) break;
-          uint32_t pg[16], pu[16];
-          dequant_unit_f16<BITS>(sg.unit(kg[d], sb), kg[d].s[sb], kg[d].z[sb], pg);
-          dequant_unit_f16<BITS>(su.unit(ku[d], sb), ku[d].s[sb], ku[d].z[sb], pu);
-          const int col0 = 32 * (bk * Stream::UB + 4 * sb + q);
-          accg = mfma_unit(arow, l16, col0, pg, accg);
-          accu = mfma_unit(arow, l16, col0, pu, accu);
+          if (bb * SL::UB + 4 * sb >= nunits) break;
+          uint32_t p[16];
+          dequant_unit_f16<BITS>(gather_unit<BITS>(ln, blk[g][d], sb), blk[g][d].s[sb], blk[g][d].z[sb], p);
+          acc[g] = mfma_unit(arow, l16, 32 * (bb * SL::UB + 4 * sb + q), p, acc[g]);
         }
-        sg.load(bk + kDepthB, kg[d]);
-        su.load(bk + kDepthB, ku[d]);
+        // the loads are unconditional, so the compiler's waits count them
+        // exactly; past the last block they read the last block again (still
+        // in L2) rather than the rows' first units
+        load_block<BITS, HAS_ZP>(ln, grp[g], bb + D < nbk ? bb + D : nbk - 1, nunits, ushift, zp, blk[g][d]);
       }
     }
   }
-
-  // epilogue: lane holds rows 4q + i, column n
-  if (n >= I) return;
-  const float bg = bias_at(bias, act, ebase + (fc1_il ? 2 * n : n));
-  const float bu = bias_at(bias, act, ebase + (fc1_il ? 2 * n + 1 : I + n));
+  // the last nbk % D blocks (already loaded)
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 4 * q + i;
-    if (r < nrows) {
-      const int ex = s_exp[r];
-      const float gv = ldexpf(accg[i], ex) + bg, uv = ldexpf(accu[i], ex) + bu;
-      h32[static_cast<int64_t>(row0 + r) * I + n] = silu_mul(gv, uv);
+  for (int d = 0; d < D; ++d) {
+    if (bk + d >= nbk) break;
+    const int bb = bk + d;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        // (a group past I computes on clamped rows; its results are not stored)
+#pragma unroll
+        for (int sb = 0; sb < SL::SB; ++sb) {
+          // K is a multiple of 128, so a sub-block lies wholly inside or
+          // wholly past it; one past it has no staged A columns to read
+          if (bb * SL::UB + 4 * sb >= nunits) break;
+          uint32_t p[16];
+          dequant_unit_f16<BITS>(gather_unit<BITS>(ln, blk[g][d], sb), blk[g][d].s[sb], blk[g][d].z[sb], p);
+          acc[g] = mfma_unit(arow, l16, 32 * (bb * SL::UB + 4 * sb + q), p, acc[g]);
+        }
+      }
+  }
+
+  // epilogue: lane holds rows 4q + i, column n of each group pair
+#pragma unroll
+  for (int c = 0; c < kFc1Groups; ++c) {
+    const int n = col_w + 16 * c + l16;
+    if (n >= I) continue;
+    const float bg = bias_at(bias, act, ebase + (fc1_il ? 2 * n : n));
+    const float bu = bias_at(bias, act, ebase + (fc1_il ? 2 * n + 1 : I + n));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * q + i;
+      if (r < nrows) {
+        const int ex = s_exp[r];
+        const float gv = ldexpf(acc[2 * c][i], ex) + bg, uv = ldexpf(acc[2 * c + 1][i], ex) + bu;
+        h32[static_cast<int64_t>(row0 + r) * I + n] = silu_mul(gv, uv);
+      }
     }
   }
 }
 
-// FC2 over one tile and 256 output columns. grid as FC1, block = 512,
+// FC2 over one tile and kFc2Cols output columns. grid as FC1, block = 512,
 // dynamic LDS = 16 * I * 2 bytes.
 template <int BITS, bool HAS_ZP>
 __global__ __launch_bounds__(kSmallThreads) void small_fc2_kernel(
@@ -294,28 +327,27 @@ __global__ __launch_bounds__(kSmallThreads) void small_fc2_kernel(
   const int q = lane >> 4, l16 = lane & 15;
   const int ld = I;
 
+  // the wave's output rows: kFc2Groups groups of 16
+  using SL = StreamLanes<BITS>;
+  const SL ln(lane, row_bytes, nblk);
   const int nunits = I / 32;
   const int64_t ebase = static_cast<int64_t>(e) * H;
-  using Stream = RowBlockStream<BITS, HAS_ZP>;
-  int cols[2];
-  Stream w2[2];
+  const int row_w = nb * kFc2Cols + __builtin_amdgcn_readfirstlane(wave) * 16 * kFc2Groups;
+  RowGroup grp[kFc2Groups];
 #pragma unroll
-  for (int sidx = 0; sidx < 2; ++sidx) {
-    cols[sidx] = nb * kFc2Cols + wave * 32 + 16 * sidx + l16;
-    w2[sidx].init(
-        [=](int r) {
-          const int c0 = nb * kFc2Cols + wave * 32 + 16 * sidx + r;
-          const int64_t row = ebase + (c0 < H ? c0 : 0);
-          return RowPtrs{codes + row * row_bytes, scales + row * nblk, HAS_ZP ? zps + row * nblk : nullptr};
-        },
-        lane, zp, ushift, nunits);
+  for (int g = 0; g < kFc2Groups; ++g) {
+    const int m0 = row_w + 16 * g;
+    const int64_t row = ebase + (m0 < H ? m0 : 0);
+    grp[g] = RowGroup{codes + row * row_bytes, scales + row * nblk, HAS_ZP ? zps + row * nblk : nullptr};
   }
-  const int nbk = (nunits + Stream::UB - 1) / Stream::UB;
-  typename Stream::Block bv[2][kDepthB];
+  const int nbk = (nunits + SL::UB - 1) / SL::UB;
+  constexpr int D = kFc2Depth;
+  RowBlock<BITS> blk[kFc2Groups][D];
 #pragma unroll
-  for (int d = 0; d < kDepthB; ++d)
+  for (int d = 0; d < D; ++d)
 #pragma unroll
-    for (int sidx = 0; sidx < 2; ++sidx) w2[sidx].load(d, bv[sidx][d]);
+    for (int g = 0; g < kFc2Groups; ++g)
+      load_block<BITS, HAS_ZP>(ln, grp[g], d < nbk ? d : nbk - 1, nunits, ushift, zp, blk[g][d]);
 
   // stage h rows as fp16 with the row's range exponent (while the first
   // blocks' loads are in flight); wave w takes rows
@@ -357,38 +389,57 @@ __global__ __launch_bounds__(kSmallThreads) void small_fc2_kernel(
 
   __syncthreads();
 
-  sf32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  sf32x4_t acc[kFc2Groups];
+#pragma unroll
+  for (int g = 0; g < kFc2Groups; ++g) acc[g] = sf32x4_t{0.f, 0.f, 0.f, 0.f};
   const uint16_t* arow = smem + l16 * ld;
-  for (int b0 = 0; b0 < nbk; b0 += kDepthB) {
+  int bk = 0;
+  for (; bk + D <= nbk; bk += D) {
 #pragma unroll
-    for (int d = 0; d < kDepthB; ++d) {
-      const int bk = b0 + d;
-      if (bk < nbk) {
+    for (int d = 0; d < D; ++d) {
+      const int bb = bk + d;
 #pragma unroll
-        for (int sidx = 0; sidx < 2; ++sidx) {
+      for (int g = 0; g < kFc2Groups; ++g) {
+        // (a group past H computes on clamped rows; its results are not stored)
 #pragma unroll
-          for (int sb = 0; sb < Stream::SB; ++sb) {
-            if (bk * Stream::UB + 4 * sb >= nunits) break;   // past K (K % 128 == 0)
-            uint32_t p[16];
-            dequant_unit_f16<BITS>(w2[sidx].unit(bv[sidx][d], sb), bv[sidx][d].s[sb], bv[sidx][d].z[sb], p);
-            acc[sidx] = mfma_unit(arow, l16, 32 * (bk * Stream::UB + 4 * sb + q), p, acc[sidx]);
-          }
-          w2[sidx].load(bk + kDepthB, bv[sidx][d]);
+        for (int sb = 0; sb < SL::SB; ++sb) {
+          if (bb * SL::UB + 4 * sb >= nunits) break;   // past K (K % 128 == 0)
+          uint32_t p[16];
+          dequant_unit_f16<BITS>(gather_unit<BITS>(ln, blk[g][d], sb), blk[g][d].s[sb], blk[g][d].z[sb], p);
+          acc[g] = mfma_unit(arow, l16, 32 * (bb * SL::UB + 4 * sb + q), p, acc[g]);
         }
+        load_block<BITS, HAS_ZP>(ln, grp[g], bb + D < nbk ? bb + D : nbk - 1, nunits, ushift, zp, blk[g][d]);
       }
     }
   }
+  // the last nbk % D blocks (already loaded)
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    if (bk + d >= nbk) break;
+    const int bb = bk + d;
+#pragma unroll
+      for (int g = 0; g < kFc2Groups; ++g) {
+        // (a group past H computes on clamped rows; its results are not stored)
+#pragma unroll
+        for (int sb = 0; sb < SL::SB; ++sb) {
+          if (bb * SL::UB + 4 * sb >= nunits) break;   // past K (K % 128 == 0)
+          uint32_t p[16];
+          dequant_unit_f16<BITS>(gather_unit<BITS>(ln, blk[g][d], sb), blk[g][d].s[sb], blk[g][d].z[sb], p);
+          acc[g] = mfma_unit(arow, l16, 32 * (bb * SL::UB + 4 * sb + q), p, acc[g]);
+        }
+      }
+  }
 
 #pragma unroll
-  for (int sidx = 0; sidx < 2; ++sidx) {
-    const int m = cols[sidx];
+  for (int g = 0; g < kFc2Groups; ++g) {
+    const int m = row_w + 16 * g + l16;
     if (m >= H) continue;
     const float b = bias_at(bias, act, ebase + m);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 4 * q + i;
       if (r < nrows)
-        __builtin_nontemporal_store(ldexpf(acc[sidx][i], s_exp[r]) + b,
+        __builtin_nontemporal_store(ldexpf(acc[g][i], s_exp[r]) + b,
                                     &y32[static_cast<int64_t>(row0 + r) * H + m]);
     }
   }
