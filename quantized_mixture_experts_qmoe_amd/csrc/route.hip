@@ -87,15 +87,35 @@ __global__ __launch_bounds__(512) void route_topk_hist_wide_kernel(
   for (int e = threadIdx.x; e < E; e += 512) hist[static_cast<int64_t>(blockIdx.x) * E + e] = s_hist[e];
 }
 
-// Inclusive scan of s[0..n) in place (n <= 1024, blockDim.x == 1024).
-__device__ void block_scan_inclusive(int32_t* s, int n) {
-  for (int off = 1; off < n; off <<= 1) {
-    int32_t v = 0;
-    if (threadIdx.x < n && threadIdx.x >= off) v = s[threadIdx.x - off];
-    __syncthreads();
-    if (threadIdx.x < n) s[threadIdx.x] += v;
-    __syncthreads();
+// Inclusive scans of a[0..n) and b[0..n) in place (n <= 1024, blockDim.x ==
+// 1024, each thread tid < n having written a[tid] and b[tid]): a shuffle
+// scan per wave, then the preceding waves' totals; two barriers in all.
+__device__ void block_scan2_inclusive(int32_t* a, int32_t* b, int n) {
+  __shared__ int32_t s_wa[16], s_wb[16];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid >> 6;
+  int32_t va = tid < n ? a[tid] : 0, vb = tid < n ? b[tid] : 0;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int32_t ta = __shfl_up(va, off, kWave), tb = __shfl_up(vb, off, kWave);
+    if (lane >= off) {
+      va += ta;
+      vb += tb;
+    }
   }
+  if (lane == kWave - 1) {
+    s_wa[w] = va;
+    s_wb[w] = vb;
+  }
+  __syncthreads();
+  for (int i = 0; i < w; ++i) {
+    va += s_wa[i];
+    vb += s_wb[i];
+  }
+  if (tid < n) {
+    a[tid] = va;
+    b[tid] = vb;
+  }
+  __syncthreads();
 }
 
 // One workgroup of 1024 threads. Thread (e, p) owns expert e and the p-th
@@ -151,9 +171,7 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restr
     s_scan[tid] = run;
     s_tiles[tid] = (run + tile_m - 1) / tile_m;
   }
-  __syncthreads();
-  block_scan_inclusive(s_scan, E);
-  block_scan_inclusive(s_tiles, E);
+  block_scan2_inclusive(s_scan, s_tiles, E);
   if (tid < E) {
     offsets[tid + 1] = s_scan[tid];
     if (tid == 0) offsets[0] = 0;
@@ -320,9 +338,7 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
     s_scan[tid] = run;
     s_tiles[tid] = (run + tile_m - 1) / tile_m;
   }
-  __syncthreads();
-  block_scan_inclusive(s_scan, E);
-  block_scan_inclusive(s_tiles, E);
+  block_scan2_inclusive(s_scan, s_tiles, E);
   if (tid < E) {
     offsets[tid + 1] = s_scan[tid];
     if (tid == 0) offsets[0] = 0;

@@ -54,6 +54,7 @@ constexpr int kFc1Groups = 1;                        // 16-column groups of h pe
 constexpr int kFc2Groups = 4;                        // 16-row groups of outputs per FC2 wave
 constexpr int kFc1Depth = 2;                         // row blocks in flight per FC1 row group
 constexpr int kFc2Depth = 1;                         // and per FC2 row group
+constexpr int kTransBytes = 2048;                    // per-wave LDS slice for a block's units
 constexpr int kFc1Cols = kSmallWaves * 16 * kFc1Groups;   // h columns per FC1 workgroup
 constexpr int kFc2Cols = kSmallWaves * 16 * kFc2Groups;   // output columns per FC2 workgroup
 
@@ -88,7 +89,8 @@ struct StreamLanes {
   int64_t cofs[NI];   // byte offset (from the group's first row) of the row this lane
                       // loads in instruction m
   int64_t sofs;       // element offset of this lane's own row's scales
-  int src[SB];        // ds_bpermute byte address of the lane holding its unit
+  static constexpr int SLOT = BITS == 2 ? 8 : 16;   // bytes per unit in the LDS slice
+  int tofs[SB];       // byte offset, in the wave's LDS slice, of the unit this lane takes
   // rows of every group a wave streams lie rstride bytes apart (their
   // scales and zero points sstride elements apart)
   __device__ __forceinline__ StreamLanes(int lane, int64_t rstride, int64_t sstride) {
@@ -100,7 +102,7 @@ struct StreamLanes {
     for (int m = 0; m < NI; ++m) cofs[m] = (RPI * m + lane / UB) * rstride;
     sofs = n * sstride;
 #pragma unroll
-    for (int sb = 0; sb < SB; ++sb) src[sb] = 4 * ((n % RPI) * UB + 4 * sb + q);
+    for (int sb = 0; sb < SB; ++sb) tofs[sb] = (msel * kWave + (n % RPI) * UB + 4 * sb + q) * SLOT;
   }
 };
 
@@ -137,21 +139,38 @@ __device__ __forceinline__ void load_block(const StreamLanes<BITS>& ln, const Ro
   }
 }
 
-// unit 4 * sb + q of this lane's row, from the lanes that loaded it
+// A block's units go through the wave's LDS slice (kTransBytes): each lane
+// stores the units it loaded (instruction m at slot m * 64 + lane), then
+// reads back unit 4 * sb + q of its own row for each sub-block. The slice
+// is the wave's own and LDS accesses of a wave complete in order, so no
+// barrier is needed.
 template <int BITS>
-__device__ __forceinline__ UnitWords<BITS> gather_unit(const StreamLanes<BITS>& ln, const RowBlock<BITS>& blk,
-                                                       int sb) {
-  UnitWords<BITS> w;
+__device__ __forceinline__ void stash_block(const RowBlock<BITS>& blk, uint8_t* tb, int lane) {
+  using SL = StreamLanes<BITS>;
 #pragma unroll
-  for (int d = 0; d < BITS; ++d) {
-    uint32_t v = 0;
-#pragma unroll
-    for (int m = 0; m < StreamLanes<BITS>::NI; ++m) {
-      const uint32_t t = static_cast<uint32_t>(
-          __builtin_amdgcn_ds_bpermute(ln.src[sb], static_cast<int>(blk.raw[m].w[d])));
-      v = ln.msel == m ? t : v;
+  for (int m = 0; m < SL::NI; ++m) {
+    uint8_t* p = tb + (m * kWave + lane) * SL::SLOT;
+    if constexpr (BITS == 2) {
+      *reinterpret_cast<uint2*>(p) = make_uint2(blk.raw[m].w[0], blk.raw[m].w[1]);
+    } else if constexpr (BITS == 4) {
+      *reinterpret_cast<uint4*>(p) = make_uint4(blk.raw[m].w[0], blk.raw[m].w[1], blk.raw[m].w[2], blk.raw[m].w[3]);
+    } else {
+      *reinterpret_cast<uint4*>(p) = make_uint4(blk.raw[m].w[0], blk.raw[m].w[1], blk.raw[m].w[2], 0u);
     }
-    w.w[d] = v;
+  }
+}
+
+template <int BITS>
+__device__ __forceinline__ UnitWords<BITS> fetch_unit(const StreamLanes<BITS>& ln, const uint8_t* tb, int sb) {
+  UnitWords<BITS> w;
+  const uint8_t* p = tb + ln.tofs[sb];
+  if constexpr (BITS == 2) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    w.w[0] = v.x; w.w[1] = v.y;
+  } else {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    w.w[0] = v.x; w.w[1] = v.y; w.w[2] = v.z;
+    if constexpr (BITS == 4) w.w[3] = v.w;
   }
   return w;
 }
@@ -179,7 +198,7 @@ __device__ __forceinline__ sf32x4_t mfma_unit(const uint16_t* arow, int l16, int
 
 // FC1 + SwiGLU over one tile (<= 16 routes of expert e) and kFc1Cols h columns.
 // grid = 8 * ceil(max_tiles * n_blocks / 8), block = 512, dynamic LDS =
-// 16 * H * 2 bytes.
+// 16 * H * 2 bytes of staged rows + one kTransBytes slice per wave.
 template <int BITS, bool HAS_ZP>
 __global__ __launch_bounds__(kSmallThreads) void small_fc1_kernel(
     const uint16_t* __restrict__ xa, const int8_t* __restrict__ xexp,
@@ -189,7 +208,6 @@ __global__ __launch_bounds__(kSmallThreads) void small_fc1_kernel(
     int64_t row_bytes, int64_t nblk, int H, int I, bool fc1_il, const void* __restrict__ bias,
     int act, int n_blocks, float* __restrict__ h32) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  __shared__ int s_exp[kSmallRows];
   const int active = num_tiles[0] * n_blocks;
   const int L = small_logical(active);
   if (L < 0) return;
@@ -198,6 +216,7 @@ __global__ __launch_bounds__(kSmallThreads) void small_fc1_kernel(
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
   const int q = lane >> 4, l16 = lane & 15;
   const int ld = H;
+  uint8_t* tb = reinterpret_cast<uint8_t*>(smem + kSmallRows * H) + wave * kTransBytes;
 
   // the wave's h columns: kFc1Groups groups of 16, each streaming its 16
   // gate rows (group 2c) and 16 up rows (group 2c + 1)
@@ -225,18 +244,14 @@ __global__ __launch_bounds__(kSmallThreads) void small_fc1_kernel(
     for (int g = 0; g < NG; ++g)
       load_block<BITS, HAS_ZP>(ln, grp[g], d < nbk ? d : nbk - 1, nunits, ushift, zp, blk[g][d]);
 
-  // stage the tile's activation rows (and their exponents) while the first
-  // blocks' loads are in flight
+  // stage the tile's activation rows while the first blocks' loads are in
+  // flight
   const int upr = H / 8;   // 16-byte pieces per row
   for (int i = threadIdx.x; i < nrows * upr; i += kSmallThreads) {
     const int r = i / upr, c = i % upr;
     const int64_t tok = sorted_routes[row0 + r] / k;
     *reinterpret_cast<uint4*>(smem + r * ld + swz(r, c)) =
         *reinterpret_cast<const uint4*>(xa + tok * H + 8 * c);
-  }
-  if (threadIdx.x < kSmallRows) {
-    const int r = threadIdx.x;
-    s_exp[r] = (xexp != nullptr && r < nrows) ? xexp[sorted_routes[row0 + r] / k] : 0;
   }
   __syncthreads();
 
@@ -252,19 +267,27 @@ __global__ __launch_bounds__(kSmallThreads) void small_fc1_kernel(
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
         // (a group past I computes on clamped rows; its results are not stored)
+        stash_block<BITS>(blk[g][d], tb, lane);
+        uint32_t sc[SL::SB];
+        int zc[SL::SB];
+#pragma unroll
+        for (int sb = 0; sb < SL::SB; ++sb) {
+          sc[sb] = blk[g][d].s[sb];
+          zc[sb] = blk[g][d].z[sb];
+        }
+        // the next load goes out as soon as the block is in LDS; the loads
+        // are unconditional, so the compiler's waits count them exactly
+        // (past the last block they read the last block again, still in L2)
+        load_block<BITS, HAS_ZP>(ln, grp[g], bb + D < nbk ? bb + D : nbk - 1, nunits, ushift, zp, blk[g][d]);
 #pragma unroll
         for (int sb = 0; sb < SL::SB; ++sb) {
           // K is a multiple of 128, so a sub-block lies wholly inside or
           // wholly past it; one past it has no staged A columns to read
           if (bb * SL::UB + 4 * sb >= nunits) break;
           uint32_t p[16];
-          dequant_unit_f16<BITS>(gather_unit<BITS>(ln, blk[g][d], sb), blk[g][d].s[sb], blk[g][d].z[sb], p);
+          dequant_unit_f16<BITS>(fetch_unit<BITS>(ln, tb, sb), sc[sb], zc[sb], p);
           acc[g] = mfma_unit(arow, l16, 32 * (bb * SL::UB + 4 * sb + q), p, acc[g]);
         }
-        // the loads are unconditional, so the compiler's waits count them
-        // exactly; past the last block they read the last block again (still
-        // in L2) rather than the rows' first units
-        load_block<BITS, HAS_ZP>(ln, grp[g], bb + D < nbk ? bb + D : nbk - 1, nunits, ushift, zp, blk[g][d]);
       }
     }
   }
@@ -275,14 +298,12 @@ __global__ __launch_bounds__(kSmallThreads) void small_fc1_kernel(
     const int bb = bk + d;
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
-        // (a group past I computes on clamped rows; its results are not stored)
+        stash_block<BITS>(blk[g][d], tb, lane);
 #pragma unroll
         for (int sb = 0; sb < SL::SB; ++sb) {
-          // K is a multiple of 128, so a sub-block lies wholly inside or
-          // wholly past it; one past it has no staged A columns to read
           if (bb * SL::UB + 4 * sb >= nunits) break;
           uint32_t p[16];
-          dequant_unit_f16<BITS>(gather_unit<BITS>(ln, blk[g][d], sb), blk[g][d].s[sb], blk[g][d].z[sb], p);
+          dequant_unit_f16<BITS>(fetch_unit<BITS>(ln, tb, sb), blk[g][d].s[sb], blk[g][d].z[sb], p);
           acc[g] = mfma_unit(arow, l16, 32 * (bb * SL::UB + 4 * sb + q), p, acc[g]);
         }
       }
@@ -299,7 +320,7 @@ __global__ __launch_bounds__(kSmallThreads) void small_fc1_kernel(
     for (int i = 0; i < 4; ++i) {
       const int r = 4 * q + i;
       if (r < nrows) {
-        const int ex = s_exp[r];
+        const int ex = xexp != nullptr ? xexp[sorted_routes[row0 + r] / k] : 0;
         const float gv = ldexpf(acc[2 * c][i], ex) + bg, uv = ldexpf(acc[2 * c + 1][i], ex) + bu;
         h32[static_cast<int64_t>(row0 + r) * I + n] = silu_mul(gv, uv);
       }
@@ -308,7 +329,7 @@ __global__ __launch_bounds__(kSmallThreads) void small_fc1_kernel(
 }
 
 // FC2 over one tile and kFc2Cols output columns. grid as FC1, block = 512,
-// dynamic LDS = 16 * I * 2 bytes.
+// dynamic LDS = 16 * I * 2 + 8 * kTransBytes bytes.
 template <int BITS, bool HAS_ZP>
 __global__ __launch_bounds__(kSmallThreads) void small_fc2_kernel(
     const float* __restrict__ h32, const int4* __restrict__ tiles,
@@ -326,6 +347,7 @@ __global__ __launch_bounds__(kSmallThreads) void small_fc2_kernel(
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
   const int q = lane >> 4, l16 = lane & 15;
   const int ld = I;
+  uint8_t* tb = reinterpret_cast<uint8_t*>(smem + kSmallRows * I) + wave * kTransBytes;
 
   // the wave's output rows: kFc2Groups groups of 16
   using SL = StreamLanes<BITS>;
@@ -401,14 +423,22 @@ __global__ __launch_bounds__(kSmallThreads) void small_fc2_kernel(
 #pragma unroll
       for (int g = 0; g < kFc2Groups; ++g) {
         // (a group past H computes on clamped rows; its results are not stored)
+        stash_block<BITS>(blk[g][d], tb, lane);
+        uint32_t sc[SL::SB];
+        int zc[SL::SB];
+#pragma unroll
+        for (int sb = 0; sb < SL::SB; ++sb) {
+          sc[sb] = blk[g][d].s[sb];
+          zc[sb] = blk[g][d].z[sb];
+        }
+        load_block<BITS, HAS_ZP>(ln, grp[g], bb + D < nbk ? bb + D : nbk - 1, nunits, ushift, zp, blk[g][d]);
 #pragma unroll
         for (int sb = 0; sb < SL::SB; ++sb) {
           if (bb * SL::UB + 4 * sb >= nunits) break;   // past K (K % 128 == 0)
           uint32_t p[16];
-          dequant_unit_f16<BITS>(gather_unit<BITS>(ln, blk[g][d], sb), blk[g][d].s[sb], blk[g][d].z[sb], p);
+          dequant_unit_f16<BITS>(fetch_unit<BITS>(ln, tb, sb), sc[sb], zc[sb], p);
           acc[g] = mfma_unit(arow, l16, 32 * (bb * SL::UB + 4 * sb + q), p, acc[g]);
         }
-        load_block<BITS, HAS_ZP>(ln, grp[g], bb + D < nbk ? bb + D : nbk - 1, nunits, ushift, zp, blk[g][d]);
       }
     }
   }
@@ -419,12 +449,12 @@ __global__ __launch_bounds__(kSmallThreads) void small_fc2_kernel(
     const int bb = bk + d;
 #pragma unroll
       for (int g = 0; g < kFc2Groups; ++g) {
-        // (a group past H computes on clamped rows; its results are not stored)
+        stash_block<BITS>(blk[g][d], tb, lane);
 #pragma unroll
         for (int sb = 0; sb < SL::SB; ++sb) {
-          if (bb * SL::UB + 4 * sb >= nunits) break;   // past K (K % 128 == 0)
+          if (bb * SL::UB + 4 * sb >= nunits) break;
           uint32_t p[16];
-          dequant_unit_f16<BITS>(gather_unit<BITS>(ln, blk[g][d], sb), blk[g][d].s[sb], blk[g][d].z[sb], p);
+          dequant_unit_f16<BITS>(fetch_unit<BITS>(ln, tb, sb), blk[g][d].s[sb], blk[g][d].z[sb], p);
           acc[g] = mfma_unit(arow, l16, 32 * (bb * SL::UB + 4 * sb + q), p, acc[g]);
         }
       }
@@ -459,8 +489,8 @@ hipError_t launch_small_gemms(const Layer& L, const uint16_t* xa, const int8_t* 
   const int ushift = L.bs == 32 ? 0 : L.bs == 64 ? 1 : 2;
   const int nb1 = (I + kFc1Cols - 1) / kFc1Cols, nb2 = (H + kFc2Cols - 1) / kFc2Cols;
   const int64_t g1 = 8 * ((W.max_tiles * nb1 + 7) / 8), g2 = 8 * ((W.max_tiles * nb2 + 7) / 8);
-  const size_t lds1 = static_cast<size_t>(kSmallRows) * H * 2;
-  const size_t lds2 = static_cast<size_t>(kSmallRows) * I * 2;
+  const size_t lds1 = static_cast<size_t>(kSmallRows) * H * 2 + kSmallWaves * kTransBytes;
+  const size_t lds2 = static_cast<size_t>(kSmallRows) * I * 2 + kSmallWaves * kTransBytes;
   auto fc1 = L.fc1_zp ? small_fc1_kernel<BITS, true> : small_fc1_kernel<BITS, false>;
   auto fc2 = L.fc2_zp ? small_fc2_kernel<BITS, true> : small_fc2_kernel<BITS, false>;
   fc1<<<static_cast<unsigned>(g1), kSmallThreads, lds1, s>>>(
@@ -477,15 +507,17 @@ hipError_t launch_small_gemms(const Layer& L, const uint16_t* xa, const int8_t* 
 }  // namespace
 
 bool small_path_supported(const Layer& L) {
-  // K values in whole 128-wide blocks (four units per lane and block), and a
-  // tile's staged rows (16 x K fp16) within 128 KB of LDS
+  // K values in whole 128-wide sub-blocks, and a tile's staged rows (16 x K
+  // fp16, at most 128 KB) plus the waves' 16 KB of slices within the 160 KB
+  // of LDS
   return L.H % 128 == 0 && L.I % 128 == 0 && L.H <= 4096 && L.I <= 4096;
 }
 
 // Allow each instance the dynamic LDS its largest layer needs (beyond the
 // 64 KB default of a launch).
 hipError_t prepare_small(const Layer& L) {
-  const int b1 = static_cast<int>(kSmallRows * L.H * 2), b2 = static_cast<int>(kSmallRows * L.I * 2);
+  const int b1 = static_cast<int>(kSmallRows * L.H * 2 + kSmallWaves * kTransBytes);
+  const int b2 = static_cast<int>(kSmallRows * L.I * 2 + kSmallWaves * kTransBytes);
   const void* f1[] = {reinterpret_cast<const void*>(&small_fc1_kernel<4, false>),
                       reinterpret_cast<const void*>(&small_fc1_kernel<4, true>),
                       reinterpret_cast<const void*>(&small_fc1_kernel<3, false>),
