@@ -964,6 +964,26 @@ def test_small_path_formats(bits, bs):
     check_prefill(wl, small_layer(wl, 64), emulation=True)
 
 
+@pytest.mark.parametrize("kw,T", [
+    (dict(hidden=640, inter=640, block_size=128, num_experts=6, top_k=3), 23),
+    (dict(hidden=640, inter=640, block_size=64, num_experts=6, top_k=3, bits=2), 17),
+    (dict(hidden=384, inter=896, block_size=128, num_experts=4, top_k=2, bits=3), 11),
+    (dict(hidden=4096, inter=4096, block_size=128, num_experts=4, top_k=2), 9)])
+def test_small_path_ragged_and_largest_shapes(kw, T):
+    """Shapes whose K is not a multiple of the 256-K weight blocks (a tail
+    block with a sub-block past K), whose h columns and output rows end
+    inside a workgroup's groups (groups past I or H computed on clamped rows
+    and not stored), and the largest shape the small-batch path takes
+    (H = I = 4096: 144 KB of LDS per workgroup): against the plain oracle and
+    per element against the emulation."""
+    d = dict(kw)
+    bits = d.pop("bits", 4)
+    spec = small_spec(bits, d.pop("block_size"), **d)
+    wl = qi.make_layer(spec, T=T, seed=300 + T + spec.hidden)
+    say(f"small path H={spec.hidden} I={spec.inter} bits={bits} bs={spec.block_size} T={T}")
+    check_prefill(wl, small_layer(wl, 32), emulation=True)
+
+
 @pytest.mark.parametrize("T", [1, 3, 4])
 def test_small_path_few_tokens(T):
     """The small-batch path also computes 1..4 tokens (forced): the same
