@@ -181,6 +181,26 @@ def test_small_routing_bit_exact(kw, T):
     assert rep.ok, rep
 
 
+@pytest.mark.parametrize("E,k", [(1, 1), (8, 8), (2, 1)])
+@pytest.mark.parametrize("T", [1, 4, 9, 40, 300])
+def test_degenerate_expert_counts(E, k, T):
+    """One expert for every token (E = k = 1), every expert for every token
+    (k = E, whose routing weights are the plain softmax of all logits) and
+    top-1 of two, on each path the default dispatch takes (fused decode,
+    grouped decode, small-batch path, grouped GEMMs): routing bit-exact and
+    the output matches the oracle."""
+    spec = small_spec(4, 32, num_experts=E, top_k=k)
+    wl = qi.make_layer(spec, T=T, seed=500 + 10 * E + k + T)
+    layer = layer_for(wl, 300)
+    out, ws = run(layer, wl.tokens.x, wl.tokens.logits)
+    ids, _ = layer.routing_from_workspace(T, ws)
+    rid, _ = oracle.route(wl.tokens.logits, k)
+    assert np.array_equal(ids.cpu().numpy(), rid)
+    rep = compare(out, oracle_acc(wl))
+    say(f"E={E} k={k} T={T}: {rep}")
+    assert rep.ok, rep
+
+
 def test_routing_constructed_ties():
     wl = qi.make_workload("decode", T=64)
     l = wl.tokens.logits.clone()
