@@ -48,6 +48,11 @@
 // four rows; FC2 gives them 8 quant blocks x 2 sets of four rows. One unit of
 // 32 codes feeds eight consecutive MFMAs of one block.
 //
+// Weight codes and scales are read through buffer resources. Every load of an
+// item is issued unconditionally, so the compiler's wait counts stay static; a
+// load for an item the wave has no use for (past the end of its range) gets a
+// resource with no records, which returns zeros without touching memory.
+//
 // Exactness: each code enters as the bf16 value 1 + q/128 (its bits OR-ed
 // into the mantissa of 1.0); the block sum is then
 // sum((q - zp) * v) = 128 * D - (128 + zp) * sum(v), scaled by the fp16 block
@@ -77,6 +82,9 @@ constexpr int kFusedThreads = kFusedWaves * kWave;
 constexpr int kKeySlots = kFusedMaxExperts / kWave;   // logits per lane in the top-k
 constexpr int kMaxRoutes = kDecodeMaxTokens * kMaxTopK;
 constexpr int kMaxGroups = 256;                       // output row groups of 8 (H <= 2048)
+constexpr int kXRow = 2048 / 8 + 1;                   // 16-byte vectors per token row of x in LDS
+                                                      // (H <= 2048, padded by one vector)
+static_assert(kDecodeMaxTokens * (kXRow - 1) <= 2 * kFusedThreads, "x staging: two vectors per thread");
 constexpr int kMaxI32 = 32;                           // FC2 quant blocks staged (I <= 1024)
 constexpr int kCap1 = 32;                             // FC1 items buffered per wave (even)
 constexpr int kCap2 = 16;                             // FC2 items buffered per wave (multiple of 4)
@@ -161,6 +169,9 @@ struct FusedLds {
   uint4 ahi[kMaxI32 / 8][4][32];
   uint4 alo[kMaxI32 / 8][4][32];
   float hsum[kDecodeMaxTokens][kMaxI32];
+  // x (FC1 A operand source), token rows padded so the four tokens of a quad
+  // fall in different banks
+  uint4 xs[kDecodeMaxTokens][kXRow];
   // per-wave result buffers: h [token][2 * item + row], y [token][8 * item + row]
   float hbuf[kFusedWaves][kDecodeMaxTokens][2 * kCap1];
   float ybuf[kFusedWaves][kDecodeMaxTokens][8 * kCap2];
@@ -193,6 +204,33 @@ __device__ __forceinline__ float quad_get(float v) {
   return dpp_f<T * 0x55>(v);
 }
 
+// A raw buffer resource over `bytes` bytes at p (stride 0: offsets are byte
+// offsets, range-checked against `bytes`; 0x00020000 is the gfx9 data-format
+// word for raw dword access). bytes = 0 makes every load return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+// One unit (32 codes) at byte offset off of a resource.
+template <int BITS>
+__device__ __forceinline__ UnitWords<BITS> load_unit_rsrc(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  UnitWords<BITS> u;
+  if constexpr (BITS == 4) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    u.w[0] = v[0]; u.w[1] = v[1]; u.w[2] = v[2]; u.w[3] = v[3];
+  } else if constexpr (BITS == 2) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    u.w[0] = v[0]; u.w[1] = v[1];
+  } else {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, 0);
+    u.w[0] = v[0]; u.w[1] = v[1]; u.w[2] = v[2];
+  }
+  return u;
+}
+__device__ __forceinline__ uint32_t load_u16_rsrc(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+
 }  // namespace
 
 struct FusedArgs {
@@ -207,6 +245,7 @@ struct FusedArgs {
   int normalize;     // routing weights over the selected k (1) or over all experts (0)
   int fc1_il;        // FC1 rows interleaved: 2n gate n, 2n+1 up n
   int64_t rb1, rb2, nb1, nb2;
+  uint32_t c1_bytes, s1_bytes, c2_bytes, s2_bytes;   // sizes of c1, s1, c2, s2 (< 2^31)
   int32_t* ws_ids;
   float* ws_w;
   uint64_t* hx;      // exchange: h [route][inter]
@@ -245,7 +284,8 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
   const float zc = 128.0f + static_cast<float>(zp);
 
   // ---- loads that need no routing: token `wave`'s logits, then x (FC1 A
-  // operand); all addresses clamped in range, values masked afterwards
+  // operand), two 16-byte vectors per thread, staged in LDS once per
+  // workgroup; all addresses clamped in range, values masked afterwards
   uint16_t lg[kKeySlots];
   if (wave < T) {
 #pragma unroll
@@ -255,15 +295,12 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
     }
   }
   const int nkb1 = H / 32;
-  uint4 xraw[U1][4];
-#pragma unroll
-  for (int c = 0; c < U1; ++c) {
-    const int kb = blk + 16 * c;
-    const int kbc = kb < nkb1 ? kb : 0, tc = q4 < T ? q4 : 0;
-    const uint4* src = reinterpret_cast<const uint4*>(a.x + static_cast<int64_t>(tc) * H + 32 * kbc);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) xraw[c][q] = src[q];
-  }
+  // (a thread past the end re-reads a vector other threads also read, so no
+  // single line gets every spare thread's request)
+  const int xrow = H / 8, nx = T * xrow;   // vectors per token row, in all
+  const int xi0 = static_cast<int>(threadIdx.x), xi1 = xi0 + kFusedThreads;
+  const uint4 xv0 = reinterpret_cast<const uint4*>(a.x)[xi0 % nx];
+  const uint4 xv1 = reinterpret_cast<const uint4*>(a.x)[xi1 % nx];
   if (threadIdx.x < kDecodeMaxTokens * kFusedMaxExperts / 4)
     reinterpret_cast<uint32_t*>(&S.slot[0][0])[threadIdx.x] = 0xFFFFFFFFu;
   if (threadIdx.x < kFusedMaxExperts / 32) S.emask[threadIdx.x] = 0u;
@@ -303,6 +340,8 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
       atomicOr(&S.emask[e >> 5], 1u << (e & 31));
     }
   }
+  if (xi0 < nx) S.xs[xi0 / xrow][xi0 % xrow] = xv0;
+  if (xi1 < nx) S.xs[xi1 / xrow][xi1 % xrow] = xv1;
   __syncthreads();
   // distinct experts in ascending order: prefix of the mask words' popcounts
   if (wave == 0) {
@@ -363,21 +402,27 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
   const int bsh = (bs == 32) ? 0 : (bs == 64) ? 1 : 2;   // bs = 32 << bsh: block of unit kb
   // Loads of one item: branch-free (out-of-range quant blocks read unit 0 and
   // get a zero scale when used); scales stay raw fp16 until used.
-  auto load_fc1 = [&](int it, UnitWords<BITS> (&wv)[U1], uint32_t (&sc)[U1], uint32_t& bv,
+  // (live: the wave uses the item; otherwise its loads read nothing. it and
+  // live are wave-uniform, so the resources stay in scalar registers.)
+  auto load_fc1 = [&](int it, bool live, UnitWords<BITS> (&wv)[U1], uint32_t (&sc)[U1], uint32_t& bv,
                       uint32_t (&zv)[U1]) {
     const int e = S.dlist[it / g1];
     const int n = 2 * (it % g1) + (q4 & 1);
     const int row = a.fc1_il ? 2 * n + (q4 >> 1) : ((q4 < 2) ? n : I + n);
-    const uint8_t* rowp = a.c1 + (static_cast<int64_t>(e) * 2 * I + row) * a.rb1;
-    const uint16_t* srow = a.s1 + (static_cast<int64_t>(e) * 2 * I + row) * a.nb1;
+    const uint32_t grow = static_cast<uint32_t>(e * 2 * I + row);
+    const __amdgpu_buffer_rsrc_t rc = raw_rsrc(a.c1, live ? a.c1_bytes : 0u);
+    const __amdgpu_buffer_rsrc_t rs = raw_rsrc(a.s1, live ? a.s1_bytes : 0u);
+    const uint32_t cofs = grow * static_cast<uint32_t>(a.rb1);
+    const uint32_t sofs = grow * static_cast<uint32_t>(a.nb1);
 #pragma unroll
     for (int c = 0; c < U1; ++c) {
       const int kb = blk + 16 * c;
       const int kbc = kb < nkb1 ? kb : 0;
-      wv[c] = load_unit<BITS>(rowp + kbc * (4 * BITS));
-      sc[c] = srow[kbc >> bsh];
+      wv[c] = load_unit_rsrc<BITS>(rc, cofs + kbc * (4 * BITS));
+      sc[c] = load_u16_rsrc(rs, 2 * (sofs + (kbc >> bsh)));
     }
     if constexpr (EX) {
+      (void)live;
       bv = a.b1 ? a.b1[static_cast<int64_t>(e) * 2 * I + row] : 0u;
       const uint8_t* zrow = a.z1 ? a.z1 + (static_cast<int64_t>(e) * 2 * I + row) * a.nb1 : nullptr;
 #pragma unroll
@@ -387,18 +432,21 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
       }
     }
   };
-  auto load_fc2 = [&](int d, int q, UnitWords<BITS> (&wv)[U2], uint32_t (&sc)[U2], uint32_t& bv,
-                      uint32_t (&zv)[U2]) {
+  auto load_fc2 = [&](int d, int q, bool live, UnitWords<BITS> (&wv)[U2], uint32_t (&sc)[U2],
+                      uint32_t& bv, uint32_t (&zv)[U2]) {
     const int e = S.dlist[d];
     const int m = q * 8 + (blk >= 8 ? 4 : 0) + q4;
-    const uint8_t* rowp = a.c2 + (static_cast<int64_t>(e) * H + m) * a.rb2;
-    const uint16_t* srow = a.s2 + (static_cast<int64_t>(e) * H + m) * a.nb2;
+    const uint32_t grow = static_cast<uint32_t>(e * H + m);
+    const __amdgpu_buffer_rsrc_t rc = raw_rsrc(a.c2, live ? a.c2_bytes : 0u);
+    const __amdgpu_buffer_rsrc_t rs = raw_rsrc(a.s2, live ? a.s2_bytes : 0u);
+    const uint32_t cofs = grow * static_cast<uint32_t>(a.rb2);
+    const uint32_t sofs = grow * static_cast<uint32_t>(a.nb2);
 #pragma unroll
     for (int c = 0; c < U2; ++c) {
       const int kb = (blk & 7) + 8 * c;
       const int kbc = kb < nkb2 ? kb : 0;
-      wv[c] = load_unit<BITS>(rowp + kbc * (4 * BITS));
-      sc[c] = srow[kbc >> bsh];
+      wv[c] = load_unit_rsrc<BITS>(rc, cofs + kbc * (4 * BITS));
+      sc[c] = load_u16_rsrc(rs, 2 * (sofs + (kbc >> bsh)));
     }
     if constexpr (EX) {
       bv = a.b2 ? a.b2[static_cast<int64_t>(e) * H + m] : 0u;
@@ -412,37 +460,40 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
   };
 
   // ---- issue: the first two FC1 items, then the first two FC2 items. The
-  // loads are unconditional (a wave without items reads a valid item it
-  // never uses), so the compiler's wait counts stay exact.
+  // loads are unconditional (an item past the wave's range is a valid index
+  // whose loads read nothing), so the compiler's wait counts stay exact.
   UnitWords<BITS> w1A[U1], w1B[U1];
   uint32_t s1A[U1], s1B[U1];   // raw fp16 scales, one per register
   uint32_t b1A = 0u, b1B = 0u, z1A[U1], z1B[U1];   // raw bias and zero points (EX)
   // (sched_barrier keeps the issue order A, B, FC2 A, FC2 B that the waits
   // below count on)
   const int last1 = max(i1_1 - 1, 0);
-  load_fc1(min(i1_0, last1), w1A, s1A, b1A, z1A);
+  load_fc1(min(i1_0, last1), i1_0 < i1_1, w1A, s1A, b1A, z1A);
   __builtin_amdgcn_sched_barrier(0);
-  load_fc1(min(i1_0 + 1, last1), w1B, s1B, b1B, z1B);
+  load_fc1(min(i1_0 + 1, last1), i1_0 + 1 < i1_1, w1B, s1B, b1B, z1B);
   __builtin_amdgcn_sched_barrier(0);
   UnitWords<BITS> w2A[U2], w2B[U2];
   uint32_t s2A[U2], s2B[U2];
   uint32_t b2A = 0u, b2B = 0u, z2A[U2], z2B[U2];
   const int last2 = max(q1 - 1, 0);
-  load_fc2(dA, min(q0, last2), w2A, s2A, b2A, z2A);
-  load_fc2(dA, min(q0 + 1, last2), w2B, s2B, b2B, z2B);
+  load_fc2(dA, min(q0, last2), q0 < q1, w2A, s2A, b2A, z2A);
+  load_fc2(dA, min(q0 + 1, last2), q0 + 1 < q1, w2B, s2B, b2B, z2B);
   __builtin_amdgcn_sched_barrier(0);
 
-  // x pairs and their sums (the x loads have long completed)
+  // x pairs and their sums (x was staged in LDS before the routing's last barrier)
   uint32_t xp[U1][16];
   float sx[U1];
 #pragma unroll
   for (int c = 0; c < U1; ++c) {
-    const bool ok = (blk + 16 * c) < nkb1 && q4 < T;
+    const int kb = blk + 16 * c;
+    const bool ok = kb < nkb1 && q4 < T;
+    const int kbc = kb < nkb1 ? kb : 0, tc = q4 < T ? q4 : 0;
     uint32_t v[16];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      v[4 * q] = ok ? xraw[c][q].x : 0u; v[4 * q + 1] = ok ? xraw[c][q].y : 0u;
-      v[4 * q + 2] = ok ? xraw[c][q].z : 0u; v[4 * q + 3] = ok ? xraw[c][q].w : 0u;
+      const uint4 xq = S.xs[tc][4 * kbc + q];
+      v[4 * q] = ok ? xq.x : 0u; v[4 * q + 1] = ok ? xq.y : 0u;
+      v[4 * q + 2] = ok ? xq.z : 0u; v[4 * q + 3] = ok ? xq.w : 0u;
     }
     float sum = 0.0f;
 #pragma unroll
@@ -512,9 +563,9 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
     const int c1 = min(c0 + kCap1, i1_1);
     for (int it = c0; it < c1; it += 2) {
       fc1_item(w1A, s1A, b1A, z1A, it - c0);
-      load_fc1(min(it + 2, last1), w1A, s1A, b1A, z1A);
+      load_fc1(min(it + 2, last1), it + 2 < i1_1, w1A, s1A, b1A, z1A);
       if (it + 1 < c1) fc1_item(w1B, s1B, b1B, z1B, it + 1 - c0);
-      load_fc1(min(it + 3, last1), w1B, s1B, b1B, z1B);
+      load_fc1(min(it + 3, last1), it + 3 < i1_1, w1B, s1B, b1B, z1B);
     }
     // write this chunk's h (coalesced along n per token)
     const int ni2 = 2 * (c1 - c0);
@@ -531,8 +582,8 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
   UnitWords<BITS> w2C[U2], w2D[U2];
   uint32_t s2C[U2], s2D[U2];
   uint32_t b2C = 0u, b2D = 0u, z2C[U2], z2D[U2];
-  load_fc2(dA, min(q0 + 2, last2), w2C, s2C, b2C, z2C);
-  load_fc2(dA, min(q0 + 3, last2), w2D, s2D, b2D, z2D);
+  load_fc2(dA, min(q0 + 2, last2), q0 + 2 < q1, w2C, s2C, b2C, z2C);
+  load_fc2(dA, min(q0 + 3, last2), q0 + 3 < q1, w2D, s2D, b2D, z2D);
 
   // ---- phase 2: FC2 of this workgroup's expert(s)
   for (int d = dA; d < dB; ++d) {
@@ -618,10 +669,10 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
       for (int t = 0; t < kDecodeMaxTokens; ++t) corr2[c][t] = ok ? (EX ? 1.0f : zc) * S.hsum[t][kb] : 0.0f;
     }
     if (d != dA) {
-      load_fc2(d, q0, w2A, s2A, b2A, z2A);
-      load_fc2(d, min(q0 + 1, last2), w2B, s2B, b2B, z2B);
-      load_fc2(d, min(q0 + 2, last2), w2C, s2C, b2C, z2C);
-      load_fc2(d, min(q0 + 3, last2), w2D, s2D, b2D, z2D);
+      load_fc2(d, q0, true, w2A, s2A, b2A, z2A);
+      load_fc2(d, min(q0 + 1, last2), q0 + 1 < q1, w2B, s2B, b2B, z2B);
+      load_fc2(d, min(q0 + 2, last2), q0 + 2 < q1, w2C, s2C, b2C, z2C);
+      load_fc2(d, min(q0 + 3, last2), q0 + 3 < q1, w2D, s2D, b2D, z2D);
     }
     auto fc2_item = [&](const UnitWords<BITS> (&wv)[U2], const uint32_t (&sc)[U2], uint32_t bv,
                         const uint32_t (&zv)[U2], int li) {
@@ -663,13 +714,13 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
       const int c1 = min(c0 + kCap2, q1);
       for (int q = c0; q < c1; q += 4) {
         fc2_item(w2A, s2A, b2A, z2A, q - c0);
-        load_fc2(d, min(q + 4, last2), w2A, s2A, b2A, z2A);
+        load_fc2(d, min(q + 4, last2), q + 4 < q1, w2A, s2A, b2A, z2A);
         if (q + 1 < c1) fc2_item(w2B, s2B, b2B, z2B, q + 1 - c0);
-        load_fc2(d, min(q + 5, last2), w2B, s2B, b2B, z2B);
+        load_fc2(d, min(q + 5, last2), q + 5 < q1, w2B, s2B, b2B, z2B);
         if (q + 2 < c1) fc2_item(w2C, s2C, b2C, z2C, q + 2 - c0);
-        load_fc2(d, min(q + 6, last2), w2C, s2C, b2C, z2C);
+        load_fc2(d, min(q + 6, last2), q + 6 < q1, w2C, s2C, b2C, z2C);
         if (q + 3 < c1) fc2_item(w2D, s2D, b2D, z2D, q + 3 - c0);
-        load_fc2(d, min(q + 7, last2), w2D, s2D, b2D, z2D);
+        load_fc2(d, min(q + 7, last2), q + 7 < q1, w2D, s2D, b2D, z2D);
       }
       // write this chunk's y (coalesced along m per token)
       const int nm = 8 * (c1 - c0);
@@ -781,7 +832,10 @@ bool fused_decode_supported(const Layer& L) {
   return (L.act_bf16 || L.act == kActF16) && fused_u1(L) > 0 && (!ex || fused_u2(L) <= 3) &&
          fused_u2(L) > 0 &&
          L.H % 8 == 0 && L.I % 2 == 0 &&
-         L.E <= kFusedMaxExperts && L.k <= kMaxTopK && fused_kernel_for(L) != nullptr;
+         L.E <= kFusedMaxExperts && L.k <= kMaxTopK && fused_kernel_for(L) != nullptr &&
+         // buffer resources take byte sizes below 2^31
+         L.E * 2 * L.I * L.fc1_row_bytes < (int64_t{1} << 31) &&
+         L.E * L.H * L.fc2_row_bytes < (int64_t{1} << 31);
 }
 
 int fused_decode_grid(const Layer& L, int device) {
@@ -840,6 +894,10 @@ hipError_t launch_decode_fused(const Layer& L, const void* x, const void* logits
   fa.rb2 = L.fc2_row_bytes;
   fa.nb1 = L.fc1_nblk;
   fa.nb2 = L.fc2_nblk;
+  fa.c1_bytes = static_cast<uint32_t>(L.E * 2 * L.I * L.fc1_row_bytes);
+  fa.s1_bytes = static_cast<uint32_t>(L.E * 2 * L.I * L.fc1_nblk * 2);
+  fa.c2_bytes = static_cast<uint32_t>(L.E * L.H * L.fc2_row_bytes);
+  fa.s2_bytes = static_cast<uint32_t>(L.E * L.H * L.fc2_nblk * 2);
   fa.b1 = static_cast<const uint16_t*>(L.fc1_bias);
   fa.b2 = static_cast<const uint16_t*>(L.fc2_bias);
   fa.z1 = L.fc1_zp;
