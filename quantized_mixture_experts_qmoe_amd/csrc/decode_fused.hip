@@ -15,11 +15,14 @@
 //      the distinct experts, in ascending expert order, come from an LDS
 //      bitmask;
 //   1. FC1 + SwiGLU: items of two gate rows and the two matching up rows of
-//      one expert, dealt to the waves in contiguous ranges. Each wave issues
+//      one expert, dealt to the workgroups in contiguous ranges; inside a
+//      workgroup each wave starts with two items and then claims the next
+//      unclaimed one from an LDS counter whenever it finishes one, so waves
+//      that the memory system serves sooner take more items. Each wave issues
 //      the loads of its first two FC1 items and its first two FC2 items
 //      before computing anything, keeps two items in flight, buffers its h
-//      values in LDS and writes them out once; right after its last FC1 item
-//      it issues the loads of its third and fourth FC2 items;
+//      values in LDS and writes them out in batches; right after its last FC1
+//      item it issues the loads of its third and fourth FC2 items;
 //   2. FC2: a workgroup works on one expert (or, with more experts than
 //      workgroups, on whole experts in turn). It stages the expert's h in LDS
 //      as bf16 hi/lo pairs, waiting for each value to arrive, and its waves
@@ -161,6 +164,8 @@ struct FusedLds {
   int8_t slot[kDecodeMaxTokens][kFusedMaxExperts];    // (token, expert) -> slot, or -1
   int32_t dlist[kMaxRoutes];                          // distinct index -> expert (ascending)
   int nd;
+  int next1;                                          // next unclaimed FC1 item of the workgroup
+  int32_t hitem[kFusedWaves][kCap1];                  // FC1 item of each buffered h pair
   // FC2 A operand of one expert, in register order: unit c, 16-byte chunk j
   // (pairs 4j..4j+3), lane l (token l & 3, quant block (l >> 2) + 8c; lanes
   // l and l + 32 use the same slot), so a wave's ds_read_b128 are bank-conflict
@@ -358,7 +363,12 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
       S.dlist[pos++] = lane * 32 + (__ffs(m) - 1);
       m &= m - 1u;
     }
-    if (lane == kFusedMaxExperts / 32 - 1) S.nd = incl;
+    if (lane == kFusedMaxExperts / 32 - 1) {
+      S.nd = incl;
+      // the workgroup's first FC1 items are dealt statically, two per wave
+      const uint32_t n1 = static_cast<uint32_t>(incl) * static_cast<uint32_t>(I / 2);
+      S.next1 = static_cast<int>(n1 * blockIdx.x / gridDim.x) + 2 * kFusedWaves;
+    }
   }
   __syncthreads();
   const int D = __builtin_amdgcn_readfirstlane(S.nd);
@@ -369,14 +379,14 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
     }
 
   // ---- work ranges
-  // FC1: items (expert d, row pair p), contiguous per wave over the grid
+  // FC1: items (expert d, row pair p), contiguous per workgroup over the grid
   const int g1 = I / 2;
   const int n1 = D * g1;
-  // (unsigned 32-bit range arithmetic: n1 <= 128 * 512 and gw < 8192, so
-  // every product fits, and the divisions stay short scalar sequences)
-  const uint32_t un1 = static_cast<uint32_t>(n1), ugw = static_cast<uint32_t>(gw), uNW = static_cast<uint32_t>(NW);
-  const int i1_0 = static_cast<int>(un1 * ugw / uNW);
-  const int i1_1 = static_cast<int>(un1 * (ugw + 1) / uNW);
+  // (unsigned 32-bit range arithmetic: n1 <= 32 * 512 and blockIdx.x < 1024,
+  // so every product fits, and the divisions stay short scalar sequences)
+  const uint32_t un1 = static_cast<uint32_t>(n1), uNG = static_cast<uint32_t>(gridDim.x);
+  const int w1_0 = static_cast<int>(un1 * blockIdx.x / uNG);
+  const int w1_1 = static_cast<int>(un1 * (blockIdx.x + 1) / uNG);
   // FC2: items (expert d, group q of 8 output rows); a workgroup owns a slice
   // of one expert when there are at least as many workgroups as experts,
   // otherwise whole experts [dA, dB)
@@ -467,10 +477,11 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
   uint32_t b1A = 0u, b1B = 0u, z1A[U1], z1B[U1];   // raw bias and zero points (EX)
   // (sched_barrier keeps the issue order A, B, FC2 A, FC2 B that the waits
   // below count on)
-  const int last1 = max(i1_1 - 1, 0);
-  load_fc1(min(i1_0, last1), i1_0 < i1_1, w1A, s1A, b1A, z1A);
+  const int last1 = max(w1_1 - 1, 0);
+  int itA = w1_0 + wave, itB = w1_0 + kFusedWaves + wave;   // (itA past the end => itB too)
+  load_fc1(min(itA, last1), itA < w1_1, w1A, s1A, b1A, z1A);
   __builtin_amdgcn_sched_barrier(0);
-  load_fc1(min(i1_0 + 1, last1), i1_0 + 1 < i1_1, w1B, s1B, b1B, z1B);
+  load_fc1(min(itB, last1), itB < w1_1, w1B, s1B, b1B, z1B);
   __builtin_amdgcn_sched_barrier(0);
   UnitWords<BITS> w2A[U2], w2B[U2];
   uint32_t s2A[U2], s2B[U2];
@@ -558,26 +569,46 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
       for (int t = 0; t < kDecodeMaxTokens; ++t) S.hbuf[wave][t][2 * li + lane] = silu_mul(acc[t], up[t]);
   };
 
-  // ---- phase 1: FC1 + SwiGLU, two items in flight, results flushed per chunk
-  for (int c0 = i1_0; c0 < i1_1; c0 += kCap1) {
-    const int c1 = min(c0 + kCap1, i1_1);
-    for (int it = c0; it < c1; it += 2) {
-      fc1_item(w1A, s1A, b1A, z1A, it - c0);
-      load_fc1(min(it + 2, last1), it + 2 < i1_1, w1A, s1A, b1A, z1A);
-      if (it + 1 < c1) fc1_item(w1B, s1B, b1B, z1B, it + 1 - c0);
-      load_fc1(min(it + 3, last1), it + 3 < i1_1, w1B, s1B, b1B, z1B);
-    }
-    // write this chunk's h (coalesced along n per token)
-    const int ni2 = 2 * (c1 - c0);
+  // ---- phase 1: FC1 + SwiGLU, two items in flight, claimed one at a time;
+  // results buffered per wave and written out in batches
+  auto claim = [&]() -> int {   // the workgroup's next FC1 item (wave-uniform)
+    int v = 0;
+    if (lane == 0) v = atomicAdd(&S.next1, 1);
+    return __builtin_amdgcn_readfirstlane(v);
+  };
+  auto flush_h = [&](int nb) {  // write the nb buffered items' h (pairs contiguous)
+    const int ni2 = 2 * nb;
     for (int i = lane; i < T * ni2; i += kWave) {
       const int t = i / ni2, nl = i % ni2;
-      const int it = c0 + nl / 2, d = it / g1;
+      const int it = S.hitem[wave][nl >> 1], d = it / g1;
       const int slot = S.slot[t][S.dlist[d]];
       if (slot >= 0)
         put_tagged(a.hx + static_cast<int64_t>(t * k + slot) * I + 2 * (it % g1) + (nl & 1),
                    S.hbuf[wave][t][nl], a.epoch);
     }
+  };
+  int nbuf = 0;   // items in this wave's h buffer
+  while (itA < w1_1) {
+    fc1_item(w1A, s1A, b1A, z1A, nbuf);
+    if (lane == 0) S.hitem[wave][nbuf] = itA;
+    ++nbuf;
+    const int nA = claim();
+    load_fc1(min(nA, last1), nA < w1_1, w1A, s1A, b1A, z1A);
+    if (itB < w1_1) {
+      fc1_item(w1B, s1B, b1B, z1B, nbuf);
+      if (lane == 0) S.hitem[wave][nbuf] = itB;
+      ++nbuf;
+    }
+    const int nB = claim();   // (claimed after nA: nA past the end => nB too)
+    load_fc1(min(nB, last1), nB < w1_1, w1B, s1B, b1B, z1B);
+    itA = nA;
+    itB = nB;
+    if (nbuf + 2 > kCap1) {
+      flush_h(nbuf);
+      nbuf = 0;
+    }
   }
+  flush_h(nbuf);
   // the third and fourth FC2 items of this wave (FC1's registers are free now)
   UnitWords<BITS> w2C[U2], w2D[U2];
   uint32_t s2C[U2], s2D[U2];
