@@ -609,12 +609,15 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
     }
   }
   flush_h(nbuf);
-  // the third and fourth FC2 items of this wave (FC1's registers are free now)
+  // the third and fourth FC2 items of this wave (FC1's registers are free
+  // now). Loads past the wave's range are not issued at all from here on:
+  // nothing later is timed on them, and a wave that skips them leaves the
+  // memory pipeline to the waves still streaming.
   UnitWords<BITS> w2C[U2], w2D[U2];
   uint32_t s2C[U2], s2D[U2];
   uint32_t b2C = 0u, b2D = 0u, z2C[U2], z2D[U2];
-  load_fc2(dA, min(q0 + 2, last2), q0 + 2 < q1, w2C, s2C, b2C, z2C);
-  load_fc2(dA, min(q0 + 3, last2), q0 + 3 < q1, w2D, s2D, b2D, z2D);
+  if (q0 + 2 < q1) load_fc2(dA, q0 + 2, true, w2C, s2C, b2C, z2C);
+  if (q0 + 3 < q1) load_fc2(dA, q0 + 3, true, w2D, s2D, b2D, z2D);
 
   // ---- phase 2: FC2 of this workgroup's expert(s)
   for (int d = dA; d < dB; ++d) {
@@ -701,9 +704,9 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
     }
     if (d != dA) {
       load_fc2(d, q0, true, w2A, s2A, b2A, z2A);
-      load_fc2(d, min(q0 + 1, last2), q0 + 1 < q1, w2B, s2B, b2B, z2B);
-      load_fc2(d, min(q0 + 2, last2), q0 + 2 < q1, w2C, s2C, b2C, z2C);
-      load_fc2(d, min(q0 + 3, last2), q0 + 3 < q1, w2D, s2D, b2D, z2D);
+      if (q0 + 1 < q1) load_fc2(d, q0 + 1, true, w2B, s2B, b2B, z2B);
+      if (q0 + 2 < q1) load_fc2(d, q0 + 2, true, w2C, s2C, b2C, z2C);
+      if (q0 + 3 < q1) load_fc2(d, q0 + 3, true, w2D, s2D, b2D, z2D);
     }
     auto fc2_item = [&](const UnitWords<BITS> (&wv)[U2], const uint32_t (&sc)[U2], uint32_t bv,
                         const uint32_t (&zv)[U2], int li) {
@@ -745,13 +748,13 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
       const int c1 = min(c0 + kCap2, q1);
       for (int q = c0; q < c1; q += 4) {
         fc2_item(w2A, s2A, b2A, z2A, q - c0);
-        load_fc2(d, min(q + 4, last2), q + 4 < q1, w2A, s2A, b2A, z2A);
+        if (q + 4 < q1) load_fc2(d, q + 4, true, w2A, s2A, b2A, z2A);
         if (q + 1 < c1) fc2_item(w2B, s2B, b2B, z2B, q + 1 - c0);
-        load_fc2(d, min(q + 5, last2), q + 5 < q1, w2B, s2B, b2B, z2B);
+        if (q + 5 < q1) load_fc2(d, q + 5, true, w2B, s2B, b2B, z2B);
         if (q + 2 < c1) fc2_item(w2C, s2C, b2C, z2C, q + 2 - c0);
-        load_fc2(d, min(q + 6, last2), q + 6 < q1, w2C, s2C, b2C, z2C);
+        if (q + 6 < q1) load_fc2(d, q + 6, true, w2C, s2C, b2C, z2C);
         if (q + 3 < c1) fc2_item(w2D, s2D, b2D, z2D, q + 3 - c0);
-        load_fc2(d, min(q + 7, last2), q + 7 < q1, w2D, s2D, b2D, z2D);
+        if (q + 7 < q1) load_fc2(d, q + 7, true, w2D, s2D, b2D, z2D);
       }
       // write this chunk's y (coalesced along m per token)
       const int nm = 8 * (c1 - c0);
