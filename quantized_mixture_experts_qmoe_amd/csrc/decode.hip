@@ -18,11 +18,11 @@
 // the combine ("[CUDA] Add MoEPacked CPU/GPU hybrid offload and consolidate
 // QMoE/GGUF offload optimizations", Key Changes item 4).
 //
-// Arithmetic: codes are turned into bf16 pairs 1 + q/128 (exact) and dotted
+// Arithmetic: codes are turned into bf16 pairs 128 + q (exact) and dotted
 // with bf16 activations by v_dot2_f32_bf16 into an fp32 accumulator that
-// starts at -(1 + zp/128) * sum(x); the block result is then
-// sum((q - zp) * x) / 128, scaled by 128 * s. fp32 activations (and the fp32
-// FC2 input h) use plain fp32 FMAs on the integer codes instead.
+// starts at -(128 + zp) * sum(x); the block result is then
+// sum((q - zp) * x), scaled by s. fp32 activations (and the fp32 FC2 input
+// h) use plain fp32 FMAs on the integer codes instead.
 #include "device.h"
 #include "internal.h"
 
@@ -42,7 +42,7 @@ struct XFloats {
   float sum[UPL];
 };
 
-// sum((q - zp) * x) / 128 over one unit, bf16 activations.
+// sum((q - zp) * x) over one unit, bf16 activations.
 template <int BITS>
 __device__ __forceinline__ float unit_dot_pairs(const uint32_t (&wp)[16], const uint32_t (&xp)[16],
                                                 float corr) {
@@ -188,14 +188,13 @@ __global__ __launch_bounds__(256) void decode_fc1_kernel(
             gp[p] = unit_pair<BITS>(gw[i], p);
             upp[p] = unit_pair<BITS>(uw[i], p);
           }
-          const float gsc = 128.0f * gs[i], usc = 128.0f * us[i];
 #pragma unroll
           for (int t = 0; t < kDecodeMaxTokens; ++t) {
             if (slot[t] < 0) continue;
-            const float gc = -(1.0f + static_cast<float>(gz[i]) * (1.0f / 128.0f)) * xp[t].sum[i];
-            const float uc = -(1.0f + static_cast<float>(uz[i]) * (1.0f / 128.0f)) * xp[t].sum[i];
-            g[t] = fmaf(gsc, unit_dot_pairs<BITS>(gp, xp[t].p[i], gc), g[t]);
-            up[t] = fmaf(usc, unit_dot_pairs<BITS>(upp, xp[t].p[i], uc), up[t]);
+            const float gc = -(128.0f + static_cast<float>(gz[i])) * xp[t].sum[i];
+            const float uc = -(128.0f + static_cast<float>(uz[i])) * xp[t].sum[i];
+            g[t] = fmaf(gs[i], unit_dot_pairs<BITS>(gp, xp[t].p[i], gc), g[t]);
+            up[t] = fmaf(us[i], unit_dot_pairs<BITS>(upp, xp[t].p[i], uc), up[t]);
           }
         } else {
 #pragma unroll

@@ -56,11 +56,13 @@
 // load for an item the wave has no use for (past the end of its range) gets a
 // resource with no records, which returns zeros without touching memory.
 //
-// Exactness: each code enters as the bf16 value 1 + q/128 (its bits OR-ed
-// into the mantissa of 1.0); the block sum is then
-// sum((q - zp) * v) = 128 * D - (128 + zp) * sum(v), scaled by the fp16 block
-// scale in fp32. x is bf16 and exact; the fp32 h of FC2 enters as bf16 hi + lo
-// (16 significant bits) through two MFMAs into the same accumulator.
+// Exactness: each code enters as the bf16 value 128 + q (the code is the low
+// mantissa byte of 128.0); the block sum is then
+// sum((q - zp) * v) = D - (128 + zp) * sum(v), scaled by the fp16 block scale
+// in fp32. x is bf16 and exact; the fp32 h of FC2 enters as bf16 hi + lo
+// (16 significant bits) through two MFMAs into the same accumulator. With
+// fp16 activations FC1's codes enter as fp16 1 + q/128 instead, and the
+// block sum is 128 * D - (128 + zp) * sum(v).
 //
 // Semantics: SwiGLU experts, fc1 rows = 2 * inter ("[CUDA/CPU] Add AVX2 INT4
 // cold-expert kernel and zero-cold doorbell short-circuit for QMoE offload",
@@ -543,13 +545,14 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
         dv = F16 ? mfma4_f16(xp[c][2 * m], xp[c][2 * m + 1], wp[2 * m], wp[2 * m + 1], dv)
                  : mfma4(xp[c][2 * m], xp[c][2 * m + 1], wp[2 * m], wp[2 * m + 1], dv);
       const float s = (blk + 16 * c) < nkb1 ? half_to_f32(static_cast<uint16_t>(sc[c])) : 0.0f;
-      const float s128 = 128.0f * s;
+      // (bf16 codes enter as 128 + q, fp16 codes as 1 + q/128)
+      const float sw = F16 ? 128.0f * s : s;
       // (with EX: the same product (128 + zp) * sum(x) as the scalar path
       // forms once, so a tensor holding the scalar gives identical bits)
       const float zcl = 128.0f + static_cast<float>(zv[c]);
 #pragma unroll
       for (int t = 0; t < kDecodeMaxTokens; ++t)
-        acc[t] = fmaf(s128, dv[t], fmaf(-s, EX ? zcl * corr1[c][t] : corr1[c][t], acc[t]));
+        acc[t] = fmaf(sw, dv[t], fmaf(-s, EX ? zcl * corr1[c][t] : corr1[c][t], acc[t]));
     }
     // sum over the 16 blocks: lanes 0..3 end with rows 0..3 (gate n, gate
     // n+1, up n, up n+1); lanes 0 and 1 then take the up sums of lanes 2, 3
@@ -723,11 +726,10 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
           dv = mfma4(hlo[c][2 * m], hlo[c][2 * m + 1], wp[2 * m], wp[2 * m + 1], dv);
         }
         const float s = ((blk & 7) + 8 * c) < nkb2 ? half_to_f32(static_cast<uint16_t>(sc[c])) : 0.0f;
-        const float s128 = 128.0f * s;
         const float zcl = 128.0f + static_cast<float>(zv[c]);
 #pragma unroll
         for (int t = 0; t < kDecodeMaxTokens; ++t)
-          acc[t] = fmaf(s128, dv[t], fmaf(-s, EX ? zcl * corr2[c][t] : corr2[c][t], acc[t]));
+          acc[t] = fmaf(s, dv[t], fmaf(-s, EX ? zcl * corr2[c][t] : corr2[c][t], acc[t]));
       }
       // sum over the 8 quant blocks of each half wave: lanes 0..3 end with
       // rows 0..3 of the item, lanes 32..35 with rows 4..7

@@ -2,7 +2,7 @@
 //
 //   out_f32[n][k]  = (q - zp) * s as the decode GEMV reads it (zp the scalar
 //                    zero point or the row's per-block code): the code comes
-//                    back out of the bf16 pair 1 + q/128 that unit_pair builds
+//                    back out of the bf16 pair 128 + q that unit_pair builds
 //                    (exact), placed at the code index pair_a/pair_b name;
 //   out_f16[n][k]  = the fp16 operand fp16((q - zp) * s) the batched paths
 //                    feed the matrix cores, from the same routine
@@ -37,8 +37,8 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
 #pragma unroll
     for (int p = 0; p < 16; ++p) {
       const uint32_t pr = unit_pair<BITS>(w, p);
-      const float qa = (bf16_to_f32(pr & 0xFFFFu) - 1.0f) * 128.0f;
-      const float qb = (bf16_to_f32(pr >> 16) - 1.0f) * 128.0f;
+      const float qa = bf16_to_f32(pr & 0xFFFFu) - 128.0f;
+      const float qb = bf16_to_f32(pr >> 16) - 128.0f;
       out_f32[base + pair_a(BITS, p)] = (qa - static_cast<float>(zp)) * s;
       out_f32[base + pair_b(BITS, p)] = (qb - static_cast<float>(zp)) * s;
     }

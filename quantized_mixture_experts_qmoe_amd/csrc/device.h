@@ -99,11 +99,13 @@ __device__ __forceinline__ uint32_t unit_code(const UnitWords<BITS>& u, int i) {
   return ((u.w[d] >> o) | (u.w[d + 1] << (32 - o))) & mask;
 }
 
-// Pair p (0..15) of a unit, as two bf16 values 1 + q_a/128 (low half) and
-// 1 + q_b/128 (high half): the code is OR-ed into the low mantissa bits of
-// bf16 1.0 (0x3F80), which is exact for q < 128. pair_a/pair_b name the code
-// indices so the activations can be paired the same way. INT4 and INT2 pair
-// codes 16 bits apart so one shift and one AND-OR make a pair.
+// Pair p (0..15) of a unit, as two bf16 values 128 + q_a (low half) and
+// 128 + q_b (high half): the code is the low mantissa byte of bf16 128.0
+// (0x4300), which is exact for q < 128 (the ulp at 128 is 1). pair_a/pair_b
+// name the code indices so the activations can be paired the same way. INT4
+// and INT2 pair codes 16 bits apart, i.e. two bytes apart once each byte
+// holds one code: a mask (and a shift) per word puts one code in each byte,
+// and one byte permute per pair inserts the 0x43 exponent bytes.
 __host__ __device__ constexpr int pair_a(int bits, int p) {
   return bits == 4 ? 8 * (p / 4) + (p % 4) : bits == 2 ? 16 * (p / 8) + (p % 8) : 2 * p;
 }
@@ -113,12 +115,24 @@ __host__ __device__ constexpr int pair_b(int bits, int p) {
 
 template <int BITS>
 __device__ __forceinline__ uint32_t unit_pair(const UnitWords<BITS>& u, int p) {
+  // v_perm_b32 picks bytes of {0x43434343 (bytes 4-7), codes (bytes 0-3)}:
+  // selector 0x04020400 makes (0x4300 | byte 0, 0x4300 | byte 2), 0x04030401
+  // the same from bytes 1 and 3
+  constexpr uint32_t kExp = 0x43434343u, kSel02 = 0x04020400u, kSel13 = 0x04030401u;
   if constexpr (BITS == 4) {
-    return ((u.w[p >> 2] >> (4 * (p & 3))) & 0x000F000Fu) | 0x3F803F80u;
+    // nibbles j and j + 4 of word p / 4 (j = p % 4): the even nibbles are the
+    // bytes of w & 0x0F0F0F0F, the odd ones those of (w >> 4) & 0x0F0F0F0F
+    const uint32_t w = u.w[p >> 2];
+    const uint32_t f = (p & 1) ? ((w >> 4) & 0x0F0F0F0Fu) : (w & 0x0F0F0F0Fu);
+    return __builtin_amdgcn_perm(kExp, f, (p & 2) ? kSel13 : kSel02);
   } else if constexpr (BITS == 2) {
-    return ((u.w[p >> 3] >> (2 * (p & 7))) & 0x00030003u) | 0x3F803F80u;
+    // fields j and j + 8 of word p / 8 (j = p % 8): field 4b + i is byte b of
+    // (w >> 2i) & 0x03030303
+    const uint32_t w = u.w[p >> 3];
+    const uint32_t f = (w >> (2 * (p & 3))) & 0x03030303u;
+    return __builtin_amdgcn_perm(kExp, f, (p & 4) ? kSel13 : kSel02);
   } else {
-    return unit_code<3>(u, 2 * p) | (unit_code<3>(u, 2 * p + 1) << 16) | 0x3F803F80u;
+    return unit_code<3>(u, 2 * p) | (unit_code<3>(u, 2 * p + 1) << 16) | 0x43004300u;
   }
 }
 
