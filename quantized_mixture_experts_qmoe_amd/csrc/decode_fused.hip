@@ -612,15 +612,14 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
     }
   }
   flush_h(nbuf);
-  // the third and fourth FC2 items of this wave (FC1's registers are free
-  // now). Loads past the wave's range are not issued at all from here on:
-  // nothing later is timed on them, and a wave that skips them leaves the
-  // memory pipeline to the waves still streaming.
+  // the third and fourth FC2 items of this wave, loaded once h is staged
+  // (the waits on h's entries would otherwise also wait for them: loads
+  // complete in order). Loads past the wave's range are not issued at all
+  // from here on: nothing later is timed on them, and a wave that skips
+  // them leaves the memory pipeline to the waves still streaming.
   UnitWords<BITS> w2C[U2], w2D[U2];
   uint32_t s2C[U2], s2D[U2];
   uint32_t b2C = 0u, b2D = 0u, z2C[U2], z2D[U2];
-  if (q0 + 2 < q1) load_fc2(dA, q0 + 2, true, w2C, s2C, b2C, z2C);
-  if (q0 + 3 < q1) load_fc2(dA, q0 + 3, true, w2D, s2D, b2D, z2D);
 
   // ---- phase 2: FC2 of this workgroup's expert(s)
   for (int d = dA; d < dB; ++d) {
@@ -689,6 +688,10 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
     }
     __syncthreads();
     if (q0 >= q1) continue;
+    if (d == dA) {
+      if (q0 + 2 < q1) load_fc2(dA, q0 + 2, true, w2C, s2C, b2C, z2C);
+      if (q0 + 3 < q1) load_fc2(dA, q0 + 3, true, w2D, s2D, b2D, z2D);
+    }
     // this wave's A operand for expert d
     uint32_t hhi[U2][16], hlo[U2][16];
     float corr2[U2][kDecodeMaxTokens];
