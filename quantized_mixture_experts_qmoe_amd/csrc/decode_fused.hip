@@ -164,9 +164,9 @@ struct FusedLds {
   float w[kMaxRoutes];                                // routing weight of route r
   uint32_t emask[kFusedMaxExperts / 32];              // experts selected by any token
   int8_t slot[kDecodeMaxTokens][kFusedMaxExperts];    // (token, expert) -> slot, or -1
-  int32_t dlist[kMaxRoutes];                          // distinct index -> expert (ascending)
-  int nd;
-  int next1;                                          // next unclaimed FC1 item of the workgroup
+  int32_t dlist[kFusedWaves][kMaxRoutes];             // distinct index -> expert (ascending),
+                                                      // one copy per wave
+  int next1;                                          // FC1 items claimed past the static ones
   int32_t hitem[kFusedWaves][kCap1];                  // FC1 item of each buffered h pair
   // FC2 A operand of one expert, in register order: unit c, 16-byte chunk j
   // (pairs 4j..4j+3), lane l (token l & 3, quant block (l >> 2) + 8c; lanes
@@ -311,6 +311,7 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
   if (threadIdx.x < kDecodeMaxTokens * kFusedMaxExperts / 4)
     reinterpret_cast<uint32_t*>(&S.slot[0][0])[threadIdx.x] = 0xFFFFFFFFu;
   if (threadIdx.x < kFusedMaxExperts / 32) S.emask[threadIdx.x] = 0u;
+  if (threadIdx.x == 0) S.next1 = 0;
   __syncthreads();
 
   // ---- routing: wave t selects token t's experts
@@ -350,8 +351,11 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
   if (xi0 < nx) S.xs[xi0 / xrow][xi0 % xrow] = xv0;
   if (xi1 < nx) S.xs[xi1 / xrow][xi1 % xrow] = xv1;
   __syncthreads();
-  // distinct experts in ascending order: prefix of the mask words' popcounts
-  if (wave == 0) {
+  // distinct experts in ascending order (prefix of the mask words'
+  // popcounts), built by every wave into its own copy, so no barrier waits
+  // for one wave to build it; LDS accesses of a wave complete in order
+  int D;
+  {
     uint32_t m = (lane < (E + 31) / 32) ? S.emask[lane] : 0u;
     const int pc = __popc(m);
     int incl = pc;
@@ -362,18 +366,11 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
     }
     int pos = incl - pc;
     while (m) {
-      S.dlist[pos++] = lane * 32 + (__ffs(m) - 1);
+      S.dlist[wave][pos++] = lane * 32 + (__ffs(m) - 1);
       m &= m - 1u;
     }
-    if (lane == kFusedMaxExperts / 32 - 1) {
-      S.nd = incl;
-      // the workgroup's first FC1 items are dealt statically, two per wave
-      const uint32_t n1 = static_cast<uint32_t>(incl) * static_cast<uint32_t>(I / 2);
-      S.next1 = static_cast<int>(n1 * blockIdx.x / gridDim.x) + 2 * kFusedWaves;
-    }
+    D = __builtin_amdgcn_readlane(incl, kFusedMaxExperts / 32 - 1);
   }
-  __syncthreads();
-  const int D = __builtin_amdgcn_readfirstlane(S.nd);
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i < R; i += kFusedThreads) {
       a.ws_ids[i] = S.ids[i];
@@ -418,7 +415,7 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
   // live are wave-uniform, so the resources stay in scalar registers.)
   auto load_fc1 = [&](int it, bool live, UnitWords<BITS> (&wv)[U1], uint32_t (&sc)[U1], uint32_t& bv,
                       uint32_t (&zv)[U1]) {
-    const int e = S.dlist[it / g1];
+    const int e = S.dlist[wave][it / g1];
     const int n = 2 * (it % g1) + (q4 & 1);
     const int row = a.fc1_il ? 2 * n + (q4 >> 1) : ((q4 < 2) ? n : I + n);
     const uint32_t grow = static_cast<uint32_t>(e * 2 * I + row);
@@ -446,7 +443,7 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
   };
   auto load_fc2 = [&](int d, int q, bool live, UnitWords<BITS> (&wv)[U2], uint32_t (&sc)[U2],
                       uint32_t& bv, uint32_t (&zv)[U2]) {
-    const int e = S.dlist[d];
+    const int e = S.dlist[wave][d];
     const int m = q * 8 + (blk >= 8 ? 4 : 0) + q4;
     const uint32_t grow = static_cast<uint32_t>(e * H + m);
     const __amdgpu_buffer_rsrc_t rc = raw_rsrc(a.c2, live ? a.c2_bytes : 0u);
@@ -577,14 +574,14 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
   auto claim = [&]() -> int {   // the workgroup's next FC1 item (wave-uniform)
     int v = 0;
     if (lane == 0) v = atomicAdd(&S.next1, 1);
-    return __builtin_amdgcn_readfirstlane(v);
+    return w1_0 + 2 * kFusedWaves + __builtin_amdgcn_readfirstlane(v);
   };
   auto flush_h = [&](int nb) {  // write the nb buffered items' h (pairs contiguous)
     const int ni2 = 2 * nb;
     for (int i = lane; i < T * ni2; i += kWave) {
       const int t = i / ni2, nl = i % ni2;
       const int it = S.hitem[wave][nl >> 1], d = it / g1;
-      const int slot = S.slot[t][S.dlist[d]];
+      const int slot = S.slot[t][S.dlist[wave][d]];
       if (slot >= 0)
         put_tagged(a.hx + static_cast<int64_t>(t * k + slot) * I + 2 * (it % g1) + (nl & 1),
                    S.hbuf[wave][t][nl], a.epoch);
@@ -624,7 +621,7 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
   // ---- phase 2: FC2 of this workgroup's expert(s)
   for (int d = dA; d < dB; ++d) {
     __syncthreads();   // previous expert's staging area is free
-    const int e = S.dlist[d];
+    const int e = S.dlist[wave][d];
     // stage h of expert d in register order (see FusedLds)
     for (int i = threadIdx.x; i < U2 * 4 * 32; i += kFusedThreads) {
       const int c = i / 128, j = (i / 32) % 4, l = i % 32;
