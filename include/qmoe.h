@@ -280,7 +280,7 @@ qmoe_status qmoe_route(qmoe_handle *handle, const void *logits, int64_t num_toke
  * kernel and zero-cold doorbell short-circuit for QMoE offload",
  * Motivation & Summary item 3: unsigned codes with a zero point):
  *   out_f32  device fp32 [N, K]: (q - zp) * s, exact, from the codes the
- *            decode paths' matrix operands carry (each code as 1 + q/128)
+ *            decode paths' matrix operands carry (each code as bf16 128 + q)
  *   out_f16  device fp16 bits [N, K]: fp16((q - zp) * s), rounded once to
  *            nearest even, from the same routine the grouped GEMMs' staging
  *            calls
