@@ -487,7 +487,9 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
   uint32_t b2A = 0u, b2B = 0u, z2A[U2], z2B[U2];
   const int last2 = max(q1 - 1, 0);
   load_fc2(dA, min(q0, last2), q0 < q1, w2A, s2A, b2A, z2A);
-  load_fc2(dA, min(q0 + 1, last2), q0 + 1 < q1, w2B, s2B, b2B, z2B);
+  // (a wave with a single FC2 item, as every wave has at M=1, loads no
+  // second one)
+  if (q0 + 1 < q1) load_fc2(dA, q0 + 1, true, w2B, s2B, b2B, z2B);
   __builtin_amdgcn_sched_barrier(0);
 
   // x pairs and their sums (x was staged in LDS before the routing's last barrier)
