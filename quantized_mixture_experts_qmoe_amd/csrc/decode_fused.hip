@@ -19,10 +19,11 @@
 //      workgroup each wave starts with two items and then claims the next
 //      unclaimed one from an LDS counter whenever it finishes one, so waves
 //      that the memory system serves sooner take more items. Each wave issues
-//      the loads of its first two FC1 items and its first two FC2 items
-//      before computing anything, keeps two items in flight, buffers its h
-//      values in LDS and writes them out in batches; right after its last FC1
-//      item it issues the loads of its third and fourth FC2 items;
+//      the loads of its first two FC1 items before computing anything, those
+//      of its first two FC2 items after its first FC1 item, keeps two FC1
+//      items in flight, buffers its h values in LDS and writes them out in
+//      batches; the loads of its third and fourth FC2 items follow once the
+//      expert's h is staged;
 //   2. FC2: a workgroup works on one expert (or, with more experts than
 //      workgroups, on whole experts in turn). It stages the expert's h in LDS
 //      as bf16 hi/lo pairs, waiting for each value to arrive, and its waves
@@ -474,8 +475,8 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
   UnitWords<BITS> w1A[U1], w1B[U1];
   uint32_t s1A[U1], s1B[U1];   // raw fp16 scales, one per register
   uint32_t b1A = 0u, b1B = 0u, z1A[U1], z1B[U1];   // raw bias and zero points (EX)
-  // (sched_barrier keeps the issue order A, B, FC2 A, FC2 B that the waits
-  // below count on)
+  // (sched_barrier keeps the issue order A, B that the waits below count
+  // on; the first FC2 items follow the wave's first FC1 item)
   const int last1 = max(w1_1 - 1, 0);
   int itA = w1_0 + wave, itB = w1_0 + kFusedWaves + wave;   // (itA past the end => itB too)
   load_fc1(min(itA, last1), itA < w1_1, w1A, s1A, b1A, z1A);
@@ -486,11 +487,14 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
   uint32_t s2A[U2], s2B[U2];
   uint32_t b2A = 0u, b2B = 0u, z2A[U2], z2B[U2];
   const int last2 = max(q1 - 1, 0);
-  load_fc2(dA, min(q0, last2), q0 < q1, w2A, s2A, b2A, z2A);
-  // (a wave with a single FC2 item, as every wave has at M=1, loads no
-  // second one)
-  if (q0 + 1 < q1) load_fc2(dA, q0 + 1, true, w2B, s2B, b2B, z2B);
-  __builtin_amdgcn_sched_barrier(0);
+  // FC2's first two items load once the wave's first FC1 item is computed,
+  // so the FC1 loads go out first; FC2 needs its weights only after h is
+  // staged. (A wave with a single FC2 item, as every wave has at M=1, loads
+  // no second one.)
+  auto load_fc2_first = [&]() {
+    load_fc2(dA, min(q0, last2), q0 < q1, w2A, s2A, b2A, z2A);
+    if (q0 + 1 < q1) load_fc2(dA, q0 + 1, true, w2B, s2B, b2B, z2B);
+  };
 
   // x pairs and their sums (x was staged in LDS before the routing's last barrier)
   uint32_t xp[U1][16];
@@ -590,6 +594,26 @@ __global__ __launch_bounds__(kFusedThreads) void decode_fused_kernel(FusedArgs a
     }
   };
   int nbuf = 0;   // items in this wave's h buffer
+  // (the loop's first pass, with FC2's first loads after the first item)
+  if (itA < w1_1) {
+    fc1_item(w1A, s1A, b1A, z1A, nbuf);
+    if (lane == 0) S.hitem[wave][nbuf] = itA;
+    ++nbuf;
+    const int nA = claim();
+    load_fc1(min(nA, last1), nA < w1_1, w1A, s1A, b1A, z1A);
+    load_fc2_first();
+    if (itB < w1_1) {
+      fc1_item(w1B, s1B, b1B, z1B, nbuf);
+      if (lane == 0) S.hitem[wave][nbuf] = itB;
+      ++nbuf;
+    }
+    const int nB = claim();
+    load_fc1(min(nB, last1), nB < w1_1, w1B, s1B, b1B, z1B);
+    itA = nA;
+    itB = nB;
+  } else {
+    load_fc2_first();
+  }
   while (itA < w1_1) {
     fc1_item(w1A, s1A, b1A, z1A, nbuf);
     if (lane == 0) S.hitem[wave][nbuf] = itA;
