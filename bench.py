@@ -211,7 +211,10 @@ def time_steps(step, K: int, hold_s: float):
 
 
 def kernel_times(layers, step, K: int, hold_s: float):
-    """Average duration (ms) per kernel role, from events the stage hook records."""
+    """Duration (ms) per kernel role: the median over the calls of the
+    interval between the events the stage hook records around it. (A host
+    stall while the steps are enqueued lands in one interval; the median
+    keeps it out.)"""
     marks = []
 
     def hook(stage, name):
@@ -228,14 +231,12 @@ def kernel_times(layers, step, K: int, hold_s: float):
     torch.cuda.synchronize()
     for L in layers:
         L.set_stage_hook(None)
-    sums, counts = {}, {}
+    per = {}
     for a, b in zip(marks, marks[1:]):
         if b[0] == 0:
             continue            # next call starts
-        ms = a[2].elapsed_time(b[2])
-        sums[b[1]] = sums.get(b[1], 0.0) + ms
-        counts[b[1]] = counts.get(b[1], 0) + 1
-    return {k: sums[k] / counts[k] for k in sums}
+        per.setdefault(b[1], []).append(a[2].elapsed_time(b[2]))
+    return {k: float(np.median(v)) for k, v in per.items()}
 
 
 # ----------------------------------------------------------------- workloads

@@ -379,7 +379,20 @@ void grouped_gemm_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         re[i] = static_cast<int16_t>(Bs[0][(prow + quad * 4 + i) * kLdsStride + kKT]);
-      const bool scaled = __ballot((re[0] | re[1] | re[2] | re[3]) != 0) != 0;
+      // the row exponents, then the bias, in place; both branches are
+      // wave-uniform, so the common case (no exponent, no bias) skips them
+      if (__ballot((re[0] | re[1] | re[2] | re[3]) != 0) != 0) {
+#pragma unroll
+        for (int tn = 0; tn < NT; ++tn)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[tm][tn][i] = ldexpf(acc[tm][tn][i], re[i]);
+      }
+      if (bias != nullptr) {
+#pragma unroll
+        for (int tn = 0; tn < NT; ++tn)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[tm][tn][i] += bcol[tn];
+      }
       if (FC1) {
         // h of this lane's 4 rows x NH columns, then per (row, 32-column
         // chunk of fragments 2c, 2c+1) the exponent that keeps the chunk in
@@ -389,10 +402,7 @@ void grouped_gemm_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int tn = 0; tn < NH; ++tn)
-            hv[i][tn] = scaled ? silu_mul_fast(ldexpf(acc[tm][tn][i], re[i]) + bcol[tn],
-                                               ldexpf(acc[tm][tn + NH][i], re[i]) + bcol[tn + NH])
-                               : silu_mul_fast(acc[tm][tn][i] + bcol[tn], acc[tm][tn + NH][i] + bcol[tn + NH]);
+          for (int tn = 0; tn < NH; ++tn) hv[i][tn] = silu_mul_fast(acc[tm][tn][i], acc[tm][tn + NH][i]);
         constexpr int NC = NH / 2;
         int ce[4][NC];
         // a chunk needs an exponent only if its maximum leaves [2^-14, 2^15]:
@@ -422,6 +432,10 @@ void grouped_gemm_kernel(
               m = fmaxf(m, row_rotate<1>(m));
               ce[i][c] = h_chunk_exponent(m);
             }
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int tn = 0; tn < NH; ++tn) hv[i][tn] = ldexpf(hv[i][tn], -ce[i][tn / 2]);
         }
         // h goes out in operand order, the order FC2's A rows need
         const int hpos = operand_pos(operand_perm(BITS), l16);
@@ -429,8 +443,7 @@ void grouped_gemm_kernel(
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int tn = 0; tn < NH; ++tn)
-            stg_h[(quad * 4 + i) * 72 + tn * 16 + hpos] =
-                __builtin_bit_cast(uint16_t, static_cast<_Float16>(ldexpf(hv[i][tn], -ce[i][tn / 2])));
+            stg_h[(quad * 4 + i) * 72 + tn * 16 + hpos] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(hv[i][tn]));
         if (l16 == 0) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -455,8 +468,7 @@ void grouped_gemm_kernel(
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int tn = 0; tn < NT; ++tn)
-            stg_y[(quad * 4 + i) * 132 + tn * 16 + l16] =
-                (scaled ? ldexpf(acc[tm][tn][i], re[i]) : acc[tm][tn][i]) + bcol[tn];
+            stg_y[(quad * 4 + i) * 132 + tn * 16 + l16] = acc[tm][tn][i];
         // 16 rows x NT*16 columns: NT*4 float4 per row
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
