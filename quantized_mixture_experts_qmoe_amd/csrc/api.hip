@@ -57,9 +57,9 @@ constexpr int kForceNone = 0, kForcePrefill = 1, kForceSmall = 2, kForceGrouped 
 // call; larger batches run the grouped GEMMs on 256-row tiles. Measured on
 // the Qwen3-30B-A3B-shaped INT4 layer (us per call, cold weights):
 //   tokens          5     8     9    12    16    24    32    64   128   256   384
-//   grouped decode 53    65    85    95   125   185
-//   small path           75    75    84    87         110   128   148   214   276
-//   grouped GEMMs 114   158         177   179   241   244   251   258   265   238
+//   grouped decode 45    55    71    81   107   158
+//   small path     55    71    72    81    84   101   106   121   144   211   263
+//   grouped GEMMs 100   135   136   152   154   204   207   213   224   231   232
 // QMOE_FORCE_PATH=grouped extends the grouped decode to 24 tokens.
 constexpr int64_t kGroupedDecodeMaxTokens = 8;
 constexpr int64_t kGroupedDecodeForcedMax = 24;
