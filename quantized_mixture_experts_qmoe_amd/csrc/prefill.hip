@@ -27,7 +27,7 @@
 // the MFMAs of stage s while the other dequantizes and stores its share of
 // stage s+1 (its own A rows and half of B) and issues its global loads for
 // stage s+2; each SIMD holds one wave of each group, so its matrix and vector
-// work overlap.
+// work overlap. The MFMA wave raises its issue priority for its phase.
 // A combine kernel then sums each token's k slots in slot order and rounds
 // once.
 //
@@ -317,8 +317,15 @@ void grouped_gemm_kernel(
   // loop per group (same barrier sequence), so each keeps only its own live
   // registers.
   auto kloop = [&](auto ntc) {
+    // (the MFMA wave of each SIMD runs at a raised issue priority, so its
+    // matrix instructions go first and the other group's dequantization
+    // fills the remaining issue slots)
     auto mfma_stage = [&](int buf) {
-      if (wave_live) mfma_steps(buf, ntc);
+      if (wave_live) {
+        __builtin_amdgcn_s_setprio(1);
+        mfma_steps(buf, ntc);
+        __builtin_amdgcn_s_setprio(0);
+      }
     };
     if (grp == 0) {
       for (int st = 0; st < ns; ++st) {
