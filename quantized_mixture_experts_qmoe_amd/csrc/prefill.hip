@@ -507,16 +507,34 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int m = (blockIdx.x * 256 + threadIdx.x) * 4;
   if (m >= H) return;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = 0; j < k; ++j) {
-    const int64_t p = inv_pos[t * k + j];
-    const float w = topk_w[t * k + j];
-    // each y value is read exactly once: non-temporal loads (27% faster
-    // than cached ones at 8K tokens)
-    const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(y + p * H + m));
+  // (each y value is read exactly once: non-temporal loads, 27% faster than
+  // cached ones at 8K tokens)
+  auto add = [&](float w, const f32x4_t& v) {
     acc.x = fmaf(w, v[0], acc.x);
     acc.y = fmaf(w, v[1], acc.y);
     acc.z = fmaf(w, v[2], acc.z);
     acc.w = fmaf(w, v[3], acc.w);
+  };
+  // slots in groups of eight: a group's loads all go out before its sums,
+  // which still run in slot order
+  int j = 0;
+  for (; j + 8 <= k; j += 8) {
+    int64_t p[8];
+    float w[8];
+    f32x4_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      p[u] = inv_pos[t * k + j + u];
+      w[u] = topk_w[t * k + j + u];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(y + p[u] * H + m));
+#pragma unroll
+    for (int u = 0; u < 8; ++u) add(w[u], v[u]);
+  }
+  for (; j < k; ++j) {
+    const int64_t p = inv_pos[t * k + j];
+    add(topk_w[t * k + j], __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(y + p * H + m)));
   }
   if constexpr (ACT == kActBF16) {
     uint2 o;
