@@ -565,32 +565,34 @@ __global__ __launch_bounds__(256) void stage_x_f16_kernel(const void* __restrict
 // Between the GEMMs: each route's h chunks brought to the route's largest
 // chunk exponent E (a chunk stored at e < E is multiplied by 2^(e - E), one
 // more fp16 rounding), and E written to rexp[route] for FC2. Chunks are
-// rewritten only in the rare routes whose exponents differ. One wave per
-// route; lane c reads chunk c's exponent.
+// rewritten only in the rare routes whose exponents differ. One thread per
+// route: it reads the route's exponent row (h_exp_stride bytes, 16-byte
+// aligned) 16 bytes at a time.
 __global__ __launch_bounds__(256) void h_common_exponent_kernel(uint16_t* __restrict__ h16,
                                                                const int8_t* __restrict__ hexp,
                                                                int8_t* __restrict__ rexp, int64_t R,
                                                                int I) {
-  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (r >= R) return;
-  const int lane = threadIdx.x & (kWave - 1);
   const int nchk = I / 32, hs = h_exp_stride(I);
   const int8_t* er = hexp + r * hs;
   int emax = -128, emin = 127;
-  for (int c = lane; c < nchk; c += kWave) {
-    const int e = er[c];
-    emax = max(emax, e);
-    emin = min(emin, e);
-  }
+  for (int c0 = 0; c0 < nchk; c0 += 16) {
+    const uint4 v = *reinterpret_cast<const uint4*>(er + c0);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-  for (int off = kWave / 2; off >= 1; off >>= 1) {
-    emax = max(emax, __shfl_xor(emax, off, kWave));
-    emin = min(emin, __shfl_xor(emin, off, kWave));
+    for (int b = 0; b < 16; ++b) {
+      if (c0 + b < nchk) {
+        const int e = static_cast<int8_t>(w[b >> 2] >> (8 * (b & 3)));
+        emax = max(emax, e);
+        emin = min(emin, e);
+      }
+    }
   }
-  if (lane == 0) rexp[r] = static_cast<int8_t>(emax);
+  rexp[r] = static_cast<int8_t>(emax);
   if (emin == emax) return;
-  // rare: rescale the chunks below E (8 fp16 values per lane and step)
-  for (int i = lane * 8; i < I; i += kWave * 8) {
+  // rare: rescale the chunks below E (8 fp16 values per step)
+  for (int i = 0; i < I; i += 8) {
     const int d = er[i >> 5] - emax;
     if (d == 0) continue;
     const uint16_t fb = d >= -14 ? static_cast<uint16_t>((d + 15) << 10)
@@ -633,7 +635,7 @@ hipError_t launch_gemms(const Layer& L, const uint16_t* xa, const int8_t* xexp, 
       L.fc1_row_bytes, L.fc1_nblk,
       tiles, ntiles, nt1, hb, nullptr, xexp, hexp);
   stage_done(L, 6, "gemm_fc1_swiglu");
-  h_common_exponent_kernel<<<static_cast<unsigned>((W.R + 3) / 4), 256, 0, s>>>(hb, hexp, rexp, W.R, I);
+  h_common_exponent_kernel<<<static_cast<unsigned>((W.R + 255) / 256), 256, 0, s>>>(hb, hexp, rexp, W.R, I);
   stage_done(L, 9, "h_common_exponent");
   fc2<<<static_cast<unsigned>(g2), kGemmThreads, 0, s>>>(
       hb, sorted, L.k, L.fc2_codes, L.fc2_scales, I, H, I, bs_shift, L.zp, L.fc2_zp, false, L.fc2_bias,
