@@ -310,16 +310,19 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
   // per chunk of 64 routes: each route's rank among the chunk's earlier
   // routes with its expert, and the chunk's count per expert (written by
   // the expert's last route in the chunk)
+  // (the lanes holding the same expert: the AND over the expert's bits of
+  // each bit's ballot or its complement)
   for (int c = wave; c < nch; c += 16) {
     const int r = 64 * c + lane;
     const int e = r < R ? s_id[r] : -1;
-    int rank = 0;
-    bool later = false;
-    for (int j = 0; j < kWave; ++j) {
-      const int ej = __shfl(e, j, kWave);
-      rank += (j < lane && ej == e) ? 1 : 0;
-      later = later || (j > lane && ej == e);
+    uint64_t same = __ballot(r < R);
+    for (int b = 0; (1 << b) < E; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t bb = __ballot(bit);
+      same &= bit ? bb : ~bb;
     }
+    const int rank = __popcll(same & ((1ull << lane) - 1ull));
+    const bool later = lane < kWave - 1 && (same >> (lane + 1)) != 0;
     if (r < R) {
       s_rank[r] = static_cast<uint8_t>(rank);
       if (!later) s_tab[c * E + e] = rank + 1;
